@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""EFLA chunked-forward benchmark on one MI355X.
+
+One step = one efla_chunk_fwd pass (coefficients + UT transform + sequential
+recurrence with the fused output) over the 1.3B-model-shaped layer:
+B=4, H=16, L=4096, d_k=d_v=128, chunk=64, bf16 q/k/v/beta/o, fp32 states.
+Inputs are synthetic and seeded, resident in HBM before timing starts.
+
+Prints ONE JSON line.  Besides the contract fields it carries:
+  roofline      the dominant kernel (the recurrence) against the HBM peak,
+                from HIP events recorded around it inside the timed loop
+  stages        per-stage event times and the whole-path fraction of peak
+  decode        efla_step at [256, 16, 128, 128] (fp32 state), back to back
+  cpu_baseline  the fp64 oracle on the same workload, on this host's cores
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "EFLA chunked-fwd tokens/s at H=16,d=128,L=4096; % of MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+KERNEL_SOURCES = ["delta_rule_sequence_efla_amd/csrc/chunk_kernels.h",
+                  "delta_rule_sequence_efla_amd/csrc/common.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "recurrence_shape_1p3b_traffic.txt")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="shape_1p3b")
+    ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cold-iters", type=int, default=10,
+                    help="extra iterations each preceded by a 1 GiB cache-flushing write")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 256 MiB device copy (HBM counter calibration under rocprofv3)")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(per_launch_units: dict):
+    """HBM bytes per recurrence launch from the committed rocprofv3 counter summary,
+    or None when it is missing or was taken on different kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            kv[key.strip()] = val.strip()
+    if kv.get("source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def pct(xs, p):
+    xs = sorted(xs)
+    i = min(len(xs) - 1, max(0, int(round(p / 100.0 * (len(xs) - 1)))))
+    return xs[i]
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the EFLA hot path shards over (batch, head) with no exchange, see DESIGN.md.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from delta_rule_sequence_efla_amd import efla
+    from delta_rule_sequence_efla_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = W.get(args.workload)
+    print(f"[bench] generating {w.name}: B={w.B} H={w.H} L={w.L} d={w.dk}/{w.dv} C={w.chunk}",
+          file=sys.stderr, flush=True)
+    inp = W.generate(w, device=dev)
+    q, k, v, beta, s0 = inp["q"], inp["k"], inp["v"], inp["beta"], inp["s0"]
+    o = torch.empty((w.B, w.L, w.H, w.dv), dtype=q.dtype, device=dev)
+    s_final = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    ws = efla.alloc_workspace(w.B, w.H, w.L, w.dk, w.dv, w.chunk, q.dtype, dev)
+    ut, rec = efla.prepare_chunk_stages(q, k, v, beta, s0, o, s_final, ws, chunk=w.chunk)
+
+    esz = q.element_size()
+    n_ht = w.B * w.H * w.L
+    nc = (w.L + w.chunk - 1) // w.chunk
+    state_bytes = w.B * w.H * w.dk * w.dv * 4
+    t_bytes = w.B * w.H * nc * w.chunk * w.chunk * esz
+    # algorithmic bytes: what each stage must read and write once
+    path_bytes = n_ht * ((2 * w.dk + 2 * w.dv) * esz + esz) + (state_bytes if s0 is not None else 0) \
+        + state_bytes
+    rec_bytes = n_ht * (2 * w.dk + 2 * w.dv) * esz + t_bytes + \
+        (state_bytes if s0 is not None else 0) + state_bytes
+    ut_bytes = n_ht * (w.dk + 1) * esz + t_bytes
+    path_flops = n_ht * (6 * w.dk * w.dv + 5 * w.chunk * max(w.dk, w.dv) + w.chunk ** 2 // 3)
+
+    for _ in range(args.warmup):
+        ut()
+        rec()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()
+        ut()
+        ev[i][1].record()
+        rec()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / K
+    ut_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
+    rec_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
+    path_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in range(K)]
+    rec_avg = sum(rec_ms) / K
+    ut_avg = sum(ut_ms) / K
+    path_avg = sum(path_ms) / K
+
+    tokens = w.B * w.L
+    value = tokens / (ms_per_step / 1e3)
+    achieved = rec_bytes / (rec_avg / 1e3) / 1e9
+    traffic = read_traffic({})
+
+    # cold-cache iterations: a 1 GiB write evicts L2 and the Infinity Cache first
+    cold = None
+    if args.cold_iters > 0:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        cms = []
+        for _ in range(args.cold_iters):
+            flush.fill_(1.0)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            ut()
+            rec()
+            b.record()
+            torch.cuda.synchronize()
+            cms.append(a.elapsed_time(b))
+        del flush
+        cold = {"median_us": round(pct(cms, 50) * 1e3, 2), "p10_us": round(pct(cms, 10) * 1e3, 2),
+                "p90_us": round(pct(cms, 90) * 1e3, 2),
+                "tokens_per_s": round(tokens / (pct(cms, 50) / 1e3), 1)}
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 26, dtype=torch.float32, device=dev)   # 256 MiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    decode = None
+    if not args.no_decode:
+        wd = W.get("decode_1p3b")
+        dinp = W.generate_decode(wd, device=dev, steps=1)
+        state = dinp["s0"].clone()
+        od = torch.empty((wd.B, wd.H, wd.dv), dtype=q.dtype, device=dev)
+        stp = efla.prepare_step(dinp["q"][0], dinp["k"][0], dinp["v"][0], dinp["beta"][0], state, od)
+        for _ in range(3):
+            stp()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.decode_steps):
+            stp()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / args.decode_steps
+        heads = wd.B * wd.H
+        dbytes = heads * (2 * wd.dk * wd.dv * 4 + (2 * wd.dk + 2 * wd.dv + 1) * esz)
+        decode = {"workload": "decode_1p3b", "N": wd.B, "H": wd.H, "d": wd.dk, "us_per_step": round(us, 2),
+                  "tokens_per_s": round(wd.B / (us / 1e6), 1),
+                  "roofline": {"bound": "hbm", "achieved": round(dbytes / (us / 1e6) / 1e9, 1),
+                               "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": round(dbytes / (us / 1e6) / 1e9 / HBM_PEAK_GBS, 4),
+                               "traffic": None},
+                  "note": "back-to-back steps on the same resident state"}
+        del state, dinp
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        from delta_rule_sequence_efla_amd.workloads import to_f64
+        cores = oracle.default_threads()
+        threads = min(cores, w.B * w.H)
+        qa, ka, va, ba, sa = (to_f64(x) for x in (q, k, v, beta, s0))
+        t = time.perf_counter()
+        oracle.forward(qa, ka, va, ba, sa, nthreads=threads)
+        ct = time.perf_counter() - t
+        cpu = {"value": round(tokens / ct, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"the whole {w.name} workload ({w.B * w.H} sequences x {w.L} tokens), "
+                         f"fp64 token-by-token recurrence, one pass, {ct:.2f} s wall"}
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if q.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d_k": w.dk, "d_v": w.dv,
+                   "chunk": w.chunk, "state": "fp32", "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "recurrence_kernel", "avg_us": round(rec_avg * 1e3, 2),
+                     "algorithmic_bytes": rec_bytes},
+        "stages": {"ut_transform_us": round(ut_avg * 1e3, 2), "ut_transform_bytes": ut_bytes,
+                   "recurrence_us": round(rec_avg * 1e3, 2),
+                   "path_us_events": round(path_avg * 1e3, 2), "path_algorithmic_bytes": path_bytes,
+                   "path_hbm_frac": round(path_bytes / (path_avg / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                   "path_mfma_frac": round(path_flops / (path_avg / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                   "head_tokens_per_s": round(n_ht / (ms_per_step / 1e3), 1)},
+        "cold": cold,
+        "decode": decode,
+        "cpu_baseline": cpu,
+        "kernel_source_sha256_16": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,176 @@
+// api.hip -- the C ABI of libefla (declared in include/efla.h): argument
+// validation, workspace sizing, choice of kernel instance, launches on the
+// caller's stream.  Nothing here allocates device memory or synchronizes.
+#include <stdlib.h>
+#include <string.h>
+
+#include "efla.h"
+#include "launchers.h"
+
+namespace {
+
+bool valid_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool valid_chunk(int c) { return c == 16 || c == 32 || c == 64; }
+bool valid_dtype(efla_dtype dt) { return dt == EFLA_F32 || dt == EFLA_BF16; }
+size_t elem_bytes(efla_dtype dt) { return dt == EFLA_BF16 ? 2 : 4; }
+constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
+
+efla_status from_hip(hipError_t e) { return e == hipSuccess ? EFLA_OK : EFLA_ERR_HIP; }
+
+// The kernels move q, k, v, T and states with 16-byte vector accesses.
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape checks shared by the chunked entry points (pointer checks are separate).
+efla_status check_chunk_shape(int B, int H, int64_t L, int d_k, int d_v, int chunk, efla_dtype dt) {
+  if (B < 1 || H < 1 || L < 0 || !valid_dtype(dt)) return EFLA_ERR_INVALID_ARG;
+  if (!valid_dim(d_k) || !valid_dim(d_v) || !valid_chunk(chunk)) return EFLA_ERR_UNSUPPORTED;
+  const int64_t bh = int64_t(B) * H;
+  const int64_t nc = (L + chunk - 1) / chunk;
+  if (bh * (d_v / 16) > kMaxGrid || bh * nc > kMaxGrid || nc > kMaxGrid) return EFLA_ERR_UNSUPPORTED;
+  return EFLA_OK;
+}
+
+// Width of the value block one recurrence workgroup owns.  Wider blocks share
+// more of each chunk's K/Q/T staging and P = tril(Q K^T) per workgroup; narrower
+// blocks give more workgroups.  Take the widest block that still gives at least
+// one workgroup per compute unit (256 on MI355X).  EFLA_VALUE_BLOCK (16, 32 or
+// 64) overrides the choice for tuning; fp32 always uses 16.
+int choose_value_block(efla_dtype dt, int64_t bh, int d_v) {
+  if (dt == EFLA_F32) return 16;
+  if (const char* env = getenv("EFLA_VALUE_BLOCK")) {
+    const int bv = atoi(env);
+    if ((bv == 16 || bv == 32 || bv == 64) && bv <= d_v) return bv;
+  }
+  for (int bv : {64, 32})
+    if (bv <= d_v && bh * (d_v / bv) >= 256) return bv;
+  return 16;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* efla_status_string(efla_status s) {
+  switch (s) {
+    case EFLA_OK: return "EFLA_OK";
+    case EFLA_ERR_INVALID_ARG: return "EFLA_ERR_INVALID_ARG: null pointer, negative size or bad enum";
+    case EFLA_ERR_UNSUPPORTED: return "EFLA_ERR_UNSUPPORTED: d_k/d_v must be 16/32/64/128, chunk 16/32/64";
+    case EFLA_ERR_WORKSPACE: return "EFLA_ERR_WORKSPACE: workspace missing or too small";
+    case EFLA_ERR_HIP: return "EFLA_ERR_HIP: a HIP launch or runtime call failed";
+  }
+  return "EFLA_ERR_UNKNOWN";
+}
+
+efla_status efla_coeff(const void* k, const void* beta, float* lambda, float* alpha, int64_t n_tok,
+                       int d_k, efla_dtype dtype, void* stream) {
+  if (n_tok < 0 || !valid_dtype(dtype)) return EFLA_ERR_INVALID_ARG;
+  if (!valid_dim(d_k)) return EFLA_ERR_UNSUPPORTED;
+  if (n_tok == 0) return EFLA_OK;
+  if (k == nullptr || beta == nullptr || alpha == nullptr) return EFLA_ERR_INVALID_ARG;
+  if ((n_tok + 255) / 256 > kMaxGrid) return EFLA_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == EFLA_BF16)
+    return from_hip(efla::launch_coeff<uint16_t>(static_cast<const uint16_t*>(k),
+                                                 static_cast<const uint16_t*>(beta), lambda, alpha,
+                                                 n_tok, d_k, s));
+  return from_hip(efla::launch_coeff<float>(static_cast<const float*>(k), static_cast<const float*>(beta),
+                                            lambda, alpha, n_tok, d_k, s));
+}
+
+size_t efla_chunk_fwd_workspace_size(int B, int H, int64_t L, int d_k, int d_v, int chunk,
+                                     efla_dtype dtype) {
+  if (check_chunk_shape(B, H, L, d_k, d_v, chunk, dtype) != EFLA_OK) return 0;
+  const int64_t nc = (L + chunk - 1) / chunk;
+  return size_t(B) * size_t(H) * size_t(nc) * size_t(chunk) * size_t(chunk) * elem_bytes(dtype);
+}
+
+efla_status efla_chunk_ut_transform(const void* k, const void* beta, int B, int H, int64_t L, int d_k,
+                                    int chunk, efla_dtype dtype, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  const efla_status st = check_chunk_shape(B, H, L, d_k, 16, chunk, dtype);
+  if (st != EFLA_OK) return st;
+  if (L == 0) return EFLA_OK;
+  if (k == nullptr || beta == nullptr || !aligned16(k)) return EFLA_ERR_INVALID_ARG;
+  const size_t need = efla_chunk_fwd_workspace_size(B, H, L, d_k, 16, chunk, dtype);
+  if (workspace == nullptr || workspace_bytes < need) return EFLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return EFLA_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == EFLA_BF16)
+    return from_hip(efla::launch_ut_transform<uint16_t>(static_cast<const uint16_t*>(k),
+                                                        static_cast<const uint16_t*>(beta),
+                                                        static_cast<uint16_t*>(workspace), B, H, L, d_k,
+                                                        chunk, s));
+  return from_hip(efla::launch_ut_transform<float>(static_cast<const float*>(k),
+                                                   static_cast<const float*>(beta),
+                                                   static_cast<float*>(workspace), B, H, L, d_k, chunk,
+                                                   s));
+}
+
+efla_status efla_chunk_recurrence(const void* q, const void* k, const void* v, const float* s0, void* o,
+                                  float* s_final, int B, int H, int64_t L, int d_k, int d_v, int chunk,
+                                  efla_dtype dtype, const void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  const efla_status st = check_chunk_shape(B, H, L, d_k, d_v, chunk, dtype);
+  if (st != EFLA_OK) return st;
+  if (L > 0) {
+    if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return EFLA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return EFLA_ERR_INVALID_ARG;
+    const size_t need = efla_chunk_fwd_workspace_size(B, H, L, d_k, d_v, chunk, dtype);
+    if (workspace == nullptr || workspace_bytes < need) return EFLA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return EFLA_ERR_INVALID_ARG;
+  }
+  if (L == 0 && s_final == nullptr) return EFLA_OK;
+  const int64_t bh = int64_t(B) * H;
+  const int bv = choose_value_block(dtype, bh, d_v);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == EFLA_BF16)
+    return from_hip(efla::launch_recurrence<uint16_t>(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+        static_cast<const uint16_t*>(workspace), s0, static_cast<uint16_t*>(o), s_final, B, H, L, d_k,
+        d_v, chunk, bv, s));
+  return from_hip(efla::launch_recurrence<float>(
+      static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
+      static_cast<const float*>(workspace), s0, static_cast<float*>(o), s_final, B, H, L, d_k, d_v, chunk,
+      bv, s));
+}
+
+efla_status efla_chunk_fwd(const void* q, const void* k, const void* v, const void* beta, const float* s0,
+                           void* o, float* s_final, int B, int H, int64_t L, int d_k, int d_v, int chunk,
+                           efla_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  const efla_status st = check_chunk_shape(B, H, L, d_k, d_v, chunk, dtype);
+  if (st != EFLA_OK) return st;
+  if (L > 0) {
+    if (q == nullptr || k == nullptr || v == nullptr || beta == nullptr || o == nullptr)
+      return EFLA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return EFLA_ERR_INVALID_ARG;
+    const size_t need = efla_chunk_fwd_workspace_size(B, H, L, d_k, d_v, chunk, dtype);
+    if (workspace == nullptr || workspace_bytes < need) return EFLA_ERR_WORKSPACE;
+    const efla_status s1 =
+        efla_chunk_ut_transform(k, beta, B, H, L, d_k, chunk, dtype, workspace, workspace_bytes, stream);
+    if (s1 != EFLA_OK) return s1;
+  }
+  return efla_chunk_recurrence(q, k, v, s0, o, s_final, B, H, L, d_k, d_v, chunk, dtype, workspace,
+                               workspace_bytes, stream);
+}
+
+efla_status efla_step(const void* q, const void* k, const void* v, const void* beta, float* state, void* o,
+                      int N, int H, int d_k, int d_v, efla_dtype dtype, void* stream) {
+  if (N < 0 || H < 0 || !valid_dtype(dtype)) return EFLA_ERR_INVALID_ARG;
+  if (!valid_dim(d_k) || !valid_dim(d_v)) return EFLA_ERR_UNSUPPORTED;
+  const int64_t units = int64_t(N) * H;
+  if (units == 0) return EFLA_OK;
+  if (units > kMaxGrid) return EFLA_ERR_UNSUPPORTED;
+  if (q == nullptr || k == nullptr || v == nullptr || beta == nullptr || state == nullptr || o == nullptr)
+    return EFLA_ERR_INVALID_ARG;
+  if (!aligned16(state)) return EFLA_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == EFLA_BF16)
+    return from_hip(efla::launch_step<uint16_t>(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+        static_cast<const uint16_t*>(beta), state, static_cast<uint16_t*>(o), units, d_k, d_v, s));
+  return from_hip(efla::launch_step<float>(static_cast<const float*>(q), static_cast<const float*>(k),
+                                           static_cast<const float*>(v), static_cast<const float*>(beta),
+                                           state, static_cast<float*>(o), units, d_k, d_v, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,10 @@
+// chunk_f32.hip -- fp32 instantiations of the chunked EFLA kernels.
+#include "chunk_kernels.h"
+
+namespace efla {
+template hipError_t launch_ut_transform<float>(const float*, const float*, float*, int, int, int64_t,
+                                               int, int, hipStream_t);
+template hipError_t launch_recurrence<float>(const float*, const float*, const float*, const float*,
+                                             const float*, float*, float*, int, int, int64_t, int, int,
+                                             int, int, hipStream_t);
+}  // namespace efla

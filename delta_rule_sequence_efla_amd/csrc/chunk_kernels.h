@@ -1,0 +1,490 @@
+// chunk_kernels.h -- chunkwise-parallel EFLA forward on gfx950.
+//
+// The update rule of the pages' Method step 3,
+//     S_t = (I - a_t k_t k_t^T) S_{t-1} + a_t k_t v_t^T,   o_t = S_t^T q_t,
+// keeps the rank-1 structure of the delta rule, so a chunk of C tokens with
+// start state S can be processed with dense products (the WY/UT scheme the
+// pages name).  With K, V, Q the chunk's rows and a the chunk's coefficients:
+//     T  = (I + tril(diag(a) K K^T, -1))^{-1} diag(a)          [UT transform]
+//     U' = T (V - K S)                                           [pseudo-values]
+//     O  = Q S + tril(Q K^T) U'          (diagonal included: o_t sees S_t)
+//     S <- S + K^T U'
+// Stage 1 (ut_transform_kernel) computes T for every chunk in parallel.
+// Stage 2 (recurrence_kernel) walks the chunks of one (batch, head, value
+// block) in order, keeping that block of S in registers in fp32.
+#pragma once
+
+#include "launchers.h"
+
+namespace efla {
+
+// Lower-triangular 16x16 tile pairs (r >= c) in row-major order: i -> (r, c).
+__device__ __forceinline__ void lower_tile(int i, int& r, int& c) {
+  r = 0;
+  c = i;
+  while (c > r) {
+    c -= r + 1;
+    ++r;
+  }
+}
+
+// Copy C rows of a [*, rowstride] global matrix (row t at base + t*rowstride)
+// into LDS with the given pitch; rows past `valid` are written as zeros.
+template <typename T, int ROWS, int COLS>
+__device__ __forceinline__ void stage_rows(T* dst, int pitch, const T* src, int64_t rowstride,
+                                           int valid, int tid) {
+  constexpr int VN = Vec16<T>::n;
+  constexpr int VPR = COLS / VN;
+#pragma unroll 2
+  for (int i = tid; i < ROWS * VPR; i += kThreads) {
+    const int t = i / VPR, c = (i % VPR) * VN;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (t < valid) val = *reinterpret_cast<const u32x4*>(src + t * rowstride + c);
+    *reinterpret_cast<u32x4*>(dst + t * pitch + c) = val;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Stage 1: per-chunk UT transform.  One workgroup per (b, h, chunk).
+//   a_t = beta_t * phi(beta_t ||k_t||^2)        (fused coefficient)
+//   A   = tril(diag(a) K K^T, -1)               (bf16 / fp32 matrix cores)
+//   X   = (I + A)^{-1}                          (blocked forward substitution, fp32)
+//   T   = X diag(a)                             -> workspace [B,H,NC,C,C]
+// ---------------------------------------------------------------------------
+template <typename T, int DK, int C>
+__global__ __launch_bounds__(kThreads) void ut_transform_kernel(const T* __restrict__ k,
+                                                                const T* __restrict__ beta,
+                                                                T* __restrict__ tws, int H,
+                                                                int64_t L, int NC) {
+  constexpr int DKP = round_up(DK, 32), CP = round_up(C, 32);
+  constexpr int NRT = C / 16, NKU_D = DKP / 32;
+  constexpr int KP = DKP + (sizeof(T) == 2 ? 8 : 4);
+  constexpr int AP = C + 4;
+  __shared__ __align__(16) T Ks[CP * KP];
+  __shared__ float alpha_s[CP];
+  __shared__ __align__(16) float As[C * AP];
+  __shared__ __align__(16) float Xs[C * AP];
+
+  const int64_t wg = blockIdx.x;
+  const int chunk = int(wg % NC);
+  const int64_t bh = wg / NC;
+  const int64_t b = bh / H, h = bh % H;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, g = lane >> 4;
+  const int64_t t0 = int64_t(chunk) * C;
+  const int valid = int(L - t0 < C ? L - t0 : C);
+  const int64_t row0 = (b * L + t0) * H + h;  // token t0 of this (b, h)
+
+  for (int i = tid; i < CP * KP; i += kThreads) Ks[i] = T(0);
+  for (int i = tid; i < C * AP; i += kThreads) {
+    As[i] = 0.0f;
+    Xs[i] = 0.0f;
+  }
+  __syncthreads();
+  stage_rows<T, C, DK>(Ks, KP, k + row0 * DK, int64_t(H) * DK, valid, tid);
+  __syncthreads();
+
+  if (tid < CP) {
+    float a = 0.0f;
+    if (tid < valid) {
+      float lam = 0.0f;
+      for (int d = 0; d < DK; ++d) {
+        const float x = to_f32(Ks[tid * KP + d]);
+        lam = fmaf(x, x, lam);
+      }
+      a = efla_alpha(to_f32(beta[row0 + int64_t(tid) * H]), lam);
+    }
+    alpha_s[tid] = a;
+  }
+  __syncthreads();
+
+  // A = strictly-lower part of diag(a) K K^T.
+  constexpr int NTILE = NRT * (NRT + 1) / 2;
+  for (int i = w; i < NTILE; i += 4) {
+    int r, c;
+    lower_tile(i, r, c);
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int ku = 0; ku < NKU_D; ++ku)
+      mma(acc, lds_frag(Ks, KP, 16 * r + li, ku, g), lds_frag(Ks, KP, 16 * c + li, ku, g));
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int ii = 16 * r + 4 * g + qq, jj = 16 * c + li;
+      if (ii > jj) As[ii * AP + jj] = alpha_s[ii] * acc[qq];
+    }
+  }
+  __syncthreads();
+
+  // Diagonal 16x16 blocks of X = (I + A)^{-1}: forward substitution, one lane
+  // per column of the block.
+  if (w < NRT && lane < 16) {
+    const int base = 16 * w, c = lane;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float s = (r == c) ? 1.0f : 0.0f;
+#pragma unroll
+      for (int m = 0; m < r; ++m) s = fmaf(-As[(base + r) * AP + base + m], x[m], s);
+      x[r] = s;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Xs[(base + r) * AP + base + c] = x[r];
+  }
+  __syncthreads();
+
+  // Off-diagonal blocks, one block row at a time:
+  //   X_ij = -X_ii * sum_{j <= m < i} A_im X_mj     (fp32 matrix cores)
+  for (int i = 1; i < NRT; ++i) {
+    for (int j = w; j < i; j += 4) {
+      f32x4 R = zero4();
+      for (int m = j; m < i; ++m) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const float a = As[(16 * i + li) * AP + 16 * m + 4 * g + qq];
+          const float bb = Xs[(16 * m + 4 * g + qq) * AP + 16 * j + li];
+          R = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, R, 0, 0, 0);
+        }
+      }
+      f32x4 Y = zero4();
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const float a = Xs[(16 * i + li) * AP + 16 * i + 4 * g + qq];
+        Y = __builtin_amdgcn_mfma_f32_16x16x4f32(a, R[qq], Y, 0, 0, 0);
+      }
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) Xs[(16 * i + 4 * g + qq) * AP + 16 * j + li] = -Y[qq];
+    }
+    __syncthreads();
+  }
+
+  // T = X diag(a), lower triangle, zeros above.
+  constexpr int VN = Vec16<T>::n;
+  constexpr int VPR = C / VN;
+  T* out = tws + (bh * NC + chunk) * int64_t(C) * C;
+  for (int i = tid; i < C * VPR; i += kThreads) {
+    const int t = i / VPR, s0 = (i % VPR) * VN;
+    union {
+      u32x4 u;
+      T e[VN];
+    } pk;
+#pragma unroll
+    for (int e = 0; e < VN; ++e) {
+      const int s = s0 + e;
+      pk.e[e] = from_f32<T>(s <= t ? Xs[t * AP + s] * alpha_s[s] : 0.0f);
+    }
+    *reinterpret_cast<u32x4*>(out + t * C + s0) = pk.u;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Stage 2: the sequential pass.  One workgroup of four wavefronts per
+// (b, h, value block of BV columns); columns of S evolve independently, so
+// value blocks are exact splits.  Wave w owns value tile cw = w % NCT and the
+// key-dim k-units {pw, pw + NDP, ...} with pw = w / NCT: its part of S stays
+// in registers (fp32) for the whole sequence.  Per chunk:
+//   Y_p = K[:, dims_p] S_p,  Z_p = Q[:, dims_p] S_p     (partial, own dims)
+//   P   = tril(Q K^T)                                    (shared via LDS)
+//   Y = sum_p Y_p, Z = sum_p Z_p                         (LDS exchange)
+//   U' = T (V - Y)          (every part computes all rows of its value tile)
+//   S_p += K^T[dims_p, :] U'
+//   O   = Z + P U'          (rows rt with rt % NDP == pw)
+// ---------------------------------------------------------------------------
+template <typename T, int DK, int C, int BV>
+__global__ __launch_bounds__(kThreads) void recurrence_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ tws, const float* __restrict__ s0, T* __restrict__ o,
+    float* __restrict__ sfin, int H, int64_t L, int NC, int DV, int NVB, int remap) {
+  constexpr int DKP = round_up(DK, 32), CP = round_up(C, 32);
+  constexpr int NRT = C / 16, NKU_D = DKP / 32, NKU_C = CP / 32;
+  constexpr int NCT = BV / 16, NDP = 4 / NCT;
+  constexpr int MAXO = cdiv(NKU_D, NDP);
+  constexpr int PADE = sizeof(T) == 2 ? 8 : 4;
+  constexpr int QP = DKP + PADE, VP = BV + PADE, TP = CP + PADE;
+  constexpr int NX = NDP > 1 ? NDP * NRT * NCT * kWave : 1;
+  static_assert(NCT * NDP == 4, "four wavefronts per workgroup");
+  __shared__ __align__(16) T Qs[CP * QP];
+  __shared__ __align__(16) T Ks[CP * QP];
+  __shared__ __align__(16) T Vs[C * VP];
+  __shared__ __align__(16) T Ts[C * TP];
+  __shared__ __align__(16) T Ps[C * TP];
+  __shared__ __align__(16) f32x4 Xy[NX];
+  __shared__ __align__(16) f32x4 Xz[NX];
+
+  // Workgroup -> (bh, value block).  With remap, all value blocks of one (b, h)
+  // get the same blockIdx % 8, i.e. the same XCD and L2, so their shared reads
+  // of q, k and T hit one cache.
+  const int x = blockIdx.x;
+  int bh, vb;
+  if (remap) {
+    const int slot = x >> 3;
+    vb = slot % NVB;
+    bh = (slot / NVB) * 8 + (x & 7);
+  } else {
+    bh = x / NVB;
+    vb = x % NVB;
+  }
+  const int64_t b = bh / H, h = bh % H;
+  const int v0 = vb * BV;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, g = lane >> 4;
+  const int cw = w % NCT, pw = w / NCT;
+  const int col = v0 + 16 * cw + li;  // this lane's value column
+
+  for (int i = tid; i < CP * QP; i += kThreads) {
+    Qs[i] = T(0);
+    Ks[i] = T(0);
+  }
+  for (int i = tid; i < C * VP; i += kThreads) Vs[i] = T(0);
+  for (int i = tid; i < C * TP; i += kThreads) {
+    Ts[i] = T(0);
+    Ps[i] = T(0);
+  }
+
+  // S tiles: Sacc[j][hh] covers key dims 32*ku + 16*hh + (0..15), ku = pw + j*NDP.
+  f32x4 Sacc[MAXO][2];
+#pragma unroll
+  for (int j = 0; j < MAXO; ++j) {
+    const int ku = pw + j * NDP;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int dim = 32 * ku + 16 * hh + 4 * g + qq;
+        Sacc[j][hh][qq] =
+            (s0 != nullptr && ku < NKU_D && dim < DK) ? s0[(int64_t(bh) * DK + dim) * DV + col] : 0.0f;
+      }
+  }
+
+  const int64_t qk_stride = int64_t(H) * DK, v_stride = int64_t(H) * DV;
+  for (int n = 0; n < NC; ++n) {
+    const int64_t t0 = int64_t(n) * C;
+    const int valid = int(L - t0 < C ? L - t0 : C);
+    const int64_t row0 = (b * L + t0) * H + h;
+    __syncthreads();  // previous chunk's LDS reads are done
+    stage_rows<T, C, DK>(Qs, QP, q + row0 * DK, qk_stride, valid, tid);
+    stage_rows<T, C, DK>(Ks, QP, k + row0 * DK, qk_stride, valid, tid);
+    stage_rows<T, C, BV>(Vs, VP, v + row0 * DV + v0, v_stride, valid, tid);
+    stage_rows<T, C, C>(Ts, TP, tws + (int64_t(bh) * NC + n) * C * C, C, C, tid);
+    __syncthreads();
+
+    // partial K S and Q S over this wave's key dims
+    f32x4 Y[NRT], Z[NRT];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      Y[rt] = zero4();
+      Z[rt] = zero4();
+    }
+#pragma unroll
+    for (int j = 0; j < MAXO; ++j) {
+      const int ku = pw + j * NDP;
+      if (ku < NKU_D) {
+        const Frag<T> bS = acc_frag<T>(Sacc[j][0], Sacc[j][1]);
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+          mma(Y[rt], lds_frag(Ks, QP, 16 * rt + li, ku, g), bS);
+          mma(Z[rt], lds_frag(Qs, QP, 16 * rt + li, ku, g), bS);
+        }
+      }
+    }
+
+    // P = tril(Q K^T), computed as P^T tiles (s-tile c <= t-tile r), into LDS.
+    constexpr int NTILE = NRT * (NRT + 1) / 2;
+    for (int i = w; i < NTILE; i += 4) {
+      int r, c;
+      lower_tile(i, r, c);
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int ku = 0; ku < NKU_D; ++ku)
+        mma(acc, lds_frag(Ks, QP, 16 * c + li, ku, g), lds_frag(Qs, QP, 16 * r + li, ku, g));
+      // acc[qq] = P[t = 16r + li][s = 16c + 4g + qq]
+      if (r == c) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          if (4 * g + qq > li) acc[qq] = 0.0f;
+      }
+      st4(Ps + (16 * r + li) * TP + 16 * c + 4 * g, acc);
+    }
+
+    if constexpr (NDP > 1) {
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        Xy[((pw * NRT + rt) * NCT + cw) * kWave + lane] = Y[rt];
+        Xz[((pw * NRT + rt) * NCT + cw) * kWave + lane] = Z[rt];
+      }
+    }
+    __syncthreads();
+    if constexpr (NDP > 1) {
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        f32x4 sy = zero4(), sz = zero4();
+#pragma unroll
+        for (int p = 0; p < NDP; ++p) {
+          sy += Xy[((p * NRT + rt) * NCT + cw) * kWave + lane];
+          sz += Xz[((p * NRT + rt) * NCT + cw) * kWave + lane];
+        }
+        Y[rt] = sy;
+        Z[rt] = sz;
+      }
+    }
+
+    // D = V - K S  (in place of Y), then U' = T D
+    f32x4 U[2 * NKU_C];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq)
+        Y[rt][qq] = to_f32(Vs[(16 * rt + 4 * g + qq) * VP + 16 * cw + li]) - Y[rt][qq];
+#pragma unroll
+    for (int rt = 0; rt < 2 * NKU_C; ++rt) {
+      U[rt] = zero4();
+      if (rt < NRT) {
+#pragma unroll
+        for (int ku = 0; ku < NKU_C; ++ku) {
+          if (32 * ku <= 16 * rt + 15) {
+            const f32x4 dlo = Y[2 * ku];
+            const f32x4 dhi = (2 * ku + 1 < NRT) ? Y[(2 * ku + 1) % NRT] : zero4();
+            mma(U[rt], lds_frag(Ts, TP, 16 * rt + li, ku, g), acc_frag<T>(dlo, dhi));
+          }
+        }
+      }
+    }
+
+    // S_p += K^T[dims_p, :] U'
+#pragma unroll
+    for (int j = 0; j < MAXO; ++j) {
+      const int ku = pw + j * NDP;
+      if (ku < NKU_D) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int dt = 2 * ku + hh;
+          if (16 * dt < DK) {
+#pragma unroll
+            for (int kt = 0; kt < NKU_C; ++kt)
+              mma(Sacc[j][hh], lds_frag_t(Ks, QP, 16 * dt + li, kt, g),
+                  acc_frag<T>(U[2 * kt], U[2 * kt + 1]));
+          }
+        }
+      }
+    }
+
+    // O = Q S + P U' for this wave's rows
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      if (rt % NDP == pw) {
+        f32x4 acc = Z[rt];
+#pragma unroll
+        for (int ku = 0; ku < NKU_C; ++ku)
+          if (32 * ku <= 16 * rt + 15)
+            mma(acc, lds_frag(Ps, TP, 16 * rt + li, ku, g), acc_frag<T>(U[2 * ku], U[2 * ku + 1]));
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const int t = 16 * rt + 4 * g + qq;
+          if (t < valid) o[(row0 + int64_t(t) * H) * DV + col] = from_f32<T>(acc[qq]);
+        }
+      }
+    }
+  }
+
+  if (sfin != nullptr) {
+#pragma unroll
+    for (int j = 0; j < MAXO; ++j) {
+      const int ku = pw + j * NDP;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const int dim = 32 * ku + 16 * hh + 4 * g + qq;
+          if (ku < NKU_D && dim < DK) sfin[(int64_t(bh) * DK + dim) * DV + col] = Sacc[j][hh][qq];
+        }
+    }
+  }
+}
+
+
+template <typename T, int DK, int C>
+hipError_t ut_transform_launch_impl(const T* k, const T* beta, T* tws, int B, int H, int64_t L,
+                                    hipStream_t stream) {
+  const int NC = int((L + C - 1) / C);
+  const int64_t nwg = int64_t(B) * H * NC;
+  if (nwg == 0) return hipSuccess;
+  hipLaunchKernelGGL((ut_transform_kernel<T, DK, C>), dim3(unsigned(nwg)), dim3(kThreads), 0, stream,
+                     k, beta, tws, H, L, NC);
+  return hipGetLastError();
+}
+
+template <typename T, int DK, int C, int BV>
+hipError_t recurrence_launch_impl(const T* q, const T* k, const T* v, const T* tws, const float* s0,
+                                  T* o, float* sfin, int B, int H, int64_t L, int DV,
+                                  hipStream_t stream) {
+  const int NC = int((L + C - 1) / C);
+  const int BH = B * H;
+  const int NVB = DV / BV;
+  const int nwg = BH * NVB;
+  if (nwg == 0) return hipSuccess;
+  const int remap = (BH % 8 == 0) ? 1 : 0;
+  hipLaunchKernelGGL((recurrence_kernel<T, DK, C, BV>), dim3(unsigned(nwg)), dim3(kThreads), 0, stream,
+                     q, k, v, tws, s0, o, sfin, H, L, NC, DV, NVB, remap);
+  return hipGetLastError();
+}
+
+template <typename T, int DK>
+hipError_t ut_dispatch_c(const T* k, const T* beta, T* tws, int B, int H, int64_t L, int C,
+                         hipStream_t s) {
+  switch (C) {
+    case 16: return ut_transform_launch_impl<T, DK, 16>(k, beta, tws, B, H, L, s);
+    case 32: return ut_transform_launch_impl<T, DK, 32>(k, beta, tws, B, H, L, s);
+    case 64: return ut_transform_launch_impl<T, DK, 64>(k, beta, tws, B, H, L, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t launch_ut_transform(const T* k, const T* beta, T* tws, int B, int H, int64_t L, int DK,
+                               int C, hipStream_t s) {
+  switch (DK) {
+    case 16: return ut_dispatch_c<T, 16>(k, beta, tws, B, H, L, C, s);
+    case 32: return ut_dispatch_c<T, 32>(k, beta, tws, B, H, L, C, s);
+    case 64: return ut_dispatch_c<T, 64>(k, beta, tws, B, H, L, C, s);
+    case 128: return ut_dispatch_c<T, 128>(k, beta, tws, B, H, L, C, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// Value-block widths compiled per element type: bf16 gets 16/32/64, fp32 16.
+template <typename T> struct BVSet { static constexpr bool has32 = true, has64 = true; };
+template <> struct BVSet<float> { static constexpr bool has32 = false, has64 = false; };
+
+template <typename T, int DK, int C>
+hipError_t rec_dispatch_bv(const T* q, const T* k, const T* v, const T* tws, const float* s0, T* o,
+                           float* sfin, int B, int H, int64_t L, int DV, int BV, hipStream_t s) {
+  if (BV == 16) return recurrence_launch_impl<T, DK, C, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, s);
+  if constexpr (BVSet<T>::has32)
+    if (BV == 32) return recurrence_launch_impl<T, DK, C, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, s);
+  if constexpr (BVSet<T>::has64)
+    if (BV == 64) return recurrence_launch_impl<T, DK, C, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, s);
+  return hipErrorInvalidValue;
+}
+
+template <typename T, int DK>
+hipError_t rec_dispatch_c(const T* q, const T* k, const T* v, const T* tws, const float* s0, T* o,
+                          float* sfin, int B, int H, int64_t L, int DV, int C, int BV, hipStream_t s) {
+  switch (C) {
+    case 16: return rec_dispatch_bv<T, DK, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, s);
+    case 32: return rec_dispatch_bv<T, DK, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, s);
+    case 64: return rec_dispatch_bv<T, DK, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t launch_recurrence(const T* q, const T* k, const T* v, const T* tws, const float* s0,
+                             T* o, float* sfin, int B, int H, int64_t L, int DK, int DV, int C,
+                             int BV, hipStream_t s) {
+  switch (DK) {
+    case 16: return rec_dispatch_c<T, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, C, BV, s);
+    case 32: return rec_dispatch_c<T, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, C, BV, s);
+    case 64: return rec_dispatch_c<T, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, C, BV, s);
+    case 128: return rec_dispatch_c<T, 128>(q, k, v, tws, s0, o, sfin, B, H, L, DV, C, BV, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace efla

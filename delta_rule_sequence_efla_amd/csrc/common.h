@@ -1,0 +1,151 @@
+// common.h -- device helpers shared by the EFLA kernels (gfx950 / CDNA4).
+//
+// Matrix-core conventions used by every kernel
+// --------------------------------------------
+// All products run on 16x16 output tiles.  A lane `l` of a 64-wide wavefront has
+// li = l % 16 and g = l / 16.  An accumulator tile holds D[4g + q][li] in its
+// element q (q = 0..3), the CDNA layout of v_mfma_f32_16x16x*.
+//
+// The reduction (k) index is consumed in "k-units" of 32.  A k-unit is two
+// 16-wide k tiles; element e (0..7) of a lane's operand fragment carries
+//       k = 32*ku + 16*(e/4) + 4*g + (e%4).
+// For bf16 one k-unit is one v_mfma_f32_16x16x32_bf16 (8 bf16 per lane); for
+// fp32 it is eight v_mfma_f32_16x16x4_f32 (one float per lane each).  The sum
+// over k does not depend on which k a (lane, element) slot carries as long as
+// the A and B fragments agree, and with this assignment the four rows 4g..4g+3
+// that an accumulator tile keeps in one lane are exactly the k values that lane
+// feeds to the next product.  So a product's result can be fed back as the next
+// product's operand straight from registers (accumulator -> fragment), with no
+// trip through LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace efla {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kThreads = 256;  // four wavefronts per workgroup
+
+__host__ __device__ constexpr int round_up(int x, int m) { return (x + m - 1) / m * m; }
+__host__ __device__ constexpr int cdiv(int x, int m) { return (x + m - 1) / m; }
+
+// ---- element types: float, or bf16 carried as its 16-bit pattern ----------
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float x) {
+  // round to nearest even (the hardware conversion on gfx950)
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+// ---- the coefficient of the exact flow ------------------------------------
+// alpha = (1 - e^{-beta*lambda}) / lambda, written as beta * (1 - e^{-x}) / x
+// with x = beta * lambda: no 0/0 at lambda = 0 and no loss when x underflows
+// (both give beta); x = +inf (stiff limit) gives 1/lambda.
+__device__ __forceinline__ float efla_alpha(float beta, float lam) {
+  const float x = beta * lam;
+  if (x == 0.0f) return beta;
+  if (x == __builtin_inff()) return 1.0f / lam;
+  return beta * (-expm1f(-x) / x);
+}
+
+// ---- operand fragments ------------------------------------------------------
+template <typename T> struct Frag;
+template <> struct Frag<uint16_t> { bf16x8 v; };
+template <> struct Frag<float> { float v[8]; };
+
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<uint16_t>& a, const Frag<uint16_t>& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], acc, 0, 0, 0);
+}
+
+// Fragment of a row-major LDS matrix X (pitch in elements): row `row`, k-unit ku.
+// Needs pitch % 4 == 0 and 8-byte (bf16) / 16-byte (fp32) aligned X.
+__device__ __forceinline__ Frag<uint16_t> lds_frag(const uint16_t* X, int pitch, int row, int ku, int g) {
+  const uint16_t* p = X + row * pitch + 32 * ku + 4 * g;
+  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
+  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
+  Frag<uint16_t> f;
+  f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return f;
+}
+__device__ __forceinline__ Frag<float> lds_frag(const float* X, int pitch, int row, int ku, int g) {
+  const float* p = X + row * pitch + 32 * ku + 4 * g;
+  const f32x4 lo = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 hi = *reinterpret_cast<const f32x4*>(p + 16);
+  Frag<float> f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f.v[e] = lo[e];
+    f.v[4 + e] = hi[e];
+  }
+  return f;
+}
+
+// Fragment of the TRANSPOSE of a row-major LDS matrix X[k][m]: operand row m = col.
+__device__ __forceinline__ Frag<uint16_t> lds_frag_t(const uint16_t* X, int pitch, int col, int ku, int g) {
+  Frag<uint16_t> f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int k = 32 * ku + 16 * (e / 4) + 4 * g + (e % 4);
+    f.v[e] = __builtin_bit_cast(__bf16, X[k * pitch + col]);
+  }
+  return f;
+}
+__device__ __forceinline__ Frag<float> lds_frag_t(const float* X, int pitch, int col, int ku, int g) {
+  Frag<float> f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int k = 32 * ku + 16 * (e / 4) + 4 * g + (e % 4);
+    f.v[e] = X[k * pitch + col];
+  }
+  return f;
+}
+
+// Fragment from two accumulator tiles (k tiles 2ku and 2ku+1 of the operand).
+template <typename T> __device__ __forceinline__ Frag<T> acc_frag(const f32x4& lo, const f32x4& hi);
+template <> __device__ __forceinline__ Frag<uint16_t> acc_frag<uint16_t>(const f32x4& lo, const f32x4& hi) {
+  Frag<uint16_t> f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f.v[e] = static_cast<__bf16>(lo[e]);
+    f.v[4 + e] = static_cast<__bf16>(hi[e]);
+  }
+  return f;
+}
+template <> __device__ __forceinline__ Frag<float> acc_frag<float>(const f32x4& lo, const f32x4& hi) {
+  Frag<float> f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f.v[e] = lo[e];
+    f.v[4 + e] = hi[e];
+  }
+  return f;
+}
+
+// Store four consecutive values (converted to T) to LDS: 8 B for bf16, 16 B for fp32.
+__device__ __forceinline__ void st4(uint16_t* p, const f32x4& x) {
+  bf16x4 h;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) h[e] = static_cast<__bf16>(x[e]);
+  *reinterpret_cast<bf16x4*>(p) = h;
+}
+__device__ __forceinline__ void st4(float* p, const f32x4& x) { *reinterpret_cast<f32x4*>(p) = x; }
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.0f, 0.0f, 0.0f, 0.0f}; }
+
+// 16-byte vector of T (8 bf16 or 4 fp32) used for global <-> LDS staging.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+template <typename T> struct Vec16 { static constexpr int n = 16 / sizeof(T); };
+
+}  // namespace efla

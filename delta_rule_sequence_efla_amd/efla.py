@@ -1,0 +1,265 @@
+"""Python binding of libefla (include/efla.h): argument marshalling only.
+
+Every function takes torch tensors that live on the GPU, checks shapes and
+dtypes, and passes raw device pointers plus torch's current HIP stream to the
+C ABI of the same name.  All arithmetic happens in the HIP kernels of
+``libefla.so``; there is no fallback path.  If the library is missing the first
+call raises ``RuntimeError``.
+
+EFLA ("Exact Flow Linear Attention", pages' Method steps 2-3): per (b, h),
+alpha_t = (1 - exp(-beta_t ||k_t||^2)) / ||k_t||^2,
+S_t = (I - alpha_t k_t k_t^T) S_{t-1} + alpha_t k_t v_t^T, o_t = S_t^T q_t.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libefla.so")
+
+EFLA_F32, EFLA_BF16 = 0, 1
+_DTYPES = {torch.float32: EFLA_F32, torch.bfloat16: EFLA_BF16}
+_STATUS = {0: "EFLA_OK", 1: "EFLA_ERR_INVALID_ARG", 2: "EFLA_ERR_UNSUPPORTED",
+           3: "EFLA_ERR_WORKSPACE", 4: "EFLA_ERR_HIP"}
+
+_lib = None
+_vp, _i, _i64, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+
+
+class EflaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {efla_status_string(status)}")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libefla.so (built in-tree by build.py); raise if it is absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                               "(or python delta_rule_sequence_efla_amd/build.py)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.efla_status_string.restype = ctypes.c_char_p
+        L.efla_status_string.argtypes = [_i]
+        L.efla_coeff.restype = _i
+        L.efla_coeff.argtypes = [_vp, _vp, _vp, _vp, _i64, _i, _i, _vp]
+        L.efla_chunk_fwd_workspace_size.restype = _sz
+        L.efla_chunk_fwd_workspace_size.argtypes = [_i, _i, _i64, _i, _i, _i, _i]
+        L.efla_chunk_fwd.restype = _i
+        L.efla_chunk_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i64, _i, _i, _i,
+                                     _i, _vp, _sz, _vp]
+        L.efla_chunk_ut_transform.restype = _i
+        L.efla_chunk_ut_transform.argtypes = [_vp, _vp, _i, _i, _i64, _i, _i, _i, _vp, _sz, _vp]
+        L.efla_chunk_recurrence.restype = _i
+        L.efla_chunk_recurrence.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i64, _i, _i,
+                                            _i, _i, _vp, _sz, _vp]
+        L.efla_step.restype = _i
+        L.efla_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]
+        _lib = L
+    return _lib
+
+
+def efla_status_string(status: int) -> str:
+    try:
+        return lib().efla_status_string(int(status)).decode()
+    except RuntimeError:
+        return _STATUS.get(int(status), f"status {status}")
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise EflaError(status, where)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev(*ts, dtype=None):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("EFLA tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("EFLA tensors must be contiguous")
+        if dtype is not None and t.dtype != dtype:
+            raise ValueError(f"expected dtype {dtype}, got {t.dtype}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("EFLA tensors must share one device")
+    return dev
+
+
+def _code(dtype) -> int:
+    if dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dtype}; use float32 or bfloat16")
+    return _DTYPES[dtype]
+
+
+def efla_coeff(k: torch.Tensor, beta: torch.Tensor, want_lambda: bool = True):
+    """lambda = ||k||^2 and alpha per key row; k [..., d_k], beta [...] -> fp32."""
+    dev = _dev(k, beta, dtype=k.dtype)
+    n = k.numel() // k.shape[-1]
+    if beta.numel() != n:
+        raise ValueError("beta needs one value per key row")
+    alpha = torch.empty(k.shape[:-1], dtype=torch.float32, device=dev)
+    lam = torch.empty_like(alpha) if want_lambda else None
+    with torch.cuda.device(dev):
+        _check(lib().efla_coeff(_p(k), _p(beta), _p(lam), _p(alpha), n, k.shape[-1],
+                                _code(k.dtype), _stream(dev)), "efla_coeff")
+    return lam, alpha
+
+
+def efla_chunk_fwd_workspace_size(B, H, L, d_k, d_v, chunk, dtype) -> int:
+    return int(lib().efla_chunk_fwd_workspace_size(B, H, L, d_k, d_v, chunk, _code(dtype)))
+
+
+def _chunk_shapes(q, k, v, beta, s0):
+    B, L, H, dk = k.shape
+    dv = v.shape[-1]
+    if q.shape != k.shape or v.shape[:3] != (B, L, H) or beta.shape != (B, L, H):
+        raise ValueError("expected q, k [B,L,H,dk], v [B,L,H,dv], beta [B,L,H]")
+    if s0 is not None and (s0.shape != (B, H, dk, dv) or s0.dtype != torch.float32):
+        raise ValueError("s0 must be float32 [B,H,dk,dv]")
+    return B, L, H, dk, dv
+
+
+def alloc_workspace(B, H, L, d_k, d_v, chunk, dtype, device) -> torch.Tensor:
+    n = efla_chunk_fwd_workspace_size(B, H, L, d_k, d_v, chunk, dtype)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def efla_chunk_fwd(q, k, v, beta, s0=None, chunk: int = 64, o=None, s_final=None,
+                   workspace=None, want_final: bool = True):
+    """Chunked EFLA forward.  Returns (o [B,L,H,dv] in q's dtype, S_L fp32 or None)."""
+    dev = _dev(q, k, v, beta, o, workspace, dtype=None)
+    _dev(q, k, v, beta, o, dtype=q.dtype)
+    _dev(s0, s_final, dtype=torch.float32)
+    B, L, H, dk, dv = _chunk_shapes(q, k, v, beta, s0)
+    if o is None:
+        o = torch.empty((B, L, H, dv), dtype=q.dtype, device=dev)
+    if s_final is None and want_final:
+        s_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = alloc_workspace(B, H, L, dk, dv, chunk, q.dtype, dev)
+    with torch.cuda.device(dev):
+        _check(lib().efla_chunk_fwd(_p(q), _p(k), _p(v), _p(beta), _p(s0), _p(o), _p(s_final),
+                                    B, H, L, dk, dv, chunk, _code(q.dtype), _p(workspace),
+                                    workspace.numel(), _stream(dev)), "efla_chunk_fwd")
+    return o, s_final
+
+
+def efla_chunk_ut_transform(k, beta, chunk: int = 64, workspace=None):
+    """Stage 1 only: per-chunk T into the workspace (returned as [B,H,NC,C,C] view)."""
+    dev = _dev(k, beta, dtype=k.dtype)
+    B, L, H, dk = k.shape
+    if workspace is None:
+        workspace = alloc_workspace(B, H, L, dk, 16, chunk, k.dtype, dev)
+    with torch.cuda.device(dev):
+        _check(lib().efla_chunk_ut_transform(_p(k), _p(beta), B, H, L, dk, chunk, _code(k.dtype),
+                                             _p(workspace), workspace.numel(), _stream(dev)),
+               "efla_chunk_ut_transform")
+    nc = (L + chunk - 1) // chunk
+    n = B * H * nc * chunk * chunk
+    return workspace, workspace[: n * k.element_size()].view(k.dtype).view(B, H, nc, chunk, chunk)
+
+
+def efla_chunk_recurrence(q, k, v, workspace, s0=None, chunk: int = 64, o=None, s_final=None,
+                          want_final: bool = True):
+    """Stage 2 only, reading T from a workspace filled by efla_chunk_ut_transform."""
+    dev = _dev(q, k, v, o, dtype=q.dtype)
+    _dev(s0, s_final, dtype=torch.float32)
+    B, L, H, dk = k.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((B, L, H, dv), dtype=q.dtype, device=dev)
+    if s_final is None and want_final:
+        s_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib().efla_chunk_recurrence(_p(q), _p(k), _p(v), _p(s0), _p(o), _p(s_final), B, H, L,
+                                           dk, dv, chunk, _code(q.dtype), _p(workspace),
+                                           workspace.numel(), _stream(dev)), "efla_chunk_recurrence")
+    return o, s_final
+
+
+def efla_step(q, k, v, beta, state, o=None):
+    """One decode step in place on state [N,H,dk,dv] (fp32).  Returns o [N,H,dv]."""
+    dev = _dev(q, k, v, beta, o, dtype=q.dtype)
+    _dev(state, dtype=torch.float32)
+    N, H, dk = k.shape
+    dv = v.shape[-1]
+    if q.shape != k.shape or v.shape[:2] != (N, H) or beta.shape != (N, H) \
+            or state.shape != (N, H, dk, dv):
+        raise ValueError("expected q, k [N,H,dk], v [N,H,dv], beta [N,H], state [N,H,dk,dv]")
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib().efla_step(_p(q), _p(k), _p(v), _p(beta), _p(state), _p(o), N, H, dk, dv,
+                               _code(q.dtype), _stream(dev)), "efla_step")
+    return o
+
+
+class PreparedCall:
+    """A C-ABI call with its arguments marshalled once (for tight timing loops).
+
+    Calling it re-issues the same launch on the stream captured at preparation;
+    the tensors passed to ``prepare_*`` must stay alive and unchanged in shape.
+    """
+
+    def __init__(self, fn, args, where: str, keep):
+        self._fn, self._args, self._where, self._keep = fn, args, where, keep
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st != 0:
+            raise EflaError(st, self._where)
+
+
+def prepare_chunk_stages(q, k, v, beta, s0, o, s_final, workspace, chunk: int = 64):
+    """(ut_transform, recurrence) prepared calls: together exactly efla_chunk_fwd."""
+    dev = _dev(q, k, v, beta, o, dtype=q.dtype)
+    _dev(s0, s_final, dtype=torch.float32)
+    B, L, H, dk, dv = _chunk_shapes(q, k, v, beta, s0)
+    code = _code(q.dtype)
+    stream = _stream(dev)
+    ws, nbytes = _p(workspace), workspace.numel()
+    ut = PreparedCall(lib().efla_chunk_ut_transform,
+                      (_p(k), _p(beta), B, H, L, dk, chunk, code, ws, nbytes, stream),
+                      "efla_chunk_ut_transform", (k, beta, workspace))
+    rec = PreparedCall(lib().efla_chunk_recurrence,
+                       (_p(q), _p(k), _p(v), _p(s0), _p(o), _p(s_final), B, H, L, dk, dv, chunk,
+                        code, ws, nbytes, stream),
+                       "efla_chunk_recurrence", (q, k, v, s0, o, s_final, workspace))
+    return ut, rec
+
+
+def prepare_chunk_fwd(q, k, v, beta, s0, o, s_final, workspace, chunk: int = 64):
+    dev = _dev(q, k, v, beta, o, dtype=q.dtype)
+    _dev(s0, s_final, dtype=torch.float32)
+    B, L, H, dk, dv = _chunk_shapes(q, k, v, beta, s0)
+    return PreparedCall(lib().efla_chunk_fwd,
+                        (_p(q), _p(k), _p(v), _p(beta), _p(s0), _p(o), _p(s_final), B, H, L, dk, dv,
+                         chunk, _code(q.dtype), _p(workspace), workspace.numel(), _stream(dev)),
+                        "efla_chunk_fwd", (q, k, v, beta, s0, o, s_final, workspace))
+
+
+def prepare_step(q, k, v, beta, state, o):
+    dev = _dev(q, k, v, beta, o, dtype=q.dtype)
+    _dev(state, dtype=torch.float32)
+    N, H, dk = k.shape
+    dv = v.shape[-1]
+    return PreparedCall(lib().efla_step,
+                        (_p(q), _p(k), _p(v), _p(beta), _p(state), _p(o), N, H, dk, dv,
+                         _code(q.dtype), _stream(dev)),
+                        "efla_step", (q, k, v, beta, state, o))

@@ -1,0 +1,146 @@
+/*
+ * efla.h -- C ABI of the MI355X (gfx950) Exact Flow Linear Attention library.
+ *
+ * The method ("Exact Flow Linear Attention: Exact Solution from Continuous-Time
+ * Dynamics", gist.science summary pages, Method steps 2-3): per (batch, head)
+ * sequence, with lambda_t = ||k_t||^2 and
+ *     alpha_t = (1 - exp(-beta_t * lambda_t)) / lambda_t,
+ * the associative state S (d_k x d_v) evolves as
+ *     S_t = (I - alpha_t k_t k_t^T) S_{t-1} + alpha_t k_t v_t^T
+ * and the output is read out after each update as o_t = S_t^T q_t.
+ * The pages note that the update keeps the rank-1 structure of the delta rule,
+ * so the WY/UT chunkwise-parallel scheme applies (Method step 3); the chunked
+ * entry points below compute exactly that recurrence, chunk by chunk.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates nothing and keeps no mutable global state; calls on different
+ *     streams with disjoint outputs may run concurrently.
+ *   - Layouts are dense row-major:
+ *         q, k   [B, L, H, d_k]       v, o   [B, L, H, d_v]       beta [B, L, H]
+ *         state  [B, H, d_k, d_v]  (float32; S[i][j], i = key dim, j = value dim)
+ *     Decode uses the same layouts with L = 1 folded away: q, k [N, H, d_k],
+ *     v, o [N, H, d_v], beta [N, H], state [N, H, d_k, d_v].
+ *   - dtype selects the element type of q, k, v, beta and o (float32 or
+ *     bfloat16).  States are always float32; arithmetic is float32 (bf16 inputs
+ *     feed bf16 matrix-core products with float32 accumulation).
+ *   - Supported sizes: d_k, d_v in {16, 32, 64, 128}; chunk in {16, 32, 64};
+ *     any L >= 0 (a ragged last chunk is handled); B, H >= 1 with B*H < 2^31.
+ *   - stream is a hipStream_t passed as void* (NULL = default stream).  Calls are
+ *     asynchronous: EFLA_OK means the work was enqueued.
+ *   - q, k, v, the workspace and decode states must be 16-byte aligned (torch
+ *     allocations are); a misaligned pointer is EFLA_ERR_INVALID_ARG.
+ *   - Errors: arguments are validated before anything is launched; on a
+ *     validation error nothing is written.  A failed launch returns
+ *     EFLA_ERR_HIP; outputs are then undefined.  NaN/Inf inputs are not checked
+ *     and propagate.
+ */
+#ifndef EFLA_H
+#define EFLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum efla_status {
+    EFLA_OK = 0,
+    EFLA_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad enum       */
+    EFLA_ERR_UNSUPPORTED = 2, /* d_k / d_v / chunk outside the supported set  */
+    EFLA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required   */
+    EFLA_ERR_HIP = 4          /* a HIP launch or runtime call failed          */
+} efla_status;
+
+typedef enum efla_dtype {
+    EFLA_F32 = 0,  /* float32 q, k, v, beta, o */
+    EFLA_BF16 = 1  /* bfloat16 q, k, v, beta, o */
+} efla_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *efla_status_string(efla_status s);
+
+/*
+ * efla_coeff -- the coefficient of Method step 3 for n_tok key rows.
+ *   k      [n_tok, d_k] (dtype), beta [n_tok] (dtype)
+ *   lambda [n_tok] float32 out, may be NULL: lambda_t = ||k_t||^2
+ *   alpha  [n_tok] float32 out: alpha_t = (1 - exp(-beta_t lambda_t)) / lambda_t,
+ *          evaluated as beta_t * (-expm1(-x)/x), x = beta_t * lambda_t, which is
+ *          beta_t when x == 0 (lambda -> 0 limit) and 1/lambda_t when x == +inf.
+ * n_tok may be 0 (nothing is launched).
+ */
+efla_status efla_coeff(const void *k, const void *beta, float *lambda, float *alpha,
+                       int64_t n_tok, int d_k, efla_dtype dtype, void *stream);
+
+/*
+ * Bytes of device workspace efla_chunk_fwd needs (0 if L == 0).  The workspace
+ * holds, per (b, h, chunk), the chunk's UT-transform matrix
+ * T = (I + tril(diag(alpha) K K^T, -1))^{-1} diag(alpha)  (chunk x chunk, dtype).
+ * Returns 0 for unsupported arguments.
+ */
+size_t efla_chunk_fwd_workspace_size(int B, int H, int64_t L, int d_k, int d_v,
+                                     int chunk, efla_dtype dtype);
+
+/*
+ * efla_chunk_fwd -- chunkwise-parallel EFLA forward pass (Method step 3 and the
+ * WY/UT chunked scheme it refers to).  For every (b, h):
+ *     S = s0[b, h] (or zeros if s0 == NULL)
+ *     for t = 0 .. L-1:  S = (I - alpha_t k_t k_t^T) S + alpha_t k_t v_t^T;
+ *                        o[b, t, h] = S^T q_t
+ *     s_final[b, h] = S     (skipped if s_final == NULL; may alias s0)
+ * computed chunk by chunk: per chunk of C tokens with start state S,
+ *     T  = (I + tril(diag(alpha) K K^T, -1))^{-1} diag(alpha)
+ *     U' = T (V - K S);   O = Q S + tril(Q K^T) U';   S <- S + K^T U'.
+ * q, k, v, beta, o in dtype; s0, s_final float32.  workspace must hold
+ * efla_chunk_fwd_workspace_size(...) bytes, 16-byte aligned.  o must not
+ * alias any input.
+ */
+efla_status efla_chunk_fwd(const void *q, const void *k, const void *v, const void *beta,
+                           const float *s0, void *o, float *s_final,
+                           int B, int H, int64_t L, int d_k, int d_v, int chunk,
+                           efla_dtype dtype, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/*
+ * The two stages of efla_chunk_fwd, exposed so that each can be checked and
+ * timed on its own.  Calling efla_chunk_ut_transform then efla_chunk_recurrence
+ * on the same stream with the same workspace is exactly efla_chunk_fwd.
+ *
+ * efla_chunk_ut_transform -- per (b, h, chunk): alpha from k and beta (as
+ * efla_coeff), then the chunk's T (definition above) written to the workspace
+ * as [B, H, ceil(L/chunk), chunk, chunk] row-major in dtype; entries above the
+ * diagonal and rows/columns of tokens past L are zero.
+ */
+efla_status efla_chunk_ut_transform(const void *k, const void *beta, int B, int H, int64_t L,
+                                    int d_k, int chunk, efla_dtype dtype, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+
+/*
+ * efla_chunk_recurrence -- the sequential pass over chunks of every (b, h):
+ * U' = T (V - K S), O = Q S + tril(Q K^T) U', S <- S + K^T U', reading T from
+ * a workspace filled by efla_chunk_ut_transform with the same sizes.
+ */
+efla_status efla_chunk_recurrence(const void *q, const void *k, const void *v,
+                                  const float *s0, void *o, float *s_final,
+                                  int B, int H, int64_t L, int d_k, int d_v, int chunk,
+                                  efla_dtype dtype, const void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/*
+ * efla_step -- one decode step: a single token per (n, h) applied in place
+ * (Method step 3):
+ *     state[n, h] = (I - alpha k k^T) state[n, h] + alpha k v^T
+ *     o[n, h]     = state[n, h]^T q        (post-update readout)
+ * q, k [N, H, d_k], v, o [N, H, d_v], beta [N, H] in dtype; state [N, H, d_k, d_v]
+ * float32, read and written once.  N*H may be 0.
+ */
+efla_status efla_step(const void *q, const void *k, const void *v, const void *beta,
+                      float *state, void *o, int N, int H, int d_k, int d_v,
+                      efla_dtype dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EFLA_H */

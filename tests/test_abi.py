@@ -1,0 +1,106 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/efla.h declares, and rejects bad arguments before
+launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from delta_rule_sequence_efla_amd import efla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "efla.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(efla_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ["efla_coeff", "efla_chunk_fwd_workspace_size", "efla_chunk_fwd", "efla_step",
+                     "efla_status_string", "efla_chunk_ut_transform", "efla_chunk_recurrence"]:
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = efla.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), f"libefla.so does not export {name}"
+
+
+def test_status_strings():
+    for code, prefix in [(0, "EFLA_OK"), (1, "EFLA_ERR_INVALID_ARG"), (2, "EFLA_ERR_UNSUPPORTED"),
+                         (3, "EFLA_ERR_WORKSPACE"), (4, "EFLA_ERR_HIP")]:
+        assert efla.efla_status_string(code).startswith(prefix)
+    assert efla.efla_status_string(99) == "EFLA_ERR_UNKNOWN"
+
+
+def test_workspace_size():
+    f = efla.efla_chunk_fwd_workspace_size
+    # 1.3B-shaped layer: 4*16 sequences x 64 chunks x 64x64 bf16
+    assert f(4, 16, 4096, 128, 128, 64, torch.bfloat16) == 4 * 16 * 64 * 64 * 64 * 2
+    assert f(1, 1, 65, 16, 16, 16, torch.float32) == 5 * 16 * 16 * 4  # ragged: 5 chunks
+    assert f(1, 1, 0, 16, 16, 16, torch.float32) == 0
+    assert f(1, 1, 64, 24, 16, 16, torch.float32) == 0    # unsupported d_k
+    assert f(1, 1, 64, 16, 16, 48, torch.float32) == 0    # unsupported chunk
+    assert f(0, 1, 64, 16, 16, 16, torch.float32) == 0
+
+
+def test_validation_happens_before_any_launch():
+    L = efla.lib()
+    nul = None
+    # unsupported sizes
+    assert L.efla_chunk_fwd(nul, nul, nul, nul, nul, nul, nul, 1, 1, 64, 24, 16, 16, 0, nul, 0, nul) == 2
+    assert L.efla_chunk_fwd(nul, nul, nul, nul, nul, nul, nul, 1, 1, 64, 16, 16, 8, 0, nul, 0, nul) == 2
+    assert L.efla_step(nul, nul, nul, nul, nul, nul, 1, 1, 16, 200, 1, nul) == 2
+    assert L.efla_coeff(nul, nul, nul, nul, 5, 12, 0, nul) == 2
+    # invalid arguments
+    assert L.efla_chunk_fwd(nul, nul, nul, nul, nul, nul, nul, 0, 1, 64, 16, 16, 16, 0, nul, 0, nul) == 1
+    assert L.efla_chunk_fwd(nul, nul, nul, nul, nul, nul, nul, 1, 1, -1, 16, 16, 16, 0, nul, 0, nul) == 1
+    assert L.efla_chunk_fwd(nul, nul, nul, nul, nul, nul, nul, 1, 1, 64, 16, 16, 16, 7, nul, 0, nul) == 1
+    assert L.efla_chunk_fwd(nul, nul, nul, nul, nul, nul, nul, 1, 1, 64, 16, 16, 16, 0, nul, 0, nul) == 1
+    assert L.efla_step(nul, nul, nul, nul, nul, nul, 2, 2, 16, 16, 0, nul) == 1
+    assert L.efla_coeff(nul, nul, nul, nul, 5, 16, 0, nul) == 1
+    assert L.efla_coeff(nul, nul, nul, nul, -1, 16, 0, nul) == 1
+    # workspace too small (pointers are never dereferenced: validation fails first)
+    fake = ctypes.c_void_p(4096)
+    assert L.efla_chunk_fwd(fake, fake, fake, fake, nul, fake, nul, 1, 1, 64, 16, 16, 16, 0,
+                            nul, 0, nul) == 3
+    assert L.efla_chunk_fwd(fake, fake, fake, fake, nul, fake, nul, 1, 1, 64, 16, 16, 16, 0,
+                            fake, 1023, nul) == 3
+    # misaligned q
+    odd = ctypes.c_void_p(4098)
+    assert L.efla_chunk_fwd(odd, fake, fake, fake, nul, fake, nul, 1, 1, 64, 16, 16, 16, 0,
+                            fake, 4096, nul) == 1
+    # nothing to do is success without a launch
+    assert L.efla_step(nul, nul, nul, nul, nul, nul, 0, 4, 16, 16, 0, nul) == 0
+    assert L.efla_coeff(nul, nul, nul, nul, 0, 16, 0, nul) == 0
+    assert L.efla_chunk_fwd(nul, nul, nul, nul, nul, nul, nul, 1, 1, 0, 16, 16, 16, 0, nul, 0, nul) == 0
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(efla, "_lib", None)
+    monkeypatch.setattr(efla, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        efla.lib()
+
+
+def test_binding_rejects_host_tensors():
+    x = torch.zeros(1, 4, 1, 16)
+    with pytest.raises(ValueError):
+        efla.efla_chunk_fwd(x, x, x, torch.zeros(1, 4, 1), chunk=16)
+
+
+def test_product_package_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "delta_rule_sequence_efla_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "efla_oracle" not in text, f

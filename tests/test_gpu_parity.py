@@ -1,0 +1,274 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Tolerances are normwise per tensor (max|x - y| / max|y|): fp32 inputs <= 1e-4
+on o and on the final state; bf16 inputs (fp32 state and accumulation) <= 2e-2
+on o and <= 1e-2 on the final state.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from delta_rule_sequence_efla_amd import efla
+from delta_rule_sequence_efla_amd import workloads as W
+from delta_rule_sequence_efla_amd.workloads import to_f64
+from tests._util import TOL, dtype_name, normwise, oracle_forward, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _gen(name, **kw):
+    require_gpu()
+    sizes = {k: kw.pop(k) for k in ("B", "H", "L", "seed") if k in kw}
+    w = W.get(name, **kw)
+    return w, W.generate(w, device="cuda", **sizes)
+
+
+def _check_forward(inp, chunk, label, tol=None):
+    o, sf = efla.efla_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["s0"], chunk=chunk)
+    torch.cuda.synchronize()
+    ro, rs = oracle_forward(inp)
+    tol = tol or TOL[dtype_name(inp["q"])]
+    eo, es = normwise(to_f64(o), ro), normwise(to_f64(sf), rs)
+    _say(f"[parity] {label}: o err {eo:.3e} (tol {tol['o']}), S err {es:.3e} (tol {tol['s']})")
+    assert np.isfinite(to_f64(o)).all() and np.isfinite(to_f64(sf)).all()
+    assert eo <= tol["o"], f"{label}: output error {eo:.3e}"
+    assert es <= tol["s"], f"{label}: state error {es:.3e}"
+    return o, sf
+
+
+# ---------------------------------------------------------------------------
+# coefficient (efla_coeff)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_coeff_matches_oracle(dtype):
+    require_gpu()
+    dk = 16
+    lams = [0.0, 1e-30, 1e-12, 1e-6, 1e-3, 0.1, 1.0, 16.0, 88.0, 900.0, 1e4]
+    betas = [0.0, 1e-8, 0.05, 0.5, 1.0, 3.0, 10.0]
+    rows, bs = [], []
+    for lam in lams:
+        for b in betas:
+            r = np.zeros(dk)
+            r[0] = math.sqrt(lam)
+            rows.append(r)
+            bs.append(b)
+    rng = np.random.default_rng(7)
+    for _ in range(200):  # random keys over the stiff range, all dims populated
+        rows.append(rng.standard_normal(dk) * math.exp(rng.uniform(math.log(0.1), math.log(30))))
+        bs.append(rng.uniform(0, 10))
+    k = torch.tensor(np.array(rows), dtype=torch.float32).to(dtype).cuda()
+    beta = torch.tensor(np.array(bs), dtype=torch.float32).to(dtype).cuda()
+    lam_g, alp_g = efla.efla_coeff(k, beta)
+    torch.cuda.synchronize()
+    lam_r, alp_r = oracle.coeff(to_f64(k), to_f64(beta))
+    lam_g, alp_g = to_f64(lam_g), to_f64(alp_g)
+    np.testing.assert_allclose(lam_g, lam_r, rtol=2e-6, atol=0)
+    np.testing.assert_allclose(alp_g, alp_r, rtol=2e-6, atol=1e-37)
+    # exact special cases: x == 0 gives beta, beta == 0 gives 0
+    zero_x = (lam_r == 0) | (to_f64(beta) == 0)
+    assert np.array_equal(alp_g[zero_x], to_f64(beta)[zero_x])
+
+
+# ---------------------------------------------------------------------------
+# chunked forward: small shapes spanning every template axis, ragged tails
+# ---------------------------------------------------------------------------
+
+SMALL = [
+    # dtype, dk, dv, chunk, L
+    ("f32", 16, 16, 16, 64),
+    ("f32", 32, 64, 32, 75),
+    ("f32", 64, 32, 16, 33),
+    ("f32", 128, 128, 64, 200),
+    ("f32", 128, 16, 32, 47),
+    ("bf16", 16, 16, 16, 40),
+    ("bf16", 32, 32, 64, 1),
+    ("bf16", 64, 64, 64, 300),
+    ("bf16", 128, 128, 64, 257),
+    ("bf16", 16, 128, 32, 100),
+    ("bf16", 128, 16, 16, 50),
+    ("bf16", 64, 128, 32, 129),
+    ("bf16", 128, 64, 16, 96),
+]
+
+
+@pytest.mark.parametrize("dt,dk,dv,chunk,L", SMALL, ids=lambda x: str(x))
+def test_chunk_fwd_small_shapes(dt, dk, dv, chunk, L):
+    w, inp = _gen("shape_340m", dtype=dt, dk=dk, dv=dv, chunk=chunk, B=2, H=3, L=L,
+                  seed=5000 + dk + dv + chunk + L)
+    _check_forward(inp, chunk, f"{dt} dk{dk} dv{dv} C{chunk} L{L}")
+
+
+def test_tiny_fp32_workload():
+    """B=1, H=1, L=64, d=16, chunk=16, unnormalised N(0,1) q/k, zero initial state."""
+    w, inp = _gen("tiny_fp32")
+    assert inp["s0"] is None
+    _check_forward(inp, w.chunk, "tiny_fp32")
+
+
+@pytest.mark.parametrize("bv", ["16", "32", "64"])
+def test_value_block_widths_agree(bv, monkeypatch):
+    """Every value-block width of the recurrence gives oracle parity; the
+    choice is a launch-shape detail, not a different computation."""
+    monkeypatch.setenv("EFLA_VALUE_BLOCK", bv)
+    w, inp = _gen("shape_340m", B=2, H=4, L=200, seed=61)
+    _check_forward(inp, 64, f"value block {bv}")
+
+
+def test_unnormalised_bf16_stiff_small():
+    w, inp = _gen("stiff_64k", B=2, H=4, L=700, seed=77)
+    _check_forward(inp, 64, "stiff small")
+
+
+# ---------------------------------------------------------------------------
+# stage 1 against the oracle through the WY identity:
+#   prod_t (I - a_t k_t k_t^T) = I - K^T T K     and     K^T T V = S_C from zero.
+# ---------------------------------------------------------------------------
+
+def test_ut_transform_wy_identity():
+    require_gpu()
+    rng = np.random.default_rng(3)
+    C, dk = 32, 32
+    k = rng.standard_normal((1, C, 1, dk)) * np.exp(rng.uniform(-1, 1, (1, C, 1, 1)))
+    beta = rng.uniform(0, 2, (1, C, 1))
+    kt = torch.tensor(k, dtype=torch.float32).cuda()
+    bt = torch.tensor(beta, dtype=torch.float32).cuda()
+    _, T = efla.efla_chunk_ut_transform(kt, bt, chunk=C)
+    torch.cuda.synchronize()
+    T = to_f64(T)[0, 0, 0]
+    K = to_f64(kt)[0, :, 0]
+    assert np.array_equal(np.triu(T, 1), np.zeros_like(T))
+    _, prod = oracle.forward(np.zeros((1, C, 1, dk)), K[None, :, None], np.zeros((1, C, 1, dk)),
+                             to_f64(bt), np.eye(dk)[None, None])
+    lhs = np.eye(dk) - K.T @ T @ K
+    assert normwise(lhs, prod[0, 0]) <= 2e-5
+    V = rng.standard_normal((C, 8))
+    _, s_from_zero = oracle.forward(np.zeros((1, C, 1, dk)), K[None, :, None], V[None, :, None],
+                                    to_f64(bt), None)
+    assert normwise(K.T @ T @ V, s_from_zero[0, 0]) <= 2e-5
+
+
+# ---------------------------------------------------------------------------
+# invariances and edge cases
+# ---------------------------------------------------------------------------
+
+def test_chunk_size_invariance_and_stage_split():
+    w, inp = _gen("shape_340m", dtype="f32", B=2, H=2, L=150, seed=90)
+    outs = []
+    for c in (16, 32, 64):
+        o, sf = efla.efla_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["s0"], chunk=c)
+        outs.append((to_f64(o), to_f64(sf)))
+    torch.cuda.synchronize()
+    for o, sf in outs[1:]:
+        assert normwise(o, outs[0][0]) <= 1e-5 and normwise(sf, outs[0][1]) <= 1e-5
+    # the two stages called separately are the same computation as efla_chunk_fwd
+    ws, _ = efla.efla_chunk_ut_transform(inp["k"], inp["beta"], chunk=64)
+    o2, s2 = efla.efla_chunk_recurrence(inp["q"], inp["k"], inp["v"], ws, inp["s0"], chunk=64)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_f64(o2), outs[2][0]) and np.array_equal(to_f64(s2), outs[2][1])
+
+
+def test_split_resume_and_decode_equivalence():
+    w, inp = _gen("shape_340m", dtype="f32", B=2, H=3, L=90, dk=32, dv=64, seed=91)
+    q, k, v, beta, s0 = inp["q"], inp["k"], inp["v"], inp["beta"], inp["s0"]
+    o, sf = efla.efla_chunk_fwd(q, k, v, beta, s0, chunk=32)
+    o1, s1 = efla.efla_chunk_fwd(q[:, :41].contiguous(), k[:, :41].contiguous(),
+                                 v[:, :41].contiguous(), beta[:, :41].contiguous(), s0, chunk=32)
+    o2, s2 = efla.efla_chunk_fwd(q[:, 41:].contiguous(), k[:, 41:].contiguous(),
+                                 v[:, 41:].contiguous(), beta[:, 41:].contiguous(), s1, chunk=32)
+    st = s0.clone()
+    steps = [efla.efla_step(q[:, t].contiguous(), k[:, t].contiguous(), v[:, t].contiguous(),
+                            beta[:, t].contiguous(), st) for t in range(90)]
+    torch.cuda.synchronize()
+    assert normwise(to_f64(torch.cat([o1, o2], 1)), to_f64(o)) <= 1e-5
+    assert normwise(to_f64(s2), to_f64(sf)) <= 1e-5
+    assert normwise(to_f64(torch.stack(steps, 1)), to_f64(o)) <= 1e-5
+    assert normwise(to_f64(st), to_f64(sf)) <= 1e-5
+
+
+def test_deterministic_bitwise():
+    w, inp = _gen("shape_340m", B=2, H=8, L=300, seed=92)
+    runs = []
+    for _ in range(4):
+        o, sf = efla.efla_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["s0"], chunk=64)
+        runs.append((o.clone(), sf.clone()))
+    torch.cuda.synchronize()
+    for o, sf in runs[1:]:
+        assert torch.equal(o, runs[0][0]) and torch.equal(sf, runs[0][1])
+
+
+def test_empty_sequence_copies_state():
+    w, inp = _gen("shape_340m", B=2, H=2, L=0, seed=93)
+    o, sf = efla.efla_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["s0"], chunk=64)
+    torch.cuda.synchronize()
+    assert o.shape[1] == 0 and torch.equal(sf, inp["s0"])
+    o, sf = efla.efla_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["beta"], None, chunk=64)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(sf) == 0
+
+
+def test_degenerate_tokens():
+    """beta = 0 and zero keys are identity steps; beta*lambda huge overwrites."""
+    w, inp = _gen("shape_340m", dtype="f32", B=1, H=2, L=70, dk=32, dv=32, seed=94)
+    beta = inp["beta"].clone()
+    k = inp["k"].clone()
+    beta[:, 5:9] = 0.0
+    k[:, 20:23] = 0.0
+    beta[:, 40:44] = 1e6
+    inp = dict(inp, beta=beta, k=k)
+    _check_forward(inp, 32, "degenerate tokens")
+
+
+def test_invalid_arguments_are_rejected():
+    require_gpu()
+    q = torch.zeros(1, 8, 1, 16, device="cuda")
+    with pytest.raises(efla.EflaError) as e:
+        efla.efla_chunk_fwd(q, q, q, torch.zeros(1, 8, 1, device="cuda"), chunk=48)
+    assert e.value.status == 2
+    ws = torch.empty(4, dtype=torch.uint8, device="cuda")
+    with pytest.raises(efla.EflaError) as e:
+        efla.efla_chunk_fwd(q, q, q, torch.zeros(1, 8, 1, device="cuda"), chunk=16, workspace=ws)
+    assert e.value.status == 3
+
+
+# ---------------------------------------------------------------------------
+# decode (efla_step), 16 consecutive steps at the 1.3B-layer decode shape
+# ---------------------------------------------------------------------------
+
+def test_decode_1p3b_sixteen_steps():
+    require_gpu()
+    w = W.get("decode_1p3b")
+    inp = W.generate_decode(w, device="cuda")
+    state = inp["s0"].clone()
+    ref_state = to_f64(inp["s0"])
+    worst_o = 0.0
+    for s in range(w.steps):
+        o = efla.efla_step(inp["q"][s], inp["k"][s], inp["v"][s], inp["beta"][s], state)
+        torch.cuda.synchronize()
+        ro, ref_state = oracle.step(to_f64(inp["q"][s]), to_f64(inp["k"][s]), to_f64(inp["v"][s]),
+                                    to_f64(inp["beta"][s]), ref_state)
+        worst_o = max(worst_o, normwise(to_f64(o), ro))
+    es = normwise(to_f64(state), ref_state)
+    _say(f"[parity] decode_1p3b x{w.steps}: worst o err {worst_o:.3e}, S err {es:.3e}")
+    assert worst_o <= TOL["bf16"]["o"]
+    assert es <= 1e-4  # fp32 state and arithmetic: far inside the bf16 bound
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, in the launch configuration the benchmark times
+# ---------------------------------------------------------------------------
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["small_bf16", "shape_340m", "shape_1p3b", "stiff_64k"])
+def test_full_size_workloads(name):
+    w, inp = _gen(name)
+    _say(f"[parity] {name}: B={w.B} H={w.H} L={w.L} dk={w.dk} dv={w.dv} chunk={w.chunk}")
+    _check_forward(inp, w.chunk, name)
