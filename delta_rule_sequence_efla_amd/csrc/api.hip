@@ -114,7 +114,7 @@ efla_status efla_chunk_recurrence(const void* q, const void* k, const void* v, c
   if (st != EFLA_OK) return st;
   if (L > 0) {
     if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return EFLA_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return EFLA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return EFLA_ERR_INVALID_ARG;
     const size_t need = efla_chunk_fwd_workspace_size(B, H, L, d_k, d_v, chunk, dtype);
     if (workspace == nullptr || workspace_bytes < need) return EFLA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return EFLA_ERR_INVALID_ARG;
@@ -123,11 +123,27 @@ efla_status efla_chunk_recurrence(const void* q, const void* k, const void* v, c
   const int64_t bh = int64_t(B) * H;
   const int bv = choose_value_block(dtype, bh, d_v);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == EFLA_BF16)
+  if (dtype == EFLA_BF16) {
+    // Kernel choice: v4 (DMA-fed ring) where it applies, else v3, else the
+    // generic kernel.  EFLA_RECURRENCE_IMPL=v2|v3|v4 pins one for comparisons.
+    const char* impl = getenv("EFLA_RECURRENCE_IMPL");
+    const bool want_v2 = impl && strcmp(impl, "v2") == 0, want_v3 = impl && strcmp(impl, "v3") == 0;
+    if (!want_v2 && !want_v3 && efla::recurrence_v4_supported(d_k, chunk, bv))
+      return from_hip(efla::launch_recurrence_v4_bf16(
+          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+          static_cast<const uint16_t*>(workspace), s0, static_cast<uint16_t*>(o), s_final, B, H, L, d_k,
+          d_v, chunk, bv, s));
+    const bool use_v3 = efla::recurrence_v3_supported(d_k, chunk) && !want_v2;
+    if (use_v3)
+      return from_hip(efla::launch_recurrence_v3_bf16(
+          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+          static_cast<const uint16_t*>(workspace), s0, static_cast<uint16_t*>(o), s_final, B, H, L, d_k,
+          d_v, chunk, bv, s));
     return from_hip(efla::launch_recurrence<uint16_t>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
         static_cast<const uint16_t*>(workspace), s0, static_cast<uint16_t*>(o), s_final, B, H, L, d_k,
         d_v, chunk, bv, s));
+  }
   return from_hip(efla::launch_recurrence<float>(
       static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
       static_cast<const float*>(workspace), s0, static_cast<float*>(o), s_final, B, H, L, d_k, d_v, chunk,
@@ -142,7 +158,7 @@ efla_status efla_chunk_fwd(const void* q, const void* k, const void* v, const vo
   if (L > 0) {
     if (q == nullptr || k == nullptr || v == nullptr || beta == nullptr || o == nullptr)
       return EFLA_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return EFLA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return EFLA_ERR_INVALID_ARG;
     const size_t need = efla_chunk_fwd_workspace_size(B, H, L, d_k, d_v, chunk, dtype);
     if (workspace == nullptr || workspace_bytes < need) return EFLA_ERR_WORKSPACE;
     const efla_status s1 =

@@ -28,28 +28,68 @@ __device__ __forceinline__ void lower_tile(int i, int& r, int& c) {
   }
 }
 
-// Copy C rows of a [*, rowstride] global matrix (row t at base + t*rowstride)
-// into LDS with the given pitch; rows past `valid` are written as zeros.
+// Rows [0, ROWS) x cols [0, COLS) of a strided global matrix (row t at
+// src + t*rowstride), moved in 16-byte vectors through registers so that the
+// loads of the next chunk can be in flight while the current one is computed.
+// Rows at or past `valid` load as zeros.
 template <typename T, int ROWS, int COLS>
-__device__ __forceinline__ void stage_rows(T* dst, int pitch, const T* src, int64_t rowstride,
-                                           int valid, int tid) {
-  constexpr int VN = Vec16<T>::n;
-  constexpr int VPR = COLS / VN;
-#pragma unroll 2
-  for (int i = tid; i < ROWS * VPR; i += kThreads) {
-    const int t = i / VPR, c = (i % VPR) * VN;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (t < valid) val = *reinterpret_cast<const u32x4*>(src + t * rowstride + c);
-    *reinterpret_cast<u32x4*>(dst + t * pitch + c) = val;
+struct RowStager {
+  static constexpr int VN = Vec16<T>::n, VPR = COLS / VN, TOT = ROWS * VPR, CNT = cdiv(TOT, kThreads);
+  u32x4 r[CNT];
+
+  __device__ __forceinline__ void load(const T* src, int64_t rowstride, int valid, int tid) {
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) {
+      const int idx = tid + i * kThreads;
+      const int t = idx / VPR, c = (idx % VPR) * VN;
+      r[i] = u32x4{0u, 0u, 0u, 0u};
+      if (idx < TOT && t < valid) r[i] = *reinterpret_cast<const u32x4*>(src + t * rowstride + c);
+    }
   }
+  __device__ __forceinline__ void store(T* dst, int pitch, int tid) const {
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) {
+      const int idx = tid + i * kThreads;
+      if (idx < TOT) {
+        const int t = idx / VPR, c = (idx % VPR) * VN;
+        *reinterpret_cast<u32x4*>(dst + t * pitch + c) = r[i];
+      }
+    }
+  }
+  // Transposed copy: element (t, c + e) goes to dst[(c + e) * pitch + t].
+  __device__ __forceinline__ void store_t(T* dst, int pitch, int tid) const {
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) {
+      const int idx = tid + i * kThreads;
+      if (idx < TOT) {
+        const int t = idx / VPR, c = (idx % VPR) * VN;
+        union {
+          u32x4 u;
+          T e[VN];
+        } x;
+        x.u = r[i];
+#pragma unroll
+        for (int e = 0; e < VN; ++e) dst[(c + e) * pitch + t] = x.e[e];
+      }
+    }
+  }
+};
+
+// Zero `n` elements of an LDS array (n * sizeof(T) a multiple of 16 bytes).
+template <typename T>
+__device__ __forceinline__ void lds_zero(T* p, int n, int tid) {
+  u32x4* v = reinterpret_cast<u32x4*>(p);
+  const int nv = n * int(sizeof(T)) / 16;
+  for (int i = tid; i < nv; i += kThreads) v[i] = u32x4{0u, 0u, 0u, 0u};
 }
 
 // ---------------------------------------------------------------------------
 // Stage 1: per-chunk UT transform.  One workgroup per (b, h, chunk).
-//   a_t = beta_t * phi(beta_t ||k_t||^2)        (fused coefficient)
-//   A   = tril(diag(a) K K^T, -1)               (bf16 / fp32 matrix cores)
-//   X   = (I + A)^{-1}                          (blocked forward substitution, fp32)
-//   T   = X diag(a)                             -> workspace [B,H,NC,C,C]
+//   G   = K K^T                                   (matrix cores; diagonal = lambda)
+//   a_t = beta_t * phi(beta_t * lambda_t)         (fused coefficient)
+//   X   = (I + diag(a) tril(G, -1))^{-1}          (blocked forward substitution, fp32)
+//   T   = X diag(a)                               -> workspace [B,H,NC,C,C]
+// The row scaling diag(a) is applied inside the solve instead of to G.
 // ---------------------------------------------------------------------------
 template <typename T, int DK, int C>
 __global__ __launch_bounds__(kThreads) void ut_transform_kernel(const T* __restrict__ k,
@@ -61,9 +101,9 @@ __global__ __launch_bounds__(kThreads) void ut_transform_kernel(const T* __restr
   constexpr int KP = DKP + (sizeof(T) == 2 ? 8 : 4);
   constexpr int AP = C + 4;
   __shared__ __align__(16) T Ks[CP * KP];
-  __shared__ float alpha_s[CP];
-  __shared__ __align__(16) float As[C * AP];
-  __shared__ __align__(16) float Xs[C * AP];
+  __shared__ float lam_s[CP], alpha_s[CP];
+  __shared__ __align__(16) float Gs[C * AP];  // strictly lower part of K K^T
+  __shared__ __align__(16) float Xs[C * AP];  // X = (I + A)^{-1}, lower blocks
 
   const int64_t wg = blockIdx.x;
   const int chunk = int(wg % NC);
@@ -74,30 +114,18 @@ __global__ __launch_bounds__(kThreads) void ut_transform_kernel(const T* __restr
   const int valid = int(L - t0 < C ? L - t0 : C);
   const int64_t row0 = (b * L + t0) * H + h;  // token t0 of this (b, h)
 
-  for (int i = tid; i < CP * KP; i += kThreads) Ks[i] = T(0);
-  for (int i = tid; i < C * AP; i += kThreads) {
-    As[i] = 0.0f;
-    Xs[i] = 0.0f;
-  }
-  __syncthreads();
-  stage_rows<T, C, DK>(Ks, KP, k + row0 * DK, int64_t(H) * DK, valid, tid);
-  __syncthreads();
-
-  if (tid < CP) {
-    float a = 0.0f;
-    if (tid < valid) {
-      float lam = 0.0f;
-      for (int d = 0; d < DK; ++d) {
-        const float x = to_f32(Ks[tid * KP + d]);
-        lam = fmaf(x, x, lam);
-      }
-      a = efla_alpha(to_f32(beta[row0 + int64_t(tid) * H]), lam);
-    }
-    alpha_s[tid] = a;
+  if constexpr (DK < DKP || C < CP) lds_zero(Ks, CP * KP, tid);
+  float bt = 0.0f;
+  if (tid < valid) bt = to_f32(beta[row0 + int64_t(tid) * H]);
+  {
+    RowStager<T, C, DK> sk;
+    sk.load(k + row0 * DK, int64_t(H) * DK, valid, tid);
+    if constexpr (DK < DKP || C < CP) __syncthreads();
+    sk.store(Ks, KP, tid);
   }
   __syncthreads();
 
-  // A = strictly-lower part of diag(a) K K^T.
+  // G tiles on and below the diagonal; the diagonal gives lambda.
   constexpr int NTILE = NRT * (NRT + 1) / 2;
   for (int i = w; i < NTILE; i += 4) {
     int r, c;
@@ -109,41 +137,46 @@ __global__ __launch_bounds__(kThreads) void ut_transform_kernel(const T* __restr
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       const int ii = 16 * r + 4 * g + qq, jj = 16 * c + li;
-      if (ii > jj) As[ii * AP + jj] = alpha_s[ii] * acc[qq];
+      if (ii > jj) Gs[ii * AP + jj] = acc[qq];
+      if (ii == jj) lam_s[ii] = acc[qq];
     }
   }
   __syncthreads();
+  if (tid < C) alpha_s[tid] = (tid < valid) ? efla_alpha(bt, lam_s[tid]) : 0.0f;
+  __syncthreads();
 
-  // Diagonal 16x16 blocks of X = (I + A)^{-1}: forward substitution, one lane
-  // per column of the block.
+  // Diagonal 16x16 blocks of X: forward substitution, one lane per column:
+  //   x_r = delta_rc - a_r * sum_{m < r} G_rm x_m
   if (w < NRT && lane < 16) {
     const int base = 16 * w, c = lane;
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float s = (r == c) ? 1.0f : 0.0f;
+      float s = 0.0f;
 #pragma unroll
-      for (int m = 0; m < r; ++m) s = fmaf(-As[(base + r) * AP + base + m], x[m], s);
-      x[r] = s;
+      for (int m = 0; m < r; ++m) s = fmaf(Gs[(base + r) * AP + base + m], x[m], s);
+      x[r] = (r == c ? 1.0f : 0.0f) - alpha_s[base + r] * s;
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) Xs[(base + r) * AP + base + c] = x[r];
   }
   __syncthreads();
 
-  // Off-diagonal blocks, one block row at a time:
-  //   X_ij = -X_ii * sum_{j <= m < i} A_im X_mj     (fp32 matrix cores)
+  // Off-diagonal blocks, one block row at a time (fp32 matrix cores):
+  //   X_ij = -X_ii * diag(a_i) * sum_{j <= m < i} G_im X_mj
   for (int i = 1; i < NRT; ++i) {
     for (int j = w; j < i; j += 4) {
       f32x4 R = zero4();
       for (int m = j; m < i; ++m) {
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
-          const float a = As[(16 * i + li) * AP + 16 * m + 4 * g + qq];
+          const float a = Gs[(16 * i + li) * AP + 16 * m + 4 * g + qq];
           const float bb = Xs[(16 * m + 4 * g + qq) * AP + 16 * j + li];
           R = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, R, 0, 0, 0);
         }
       }
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) R[qq] *= alpha_s[16 * i + 4 * g + qq];
       f32x4 Y = zero4();
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
@@ -187,6 +220,8 @@ __global__ __launch_bounds__(kThreads) void ut_transform_kernel(const T* __restr
 //   U' = T (V - Y)          (every part computes all rows of its value tile)
 //   S_p += K^T[dims_p, :] U'
 //   O   = Z + P U'          (rows rt with rt % NDP == pw)
+// The global loads of chunk n+1 are issued before chunk n is computed and land
+// in LDS after it, so HBM latency overlaps the per-chunk dependency chain.
 // ---------------------------------------------------------------------------
 template <typename T, int DK, int C, int BV>
 __global__ __launch_bounds__(kThreads) void recurrence_kernel(
@@ -197,15 +232,20 @@ __global__ __launch_bounds__(kThreads) void recurrence_kernel(
   constexpr int NRT = C / 16, NKU_D = DKP / 32, NKU_C = CP / 32;
   constexpr int NCT = BV / 16, NDP = 4 / NCT;
   constexpr int MAXO = cdiv(NKU_D, NDP);
-  constexpr int PADE = sizeof(T) == 2 ? 8 : 4;
+  constexpr bool kBF16 = sizeof(T) == 2;
+  constexpr int PADE = kBF16 ? 8 : 4;
   constexpr int QP = DKP + PADE, VP = BV + PADE, TP = CP + PADE;
+  constexpr int KTP = CP + PADE;                 // pitch of the transposed K copy
   constexpr int NX = NDP > 1 ? NDP * NRT * NCT * kWave : 1;
+  constexpr int OP = 16 + PADE;                  // pitch of a wave's output staging tile
   static_assert(NCT * NDP == 4, "four wavefronts per workgroup");
   __shared__ __align__(16) T Qs[CP * QP];
   __shared__ __align__(16) T Ks[CP * QP];
+  __shared__ __align__(16) T Kt[kBF16 ? DKP * KTP : 8];  // K^T for the state update (bf16)
   __shared__ __align__(16) T Vs[C * VP];
   __shared__ __align__(16) T Ts[C * TP];
   __shared__ __align__(16) T Ps[C * TP];
+  __shared__ __align__(16) T Os[4 * 16 * OP];
   __shared__ __align__(16) f32x4 Xy[NX];
   __shared__ __align__(16) f32x4 Xz[NX];
 
@@ -227,16 +267,16 @@ __global__ __launch_bounds__(kThreads) void recurrence_kernel(
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, g = lane >> 4;
   const int cw = w % NCT, pw = w / NCT;
   const int col = v0 + 16 * cw + li;  // this lane's value column
+  T* Ow = Os + w * 16 * OP;            // this wave's output staging tile
 
-  for (int i = tid; i < CP * QP; i += kThreads) {
-    Qs[i] = T(0);
-    Ks[i] = T(0);
+  // Zero what staging never writes: padding rows/columns and the upper part of P.
+  if constexpr (DK < DKP || C < CP) {
+    lds_zero(Qs, CP * QP, tid);
+    lds_zero(Ks, CP * QP, tid);
+    if constexpr (kBF16) lds_zero(Kt, DKP * KTP, tid);
   }
-  for (int i = tid; i < C * VP; i += kThreads) Vs[i] = T(0);
-  for (int i = tid; i < C * TP; i += kThreads) {
-    Ts[i] = T(0);
-    Ps[i] = T(0);
-  }
+  if constexpr (C < CP) lds_zero(Ts, C * TP, tid);
+  lds_zero(Ps, C * TP, tid);
 
   // S tiles: Sacc[j][hh] covers key dims 32*ku + 16*hh + (0..15), ku = pw + j*NDP.
   f32x4 Sacc[MAXO][2];
@@ -254,16 +294,36 @@ __global__ __launch_bounds__(kThreads) void recurrence_kernel(
   }
 
   const int64_t qk_stride = int64_t(H) * DK, v_stride = int64_t(H) * DV;
+  RowStager<T, C, DK> sq, sk;
+  RowStager<T, C, BV> sv;
+  RowStager<T, C, C> st;
+  auto load_chunk = [&](int n) {
+    const int64_t t0 = int64_t(n) * C;
+    const int valid = int(L - t0 < C ? L - t0 : C);
+    const int64_t row0 = (b * L + t0) * H + h;
+    sq.load(q + row0 * DK, qk_stride, valid, tid);
+    sk.load(k + row0 * DK, qk_stride, valid, tid);
+    sv.load(v + row0 * DV + v0, v_stride, valid, tid);
+    st.load(tws + (int64_t(bh) * NC + n) * C * C, C, C, tid);
+  };
+  auto store_chunk = [&]() {
+    sq.store(Qs, QP, tid);
+    sk.store(Ks, QP, tid);
+    if constexpr (kBF16) sk.store_t(Kt, KTP, tid);
+    sv.store(Vs, VP, tid);
+    st.store(Ts, TP, tid);
+  };
+
+  if (NC > 0) load_chunk(0);
+  __syncthreads();  // zero-fill done
+  if (NC > 0) store_chunk();
+  __syncthreads();
+
   for (int n = 0; n < NC; ++n) {
     const int64_t t0 = int64_t(n) * C;
     const int valid = int(L - t0 < C ? L - t0 : C);
     const int64_t row0 = (b * L + t0) * H + h;
-    __syncthreads();  // previous chunk's LDS reads are done
-    stage_rows<T, C, DK>(Qs, QP, q + row0 * DK, qk_stride, valid, tid);
-    stage_rows<T, C, DK>(Ks, QP, k + row0 * DK, qk_stride, valid, tid);
-    stage_rows<T, C, BV>(Vs, VP, v + row0 * DV + v0, v_stride, valid, tid);
-    stage_rows<T, C, C>(Ts, TP, tws + (int64_t(bh) * NC + n) * C * C, C, C, tid);
-    __syncthreads();
+    if (n + 1 < NC) load_chunk(n + 1);  // in flight during this chunk
 
     // partial K S and Q S over this wave's key dims
     f32x4 Y[NRT], Z[NRT];
@@ -312,13 +372,20 @@ __global__ __launch_bounds__(kThreads) void recurrence_kernel(
     }
     __syncthreads();
     if constexpr (NDP > 1) {
+      // Sum the partials in part order 0..NDP-1 (own part from registers), so
+      // every part of a value tile gets bitwise the same K S.
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) {
         f32x4 sy = zero4(), sz = zero4();
 #pragma unroll
         for (int p = 0; p < NDP; ++p) {
-          sy += Xy[((p * NRT + rt) * NCT + cw) * kWave + lane];
-          sz += Xz[((p * NRT + rt) * NCT + cw) * kWave + lane];
+          if (p == pw) {
+            sy += Y[rt];
+            sz += Z[rt];
+          } else {
+            sy += Xy[((p * NRT + rt) * NCT + cw) * kWave + lane];
+            if (rt % NDP == pw) sz += Xz[((p * NRT + rt) * NCT + cw) * kWave + lane];
+          }
         }
         Y[rt] = sy;
         Z[rt] = sz;
@@ -357,15 +424,21 @@ __global__ __launch_bounds__(kThreads) void recurrence_kernel(
           const int dt = 2 * ku + hh;
           if (16 * dt < DK) {
 #pragma unroll
-            for (int kt = 0; kt < NKU_C; ++kt)
-              mma(Sacc[j][hh], lds_frag_t(Ks, QP, 16 * dt + li, kt, g),
-                  acc_frag<T>(U[2 * kt], U[2 * kt + 1]));
+            for (int kt = 0; kt < NKU_C; ++kt) {
+              Frag<T> aK;
+              if constexpr (kBF16)
+                aK = lds_frag(Kt, KTP, 16 * dt + li, kt, g);
+              else
+                aK = lds_frag_t(Ks, QP, 16 * dt + li, kt, g);
+              mma(Sacc[j][hh], aK, acc_frag<T>(U[2 * kt], U[2 * kt + 1]));
+            }
           }
         }
       }
     }
 
-    // O = Q S + P U' for this wave's rows
+    // O = Q S + P U' for this wave's rows, staged through a wave-private LDS
+    // tile so that each row leaves as whole 16-byte stores.
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
       if (rt % NDP == pw) {
@@ -375,12 +448,21 @@ __global__ __launch_bounds__(kThreads) void recurrence_kernel(
           if (32 * ku <= 16 * rt + 15)
             mma(acc, lds_frag(Ps, TP, 16 * rt + li, ku, g), acc_frag<T>(U[2 * ku], U[2 * ku + 1]));
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const int t = 16 * rt + 4 * g + qq;
-          if (t < valid) o[(row0 + int64_t(t) * H) * DV + col] = from_f32<T>(acc[qq]);
+        for (int qq = 0; qq < 4; ++qq) Ow[(4 * g + qq) * OP + li] = from_f32<T>(acc[qq]);
+        constexpr int VN = Vec16<T>::n, VPRow = 16 / VN;  // vectors per 16-wide row
+        if (lane < 16 * VPRow) {
+          const int r = lane / VPRow, c = (lane % VPRow) * VN;
+          const int t = 16 * rt + r;
+          const u32x4 val = *reinterpret_cast<const u32x4*>(Ow + r * OP + c);
+          if (t < valid)
+            *reinterpret_cast<u32x4*>(o + (row0 + int64_t(t) * H) * DV + v0 + 16 * cw + c) = val;
         }
       }
     }
+
+    __syncthreads();  // every wave is done reading this chunk's LDS
+    if (n + 1 < NC) store_chunk();
+    __syncthreads();
   }
 
   if (sfin != nullptr) {
@@ -397,7 +479,6 @@ __global__ __launch_bounds__(kThreads) void recurrence_kernel(
     }
   }
 }
-
 
 template <typename T, int DK, int C>
 hipError_t ut_transform_launch_impl(const T* k, const T* beta, T* tws, int B, int H, int64_t L,

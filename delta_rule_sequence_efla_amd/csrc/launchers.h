@@ -24,4 +24,19 @@ hipError_t launch_recurrence(const T* q, const T* k, const T* v, const T* tws, c
                              T* o, float* sfin, int B, int H, int64_t L, int DK, int DV, int C,
                              int BV, hipStream_t stream);
 
+// bf16 recurrence with one wavefront per 16 value columns (recurrence_v3.h);
+// covers d_k in {32, 64, 128} and chunk in {32, 64}.
+bool recurrence_v3_supported(int DK, int C);
+hipError_t launch_recurrence_v3_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                     const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
+                                     int B, int H, int64_t L, int DK, int DV, int C, int BV,
+                                     hipStream_t s);
+
+// bf16 recurrence with DMA-fed LDS ring (recurrence_v4.h); same coverage.
+bool recurrence_v4_supported(int DK, int C, int BV);
+hipError_t launch_recurrence_v4_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                     const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
+                                     int B, int H, int64_t L, int DK, int DV, int C, int BV,
+                                     hipStream_t s);
+
 }  // namespace efla

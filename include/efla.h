@@ -28,7 +28,7 @@
  *     any L >= 0 (a ragged last chunk is handled); B, H >= 1 with B*H < 2^31.
  *   - stream is a hipStream_t passed as void* (NULL = default stream).  Calls are
  *     asynchronous: EFLA_OK means the work was enqueued.
- *   - q, k, v, the workspace and decode states must be 16-byte aligned (torch
+ *   - q, k, v, o (chunked), the workspace and decode states must be 16-byte aligned (torch
  *     allocations are); a misaligned pointer is EFLA_ERR_INVALID_ARG.
  *   - Errors: arguments are validated before anything is launched; on a
  *     validation error nothing is written.  A failed launch returns

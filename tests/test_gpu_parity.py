@@ -114,13 +114,16 @@ def test_tiny_fp32_workload():
     _check_forward(inp, w.chunk, "tiny_fp32")
 
 
+@pytest.mark.parametrize("impl", ["v4", "v3", "v2"])
 @pytest.mark.parametrize("bv", ["16", "32", "64"])
-def test_value_block_widths_agree(bv, monkeypatch):
-    """Every value-block width of the recurrence gives oracle parity; the
-    choice is a launch-shape detail, not a different computation."""
+@pytest.mark.parametrize("dk,chunk", [(128, 64), (64, 32), (32, 64)])
+def test_value_block_widths_agree(bv, impl, dk, chunk, monkeypatch):
+    """Every value-block width and both bf16 recurrence kernels give oracle
+    parity; these are launch-shape choices, not different computations."""
     monkeypatch.setenv("EFLA_VALUE_BLOCK", bv)
-    w, inp = _gen("shape_340m", B=2, H=4, L=200, seed=61)
-    _check_forward(inp, 64, f"value block {bv}")
+    monkeypatch.setenv("EFLA_RECURRENCE_IMPL", impl)
+    w, inp = _gen("shape_340m", B=2, H=4, L=200, dk=dk, dv=64, seed=61)
+    _check_forward(inp, chunk, f"{impl} value block {bv} dk {dk} C {chunk}")
 
 
 def test_unnormalised_bf16_stiff_small():
