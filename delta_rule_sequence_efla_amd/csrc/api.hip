@@ -31,19 +31,42 @@ efla_status check_chunk_shape(int B, int H, int64_t L, int d_k, int d_v, int chu
 }
 
 // Width of the value block one recurrence workgroup owns.  Wider blocks share
-// more of each chunk's K/Q/T staging and P = tril(Q K^T) per workgroup; narrower
-// blocks give more workgroups.  Take the widest block that still gives at least
-// one workgroup per compute unit (256 on MI355X).  EFLA_VALUE_BLOCK (16, 32 or
-// 64) overrides the choice for tuning; fp32 always uses 16.
-int choose_value_block(efla_dtype dt, int64_t bh, int d_v) {
+// each chunk's K/Q/T staging and P = tril(Q K^T) over more value columns.
+// EFLA_VALUE_BLOCK (16, 32 or 64) overrides the choice for tuning; fp32 always
+// uses 16.
+int choose_value_block(efla_dtype dt, int d_v) {
   if (dt == EFLA_F32) return 16;
   if (const char* env = getenv("EFLA_VALUE_BLOCK")) {
     const int bv = atoi(env);
     if ((bv == 16 || bv == 32 || bv == 64) && bv <= d_v) return bv;
   }
-  for (int bv : {64, 32})
-    if (bv <= d_v && bh * (d_v / bv) >= 256) return bv;
-  return 16;
+  // Every 16 value columns of a (b, h) form one sequential chain whatever the
+  // block width, so a wider block costs no parallelism; 32 columns is the
+  // width of the paired-wavefront kernel.
+  return d_v >= 32 ? 32 : 16;
+}
+
+// Which recurrence kernel runs for given sizes.  bf16: the paired-wavefront
+// kernel (recurrence_v5.h) where it applies, else one wavefront per tile with
+// the DMA-fed ring (recurrence_v4.h), else the register-staged one
+// (recurrence_v3.h), else the generic kernel; fp32 always takes the generic
+// kernel.  EFLA_RECURRENCE_IMPL=v2|v3|v4 pins an older kernel for comparisons
+// (falling through where it does not apply).
+enum class Rec { kGeneric, kV3, kV4, kV5 };
+struct RecChoice {
+  Rec kind;
+  int bv;
+};
+RecChoice choose_recurrence(efla_dtype dt, int d_k, int d_v, int chunk) {
+  const int bv = choose_value_block(dt, d_v);
+  if (dt != EFLA_BF16) return {Rec::kGeneric, bv};
+  const char* impl = getenv("EFLA_RECURRENCE_IMPL");
+  const bool v2 = impl && strcmp(impl, "v2") == 0, v3 = impl && strcmp(impl, "v3") == 0;
+  const bool v4 = impl && strcmp(impl, "v4") == 0;
+  if (!v2 && !v3 && !v4 && efla::recurrence_v5_supported(d_k, chunk, bv)) return {Rec::kV5, bv};
+  if (!v2 && !v3 && efla::recurrence_v4_supported(d_k, chunk, bv)) return {Rec::kV4, bv};
+  if (!v2 && efla::recurrence_v3_supported(d_k, chunk)) return {Rec::kV3, bv};
+  return {Rec::kGeneric, bv};
 }
 
 }  // namespace
@@ -120,34 +143,45 @@ efla_status efla_chunk_recurrence(const void* q, const void* k, const void* v, c
     if (!aligned16(workspace)) return EFLA_ERR_INVALID_ARG;
   }
   if (L == 0 && s_final == nullptr) return EFLA_OK;
-  const int64_t bh = int64_t(B) * H;
-  const int bv = choose_value_block(dtype, bh, d_v);
+  const RecChoice rc = choose_recurrence(dtype, d_k, d_v, chunk);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == EFLA_BF16) {
-    // Kernel choice: v4 (DMA-fed ring) where it applies, else v3, else the
-    // generic kernel.  EFLA_RECURRENCE_IMPL=v2|v3|v4 pins one for comparisons.
-    const char* impl = getenv("EFLA_RECURRENCE_IMPL");
-    const bool want_v2 = impl && strcmp(impl, "v2") == 0, want_v3 = impl && strcmp(impl, "v3") == 0;
-    if (!want_v2 && !want_v3 && efla::recurrence_v4_supported(d_k, chunk, bv))
-      return from_hip(efla::launch_recurrence_v4_bf16(
-          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-          static_cast<const uint16_t*>(workspace), s0, static_cast<uint16_t*>(o), s_final, B, H, L, d_k,
-          d_v, chunk, bv, s));
-    const bool use_v3 = efla::recurrence_v3_supported(d_k, chunk) && !want_v2;
-    if (use_v3)
-      return from_hip(efla::launch_recurrence_v3_bf16(
-          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-          static_cast<const uint16_t*>(workspace), s0, static_cast<uint16_t*>(o), s_final, B, H, L, d_k,
-          d_v, chunk, bv, s));
-    return from_hip(efla::launch_recurrence<uint16_t>(
-        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-        static_cast<const uint16_t*>(workspace), s0, static_cast<uint16_t*>(o), s_final, B, H, L, d_k,
-        d_v, chunk, bv, s));
+    const auto* qb = static_cast<const uint16_t*>(q);
+    const auto* kb = static_cast<const uint16_t*>(k);
+    const auto* vb = static_cast<const uint16_t*>(v);
+    const auto* tb = static_cast<const uint16_t*>(workspace);
+    auto* ob = static_cast<uint16_t*>(o);
+    switch (rc.kind) {
+      case Rec::kV5:
+        return from_hip(efla::launch_recurrence_v5_bf16(qb, kb, vb, tb, s0, ob, s_final, B, H, L, d_k, d_v,
+                                                        chunk, rc.bv, s));
+      case Rec::kV4:
+        return from_hip(efla::launch_recurrence_v4_bf16(qb, kb, vb, tb, s0, ob, s_final, B, H, L, d_k, d_v,
+                                                        chunk, rc.bv, s));
+      case Rec::kV3:
+        return from_hip(efla::launch_recurrence_v3_bf16(qb, kb, vb, tb, s0, ob, s_final, B, H, L, d_k, d_v,
+                                                        chunk, rc.bv, s));
+      case Rec::kGeneric:
+        break;
+    }
+    return from_hip(efla::launch_recurrence<uint16_t>(qb, kb, vb, tb, s0, ob, s_final, B, H, L, d_k, d_v,
+                                                      chunk, rc.bv, s));
   }
   return from_hip(efla::launch_recurrence<float>(
       static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
       static_cast<const float*>(workspace), s0, static_cast<float*>(o), s_final, B, H, L, d_k, d_v, chunk,
-      bv, s));
+      rc.bv, s));
+}
+
+const char* efla_chunk_recurrence_kernel(int d_k, int d_v, int chunk, efla_dtype dtype) {
+  if (!valid_dtype(dtype) || !valid_dim(d_k) || !valid_dim(d_v) || !valid_chunk(chunk)) return "unsupported";
+  switch (choose_recurrence(dtype, d_k, d_v, chunk).kind) {
+    case Rec::kV5: return "recurrence_v5_kernel";
+    case Rec::kV4: return "recurrence_v4_kernel";
+    case Rec::kV3: return "recurrence_v3_kernel";
+    case Rec::kGeneric: break;
+  }
+  return "recurrence_kernel";
 }
 
 efla_status efla_chunk_fwd(const void* q, const void* k, const void* v, const void* beta, const float* s0,

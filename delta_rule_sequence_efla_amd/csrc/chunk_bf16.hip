@@ -2,6 +2,7 @@
 #include "chunk_kernels.h"
 #include "recurrence_v3.h"
 #include "recurrence_v4.h"
+#include "recurrence_v5.h"
 
 namespace efla {
 template hipError_t launch_ut_transform<uint16_t>(const uint16_t*, const uint16_t*, uint16_t*, int, int,
@@ -25,5 +26,12 @@ hipError_t launch_recurrence_v4_bf16(const uint16_t* q, const uint16_t* k, const
                                      int B, int H, int64_t L, int DK, int DV, int C, int BV,
                                      hipStream_t s) {
   return launch_recurrence_v4(q, k, v, tws, s0, o, sfin, B, H, L, DK, DV, C, BV, s);
+}
+bool recurrence_v5_supported(int DK, int C, int BV) { return v5_supported(DK, C, BV); }
+hipError_t launch_recurrence_v5_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                     const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
+                                     int B, int H, int64_t L, int DK, int DV, int C, int BV,
+                                     hipStream_t s) {
+  return launch_recurrence_v5(q, k, v, tws, s0, o, sfin, B, H, L, DK, DV, C, BV, s);
 }
 }  // namespace efla

@@ -45,6 +45,8 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         L.efla_status_string.restype = ctypes.c_char_p
         L.efla_status_string.argtypes = [_i]
+        L.efla_chunk_recurrence_kernel.restype = ctypes.c_char_p
+        L.efla_chunk_recurrence_kernel.argtypes = [_i, _i, _i, _i]
         L.efla_coeff.restype = _i
         L.efla_coeff.argtypes = [_vp, _vp, _vp, _vp, _i64, _i, _i, _vp]
         L.efla_chunk_fwd_workspace_size.restype = _sz
@@ -68,6 +70,11 @@ def efla_status_string(status: int) -> str:
         return lib().efla_status_string(int(status)).decode()
     except RuntimeError:
         return _STATUS.get(int(status), f"status {status}")
+
+
+def efla_chunk_recurrence_kernel(d_k: int, d_v: int, chunk: int, dtype) -> str:
+    """Base name of the recurrence kernel the library launches for these sizes."""
+    return lib().efla_chunk_recurrence_kernel(int(d_k), int(d_v), int(chunk), _code(dtype)).decode()
 
 
 def _check(status: int, where: str) -> None:

@@ -62,6 +62,15 @@ typedef enum efla_dtype {
 const char *efla_status_string(efla_status s);
 
 /*
+ * Base name of the GPU kernel that efla_chunk_recurrence (and the second
+ * stage of efla_chunk_fwd) launches for these sizes, as a profiler lists it
+ * (e.g. "recurrence_v5_kernel"); "unsupported" for sizes outside the
+ * supported set.  Static string, never NULL; launches nothing.  For profiling
+ * and roofline accounting only.
+ */
+const char *efla_chunk_recurrence_kernel(int d_k, int d_v, int chunk, efla_dtype dtype);
+
+/*
  * efla_coeff -- the coefficient of Method step 3 for n_tok key rows.
  *   k      [n_tok, d_k] (dtype), beta [n_tok] (dtype)
  *   lambda [n_tok] float32 out, may be NULL: lambda_t = ||k_t||^2

@@ -40,6 +40,18 @@ def test_status_strings():
     assert efla.efla_status_string(99) == "EFLA_ERR_UNKNOWN"
 
 
+def test_recurrence_kernel_names():
+    """The kernel-name query follows the dispatch rule and launches nothing."""
+    import torch
+    name = efla.efla_chunk_recurrence_kernel
+    assert name(128, 128, 64, torch.bfloat16) == "recurrence_v5_kernel"
+    assert name(128, 16, 64, torch.bfloat16) == "recurrence_v4_kernel"   # one 16-column tile
+    assert name(16, 64, 16, torch.bfloat16) == "recurrence_kernel"       # d_k 16, chunk 16
+    assert name(128, 128, 64, torch.float32) == "recurrence_kernel"
+    assert name(48, 128, 64, torch.bfloat16) == "unsupported"
+    assert name(128, 128, 128, torch.bfloat16) == "unsupported"
+
+
 def test_workspace_size():
     f = efla.efla_chunk_fwd_workspace_size
     # 1.3B-shaped layer: 4*16 sequences x 64 chunks x 64x64 bf16

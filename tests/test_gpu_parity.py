@@ -114,12 +114,13 @@ def test_tiny_fp32_workload():
     _check_forward(inp, w.chunk, "tiny_fp32")
 
 
-@pytest.mark.parametrize("impl", ["v4", "v3", "v2"])
+@pytest.mark.parametrize("impl", ["v5", "v4", "v3", "v2"])
 @pytest.mark.parametrize("bv", ["16", "32", "64"])
 @pytest.mark.parametrize("dk,chunk", [(128, 64), (64, 32), (32, 64)])
 def test_value_block_widths_agree(bv, impl, dk, chunk, monkeypatch):
-    """Every value-block width and both bf16 recurrence kernels give oracle
-    parity; these are launch-shape choices, not different computations."""
+    """Every value-block width and every bf16 recurrence kernel give oracle
+    parity; these are launch-shape choices, not different computations (a
+    pinned kernel that does not take a width falls through to the next one)."""
     monkeypatch.setenv("EFLA_VALUE_BLOCK", bv)
     monkeypatch.setenv("EFLA_RECURRENCE_IMPL", impl)
     w, inp = _gen("shape_340m", B=2, H=4, L=200, dk=dk, dv=64, seed=61)
