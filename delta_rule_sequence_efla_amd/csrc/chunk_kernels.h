@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void ut_transform_kernel(const T* __restr
   const int chunk = int(wg % NC);
   const int64_t bh = wg / NC;
   const int64_t b = bh / H, h = bh % H;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), li = lane & 15, g = lane >> 4;
   const int64_t t0 = int64_t(chunk) * C;
   const int valid = int(L - t0 < C ? L - t0 : C);
   const int64_t row0 = (b * L + t0) * H + h;  // token t0 of this (b, h)
@@ -264,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void recurrence_kernel(
   }
   const int64_t b = bh / H, h = bh % H;
   const int v0 = vb * BV;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), li = lane & 15, g = lane >> 4;
   const int cw = w % NCT, pw = w / NCT;
   const int col = v0 + 16 * cw + li;  // this lane's value column
   T* Ow = Os + w * 16 * OP;            // this wave's output staging tile

@@ -31,6 +31,11 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 constexpr int kThreads = 256;  // four wavefronts per workgroup
 
+// Index of this wavefront in its workgroup, as a wave-uniform (scalar) value:
+// branches on it are scalar branches, and addresses derived from it stay in
+// scalar registers, where threadIdx.x / 64 would look lane-dependent.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6); }
+
 __host__ __device__ constexpr int round_up(int x, int m) { return (x + m - 1) / m * m; }
 __host__ __device__ constexpr int cdiv(int x, int m) { return (x + m - 1) / m; }
 

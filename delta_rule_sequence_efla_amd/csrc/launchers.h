@@ -40,9 +40,17 @@ hipError_t launch_recurrence_v4_bf16(const uint16_t* q, const uint16_t* k, const
                                      hipStream_t s);
 
 // bf16 recurrence with chain / output wavefront pairs (recurrence_v5.h);
-// value blocks of 16 or 32 columns.
+// value blocks of 32 columns.
 bool recurrence_v5_supported(int DK, int C, int BV);
 hipError_t launch_recurrence_v5_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                     const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
+                                     int B, int H, int64_t L, int DK, int DV, int C, int BV,
+                                     hipStream_t s);
+
+// bf16 recurrence with one role per wavefront: chain, output, P, DMA
+// (recurrence_v6.h); value blocks of 16 or 32 columns.
+bool recurrence_v6_supported(int DK, int C, int BV);
+hipError_t launch_recurrence_v6_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                      const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
                                      int B, int H, int64_t L, int DK, int DV, int C, int BV,
                                      hipStream_t s);

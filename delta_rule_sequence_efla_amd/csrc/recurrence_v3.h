@@ -133,7 +133,7 @@ __global__ __launch_bounds__(4 * BV) void recurrence_v3_kernel(  // 4*BV = (BV/1
   }
   const int64_t b = bh / H, h = bh % H;
   const int v0 = vb * BV;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), li = lane & 15, g = lane >> 4;
   const int col = v0 + 16 * w + li;
   uint16_t* Ow = Os + w * 16 * OP;
 

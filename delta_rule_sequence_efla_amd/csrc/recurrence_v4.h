@@ -261,7 +261,7 @@ __global__ __launch_bounds__(4 * BV) void recurrence_v4_kernel(
   }
   const int64_t b = bh / H, h = bh % H;
   const int v0 = vb * BV;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), li = lane & 15, g = lane >> 4;
   const int col = v0 + 16 * w + li;
 
   const int64_t qk_stride = int64_t(H) * DK, v_stride = int64_t(H) * DV;

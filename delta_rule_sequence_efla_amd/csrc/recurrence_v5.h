@@ -73,7 +73,7 @@ __global__ __launch_bounds__(8 * BV) void recurrence_v5_kernel(
   }
   const int64_t b = bh / H, h = bh % H;
   const int v0 = vb * BV;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), li = lane & 15, g = lane >> 4;
   const bool chain = w < NT;
   const int tile = chain ? w : w - NT;  // value tile of this wave
   const int col = v0 + 16 * tile + li;
