@@ -26,9 +26,15 @@ CFLAGS = [
 ]
 
 
+# Per-source flags.  The one-role-per-wavefront recurrence keeps its matrix-core
+# accumulators in ordinary VGPRs, so results feed the bf16 conversions that
+# follow every product without a copy out of the accumulation registers.
+SOURCE_FLAGS = {"chunk_bf16_v6.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

@@ -57,6 +57,43 @@ __device__ __forceinline__ int swz_chunk(int r, int c) {
   return c ^ swz_lane<NCH>(r % RPI) ^ swz_instr<NCH>(r / RPI);
 }
 
+// A second swizzle, for tiles read with 16-byte row fragments (16 rows, one
+// 16-byte chunk each) and with transposing reads of 4 rows x 4 consecutive
+// chunks (8 bytes of each): s(r) = f(r % RPI) ^ g(r / RPI) with
+//   16 chunks per row: s = 4 (r & 3) ^ ((r >> 2) & 3)
+//    8 chunks per row: s = 4 ((r >> 1) & 1) ^ ((r >> 2) & 1) ^ 2 ((r >> 3) & 1)
+//    4 chunks per row: s = (r >> 2) & 3
+// Any 16 consecutive (16-aligned) rows then land on distinct bank groups, and
+// so do the 16 (row, chunk) pairs of a transposing read.
+template <int NCH>
+__device__ __forceinline__ int swzw_lane(int rr) {  // rr = r % RPI
+  if constexpr (NCH >= 16) return 4 * (rr & 3);
+  else if constexpr (NCH == 8) return 4 * ((rr >> 1) & 1) + ((rr >> 2) & 1);
+  else if constexpr (NCH == 4) return (rr >> 2) & 3;
+  else return 0;
+}
+template <int NCH>
+__device__ __forceinline__ int swzw_instr(int b) {  // b = r / RPI
+  if constexpr (NCH >= 16) return b & 3;
+  else if constexpr (NCH == 8) return 2 * (b & 1);
+  else return 0;
+}
+template <int NCH, bool WIDE>
+__device__ __forceinline__ int swz_lane_of(int rr) {
+  if constexpr (WIDE) return swzw_lane<NCH>(rr);
+  else return swz_lane<NCH>(rr);
+}
+template <int NCH, bool WIDE>
+__device__ __forceinline__ int swz_instr_of(int b) {
+  if constexpr (WIDE) return swzw_instr<NCH>(b);
+  else return swz_instr<NCH>(b);
+}
+template <int ROWE>
+__device__ __forceinline__ int swzw_off(int r, int col) {
+  constexpr int NCH = ROWE / 8, RPI = 64 / NCH;
+  return r * ROWE + (((col >> 3) ^ swzw_lane<NCH>(r % RPI) ^ swzw_instr<NCH>(r / RPI)) * 8) + (col & 7);
+}
+
 // Element offset of (r, col) in a swizzled bf16 tile with ROWE elements per row.
 template <int ROWE>
 __device__ __forceinline__ int swz_off(int r, int col) {
@@ -130,7 +167,7 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
 // computes, once, each lane's byte offset for every instruction of a full
 // tile; a ragged tile (rows at or past `valid` re-read row 0) takes the
 // slower per-instruction path.
-template <int ROWS, int ROWE, int NW>
+template <int ROWS, int ROWE, int NW, bool WIDE = false>
 struct DmaTile {
   static constexpr int BYTES = ROWS * ROWE * 2, NINSTR = BYTES / 1024, PER_WAVE = cdiv(NINSTR, NW);
   static constexpr int NCH = ROWE / 8, RPI = 64 / NCH;
@@ -145,11 +182,12 @@ struct DmaTile {
   __device__ __forceinline__ void init(int64_t stride, int lane, int wave) {
     w = __builtin_amdgcn_readfirstlane(wave);  // uniform: LDS addresses stay scalar
     lrow = lane / NCH;
-    off_chunk = 16u * uint32_t((lane % NCH) ^ swz_lane<NCH>(lrow));
+    off_chunk = 16u * uint32_t((lane % NCH) ^ swz_lane_of<NCH, WIDE>(lrow));
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int ins = instr(w, i);
-      off[i] = uint32_t((RPI * ins + lrow) * stride * 2) + (off_chunk ^ (16u * uint32_t(swz_instr<NCH>(ins))));
+      off[i] = uint32_t((RPI * ins + lrow) * stride * 2) +
+               (off_chunk ^ (16u * uint32_t(swz_instr_of<NCH, WIDE>(ins))));
     }
   }
   // Instruction i of this wave for the tile at LDS byte address lds_tile
@@ -160,16 +198,17 @@ struct DmaTile {
     const int ins = instr(w, i);
     uint32_t voff = off[i];
     if constexpr (RAGGED) {
-      const uint32_t xo = 16u * uint32_t(swz_instr<NCH>(ins));
+      const uint32_t xo = 16u * uint32_t(swz_instr_of<NCH, WIDE>(ins));
       voff = (RPI * ins + lrow < valid) ? voff : (off_chunk ^ xo);
     }
     dma16(src, voff, lds_tile + uint32_t(ins) * 1024u);
   }
 };
 
-template <int DK, int C, int BV, int NW>
+// WIDE_QK selects the 16-byte-fragment swizzle for the Q and K tiles.
+template <int DK, int C, int BV, int NW, bool WIDE_QK = false>
 struct ChunkDma {
-  using TQ = DmaTile<C, DK, NW>;
+  using TQ = DmaTile<C, DK, NW, WIDE_QK>;
   using TT = DmaTile<C, C, NW>;
   using TV = DmaTile<C, BV, NW>;
   static constexpr int PQ = TQ::PER_WAVE, PT = TT::PER_WAVE, PV = TV::PER_WAVE;

@@ -23,11 +23,50 @@
 //     chain: S update -> publish S | output: O^T, store |             | DMA: other half
 // The chain's products (about 2 * 38 per 16 columns and chunk) are the
 // critical path; everything else runs beside them.
+//
+// Key-dimension order.  The sum over the key dimension in K S, Q S and
+// Q K^T does not depend on the order in which the k slots of the matrix-core
+// fragments visit the key dims, as long as every operand uses the same one.
+// Here logical dim 32 ku + 16 h + 4 g + q (the slot that accumulator rows
+// 4g..4g+3 of a state tile feed) is physical dim 32 ku + 8 g + 4 h + q, so a
+// lane's eight elements of a Q or K row fragment are contiguous: one 16-byte
+// LDS read instead of two 8-byte ones.  The state tile rows are logical dims;
+// only the initial-state load and the final-state store map them back.
 #pragma once
 
 #include "recurrence_v5.h"
 
 namespace efla {
+
+// Physical key dim of logical key dim l (see above).
+__host__ __device__ constexpr int key_phys(int l) {
+  return 32 * (l / 32) + 8 * ((l % 16) / 4) + 4 * ((l % 32) / 16) + l % 4;
+}
+
+// Row fragment of a Q/K tile in the 16-byte layout: lane (li, g) holds
+// physical columns 32 ku + 8 g .. + 7 of row `row`.
+template <int ROWE>
+__device__ __forceinline__ Frag<uint16_t> wide_frag(const uint16_t* X, int row, int ku, int g) {
+  Frag<uint16_t> f;
+  f.v = *reinterpret_cast<const bf16x8*>(X + swzw_off<ROWE>(row, 32 * ku + 8 * g));
+  return f;
+}
+
+// K^T fragment for state rows dt (logical key dims 16 dt + i), tokens of
+// k-unit kt: the transposing read returns, in lane i of each 16-lane group,
+// column base(i / 4) + i % 4 of four rows, and base(m) = key_phys(16 dt + 4 m)
+// = 32 (dt / 2) + 4 (dt % 2) + 8 m puts logical dim 16 dt + i there.
+template <int ROWE>
+__device__ __forceinline__ Frag<uint16_t> wide_frag_tr(const uint16_t* X, int dt, int kt, int lane) {
+  const int j = lane & 15, g = lane >> 4;
+  const int r = 32 * kt + 4 * g + (j >> 2);
+  const int c = 32 * (dt >> 1) + 4 * (dt & 1) + 8 * (j & 3);
+  const bf16x4 lo = lds_read_tr(X + swzw_off<ROWE>(r, c));
+  const bf16x4 hi = lds_read_tr(X + swzw_off<ROWE>(r + 16, c));
+  Frag<uint16_t> f;
+  f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return f;
+}
 
 template <int DK, int C, int BV>
 struct V6Shape {
@@ -37,7 +76,7 @@ struct V6Shape {
   static constexpr int QOFF = 0, KOFF = C * DK, TOFF = 2 * C * DK, VOFF = 2 * C * DK + C * C;
   static constexpr int SLOT = 2 * C * DK + C * C + C * BV;
   static constexpr int NPF = (NRT == 4) ? 6 : 2;  // P fragments (rt, ku) with 32 ku <= 16 rt + 15
-  using Dma = ChunkDma<DK, C, BV, 1>;             // every transfer from the DMA wave
+  using Dma = ChunkDma<DK, C, BV, 1, true>;       // every transfer from the DMA wave
   static constexpr int DMA_COUNT = Dma::COUNT;
   enum Role { kChain = 0, kOut = 1, kP = 2, kDma = 3 };
 };
@@ -111,7 +150,7 @@ __global__ __launch_bounds__(256) void recurrence_v6_kernel(
     wait_vmcnt<0>();
   } else if (role == S::kChain) {
     // -------------------------------------------------------------- chain
-    // St[ct][dt][qq] = S[16 dt + 4 g + qq][v0 + 16 ct + li]
+    // St[ct][dt][qq] = S[key_phys(16 dt + 4 g + qq)][v0 + 16 ct + li]
     f32x4 St[NT][NDT];
     Frag<uint16_t> bS[NT][NKU_D];
 #pragma unroll
@@ -121,7 +160,8 @@ __global__ __launch_bounds__(256) void recurrence_v6_kernel(
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq)
-          St[ct][dt][qq] = s0 != nullptr ? s0[(int64_t(bh) * DK + 16 * dt + 4 * g + qq) * DV + col] : 0.0f;
+          St[ct][dt][qq] =
+              s0 != nullptr ? s0[(int64_t(bh) * DK + key_phys(16 * dt + 4 * g + qq)) * DV + col] : 0.0f;
 #pragma unroll
       for (int ku = 0; ku < NKU_D; ++ku) {
         bS[ct][ku] = acc_frag<uint16_t>(St[ct][2 * ku], St[ct][2 * ku + 1]);
@@ -158,7 +198,7 @@ __global__ __launch_bounds__(256) void recurrence_v6_kernel(
       for (int ku = 0; ku < NKU_D; ++ku) {
         Frag<uint16_t> Kf[NRT];
 #pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) Kf[rt] = sw_frag<DK>(Ks, 16 * rt + li, ku, g);
+        for (int rt = 0; rt < NRT; ++rt) Kf[rt] = wide_frag<DK>(Ks, 16 * rt + li, ku, g);
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
@@ -198,14 +238,14 @@ __global__ __launch_bounds__(256) void recurrence_v6_kernel(
 #pragma unroll
       for (int dt = 0; dt < NH; ++dt)
 #pragma unroll
-        for (int kt = 0; kt < NKU_C; ++kt) KTa[dt][kt] = sw_frag_tr<DK>(Ks, 16 * dt, kt, lane);
+        for (int kt = 0; kt < NKU_C; ++kt) KTa[dt][kt] = wide_frag_tr<DK>(Ks, dt, kt, lane);
       sync();  // B
       // S += K^T U', then publish S_{n+1}
       Frag<uint16_t> KTb[NDT - NH > 0 ? NDT - NH : 1][NKU_C];
 #pragma unroll
       for (int dt = NH; dt < NDT; ++dt)
 #pragma unroll
-        for (int kt = 0; kt < NKU_C; ++kt) KTb[dt - NH][kt] = sw_frag_tr<DK>(Ks, 16 * dt, kt, lane);
+        for (int kt = 0; kt < NKU_C; ++kt) KTb[dt - NH][kt] = wide_frag_tr<DK>(Ks, dt, kt, lane);
 #pragma unroll
       for (int dt = 0; dt < NH; ++dt)
 #pragma unroll
@@ -238,7 +278,7 @@ __global__ __launch_bounds__(256) void recurrence_v6_kernel(
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
           for (int qq = 0; qq < 4; ++qq)
-            sfin[(int64_t(bh) * DK + 16 * dt + 4 * g + qq) * DV + v0 + 16 * ct + li] = St[ct][dt][qq];
+            sfin[(int64_t(bh) * DK + key_phys(16 * dt + 4 * g + qq)) * DV + v0 + 16 * ct + li] = St[ct][dt][qq];
     }
   } else if (role == S::kOut) {
     // ------------------------------------------------------------- output
@@ -257,7 +297,7 @@ __global__ __launch_bounds__(256) void recurrence_v6_kernel(
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) bSo[ct].v = bS_buf[ct][ku][lane];
 #pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) Qf[rt] = sw_frag<DK>(Qs, 16 * rt + li, ku, g);
+        for (int rt = 0; rt < NRT; ++rt) Qf[rt] = wide_frag<DK>(Qs, 16 * rt + li, ku, g);
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
@@ -312,8 +352,8 @@ __global__ __launch_bounds__(256) void recurrence_v6_kernel(
         Frag<uint16_t> Qf[NRT], Kf[NRT];
 #pragma unroll
         for (int r = 0; r < NRT; ++r) {
-          Qf[r] = sw_frag<DK>(Qs, 16 * r + li, ku, g);
-          Kf[r] = sw_frag<DK>(Ks, 16 * r + li, ku, g);
+          Qf[r] = wide_frag<DK>(Qs, 16 * r + li, ku, g);
+          Kf[r] = wide_frag<DK>(Ks, 16 * r + li, ku, g);
         }
 #pragma unroll
         for (int r = 0; r < NRT; ++r)
