@@ -46,13 +46,13 @@ int choose_value_block(efla_dtype dt, int d_v) {
   return d_v >= 32 ? 32 : 16;
 }
 
-// Which recurrence kernel runs for given sizes.  bf16: the one-role-per-
-// wavefront kernel (recurrence_v6.h) where it applies, else one wavefront per
-// tile with the DMA-fed ring (recurrence_v4.h), else the register-staged one
-// (recurrence_v3.h), else the generic kernel; fp32 always takes the generic
-// kernel.  EFLA_RECURRENCE_IMPL=v2|v3|v4|v5 pins an older kernel for
-// comparisons (falling through where it does not apply).
-enum class Rec { kGeneric, kV3, kV4, kV5, kV6 };
+// Which recurrence kernel runs for given sizes.  bf16: one role per wavefront
+// with one chain wavefront per state tile (recurrence_v7.h) where it applies,
+// else one wavefront per tile with the DMA-fed ring (recurrence_v4.h), else
+// the register-staged one (recurrence_v3.h), else the generic kernel; fp32
+// always takes the generic kernel.  EFLA_RECURRENCE_IMPL=v2|v3|v4|v5|v6 pins
+// an older kernel for comparisons (falling through where it does not apply).
+enum class Rec { kGeneric, kV3, kV4, kV5, kV6, kV7 };
 struct RecChoice {
   Rec kind;
   int bv;
@@ -63,6 +63,8 @@ RecChoice choose_recurrence(efla_dtype dt, int d_k, int d_v, int chunk) {
   const char* impl = getenv("EFLA_RECURRENCE_IMPL");
   const bool v2 = impl && strcmp(impl, "v2") == 0, v3 = impl && strcmp(impl, "v3") == 0;
   const bool v4 = impl && strcmp(impl, "v4") == 0, v5 = impl && strcmp(impl, "v5") == 0;
+  const bool v6 = impl && strcmp(impl, "v6") == 0;
+  if (!v2 && !v3 && !v4 && !v5 && !v6 && efla::recurrence_v7_supported(d_k, chunk, bv)) return {Rec::kV7, bv};
   if (!v2 && !v3 && !v4 && !v5 && efla::recurrence_v6_supported(d_k, chunk, bv)) return {Rec::kV6, bv};
   if (!v2 && !v3 && !v4 && efla::recurrence_v5_supported(d_k, chunk, bv)) return {Rec::kV5, bv};
   if (!v2 && !v3 && efla::recurrence_v4_supported(d_k, chunk, bv)) return {Rec::kV4, bv};
@@ -153,6 +155,9 @@ efla_status efla_chunk_recurrence(const void* q, const void* k, const void* v, c
     const auto* tb = static_cast<const uint16_t*>(workspace);
     auto* ob = static_cast<uint16_t*>(o);
     switch (rc.kind) {
+      case Rec::kV7:
+        return from_hip(efla::launch_recurrence_v7_bf16(qb, kb, vb, tb, s0, ob, s_final, B, H, L, d_k, d_v,
+                                                        chunk, rc.bv, s));
       case Rec::kV6:
         return from_hip(efla::launch_recurrence_v6_bf16(qb, kb, vb, tb, s0, ob, s_final, B, H, L, d_k, d_v,
                                                         chunk, rc.bv, s));
@@ -180,6 +185,7 @@ efla_status efla_chunk_recurrence(const void* q, const void* k, const void* v, c
 const char* efla_chunk_recurrence_kernel(int d_k, int d_v, int chunk, efla_dtype dtype) {
   if (!valid_dtype(dtype) || !valid_dim(d_k) || !valid_dim(d_v) || !valid_chunk(chunk)) return "unsupported";
   switch (choose_recurrence(dtype, d_k, d_v, chunk).kind) {
+    case Rec::kV7: return "recurrence_v7_kernel";
     case Rec::kV6: return "recurrence_v6_kernel";
     case Rec::kV5: return "recurrence_v5_kernel";
     case Rec::kV4: return "recurrence_v4_kernel";

@@ -55,4 +55,12 @@ hipError_t launch_recurrence_v6_bf16(const uint16_t* q, const uint16_t* k, const
                                      int B, int H, int64_t L, int DK, int DV, int C, int BV,
                                      hipStream_t s);
 
+// bf16 recurrence with one role per wavefront and one chain wavefront per
+// 16-column state tile (recurrence_v7.h); value blocks of 16 or 32 columns.
+bool recurrence_v7_supported(int DK, int C, int BV);
+hipError_t launch_recurrence_v7_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                     const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
+                                     int B, int H, int64_t L, int DK, int DV, int C, int BV,
+                                     hipStream_t s);
+
 }  // namespace efla

@@ -1,0 +1,369 @@
+// recurrence_v7.h -- the sequential chunk pass for bf16 inputs with one role
+// per wavefront and one chain wavefront per 16-column state tile.
+//
+// Same roles and data movement as recurrence_v6.h (chain, output, P, DMA;
+// three-slot LDS ring fed by global_load_lds_dwordx4; 16-byte Q/K fragments
+// under the key-dimension relabeling), but the state of a workgroup's BV
+// columns is split over BV/16 chain wavefronts of 16 columns each.  A
+// chain's products per chunk (K S, T (V - K S), K^T U': 38 matrix-core ops
+// per tile) then run on separate SIMDs, which halves the critical path of a
+// 32-column block.  Wavefronts: P, chain 0 .. BV/16-1, output, DMA (five for
+// BV = 32; the DMA wave, which mostly waits, shares a SIMD with the P wave).
+// Two barriers per chunk:
+//   A (chunk n in LDS, S_n fragments published)
+//     chains: Y, U' -> publish U'   | output: Z^T        | P: P -> publish | DMA: half of chunk n+2
+//   B (U' and P published)
+//     chains: S update -> publish S | output: O^T, store |                 | DMA: other half
+#pragma once
+
+#include "recurrence_v6.h"
+
+namespace efla {
+
+template <int DK, int C, int BV>
+struct V7Shape {
+  static constexpr int NT = BV / 16;  // state tiles of the workgroup = chain wavefronts
+  static constexpr int NWAVES = NT + 3, THREADS = NWAVES * kWave;
+  static constexpr int NRT = C / 16, NDT = DK / 16, NKU_D = DK / 32, NKU_C = C / 32;
+  static constexpr int QOFF = 0, KOFF = C * DK, TOFF = 2 * C * DK, VOFF = 2 * C * DK + C * C;
+  static constexpr int SLOT = 2 * C * DK + C * C + C * BV;
+  static constexpr int NPF = (NRT == 4) ? 6 : 2;  // P fragments (rt, ku) with 32 ku <= 16 rt + 15
+  using Dma = ChunkDma<DK, C, BV, 1, true>;       // every transfer from the DMA wave
+  static constexpr int DMA_COUNT = Dma::COUNT;
+  // wave 0 is the P wave, waves 1..NT the chains, then output and DMA
+  static constexpr int kP = 0, kChain0 = 1, kOut = NT + 1, kDma = NT + 2;
+};
+
+template <int DK, int C, int BV>
+__global__ __launch_bounds__(64 * (BV / 16 + 3)) void recurrence_v7_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ tws, const float* __restrict__ s0, uint16_t* __restrict__ o,
+    float* __restrict__ sfin, int H, int64_t L, int NC, int DV, int NVB, int remap) {
+  using S = V7Shape<DK, C, BV>;
+  constexpr int NT = S::NT, NRT = S::NRT, NDT = S::NDT, NKU_D = S::NKU_D, NKU_C = S::NKU_C;
+  constexpr int NPF = S::NPF;
+  __shared__ __align__(1024) uint16_t slot0[S::SLOT];
+  __shared__ __align__(1024) uint16_t slot1[S::SLOT];
+  __shared__ __align__(1024) uint16_t slot2[S::SLOT];
+  __shared__ __align__(16) bf16x8 bS_buf[NT][NKU_D][kWave];  // S_n as operand fragments
+  __shared__ __align__(16) bf16x8 bU_buf[NT][NKU_C][kWave];  // U'_n as operand fragments
+  __shared__ __align__(16) bf16x8 P_buf[NPF][kWave];         // P_n as operand fragments
+
+  const int x = blockIdx.x;
+  int bh, vb;
+  if (remap) {  // all value blocks of one (b, h) on one XCD (same blockIdx % 8)
+    const int slot = x >> 3;
+    vb = slot % NVB;
+    bh = (slot / NVB) * 8 + (x & 7);
+  } else {
+    bh = x / NVB;
+    vb = x % NVB;
+  }
+  const int64_t b = bh / H, h = bh % H;
+  const int v0 = vb * BV;
+  const int lane = threadIdx.x & 63, role = wave_id(), li = lane & 15, g = lane >> 4;
+  auto chunk_valid = [&](int n) { return int(L - int64_t(n) * C < C ? L - int64_t(n) * C : C); };
+  auto row_of = [&](int n) { return (b * L + int64_t(n) * C) * H + h; };
+  auto sync = [&]() {  // this wave's LDS writes done, then the workgroup barrier
+    wait_lgkm0();
+    barrier_nowait();
+  };
+
+  if (role == S::kDma) {
+    // ---------------------------------------------------------------- DMA
+    typename S::Dma dma;
+    dma.init(int64_t(H) * DK, int64_t(H) * DV, lane, 0);
+    auto chunk_src = [&](int n) {
+      const int64_t r0 = row_of(n);
+      using U = const uint16_t*;
+      return typename S::Dma::Src{(U)uniform_ptr(q + r0 * DK), (U)uniform_ptr(k + r0 * DK),
+                                  (U)uniform_ptr(tws + (int64_t(bh) * NC + n) * C * C),
+                                  (U)uniform_ptr(v + r0 * DV + v0), chunk_valid(n)};
+    };
+    constexpr int D = S::DMA_COUNT;
+    if (NC > 0) dma.issue_part(0, 1, lds_addr_of(slot0), chunk_src(0));
+    if (NC > 1) dma.issue_part(0, 1, lds_addr_of(slot1), chunk_src(1));
+    auto step = [&](uint16_t* fill, int n) {
+      // chunk n is complete once at most chunk n+1's transfers are outstanding
+      if (n + 1 < NC) wait_vmcnt<D>();
+      else wait_vmcnt<0>();
+      sync();  // A
+      const bool more = n + 2 < NC;
+      const auto src = chunk_src(more ? n + 2 : n);
+      const uint32_t fa = lds_addr_of(fill);
+      if (more) dma.issue_part(0, 2, fa, src);
+      sync();  // B
+      if (more) dma.issue_part(1, 2, fa, src);
+    };
+    for (int n = 0; n < NC; n += 3) {
+      step(slot2, n);
+      if (n + 1 < NC) step(slot0, n + 1);
+      if (n + 2 < NC) step(slot1, n + 2);
+    }
+    wait_vmcnt<0>();
+  } else if (role >= S::kChain0 && role < S::kChain0 + NT) {
+    // -------------------------------------------------------------- chain
+    const int ct = role - S::kChain0;  // this wave's state tile
+    const int col = v0 + 16 * ct + li;
+    // St[dt][qq] = S[key_phys(16 dt + 4 g + qq)][col]
+    f32x4 St[NDT];
+    Frag<uint16_t> bS[NKU_D];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq)
+        St[dt][qq] = s0 != nullptr ? s0[(int64_t(bh) * DK + key_phys(16 * dt + 4 * g + qq)) * DV + col] : 0.0f;
+#pragma unroll
+    for (int ku = 0; ku < NKU_D; ++ku) {
+      bS[ku] = acc_frag<uint16_t>(St[2 * ku], St[2 * ku + 1]);
+      bS_buf[ct][ku][lane] = bS[ku].v;
+    }
+    auto step = [&](const uint16_t* __restrict__ cur) {
+      const uint16_t* Ks = cur + S::KOFF;
+      const uint16_t* Ts = cur + S::TOFF;
+      const uint16_t* Vs = cur + S::VOFF;
+      sync();  // A
+      // operands that only depend on the chunk: this tile's V columns and T
+      bf16x4 Vt[NRT];
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        const int j = lane & 15;
+        Vt[rt] = lds_read_tr(Vs + swz_off<BV>(16 * rt + 4 * g + (j >> 2), 16 * ct + 4 * (j & 3)));
+      }
+      Frag<uint16_t> Tf[NRT][NKU_C];
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int ku = 0; ku < NKU_C; ++ku)
+          if (32 * ku <= 16 * rt + 15) Tf[rt][ku] = sw_frag<C>(Ts, 16 * rt + li, ku, g);
+      // Y = K S
+      f32x4 Y[NRT];
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) Y[rt] = zero4();
+#pragma unroll
+      for (int ku = 0; ku < NKU_D; ++ku) {
+        Frag<uint16_t> Kf[NRT];
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) Kf[rt] = wide_frag<DK>(Ks, 16 * rt + li, ku, g);
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) mma(Y[rt], Kf[rt], bS[ku]);
+      }
+      // D = V - Y, U' = T D, published for the output wave
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) Y[rt][qq] = static_cast<float>(Vt[rt][qq]) - Y[rt][qq];
+      Frag<uint16_t> bD[NKU_C];
+#pragma unroll
+      for (int ku = 0; ku < NKU_C; ++ku)
+        bD[ku] = acc_frag<uint16_t>(Y[2 * ku], 2 * ku + 1 < NRT ? Y[(2 * ku + 1) % NRT] : zero4());
+      f32x4 U[2 * NKU_C];
+#pragma unroll
+      for (int rt = 0; rt < 2 * NKU_C; ++rt) {
+        U[rt] = zero4();
+        if (rt < NRT) {
+#pragma unroll
+          for (int ku = 0; ku < NKU_C; ++ku)
+            if (32 * ku <= 16 * rt + 15) mma(U[rt], Tf[rt][ku], bD[ku]);
+        }
+      }
+      Frag<uint16_t> bU[NKU_C];
+#pragma unroll
+      for (int ku = 0; ku < NKU_C; ++ku) {
+        bU[ku] = acc_frag<uint16_t>(U[2 * ku], U[2 * ku + 1]);
+        bU_buf[ct][ku][lane] = bU[ku].v;
+      }
+      // the first K^T fragments are fetched before the barrier
+      constexpr int NH = (NDT + 1) / 2;
+      Frag<uint16_t> KTa[NH][NKU_C];
+#pragma unroll
+      for (int dt = 0; dt < NH; ++dt)
+#pragma unroll
+        for (int kt = 0; kt < NKU_C; ++kt) KTa[dt][kt] = wide_frag_tr<DK>(Ks, dt, kt, lane);
+      sync();  // B
+      // S += K^T U', then publish S_{n+1}
+      Frag<uint16_t> KTb[NDT - NH > 0 ? NDT - NH : 1][NKU_C];
+#pragma unroll
+      for (int dt = NH; dt < NDT; ++dt)
+#pragma unroll
+        for (int kt = 0; kt < NKU_C; ++kt) KTb[dt - NH][kt] = wide_frag_tr<DK>(Ks, dt, kt, lane);
+#pragma unroll
+      for (int dt = 0; dt < NH; ++dt)
+#pragma unroll
+        for (int kt = 0; kt < NKU_C; ++kt) mma(St[dt], KTa[dt][kt], bU[kt]);
+#pragma unroll
+      for (int dt = NH; dt < NDT; ++dt)
+#pragma unroll
+        for (int kt = 0; kt < NKU_C; ++kt) mma(St[dt], KTb[dt - NH][kt], bU[kt]);
+#pragma unroll
+      for (int ku = 0; ku < NKU_D; ++ku) {
+        bS[ku] = acc_frag<uint16_t>(St[2 * ku], St[2 * ku + 1]);
+        bS_buf[ct][ku][lane] = bS[ku].v;
+      }
+    };
+    for (int n = 0; n < NC; n += 3) {
+      step(slot0);
+      if (n + 1 < NC) step(slot1);
+      if (n + 2 < NC) step(slot2);
+    }
+    if (sfin != nullptr) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          sfin[(int64_t(bh) * DK + key_phys(16 * dt + 4 * g + qq)) * DV + col] = St[dt][qq];
+    }
+  } else if (role == S::kOut) {
+    // ------------------------------------------------------------- output
+    auto step = [&](const uint16_t* __restrict__ cur, int n) {
+      const uint16_t* Qs = cur + S::QOFF;
+      sync();  // A
+      // Zt[ct][rt][qq] = Z[16 rt + li][16 ct + 4 g + qq]  (Z^T = S^T Q^T)
+      f32x4 Zt[NT][NRT];
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) Zt[ct][rt] = zero4();
+#pragma unroll
+      for (int ku = 0; ku < NKU_D; ++ku) {
+        Frag<uint16_t> bSo[NT], Qf[NRT];
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) bSo[ct].v = bS_buf[ct][ku][lane];
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) Qf[rt] = wide_frag<DK>(Qs, 16 * rt + li, ku, g);
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+          for (int ct = 0; ct < NT; ++ct) mma(Zt[ct][rt], bSo[ct], Qf[rt]);
+      }
+      sync();  // B
+      // O^T = Z^T + U'^T P^T; lane (li, g) stores O[16 rt + li][16 ct + 4g .. 4g + 3]
+      const int valid = chunk_valid(n);
+      const int64_t row0 = row_of(n);
+      Frag<uint16_t> pf[NPF];
+#pragma unroll
+      for (int i = 0; i < NPF; ++i) pf[i].v = P_buf[i][lane];
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) {
+        Frag<uint16_t> bUo[NKU_C];
+#pragma unroll
+        for (int ku = 0; ku < NKU_C; ++ku) bUo[ku].v = bU_buf[ct][ku][lane];
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+          f32x4 acc = Zt[ct][rt];
+#pragma unroll
+          for (int ku = 0; ku < NKU_C; ++ku)
+            if (32 * ku <= 16 * rt + 15) mma(acc, bUo[ku], pf[pf_index(rt, ku)]);
+          const int t = 16 * rt + li;
+          bf16x4 ov;
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) ov[qq] = static_cast<__bf16>(acc[qq]);
+          if (t < valid)
+            *reinterpret_cast<bf16x4*>(o + (row0 + int64_t(t) * H) * DV + v0 + 16 * ct + 4 * g) = ov;
+        }
+      }
+    };
+    for (int n = 0; n < NC; n += 3) {
+      step(slot0, n);
+      if (n + 1 < NC) step(slot1, n + 1);
+      if (n + 2 < NC) step(slot2, n + 2);
+    }
+  } else if (role == S::kP) {
+    // ------------------------------------------------------------------ P
+    auto step = [&](const uint16_t* __restrict__ cur) {
+      const uint16_t* Qs = cur + S::QOFF;
+      const uint16_t* Ks = cur + S::KOFF;
+      sync();  // A
+      // Pt[r][c][qq] = P[16 r + li][16 c + 4 g + qq] for c <= r
+      f32x4 Pt[NRT][NRT];
+#pragma unroll
+      for (int r = 0; r < NRT; ++r)
+#pragma unroll
+        for (int c = 0; c < NRT; ++c) Pt[r][c] = zero4();
+#pragma unroll
+      for (int ku = 0; ku < NKU_D; ++ku) {
+        Frag<uint16_t> Qf[NRT], Kf[NRT];
+#pragma unroll
+        for (int r = 0; r < NRT; ++r) {
+          Qf[r] = wide_frag<DK>(Qs, 16 * r + li, ku, g);
+          Kf[r] = wide_frag<DK>(Ks, 16 * r + li, ku, g);
+        }
+#pragma unroll
+        for (int r = 0; r < NRT; ++r)
+#pragma unroll
+          for (int c = 0; c <= r; ++c) mma(Pt[r][c], Kf[c], Qf[r]);
+      }
+#pragma unroll
+      for (int r = 0; r < NRT; ++r) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          if (4 * g + qq > li) Pt[r][r][qq] = 0.0f;
+#pragma unroll
+        for (int ku = 0; ku < NKU_C; ++ku)
+          if (32 * ku <= 16 * r + 15) {
+            const f32x4 phi = (2 * ku + 1 <= r) ? Pt[r][(2 * ku + 1) % NRT] : zero4();
+            P_buf[pf_index(r, ku)][lane] = acc_frag<uint16_t>(Pt[r][2 * ku], phi).v;
+          }
+      }
+      sync();  // B
+    };
+    for (int n = 0; n < NC; n += 3) {
+      step(slot0);
+      if (n + 1 < NC) step(slot1);
+      if (n + 2 < NC) step(slot2);
+    }
+  }
+}
+
+// Shapes: d_k in {32, 64, 128}, chunk in {32, 64}, value block 16 or 32.
+inline bool v7_supported(int DK, int C, int BV) {
+  return (DK == 32 || DK == 64 || DK == 128) && (C == 32 || C == 64) && (BV == 16 || BV == 32);
+}
+
+template <int DK, int C, int BV>
+hipError_t recurrence_v7_launch_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                     const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
+                                     int B, int H, int64_t L, int DV, hipStream_t stream) {
+  const int NC = int((L + C - 1) / C);
+  const int BH = B * H;
+  const int NVB = DV / BV;
+  const int nwg = BH * NVB;
+  if (nwg == 0) return hipSuccess;
+  const int remap = (BH % 8 == 0) ? 1 : 0;
+  hipLaunchKernelGGL((recurrence_v7_kernel<DK, C, BV>), dim3(unsigned(nwg)), dim3(V7Shape<DK, C, BV>::THREADS),
+                     0, stream, q, k, v, tws, s0, o, sfin, H, L, NC, DV, NVB, remap);
+  return hipGetLastError();
+}
+
+template <int DK, int C>
+hipError_t recurrence_v7_bv(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* tws,
+                            const float* s0, uint16_t* o, float* sfin, int B, int H, int64_t L, int DV,
+                            int BV, hipStream_t s) {
+  switch (BV) {
+    case 16: return recurrence_v7_launch_impl<DK, C, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, s);
+    case 32: return recurrence_v7_launch_impl<DK, C, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+inline hipError_t launch_recurrence_v7(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                       const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
+                                       int B, int H, int64_t L, int DK, int DV, int C, int BV,
+                                       hipStream_t s) {
+  if (C == 32) {
+    switch (DK) {
+      case 32: return recurrence_v7_bv<32, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, s);
+      case 64: return recurrence_v7_bv<64, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, s);
+      case 128: return recurrence_v7_bv<128, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, s);
+    }
+  } else if (C == 64) {
+    switch (DK) {
+      case 32: return recurrence_v7_bv<32, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, s);
+      case 64: return recurrence_v7_bv<64, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, s);
+      case 128: return recurrence_v7_bv<128, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace efla

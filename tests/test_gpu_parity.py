@@ -114,7 +114,7 @@ def test_tiny_fp32_workload():
     _check_forward(inp, w.chunk, "tiny_fp32")
 
 
-@pytest.mark.parametrize("impl", ["v6", "v5", "v4", "v3", "v2"])
+@pytest.mark.parametrize("impl", ["v7", "v6", "v5", "v4", "v3", "v2"])
 @pytest.mark.parametrize("bv", ["16", "32", "64"])
 @pytest.mark.parametrize("dk,chunk", [(128, 64), (64, 32), (32, 64)])
 def test_value_block_widths_agree(bv, impl, dk, chunk, monkeypatch):
