@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libefla.so")
 SOURCES = ["api.hip", "step_kernels.hip", "chunk_bf16.hip", "chunk_bf16_v6.hip", "chunk_bf16_v7.hip",
-           "chunk_f32.hip"]
+           "ut_bf16.hip", "chunk_f32.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 CFLAGS = [
@@ -31,7 +31,8 @@ CFLAGS = [
 # accumulators in ordinary VGPRs, so results feed the bf16 conversions that
 # follow every product without a copy out of the accumulation registers.
 SOURCE_FLAGS = {"chunk_bf16_v6.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-                "chunk_bf16_v7.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+                "chunk_bf16_v7.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "ut_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

@@ -121,6 +121,13 @@ efla_status efla_chunk_ut_transform(const void* k, const void* beta, int B, int 
   if (workspace == nullptr || workspace_bytes < need) return EFLA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return EFLA_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // bf16: one wavefront per chunk (ut_wave.h) where it applies, else one
+  // workgroup per chunk; EFLA_UT_IMPL=v1 pins the latter for comparisons.
+  const char* impl = getenv("EFLA_UT_IMPL");
+  const bool want_v1 = impl && strcmp(impl, "v1") == 0;
+  if (dtype == EFLA_BF16 && !want_v1 && efla::ut_wave_bf16_supported(d_k, chunk))
+    return from_hip(efla::launch_ut_wave_bf16(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(beta),
+                                              static_cast<uint16_t*>(workspace), B, H, L, d_k, chunk, s));
   if (dtype == EFLA_BF16)
     return from_hip(efla::launch_ut_transform<uint16_t>(static_cast<const uint16_t*>(k),
                                                         static_cast<const uint16_t*>(beta),

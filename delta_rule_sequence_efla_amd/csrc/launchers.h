@@ -63,4 +63,10 @@ hipError_t launch_recurrence_v7_bf16(const uint16_t* q, const uint16_t* k, const
                                      int B, int H, int64_t L, int DK, int DV, int C, int BV,
                                      hipStream_t s);
 
+// bf16 UT transform with one wavefront per chunk (ut_wave.h); d_k in
+// {32, 64, 128}, chunk in {32, 64}.
+bool ut_wave_bf16_supported(int DK, int C);
+hipError_t launch_ut_wave_bf16(const uint16_t* k, const uint16_t* beta, uint16_t* tws, int B, int H, int64_t L,
+                               int DK, int C, hipStream_t s);
+
 }  // namespace efla

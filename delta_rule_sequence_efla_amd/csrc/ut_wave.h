@@ -1,0 +1,239 @@
+// ut_wave.h -- the per-chunk UT transform for bf16 inputs, one wavefront per
+// chunk, with every operand in registers.
+//
+// For a chunk of C tokens with key rows K and coefficients a (Method step 3
+// of the pages, computed here from beta and lambda = ||k||^2):
+//     G = K K^T,   X = (I + diag(a) tril(G, -1))^{-1},   T = X diag(a)
+// written row-major to the workspace [B, H, NC, C, C] (zeros above the
+// diagonal and in rows/columns of tokens past L).
+//
+// Layout of the work inside one wavefront:
+//   * K is loaded straight from global memory as 16-byte row fragments.  The
+//     sum over the key dimension in K K^T does not depend on the order in
+//     which the fragment slots visit the dims, so each lane takes 8
+//     consecutive dims (one 16-byte load) per k-unit.
+//   * G tiles come from bf16 matrix-core products: the diagonal 16x16 tiles
+//     (for lambda and the diagonal solves) and the tiles above the diagonal,
+//     which by symmetry are the transposes of the tiles below it.
+//   * The diagonal 16x16 blocks of X are solved by forward substitution, one
+//     lane per column, all blocks at once (through a small LDS copy of the
+//     diagonal G blocks, read as broadcasts).
+//   * The blocks below the diagonal follow block by block,
+//         X_ij = -X_ii diag(a_i) sum_{j <= m < i} G_im X_mj,
+//     on fp32 16x16x4 matrix-core products.  In the kk-th of the four
+//     products that make up a 16-deep sum, lane group g supplies k = 4 g + kk:
+//     then the B operand is element kk of an accumulator tile as it stands,
+//     and the A operand is element kk of the accumulator tile of its
+//     transpose, so every product reads its operands from registers.
+//   * T is staged through LDS as bf16 and stored with 16-byte row writes.
+#pragma once
+
+#include "common.h"
+
+namespace efla {
+
+template <int DK, int C>
+struct UtWaveShape {
+  static constexpr int NRT = C / 16, NKU = DK / 32;
+  static constexpr int GP = 17;                       // padded pitch of the 16x16 fp32 blocks
+  static constexpr int BLK = 16 * GP;                 // floats per block
+  static constexpr int TP = C + 8;                    // padded pitch of the bf16 T staging tile
+  static constexpr int SCRATCH = (2 * 4 * BLK * 4 > C * TP * 2) ? 2 * 4 * BLK * 4 : C * TP * 2;  // bytes
+  static constexpr int WAVES = 4;                     // chunks per workgroup
+};
+
+// acc += A B over a 16-deep sum with fp32 16x16x4 products: At holds the
+// accumulator tile of A^T (element kk of lane (li, g) = A[li][4 g + kk]) and
+// B the accumulator tile of B (element kk of lane (li, g) = B[4 g + kk][li]).
+__device__ __forceinline__ void mma16_f32(f32x4& acc, const f32x4& At, const f32x4& B) {
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(At[kk], B[kk], acc, 0, 0, 0);
+}
+
+// Compiler-level ordering point for LDS traffic inside one wavefront (the
+// hardware executes a wavefront's LDS operations in order).
+__device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory"); }
+
+template <int DK, int C>
+__global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict__ k,
+                                                      const uint16_t* __restrict__ beta,
+                                                      uint16_t* __restrict__ tws, int H, int64_t L, int NC,
+                                                      int64_t nchunks) {
+  using S = UtWaveShape<DK, C>;
+  constexpr int NRT = S::NRT, NKU = S::NKU, GP = S::GP, BLK = S::BLK, TP = S::TP;
+  __shared__ __align__(16) unsigned char scratch_all[S::WAVES][S::SCRATCH];
+  __shared__ float a_all[S::WAVES][64];
+
+  const int lane = threadIdx.x & 63, w = wave_id(), li = lane & 15, g = lane >> 4;
+  const int64_t id = int64_t(blockIdx.x) * S::WAVES + w;  // chunk handled by this wavefront
+  if (id >= nchunks) return;                              // no workgroup barriers below
+  const int chunk = int(id % NC);
+  const int64_t bh = id / NC;
+  const int64_t b = bh / H, h = bh % H;
+  const int64_t t0 = int64_t(chunk) * C;
+  const int valid = int(L - t0 < C ? L - t0 : C);
+  const int64_t row0 = (b * L + t0) * H + h;
+  float* Gs = reinterpret_cast<float*>(scratch_all[w]);   // [4][16][GP] diagonal G blocks
+  float* Xs = Gs + 4 * BLK;                               // [4][16][GP] diagonal X blocks
+  uint16_t* Ts = reinterpret_cast<uint16_t*>(scratch_all[w]);  // [C][TP] bf16 (after Gs/Xs are read)
+  float* as = a_all[w];
+
+  // ---- K row fragments and beta ------------------------------------------
+  Frag<uint16_t> Kf[NRT][NKU];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    const int t = 16 * rt + li;
+    const uint16_t* src = k + (row0 + int64_t(t) * H) * DK + 8 * g;
+#pragma unroll
+    for (int ku = 0; ku < NKU; ++ku) {
+      if (t < valid) Kf[rt][ku].v = *reinterpret_cast<const bf16x8*>(src + 32 * ku);
+      else Kf[rt][ku].v = bf16x8{};
+    }
+  }
+  const float bt = (lane < valid) ? to_f32(beta[row0 + int64_t(lane) * H]) : 0.0f;
+
+  // ---- G: diagonal tiles and the tiles above the diagonal ----------------
+  // Gd[b][qq] = G[16b + 4g + qq][16b + li];  Gu[i][m][qq] = G[16m + 4g + qq][16i + li], m < i
+  f32x4 Gd[NRT];
+  f32x4 Gu[NRT][NRT];
+#pragma unroll
+  for (int bb = 0; bb < NRT; ++bb) {
+    Gd[bb] = zero4();
+#pragma unroll
+    for (int ku = 0; ku < NKU; ++ku) mma(Gd[bb], Kf[bb][ku], Kf[bb][ku]);
+  }
+#pragma unroll
+  for (int i = 1; i < NRT; ++i)
+#pragma unroll
+    for (int m = 0; m < i; ++m) {
+      Gu[i][m] = zero4();
+#pragma unroll
+      for (int ku = 0; ku < NKU; ++ku) mma(Gu[i][m], Kf[m][ku], Kf[i][ku]);
+    }
+
+  // ---- lambda (the diagonal of G) and a ----------------------------------
+#pragma unroll
+  for (int bb = 0; bb < NRT; ++bb) {
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      Gs[bb * BLK + (4 * g + qq) * GP + li] = Gd[bb][qq];
+    }
+  }
+  wave_lds_order();
+  if (lane < C) {
+    const float lam = Gs[(lane >> 4) * BLK + (lane & 15) * GP + (lane & 15)];
+    as[lane] = (lane < valid) ? efla_alpha(bt, lam) : 0.0f;
+  }
+  wave_lds_order();
+
+  // ---- diagonal blocks of X: forward substitution, lane = (block, column) --
+  //   x_r = delta_rc - a_r * sum_{m < r} G_rm x_m
+  {
+    const int bb = lane >> 4, c = lane & 15;
+    if (bb < NRT) {
+      const float* Gb = Gs + bb * BLK;
+      const float* ab = as + 16 * bb;
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float s = 0.0f;
+#pragma unroll
+        for (int m = 0; m < r; ++m) s = fmaf(Gb[r * GP + m], x[m], s);
+        x[r] = (r == c ? 1.0f : 0.0f) - ab[r] * s;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Xs[bb * BLK + r * GP + c] = x[r];
+    }
+  }
+  wave_lds_order();
+  // X[i][j][qq] = X[16i + 4g + qq][16j + li] (accumulator tiles), XT[i] the tile of X_ii^T
+  f32x4 X[NRT][NRT], XT[NRT];
+#pragma unroll
+  for (int bb = 0; bb < NRT; ++bb)
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      X[bb][bb][qq] = Xs[bb * BLK + (4 * g + qq) * GP + li];
+      XT[bb][qq] = Xs[bb * BLK + li * GP + 4 * g + qq];
+    }
+  // row coefficients a[16 i + 4 g + qq] and column coefficients a[16 j + li]
+  f32x4 arow[NRT];
+  float acol[NRT];
+#pragma unroll
+  for (int i = 0; i < NRT; ++i) {
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) arow[i][qq] = as[16 * i + 4 * g + qq];
+    acol[i] = as[16 * i + li];
+  }
+  wave_lds_order();
+
+  // ---- blocks below the diagonal ----------------------------------------
+#pragma unroll
+  for (int i = 1; i < NRT; ++i)
+#pragma unroll
+    for (int j = 0; j < i; ++j) {
+      f32x4 R = zero4();
+#pragma unroll
+      for (int m = j; m < i; ++m) mma16_f32(R, Gu[i][m], X[m][j]);  // Gu[i][m] is the tile of G_im^T
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) R[qq] *= arow[i][qq];
+      f32x4 Y = zero4();
+      mma16_f32(Y, XT[i], R);
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) X[i][j][qq] = -Y[qq];
+    }
+
+  // ---- T = X diag(a): stage as bf16 rows, then 16-byte row stores --------
+#pragma unroll
+  for (int i = 0; i < NRT; ++i)
+#pragma unroll
+    for (int j = 0; j < NRT; ++j)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int r = 16 * i + 4 * g + qq, c = 16 * j + li;
+        float val = 0.0f;
+        if (j < i || (j == i && c <= r)) val = X[i][j][qq] * acol[j];
+        Ts[r * TP + c] = from_f32<uint16_t>(val);
+      }
+  wave_lds_order();
+  uint16_t* out = tws + id * int64_t(C) * C;
+  constexpr int VPR = C / 8;  // 16-byte vectors per row
+#pragma unroll
+  for (int idx = lane; idx < C * VPR; idx += 64) {
+    const int r = idx / VPR, c0 = (idx % VPR) * 8;
+    *reinterpret_cast<u32x4*>(out + r * C + c0) = *reinterpret_cast<const u32x4*>(Ts + r * TP + c0);
+  }
+}
+
+inline bool ut_wave_supported(int DK, int C) { return (DK == 32 || DK == 64 || DK == 128) && (C == 32 || C == 64); }
+
+template <int DK, int C>
+hipError_t ut_wave_launch_impl(const uint16_t* k, const uint16_t* beta, uint16_t* tws, int B, int H, int64_t L,
+                               hipStream_t stream) {
+  const int NC = int((L + C - 1) / C);
+  const int64_t nchunks = int64_t(B) * H * NC;
+  if (nchunks == 0) return hipSuccess;
+  const int64_t nwg = (nchunks + UtWaveShape<DK, C>::WAVES - 1) / UtWaveShape<DK, C>::WAVES;
+  hipLaunchKernelGGL((ut_wave_kernel<DK, C>), dim3(unsigned(nwg)), dim3(64 * UtWaveShape<DK, C>::WAVES), 0, stream,
+                     k, beta, tws, H, L, NC, nchunks);
+  return hipGetLastError();
+}
+
+inline hipError_t launch_ut_wave(const uint16_t* k, const uint16_t* beta, uint16_t* tws, int B, int H, int64_t L,
+                                 int DK, int C, hipStream_t s) {
+  if (C == 32) {
+    switch (DK) {
+      case 32: return ut_wave_launch_impl<32, 32>(k, beta, tws, B, H, L, s);
+      case 64: return ut_wave_launch_impl<64, 32>(k, beta, tws, B, H, L, s);
+      case 128: return ut_wave_launch_impl<128, 32>(k, beta, tws, B, H, L, s);
+    }
+  } else if (C == 64) {
+    switch (DK) {
+      case 32: return ut_wave_launch_impl<32, 64>(k, beta, tws, B, H, L, s);
+      case 64: return ut_wave_launch_impl<64, 64>(k, beta, tws, B, H, L, s);
+      case 128: return ut_wave_launch_impl<128, 64>(k, beta, tws, B, H, L, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace efla

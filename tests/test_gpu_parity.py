@@ -160,6 +160,47 @@ def test_ut_transform_wy_identity():
     assert normwise(K.T @ T @ V, s_from_zero[0, 0]) <= 2e-5
 
 
+@pytest.mark.parametrize("dk,C", [(32, 32), (64, 32), (128, 32), (32, 64), (64, 64), (128, 64)])
+def test_ut_transform_bf16_wy_identity(dk, C, monkeypatch):
+    """bf16 stage 1 (both kernels) on ragged chunks with stiff and tiny keys:
+    exact zeros above the diagonal and past L, and the WY identity against
+    the oracle per chunk.  T is rounded to bf16 (relative 2^-9), hence 1e-2."""
+    require_gpu()
+    rng = np.random.default_rng(1000 + dk + C)
+    B, H, L = 2, 3, 2 * C + C // 2 + 3                    # two full chunks and a ragged one
+    scale = np.exp(rng.uniform(np.log(0.1), np.log(30.0), (B, L, H, 1)))
+    k = rng.standard_normal((B, L, H, dk))
+    k = k / np.linalg.norm(k, axis=-1, keepdims=True) * scale
+    beta = rng.uniform(0, 10, (B, L, H))
+    kt = torch.tensor(k, dtype=torch.float32).to(torch.bfloat16).cuda()
+    bt = torch.tensor(beta, dtype=torch.float32).to(torch.bfloat16).cuda()
+    K64, B64 = to_f64(kt), to_f64(bt)
+    Ts = {}
+    for impl in ("v2", "v1"):
+        monkeypatch.setenv("EFLA_UT_IMPL", impl)
+        _, T = efla.efla_chunk_ut_transform(kt, bt, chunk=C)
+        torch.cuda.synchronize()
+        Ts[impl] = to_f64(T)
+    nc = -(-L // C)
+    for impl, T in Ts.items():
+        assert T.shape == (B, H, nc, C, C)
+        for b in range(B):
+            for h in range(H):
+                for n in range(nc):
+                    Tn = T[b, h, n]
+                    v = min(C, L - n * C)
+                    assert np.array_equal(np.triu(Tn, 1), np.zeros_like(Tn)), (impl, b, h, n)
+                    assert not Tn[v:].any() and not Tn[:, v:].any(), (impl, b, h, n)
+                    Kc = K64[b, n * C:n * C + v, h]
+                    _, prod = oracle.forward(np.zeros((1, v, 1, dk)), Kc[None, :, None],
+                                             np.zeros((1, v, 1, dk)), B64[b, n * C:n * C + v, h][None, :, None],
+                                             np.eye(dk)[None, None])
+                    lhs = np.eye(dk) - Kc.T @ Tn[:v, :v] @ Kc
+                    assert normwise(lhs, prod[0, 0]) <= 1e-2, (impl, b, h, n, normwise(lhs, prod[0, 0]))
+    # the two kernels agree up to fp32 summation order and bf16 rounding of T
+    assert normwise(Ts["v2"], Ts["v1"]) <= 1e-2
+
+
 # ---------------------------------------------------------------------------
 # invariances and edge cases
 # ---------------------------------------------------------------------------
