@@ -115,6 +115,10 @@ __global__ __launch_bounds__(256) void recurrence_v6_kernel(
     wait_lgkm0();
     barrier_nowait();
   };
+  // The DMA wave writes LDS only through global_load_lds, whose completion it
+  // tracks with vmcnt; an lgkmcnt drain there would wait for transfers still
+  // in flight (they count against it too), so it passes the barriers directly.
+  auto sync_dma = [&]() { barrier_nowait(); };
 
   if (role == S::kDma) {
     // ---------------------------------------------------------------- DMA
@@ -134,12 +138,12 @@ __global__ __launch_bounds__(256) void recurrence_v6_kernel(
       // chunk n is complete once at most chunk n+1's transfers are outstanding
       if (n + 1 < NC) wait_vmcnt<D>();
       else wait_vmcnt<0>();
-      sync();  // A
+      sync_dma();  // A
       const bool more = n + 2 < NC;
       const auto src = chunk_src(more ? n + 2 : n);
       const uint32_t fa = lds_addr_of(fill);
       if (more) dma.issue_part(0, 2, fa, src);
-      sync();  // B
+      sync_dma();  // B
       if (more) dma.issue_part(1, 2, fa, src);
     };
     for (int n = 0; n < NC; n += 3) {

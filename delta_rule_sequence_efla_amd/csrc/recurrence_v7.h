@@ -68,6 +68,10 @@ __global__ __launch_bounds__(64 * (BV / 16 + 3)) void recurrence_v7_kernel(
     wait_lgkm0();
     barrier_nowait();
   };
+  // The DMA wave writes LDS only through global_load_lds, whose completion it
+  // tracks with vmcnt; an lgkmcnt drain there would wait for transfers still
+  // in flight (they count against it too), so it passes the barriers directly.
+  auto sync_dma = [&]() { barrier_nowait(); };
 
   if (role == S::kDma) {
     // ---------------------------------------------------------------- DMA
@@ -87,12 +91,12 @@ __global__ __launch_bounds__(64 * (BV / 16 + 3)) void recurrence_v7_kernel(
       // chunk n is complete once at most chunk n+1's transfers are outstanding
       if (n + 1 < NC) wait_vmcnt<D>();
       else wait_vmcnt<0>();
-      sync();  // A
+      sync_dma();  // A
       const bool more = n + 2 < NC;
       const auto src = chunk_src(more ? n + 2 : n);
       const uint32_t fa = lds_addr_of(fill);
       if (more) dma.issue_part(0, 2, fa, src);
-      sync();  // B
+      sync_dma();  // B
       if (more) dma.issue_part(1, 2, fa, src);
     };
     for (int n = 0; n < NC; n += 3) {
@@ -173,28 +177,18 @@ __global__ __launch_bounds__(64 * (BV / 16 + 3)) void recurrence_v7_kernel(
         bU[ku] = acc_frag<uint16_t>(U[2 * ku], U[2 * ku + 1]);
         bU_buf[ct][ku][lane] = bU[ku].v;
       }
-      // the first K^T fragments are fetched before the barrier
-      constexpr int NH = (NDT + 1) / 2;
-      Frag<uint16_t> KTa[NH][NKU_C];
-#pragma unroll
-      for (int dt = 0; dt < NH; ++dt)
-#pragma unroll
-        for (int kt = 0; kt < NKU_C; ++kt) KTa[dt][kt] = wide_frag_tr<DK>(Ks, dt, kt, lane);
       sync();  // B
-      // S += K^T U', then publish S_{n+1}
-      Frag<uint16_t> KTb[NDT - NH > 0 ? NDT - NH : 1][NKU_C];
+      // S += K^T U' (the K^T fragments are read after the barrier, where the
+      // LDS is less busy), then publish S_{n+1}
+      Frag<uint16_t> KT[NDT][NKU_C];
 #pragma unroll
-      for (int dt = NH; dt < NDT; ++dt)
+      for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int kt = 0; kt < NKU_C; ++kt) KTb[dt - NH][kt] = wide_frag_tr<DK>(Ks, dt, kt, lane);
+        for (int kt = 0; kt < NKU_C; ++kt) KT[dt][kt] = wide_frag_tr<DK>(Ks, dt, kt, lane);
 #pragma unroll
-      for (int dt = 0; dt < NH; ++dt)
+      for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int kt = 0; kt < NKU_C; ++kt) mma(St[dt], KTa[dt][kt], bU[kt]);
-#pragma unroll
-      for (int dt = NH; dt < NDT; ++dt)
-#pragma unroll
-        for (int kt = 0; kt < NKU_C; ++kt) mma(St[dt], KTb[dt - NH][kt], bU[kt]);
+        for (int kt = 0; kt < NKU_C; ++kt) mma(St[dt], KT[dt][kt], bU[kt]);
 #pragma unroll
       for (int ku = 0; ku < NKU_D; ++ku) {
         bS[ku] = acc_frag<uint16_t>(St[2 * ku], St[2 * ku + 1]);
