@@ -15,8 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libefla.so")
-SOURCES = ["api.hip", "step_kernels.hip", "chunk_bf16.hip", "chunk_bf16_v6.hip", "chunk_bf16_v7.hip",
-           "ut_bf16.hip", "chunk_f32.hip"]
+SOURCES = ["api.hip", "step_kernels.hip", "chunk_bf16.hip", "chunk_bf16_roles.hip", "ut_bf16.hip",
+           "chunk_f32.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 CFLAGS = [
@@ -27,11 +27,11 @@ CFLAGS = [
 ]
 
 
-# Per-source flags.  The one-role-per-wavefront recurrences keep their matrix-core
-# accumulators in ordinary VGPRs, so results feed the bf16 conversions that
-# follow every product without a copy out of the accumulation registers.
-SOURCE_FLAGS = {"chunk_bf16_v6.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-                "chunk_bf16_v7.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+# Per-source flags.  The one-role-per-wavefront recurrence and the UT transform
+# keep their matrix-core accumulators in ordinary VGPRs, so results feed the
+# bf16 conversions that follow every product without a copy out of the
+# accumulation registers.
+SOURCE_FLAGS = {"chunk_bf16_roles.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
                 "ut_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 

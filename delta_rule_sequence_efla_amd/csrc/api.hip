@@ -41,18 +41,17 @@ int choose_value_block(efla_dtype dt, int d_v) {
     if ((bv == 16 || bv == 32 || bv == 64) && bv <= d_v) return bv;
   }
   // Every 16 value columns of a (b, h) form one sequential chain whatever the
-  // block width, so a wider block costs no parallelism; 32 columns is the
-  // width of the paired-wavefront kernel.
+  // block width, so a wider block costs no parallelism; 32 columns (two chain
+  // wavefronts) is the width the one-role-per-wavefront kernel is built for.
   return d_v >= 32 ? 32 : 16;
 }
 
-// Which recurrence kernel runs for given sizes.  bf16: one role per wavefront
-// with one chain wavefront per state tile (recurrence_v7.h) where it applies,
-// else one wavefront per tile with the DMA-fed ring (recurrence_v4.h), else
-// the register-staged one (recurrence_v3.h), else the generic kernel; fp32
-// always takes the generic kernel.  EFLA_RECURRENCE_IMPL=v2|v3|v4|v5|v6 pins
-// an older kernel for comparisons (falling through where it does not apply).
-enum class Rec { kGeneric, kV3, kV4, kV5, kV6, kV7 };
+// Which recurrence kernel runs for given sizes.  bf16: one role per
+// wavefront (recurrence_roles.h) where it applies, else the generic kernel;
+// fp32 always takes the generic kernel.  EFLA_RECURRENCE_IMPL=tile|generic
+// selects the one-wavefront-per-tile kernel (recurrence_tile.h) or the generic
+// one for comparisons (falling through where the choice does not apply).
+enum class Rec { kGeneric, kTile, kRoles };
 struct RecChoice {
   Rec kind;
   int bv;
@@ -61,14 +60,10 @@ RecChoice choose_recurrence(efla_dtype dt, int d_k, int d_v, int chunk) {
   const int bv = choose_value_block(dt, d_v);
   if (dt != EFLA_BF16) return {Rec::kGeneric, bv};
   const char* impl = getenv("EFLA_RECURRENCE_IMPL");
-  const bool v2 = impl && strcmp(impl, "v2") == 0, v3 = impl && strcmp(impl, "v3") == 0;
-  const bool v4 = impl && strcmp(impl, "v4") == 0, v5 = impl && strcmp(impl, "v5") == 0;
-  const bool v6 = impl && strcmp(impl, "v6") == 0;
-  if (!v2 && !v3 && !v4 && !v5 && !v6 && efla::recurrence_v7_supported(d_k, chunk, bv)) return {Rec::kV7, bv};
-  if (!v2 && !v3 && !v4 && !v5 && efla::recurrence_v6_supported(d_k, chunk, bv)) return {Rec::kV6, bv};
-  if (!v2 && !v3 && !v4 && efla::recurrence_v5_supported(d_k, chunk, bv)) return {Rec::kV5, bv};
-  if (!v2 && !v3 && efla::recurrence_v4_supported(d_k, chunk, bv)) return {Rec::kV4, bv};
-  if (!v2 && efla::recurrence_v3_supported(d_k, chunk)) return {Rec::kV3, bv};
+  const bool generic = impl && strcmp(impl, "generic") == 0, tile = impl && strcmp(impl, "tile") == 0;
+  if (generic) return {Rec::kGeneric, bv};
+  if (!tile && efla::recurrence_roles_supported(d_k, chunk, bv)) return {Rec::kRoles, bv};
+  if (efla::recurrence_tile_supported(d_k, chunk, bv)) return {Rec::kTile, bv};
   return {Rec::kGeneric, bv};
 }
 
@@ -122,10 +117,10 @@ efla_status efla_chunk_ut_transform(const void* k, const void* beta, int B, int 
   if (!aligned16(workspace)) return EFLA_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // bf16: one wavefront per chunk (ut_wave.h) where it applies, else one
-  // workgroup per chunk; EFLA_UT_IMPL=v1 pins the latter for comparisons.
+  // workgroup per chunk; EFLA_UT_IMPL=workgroup pins the latter for comparisons.
   const char* impl = getenv("EFLA_UT_IMPL");
-  const bool want_v1 = impl && strcmp(impl, "v1") == 0;
-  if (dtype == EFLA_BF16 && !want_v1 && efla::ut_wave_bf16_supported(d_k, chunk))
+  const bool want_wg = impl && strcmp(impl, "workgroup") == 0;
+  if (dtype == EFLA_BF16 && !want_wg && efla::ut_wave_bf16_supported(d_k, chunk))
     return from_hip(efla::launch_ut_wave_bf16(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(beta),
                                               static_cast<uint16_t*>(workspace), B, H, L, d_k, chunk, s));
   if (dtype == EFLA_BF16)
@@ -162,21 +157,12 @@ efla_status efla_chunk_recurrence(const void* q, const void* k, const void* v, c
     const auto* tb = static_cast<const uint16_t*>(workspace);
     auto* ob = static_cast<uint16_t*>(o);
     switch (rc.kind) {
-      case Rec::kV7:
-        return from_hip(efla::launch_recurrence_v7_bf16(qb, kb, vb, tb, s0, ob, s_final, B, H, L, d_k, d_v,
-                                                        chunk, rc.bv, s));
-      case Rec::kV6:
-        return from_hip(efla::launch_recurrence_v6_bf16(qb, kb, vb, tb, s0, ob, s_final, B, H, L, d_k, d_v,
-                                                        chunk, rc.bv, s));
-      case Rec::kV5:
-        return from_hip(efla::launch_recurrence_v5_bf16(qb, kb, vb, tb, s0, ob, s_final, B, H, L, d_k, d_v,
-                                                        chunk, rc.bv, s));
-      case Rec::kV4:
-        return from_hip(efla::launch_recurrence_v4_bf16(qb, kb, vb, tb, s0, ob, s_final, B, H, L, d_k, d_v,
-                                                        chunk, rc.bv, s));
-      case Rec::kV3:
-        return from_hip(efla::launch_recurrence_v3_bf16(qb, kb, vb, tb, s0, ob, s_final, B, H, L, d_k, d_v,
-                                                        chunk, rc.bv, s));
+      case Rec::kRoles:
+        return from_hip(efla::launch_recurrence_roles_bf16(qb, kb, vb, tb, s0, ob, s_final, B, H, L, d_k, d_v,
+                                                           chunk, rc.bv, s));
+      case Rec::kTile:
+        return from_hip(efla::launch_recurrence_tile_bf16(qb, kb, vb, tb, s0, ob, s_final, B, H, L, d_k, d_v,
+                                                          chunk, rc.bv, s));
       case Rec::kGeneric:
         break;
     }
@@ -192,11 +178,8 @@ efla_status efla_chunk_recurrence(const void* q, const void* k, const void* v, c
 const char* efla_chunk_recurrence_kernel(int d_k, int d_v, int chunk, efla_dtype dtype) {
   if (!valid_dtype(dtype) || !valid_dim(d_k) || !valid_dim(d_v) || !valid_chunk(chunk)) return "unsupported";
   switch (choose_recurrence(dtype, d_k, d_v, chunk).kind) {
-    case Rec::kV7: return "recurrence_v7_kernel";
-    case Rec::kV6: return "recurrence_v6_kernel";
-    case Rec::kV5: return "recurrence_v5_kernel";
-    case Rec::kV4: return "recurrence_v4_kernel";
-    case Rec::kV3: return "recurrence_v3_kernel";
+    case Rec::kRoles: return "recurrence_roles_kernel";
+    case Rec::kTile: return "recurrence_tile_kernel";
     case Rec::kGeneric: break;
   }
   return "recurrence_kernel";

@@ -24,44 +24,22 @@ hipError_t launch_recurrence(const T* q, const T* k, const T* v, const T* tws, c
                              T* o, float* sfin, int B, int H, int64_t L, int DK, int DV, int C,
                              int BV, hipStream_t stream);
 
-// bf16 recurrence with one wavefront per 16 value columns (recurrence_v3.h);
-// covers d_k in {32, 64, 128} and chunk in {32, 64}.
-bool recurrence_v3_supported(int DK, int C);
-hipError_t launch_recurrence_v3_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                     const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
-                                     int B, int H, int64_t L, int DK, int DV, int C, int BV,
-                                     hipStream_t s);
+// bf16 recurrence with one wavefront per 16-column state tile and a DMA-fed
+// LDS ring (recurrence_tile.h); d_k in {32, 64, 128}, chunk in {32, 64},
+// value blocks of 16, 32 or 64 columns.
+bool recurrence_tile_supported(int DK, int C, int BV);
+hipError_t launch_recurrence_tile_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                       const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
+                                       int B, int H, int64_t L, int DK, int DV, int C, int BV,
+                                       hipStream_t s);
 
-// bf16 recurrence with DMA-fed LDS ring (recurrence_v4.h); same coverage.
-bool recurrence_v4_supported(int DK, int C, int BV);
-hipError_t launch_recurrence_v4_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                     const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
-                                     int B, int H, int64_t L, int DK, int DV, int C, int BV,
-                                     hipStream_t s);
-
-// bf16 recurrence with chain / output wavefront pairs (recurrence_v5.h);
-// value blocks of 32 columns.
-bool recurrence_v5_supported(int DK, int C, int BV);
-hipError_t launch_recurrence_v5_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                     const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
-                                     int B, int H, int64_t L, int DK, int DV, int C, int BV,
-                                     hipStream_t s);
-
-// bf16 recurrence with one role per wavefront: chain, output, P, DMA
-// (recurrence_v6.h); value blocks of 16 or 32 columns.
-bool recurrence_v6_supported(int DK, int C, int BV);
-hipError_t launch_recurrence_v6_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                     const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
-                                     int B, int H, int64_t L, int DK, int DV, int C, int BV,
-                                     hipStream_t s);
-
-// bf16 recurrence with one role per wavefront and one chain wavefront per
-// 16-column state tile (recurrence_v7.h); value blocks of 16 or 32 columns.
-bool recurrence_v7_supported(int DK, int C, int BV);
-hipError_t launch_recurrence_v7_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                     const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
-                                     int B, int H, int64_t L, int DK, int DV, int C, int BV,
-                                     hipStream_t s);
+// bf16 recurrence with one role per wavefront: chain wavefronts, output, P
+// and DMA (recurrence_roles.h); same d_k and chunk, value blocks of 16 or 32.
+bool recurrence_roles_supported(int DK, int C, int BV);
+hipError_t launch_recurrence_roles_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                        const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
+                                        int B, int H, int64_t L, int DK, int DV, int C, int BV,
+                                        hipStream_t s);
 
 // bf16 UT transform with one wavefront per chunk (ut_wave.h); d_k in
 // {32, 64, 128}, chunk in {32, 64}.

@@ -1,0 +1,306 @@
+// lds_ring.h -- LDS and data-movement helpers of the bf16 recurrence kernels
+// on gfx950: the transposing LDS read, the XOR swizzles of the chunk tiles,
+// row fragments of swizzled tiles, direct global -> LDS transfers
+// (global_load_lds_dwordx4) of whole chunk tiles into a ring slot, explicit
+// wait counts and a barrier that does not drain memory operations.
+#pragma once
+
+#include "common.h"
+
+namespace efla {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives halfword
+// (i % 4) of the 8-byte words addressed by lanes 4e + i/4, e = 0..3.  So if
+// lane j addresses row r0 + j/4, columns c0 + 4(j%4) .. +3 of a row-major
+// bf16 matrix, lane i receives column c0 + i of rows r0 .. r0 + 3.
+__device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)((__attribute__((address_space(3))) uint16_t*)(p)));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// Physical 16-byte chunk for logical chunk `c` of row `r` in a row of NCH
+// chunks (NCH = row bytes / 16).  A 1 KiB DMA instruction covers RPI = 64/NCH
+// rows, and the swizzle is f(r % RPI) ^ g(r / RPI): the lane-dependent part is
+// the same for every instruction, the instruction-dependent part is uniform.
+// It spreads any 16 consecutive rows over distinct bank groups (row-fragment
+// reads, 16 rows x 8 B) and keeps the two chunks of any 4 consecutive rows
+// apart (transposing reads, 4 rows x 32 B).  Rows share the 64 LDS banks
+// 256 / (16 NCH) at a time.
+template <int NCH>
+__device__ __forceinline__ int swz_lane(int rr) {  // f: rr = r % RPI
+  if constexpr (NCH >= 16) return 2 * (rr & 3);
+  else if constexpr (NCH == 8) return 2 * ((rr >> 1) & 3);
+  else if constexpr (NCH == 4) return (rr >> 2) & 3;
+  else return 0;
+}
+template <int NCH>
+__device__ __forceinline__ int swz_instr(int b) {  // g: b = r / RPI
+  if constexpr (NCH >= 16) return (b & 1) | ((b & 2) << 2);
+  else if constexpr (NCH == 8) return b & 1;
+  else return 0;
+}
+template <int NCH>
+__device__ __forceinline__ int swz_chunk(int r, int c) {
+  constexpr int RPI = 64 / NCH;
+  return c ^ swz_lane<NCH>(r % RPI) ^ swz_instr<NCH>(r / RPI);
+}
+
+// A second swizzle, for tiles read with 16-byte row fragments (16 rows, one
+// 16-byte chunk each) and with transposing reads of 4 rows x 4 consecutive
+// chunks (8 bytes of each): s(r) = f(r % RPI) ^ g(r / RPI) with
+//   16 chunks per row: s = 4 (r & 3) ^ ((r >> 2) & 3)
+//    8 chunks per row: s = 4 ((r >> 1) & 1) ^ ((r >> 2) & 1) ^ 2 ((r >> 3) & 1)
+//    4 chunks per row: s = (r >> 2) & 3
+// Any 16 consecutive (16-aligned) rows then land on distinct bank groups, and
+// so do the 16 (row, chunk) pairs of a transposing read.
+template <int NCH>
+__device__ __forceinline__ int swzw_lane(int rr) {  // rr = r % RPI
+  if constexpr (NCH >= 16) return 4 * (rr & 3);
+  else if constexpr (NCH == 8) return 4 * ((rr >> 1) & 1) + ((rr >> 2) & 1);
+  else if constexpr (NCH == 4) return (rr >> 2) & 3;
+  else return 0;
+}
+template <int NCH>
+__device__ __forceinline__ int swzw_instr(int b) {  // b = r / RPI
+  if constexpr (NCH >= 16) return b & 3;
+  else if constexpr (NCH == 8) return 2 * (b & 1);
+  else return 0;
+}
+template <int NCH, bool WIDE>
+__device__ __forceinline__ int swz_lane_of(int rr) {
+  if constexpr (WIDE) return swzw_lane<NCH>(rr);
+  else return swz_lane<NCH>(rr);
+}
+template <int NCH, bool WIDE>
+__device__ __forceinline__ int swz_instr_of(int b) {
+  if constexpr (WIDE) return swzw_instr<NCH>(b);
+  else return swz_instr<NCH>(b);
+}
+template <int ROWE>
+__device__ __forceinline__ int swzw_off(int r, int col) {
+  constexpr int NCH = ROWE / 8, RPI = 64 / NCH;
+  return r * ROWE + (((col >> 3) ^ swzw_lane<NCH>(r % RPI) ^ swzw_instr<NCH>(r / RPI)) * 8) + (col & 7);
+}
+
+// Element offset of (r, col) in a swizzled bf16 tile with ROWE elements per row.
+template <int ROWE>
+__device__ __forceinline__ int swz_off(int r, int col) {
+  constexpr int NCH = ROWE / 8;
+  return r * ROWE + swz_chunk<NCH>(r, col >> 3) * 8 + (col & 7);
+}
+
+template <int ROWE>
+__device__ __forceinline__ Frag<uint16_t> sw_frag(const uint16_t* X, int row, int ku, int g) {
+  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(X + swz_off<ROWE>(row, 32 * ku + 4 * g));
+  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(X + swz_off<ROWE>(row, 32 * ku + 16 + 4 * g));
+  Frag<uint16_t> f;
+  f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return f;
+}
+
+// Transposed fragment (operand row = column m0 + li of X, k = rows of X).
+template <int ROWE>
+__device__ __forceinline__ Frag<uint16_t> sw_frag_tr(const uint16_t* X, int m0, int ku, int lane) {
+  const int j = lane & 15, g = lane >> 4;
+  const int r = 32 * ku + 4 * g + (j >> 2), c = m0 + 4 * (j & 3);
+  const bf16x4 lo = lds_read_tr(X + swz_off<ROWE>(r, c));
+  const bf16x4 hi = lds_read_tr(X + swz_off<ROWE>(r + 16, c));
+  Frag<uint16_t> f;
+  f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return f;
+}
+
+// One direct global -> LDS transfer of 16 bytes per lane: lane L reads
+// sbase + voff (voff per lane) and its bytes land at LDS byte address
+// lds_addr + 16 L (lds_addr wave-uniform, held in M0).  Issued through inline
+// asm so the compiler's wait-count model, which cannot tell ring slots apart,
+// does not add a drain of all transfers before every LDS read; the kernel
+// waits for exactly the transfers it needs.  The asm is volatile, so it stays
+// ordered with the kernel's waits and barriers (also volatile asm), but it
+// has no memory clobber: it only writes an LDS slot nobody reads until the
+// next barrier, so LDS reads and products may be scheduled around it.  M0 is
+// saved and restored around the transfer, and s_nop covers the M0-write hazard.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      // readfirstlane: a no-op on a value already in a scalar register, and a
+      // guard where the compiler keeps the (uniform) address in a vector one
+      : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_addr)));
+}
+
+// A pointer the whole wavefront agrees on, moved to scalar registers.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(u >> 32));
+  return reinterpret_cast<const void*>((uint64_t(hi) << 32) | lo);
+}
+
+// LDS byte address of a __shared__ object, as a wave-uniform (scalar) value.
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const void*)(p))));
+}
+
+// DMA of ROWS x ROWE bf16 (row t at src + t*stride) into a swizzled LDS tile.
+// The tile is a multiple of 1 KiB; wave w of NW issues instructions w, w + NW,
+// ... and every wave issues exactly cdiv(ninstr, NW) of them (a wave past the
+// end repeats its last one), so all waves issue the same count.  init()
+// computes, once, each lane's byte offset for every instruction of a full
+// tile; a ragged tile (rows at or past `valid` re-read row 0) takes the
+// slower per-instruction path.
+template <int ROWS, int ROWE, int NW, bool WIDE = false>
+struct DmaTile {
+  static constexpr int BYTES = ROWS * ROWE * 2, NINSTR = BYTES / 1024, PER_WAVE = cdiv(NINSTR, NW);
+  static constexpr int NCH = ROWE / 8, RPI = 64 / NCH;
+  static_assert(BYTES % 1024 == 0, "DMA tiles are whole KiB");
+  uint32_t off[PER_WAVE];       // lane byte offset of each instruction, full tile
+  uint32_t off_chunk;           // lane's swizzled chunk offset within its row
+  int lrow, w;                  // lane's row within one instruction; wave index
+  __device__ __forceinline__ static int instr(int w, int i) {
+    const int ins = w + i * NW;
+    return ins < NINSTR ? ins : NINSTR - 1;
+  }
+  __device__ __forceinline__ void init(int64_t stride, int lane, int wave) {
+    w = __builtin_amdgcn_readfirstlane(wave);  // uniform: LDS addresses stay scalar
+    lrow = lane / NCH;
+    off_chunk = 16u * uint32_t((lane % NCH) ^ swz_lane_of<NCH, WIDE>(lrow));
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int ins = instr(w, i);
+      off[i] = uint32_t((RPI * ins + lrow) * stride * 2) +
+               (off_chunk ^ (16u * uint32_t(swz_instr_of<NCH, WIDE>(ins))));
+    }
+  }
+  // Instruction i of this wave for the tile at LDS byte address lds_tile
+  // (wave-uniform), source row 0 at src.  RAGGED: rows at or past `valid`
+  // re-read row 0 (only the last chunk of a sequence can be ragged).
+  template <bool RAGGED>
+  __device__ __forceinline__ void issue(int i, uint32_t lds_tile, const uint16_t* src, int valid) const {
+    const int ins = instr(w, i);
+    uint32_t voff = off[i];
+    if constexpr (RAGGED) {
+      const uint32_t xo = 16u * uint32_t(swz_instr_of<NCH, WIDE>(ins));
+      voff = (RPI * ins + lrow < valid) ? voff : (off_chunk ^ xo);
+    }
+    dma16(src, voff, lds_tile + uint32_t(ins) * 1024u);
+  }
+};
+
+// WIDE_QK selects the 16-byte-fragment swizzle for the Q and K tiles.
+template <int DK, int C, int BV, int NW, bool WIDE_QK = false>
+struct ChunkDma {
+  using TQ = DmaTile<C, DK, NW, WIDE_QK>;
+  using TT = DmaTile<C, C, NW>;
+  using TV = DmaTile<C, BV, NW>;
+  static constexpr int PQ = TQ::PER_WAVE, PT = TT::PER_WAVE, PV = TV::PER_WAVE;
+  static constexpr int COUNT = 2 * PQ + PT + PV;
+  static constexpr int QOFF = 0, KOFF = C * DK, TOFF = 2 * C * DK, VOFF = 2 * C * DK + C * C;
+  TQ tq;
+  TT tt;
+  TV tv;
+  int64_t qk_stride, v_stride;
+  struct Src {
+    const uint16_t *q, *k, *t, *v;
+    int valid;
+  };
+  __device__ __forceinline__ void init(int64_t qk_stride_, int64_t v_stride_, int lane, int wave) {
+    qk_stride = qk_stride_;
+    v_stride = v_stride_;
+    tq.init(qk_stride, lane, wave);
+    tt.init(C, lane, wave);
+    tv.init(v_stride, lane, wave);
+  }
+  template <bool RAGGED>
+  __device__ __forceinline__ void issue(int j, uint32_t slot, const Src& src) const {
+    if (j < PQ) tq.template issue<RAGGED>(j, slot + 2 * QOFF, src.q, src.valid);
+    else if (j < 2 * PQ) tq.template issue<RAGGED>(j - PQ, slot + 2 * KOFF, src.k, src.valid);
+    else if (j < 2 * PQ + PT) tt.template issue<false>(j - 2 * PQ, slot + 2 * TOFF, src.t, C);
+    else tv.template issue<RAGGED>(j - 2 * PQ - PT, slot + 2 * VOFF, src.v, src.valid);
+  }
+  // Piece `part` of `parts` (an even split of the COUNT instructions) into
+  // the ring slot at LDS byte address `slot`; src pointers are wave-uniform.
+  __device__ __forceinline__ void issue_part(int part, int parts, uint32_t slot, const Src& src) const {
+    if (src.valid == C) {
+#pragma unroll
+      for (int j = 0; j < COUNT; ++j)
+        if (j >= part * COUNT / parts && j < (part + 1) * COUNT / parts) issue<false>(j, slot, src);
+    } else {
+#pragma unroll
+      for (int j = 0; j < COUNT; ++j)
+        if (j >= part * COUNT / parts && j < (part + 1) * COUNT / parts) issue<true>(j, slot, src);
+    }
+  }
+};
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier that does not wait for outstanding memory operations; the
+// caller waits for exactly the transfers it needs first.  The asm memory
+// clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_nowait() { asm volatile("s_barrier" ::: "memory"); }
+
+// s_waitcnt lgkmcnt(0) only: this wave's LDS writes are complete.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14)); }
+
+// index of P fragment (rt, ku) in the flat list (row tiles 0..NRT-1, ku <= rt/2)
+__device__ __forceinline__ constexpr int pf_index(int rt, int ku) {
+  // rt=0:(0,0)->0 rt=1:(1,0)->1 rt=2:(2,0)->2,(2,1)->3 rt=3:(3,0)->4,(3,1)->5
+  return rt < 2 ? rt : 2 + 2 * (rt - 2) + ku;
+}
+
+// Key-dimension order.  The sum over the key dimension in K S, Q S and
+// Q K^T does not depend on the order in which the k slots of the matrix-core
+// fragments visit the key dims, as long as every operand uses the same one.
+// Here logical dim 32 ku + 16 h + 4 g + q (the slot that accumulator rows
+// 4g..4g+3 of a state tile feed) is physical dim 32 ku + 8 g + 4 h + q, so a
+// lane's eight elements of a Q or K row fragment are contiguous: one 16-byte
+// LDS read instead of two 8-byte ones.  The state tile rows are logical dims;
+// only the initial-state load and the final-state store map them back.
+
+// Physical key dim of logical key dim l.
+__host__ __device__ constexpr int key_phys(int l) {
+  return 32 * (l / 32) + 8 * ((l % 16) / 4) + 4 * ((l % 32) / 16) + l % 4;
+}
+
+// Row fragment of a Q/K tile in the 16-byte layout: lane (li, g) holds
+// physical columns 32 ku + 8 g .. + 7 of row `row`.
+template <int ROWE>
+__device__ __forceinline__ Frag<uint16_t> wide_frag(const uint16_t* X, int row, int ku, int g) {
+  Frag<uint16_t> f;
+  f.v = *reinterpret_cast<const bf16x8*>(X + swzw_off<ROWE>(row, 32 * ku + 8 * g));
+  return f;
+}
+
+// K^T fragment for state rows dt (logical key dims 16 dt + i), tokens of
+// k-unit kt: the transposing read returns, in lane i of each 16-lane group,
+// column base(i / 4) + i % 4 of four rows, and base(m) = key_phys(16 dt + 4 m)
+// = 32 (dt / 2) + 4 (dt % 2) + 8 m puts logical dim 16 dt + i there.
+template <int ROWE>
+__device__ __forceinline__ Frag<uint16_t> wide_frag_tr(const uint16_t* X, int dt, int kt, int lane) {
+  const int j = lane & 15, g = lane >> 4;
+  const int r = 32 * kt + 4 * g + (j >> 2);
+  const int c = 32 * (dt >> 1) + 4 * (dt & 1) + 8 * (j & 3);
+  const bf16x4 lo = lds_read_tr(X + swzw_off<ROWE>(r, c));
+  const bf16x4 hi = lds_read_tr(X + swzw_off<ROWE>(r + 16, c));
+  Frag<uint16_t> f;
+  f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return f;
+}
+
+}  // namespace efla

@@ -1,92 +1,55 @@
-// recurrence_v6.h -- the sequential chunk pass for bf16 inputs with one role
-// per wavefront.
+// recurrence_roles.h -- the sequential chunk pass for bf16 inputs with one role
+// per wavefront and one chain wavefront per 16-column state tile.
 //
 // Per chunk (start state S, T from the UT transform):
 //     U' = T (V - K S),   S <- S + K^T U',   O = Q S + tril(Q K^T) U'
-// A workgroup owns BV value columns (BV/16 state tiles) of one (b, h) and runs
-// four wavefronts, one per SIMD, each with its own loop over the chunks:
-//   * chain:  keeps S (fp32) for all BV columns and forms Y = K S,
-//             U' = T (V - Y) and S += K^T U'; K, T and V are read from LDS
-//             once per workgroup and chunk, whatever the number of tiles;
-//   * output: Z^T = S^T Q^T and O^T = Z^T + U'^T P^T (operands of the same
-//             fragments swapped, so each lane stores 4 consecutive columns);
-//   * P:      P = tril(Q K^T), shared with the output wave through LDS;
-//   * DMA:    streams the chunk inputs into a three-slot LDS ring with
-//             global_load_lds_dwordx4, two chunks ahead.  Moving data into LDS
-//             runs at well under 64 B/clock per CU, and an issuing wavefront
-//             stalls while the queue is full, so the transfers get a wavefront
-//             of their own instead of stalling the products.
+// A workgroup owns BV value columns of one (b, h); its wavefronts:
+//   * chain c (one per 16-column tile): keeps its tile of S in fp32 registers
+//     and forms Y = K S, U' = T (V - Y) and S += K^T U' (38 matrix-core ops
+//     per chunk), publishing U' and the new S as bf16 operand fragments;
+//   * output: Z^T = S^T Q^T and O^T = Z^T + U'^T P^T for all BV columns
+//     (operands of the same fragments swapped, so each lane stores 4
+//     consecutive columns);
+//   * P: P = tril(Q K^T), published through LDS;
+//   * DMA: streams Q, K, T and V into a three-slot LDS ring two chunks ahead
+//     with global_load_lds_dwordx4.  Moving data into LDS runs at well under
+//     64 B/clock per CU and an issuing wavefront stalls while the queue is
+//     full, so the transfers get a wavefront of their own.
+// Q and K row fragments are 16-byte reads under the key-dimension
+// relabeling of lds_ring.h.  Wavefronts: P, chain 0 .. BV/16-1, output, DMA
+// (five for BV = 32; the DMA wave, which mostly waits, shares a SIMD with the
+// P wave).
 // Two barriers per chunk:
 //   A (chunk n in LDS, S_n fragments published)
-//     chain: Y, U' -> publish U'   | output: Z^T    | P: P -> publish | DMA: half of chunk n+2
+//     chains: Y, U' -> publish U'   | output: Z^T        | P: P -> publish | DMA: half of chunk n+2
 //   B (U' and P published)
-//     chain: S update -> publish S | output: O^T, store |             | DMA: other half
-// The chain's products (about 2 * 38 per 16 columns and chunk) are the
-// critical path; everything else runs beside them.
-//
-// Key-dimension order.  The sum over the key dimension in K S, Q S and
-// Q K^T does not depend on the order in which the k slots of the matrix-core
-// fragments visit the key dims, as long as every operand uses the same one.
-// Here logical dim 32 ku + 16 h + 4 g + q (the slot that accumulator rows
-// 4g..4g+3 of a state tile feed) is physical dim 32 ku + 8 g + 4 h + q, so a
-// lane's eight elements of a Q or K row fragment are contiguous: one 16-byte
-// LDS read instead of two 8-byte ones.  The state tile rows are logical dims;
-// only the initial-state load and the final-state store map them back.
+//     chains: S update -> publish S | output: O^T, store |                 | DMA: other half
 #pragma once
 
-#include "recurrence_v5.h"
+#include "lds_ring.h"
 
 namespace efla {
 
-// Physical key dim of logical key dim l (see above).
-__host__ __device__ constexpr int key_phys(int l) {
-  return 32 * (l / 32) + 8 * ((l % 16) / 4) + 4 * ((l % 32) / 16) + l % 4;
-}
-
-// Row fragment of a Q/K tile in the 16-byte layout: lane (li, g) holds
-// physical columns 32 ku + 8 g .. + 7 of row `row`.
-template <int ROWE>
-__device__ __forceinline__ Frag<uint16_t> wide_frag(const uint16_t* X, int row, int ku, int g) {
-  Frag<uint16_t> f;
-  f.v = *reinterpret_cast<const bf16x8*>(X + swzw_off<ROWE>(row, 32 * ku + 8 * g));
-  return f;
-}
-
-// K^T fragment for state rows dt (logical key dims 16 dt + i), tokens of
-// k-unit kt: the transposing read returns, in lane i of each 16-lane group,
-// column base(i / 4) + i % 4 of four rows, and base(m) = key_phys(16 dt + 4 m)
-// = 32 (dt / 2) + 4 (dt % 2) + 8 m puts logical dim 16 dt + i there.
-template <int ROWE>
-__device__ __forceinline__ Frag<uint16_t> wide_frag_tr(const uint16_t* X, int dt, int kt, int lane) {
-  const int j = lane & 15, g = lane >> 4;
-  const int r = 32 * kt + 4 * g + (j >> 2);
-  const int c = 32 * (dt >> 1) + 4 * (dt & 1) + 8 * (j & 3);
-  const bf16x4 lo = lds_read_tr(X + swzw_off<ROWE>(r, c));
-  const bf16x4 hi = lds_read_tr(X + swzw_off<ROWE>(r + 16, c));
-  Frag<uint16_t> f;
-  f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return f;
-}
-
 template <int DK, int C, int BV>
-struct V6Shape {
-  static constexpr int NT = BV / 16;  // state tiles of the workgroup, all held by the chain wave
-  static constexpr int THREADS = 4 * kWave;
+struct RolesShape {
+  static constexpr int NT = BV / 16;  // state tiles of the workgroup = chain wavefronts
+  static constexpr int NWAVES = NT + 3, THREADS = NWAVES * kWave;
   static constexpr int NRT = C / 16, NDT = DK / 16, NKU_D = DK / 32, NKU_C = C / 32;
   static constexpr int QOFF = 0, KOFF = C * DK, TOFF = 2 * C * DK, VOFF = 2 * C * DK + C * C;
   static constexpr int SLOT = 2 * C * DK + C * C + C * BV;
   static constexpr int NPF = (NRT == 4) ? 6 : 2;  // P fragments (rt, ku) with 32 ku <= 16 rt + 15
   using Dma = ChunkDma<DK, C, BV, 1, true>;       // every transfer from the DMA wave
   static constexpr int DMA_COUNT = Dma::COUNT;
-  enum Role { kChain = 0, kOut = 1, kP = 2, kDma = 3 };
+  // wave 0 is the P wave, waves 1..NT the chains, then output and DMA
+  static constexpr int kP = 0, kChain0 = 1, kOut = NT + 1, kDma = NT + 2;
 };
 
 template <int DK, int C, int BV>
-__global__ __launch_bounds__(256) void recurrence_v6_kernel(
+__global__ __launch_bounds__(64 * (BV / 16 + 3)) void recurrence_roles_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ tws, const float* __restrict__ s0, uint16_t* __restrict__ o,
     float* __restrict__ sfin, int H, int64_t L, int NC, int DV, int NVB, int remap) {
-  using S = V6Shape<DK, C, BV>;
+  using S = RolesShape<DK, C, BV>;
   constexpr int NT = S::NT, NRT = S::NRT, NDT = S::NDT, NKU_D = S::NKU_D, NKU_C = S::NKU_C;
   constexpr int NPF = S::NPF;
   __shared__ __align__(1024) uint16_t slot0[S::SLOT];
@@ -152,123 +115,95 @@ __global__ __launch_bounds__(256) void recurrence_v6_kernel(
       if (n + 2 < NC) step(slot1, n + 2);
     }
     wait_vmcnt<0>();
-  } else if (role == S::kChain) {
+  } else if (role >= S::kChain0 && role < S::kChain0 + NT) {
     // -------------------------------------------------------------- chain
-    // St[ct][dt][qq] = S[key_phys(16 dt + 4 g + qq)][v0 + 16 ct + li]
-    f32x4 St[NT][NDT];
-    Frag<uint16_t> bS[NT][NKU_D];
+    const int ct = role - S::kChain0;  // this wave's state tile
+    const int col = v0 + 16 * ct + li;
+    // St[dt][qq] = S[key_phys(16 dt + 4 g + qq)][col]
+    f32x4 St[NDT];
+    Frag<uint16_t> bS[NKU_D];
 #pragma unroll
-    for (int ct = 0; ct < NT; ++ct) {
-      const int col = v0 + 16 * ct + li;
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
+      for (int qq = 0; qq < 4; ++qq)
+        St[dt][qq] = s0 != nullptr ? s0[(int64_t(bh) * DK + key_phys(16 * dt + 4 * g + qq)) * DV + col] : 0.0f;
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq)
-          St[ct][dt][qq] =
-              s0 != nullptr ? s0[(int64_t(bh) * DK + key_phys(16 * dt + 4 * g + qq)) * DV + col] : 0.0f;
-#pragma unroll
-      for (int ku = 0; ku < NKU_D; ++ku) {
-        bS[ct][ku] = acc_frag<uint16_t>(St[ct][2 * ku], St[ct][2 * ku + 1]);
-        bS_buf[ct][ku][lane] = bS[ct][ku].v;
-      }
+    for (int ku = 0; ku < NKU_D; ++ku) {
+      bS[ku] = acc_frag<uint16_t>(St[2 * ku], St[2 * ku + 1]);
+      bS_buf[ct][ku][lane] = bS[ku].v;
     }
     auto step = [&](const uint16_t* __restrict__ cur) {
       const uint16_t* Ks = cur + S::KOFF;
       const uint16_t* Ts = cur + S::TOFF;
       const uint16_t* Vs = cur + S::VOFF;
       sync();  // A
-      // operands that only depend on the chunk: the V tiles and T
-      bf16x4 Vt[NT][NRT];
+      // operands that only depend on the chunk: this tile's V columns and T
+      bf16x4 Vt[NRT];
 #pragma unroll
-      for (int ct = 0; ct < NT; ++ct)
-#pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) {
-          const int j = lane & 15;
-          Vt[ct][rt] = lds_read_tr(Vs + swz_off<BV>(16 * rt + 4 * g + (j >> 2), 16 * ct + 4 * (j & 3)));
-        }
+      for (int rt = 0; rt < NRT; ++rt) {
+        const int j = lane & 15;
+        Vt[rt] = lds_read_tr(Vs + swz_off<BV>(16 * rt + 4 * g + (j >> 2), 16 * ct + 4 * (j & 3)));
+      }
       Frag<uint16_t> Tf[NRT][NKU_C];
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
         for (int ku = 0; ku < NKU_C; ++ku)
           if (32 * ku <= 16 * rt + 15) Tf[rt][ku] = sw_frag<C>(Ts, 16 * rt + li, ku, g);
-      // Y = K S: each K fragment feeds every tile
-      f32x4 Y[NT][NRT];
+      // Y = K S
+      f32x4 Y[NRT];
 #pragma unroll
-      for (int ct = 0; ct < NT; ++ct)
-#pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) Y[ct][rt] = zero4();
+      for (int rt = 0; rt < NRT; ++rt) Y[rt] = zero4();
 #pragma unroll
       for (int ku = 0; ku < NKU_D; ++ku) {
         Frag<uint16_t> Kf[NRT];
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) Kf[rt] = wide_frag<DK>(Ks, 16 * rt + li, ku, g);
 #pragma unroll
-        for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-          for (int ct = 0; ct < NT; ++ct) mma(Y[ct][rt], Kf[rt], bS[ct][ku]);
+        for (int rt = 0; rt < NRT; ++rt) mma(Y[rt], Kf[rt], bS[ku]);
       }
       // D = V - Y, U' = T D, published for the output wave
-      Frag<uint16_t> bU[NT][NKU_C];
 #pragma unroll
-      for (int ct = 0; ct < NT; ++ct) {
+      for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-        for (int rt = 0; rt < NRT; ++rt)
+        for (int qq = 0; qq < 4; ++qq) Y[rt][qq] = static_cast<float>(Vt[rt][qq]) - Y[rt][qq];
+      Frag<uint16_t> bD[NKU_C];
 #pragma unroll
-          for (int qq = 0; qq < 4; ++qq) Y[ct][rt][qq] = static_cast<float>(Vt[ct][rt][qq]) - Y[ct][rt][qq];
-        Frag<uint16_t> bD[NKU_C];
+      for (int ku = 0; ku < NKU_C; ++ku)
+        bD[ku] = acc_frag<uint16_t>(Y[2 * ku], 2 * ku + 1 < NRT ? Y[(2 * ku + 1) % NRT] : zero4());
+      f32x4 U[2 * NKU_C];
 #pragma unroll
-        for (int ku = 0; ku < NKU_C; ++ku)
-          bD[ku] = acc_frag<uint16_t>(Y[ct][2 * ku], 2 * ku + 1 < NRT ? Y[ct][(2 * ku + 1) % NRT] : zero4());
-        f32x4 U[2 * NKU_C];
+      for (int rt = 0; rt < 2 * NKU_C; ++rt) {
+        U[rt] = zero4();
+        if (rt < NRT) {
 #pragma unroll
-        for (int rt = 0; rt < 2 * NKU_C; ++rt) {
-          U[rt] = zero4();
-          if (rt < NRT) {
-#pragma unroll
-            for (int ku = 0; ku < NKU_C; ++ku)
-              if (32 * ku <= 16 * rt + 15) mma(U[rt], Tf[rt][ku], bD[ku]);
-          }
-        }
-#pragma unroll
-        for (int ku = 0; ku < NKU_C; ++ku) {
-          bU[ct][ku] = acc_frag<uint16_t>(U[2 * ku], U[2 * ku + 1]);
-          bU_buf[ct][ku][lane] = bU[ct][ku].v;
+          for (int ku = 0; ku < NKU_C; ++ku)
+            if (32 * ku <= 16 * rt + 15) mma(U[rt], Tf[rt][ku], bD[ku]);
         }
       }
-      // the first K^T fragments are fetched before the barrier
-      constexpr int NH = (NDT + 1) / 2;
-      Frag<uint16_t> KTa[NH][NKU_C];
+      Frag<uint16_t> bU[NKU_C];
 #pragma unroll
-      for (int dt = 0; dt < NH; ++dt)
-#pragma unroll
-        for (int kt = 0; kt < NKU_C; ++kt) KTa[dt][kt] = wide_frag_tr<DK>(Ks, dt, kt, lane);
+      for (int ku = 0; ku < NKU_C; ++ku) {
+        bU[ku] = acc_frag<uint16_t>(U[2 * ku], U[2 * ku + 1]);
+        bU_buf[ct][ku][lane] = bU[ku].v;
+      }
       sync();  // B
-      // S += K^T U', then publish S_{n+1}
-      Frag<uint16_t> KTb[NDT - NH > 0 ? NDT - NH : 1][NKU_C];
+      // S += K^T U' (the K^T fragments are read after the barrier, where the
+      // LDS is less busy), then publish S_{n+1}
+      Frag<uint16_t> KT[NDT][NKU_C];
 #pragma unroll
-      for (int dt = NH; dt < NDT; ++dt)
+      for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int kt = 0; kt < NKU_C; ++kt) KTb[dt - NH][kt] = wide_frag_tr<DK>(Ks, dt, kt, lane);
+        for (int kt = 0; kt < NKU_C; ++kt) KT[dt][kt] = wide_frag_tr<DK>(Ks, dt, kt, lane);
 #pragma unroll
-      for (int dt = 0; dt < NH; ++dt)
+      for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int kt = 0; kt < NKU_C; ++kt)
+        for (int kt = 0; kt < NKU_C; ++kt) mma(St[dt], KT[dt][kt], bU[kt]);
 #pragma unroll
-          for (int ct = 0; ct < NT; ++ct) mma(St[ct][dt], KTa[dt][kt], bU[ct][kt]);
-#pragma unroll
-      for (int dt = NH; dt < NDT; ++dt)
-#pragma unroll
-        for (int kt = 0; kt < NKU_C; ++kt)
-#pragma unroll
-          for (int ct = 0; ct < NT; ++ct) mma(St[ct][dt], KTb[dt - NH][kt], bU[ct][kt]);
-#pragma unroll
-      for (int ct = 0; ct < NT; ++ct)
-#pragma unroll
-        for (int ku = 0; ku < NKU_D; ++ku) {
-          bS[ct][ku] = acc_frag<uint16_t>(St[ct][2 * ku], St[ct][2 * ku + 1]);
-          bS_buf[ct][ku][lane] = bS[ct][ku].v;
-        }
+      for (int ku = 0; ku < NKU_D; ++ku) {
+        bS[ku] = acc_frag<uint16_t>(St[2 * ku], St[2 * ku + 1]);
+        bS_buf[ct][ku][lane] = bS[ku].v;
+      }
     };
     for (int n = 0; n < NC; n += 3) {
       step(slot0);
@@ -277,12 +212,10 @@ __global__ __launch_bounds__(256) void recurrence_v6_kernel(
     }
     if (sfin != nullptr) {
 #pragma unroll
-      for (int ct = 0; ct < NT; ++ct)
+      for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-          for (int qq = 0; qq < 4; ++qq)
-            sfin[(int64_t(bh) * DK + key_phys(16 * dt + 4 * g + qq)) * DV + v0 + 16 * ct + li] = St[ct][dt][qq];
+        for (int qq = 0; qq < 4; ++qq)
+          sfin[(int64_t(bh) * DK + key_phys(16 * dt + 4 * g + qq)) * DV + col] = St[dt][qq];
     }
   } else if (role == S::kOut) {
     // ------------------------------------------------------------- output
@@ -339,7 +272,7 @@ __global__ __launch_bounds__(256) void recurrence_v6_kernel(
       if (n + 1 < NC) step(slot1, n + 1);
       if (n + 2 < NC) step(slot2, n + 2);
     }
-  } else {
+  } else if (role == S::kP) {
     // ------------------------------------------------------------------ P
     auto step = [&](const uint16_t* __restrict__ cur) {
       const uint16_t* Qs = cur + S::QOFF;
@@ -387,12 +320,12 @@ __global__ __launch_bounds__(256) void recurrence_v6_kernel(
 }
 
 // Shapes: d_k in {32, 64, 128}, chunk in {32, 64}, value block 16 or 32.
-inline bool v6_supported(int DK, int C, int BV) {
+inline bool roles_supported(int DK, int C, int BV) {
   return (DK == 32 || DK == 64 || DK == 128) && (C == 32 || C == 64) && (BV == 16 || BV == 32);
 }
 
 template <int DK, int C, int BV>
-hipError_t recurrence_v6_launch_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+hipError_t recurrence_roles_launch_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                      const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
                                      int B, int H, int64_t L, int DV, hipStream_t stream) {
   const int NC = int((L + C - 1) / C);
@@ -401,37 +334,37 @@ hipError_t recurrence_v6_launch_impl(const uint16_t* q, const uint16_t* k, const
   const int nwg = BH * NVB;
   if (nwg == 0) return hipSuccess;
   const int remap = (BH % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((recurrence_v6_kernel<DK, C, BV>), dim3(unsigned(nwg)), dim3(V6Shape<DK, C, BV>::THREADS),
+  hipLaunchKernelGGL((recurrence_roles_kernel<DK, C, BV>), dim3(unsigned(nwg)), dim3(RolesShape<DK, C, BV>::THREADS),
                      0, stream, q, k, v, tws, s0, o, sfin, H, L, NC, DV, NVB, remap);
   return hipGetLastError();
 }
 
 template <int DK, int C>
-hipError_t recurrence_v6_bv(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* tws,
+hipError_t recurrence_roles_bv(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* tws,
                             const float* s0, uint16_t* o, float* sfin, int B, int H, int64_t L, int DV,
                             int BV, hipStream_t s) {
   switch (BV) {
-    case 16: return recurrence_v6_launch_impl<DK, C, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, s);
-    case 32: return recurrence_v6_launch_impl<DK, C, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, s);
+    case 16: return recurrence_roles_launch_impl<DK, C, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, s);
+    case 32: return recurrence_roles_launch_impl<DK, C, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, s);
   }
   return hipErrorInvalidValue;
 }
 
-inline hipError_t launch_recurrence_v6(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+inline hipError_t launch_recurrence_roles(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                        const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
                                        int B, int H, int64_t L, int DK, int DV, int C, int BV,
                                        hipStream_t s) {
   if (C == 32) {
     switch (DK) {
-      case 32: return recurrence_v6_bv<32, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, s);
-      case 64: return recurrence_v6_bv<64, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, s);
-      case 128: return recurrence_v6_bv<128, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, s);
+      case 32: return recurrence_roles_bv<32, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, s);
+      case 64: return recurrence_roles_bv<64, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, s);
+      case 128: return recurrence_roles_bv<128, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, s);
     }
   } else if (C == 64) {
     switch (DK) {
-      case 32: return recurrence_v6_bv<32, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, s);
-      case 64: return recurrence_v6_bv<64, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, s);
-      case 128: return recurrence_v6_bv<128, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, s);
+      case 32: return recurrence_roles_bv<32, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, s);
+      case 64: return recurrence_roles_bv<64, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, s);
+      case 128: return recurrence_roles_bv<128, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, s);
     }
   }
   return hipErrorInvalidValue;

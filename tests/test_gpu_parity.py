@@ -114,7 +114,7 @@ def test_tiny_fp32_workload():
     _check_forward(inp, w.chunk, "tiny_fp32")
 
 
-@pytest.mark.parametrize("impl", ["v7", "v6", "v5", "v4", "v3", "v2"])
+@pytest.mark.parametrize("impl", ["roles", "tile", "generic"])
 @pytest.mark.parametrize("bv", ["16", "32", "64"])
 @pytest.mark.parametrize("dk,chunk", [(128, 64), (64, 32), (32, 64)])
 def test_value_block_widths_agree(bv, impl, dk, chunk, monkeypatch):
@@ -176,7 +176,7 @@ def test_ut_transform_bf16_wy_identity(dk, C, monkeypatch):
     bt = torch.tensor(beta, dtype=torch.float32).to(torch.bfloat16).cuda()
     K64, B64 = to_f64(kt), to_f64(bt)
     Ts = {}
-    for impl in ("v2", "v1"):
+    for impl in ("wave", "workgroup"):
         monkeypatch.setenv("EFLA_UT_IMPL", impl)
         _, T = efla.efla_chunk_ut_transform(kt, bt, chunk=C)
         torch.cuda.synchronize()
@@ -198,7 +198,7 @@ def test_ut_transform_bf16_wy_identity(dk, C, monkeypatch):
                     lhs = np.eye(dk) - Kc.T @ Tn[:v, :v] @ Kc
                     assert normwise(lhs, prod[0, 0]) <= 1e-2, (impl, b, h, n, normwise(lhs, prod[0, 0]))
     # the two kernels agree up to fp32 summation order and bf16 rounding of T
-    assert normwise(Ts["v2"], Ts["v1"]) <= 1e-2
+    assert normwise(Ts["wave"], Ts["workgroup"]) <= 1e-2
 
 
 # ---------------------------------------------------------------------------
