@@ -59,6 +59,15 @@ def _load():
         lib.oracle_step.restype = ctypes.c_int
         lib.oracle_step.argtypes = [_D, _D, _D, _D, _D, _D, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        lib.oracle_coeff_rule.restype = ctypes.c_int
+        lib.oracle_coeff_rule.argtypes = [_D, _D, _D, _D, ctypes.c_int64, ctypes.c_int, ctypes.c_int]
+        lib.oracle_forward_rule.restype = ctypes.c_int
+        lib.oracle_forward_rule.argtypes = [_D, _D, _D, _D, _D, _D, _D, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        lib.oracle_step_rule.restype = ctypes.c_int
+        lib.oracle_step_rule.argtypes = [_D, _D, _D, _D, _D, _D, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -83,7 +92,18 @@ def alpha(beta: float, lam: float) -> float:
     return float(_load().oracle_alpha(float(beta), float(lam)))
 
 
-def coeff(k, beta):
+# update rules: the exact flow (Method step 3) or one explicit Euler step of
+# length beta, the delta rule of DeltaNet (alpha = beta)
+RULES = {"exact": 0, "euler": 1}
+
+
+def _rule(rule) -> int:
+    if rule not in RULES:
+        raise ValueError(f"unknown rule {rule!r}")
+    return RULES[rule]
+
+
+def coeff(k, beta, rule: str = "exact"):
     """lambda = ||k||^2 and alpha per token.  k [..., dk], beta [...]."""
     k = _f64(k)
     beta = _f64(beta)
@@ -93,13 +113,13 @@ def coeff(k, beta):
         raise ValueError("beta must have one value per key row")
     lam = np.empty(n, np.float64)
     alp = np.empty(n, np.float64)
-    rc = _load().oracle_coeff(_p(k), _p(beta), _p(lam), _p(alp), n, dk)
+    rc = _load().oracle_coeff_rule(_p(k), _p(beta), _p(lam), _p(alp), n, dk, _rule(rule))
     if rc != 0:
         raise RuntimeError(f"oracle_coeff failed ({rc})")
     return lam.reshape(k.shape[:-1]), alp.reshape(k.shape[:-1])
 
 
-def forward(q, k, v, beta, s0=None, nthreads: int | None = None):
+def forward(q, k, v, beta, s0=None, nthreads: int | None = None, rule: str = "exact"):
     """Token-by-token EFLA over q,k [B,L,H,dk], v [B,L,H,dv], beta [B,L,H].
 
     s0 [B,H,dk,dv] or None (zeros).  Returns (o [B,L,H,dv], S_L [B,H,dk,dv]).
@@ -116,14 +136,14 @@ def forward(q, k, v, beta, s0=None, nthreads: int | None = None):
     o = np.empty((B, L, H, dv), np.float64)
     sf = np.empty((B, H, dk, dv), np.float64)
     nt = default_threads() if nthreads is None else int(nthreads)
-    rc = _load().oracle_forward(_p(q), _p(k), _p(v), _p(beta), _p(s0), _p(o),
-                                _p(sf), B, H, L, dk, dv, nt)
+    rc = _load().oracle_forward_rule(_p(q), _p(k), _p(v), _p(beta), _p(s0), _p(o),
+                                     _p(sf), B, H, L, dk, dv, nt, _rule(rule))
     if rc != 0:
         raise RuntimeError(f"oracle_forward failed ({rc})")
     return o, sf
 
 
-def step(q, k, v, beta, state):
+def step(q, k, v, beta, state, rule: str = "exact"):
     """One decode step.  q,k [N,H,dk], v [N,H,dv], beta [N,H], state [N,H,dk,dv].
 
     Returns (o [N,H,dv], new_state); the input state is not modified.
@@ -135,7 +155,7 @@ def step(q, k, v, beta, state):
     if st.shape != (N, H, dk, dv) or beta.shape != (N, H) or q.shape != k.shape:
         raise ValueError("shape mismatch")
     o = np.empty((N, H, dv), np.float64)
-    rc = _load().oracle_step(_p(q), _p(k), _p(v), _p(beta), _p(st), _p(o), N, H, dk, dv)
+    rc = _load().oracle_step_rule(_p(q), _p(k), _p(v), _p(beta), _p(st), _p(o), N, H, dk, dv, _rule(rule))
     if rc != 0:
         raise RuntimeError(f"oracle_step failed ({rc})")
     return o, st

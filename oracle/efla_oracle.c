@@ -15,6 +15,12 @@
  *   S_t      = (I - alpha_t k_t k_t^T) S_{t-1} + alpha_t k_t v_t^T
  *   o_t      = S_t^T q_t                    (readout: post-update state)
  *
+ * The _rule variants also run the other rule the pages discuss: one explicit
+ * Euler step of length beta_t of the same ODE, which the pages identify with
+ * the delta rule of DeltaNet (Problem statement; Key Contributions 1).  Its
+ * coefficient is alpha_t = beta_t; everything else is identical.
+ *   rule 0 = exact flow,  rule 1 = explicit Euler (delta rule)
+ *
  * alpha is evaluated as beta * (-expm1(-x)/x) with x = beta*lambda: the same
  * quantity written without cancellation; at lambda == 0 it takes its limit,
  * beta.  The
@@ -51,11 +57,18 @@ double oracle_alpha(double beta, double lam)
     return beta * (-expm1(-x) / x);
 }
 
-/* lambda_t = ||k_t||^2 and alpha_t for n_tok tokens of dimension dk. */
-int oracle_coeff(const double *k, const double *beta, double *lam_out,
-                 double *alpha_out, int64_t n_tok, int dk)
+/* alpha_t under a rule: the exact flow above, or the explicit Euler step of
+ * length beta_t, whose coefficient is beta_t itself. */
+static double rule_alpha(double beta, double lam, int rule)
 {
-    if (n_tok < 0 || dk <= 0)
+    return rule == 1 ? beta : oracle_alpha(beta, lam);
+}
+
+/* lambda_t = ||k_t||^2 and alpha_t for n_tok tokens of dimension dk. */
+int oracle_coeff_rule(const double *k, const double *beta, double *lam_out,
+                      double *alpha_out, int64_t n_tok, int dk, int rule)
+{
+    if (n_tok < 0 || dk <= 0 || (rule != 0 && rule != 1))
         return 1;
     for (int64_t t = 0; t < n_tok; ++t) {
         const double *kt = k + t * (int64_t)dk;
@@ -64,9 +77,15 @@ int oracle_coeff(const double *k, const double *beta, double *lam_out,
             lam += kt[i] * kt[i];
         if (lam_out)
             lam_out[t] = lam;
-        alpha_out[t] = oracle_alpha(beta[t], lam);
+        alpha_out[t] = rule_alpha(beta[t], lam, rule);
     }
     return 0;
+}
+
+int oracle_coeff(const double *k, const double *beta, double *lam_out,
+                 double *alpha_out, int64_t n_tok, int dk)
+{
+    return oracle_coeff_rule(k, beta, lam_out, alpha_out, n_tok, dk, 0);
 }
 
 /*
@@ -76,12 +95,13 @@ int oracle_coeff(const double *k, const double *beta, double *lam_out,
  *   o  : output row of length dv (may be NULL)
  */
 static void efla_token(double *S, double *kS, const double *q, const double *k,
-                       const double *v, double beta, double *o, int dk, int dv)
+                       const double *v, double beta, double *o, int dk, int dv,
+                       int rule)
 {
     double lam = 0.0;
     for (int i = 0; i < dk; ++i)
         lam += k[i] * k[i];
-    const double a = oracle_alpha(beta, lam);
+    const double a = rule_alpha(beta, lam, rule);
 
     /* k^T S_{t-1}  (a row vector over value dims) */
     for (int j = 0; j < dv; ++j) {
@@ -111,7 +131,7 @@ typedef struct {
     double *o, *s_final;
     int B, H, dk, dv;
     int64_t L;
-    int nthreads, tid;
+    int nthreads, tid, rule;
 } fwd_job;
 
 static void *fwd_worker(void *arg)
@@ -136,7 +156,7 @@ static void *fwd_worker(void *arg)
             const int64_t row = (b * J->L + t) * J->H + h;
             efla_token(S, kS, J->q + row * J->dk, J->k + row * J->dk,
                        J->v + row * J->dv, J->beta[row],
-                       J->o ? J->o + row * J->dv : NULL, J->dk, J->dv);
+                       J->o ? J->o + row * J->dv : NULL, J->dk, J->dv, J->rule);
         }
         if (J->s_final)
             memcpy(J->s_final + u * sdim, S, sizeof(double) * (size_t)sdim);
@@ -151,12 +171,12 @@ static void *fwd_worker(void *arg)
  * s0 may be NULL (zero initial state); o and s_final may be NULL.
  * s_final may alias s0.  Returns 0 on success.
  */
-int oracle_forward(const double *q, const double *k, const double *v,
-                   const double *beta, const double *s0, double *o,
-                   double *s_final, int B, int H, int64_t L, int dk, int dv,
-                   int nthreads)
+int oracle_forward_rule(const double *q, const double *k, const double *v,
+                        const double *beta, const double *s0, double *o,
+                        double *s_final, int B, int H, int64_t L, int dk, int dv,
+                        int nthreads, int rule)
 {
-    if (B < 0 || H < 0 || L < 0 || dk <= 0 || dv <= 0)
+    if (B < 0 || H < 0 || L < 0 || dk <= 0 || dv <= 0 || (rule != 0 && rule != 1))
         return 1;
     const int64_t units = (int64_t)B * H;
     if (nthreads < 1)
@@ -172,7 +192,7 @@ int oracle_forward(const double *q, const double *k, const double *v,
     }
     int rc = 0;
     for (int i = 0; i < nthreads; ++i) {
-        fwd_job J = {q, k, v, beta, s0, o, s_final, B, H, dk, dv, L, nthreads, i};
+        fwd_job J = {q, k, v, beta, s0, o, s_final, B, H, dk, dv, L, nthreads, i, rule};
         jobs[i] = J;
     }
     int started = 0;
@@ -196,15 +216,24 @@ int oracle_forward(const double *q, const double *k, const double *v,
     return rc;
 }
 
+int oracle_forward(const double *q, const double *k, const double *v,
+                   const double *beta, const double *s0, double *o,
+                   double *s_final, int B, int H, int64_t L, int dk, int dv,
+                   int nthreads)
+{
+    return oracle_forward_rule(q, k, v, beta, s0, o, s_final, B, H, L, dk, dv,
+                               nthreads, 0);
+}
+
 /*
  * One decode step: a single token per (n, h) applied to the state in place.
  *   q, k [N, H, dk]   v, o [N, H, dv]   beta [N, H]   state [N, H, dk, dv]
  */
-int oracle_step(const double *q, const double *k, const double *v,
-                const double *beta, double *state, double *o, int N, int H,
-                int dk, int dv)
+int oracle_step_rule(const double *q, const double *k, const double *v,
+                     const double *beta, double *state, double *o, int N, int H,
+                     int dk, int dv, int rule)
 {
-    if (N < 0 || H < 0 || dk <= 0 || dv <= 0)
+    if (N < 0 || H < 0 || dk <= 0 || dv <= 0 || (rule != 0 && rule != 1))
         return 1;
     double *kS = (double *)malloc(sizeof(double) * (size_t)dv);
     if (!kS)
@@ -212,7 +241,14 @@ int oracle_step(const double *q, const double *k, const double *v,
     const int64_t sdim = (int64_t)dk * dv;
     for (int64_t u = 0; u < (int64_t)N * H; ++u)
         efla_token(state + u * sdim, kS, q + u * dk, k + u * dk, v + u * dv,
-                   beta[u], o ? o + u * dv : NULL, dk, dv);
+                   beta[u], o ? o + u * dv : NULL, dk, dv, rule);
     free(kS);
     return 0;
+}
+
+int oracle_step(const double *q, const double *k, const double *v,
+                const double *beta, double *state, double *o, int N, int H,
+                int dk, int dv)
+{
+    return oracle_step_rule(q, k, v, beta, state, o, N, H, dk, dv, 0);
 }

@@ -25,6 +25,13 @@ MUTATIONS = {
     "readout_uses_key": ("acc += S[(int64_t)i * dv + j] * q[i];", "acc += S[(int64_t)i * dv + j] * k[i];"),
     "swapped_batch_head_layout": ("const int64_t row = (b * J->L + t) * J->H + h;",
                                   "const int64_t row = (h * J->L + t) * J->B + b;"),
+    "rule_ignored": ("return rule == 1 ? beta : oracle_alpha(beta, lam);",
+                     "return oracle_alpha(beta, lam);"),
+    "rules_swapped": ("return rule == 1 ? beta : oracle_alpha(beta, lam);",
+                      "return rule == 0 ? beta : oracle_alpha(beta, lam);"),
+    "euler_half_step": ("return rule == 1 ? beta : oracle_alpha(beta, lam);",
+                        "return rule == 1 ? 0.5 * beta : oracle_alpha(beta, lam);"),
+    "forward_drops_rule": ("B, H, dk, dv, L, nthreads, i, rule};", "B, H, dk, dv, L, nthreads, i, 0};"),
     "initial_state_ignored": ("memcpy(S, J->s0 + u * sdim, sizeof(double) * (size_t)sdim);",
                               "memset(S, 0, sizeof(double) * (size_t)sdim);"),
 }
@@ -41,6 +48,11 @@ PINS = [
     pins.test_P6_stiff_limit_overwrites,
     pins.test_P9_scalar_closed_form,
     pins.test_forward_threads_and_layout,
+    pins.test_P11_euler_coefficient_is_beta,
+    pins.test_P11_euler_projection_invariants,
+    pins.test_P11_euler_unit_step_overwrites_and_large_step_expands,
+    pins.test_P11_euler_orthonormal_keys_store_values,
+    pins.test_P11_euler_forward_equals_euler_steps_and_limits,
 ]
 
 

@@ -361,3 +361,117 @@ def test_empty_sequence():
     o, sf = oracle.forward(q, k, v, beta, s0)
     assert o.shape == (2, 0, 3, 4)
     assert np.array_equal(sf, s0)
+
+
+# ---------------------------------------------------------------------------
+# P11: the Euler (delta-rule) update, the baseline the pages compare against
+# (Problem statement; Key Contributions 1: the delta rule is one explicit Euler
+# step of the same ODE).  A rank-1 update is fixed by what it does along k and
+# on the complement of k, so these pins determine the Euler step completely:
+#   k^T S_t - v^T = (1 - beta lambda) (k^T S_{t-1} - v^T),   u^T S_t = u^T S_{t-1} (u _|_ k).
+# At beta*lambda = 1 the key direction is overwritten by v; at beta*lambda = 3
+# the Euler step expands the error by 2 where the exact flow contracts it by e^-3.
+# ---------------------------------------------------------------------------
+
+def _one_step(S0, k, v, beta, rule):
+    dk, dv = S0.shape
+    _, S1 = oracle.step(np.zeros((1, 1, dk)), k[None, None], v[None, None],
+                        np.array([[beta]]), S0[None, None], rule=rule)
+    return S1[0, 0]
+
+
+def test_P11_euler_coefficient_is_beta():
+    rng = _rng(151)
+    k = rng.standard_normal((9, 5)) * rng.uniform(0.1, 4.0, (9, 1))
+    beta = rng.uniform(0.0, 5.0, 9)
+    lam_e, a_e = oracle.coeff(k, beta, rule="euler")
+    lam_x, a_x = oracle.coeff(k, beta)
+    assert np.array_equal(a_e, beta)
+    assert np.array_equal(lam_e, lam_x)
+    assert not np.allclose(a_e, a_x)
+
+
+def test_P11_euler_projection_invariants():
+    rng = _rng(152)
+    dk, dv = 7, 5
+    for trial in range(20):
+        S0 = rng.standard_normal((dk, dv))
+        k = rng.uniform(0.2, 3.0) * rng.standard_normal(dk)
+        v = rng.standard_normal(dv)
+        lam = float(k @ k)
+        # beta*lambda spread over (0, 1), around 1 and the expanding range up to 3
+        beta = rng.uniform(0.0, 3.0) / lam
+        S1 = _one_step(S0, k, v, beta, "euler")
+        lhs = k @ S1 - v
+        rhs = (1.0 - beta * lam) * (k @ S0 - v)
+        tol = 1e-12 * max(1.0, np.abs(k @ S0).max(), np.abs(v).max())
+        assert np.abs(lhs - rhs).max() <= tol
+        u = rng.standard_normal(dk)
+        u -= (u @ k) / (k @ k) * k
+        assert np.abs(u @ S1 - u @ S0).max() <= 1e-12 * max(1.0, np.abs(u @ S0).max())
+
+
+def test_P11_euler_unit_step_overwrites_and_large_step_expands():
+    rng = _rng(153)
+    dk, dv = 6, 4
+    S0 = rng.standard_normal((dk, dv))
+    k = rng.standard_normal(dk)
+    v = rng.standard_normal(dv)
+    lam = float(k @ k)
+    err0 = k @ S0 - v
+    S1 = _one_step(S0, k, v, 1.0 / lam, "euler")
+    assert np.abs(k @ S1 - v).max() <= 1e-12 * max(1.0, np.abs(v).max(), np.abs(err0).max())
+    S3 = _one_step(S0, k, v, 3.0 / lam, "euler")
+    X3 = _one_step(S0, k, v, 3.0 / lam, "exact")
+    assert np.allclose(k @ S3 - v, -2.0 * err0, rtol=1e-12, atol=1e-12)
+    assert np.allclose(k @ X3 - v, math.exp(-3.0) * err0, rtol=1e-12, atol=1e-12)
+
+
+def test_P11_euler_orthonormal_keys_store_values():
+    """Associative memory with orthonormal keys and beta = 1: each Euler write
+    stores v_t under k_t exactly and leaves the other keys' slots alone, so
+    S_L = S_0 projected off span(K) + sum_t k_t v_t^T (keys used once each)."""
+    rng = _rng(154)
+    dk, dv, L = 8, 3, 5
+    Qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    keys = Qm[:, :L].T                       # L orthonormal rows
+    v = rng.standard_normal((L, dv))
+    q = rng.standard_normal((L, dk))
+    S0 = rng.standard_normal((dk, dv))
+    o, sf = oracle.forward(q[None, :, None], keys[None, :, None], v[None, :, None],
+                           np.ones((1, L, 1)), S0[None, None], rule="euler")
+    P_perp = np.eye(dk) - keys.T @ keys
+    want = P_perp @ S0 + keys.T @ v
+    assert np.abs(sf[0, 0] - want).max() <= 1e-12
+    for t in range(L):
+        assert np.abs(keys[t] @ sf[0, 0] - v[t]).max() <= 1e-12
+        # after token t: the first t+1 keys hold their values, the rest still hold S0
+        St = np.eye(dk) @ S0 - keys[:t + 1].T @ (keys[:t + 1] @ S0) + keys[:t + 1].T @ v[:t + 1]
+        assert np.abs(o[0, t, 0] - St.T @ q[t]).max() <= 1e-12
+
+
+def test_P11_euler_forward_equals_euler_steps_and_limits():
+    q, k, v, beta, s0 = _rand_inputs(155, 2, 21, 3, 5, 4)
+    o, sf = oracle.forward(q, k, v, beta, s0, rule="euler")
+    st = s0.copy()
+    for t in range(21):
+        ot, st = oracle.step(q[:, t], k[:, t], v[:, t], beta[:, t], st, rule="euler")
+        assert np.array_equal(ot, o[:, t])
+    assert np.array_equal(st, sf)
+    # the two rules differ at O((beta lambda)^2) per token and agree as beta -> 0
+    ox, _ = oracle.forward(q, k, v, beta, s0)
+    assert np.abs(ox - o).max() > 1e-3
+    prev = None
+    for scale in [1e-2, 1e-3, 1e-4]:
+        oe, _ = oracle.forward(q, k, v, beta * scale, s0, rule="euler")
+        ox, _ = oracle.forward(q, k, v, beta * scale, s0)
+        d = np.abs(oe - ox).max()
+        if prev is not None:
+            # one decade less beta, two decades less gap: second order
+            assert 0.01 / 1.5 <= d / prev <= 0.01 * 1.5
+        prev = d
+
+
+def test_rule_argument_is_checked():
+    with pytest.raises(ValueError):
+        oracle.coeff(np.ones((1, 2)), np.ones(1), rule="rk4")
