@@ -11,6 +11,8 @@ Prints ONE JSON line.  Besides the contract fields it carries:
                 from HIP events recorded around it inside the timed loop
   stages        per-stage event times and the whole-path fraction of peak
   decode        efla_step at [256, 16, 128, 128] (fp32 state), back to back
+  euler         the same path under the Euler (delta-rule) update, alpha = beta,
+                timed the same way: the pages' throughput comparison of the two
   cpu_baseline  the fp64 oracle on the same workload, on this host's cores
 """
 from __future__ import annotations
@@ -41,6 +43,7 @@ def parse_args():
     ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-euler", action="store_true")
     ap.add_argument("--cold-iters", type=int, default=10,
                     help="extra iterations each preceded by a 1 GiB cache-flushing write")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -180,6 +183,31 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    euler = None
+    if not args.no_euler:
+        eut, erec = efla.prepare_chunk_stages(q, k, v, beta, s0, o, s_final, ws, chunk=w.chunk, rule="euler")
+        for _ in range(args.warmup):
+            eut()
+            erec()
+        torch.cuda.synchronize()
+
+        def loop_us(stages):
+            # K back-to-back passes between two events, no events in between
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(K):
+                for f in stages:
+                    f()
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1e3 / K
+
+        xus, eus = loop_us((ut, rec)), loop_us((eut, erec))
+        euler = {"rule": "euler (alpha = beta)", "path_us": round(eus, 2),
+                 "tokens_per_s": round(tokens / (eus / 1e6), 1),
+                 "exact_path_us_same_loop": round(xus, 2),
+                 "exact_over_euler_time": round(xus / eus, 4)}
+
     decode = None
     if not args.no_decode:
         wd = W.get("decode_1p3b")
@@ -249,6 +277,7 @@ def main():
                    "head_tokens_per_s": round(n_ht / (ms_per_step / 1e3), 1)},
         "cold": cold,
         "decode": decode,
+        "euler": euler,
         "cpu_baseline": cpu,
         "kernel_source_sha256_16": kernel_source_hash(),
     }

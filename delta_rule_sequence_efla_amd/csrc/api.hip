@@ -12,6 +12,7 @@ namespace {
 bool valid_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool valid_chunk(int c) { return c == 16 || c == 32 || c == 64; }
 bool valid_dtype(efla_dtype dt) { return dt == EFLA_F32 || dt == EFLA_BF16; }
+bool valid_rule(efla_rule r) { return r == EFLA_RULE_EXACT || r == EFLA_RULE_EULER; }
 size_t elem_bytes(efla_dtype dt) { return dt == EFLA_BF16 ? 2 : 4; }
 constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
 
@@ -84,7 +85,12 @@ const char* efla_status_string(efla_status s) {
 
 efla_status efla_coeff(const void* k, const void* beta, float* lambda, float* alpha, int64_t n_tok,
                        int d_k, efla_dtype dtype, void* stream) {
-  if (n_tok < 0 || !valid_dtype(dtype)) return EFLA_ERR_INVALID_ARG;
+  return efla_coeff_rule(k, beta, lambda, alpha, n_tok, d_k, dtype, EFLA_RULE_EXACT, stream);
+}
+
+efla_status efla_coeff_rule(const void* k, const void* beta, float* lambda, float* alpha, int64_t n_tok,
+                            int d_k, efla_dtype dtype, efla_rule rule, void* stream) {
+  if (n_tok < 0 || !valid_dtype(dtype) || !valid_rule(rule)) return EFLA_ERR_INVALID_ARG;
   if (!valid_dim(d_k)) return EFLA_ERR_UNSUPPORTED;
   if (n_tok == 0) return EFLA_OK;
   if (k == nullptr || beta == nullptr || alpha == nullptr) return EFLA_ERR_INVALID_ARG;
@@ -93,9 +99,9 @@ efla_status efla_coeff(const void* k, const void* beta, float* lambda, float* al
   if (dtype == EFLA_BF16)
     return from_hip(efla::launch_coeff<uint16_t>(static_cast<const uint16_t*>(k),
                                                  static_cast<const uint16_t*>(beta), lambda, alpha,
-                                                 n_tok, d_k, s));
+                                                 n_tok, d_k, int(rule), s));
   return from_hip(efla::launch_coeff<float>(static_cast<const float*>(k), static_cast<const float*>(beta),
-                                            lambda, alpha, n_tok, d_k, s));
+                                            lambda, alpha, n_tok, d_k, int(rule), s));
 }
 
 size_t efla_chunk_fwd_workspace_size(int B, int H, int64_t L, int d_k, int d_v, int chunk,
@@ -108,6 +114,14 @@ size_t efla_chunk_fwd_workspace_size(int B, int H, int64_t L, int d_k, int d_v, 
 efla_status efla_chunk_ut_transform(const void* k, const void* beta, int B, int H, int64_t L, int d_k,
                                     int chunk, efla_dtype dtype, void* workspace,
                                     size_t workspace_bytes, void* stream) {
+  return efla_chunk_ut_transform_rule(k, beta, B, H, L, d_k, chunk, dtype, EFLA_RULE_EXACT, workspace,
+                                      workspace_bytes, stream);
+}
+
+efla_status efla_chunk_ut_transform_rule(const void* k, const void* beta, int B, int H, int64_t L, int d_k,
+                                         int chunk, efla_dtype dtype, efla_rule rule, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  if (!valid_rule(rule)) return EFLA_ERR_INVALID_ARG;
   const efla_status st = check_chunk_shape(B, H, L, d_k, 16, chunk, dtype);
   if (st != EFLA_OK) return st;
   if (L == 0) return EFLA_OK;
@@ -122,16 +136,17 @@ efla_status efla_chunk_ut_transform(const void* k, const void* beta, int B, int 
   const bool want_wg = impl && strcmp(impl, "workgroup") == 0;
   if (dtype == EFLA_BF16 && !want_wg && efla::ut_wave_bf16_supported(d_k, chunk))
     return from_hip(efla::launch_ut_wave_bf16(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(beta),
-                                              static_cast<uint16_t*>(workspace), B, H, L, d_k, chunk, s));
+                                              static_cast<uint16_t*>(workspace), B, H, L, d_k, chunk,
+                                              int(rule), s));
   if (dtype == EFLA_BF16)
     return from_hip(efla::launch_ut_transform<uint16_t>(static_cast<const uint16_t*>(k),
                                                         static_cast<const uint16_t*>(beta),
                                                         static_cast<uint16_t*>(workspace), B, H, L, d_k,
-                                                        chunk, s));
+                                                        chunk, int(rule), s));
   return from_hip(efla::launch_ut_transform<float>(static_cast<const float*>(k),
                                                    static_cast<const float*>(beta),
                                                    static_cast<float*>(workspace), B, H, L, d_k, chunk,
-                                                   s));
+                                                   int(rule), s));
 }
 
 efla_status efla_chunk_recurrence(const void* q, const void* k, const void* v, const float* s0, void* o,
@@ -188,6 +203,15 @@ const char* efla_chunk_recurrence_kernel(int d_k, int d_v, int chunk, efla_dtype
 efla_status efla_chunk_fwd(const void* q, const void* k, const void* v, const void* beta, const float* s0,
                            void* o, float* s_final, int B, int H, int64_t L, int d_k, int d_v, int chunk,
                            efla_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return efla_chunk_fwd_rule(q, k, v, beta, s0, o, s_final, B, H, L, d_k, d_v, chunk, dtype, EFLA_RULE_EXACT,
+                             workspace, workspace_bytes, stream);
+}
+
+efla_status efla_chunk_fwd_rule(const void* q, const void* k, const void* v, const void* beta,
+                                const float* s0, void* o, float* s_final, int B, int H, int64_t L, int d_k,
+                                int d_v, int chunk, efla_dtype dtype, efla_rule rule, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!valid_rule(rule)) return EFLA_ERR_INVALID_ARG;
   const efla_status st = check_chunk_shape(B, H, L, d_k, d_v, chunk, dtype);
   if (st != EFLA_OK) return st;
   if (L > 0) {
@@ -196,8 +220,8 @@ efla_status efla_chunk_fwd(const void* q, const void* k, const void* v, const vo
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return EFLA_ERR_INVALID_ARG;
     const size_t need = efla_chunk_fwd_workspace_size(B, H, L, d_k, d_v, chunk, dtype);
     if (workspace == nullptr || workspace_bytes < need) return EFLA_ERR_WORKSPACE;
-    const efla_status s1 =
-        efla_chunk_ut_transform(k, beta, B, H, L, d_k, chunk, dtype, workspace, workspace_bytes, stream);
+    const efla_status s1 = efla_chunk_ut_transform_rule(k, beta, B, H, L, d_k, chunk, dtype, rule, workspace,
+                                                        workspace_bytes, stream);
     if (s1 != EFLA_OK) return s1;
   }
   return efla_chunk_recurrence(q, k, v, s0, o, s_final, B, H, L, d_k, d_v, chunk, dtype, workspace,
@@ -206,7 +230,13 @@ efla_status efla_chunk_fwd(const void* q, const void* k, const void* v, const vo
 
 efla_status efla_step(const void* q, const void* k, const void* v, const void* beta, float* state, void* o,
                       int N, int H, int d_k, int d_v, efla_dtype dtype, void* stream) {
-  if (N < 0 || H < 0 || !valid_dtype(dtype)) return EFLA_ERR_INVALID_ARG;
+  return efla_step_rule(q, k, v, beta, state, o, N, H, d_k, d_v, dtype, EFLA_RULE_EXACT, stream);
+}
+
+efla_status efla_step_rule(const void* q, const void* k, const void* v, const void* beta, float* state,
+                           void* o, int N, int H, int d_k, int d_v, efla_dtype dtype, efla_rule rule,
+                           void* stream) {
+  if (N < 0 || H < 0 || !valid_dtype(dtype) || !valid_rule(rule)) return EFLA_ERR_INVALID_ARG;
   if (!valid_dim(d_k) || !valid_dim(d_v)) return EFLA_ERR_UNSUPPORTED;
   const int64_t units = int64_t(N) * H;
   if (units == 0) return EFLA_OK;
@@ -218,10 +248,10 @@ efla_status efla_step(const void* q, const void* k, const void* v, const void* b
   if (dtype == EFLA_BF16)
     return from_hip(efla::launch_step<uint16_t>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-        static_cast<const uint16_t*>(beta), state, static_cast<uint16_t*>(o), units, d_k, d_v, s));
+        static_cast<const uint16_t*>(beta), state, static_cast<uint16_t*>(o), units, d_k, d_v, int(rule), s));
   return from_hip(efla::launch_step<float>(static_cast<const float*>(q), static_cast<const float*>(k),
                                            static_cast<const float*>(v), static_cast<const float*>(beta),
-                                           state, static_cast<float*>(o), units, d_k, d_v, s));
+                                           state, static_cast<float*>(o), units, d_k, d_v, int(rule), s));
 }
 
 }  // extern "C"

@@ -95,7 +95,7 @@ template <typename T, int DK, int C>
 __global__ __launch_bounds__(kThreads) void ut_transform_kernel(const T* __restrict__ k,
                                                                 const T* __restrict__ beta,
                                                                 T* __restrict__ tws, int H,
-                                                                int64_t L, int NC) {
+                                                                int64_t L, int NC, int rule) {
   constexpr int DKP = round_up(DK, 32), CP = round_up(C, 32);
   constexpr int NRT = C / 16, NKU_D = DKP / 32;
   constexpr int KP = DKP + (sizeof(T) == 2 ? 8 : 4);
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(kThreads) void ut_transform_kernel(const T* __restr
     }
   }
   __syncthreads();
-  if (tid < C) alpha_s[tid] = (tid < valid) ? efla_alpha(bt, lam_s[tid]) : 0.0f;
+  if (tid < C) alpha_s[tid] = (tid < valid) ? efla_alpha_rule(bt, lam_s[tid], rule) : 0.0f;
   __syncthreads();
 
   // Diagonal 16x16 blocks of X: forward substitution, one lane per column:
@@ -481,13 +481,13 @@ __global__ __launch_bounds__(kThreads) void recurrence_kernel(
 }
 
 template <typename T, int DK, int C>
-hipError_t ut_transform_launch_impl(const T* k, const T* beta, T* tws, int B, int H, int64_t L,
+hipError_t ut_transform_launch_impl(const T* k, const T* beta, T* tws, int B, int H, int64_t L, int rule,
                                     hipStream_t stream) {
   const int NC = int((L + C - 1) / C);
   const int64_t nwg = int64_t(B) * H * NC;
   if (nwg == 0) return hipSuccess;
   hipLaunchKernelGGL((ut_transform_kernel<T, DK, C>), dim3(unsigned(nwg)), dim3(kThreads), 0, stream,
-                     k, beta, tws, H, L, NC);
+                     k, beta, tws, H, L, NC, rule);
   return hipGetLastError();
 }
 
@@ -507,24 +507,24 @@ hipError_t recurrence_launch_impl(const T* q, const T* k, const T* v, const T* t
 }
 
 template <typename T, int DK>
-hipError_t ut_dispatch_c(const T* k, const T* beta, T* tws, int B, int H, int64_t L, int C,
+hipError_t ut_dispatch_c(const T* k, const T* beta, T* tws, int B, int H, int64_t L, int C, int rule,
                          hipStream_t s) {
   switch (C) {
-    case 16: return ut_transform_launch_impl<T, DK, 16>(k, beta, tws, B, H, L, s);
-    case 32: return ut_transform_launch_impl<T, DK, 32>(k, beta, tws, B, H, L, s);
-    case 64: return ut_transform_launch_impl<T, DK, 64>(k, beta, tws, B, H, L, s);
+    case 16: return ut_transform_launch_impl<T, DK, 16>(k, beta, tws, B, H, L, rule, s);
+    case 32: return ut_transform_launch_impl<T, DK, 32>(k, beta, tws, B, H, L, rule, s);
+    case 64: return ut_transform_launch_impl<T, DK, 64>(k, beta, tws, B, H, L, rule, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename T>
 hipError_t launch_ut_transform(const T* k, const T* beta, T* tws, int B, int H, int64_t L, int DK,
-                               int C, hipStream_t s) {
+                               int C, int rule, hipStream_t s) {
   switch (DK) {
-    case 16: return ut_dispatch_c<T, 16>(k, beta, tws, B, H, L, C, s);
-    case 32: return ut_dispatch_c<T, 32>(k, beta, tws, B, H, L, C, s);
-    case 64: return ut_dispatch_c<T, 64>(k, beta, tws, B, H, L, C, s);
-    case 128: return ut_dispatch_c<T, 128>(k, beta, tws, B, H, L, C, s);
+    case 16: return ut_dispatch_c<T, 16>(k, beta, tws, B, H, L, C, rule, s);
+    case 32: return ut_dispatch_c<T, 32>(k, beta, tws, B, H, L, C, rule, s);
+    case 64: return ut_dispatch_c<T, 64>(k, beta, tws, B, H, L, C, rule, s);
+    case 128: return ut_dispatch_c<T, 128>(k, beta, tws, B, H, L, C, rule, s);
   }
   return hipErrorInvalidValue;
 }

@@ -61,6 +61,13 @@ __device__ __forceinline__ float efla_alpha(float beta, float lam) {
   return beta * (-expm1f(-x) / x);
 }
 
+// The coefficient under an update rule: rule 0 is the exact flow above; rule 1
+// is one explicit Euler step of length beta (the delta-rule / DeltaNet update
+// the pages contrast EFLA with), whose coefficient is beta itself.
+__device__ __forceinline__ float efla_alpha_rule(float beta, float lam, int rule) {
+  return rule == 1 ? beta : efla_alpha(beta, lam);
+}
+
 // ---- operand fragments ------------------------------------------------------
 template <typename T> struct Frag;
 template <> struct Frag<uint16_t> { bf16x8 v; };

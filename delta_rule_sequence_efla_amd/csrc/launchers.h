@@ -8,16 +8,16 @@
 namespace efla {
 
 template <typename T>
-hipError_t launch_coeff(const T* k, const T* beta, float* lam, float* alpha, int64_t n, int DK,
+hipError_t launch_coeff(const T* k, const T* beta, float* lam, float* alpha, int64_t n, int DK, int rule,
                         hipStream_t s);
 
 template <typename T>
 hipError_t launch_step(const T* q, const T* k, const T* v, const T* beta, float* state, T* o,
-                       int64_t units, int DK, int DV, hipStream_t s);
+                       int64_t units, int DK, int DV, int rule, hipStream_t s);
 
 template <typename T>
 hipError_t launch_ut_transform(const T* k, const T* beta, T* tws, int B, int H, int64_t L, int DK,
-                               int C, hipStream_t stream);
+                               int C, int rule, hipStream_t stream);
 
 template <typename T>
 hipError_t launch_recurrence(const T* q, const T* k, const T* v, const T* tws, const float* s0,
@@ -45,6 +45,6 @@ hipError_t launch_recurrence_roles_bf16(const uint16_t* q, const uint16_t* k, co
 // {32, 64, 128}, chunk in {32, 64}.
 bool ut_wave_bf16_supported(int DK, int C);
 hipError_t launch_ut_wave_bf16(const uint16_t* k, const uint16_t* beta, uint16_t* tws, int B, int H, int64_t L,
-                               int DK, int C, hipStream_t s);
+                               int DK, int C, int rule, hipStream_t s);
 
 }  // namespace efla

@@ -15,7 +15,8 @@ template <typename T, int DK, int DV>
 __global__ __launch_bounds__(kThreads) void step_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                         const T* __restrict__ v,
                                                         const T* __restrict__ beta,
-                                                        float* __restrict__ state, T* __restrict__ o) {
+                                                        float* __restrict__ state, T* __restrict__ o,
+                                                        int rule) {
   constexpr int NCQ = DV / 4;
   constexpr int NRG = kThreads / NCQ;
   constexpr int RPT = cdiv(DK, NRG);
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const T* __restrict__ q,
       kq += __shfl_xor(kq, off);
     }
     if (tid == 0) {
-      const float a = efla_alpha(to_f32(beta[u]), lam);
+      const float a = efla_alpha_rule(to_f32(beta[u]), lam, rule);
       coef[0] = a;
       coef[1] = a * kq;
     }
@@ -97,7 +98,7 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const T* __restrict__ q,
 template <typename T, int DK>
 __global__ __launch_bounds__(kThreads) void coeff_kernel(const T* __restrict__ k, const T* __restrict__ beta,
                                                          float* __restrict__ lam_out,
-                                                         float* __restrict__ alpha, int64_t n) {
+                                                         float* __restrict__ alpha, int64_t n, int rule) {
   const int64_t t = int64_t(blockIdx.x) * kThreads + threadIdx.x;
   if (t >= n) return;
   const T* kt = k + t * DK;
@@ -107,72 +108,72 @@ __global__ __launch_bounds__(kThreads) void coeff_kernel(const T* __restrict__ k
     lam = fmaf(x, x, lam);
   }
   if (lam_out != nullptr) lam_out[t] = lam;
-  alpha[t] = efla_alpha(to_f32(beta[t]), lam);
+  alpha[t] = efla_alpha_rule(to_f32(beta[t]), lam, rule);
 }
 
 template <typename T, int DK, int DV>
 static hipError_t step_impl(const T* q, const T* k, const T* v, const T* beta, float* state, T* o,
-                            int64_t units, hipStream_t s) {
+                            int64_t units, int rule, hipStream_t s) {
   hipLaunchKernelGGL((step_kernel<T, DK, DV>), dim3(unsigned(units)), dim3(kThreads), 0, s, q, k, v,
-                     beta, state, o);
+                     beta, state, o, rule);
   return hipGetLastError();
 }
 
 template <typename T, int DK>
 static hipError_t step_dv(const T* q, const T* k, const T* v, const T* beta, float* state, T* o,
-                          int64_t units, int DV, hipStream_t s) {
+                          int64_t units, int DV, int rule, hipStream_t s) {
   switch (DV) {
-    case 16: return step_impl<T, DK, 16>(q, k, v, beta, state, o, units, s);
-    case 32: return step_impl<T, DK, 32>(q, k, v, beta, state, o, units, s);
-    case 64: return step_impl<T, DK, 64>(q, k, v, beta, state, o, units, s);
-    case 128: return step_impl<T, DK, 128>(q, k, v, beta, state, o, units, s);
+    case 16: return step_impl<T, DK, 16>(q, k, v, beta, state, o, units, rule, s);
+    case 32: return step_impl<T, DK, 32>(q, k, v, beta, state, o, units, rule, s);
+    case 64: return step_impl<T, DK, 64>(q, k, v, beta, state, o, units, rule, s);
+    case 128: return step_impl<T, DK, 128>(q, k, v, beta, state, o, units, rule, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename T>
 hipError_t launch_step(const T* q, const T* k, const T* v, const T* beta, float* state, T* o,
-                       int64_t units, int DK, int DV, hipStream_t s) {
+                       int64_t units, int DK, int DV, int rule, hipStream_t s) {
   if (units == 0) return hipSuccess;
   switch (DK) {
-    case 16: return step_dv<T, 16>(q, k, v, beta, state, o, units, DV, s);
-    case 32: return step_dv<T, 32>(q, k, v, beta, state, o, units, DV, s);
-    case 64: return step_dv<T, 64>(q, k, v, beta, state, o, units, DV, s);
-    case 128: return step_dv<T, 128>(q, k, v, beta, state, o, units, DV, s);
+    case 16: return step_dv<T, 16>(q, k, v, beta, state, o, units, DV, rule, s);
+    case 32: return step_dv<T, 32>(q, k, v, beta, state, o, units, DV, rule, s);
+    case 64: return step_dv<T, 64>(q, k, v, beta, state, o, units, DV, rule, s);
+    case 128: return step_dv<T, 128>(q, k, v, beta, state, o, units, DV, rule, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename T, int DK>
-static hipError_t coeff_impl(const T* k, const T* beta, float* lam, float* alpha, int64_t n,
+static hipError_t coeff_impl(const T* k, const T* beta, float* lam, float* alpha, int64_t n, int rule,
                              hipStream_t s) {
   const int64_t blocks = (n + kThreads - 1) / kThreads;
   hipLaunchKernelGGL((coeff_kernel<T, DK>), dim3(unsigned(blocks)), dim3(kThreads), 0, s, k, beta, lam,
-                     alpha, n);
+                     alpha, n, rule);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_coeff(const T* k, const T* beta, float* lam, float* alpha, int64_t n, int DK,
+hipError_t launch_coeff(const T* k, const T* beta, float* lam, float* alpha, int64_t n, int DK, int rule,
                         hipStream_t s) {
   if (n == 0) return hipSuccess;
   switch (DK) {
-    case 16: return coeff_impl<T, 16>(k, beta, lam, alpha, n, s);
-    case 32: return coeff_impl<T, 32>(k, beta, lam, alpha, n, s);
-    case 64: return coeff_impl<T, 64>(k, beta, lam, alpha, n, s);
-    case 128: return coeff_impl<T, 128>(k, beta, lam, alpha, n, s);
+    case 16: return coeff_impl<T, 16>(k, beta, lam, alpha, n, rule, s);
+    case 32: return coeff_impl<T, 32>(k, beta, lam, alpha, n, rule, s);
+    case 64: return coeff_impl<T, 64>(k, beta, lam, alpha, n, rule, s);
+    case 128: return coeff_impl<T, 128>(k, beta, lam, alpha, n, rule, s);
   }
   return hipErrorInvalidValue;
 }
 
 template hipError_t launch_step<float>(const float*, const float*, const float*, const float*, float*,
-                                       float*, int64_t, int, int, hipStream_t);
+                                       float*, int64_t, int, int, int, hipStream_t);
 template hipError_t launch_step<uint16_t>(const uint16_t*, const uint16_t*, const uint16_t*,
-                                          const uint16_t*, float*, uint16_t*, int64_t, int, int,
+                                          const uint16_t*, float*, uint16_t*, int64_t, int, int, int,
                                           hipStream_t);
-template hipError_t launch_coeff<float>(const float*, const float*, float*, float*, int64_t, int,
+template hipError_t launch_coeff<float>(const float*, const float*, float*, float*, int64_t, int, int,
                                         hipStream_t);
 template hipError_t launch_coeff<uint16_t>(const uint16_t*, const uint16_t*, float*, float*, int64_t,
-                                           int, hipStream_t);
+                                           int, int, hipStream_t);
 
 }  // namespace efla

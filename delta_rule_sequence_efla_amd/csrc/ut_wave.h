@@ -58,7 +58,7 @@ template <int DK, int C>
 __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict__ k,
                                                       const uint16_t* __restrict__ beta,
                                                       uint16_t* __restrict__ tws, int H, int64_t L, int NC,
-                                                      int64_t nchunks) {
+                                                      int64_t nchunks, int rule) {
   using S = UtWaveShape<DK, C>;
   constexpr int NRT = S::NRT, NKU = S::NKU, GP = S::GP, BLK = S::BLK, TP = S::TP;
   __shared__ __align__(16) unsigned char scratch_all[S::WAVES][S::SCRATCH];
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict
   wave_lds_order();
   if (lane < C) {
     const float lam = Gs[(lane >> 4) * BLK + (lane & 15) * GP + (lane & 15)];
-    as[lane] = (lane < valid) ? efla_alpha(bt, lam) : 0.0f;
+    as[lane] = (lane < valid) ? efla_alpha_rule(bt, lam, rule) : 0.0f;
   }
   wave_lds_order();
 
@@ -208,29 +208,29 @@ inline bool ut_wave_supported(int DK, int C) { return (DK == 32 || DK == 64 || D
 
 template <int DK, int C>
 hipError_t ut_wave_launch_impl(const uint16_t* k, const uint16_t* beta, uint16_t* tws, int B, int H, int64_t L,
-                               hipStream_t stream) {
+                               int rule, hipStream_t stream) {
   const int NC = int((L + C - 1) / C);
   const int64_t nchunks = int64_t(B) * H * NC;
   if (nchunks == 0) return hipSuccess;
   const int64_t nwg = (nchunks + UtWaveShape<DK, C>::WAVES - 1) / UtWaveShape<DK, C>::WAVES;
   hipLaunchKernelGGL((ut_wave_kernel<DK, C>), dim3(unsigned(nwg)), dim3(64 * UtWaveShape<DK, C>::WAVES), 0, stream,
-                     k, beta, tws, H, L, NC, nchunks);
+                     k, beta, tws, H, L, NC, nchunks, rule);
   return hipGetLastError();
 }
 
 inline hipError_t launch_ut_wave(const uint16_t* k, const uint16_t* beta, uint16_t* tws, int B, int H, int64_t L,
-                                 int DK, int C, hipStream_t s) {
+                                 int DK, int C, int rule, hipStream_t s) {
   if (C == 32) {
     switch (DK) {
-      case 32: return ut_wave_launch_impl<32, 32>(k, beta, tws, B, H, L, s);
-      case 64: return ut_wave_launch_impl<64, 32>(k, beta, tws, B, H, L, s);
-      case 128: return ut_wave_launch_impl<128, 32>(k, beta, tws, B, H, L, s);
+      case 32: return ut_wave_launch_impl<32, 32>(k, beta, tws, B, H, L, rule, s);
+      case 64: return ut_wave_launch_impl<64, 32>(k, beta, tws, B, H, L, rule, s);
+      case 128: return ut_wave_launch_impl<128, 32>(k, beta, tws, B, H, L, rule, s);
     }
   } else if (C == 64) {
     switch (DK) {
-      case 32: return ut_wave_launch_impl<32, 64>(k, beta, tws, B, H, L, s);
-      case 64: return ut_wave_launch_impl<64, 64>(k, beta, tws, B, H, L, s);
-      case 128: return ut_wave_launch_impl<128, 64>(k, beta, tws, B, H, L, s);
+      case 32: return ut_wave_launch_impl<32, 64>(k, beta, tws, B, H, L, rule, s);
+      case 64: return ut_wave_launch_impl<64, 64>(k, beta, tws, B, H, L, rule, s);
+      case 128: return ut_wave_launch_impl<128, 64>(k, beta, tws, B, H, L, rule, s);
     }
   }
   return hipErrorInvalidValue;

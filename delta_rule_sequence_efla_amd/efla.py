@@ -61,6 +61,15 @@ def lib() -> ctypes.CDLL:
                                             _i, _i, _vp, _sz, _vp]
         L.efla_step.restype = _i
         L.efla_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]
+        L.efla_coeff_rule.restype = _i
+        L.efla_coeff_rule.argtypes = [_vp, _vp, _vp, _vp, _i64, _i, _i, _i, _vp]
+        L.efla_chunk_fwd_rule.restype = _i
+        L.efla_chunk_fwd_rule.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i64, _i, _i, _i,
+                                          _i, _i, _vp, _sz, _vp]
+        L.efla_chunk_ut_transform_rule.restype = _i
+        L.efla_chunk_ut_transform_rule.argtypes = [_vp, _vp, _i, _i, _i64, _i, _i, _i, _i, _vp, _sz, _vp]
+        L.efla_step_rule.restype = _i
+        L.efla_step_rule.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]
         _lib = L
     return _lib
 
@@ -75,6 +84,17 @@ def efla_status_string(status: int) -> str:
 def efla_chunk_recurrence_kernel(d_k: int, d_v: int, chunk: int, dtype) -> str:
     """Base name of the recurrence kernel the library launches for these sizes."""
     return lib().efla_chunk_recurrence_kernel(int(d_k), int(d_v), int(chunk), _code(dtype)).decode()
+
+
+# update rules of include/efla.h: the exact flow, or one explicit Euler step
+# (the delta rule), alpha = beta
+RULES = {"exact": 0, "euler": 1}
+
+
+def _rule(rule) -> int:
+    if rule not in RULES:
+        raise ValueError(f"unknown rule {rule!r}; use 'exact' or 'euler'")
+    return RULES[rule]
 
 
 def _check(status: int, where: str) -> None:
@@ -114,7 +134,7 @@ def _code(dtype) -> int:
     return _DTYPES[dtype]
 
 
-def efla_coeff(k: torch.Tensor, beta: torch.Tensor, want_lambda: bool = True):
+def efla_coeff(k: torch.Tensor, beta: torch.Tensor, want_lambda: bool = True, rule: str = "exact"):
     """lambda = ||k||^2 and alpha per key row; k [..., d_k], beta [...] -> fp32."""
     dev = _dev(k, beta, dtype=k.dtype)
     n = k.numel() // k.shape[-1]
@@ -123,8 +143,8 @@ def efla_coeff(k: torch.Tensor, beta: torch.Tensor, want_lambda: bool = True):
     alpha = torch.empty(k.shape[:-1], dtype=torch.float32, device=dev)
     lam = torch.empty_like(alpha) if want_lambda else None
     with torch.cuda.device(dev):
-        _check(lib().efla_coeff(_p(k), _p(beta), _p(lam), _p(alpha), n, k.shape[-1],
-                                _code(k.dtype), _stream(dev)), "efla_coeff")
+        _check(lib().efla_coeff_rule(_p(k), _p(beta), _p(lam), _p(alpha), n, k.shape[-1],
+                                     _code(k.dtype), _rule(rule), _stream(dev)), "efla_coeff")
     return lam, alpha
 
 
@@ -148,7 +168,7 @@ def alloc_workspace(B, H, L, d_k, d_v, chunk, dtype, device) -> torch.Tensor:
 
 
 def efla_chunk_fwd(q, k, v, beta, s0=None, chunk: int = 64, o=None, s_final=None,
-                   workspace=None, want_final: bool = True):
+                   workspace=None, want_final: bool = True, rule: str = "exact"):
     """Chunked EFLA forward.  Returns (o [B,L,H,dv] in q's dtype, S_L fp32 or None)."""
     dev = _dev(q, k, v, beta, o, workspace, dtype=None)
     _dev(q, k, v, beta, o, dtype=q.dtype)
@@ -161,21 +181,21 @@ def efla_chunk_fwd(q, k, v, beta, s0=None, chunk: int = 64, o=None, s_final=None
     if workspace is None:
         workspace = alloc_workspace(B, H, L, dk, dv, chunk, q.dtype, dev)
     with torch.cuda.device(dev):
-        _check(lib().efla_chunk_fwd(_p(q), _p(k), _p(v), _p(beta), _p(s0), _p(o), _p(s_final),
-                                    B, H, L, dk, dv, chunk, _code(q.dtype), _p(workspace),
-                                    workspace.numel(), _stream(dev)), "efla_chunk_fwd")
+        _check(lib().efla_chunk_fwd_rule(_p(q), _p(k), _p(v), _p(beta), _p(s0), _p(o), _p(s_final),
+                                         B, H, L, dk, dv, chunk, _code(q.dtype), _rule(rule), _p(workspace),
+                                         workspace.numel(), _stream(dev)), "efla_chunk_fwd")
     return o, s_final
 
 
-def efla_chunk_ut_transform(k, beta, chunk: int = 64, workspace=None):
+def efla_chunk_ut_transform(k, beta, chunk: int = 64, workspace=None, rule: str = "exact"):
     """Stage 1 only: per-chunk T into the workspace (returned as [B,H,NC,C,C] view)."""
     dev = _dev(k, beta, dtype=k.dtype)
     B, L, H, dk = k.shape
     if workspace is None:
         workspace = alloc_workspace(B, H, L, dk, 16, chunk, k.dtype, dev)
     with torch.cuda.device(dev):
-        _check(lib().efla_chunk_ut_transform(_p(k), _p(beta), B, H, L, dk, chunk, _code(k.dtype),
-                                             _p(workspace), workspace.numel(), _stream(dev)),
+        _check(lib().efla_chunk_ut_transform_rule(_p(k), _p(beta), B, H, L, dk, chunk, _code(k.dtype),
+                                                  _rule(rule), _p(workspace), workspace.numel(), _stream(dev)),
                "efla_chunk_ut_transform")
     nc = (L + chunk - 1) // chunk
     n = B * H * nc * chunk * chunk
@@ -200,7 +220,7 @@ def efla_chunk_recurrence(q, k, v, workspace, s0=None, chunk: int = 64, o=None, 
     return o, s_final
 
 
-def efla_step(q, k, v, beta, state, o=None):
+def efla_step(q, k, v, beta, state, o=None, rule: str = "exact"):
     """One decode step in place on state [N,H,dk,dv] (fp32).  Returns o [N,H,dv]."""
     dev = _dev(q, k, v, beta, o, dtype=q.dtype)
     _dev(state, dtype=torch.float32)
@@ -212,8 +232,8 @@ def efla_step(q, k, v, beta, state, o=None):
     if o is None:
         o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
     with torch.cuda.device(dev):
-        _check(lib().efla_step(_p(q), _p(k), _p(v), _p(beta), _p(state), _p(o), N, H, dk, dv,
-                               _code(q.dtype), _stream(dev)), "efla_step")
+        _check(lib().efla_step_rule(_p(q), _p(k), _p(v), _p(beta), _p(state), _p(o), N, H, dk, dv,
+                                    _code(q.dtype), _rule(rule), _stream(dev)), "efla_step")
     return o
 
 
@@ -233,7 +253,7 @@ class PreparedCall:
             raise EflaError(st, self._where)
 
 
-def prepare_chunk_stages(q, k, v, beta, s0, o, s_final, workspace, chunk: int = 64):
+def prepare_chunk_stages(q, k, v, beta, s0, o, s_final, workspace, chunk: int = 64, rule: str = "exact"):
     """(ut_transform, recurrence) prepared calls: together exactly efla_chunk_fwd."""
     dev = _dev(q, k, v, beta, o, dtype=q.dtype)
     _dev(s0, s_final, dtype=torch.float32)
@@ -241,8 +261,8 @@ def prepare_chunk_stages(q, k, v, beta, s0, o, s_final, workspace, chunk: int = 
     code = _code(q.dtype)
     stream = _stream(dev)
     ws, nbytes = _p(workspace), workspace.numel()
-    ut = PreparedCall(lib().efla_chunk_ut_transform,
-                      (_p(k), _p(beta), B, H, L, dk, chunk, code, ws, nbytes, stream),
+    ut = PreparedCall(lib().efla_chunk_ut_transform_rule,
+                      (_p(k), _p(beta), B, H, L, dk, chunk, code, _rule(rule), ws, nbytes, stream),
                       "efla_chunk_ut_transform", (k, beta, workspace))
     rec = PreparedCall(lib().efla_chunk_recurrence,
                        (_p(q), _p(k), _p(v), _p(s0), _p(o), _p(s_final), B, H, L, dk, dv, chunk,
@@ -251,22 +271,22 @@ def prepare_chunk_stages(q, k, v, beta, s0, o, s_final, workspace, chunk: int = 
     return ut, rec
 
 
-def prepare_chunk_fwd(q, k, v, beta, s0, o, s_final, workspace, chunk: int = 64):
+def prepare_chunk_fwd(q, k, v, beta, s0, o, s_final, workspace, chunk: int = 64, rule: str = "exact"):
     dev = _dev(q, k, v, beta, o, dtype=q.dtype)
     _dev(s0, s_final, dtype=torch.float32)
     B, L, H, dk, dv = _chunk_shapes(q, k, v, beta, s0)
-    return PreparedCall(lib().efla_chunk_fwd,
+    return PreparedCall(lib().efla_chunk_fwd_rule,
                         (_p(q), _p(k), _p(v), _p(beta), _p(s0), _p(o), _p(s_final), B, H, L, dk, dv,
-                         chunk, _code(q.dtype), _p(workspace), workspace.numel(), _stream(dev)),
+                         chunk, _code(q.dtype), _rule(rule), _p(workspace), workspace.numel(), _stream(dev)),
                         "efla_chunk_fwd", (q, k, v, beta, s0, o, s_final, workspace))
 
 
-def prepare_step(q, k, v, beta, state, o):
+def prepare_step(q, k, v, beta, state, o, rule: str = "exact"):
     dev = _dev(q, k, v, beta, o, dtype=q.dtype)
     _dev(state, dtype=torch.float32)
     N, H, dk = k.shape
     dv = v.shape[-1]
-    return PreparedCall(lib().efla_step,
+    return PreparedCall(lib().efla_step_rule,
                         (_p(q), _p(k), _p(v), _p(beta), _p(state), _p(o), N, H, dk, dv,
-                         _code(q.dtype), _stream(dev)),
+                         _code(q.dtype), _rule(rule), _stream(dev)),
                         "efla_step", (q, k, v, beta, state, o))

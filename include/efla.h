@@ -58,13 +58,29 @@ typedef enum efla_dtype {
     EFLA_BF16 = 1  /* bfloat16 q, k, v, beta, o */
 } efla_dtype;
 
+/*
+ * The update rule.  EFLA_RULE_EXACT is the exact flow of Method step 3
+ * (alpha_t = (1 - exp(-beta_t lambda_t)) / lambda_t); every entry point without
+ * a rule argument uses it.  EFLA_RULE_EULER is one explicit Euler step of
+ * length beta_t of the same ODE, which the pages identify with the delta rule
+ * of DeltaNet (Problem statement; Key Contributions 1): alpha_t = beta_t, so
+ *     S_t = (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T.
+ * Both rules share the chunked algebra and every kernel except where alpha is
+ * formed; the _rule entry points below exist to run and time the two side by
+ * side (Experimental Results: EFLA's training throughput matches DeltaNet's).
+ */
+typedef enum efla_rule {
+    EFLA_RULE_EXACT = 0,
+    EFLA_RULE_EULER = 1
+} efla_rule;
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *efla_status_string(efla_status s);
 
 /*
  * Base name of the GPU kernel that efla_chunk_recurrence (and the second
  * stage of efla_chunk_fwd) launches for these sizes, as a profiler lists it
- * (e.g. "recurrence_v5_kernel"); "unsupported" for sizes outside the
+ * (e.g. "recurrence_roles_kernel"); "unsupported" for sizes outside the
  * supported set.  Static string, never NULL; launches nothing.  For profiling
  * and roofline accounting only.
  */
@@ -81,6 +97,11 @@ const char *efla_chunk_recurrence_kernel(int d_k, int d_v, int chunk, efla_dtype
  */
 efla_status efla_coeff(const void *k, const void *beta, float *lambda, float *alpha,
                        int64_t n_tok, int d_k, efla_dtype dtype, void *stream);
+/* efla_coeff under a given rule (EFLA_RULE_EULER: alpha = beta; lambda as above).
+ * An invalid rule is EFLA_ERR_INVALID_ARG. */
+efla_status efla_coeff_rule(const void *k, const void *beta, float *lambda, float *alpha,
+                            int64_t n_tok, int d_k, efla_dtype dtype, efla_rule rule,
+                            void *stream);
 
 /*
  * Bytes of device workspace efla_chunk_fwd needs (0 if L == 0).  The workspace
@@ -110,6 +131,12 @@ efla_status efla_chunk_fwd(const void *q, const void *k, const void *v, const vo
                            int B, int H, int64_t L, int d_k, int d_v, int chunk,
                            efla_dtype dtype, void *workspace, size_t workspace_bytes,
                            void *stream);
+/* efla_chunk_fwd under a given rule (alpha per efla_rule); same workspace. */
+efla_status efla_chunk_fwd_rule(const void *q, const void *k, const void *v, const void *beta,
+                                const float *s0, void *o, float *s_final,
+                                int B, int H, int64_t L, int d_k, int d_v, int chunk,
+                                efla_dtype dtype, efla_rule rule, void *workspace,
+                                size_t workspace_bytes, void *stream);
 
 /*
  * The two stages of efla_chunk_fwd, exposed so that each can be checked and
@@ -124,6 +151,10 @@ efla_status efla_chunk_fwd(const void *q, const void *k, const void *v, const vo
 efla_status efla_chunk_ut_transform(const void *k, const void *beta, int B, int H, int64_t L,
                                     int d_k, int chunk, efla_dtype dtype, void *workspace,
                                     size_t workspace_bytes, void *stream);
+/* efla_chunk_ut_transform under a given rule (the recurrence stage has none). */
+efla_status efla_chunk_ut_transform_rule(const void *k, const void *beta, int B, int H, int64_t L,
+                                         int d_k, int chunk, efla_dtype dtype, efla_rule rule,
+                                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * efla_chunk_recurrence -- the sequential pass over chunks of every (b, h):
@@ -147,6 +178,10 @@ efla_status efla_chunk_recurrence(const void *q, const void *k, const void *v,
 efla_status efla_step(const void *q, const void *k, const void *v, const void *beta,
                       float *state, void *o, int N, int H, int d_k, int d_v,
                       efla_dtype dtype, void *stream);
+/* efla_step under a given rule. */
+efla_status efla_step_rule(const void *q, const void *k, const void *v, const void *beta,
+                           float *state, void *o, int N, int H, int d_k, int d_v,
+                           efla_dtype dtype, efla_rule rule, void *stream);
 
 #ifdef __cplusplus
 }

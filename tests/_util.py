@@ -28,10 +28,10 @@ def dtype_name(t: torch.Tensor) -> str:
     return {torch.float32: "f32", torch.bfloat16: "bf16"}[t.dtype]
 
 
-def oracle_forward(inp: dict, nthreads=None):
+def oracle_forward(inp: dict, nthreads=None, rule="exact"):
     """fp64 oracle on the exact values handed to the GPU."""
     return oracle.forward(to_f64(inp["q"]), to_f64(inp["k"]), to_f64(inp["v"]),
-                          to_f64(inp["beta"]), to_f64(inp.get("s0")), nthreads=nthreads)
+                          to_f64(inp["beta"]), to_f64(inp.get("s0")), nthreads=nthreads, rule=rule)
 
 
 def require_gpu():

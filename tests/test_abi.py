@@ -116,3 +116,26 @@ def test_product_package_does_not_import_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "efla_oracle" not in text, f
+
+
+def test_rule_is_validated_first():
+    """An update rule other than EFLA_RULE_EXACT / EFLA_RULE_EULER is
+    EFLA_ERR_INVALID_ARG on every _rule entry point, before size checks and
+    before the empty-input early return."""
+    L = efla.lib()
+    nul = None
+    for rule, want in [(0, 2), (1, 2), (2, 1), (-1, 1)]:
+        # sizes that are unsupported under a valid rule (d_k 24 / d_v 200)
+        assert L.efla_chunk_fwd_rule(nul, nul, nul, nul, nul, nul, nul, 1, 1, 64, 24, 16, 16, 0, rule,
+                                     nul, 0, nul) == want
+        assert L.efla_chunk_ut_transform_rule(nul, nul, 1, 1, 64, 24, 16, 0, rule, nul, 0, nul) == want
+        assert L.efla_step_rule(nul, nul, nul, nul, nul, nul, 1, 1, 16, 200, 1, rule, nul) == want
+        assert L.efla_coeff_rule(nul, nul, nul, nul, 5, 12, 0, rule, nul) == want
+    # empty inputs: OK under a valid rule, still rejected under a bad one
+    assert L.efla_coeff_rule(nul, nul, nul, nul, 0, 16, 0, 1, nul) == 0
+    assert L.efla_coeff_rule(nul, nul, nul, nul, 0, 16, 0, 3, nul) == 1
+    assert L.efla_step_rule(nul, nul, nul, nul, nul, nul, 0, 4, 16, 16, 0, 1, nul) == 0
+    assert L.efla_step_rule(nul, nul, nul, nul, nul, nul, 0, 4, 16, 16, 0, 3, nul) == 1
+    assert efla.RULES == {"exact": 0, "euler": 1}
+    with pytest.raises(ValueError):
+        efla._rule("rk4")

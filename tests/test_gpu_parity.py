@@ -31,10 +31,11 @@ def _gen(name, **kw):
     return w, W.generate(w, device="cuda", **sizes)
 
 
-def _check_forward(inp, chunk, label, tol=None):
-    o, sf = efla.efla_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["s0"], chunk=chunk)
+def _check_forward(inp, chunk, label, tol=None, rule="exact"):
+    o, sf = efla.efla_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["s0"], chunk=chunk,
+                                rule=rule)
     torch.cuda.synchronize()
-    ro, rs = oracle_forward(inp)
+    ro, rs = oracle_forward(inp, rule=rule)
     tol = tol or TOL[dtype_name(inp["q"])]
     eo, es = normwise(to_f64(o), ro), normwise(to_f64(sf), rs)
     _say(f"[parity] {label}: o err {eo:.3e} (tol {tol['o']}), S err {es:.3e} (tol {tol['s']})")
@@ -199,6 +200,90 @@ def test_ut_transform_bf16_wy_identity(dk, C, monkeypatch):
                     assert normwise(lhs, prod[0, 0]) <= 1e-2, (impl, b, h, n, normwise(lhs, prod[0, 0]))
     # the two kernels agree up to fp32 summation order and bf16 rounding of T
     assert normwise(Ts["wave"], Ts["workgroup"]) <= 1e-2
+
+
+# ---------------------------------------------------------------------------
+# the Euler (delta-rule) update: alpha = beta, same chunked algebra
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_coeff_euler_is_beta(dtype):
+    require_gpu()
+    g = torch.Generator().manual_seed(8)
+    k = (torch.randn(300, 64, generator=g) * 3).to(dtype).cuda()
+    beta = torch.rand(300, generator=g).to(dtype).cuda()
+    lam_e, alp_e = efla.efla_coeff(k, beta, rule="euler")
+    lam_x, _ = efla.efla_coeff(k, beta)
+    torch.cuda.synchronize()
+    assert torch.equal(alp_e, beta.float())          # exact: a conversion, no arithmetic
+    assert torch.equal(lam_e, lam_x)
+    lam_r, alp_r = oracle.coeff(to_f64(k), to_f64(beta), rule="euler")
+    assert np.array_equal(to_f64(alp_e), alp_r)
+
+
+EULER = [
+    # dtype, dk, dv, chunk, L
+    ("f32", 16, 16, 16, 64),
+    ("f32", 64, 32, 32, 75),
+    ("f32", 128, 128, 64, 130),
+    ("bf16", 32, 32, 32, 33),
+    ("bf16", 64, 128, 64, 129),
+    ("bf16", 128, 128, 64, 257),
+    ("bf16", 128, 64, 16, 96),
+]
+
+
+@pytest.mark.parametrize("dt,dk,dv,chunk,L", EULER, ids=lambda x: str(x))
+def test_chunk_fwd_euler_small_shapes(dt, dk, dv, chunk, L):
+    """Normalised keys and beta in (0, 1) keep beta*lambda <= 1, where the Euler
+    step is a contraction too; the tolerance is the exact rule's."""
+    w, inp = _gen("shape_340m", dtype=dt, dk=dk, dv=dv, chunk=chunk, B=2, H=3, L=L,
+                  seed=7000 + dk + dv + chunk + L)
+    o, _ = _check_forward(inp, chunk, f"euler {dt} dk{dk} dv{dv} C{chunk} L{L}", rule="euler")
+    ox, _ = efla.efla_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["s0"], chunk=chunk)
+    torch.cuda.synchronize()
+    assert not torch.equal(o, ox)   # the rule reached the kernels
+
+
+@pytest.mark.parametrize("ut", ["wave", "workgroup"])
+@pytest.mark.parametrize("impl", ["roles", "tile", "generic"])
+def test_euler_every_bf16_kernel(ut, impl, monkeypatch):
+    monkeypatch.setenv("EFLA_UT_IMPL", ut)
+    monkeypatch.setenv("EFLA_RECURRENCE_IMPL", impl)
+    w, inp = _gen("shape_1p3b", B=1, H=4, L=300, seed=71)
+    _check_forward(inp, 64, f"euler ut {ut} recurrence {impl}", rule="euler")
+
+
+def test_euler_stages_and_decode_agree():
+    w, inp = _gen("shape_340m", dtype="f32", B=2, H=2, L=70, dk=32, dv=64, seed=72)
+    q, k, v, beta, s0 = inp["q"], inp["k"], inp["v"], inp["beta"], inp["s0"]
+    o, sf = efla.efla_chunk_fwd(q, k, v, beta, s0, chunk=32, rule="euler")
+    ws, _ = efla.efla_chunk_ut_transform(k, beta, chunk=32, rule="euler")
+    o2, s2 = efla.efla_chunk_recurrence(q, k, v, ws, s0, chunk=32)
+    st = s0.clone()
+    steps = [efla.efla_step(q[:, t].contiguous(), k[:, t].contiguous(), v[:, t].contiguous(),
+                            beta[:, t].contiguous(), st, rule="euler") for t in range(70)]
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o) and torch.equal(s2, sf)
+    assert normwise(to_f64(torch.stack(steps, 1)), to_f64(o)) <= 1e-5
+    assert normwise(to_f64(st), to_f64(sf)) <= 1e-5
+    ro, rs = oracle_forward(inp, rule="euler")
+    assert normwise(to_f64(st), rs) <= 1e-4
+
+
+def test_decode_euler_steps():
+    require_gpu()
+    w = W.get("decode_1p3b")
+    inp = W.generate_decode(w, device="cuda", N=8, steps=4)
+    state = inp["s0"].clone()
+    ref_state = to_f64(inp["s0"])
+    for s in range(4):
+        o = efla.efla_step(inp["q"][s], inp["k"][s], inp["v"][s], inp["beta"][s], state, rule="euler")
+        torch.cuda.synchronize()
+        ro, ref_state = oracle.step(to_f64(inp["q"][s]), to_f64(inp["k"][s]), to_f64(inp["v"][s]),
+                                    to_f64(inp["beta"][s]), ref_state, rule="euler")
+        assert normwise(to_f64(o), ro) <= TOL["bf16"]["o"]
+    assert normwise(to_f64(state), ref_state) <= 1e-4
 
 
 # ---------------------------------------------------------------------------
