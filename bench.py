@@ -37,13 +37,15 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "recurrence_shape_1p3b_traffic.txt
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="shape_1p3b")
     ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-euler", action="store_true")
+    ap.add_argument("--event-every", type=int, default=8,
+                    help="record per-kernel HIP events on one timed step in this many")
     ap.add_argument("--cold-iters", type=int, default=10,
                     help="extra iterations each preceded by a 1 GiB cache-flushing write")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -131,25 +133,34 @@ def main():
         rec()
     torch.cuda.synchronize()
 
-    K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    # Timed region: K back-to-back steps.  Every E-th step is bracketed by
+    # HIP events around each kernel (on the launch stream), which gives the
+    # per-kernel durations; an event between two launches keeps them from
+    # overlapping, so only a sample of the steps carries them.
+    K, E = args.steps, max(1, args.event_every)
+    sampled = list(range(0, K, E))
+    ev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        ev[i][0].record()
-        ut()
-        ev[i][1].record()
-        rec()
-        ev[i][2].record()
+        if i in ev:
+            ev[i][0].record()
+            ut()
+            ev[i][1].record()
+            rec()
+            ev[i][2].record()
+        else:
+            ut()
+            rec()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / K
-    ut_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
-    rec_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
-    path_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in range(K)]
-    rec_avg = sum(rec_ms) / K
-    ut_avg = sum(ut_ms) / K
-    path_avg = sum(path_ms) / K
+    ut_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in sampled]
+    rec_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in sampled]
+    path_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in sampled]
+    rec_avg = sum(rec_ms) / len(sampled)
+    ut_avg = sum(ut_ms) / len(sampled)
+    path_avg = sum(path_ms) / len(sampled)
 
     tokens = w.B * w.L
     value = tokens / (ms_per_step / 1e3)
@@ -267,7 +278,7 @@ def main():
                    "chunk": w.chunk, "state": "fp32", "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": rec_kernel, "avg_us": round(rec_avg * 1e3, 2),
+                     "kernel": rec_kernel, "avg_us": round(rec_avg * 1e3, 2), "event_samples": len(sampled),
                      "algorithmic_bytes": rec_bytes},
         "stages": {"ut_transform_us": round(ut_avg * 1e3, 2), "ut_transform_bytes": ut_bytes,
                    "recurrence_us": round(rec_avg * 1e3, 2),

@@ -10,7 +10,10 @@
 //   * output: Z^T = S^T Q^T and O^T = Z^T + U'^T P^T for all BV columns
 //     (operands of the same fragments swapped, so each lane stores 4
 //     consecutive columns);
-//   * P: P = tril(Q K^T), published through LDS;
+//   * P: P = tril(Q K^T), published through LDS; half of the key dimension
+//     is summed one step early, after barrier B of the step before, where
+//     this wave would otherwise wait (the DMA wave completes chunk n+1 by
+//     then);
 //   * DMA: streams Q, K, T and V into a three-slot LDS ring two chunks ahead
 //     with global_load_lds_dwordx4.  Moving data into LDS runs at well under
 //     64 B/clock per CU and an issuing wavefront stalls while the queue is
@@ -21,9 +24,9 @@
 // P wave).
 // Two barriers per chunk:
 //   A (chunk n in LDS, S_n fragments published)
-//     chains: Y, U' -> publish U'   | output: Z^T        | P: P -> publish | DMA: half of chunk n+2
-//   B (U' and P published)
-//     chains: S update -> publish S | output: O^T, store |                 | DMA: other half
+//     chains: Y, U' -> publish U'   | output: Z^T        | P: finish P_n -> publish | DMA: half of chunk n+2
+//   B (U' and P published, chunk n+1 in LDS)
+//     chains: S update -> publish S | output: O^T, store | P: start P_{n+1}        | DMA: other half
 #pragma once
 
 #include "lds_ring.h"
@@ -94,11 +97,12 @@ __global__ __launch_bounds__(64 * (BV / 16 + 3)) void recurrence_roles_kernel(
                                   (U)uniform_ptr(tws + (int64_t(bh) * NC + n) * C * C),
                                   (U)uniform_ptr(v + r0 * DV + v0), chunk_valid(n)};
     };
-    constexpr int D = S::DMA_COUNT;
+    constexpr int D = S::DMA_COUNT, D0 = S::DMA_COUNT / 2;  // D0: transfers of part 0
     if (NC > 0) dma.issue_part(0, 1, lds_addr_of(slot0), chunk_src(0));
     if (NC > 1) dma.issue_part(0, 1, lds_addr_of(slot1), chunk_src(1));
     auto step = [&](uint16_t* fill, int n) {
       // chunk n is complete once at most chunk n+1's transfers are outstanding
+      // (already true since barrier B of the step before)
       if (n + 1 < NC) wait_vmcnt<D>();
       else wait_vmcnt<0>();
       sync_dma();  // A
@@ -106,6 +110,9 @@ __global__ __launch_bounds__(64 * (BV / 16 + 3)) void recurrence_roles_kernel(
       const auto src = chunk_src(more ? n + 2 : n);
       const uint32_t fa = lds_addr_of(fill);
       if (more) dma.issue_part(0, 2, fa, src);
+      // chunk n+1 complete before barrier B: the P wave starts on it there
+      if (more) wait_vmcnt<D0>();
+      else wait_vmcnt<0>();
       sync_dma();  // B
       if (more) dma.issue_part(1, 2, fa, src);
     };
@@ -274,18 +281,18 @@ __global__ __launch_bounds__(64 * (BV / 16 + 3)) void recurrence_roles_kernel(
     }
   } else if (role == S::kP) {
     // ------------------------------------------------------------------ P
-    auto step = [&](const uint16_t* __restrict__ cur) {
+    // P_n = tril(Q K^T) of chunk n, split over the key dimension: k-units
+    // 0 .. KH-1 after barrier B of step n-1 (chunk n is complete there, and
+    // this wave would otherwise idle), the rest after barrier A of step n.
+    constexpr int KH = NKU_D / 2;
+    // Pt[r][c][qq] = P[16 r + li][16 c + 4 g + qq] for c <= r
+    f32x4 Pt[NRT][NRT];
+    auto accumulate = [&](const uint16_t* __restrict__ cur, int ku0, int ku1) {
       const uint16_t* Qs = cur + S::QOFF;
       const uint16_t* Ks = cur + S::KOFF;
-      sync();  // A
-      // Pt[r][c][qq] = P[16 r + li][16 c + 4 g + qq] for c <= r
-      f32x4 Pt[NRT][NRT];
-#pragma unroll
-      for (int r = 0; r < NRT; ++r)
-#pragma unroll
-        for (int c = 0; c < NRT; ++c) Pt[r][c] = zero4();
 #pragma unroll
       for (int ku = 0; ku < NKU_D; ++ku) {
+        if (ku < ku0 || ku >= ku1) continue;
         Frag<uint16_t> Qf[NRT], Kf[NRT];
 #pragma unroll
         for (int r = 0; r < NRT; ++r) {
@@ -297,6 +304,18 @@ __global__ __launch_bounds__(64 * (BV / 16 + 3)) void recurrence_roles_kernel(
 #pragma unroll
           for (int c = 0; c <= r; ++c) mma(Pt[r][c], Kf[c], Qf[r]);
       }
+    };
+    auto clear = [&]() {
+#pragma unroll
+      for (int r = 0; r < NRT; ++r)
+#pragma unroll
+        for (int c = 0; c < NRT; ++c) Pt[r][c] = zero4();
+    };
+    clear();
+    auto step = [&](const uint16_t* __restrict__ cur, const uint16_t* __restrict__ nxt, int n) {
+      sync();  // A
+      if (n == 0) accumulate(cur, 0, KH);
+      accumulate(cur, KH, NKU_D);
 #pragma unroll
       for (int r = 0; r < NRT; ++r) {
 #pragma unroll
@@ -310,11 +329,13 @@ __global__ __launch_bounds__(64 * (BV / 16 + 3)) void recurrence_roles_kernel(
           }
       }
       sync();  // B
+      clear();
+      if (n + 1 < NC) accumulate(nxt, 0, KH);
     };
     for (int n = 0; n < NC; n += 3) {
-      step(slot0);
-      if (n + 1 < NC) step(slot1);
-      if (n + 2 < NC) step(slot2);
+      step(slot0, slot1, n);
+      if (n + 1 < NC) step(slot1, slot2, n + 1);
+      if (n + 2 < NC) step(slot2, slot0, n + 2);
     }
   }
 }
