@@ -13,6 +13,8 @@ Prints ONE JSON line.  Besides the contract fields it carries:
   decode        efla_step at [256, 16, 128, 128] (fp32 state), back to back
   euler         the same path under the Euler (delta-rule) update, alpha = beta,
                 timed the same way: the pages' throughput comparison of the two
+  varlen        efla_chunk_fwd_varlen on the same 16384 tokens and 16 heads packed
+                as 16 sequences of mixed length (varlen_1p3b)
   cpu_baseline  the fp64 oracle on the same workload, on this host's cores
 """
 from __future__ import annotations
@@ -44,6 +46,7 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-euler", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--event-every", type=int, default=8,
                     help="record per-kernel HIP events on one timed step in this many")
     ap.add_argument("--cold-iters", type=int, default=10,
@@ -219,6 +222,34 @@ def main():
                  "exact_path_us_same_loop": round(xus, 2),
                  "exact_over_euler_time": round(xus / eus, 4)}
 
+    varlen = None
+    if not args.no_varlen:
+        wv = W.get("varlen_1p3b")
+        lengths = W.length_mix(wv.B, wv.L, seed=wv.seed)
+        pv = W.generate_packed(wv, lengths, device=dev)
+        ov = torch.empty_like(pv["v"])
+        sv = torch.empty((wv.B, wv.H, wv.dk, wv.dv), dtype=torch.float32, device=dev)
+        wsv = torch.empty(max(1, efla.efla_chunk_fwd_varlen_workspace_size(wv.B, wv.H, wv.L, wv.dk, wv.dv,
+                                                                           wv.chunk, pv["q"].dtype)),
+                          dtype=torch.uint8, device=dev)
+        fv = efla.prepare_chunk_fwd_varlen(pv["q"], pv["k"], pv["v"], pv["beta"], pv["cu_seqlens"], pv["s0"],
+                                           ov, sv, wsv, chunk=wv.chunk)
+        for _ in range(args.warmup):
+            fv()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(K):
+            fv()
+        b.record()
+        torch.cuda.synchronize()
+        vus = a.elapsed_time(b) * 1e3 / K
+        varlen = {"workload": wv.name, "sequences": wv.B, "tokens": wv.L, "H": wv.H,
+                  "lengths_min_median_max": [min(lengths), sorted(lengths)[len(lengths) // 2], max(lengths)],
+                  "path_us": round(vus, 2), "tokens_per_s": round(wv.L / (vus / 1e6), 1),
+                  "note": "back-to-back calls; the longest sequence bounds the sequential pass"}
+        del pv, ov, sv, wsv, fv
+
     decode = None
     if not args.no_decode:
         wd = W.get("decode_1p3b")
@@ -289,6 +320,7 @@ def main():
         "cold": cold,
         "decode": decode,
         "euler": euler,
+        "varlen": varlen,
         "cpu_baseline": cpu,
         "kernel_source_sha256_16": kernel_source_hash(),
     }

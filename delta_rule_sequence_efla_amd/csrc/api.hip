@@ -68,6 +68,63 @@ RecChoice choose_recurrence(efla_dtype dt, int d_k, int d_v, int chunk) {
   return {Rec::kGeneric, bv};
 }
 
+// Stage 1 launch (arguments already validated).  Dense batch: cu == nullptr;
+// packed batch: N sequences at device offsets cu into L tokens.
+efla_status launch_ut(const void* k, const void* beta, int B, int H, int64_t L, int d_k, int chunk,
+                      efla_dtype dtype, efla_rule rule, void* workspace, const int32_t* cu, int N,
+                      hipStream_t s) {
+  // bf16: one wavefront per chunk (ut_wave.h) where it applies, else one
+  // workgroup per chunk; EFLA_UT_IMPL=workgroup pins the latter for comparisons.
+  const char* impl = getenv("EFLA_UT_IMPL");
+  const bool want_wg = impl && strcmp(impl, "workgroup") == 0;
+  if (dtype == EFLA_BF16 && !want_wg && efla::ut_wave_bf16_supported(d_k, chunk))
+    return from_hip(efla::launch_ut_wave_bf16(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(beta),
+                                              static_cast<uint16_t*>(workspace), B, H, L, d_k, chunk,
+                                              int(rule), cu, N, s));
+  if (dtype == EFLA_BF16)
+    return from_hip(efla::launch_ut_transform<uint16_t>(static_cast<const uint16_t*>(k),
+                                                        static_cast<const uint16_t*>(beta),
+                                                        static_cast<uint16_t*>(workspace), B, H, L, d_k,
+                                                        chunk, int(rule), cu, N, s));
+  return from_hip(efla::launch_ut_transform<float>(static_cast<const float*>(k),
+                                                   static_cast<const float*>(beta),
+                                                   static_cast<float*>(workspace), B, H, L, d_k, chunk,
+                                                   int(rule), cu, N, s));
+}
+
+// Stage 2 launch (arguments already validated).  The one-wavefront-per-tile
+// kernel takes dense batches only; packed batches use the role kernel there.
+efla_status launch_rec(const void* q, const void* k, const void* v, const float* s0, void* o, float* s_final,
+                       int B, int H, int64_t L, int d_k, int d_v, int chunk, efla_dtype dtype,
+                       const void* workspace, const int32_t* cu, int N, hipStream_t s) {
+  RecChoice rc = choose_recurrence(dtype, d_k, d_v, chunk);
+  if (rc.kind == Rec::kTile && cu != nullptr)
+    rc.kind = efla::recurrence_roles_supported(d_k, chunk, rc.bv) ? Rec::kRoles : Rec::kGeneric;
+  if (dtype == EFLA_BF16) {
+    const auto* qb = static_cast<const uint16_t*>(q);
+    const auto* kb = static_cast<const uint16_t*>(k);
+    const auto* vb = static_cast<const uint16_t*>(v);
+    const auto* tb = static_cast<const uint16_t*>(workspace);
+    auto* ob = static_cast<uint16_t*>(o);
+    switch (rc.kind) {
+      case Rec::kRoles:
+        return from_hip(efla::launch_recurrence_roles_bf16(qb, kb, vb, tb, s0, ob, s_final, B, H, L, d_k, d_v,
+                                                           chunk, rc.bv, cu, N, s));
+      case Rec::kTile:
+        return from_hip(efla::launch_recurrence_tile_bf16(qb, kb, vb, tb, s0, ob, s_final, B, H, L, d_k, d_v,
+                                                          chunk, rc.bv, s));
+      case Rec::kGeneric:
+        break;
+    }
+    return from_hip(efla::launch_recurrence<uint16_t>(qb, kb, vb, tb, s0, ob, s_final, B, H, L, d_k, d_v,
+                                                      chunk, rc.bv, cu, N, s));
+  }
+  return from_hip(efla::launch_recurrence<float>(
+      static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
+      static_cast<const float*>(workspace), s0, static_cast<float*>(o), s_final, B, H, L, d_k, d_v, chunk,
+      rc.bv, cu, N, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -129,24 +186,8 @@ efla_status efla_chunk_ut_transform_rule(const void* k, const void* beta, int B,
   const size_t need = efla_chunk_fwd_workspace_size(B, H, L, d_k, 16, chunk, dtype);
   if (workspace == nullptr || workspace_bytes < need) return EFLA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return EFLA_ERR_INVALID_ARG;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  // bf16: one wavefront per chunk (ut_wave.h) where it applies, else one
-  // workgroup per chunk; EFLA_UT_IMPL=workgroup pins the latter for comparisons.
-  const char* impl = getenv("EFLA_UT_IMPL");
-  const bool want_wg = impl && strcmp(impl, "workgroup") == 0;
-  if (dtype == EFLA_BF16 && !want_wg && efla::ut_wave_bf16_supported(d_k, chunk))
-    return from_hip(efla::launch_ut_wave_bf16(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(beta),
-                                              static_cast<uint16_t*>(workspace), B, H, L, d_k, chunk,
-                                              int(rule), s));
-  if (dtype == EFLA_BF16)
-    return from_hip(efla::launch_ut_transform<uint16_t>(static_cast<const uint16_t*>(k),
-                                                        static_cast<const uint16_t*>(beta),
-                                                        static_cast<uint16_t*>(workspace), B, H, L, d_k,
-                                                        chunk, int(rule), s));
-  return from_hip(efla::launch_ut_transform<float>(static_cast<const float*>(k),
-                                                   static_cast<const float*>(beta),
-                                                   static_cast<float*>(workspace), B, H, L, d_k, chunk,
-                                                   int(rule), s));
+  return launch_ut(k, beta, B, H, L, d_k, chunk, dtype, rule, workspace, nullptr, 0,
+                   static_cast<hipStream_t>(stream));
 }
 
 efla_status efla_chunk_recurrence(const void* q, const void* k, const void* v, const float* s0, void* o,
@@ -163,31 +204,8 @@ efla_status efla_chunk_recurrence(const void* q, const void* k, const void* v, c
     if (!aligned16(workspace)) return EFLA_ERR_INVALID_ARG;
   }
   if (L == 0 && s_final == nullptr) return EFLA_OK;
-  const RecChoice rc = choose_recurrence(dtype, d_k, d_v, chunk);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == EFLA_BF16) {
-    const auto* qb = static_cast<const uint16_t*>(q);
-    const auto* kb = static_cast<const uint16_t*>(k);
-    const auto* vb = static_cast<const uint16_t*>(v);
-    const auto* tb = static_cast<const uint16_t*>(workspace);
-    auto* ob = static_cast<uint16_t*>(o);
-    switch (rc.kind) {
-      case Rec::kRoles:
-        return from_hip(efla::launch_recurrence_roles_bf16(qb, kb, vb, tb, s0, ob, s_final, B, H, L, d_k, d_v,
-                                                           chunk, rc.bv, s));
-      case Rec::kTile:
-        return from_hip(efla::launch_recurrence_tile_bf16(qb, kb, vb, tb, s0, ob, s_final, B, H, L, d_k, d_v,
-                                                          chunk, rc.bv, s));
-      case Rec::kGeneric:
-        break;
-    }
-    return from_hip(efla::launch_recurrence<uint16_t>(qb, kb, vb, tb, s0, ob, s_final, B, H, L, d_k, d_v,
-                                                      chunk, rc.bv, s));
-  }
-  return from_hip(efla::launch_recurrence<float>(
-      static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
-      static_cast<const float*>(workspace), s0, static_cast<float*>(o), s_final, B, H, L, d_k, d_v, chunk,
-      rc.bv, s));
+  return launch_rec(q, k, v, s0, o, s_final, B, H, L, d_k, d_v, chunk, dtype, workspace, nullptr, 0,
+                    static_cast<hipStream_t>(stream));
 }
 
 const char* efla_chunk_recurrence_kernel(int d_k, int d_v, int chunk, efla_dtype dtype) {
@@ -255,3 +273,41 @@ efla_status efla_step_rule(const void* q, const void* k, const void* v, const vo
 }
 
 }  // extern "C"
+
+size_t efla_chunk_fwd_varlen_workspace_size(int N, int H, int64_t T, int d_k, int d_v, int chunk,
+                                            efla_dtype dtype) {
+  if (N < 1 || H < 1 || T < 0 || T > INT32_MAX || !valid_dtype(dtype)) return 0;
+  if (!valid_dim(d_k) || !valid_dim(d_v) || !valid_chunk(chunk)) return 0;
+  const int64_t slots = T / chunk + N;  // chunk slots per head
+  if (int64_t(H) * slots > kMaxGrid) return 0;
+  return size_t(H) * size_t(slots) * size_t(chunk) * size_t(chunk) * elem_bytes(dtype);
+}
+
+efla_status efla_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void* beta,
+                                  const int32_t* cu_seqlens, int N, const float* s0, void* o, float* s_final,
+                                  int H, int64_t T, int d_k, int d_v, int chunk, efla_dtype dtype,
+                                  efla_rule rule, void* workspace, size_t workspace_bytes, void* stream) {
+  if (N < 0 || H < 1 || T < 0 || !valid_dtype(dtype) || !valid_rule(rule)) return EFLA_ERR_INVALID_ARG;
+  if (!valid_dim(d_k) || !valid_dim(d_v) || !valid_chunk(chunk)) return EFLA_ERR_UNSUPPORTED;
+  if (T > INT32_MAX) return EFLA_ERR_UNSUPPORTED;  // offsets are int32
+  if (N == 0) return EFLA_OK;
+  if (cu_seqlens == nullptr) return EFLA_ERR_INVALID_ARG;
+  const int64_t slots = T / chunk + N;
+  if (int64_t(N) * H * (d_v / 16) > kMaxGrid || int64_t(H) * slots > kMaxGrid) return EFLA_ERR_UNSUPPORTED;
+  if (T > 0) {
+    if (q == nullptr || k == nullptr || v == nullptr || beta == nullptr || o == nullptr)
+      return EFLA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return EFLA_ERR_INVALID_ARG;
+    const size_t need = efla_chunk_fwd_varlen_workspace_size(N, H, T, d_k, d_v, chunk, dtype);
+    if (workspace == nullptr || workspace_bytes < need) return EFLA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return EFLA_ERR_INVALID_ARG;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T > 0) {
+    const efla_status s1 = launch_ut(k, beta, 1, H, T, d_k, chunk, dtype, rule, workspace, cu_seqlens, N, s);
+    if (s1 != EFLA_OK) return s1;
+  } else if (s_final == nullptr) {
+    return EFLA_OK;
+  }
+  return launch_rec(q, k, v, s0, o, s_final, 1, H, T, d_k, d_v, chunk, dtype, workspace, cu_seqlens, N, s);
+}

@@ -3,8 +3,8 @@
 
 namespace efla {
 template hipError_t launch_ut_transform<float>(const float*, const float*, float*, int, int, int64_t,
-                                               int, int, int, hipStream_t);
+                                               int, int, int, const int32_t*, int, hipStream_t);
 template hipError_t launch_recurrence<float>(const float*, const float*, const float*, const float*,
                                              const float*, float*, float*, int, int, int64_t, int, int,
-                                             int, int, hipStream_t);
+                                             int, int, const int32_t*, int, hipStream_t);
 }  // namespace efla

@@ -95,7 +95,8 @@ template <typename T, int DK, int C>
 __global__ __launch_bounds__(kThreads) void ut_transform_kernel(const T* __restrict__ k,
                                                                 const T* __restrict__ beta,
                                                                 T* __restrict__ tws, int H,
-                                                                int64_t L, int NC, int rule) {
+                                                                int64_t L, int NC, int rule,
+                                                                const int32_t* __restrict__ cu, int N) {
   constexpr int DKP = round_up(DK, 32), CP = round_up(C, 32);
   constexpr int NRT = C / 16, NKU_D = DKP / 32;
   constexpr int KP = DKP + (sizeof(T) == 2 ? 8 : 4);
@@ -105,14 +106,21 @@ __global__ __launch_bounds__(kThreads) void ut_transform_kernel(const T* __restr
   __shared__ __align__(16) float Gs[C * AP];  // strictly lower part of K K^T
   __shared__ __align__(16) float Xs[C * AP];  // X = (I + A)^{-1}, lower blocks
 
-  const int64_t wg = blockIdx.x;
-  const int chunk = int(wg % NC);
-  const int64_t bh = wg / NC;
-  const int64_t b = bh / H, h = bh % H;
+  const int64_t wg = blockIdx.x;  // workspace slot of this workgroup's chunk
+  // slot -> sequence and chunk (dense: wg = (b H + h) NC + chunk)
+  SeqSpan sp;
+  int chunk;
+  const int64_t h = cu == nullptr ? (wg / NC) % H : wg / NC;
+  if (cu == nullptr) {
+    chunk = int(wg % NC);
+    sp = seq_span<C>(nullptr, int(wg / NC / H), h, H, L, NC);
+  } else if (!slot_chunk<C>(cu, N, wg % NC, h, H, L, NC, sp, chunk)) {
+    return;  // a slot no chunk of the packed batch uses (uniform: before any barrier)
+  }
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), li = lane & 15, g = lane >> 4;
   const int64_t t0 = int64_t(chunk) * C;
-  const int valid = int(L - t0 < C ? L - t0 : C);
-  const int64_t row0 = (b * L + t0) * H + h;  // token t0 of this (b, h)
+  const int valid = int(sp.len - t0 < C ? sp.len - t0 : C);
+  const int64_t row0 = (sp.bos + t0) * H + h;  // token t0 of this sequence and head
 
   if constexpr (DK < DKP || C < CP) lds_zero(Ks, CP * KP, tid);
   float bt = 0.0f;
@@ -192,7 +200,7 @@ __global__ __launch_bounds__(kThreads) void ut_transform_kernel(const T* __restr
   // T = X diag(a), lower triangle, zeros above.
   constexpr int VN = Vec16<T>::n;
   constexpr int VPR = C / VN;
-  T* out = tws + (bh * NC + chunk) * int64_t(C) * C;
+  T* out = tws + wg * int64_t(C) * C;
   for (int i = tid; i < C * VPR; i += kThreads) {
     const int t = i / VPR, s0 = (i % VPR) * VN;
     union {
@@ -227,7 +235,8 @@ template <typename T, int DK, int C, int BV>
 __global__ __launch_bounds__(kThreads) void recurrence_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ tws, const float* __restrict__ s0, T* __restrict__ o,
-    float* __restrict__ sfin, int H, int64_t L, int NC, int DV, int NVB, int remap) {
+    float* __restrict__ sfin, int H, int64_t L, int NC, int DV, int NVB, int remap,
+    const int32_t* __restrict__ cu) {
   constexpr int DKP = round_up(DK, 32), CP = round_up(C, 32);
   constexpr int NRT = C / 16, NKU_D = DKP / 32, NKU_C = CP / 32;
   constexpr int NCT = BV / 16, NDP = 4 / NCT;
@@ -262,7 +271,9 @@ __global__ __launch_bounds__(kThreads) void recurrence_kernel(
     bh = x / NVB;
     vb = x % NVB;
   }
-  const int64_t b = bh / H, h = bh % H;
+  const int64_t h = bh % H;
+  const SeqSpan sp = seq_span<C>(cu, bh / H, h, H, L, NC);  // sequence bh / H
+  const int nc = sp.nc;
   const int v0 = vb * BV;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), li = lane & 15, g = lane >> 4;
   const int cw = w % NCT, pw = w / NCT;
@@ -299,12 +310,12 @@ __global__ __launch_bounds__(kThreads) void recurrence_kernel(
   RowStager<T, C, C> st;
   auto load_chunk = [&](int n) {
     const int64_t t0 = int64_t(n) * C;
-    const int valid = int(L - t0 < C ? L - t0 : C);
-    const int64_t row0 = (b * L + t0) * H + h;
+    const int valid = int(sp.len - t0 < C ? sp.len - t0 : C);
+    const int64_t row0 = (sp.bos + t0) * H + h;
     sq.load(q + row0 * DK, qk_stride, valid, tid);
     sk.load(k + row0 * DK, qk_stride, valid, tid);
     sv.load(v + row0 * DV + v0, v_stride, valid, tid);
-    st.load(tws + (int64_t(bh) * NC + n) * C * C, C, C, tid);
+    st.load(tws + (sp.slot0 + n) * C * C, C, C, tid);
   };
   auto store_chunk = [&]() {
     sq.store(Qs, QP, tid);
@@ -314,16 +325,16 @@ __global__ __launch_bounds__(kThreads) void recurrence_kernel(
     st.store(Ts, TP, tid);
   };
 
-  if (NC > 0) load_chunk(0);
+  if (nc > 0) load_chunk(0);
   __syncthreads();  // zero-fill done
-  if (NC > 0) store_chunk();
+  if (nc > 0) store_chunk();
   __syncthreads();
 
-  for (int n = 0; n < NC; ++n) {
+  for (int n = 0; n < nc; ++n) {
     const int64_t t0 = int64_t(n) * C;
-    const int valid = int(L - t0 < C ? L - t0 : C);
-    const int64_t row0 = (b * L + t0) * H + h;
-    if (n + 1 < NC) load_chunk(n + 1);  // in flight during this chunk
+    const int valid = int(sp.len - t0 < C ? sp.len - t0 : C);
+    const int64_t row0 = (sp.bos + t0) * H + h;
+    if (n + 1 < nc) load_chunk(n + 1);  // in flight during this chunk
 
     // partial K S and Q S over this wave's key dims
     f32x4 Y[NRT], Z[NRT];
@@ -461,7 +472,7 @@ __global__ __launch_bounds__(kThreads) void recurrence_kernel(
     }
 
     __syncthreads();  // every wave is done reading this chunk's LDS
-    if (n + 1 < NC) store_chunk();
+    if (n + 1 < nc) store_chunk();
     __syncthreads();
   }
 
@@ -482,49 +493,49 @@ __global__ __launch_bounds__(kThreads) void recurrence_kernel(
 
 template <typename T, int DK, int C>
 hipError_t ut_transform_launch_impl(const T* k, const T* beta, T* tws, int B, int H, int64_t L, int rule,
-                                    hipStream_t stream) {
-  const int NC = int((L + C - 1) / C);
-  const int64_t nwg = int64_t(B) * H * NC;
+                                    const int32_t* cu, int N, hipStream_t stream) {
+  const int NC = cu == nullptr ? int((L + C - 1) / C) : int(L / C) + N;  // chunk slots per sequence / head
+  const int64_t nwg = int64_t(cu == nullptr ? B : 1) * H * NC;
   if (nwg == 0) return hipSuccess;
   hipLaunchKernelGGL((ut_transform_kernel<T, DK, C>), dim3(unsigned(nwg)), dim3(kThreads), 0, stream,
-                     k, beta, tws, H, L, NC, rule);
+                     k, beta, tws, H, L, NC, rule, cu, N);
   return hipGetLastError();
 }
 
 template <typename T, int DK, int C, int BV>
 hipError_t recurrence_launch_impl(const T* q, const T* k, const T* v, const T* tws, const float* s0,
                                   T* o, float* sfin, int B, int H, int64_t L, int DV,
-                                  hipStream_t stream) {
-  const int NC = int((L + C - 1) / C);
-  const int BH = B * H;
+                                  const int32_t* cu, int N, hipStream_t stream) {
+  const int NC = cu == nullptr ? int((L + C - 1) / C) : int(L / C) + N;
+  const int BH = (cu == nullptr ? B : N) * H;
   const int NVB = DV / BV;
   const int nwg = BH * NVB;
   if (nwg == 0) return hipSuccess;
   const int remap = (BH % 8 == 0) ? 1 : 0;
   hipLaunchKernelGGL((recurrence_kernel<T, DK, C, BV>), dim3(unsigned(nwg)), dim3(kThreads), 0, stream,
-                     q, k, v, tws, s0, o, sfin, H, L, NC, DV, NVB, remap);
+                     q, k, v, tws, s0, o, sfin, H, L, NC, DV, NVB, remap, cu);
   return hipGetLastError();
 }
 
 template <typename T, int DK>
 hipError_t ut_dispatch_c(const T* k, const T* beta, T* tws, int B, int H, int64_t L, int C, int rule,
-                         hipStream_t s) {
+                         const int32_t* cu, int N, hipStream_t s) {
   switch (C) {
-    case 16: return ut_transform_launch_impl<T, DK, 16>(k, beta, tws, B, H, L, rule, s);
-    case 32: return ut_transform_launch_impl<T, DK, 32>(k, beta, tws, B, H, L, rule, s);
-    case 64: return ut_transform_launch_impl<T, DK, 64>(k, beta, tws, B, H, L, rule, s);
+    case 16: return ut_transform_launch_impl<T, DK, 16>(k, beta, tws, B, H, L, rule, cu, N, s);
+    case 32: return ut_transform_launch_impl<T, DK, 32>(k, beta, tws, B, H, L, rule, cu, N, s);
+    case 64: return ut_transform_launch_impl<T, DK, 64>(k, beta, tws, B, H, L, rule, cu, N, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename T>
 hipError_t launch_ut_transform(const T* k, const T* beta, T* tws, int B, int H, int64_t L, int DK,
-                               int C, int rule, hipStream_t s) {
+                               int C, int rule, const int32_t* cu, int N, hipStream_t s) {
   switch (DK) {
-    case 16: return ut_dispatch_c<T, 16>(k, beta, tws, B, H, L, C, rule, s);
-    case 32: return ut_dispatch_c<T, 32>(k, beta, tws, B, H, L, C, rule, s);
-    case 64: return ut_dispatch_c<T, 64>(k, beta, tws, B, H, L, C, rule, s);
-    case 128: return ut_dispatch_c<T, 128>(k, beta, tws, B, H, L, C, rule, s);
+    case 16: return ut_dispatch_c<T, 16>(k, beta, tws, B, H, L, C, rule, cu, N, s);
+    case 32: return ut_dispatch_c<T, 32>(k, beta, tws, B, H, L, C, rule, cu, N, s);
+    case 64: return ut_dispatch_c<T, 64>(k, beta, tws, B, H, L, C, rule, cu, N, s);
+    case 128: return ut_dispatch_c<T, 128>(k, beta, tws, B, H, L, C, rule, cu, N, s);
   }
   return hipErrorInvalidValue;
 }
@@ -535,22 +546,24 @@ template <> struct BVSet<float> { static constexpr bool has32 = false, has64 = f
 
 template <typename T, int DK, int C>
 hipError_t rec_dispatch_bv(const T* q, const T* k, const T* v, const T* tws, const float* s0, T* o,
-                           float* sfin, int B, int H, int64_t L, int DV, int BV, hipStream_t s) {
-  if (BV == 16) return recurrence_launch_impl<T, DK, C, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, s);
+                           float* sfin, int B, int H, int64_t L, int DV, int BV, const int32_t* cu, int N,
+                           hipStream_t s) {
+  if (BV == 16) return recurrence_launch_impl<T, DK, C, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, s);
   if constexpr (BVSet<T>::has32)
-    if (BV == 32) return recurrence_launch_impl<T, DK, C, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, s);
+    if (BV == 32) return recurrence_launch_impl<T, DK, C, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, s);
   if constexpr (BVSet<T>::has64)
-    if (BV == 64) return recurrence_launch_impl<T, DK, C, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, s);
+    if (BV == 64) return recurrence_launch_impl<T, DK, C, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, s);
   return hipErrorInvalidValue;
 }
 
 template <typename T, int DK>
 hipError_t rec_dispatch_c(const T* q, const T* k, const T* v, const T* tws, const float* s0, T* o,
-                          float* sfin, int B, int H, int64_t L, int DV, int C, int BV, hipStream_t s) {
+                          float* sfin, int B, int H, int64_t L, int DV, int C, int BV, const int32_t* cu,
+                          int N, hipStream_t s) {
   switch (C) {
-    case 16: return rec_dispatch_bv<T, DK, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, s);
-    case 32: return rec_dispatch_bv<T, DK, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, s);
-    case 64: return rec_dispatch_bv<T, DK, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, s);
+    case 16: return rec_dispatch_bv<T, DK, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, s);
+    case 32: return rec_dispatch_bv<T, DK, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, s);
+    case 64: return rec_dispatch_bv<T, DK, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, s);
   }
   return hipErrorInvalidValue;
 }
@@ -558,12 +571,12 @@ hipError_t rec_dispatch_c(const T* q, const T* k, const T* v, const T* tws, cons
 template <typename T>
 hipError_t launch_recurrence(const T* q, const T* k, const T* v, const T* tws, const float* s0,
                              T* o, float* sfin, int B, int H, int64_t L, int DK, int DV, int C,
-                             int BV, hipStream_t s) {
+                             int BV, const int32_t* cu, int N, hipStream_t s) {
   switch (DK) {
-    case 16: return rec_dispatch_c<T, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, C, BV, s);
-    case 32: return rec_dispatch_c<T, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, C, BV, s);
-    case 64: return rec_dispatch_c<T, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, C, BV, s);
-    case 128: return rec_dispatch_c<T, 128>(q, k, v, tws, s0, o, sfin, B, H, L, DV, C, BV, s);
+    case 16: return rec_dispatch_c<T, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, C, BV, cu, N, s);
+    case 32: return rec_dispatch_c<T, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, C, BV, cu, N, s);
+    case 64: return rec_dispatch_c<T, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, C, BV, cu, N, s);
+    case 128: return rec_dispatch_c<T, 128>(q, k, v, tws, s0, o, sfin, B, H, L, DV, C, BV, cu, N, s);
   }
   return hipErrorInvalidValue;
 }

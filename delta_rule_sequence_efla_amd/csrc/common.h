@@ -160,4 +160,64 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 template <typename T> struct Vec16 { static constexpr int n = 16 / sizeof(T); };
 
+// ---------------------------------------------------------------------------
+// Where the tokens and workspace chunk slots of sequence u live.
+//  * Dense batch [B, L, H, d] (cu == nullptr): u = b, tokens u L .. u L + L - 1
+//    of the token-major rows; the chunks of (u, h) use slots (u H + h) NC + n.
+//  * Packed variable-length batch [T, H, d] with offsets cu[0..N]
+//    (`L` = T): tokens cu[u] .. cu[u+1] - 1; the chunks of (u, h) use slots
+//    h NC + floor(cu[u] / C) + u + n, NC = floor(T / C) + N slots per head.
+//    Sequences get disjoint slot ranges with no prefix sum over the lengths,
+//    because floor(a / C) + ceil(l / C) <= floor((a + l) / C) + 1.
+//    Offsets are clamped into [0, T] (and each end to at least its start), so
+//    malformed offsets give wrong numbers but no access out of bounds.
+struct SeqSpan {
+  int64_t bos;    // first token
+  int64_t len;    // number of tokens
+  int nc;         // number of chunks
+  int64_t slot0;  // workspace slot of chunk 0
+};
+
+__device__ __forceinline__ int64_t clamp_offset(int64_t a, int64_t lo, int64_t hi) {
+  return a < lo ? lo : (a > hi ? hi : a);
+}
+
+template <int C>
+__device__ __forceinline__ SeqSpan seq_span(const int32_t* __restrict__ cu, int u, int64_t h, int H, int64_t L,
+                                            int NC) {
+  SeqSpan s;
+  if (cu == nullptr) {
+    s.bos = int64_t(u) * L;
+    s.len = L;
+    s.nc = NC;
+    s.slot0 = (int64_t(u) * H + h) * NC;
+  } else {
+    const int64_t a = clamp_offset(cu[u], 0, L);
+    const int64_t e = clamp_offset(cu[u + 1], a, L);
+    s.bos = a;
+    s.len = e - a;
+    s.nc = int((s.len + C - 1) / C);
+    s.slot0 = h * NC + a / C + u;
+  }
+  return s;
+}
+
+// Packed batches: slot j (0 .. NC-1) of head h belongs to chunk n of sequence
+// u, found by binary search over the slot offsets floor(cu[u] / C) + u (which
+// increase with u); false for a slot no chunk uses.
+template <int C>
+__device__ __forceinline__ bool slot_chunk(const int32_t* __restrict__ cu, int N, int64_t j, int64_t h, int H,
+                                           int64_t L, int NC, SeqSpan& sp, int& n) {
+  int lo = 0, hi = N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (clamp_offset(cu[mid], 0, L) / C + mid <= j) lo = mid;
+    else hi = mid - 1;
+  }
+  sp = seq_span<C>(cu, lo, h, H, L, NC);
+  const int64_t nn = h * NC + j - sp.slot0;
+  n = int(nn);
+  return nn >= 0 && nn < sp.nc;
+}
+
 }  // namespace efla

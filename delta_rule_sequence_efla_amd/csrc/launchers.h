@@ -1,6 +1,9 @@
 // launchers.h -- host-side launch functions of the EFLA kernels, one set per
 // element type (float, or bf16 carried as uint16_t).  Each returns the HIP
 // error of its launch; argument validation happens in the C ABI layer.
+// Chunked launchers take a dense batch (B sequences of L tokens, cu ==
+// nullptr) or a packed variable-length batch (N sequences with device
+// offsets cu[0..N] into L tokens; B is then ignored), see SeqSpan.
 #pragma once
 
 #include "common.h"
@@ -17,16 +20,16 @@ hipError_t launch_step(const T* q, const T* k, const T* v, const T* beta, float*
 
 template <typename T>
 hipError_t launch_ut_transform(const T* k, const T* beta, T* tws, int B, int H, int64_t L, int DK,
-                               int C, int rule, hipStream_t stream);
+                               int C, int rule, const int32_t* cu, int N, hipStream_t stream);
 
 template <typename T>
 hipError_t launch_recurrence(const T* q, const T* k, const T* v, const T* tws, const float* s0,
                              T* o, float* sfin, int B, int H, int64_t L, int DK, int DV, int C,
-                             int BV, hipStream_t stream);
+                             int BV, const int32_t* cu, int N, hipStream_t stream);
 
 // bf16 recurrence with one wavefront per 16-column state tile and a DMA-fed
 // LDS ring (recurrence_tile.h); d_k in {32, 64, 128}, chunk in {32, 64},
-// value blocks of 16, 32 or 64 columns.
+// value blocks of 16, 32 or 64 columns.  Dense batches only.
 bool recurrence_tile_supported(int DK, int C, int BV);
 hipError_t launch_recurrence_tile_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                        const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
@@ -39,12 +42,12 @@ bool recurrence_roles_supported(int DK, int C, int BV);
 hipError_t launch_recurrence_roles_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                         const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
                                         int B, int H, int64_t L, int DK, int DV, int C, int BV,
-                                        hipStream_t s);
+                                        const int32_t* cu, int N, hipStream_t s);
 
 // bf16 UT transform with one wavefront per chunk (ut_wave.h); d_k in
 // {32, 64, 128}, chunk in {32, 64}.
 bool ut_wave_bf16_supported(int DK, int C);
 hipError_t launch_ut_wave_bf16(const uint16_t* k, const uint16_t* beta, uint16_t* tws, int B, int H, int64_t L,
-                               int DK, int C, int rule, hipStream_t s);
+                               int DK, int C, int rule, const int32_t* cu, int N, hipStream_t s);
 
 }  // namespace efla

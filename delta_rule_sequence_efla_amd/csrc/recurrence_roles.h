@@ -51,7 +51,8 @@ template <int DK, int C, int BV>
 __global__ __launch_bounds__(64 * (BV / 16 + 3)) void recurrence_roles_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ tws, const float* __restrict__ s0, uint16_t* __restrict__ o,
-    float* __restrict__ sfin, int H, int64_t L, int NC, int DV, int NVB, int remap) {
+    float* __restrict__ sfin, int H, int64_t L, int NC, int DV, int NVB, int remap,
+    const int32_t* __restrict__ cu) {
   using S = RolesShape<DK, C, BV>;
   constexpr int NT = S::NT, NRT = S::NRT, NDT = S::NDT, NKU_D = S::NKU_D, NKU_C = S::NKU_C;
   constexpr int NPF = S::NPF;
@@ -72,11 +73,13 @@ __global__ __launch_bounds__(64 * (BV / 16 + 3)) void recurrence_roles_kernel(
     bh = x / NVB;
     vb = x % NVB;
   }
-  const int64_t b = bh / H, h = bh % H;
+  const int64_t h = bh % H;
+  const SeqSpan sp = seq_span<C>(cu, bh / H, h, H, L, NC);  // sequence bh / H
+  const int nc = sp.nc;
   const int v0 = vb * BV;
   const int lane = threadIdx.x & 63, role = wave_id(), li = lane & 15, g = lane >> 4;
-  auto chunk_valid = [&](int n) { return int(L - int64_t(n) * C < C ? L - int64_t(n) * C : C); };
-  auto row_of = [&](int n) { return (b * L + int64_t(n) * C) * H + h; };
+  auto chunk_valid = [&](int n) { return int(sp.len - int64_t(n) * C < C ? sp.len - int64_t(n) * C : C); };
+  auto row_of = [&](int n) { return (sp.bos + int64_t(n) * C) * H + h; };
   auto sync = [&]() {  // this wave's LDS writes done, then the workgroup barrier
     wait_lgkm0();
     barrier_nowait();
@@ -94,19 +97,19 @@ __global__ __launch_bounds__(64 * (BV / 16 + 3)) void recurrence_roles_kernel(
       const int64_t r0 = row_of(n);
       using U = const uint16_t*;
       return typename S::Dma::Src{(U)uniform_ptr(q + r0 * DK), (U)uniform_ptr(k + r0 * DK),
-                                  (U)uniform_ptr(tws + (int64_t(bh) * NC + n) * C * C),
+                                  (U)uniform_ptr(tws + (sp.slot0 + n) * C * C),
                                   (U)uniform_ptr(v + r0 * DV + v0), chunk_valid(n)};
     };
     constexpr int D = S::DMA_COUNT, D0 = S::DMA_COUNT / 2;  // D0: transfers of part 0
-    if (NC > 0) dma.issue_part(0, 1, lds_addr_of(slot0), chunk_src(0));
-    if (NC > 1) dma.issue_part(0, 1, lds_addr_of(slot1), chunk_src(1));
+    if (nc > 0) dma.issue_part(0, 1, lds_addr_of(slot0), chunk_src(0));
+    if (nc > 1) dma.issue_part(0, 1, lds_addr_of(slot1), chunk_src(1));
     auto step = [&](uint16_t* fill, int n) {
       // chunk n is complete once at most chunk n+1's transfers are outstanding
       // (already true since barrier B of the step before)
-      if (n + 1 < NC) wait_vmcnt<D>();
+      if (n + 1 < nc) wait_vmcnt<D>();
       else wait_vmcnt<0>();
       sync_dma();  // A
-      const bool more = n + 2 < NC;
+      const bool more = n + 2 < nc;
       const auto src = chunk_src(more ? n + 2 : n);
       const uint32_t fa = lds_addr_of(fill);
       if (more) dma.issue_part(0, 2, fa, src);
@@ -116,10 +119,10 @@ __global__ __launch_bounds__(64 * (BV / 16 + 3)) void recurrence_roles_kernel(
       sync_dma();  // B
       if (more) dma.issue_part(1, 2, fa, src);
     };
-    for (int n = 0; n < NC; n += 3) {
+    for (int n = 0; n < nc; n += 3) {
       step(slot2, n);
-      if (n + 1 < NC) step(slot0, n + 1);
-      if (n + 2 < NC) step(slot1, n + 2);
+      if (n + 1 < nc) step(slot0, n + 1);
+      if (n + 2 < nc) step(slot1, n + 2);
     }
     wait_vmcnt<0>();
   } else if (role >= S::kChain0 && role < S::kChain0 + NT) {
@@ -212,10 +215,10 @@ __global__ __launch_bounds__(64 * (BV / 16 + 3)) void recurrence_roles_kernel(
         bS_buf[ct][ku][lane] = bS[ku].v;
       }
     };
-    for (int n = 0; n < NC; n += 3) {
+    for (int n = 0; n < nc; n += 3) {
       step(slot0);
-      if (n + 1 < NC) step(slot1);
-      if (n + 2 < NC) step(slot2);
+      if (n + 1 < nc) step(slot1);
+      if (n + 2 < nc) step(slot2);
     }
     if (sfin != nullptr) {
 #pragma unroll
@@ -274,10 +277,10 @@ __global__ __launch_bounds__(64 * (BV / 16 + 3)) void recurrence_roles_kernel(
         }
       }
     };
-    for (int n = 0; n < NC; n += 3) {
+    for (int n = 0; n < nc; n += 3) {
       step(slot0, n);
-      if (n + 1 < NC) step(slot1, n + 1);
-      if (n + 2 < NC) step(slot2, n + 2);
+      if (n + 1 < nc) step(slot1, n + 1);
+      if (n + 2 < nc) step(slot2, n + 2);
     }
   } else if (role == S::kP) {
     // ------------------------------------------------------------------ P
@@ -330,12 +333,12 @@ __global__ __launch_bounds__(64 * (BV / 16 + 3)) void recurrence_roles_kernel(
       }
       sync();  // B
       clear();
-      if (n + 1 < NC) accumulate(nxt, 0, KH);
+      if (n + 1 < nc) accumulate(nxt, 0, KH);
     };
-    for (int n = 0; n < NC; n += 3) {
+    for (int n = 0; n < nc; n += 3) {
       step(slot0, slot1, n);
-      if (n + 1 < NC) step(slot1, slot2, n + 1);
-      if (n + 2 < NC) step(slot2, slot0, n + 2);
+      if (n + 1 < nc) step(slot1, slot2, n + 1);
+      if (n + 2 < nc) step(slot2, slot0, n + 2);
     }
   }
 }
@@ -348,25 +351,26 @@ inline bool roles_supported(int DK, int C, int BV) {
 template <int DK, int C, int BV>
 hipError_t recurrence_roles_launch_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                      const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
-                                     int B, int H, int64_t L, int DV, hipStream_t stream) {
-  const int NC = int((L + C - 1) / C);
-  const int BH = B * H;
+                                     int B, int H, int64_t L, int DV, const int32_t* cu, int N,
+                                     hipStream_t stream) {
+  const int NC = cu == nullptr ? int((L + C - 1) / C) : int(L / C) + N;  // chunk slots per sequence / head
+  const int BH = (cu == nullptr ? B : N) * H;
   const int NVB = DV / BV;
   const int nwg = BH * NVB;
   if (nwg == 0) return hipSuccess;
   const int remap = (BH % 8 == 0) ? 1 : 0;
   hipLaunchKernelGGL((recurrence_roles_kernel<DK, C, BV>), dim3(unsigned(nwg)), dim3(RolesShape<DK, C, BV>::THREADS),
-                     0, stream, q, k, v, tws, s0, o, sfin, H, L, NC, DV, NVB, remap);
+                     0, stream, q, k, v, tws, s0, o, sfin, H, L, NC, DV, NVB, remap, cu);
   return hipGetLastError();
 }
 
 template <int DK, int C>
 hipError_t recurrence_roles_bv(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* tws,
                             const float* s0, uint16_t* o, float* sfin, int B, int H, int64_t L, int DV,
-                            int BV, hipStream_t s) {
+                            int BV, const int32_t* cu, int N, hipStream_t s) {
   switch (BV) {
-    case 16: return recurrence_roles_launch_impl<DK, C, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, s);
-    case 32: return recurrence_roles_launch_impl<DK, C, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, s);
+    case 16: return recurrence_roles_launch_impl<DK, C, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, s);
+    case 32: return recurrence_roles_launch_impl<DK, C, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, s);
   }
   return hipErrorInvalidValue;
 }
@@ -374,18 +378,18 @@ hipError_t recurrence_roles_bv(const uint16_t* q, const uint16_t* k, const uint1
 inline hipError_t launch_recurrence_roles(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                        const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
                                        int B, int H, int64_t L, int DK, int DV, int C, int BV,
-                                       hipStream_t s) {
+                                       const int32_t* cu, int N, hipStream_t s) {
   if (C == 32) {
     switch (DK) {
-      case 32: return recurrence_roles_bv<32, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, s);
-      case 64: return recurrence_roles_bv<64, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, s);
-      case 128: return recurrence_roles_bv<128, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, s);
+      case 32: return recurrence_roles_bv<32, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, s);
+      case 64: return recurrence_roles_bv<64, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, s);
+      case 128: return recurrence_roles_bv<128, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, s);
     }
   } else if (C == 64) {
     switch (DK) {
-      case 32: return recurrence_roles_bv<32, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, s);
-      case 64: return recurrence_roles_bv<64, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, s);
-      case 128: return recurrence_roles_bv<128, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, s);
+      case 32: return recurrence_roles_bv<32, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, s);
+      case 64: return recurrence_roles_bv<64, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, s);
+      case 128: return recurrence_roles_bv<128, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, s);
     }
   }
   return hipErrorInvalidValue;

@@ -4,8 +4,9 @@
 // For a chunk of C tokens with key rows K and coefficients a (Method step 3
 // of the pages, computed here from beta and lambda = ||k||^2):
 //     G = K K^T,   X = (I + diag(a) tril(G, -1))^{-1},   T = X diag(a)
-// written row-major to the workspace [B, H, NC, C, C] (zeros above the
-// diagonal and in rows/columns of tokens past L).
+// written row-major to workspace slots of C x C (zeros above the diagonal
+// and in rows/columns of tokens past the sequence's end); common.h gives the
+// slot of each chunk, for dense and for packed variable-length batches.
 //
 // Layout of the work inside one wavefront:
 //   * K is loaded straight from global memory as 16-byte row fragments.  The
@@ -58,21 +59,29 @@ template <int DK, int C>
 __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict__ k,
                                                       const uint16_t* __restrict__ beta,
                                                       uint16_t* __restrict__ tws, int H, int64_t L, int NC,
-                                                      int64_t nchunks, int rule) {
+                                                      int64_t nchunks, int rule, const int32_t* __restrict__ cu,
+                                                      int N) {
   using S = UtWaveShape<DK, C>;
   constexpr int NRT = S::NRT, NKU = S::NKU, GP = S::GP, BLK = S::BLK, TP = S::TP;
   __shared__ __align__(16) unsigned char scratch_all[S::WAVES][S::SCRATCH];
   __shared__ float a_all[S::WAVES][64];
 
   const int lane = threadIdx.x & 63, w = wave_id(), li = lane & 15, g = lane >> 4;
-  const int64_t id = int64_t(blockIdx.x) * S::WAVES + w;  // chunk handled by this wavefront
+  const int64_t id = int64_t(blockIdx.x) * S::WAVES + w;  // workspace slot handled by this wavefront
   if (id >= nchunks) return;                              // no workgroup barriers below
-  const int chunk = int(id % NC);
-  const int64_t bh = id / NC;
-  const int64_t b = bh / H, h = bh % H;
+  // slot id -> sequence and chunk (dense: id = (b H + h) NC + chunk)
+  SeqSpan sp;
+  int chunk;
+  const int64_t h = cu == nullptr ? (id / NC) % H : id / NC;
+  if (cu == nullptr) {
+    chunk = int(id % NC);
+    sp = seq_span<C>(nullptr, int(id / NC / H), h, H, L, NC);
+  } else if (!slot_chunk<C>(cu, N, id % NC, h, H, L, NC, sp, chunk)) {
+    return;  // a slot no chunk of the packed batch uses
+  }
   const int64_t t0 = int64_t(chunk) * C;
-  const int valid = int(L - t0 < C ? L - t0 : C);
-  const int64_t row0 = (b * L + t0) * H + h;
+  const int valid = int(sp.len - t0 < C ? sp.len - t0 : C);
+  const int64_t row0 = (sp.bos + t0) * H + h;
   float* Gs = reinterpret_cast<float*>(scratch_all[w]);   // [4][16][GP] diagonal G blocks
   float* Xs = Gs + 4 * BLK;                               // [4][16][GP] diagonal X blocks
   uint16_t* Ts = reinterpret_cast<uint16_t*>(scratch_all[w]);  // [C][TP] bf16 (after Gs/Xs are read)
@@ -206,31 +215,33 @@ __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict
 
 inline bool ut_wave_supported(int DK, int C) { return (DK == 32 || DK == 64 || DK == 128) && (C == 32 || C == 64); }
 
+// Dense batches: B sequences of L tokens.  Packed batches (cu != nullptr):
+// N sequences with offsets cu in a batch of L tokens (B is ignored).
 template <int DK, int C>
 hipError_t ut_wave_launch_impl(const uint16_t* k, const uint16_t* beta, uint16_t* tws, int B, int H, int64_t L,
-                               int rule, hipStream_t stream) {
-  const int NC = int((L + C - 1) / C);
-  const int64_t nchunks = int64_t(B) * H * NC;
+                               int rule, const int32_t* cu, int N, hipStream_t stream) {
+  const int NC = cu == nullptr ? int((L + C - 1) / C) : int(L / C) + N;
+  const int64_t nchunks = int64_t(cu == nullptr ? B : 1) * H * NC;
   if (nchunks == 0) return hipSuccess;
   const int64_t nwg = (nchunks + UtWaveShape<DK, C>::WAVES - 1) / UtWaveShape<DK, C>::WAVES;
   hipLaunchKernelGGL((ut_wave_kernel<DK, C>), dim3(unsigned(nwg)), dim3(64 * UtWaveShape<DK, C>::WAVES), 0, stream,
-                     k, beta, tws, H, L, NC, nchunks, rule);
+                     k, beta, tws, H, L, NC, nchunks, rule, cu, N);
   return hipGetLastError();
 }
 
 inline hipError_t launch_ut_wave(const uint16_t* k, const uint16_t* beta, uint16_t* tws, int B, int H, int64_t L,
-                                 int DK, int C, int rule, hipStream_t s) {
+                                 int DK, int C, int rule, const int32_t* cu, int N, hipStream_t s) {
   if (C == 32) {
     switch (DK) {
-      case 32: return ut_wave_launch_impl<32, 32>(k, beta, tws, B, H, L, rule, s);
-      case 64: return ut_wave_launch_impl<64, 32>(k, beta, tws, B, H, L, rule, s);
-      case 128: return ut_wave_launch_impl<128, 32>(k, beta, tws, B, H, L, rule, s);
+      case 32: return ut_wave_launch_impl<32, 32>(k, beta, tws, B, H, L, rule, cu, N, s);
+      case 64: return ut_wave_launch_impl<64, 32>(k, beta, tws, B, H, L, rule, cu, N, s);
+      case 128: return ut_wave_launch_impl<128, 32>(k, beta, tws, B, H, L, rule, cu, N, s);
     }
   } else if (C == 64) {
     switch (DK) {
-      case 32: return ut_wave_launch_impl<32, 64>(k, beta, tws, B, H, L, rule, s);
-      case 64: return ut_wave_launch_impl<64, 64>(k, beta, tws, B, H, L, rule, s);
-      case 128: return ut_wave_launch_impl<128, 64>(k, beta, tws, B, H, L, rule, s);
+      case 32: return ut_wave_launch_impl<32, 64>(k, beta, tws, B, H, L, rule, cu, N, s);
+      case 64: return ut_wave_launch_impl<64, 64>(k, beta, tws, B, H, L, rule, cu, N, s);
+      case 128: return ut_wave_launch_impl<128, 64>(k, beta, tws, B, H, L, rule, cu, N, s);
     }
   }
   return hipErrorInvalidValue;

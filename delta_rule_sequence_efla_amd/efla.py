@@ -70,6 +70,11 @@ def lib() -> ctypes.CDLL:
         L.efla_chunk_ut_transform_rule.argtypes = [_vp, _vp, _i, _i, _i64, _i, _i, _i, _i, _vp, _sz, _vp]
         L.efla_step_rule.restype = _i
         L.efla_step_rule.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]
+        L.efla_chunk_fwd_varlen_workspace_size.restype = _sz
+        L.efla_chunk_fwd_varlen_workspace_size.argtypes = [_i, _i, _i64, _i, _i, _i, _i]
+        L.efla_chunk_fwd_varlen.restype = _i
+        L.efla_chunk_fwd_varlen.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i64, _i, _i,
+                                            _i, _i, _i, _vp, _sz, _vp]
         _lib = L
     return _lib
 
@@ -218,6 +223,61 @@ def efla_chunk_recurrence(q, k, v, workspace, s0=None, chunk: int = 64, o=None, 
                                            dk, dv, chunk, _code(q.dtype), _p(workspace),
                                            workspace.numel(), _stream(dev)), "efla_chunk_recurrence")
     return o, s_final
+
+
+def efla_chunk_fwd_varlen_workspace_size(N, H, T, d_k, d_v, chunk, dtype) -> int:
+    return int(lib().efla_chunk_fwd_varlen_workspace_size(N, H, T, d_k, d_v, chunk, _code(dtype)))
+
+
+def _varlen_shapes(q, k, v, beta, cu_seqlens, s0):
+    if k.dim() == 4 and k.shape[0] == 1:   # [1, T, H, d] packed layout
+        q, k, v, beta = q[0], k[0], v[0], beta[0]
+    T, H, dk = k.shape
+    dv = v.shape[-1]
+    if q.shape != k.shape or v.shape[:2] != (T, H) or beta.shape != (T, H):
+        raise ValueError("expected q, k [T,H,dk], v [T,H,dv], beta [T,H] (or with a leading 1)")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor of N+1 offsets")
+    N = cu_seqlens.numel() - 1
+    if s0 is not None and (s0.shape != (N, H, dk, dv) or s0.dtype != torch.float32):
+        raise ValueError("s0 must be float32 [N,H,dk,dv]")
+    return N, T, H, dk, dv
+
+
+def efla_chunk_fwd_varlen(q, k, v, beta, cu_seqlens, s0=None, chunk: int = 64, o=None, s_final=None,
+                          workspace=None, want_final: bool = True, rule: str = "exact"):
+    """Chunked forward over a packed variable-length batch: q, k [T,H,dk],
+    v [T,H,dv], beta [T,H] (a leading batch dim of 1 is accepted), int32
+    device offsets cu_seqlens [N+1].  Returns (o shaped like v, S fp32 [N,H,dk,dv])."""
+    dev = _dev(q, k, v, beta, o, workspace, cu_seqlens, dtype=None)
+    _dev(q, k, v, beta, o, dtype=q.dtype)
+    _dev(s0, s_final, dtype=torch.float32)
+    N, T, H, dk, dv = _varlen_shapes(q, k, v, beta, cu_seqlens, s0)
+    if o is None:
+        o = torch.empty(v.shape, dtype=q.dtype, device=dev)
+    if s_final is None and want_final:
+        s_final = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    if workspace is None:
+        n = efla_chunk_fwd_varlen_workspace_size(N, H, T, dk, dv, chunk, q.dtype)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib().efla_chunk_fwd_varlen(_p(q), _p(k), _p(v), _p(beta), _p(cu_seqlens), N, _p(s0), _p(o),
+                                           _p(s_final), H, T, dk, dv, chunk, _code(q.dtype), _rule(rule),
+                                           _p(workspace), workspace.numel(), _stream(dev)),
+               "efla_chunk_fwd_varlen")
+    return o, s_final
+
+
+def prepare_chunk_fwd_varlen(q, k, v, beta, cu_seqlens, s0, o, s_final, workspace, chunk: int = 64,
+                             rule: str = "exact"):
+    dev = _dev(q, k, v, beta, o, dtype=q.dtype)
+    _dev(s0, s_final, dtype=torch.float32)
+    N, T, H, dk, dv = _varlen_shapes(q, k, v, beta, cu_seqlens, s0)
+    return PreparedCall(lib().efla_chunk_fwd_varlen,
+                        (_p(q), _p(k), _p(v), _p(beta), _p(cu_seqlens), N, _p(s0), _p(o), _p(s_final), H, T,
+                         dk, dv, chunk, _code(q.dtype), _rule(rule), _p(workspace), workspace.numel(),
+                         _stream(dev)),
+                        "efla_chunk_fwd_varlen", (q, k, v, beta, cu_seqlens, s0, o, s_final, workspace))
 
 
 def efla_step(q, k, v, beta, state, o=None, rule: str = "exact"):

@@ -11,7 +11,9 @@ the "large key norm / high-energy input" regime of the pages' Problem section.
 
 Layouts: q, k [B, L, H, dk]; v [B, L, H, dv]; beta [B, L, H];
 s0 [B, H, dk, dv] float32 (or None).  Decode inputs carry a leading step axis:
-q, k [steps, N, H, dk], v [steps, N, H, dv], beta [steps, N, H].
+q, k [steps, N, H, dk], v [steps, N, H, dv], beta [steps, N, H].  Packed
+variable-length inputs: q, k [T, H, dk], v [T, H, dv], beta [T, H], int32
+offsets cu_seqlens [N + 1], s0 [N, H, dk, dv].
 """
 from __future__ import annotations
 
@@ -20,7 +22,8 @@ from dataclasses import dataclass, field, replace
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "get", "generate", "generate_decode", "to_f64"]
+__all__ = ["Workload", "WORKLOADS", "get", "generate", "generate_decode", "generate_packed", "length_mix",
+           "to_f64"]
 
 
 @dataclass(frozen=True)
@@ -66,6 +69,9 @@ WORKLOADS = {
                  note="stiff long context: |k| log-uniform in [0.1, 30], beta ~ U[0,10], 5% x100 v spikes"),
         Workload("decode_1p3b", 256, 16, 1, 128, 128, 0, "bf16", "unit_u", "sigmoid", "n002",
                  seed=1014, steps=16, note="decode: 256 sequences x 16 heads, 16 single-token steps"),
+        # B = number of sequences, L = total packed tokens (lengths from length_mix)
+        Workload("varlen_1p3b", 16, 16, 16384, 128, 128, 64, "bf16", "unit_u", "sigmoid", "n002",
+                 seed=1006, note="1.3B-shaped heads, 16 sequences of mixed length packed into 16384 tokens"),
     ]
 }
 
@@ -160,3 +166,38 @@ def to_f64(t) -> np.ndarray | None:
     if t is None:
         return None
     return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def length_mix(n: int, total: int, seed: int) -> list:
+    """n sequence lengths summing to `total`, with log-uniform shares over a
+    64x range (a few long sequences and many short ones, as a packed training
+    or serving batch holds them)."""
+    rng = np.random.default_rng(seed)
+    share = np.exp(rng.uniform(0.0, np.log(64.0), n))
+    lengths = np.floor(share / share.sum() * total).astype(np.int64)
+    lengths[np.argmax(lengths)] += total - int(lengths.sum())
+    return [int(x) for x in lengths]
+
+
+def generate_packed(w: Workload, lengths, device="cpu", H: int | None = None, seed: int | None = None,
+                    lead: int = 0, tail: int = 0) -> dict:
+    """Packed variable-length inputs with the distributions of workload w:
+    sequences of the given lengths back to back, after `lead` and before
+    `tail` tokens that belong to no sequence."""
+    H = w.H if H is None else H
+    N = len(lengths)
+    T = lead + int(sum(lengths)) + tail
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    q = _qk(rng, (T, H, w.dk), w.qk, is_key=False)
+    k = _qk(rng, (T, H, w.dk), w.qk, is_key=True)
+    v = rng.standard_normal((T, H, w.dv))
+    beta = _beta(rng, (T, H), w.beta)
+    if w.spikes > 0:
+        v[rng.random(T) < w.spikes] *= 100.0
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64) + lead
+    s0 = None
+    if w.s0 == "n002":
+        s0 = torch.from_numpy(0.02 * rng.standard_normal((N, H, w.dk, w.dv))).float().to(device)
+    return dict(q=_cast(q, w.dtype, device), k=_cast(k, w.dtype, device), v=_cast(v, w.dtype, device),
+                beta=_cast(beta, w.dtype, device), s0=s0,
+                cu_seqlens=torch.from_numpy(cu.astype(np.int32)).to(device))

@@ -168,6 +168,37 @@ efla_status efla_chunk_recurrence(const void *q, const void *k, const void *v,
                                   size_t workspace_bytes, void *stream);
 
 /*
+ * Variable-length batches.  N sequences of different lengths packed along one
+ * token axis, as a training or serving batch without padding holds them:
+ *     q, k [T, H, d_k]   v, o [T, H, d_v]   beta [T, H]   (dtype)
+ *     cu_seqlens [N + 1] int32, DEVICE memory: sequence i is tokens
+ *         cu_seqlens[i] .. cu_seqlens[i+1] - 1 (nondecreasing, cu_seqlens[0] >= 0,
+ *         cu_seqlens[N] <= T; lengths may be 0 or ragged)
+ *     s0, s_final [N, H, d_k, d_v] float32 (each nullable, as in efla_chunk_fwd)
+ * Every sequence runs the recurrence of efla_chunk_fwd on its own, from its own
+ * initial state (Method step 3 per sequence).  Tokens outside every sequence
+ * are not written.  The offsets are read on the device, so the library cannot
+ * check them: offsets that break the rules above give unspecified numbers,
+ * though every access stays inside the T tokens and the workspace (offsets
+ * are clamped into [0, T]).  T < 2^31.
+ *
+ * efla_chunk_fwd_varlen_workspace_size -- bytes of workspace for these sizes:
+ * H * (floor(T / chunk) + N) chunk slots of chunk x chunk (dtype); 0 for
+ * unsupported or invalid arguments (N < 1 included).
+ */
+size_t efla_chunk_fwd_varlen_workspace_size(int N, int H, int64_t T, int d_k, int d_v, int chunk,
+                                            efla_dtype dtype);
+/* efla_chunk_fwd_varlen -- the chunked forward pass over a packed batch (see
+ * above), under a given rule.  N == 0 launches nothing; T == 0 only copies s0
+ * (or zeros) into s_final.  Workspace, alignment and error rules as for
+ * efla_chunk_fwd. */
+efla_status efla_chunk_fwd_varlen(const void *q, const void *k, const void *v, const void *beta,
+                                  const int32_t *cu_seqlens, int N, const float *s0, void *o,
+                                  float *s_final, int H, int64_t T, int d_k, int d_v, int chunk,
+                                  efla_dtype dtype, efla_rule rule, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/*
  * efla_step -- one decode step: a single token per (n, h) applied in place
  * (Method step 3):
  *     state[n, h] = (I - alpha k k^T) state[n, h] + alpha k v^T

@@ -159,3 +159,25 @@ def step(q, k, v, beta, state, rule: str = "exact"):
     if rc != 0:
         raise RuntimeError(f"oracle_step failed ({rc})")
     return o, st
+
+
+def forward_varlen(q, k, v, beta, cu_seqlens, s0=None, nthreads: int | None = None, rule: str = "exact"):
+    """A packed variable-length batch: q, k [T,H,dk], v [T,H,dv], beta [T,H],
+    offsets cu_seqlens [N+1].  Every sequence is an independent run of
+    forward() from its own initial state s0[i] (or zeros).  Returns o [T,H,dv]
+    (zeros for tokens outside every sequence) and the final states [N,H,dk,dv]."""
+    q, k, v, beta = _f64(q), _f64(k), _f64(v), _f64(beta)
+    cu = np.asarray(cu_seqlens, dtype=np.int64).ravel()
+    T, H, dk = k.shape
+    dv = v.shape[-1]
+    N = cu.size - 1
+    o = np.zeros((T, H, dv))
+    sf = np.zeros((N, H, dk, dv))
+    for i in range(N):
+        a, e = int(cu[i]), int(cu[i + 1])
+        si = None if s0 is None else _f64(s0)[i:i + 1]
+        oi, sfi = forward(q[None, a:e], k[None, a:e], v[None, a:e], beta[None, a:e], si,
+                          nthreads=nthreads, rule=rule)
+        o[a:e] = oi[0]
+        sf[i] = sfi[0]
+    return o, sf

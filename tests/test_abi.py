@@ -139,3 +139,28 @@ def test_rule_is_validated_first():
     assert efla.RULES == {"exact": 0, "euler": 1}
     with pytest.raises(ValueError):
         efla._rule("rk4")
+
+
+def test_varlen_workspace_size_and_validation():
+    f = efla.efla_chunk_fwd_varlen_workspace_size
+    # H x (floor(T / C) + N) slots of C x C
+    assert f(3, 2, 100, 16, 16, 16, torch.float32) == 2 * (6 + 3) * 16 * 16 * 4
+    assert f(16, 16, 16384, 128, 128, 64, torch.bfloat16) == 16 * (256 + 16) * 64 * 64 * 2
+    assert f(0, 2, 100, 16, 16, 16, torch.float32) == 0
+    assert f(3, 2, 100, 24, 16, 16, torch.float32) == 0
+    assert f(3, 2, 2 ** 31, 16, 16, 16, torch.float32) == 0
+    L = efla.lib()
+    nul = None
+    fake = 4096  # never dereferenced: every case below returns before a launch
+
+    def call(N=2, H=1, T=64, dk=16, dv=16, C=16, dt=0, rule=0, cu=fake, q=fake, ws=nul, wsb=0):
+        return L.efla_chunk_fwd_varlen(q, q, q, q, cu, N, nul, q, nul, H, T, dk, dv, C, dt, rule, ws, wsb, nul)
+
+    assert call(N=-1) == 1 and call(H=0) == 1 and call(T=-1) == 1 and call(dt=5) == 1 and call(rule=2) == 1
+    assert call(dk=24) == 2 and call(C=48) == 2 and call(T=2 ** 31) == 2
+    assert call(N=0, cu=nul, q=nul) == 0          # no sequences: nothing to do
+    assert call(cu=nul) == 1                      # offsets missing
+    assert call(q=nul) == 1                       # tokens but no inputs
+    assert call(q=fake + 8) == 1                  # misaligned
+    assert call() == 3                            # no workspace
+    assert call(ws=fake, wsb=10) == 3             # too small

@@ -475,3 +475,35 @@ def test_P11_euler_forward_equals_euler_steps_and_limits():
 def test_rule_argument_is_checked():
     with pytest.raises(ValueError):
         oracle.coeff(np.ones((1, 2)), np.ones(1), rule="rk4")
+
+
+# ---------------------------------------------------------------------------
+# Packed variable-length batches: each sequence is an independent run.
+# ---------------------------------------------------------------------------
+
+def test_varlen_equal_lengths_is_the_dense_batch():
+    q, k, v, beta, s0 = _rand_inputs(161, 3, 11, 2, 4, 3)
+    o, sf = oracle.forward(q, k, v, beta, s0)
+    cu = np.arange(4) * 11
+    ov, sv = oracle.forward_varlen(q.reshape(33, 2, 4), k.reshape(33, 2, 4), v.reshape(33, 2, 3),
+                                   beta.reshape(33, 2), cu, s0)
+    assert np.array_equal(ov, o.reshape(33, 2, 3)) and np.array_equal(sv, sf)
+
+
+def test_varlen_sequences_are_independent_and_empty_ones_keep_state():
+    rng = _rng(162)
+    lengths = [5, 0, 9, 1]
+    T, H, dk, dv = 2 + sum(lengths) + 3, 2, 3, 2
+    cu = 2 + np.concatenate([[0], np.cumsum(lengths)])
+    q, k = rng.standard_normal((T, H, dk)), rng.standard_normal((T, H, dk))
+    v, beta = rng.standard_normal((T, H, dv)), rng.uniform(0, 1, (T, H))
+    s0 = rng.standard_normal((4, H, dk, dv))
+    o, sf = oracle.forward_varlen(q, k, v, beta, cu, s0)
+    assert np.array_equal(sf[1], s0[1])                      # empty sequence
+    assert not o[:2].any() and not o[-3:].any()              # tokens outside every sequence
+    k2 = k.copy()
+    k2[cu[2]:cu[3]] += 1.0                                   # perturb sequence 2 only
+    o2, sf2 = oracle.forward_varlen(q, k2, v, beta, cu, s0)
+    for i in (0, 1, 3):
+        assert np.array_equal(o2[cu[i]:cu[i + 1]], o[cu[i]:cu[i + 1]]) and np.array_equal(sf2[i], sf[i])
+    assert not np.array_equal(sf2[2], sf[2])
