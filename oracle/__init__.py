@@ -68,6 +68,12 @@ def _load():
         lib.oracle_step_rule.restype = ctypes.c_int
         lib.oracle_step_rule.argtypes = [_D, _D, _D, _D, _D, _D, ctypes.c_int,
                                          ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        lib.oracle_alpha_grad.restype = ctypes.c_int
+        lib.oracle_alpha_grad.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_int, _D]
+        lib.oracle_backward_rule.restype = ctypes.c_int
+        lib.oracle_backward_rule.argtypes = [_D] * 12 + [ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                                                         ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                         ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -141,6 +147,40 @@ def forward(q, k, v, beta, s0=None, nthreads: int | None = None, rule: str = "ex
     if rc != 0:
         raise RuntimeError(f"oracle_forward failed ({rc})")
     return o, sf
+
+
+def alpha_grad(beta: float, lam: float, rule: str = "exact"):
+    """(d alpha / d beta, d alpha / d lambda) of the coefficient under a rule."""
+    out = np.empty(2, np.float64)
+    if _load().oracle_alpha_grad(float(beta), float(lam), _rule(rule), _p(out)) != 0:
+        raise RuntimeError("oracle_alpha_grad failed")
+    return float(out[0]), float(out[1])
+
+
+def backward(q, k, v, beta, s0, do, dsf=None, nthreads: int | None = None, rule: str = "exact"):
+    """Gradients of a scalar loss through forward(): given do = dLoss/do
+    [B,L,H,dv] and dsf = dLoss/dS_L [B,H,dk,dv] (None: zero), returns
+    (dq, dk, dv, dbeta, ds0) with the shapes of q, k, v, beta and
+    [B,H,dk,dv] (reverse-mode differentiation of the token recurrence)."""
+    q, k, v, beta, do = _f64(q), _f64(k), _f64(v), _f64(beta), _f64(do)
+    B, L, H, dk = k.shape
+    dv = v.shape[-1]
+    if q.shape != k.shape or v.shape[:3] != (B, L, H) or beta.shape != (B, L, H) or do.shape != v.shape:
+        raise ValueError("shape mismatch")
+    s0 = None if s0 is None else _f64(s0)
+    dsf = None if dsf is None else _f64(dsf)
+    for s in (s0, dsf):
+        if s is not None and s.shape != (B, H, dk, dv):
+            raise ValueError("state shape mismatch")
+    gq, gk, gv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    gb = np.empty_like(beta)
+    gs0 = np.empty((B, H, dk, dv), np.float64)
+    nt = default_threads() if nthreads is None else int(nthreads)
+    rc = _load().oracle_backward_rule(_p(q), _p(k), _p(v), _p(beta), _p(s0), _p(do), _p(dsf), _p(gq), _p(gk),
+                                      _p(gv), _p(gb), _p(gs0), B, H, L, dk, dv, nt, _rule(rule))
+    if rc != 0:
+        raise RuntimeError(f"oracle_backward failed ({rc})")
+    return gq, gk, gv, gb, gs0
 
 
 def step(q, k, v, beta, state, rule: str = "exact"):

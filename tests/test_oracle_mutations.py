@@ -32,6 +32,13 @@ MUTATIONS = {
     "euler_half_step": ("return rule == 1 ? beta : oracle_alpha(beta, lam);",
                         "return rule == 1 ? 0.5 * beta : oracle_alpha(beta, lam);"),
     "forward_drops_rule": ("B, H, dk, dv, L, nthreads, i, rule};", "B, H, dk, dv, L, nthreads, i, 0};"),
+    "bwd_dq_reads_previous_state": ("acc += St[(int64_t)i * dv + j] * dO[j];", "acc += Sp[(int64_t)i * dv + j] * dO[j];"),
+    "bwd_state_grad_misses_projection": ("dS[(int64_t)i * dv + j] -= k[i] * du[j];",
+                                         "dS[(int64_t)i * dv + j] -= 0.0 * k[i] * du[j];"),
+    "bwd_psi_series_sign": ("        return -sum;", "        return sum;"),
+    "bwd_dbeta_of_euler_in_exact": ("    *da_db = exp(-x);", "    *da_db = 1.0;"),
+    "bwd_dk_drops_lambda_term": ("dkk[i] = a * acc1 - acc2 + 2.0 * dlam * k[i];", "dkk[i] = a * acc1 - acc2;"),
+    "bwd_du_unscaled": ("du[j] = a * acc;", "du[j] = acc;"),
     "initial_state_ignored": ("memcpy(S, J->s0 + u * sdim, sizeof(double) * (size_t)sdim);",
                               "memset(S, 0, sizeof(double) * (size_t)sdim);"),
 }
@@ -53,6 +60,10 @@ PINS = [
     pins.test_P11_euler_unit_step_overwrites_and_large_step_expands,
     pins.test_P11_euler_orthonormal_keys_store_values,
     pins.test_P11_euler_forward_equals_euler_steps_and_limits,
+    lambda: pins.test_P12_backward_matches_finite_differences("exact", "moderate"),
+    lambda: pins.test_P12_backward_matches_finite_differences("exact", "stiff"),
+    lambda: pins.test_P12_backward_matches_finite_differences("euler", "moderate"),
+    lambda: [pins.test_P12_alpha_derivatives_against_60_digit_differentiation(x, 1.0) for x in (1e-3, 0.3)],
 ]
 
 

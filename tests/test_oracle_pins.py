@@ -507,3 +507,100 @@ def test_varlen_sequences_are_independent_and_empty_ones_keep_state():
     for i in (0, 1, 3):
         assert np.array_equal(o2[cu[i]:cu[i + 1]], o[cu[i]:cu[i + 1]]) and np.array_equal(sf2[i], sf[i])
     assert not np.array_equal(sf2[2], sf[2])
+
+
+# ---------------------------------------------------------------------------
+# P12: the backward pass against central finite differences of the forward
+# pass (the pages give no gradient; the gradient of a scalar loss
+# L = sum(o * W) + sum(S_L * Wf) is fixed by the forward pass alone).
+# ---------------------------------------------------------------------------
+
+def _fd_inputs(seed, B, L, H, dk, dv, regime):
+    rng = _rng(seed)
+    q = rng.standard_normal((B, L, H, dk))
+    k = rng.standard_normal((B, L, H, dk))
+    v = rng.standard_normal((B, L, H, dv))
+    beta = rng.uniform(0.1, 1.0, (B, L, H))
+    if regime == "stiff":      # beta * lambda up to ~100: the contraction saturates
+        k *= rng.uniform(1.5, 4.0, (B, L, H, 1))
+        beta = rng.uniform(0.5, 3.0, (B, L, H))
+    elif regime == "small":    # beta * lambda ~ 1e-5: the series branch of the lambda derivative
+        beta = rng.uniform(1e-6, 3e-6, (B, L, H))
+    s0 = rng.standard_normal((B, H, dk, dv))
+    W = rng.standard_normal((B, L, H, dv))
+    Wf = rng.standard_normal((B, H, dk, dv))
+    return q, k, v, beta, s0, W, Wf
+
+
+def _fd_check(inputs, rule, sample=None, seed=0):
+    q, k, v, beta, s0, W, Wf = inputs
+    args = [q, k, v, beta, s0]
+    grads = oracle.backward(q, k, v, beta, s0, W, Wf, nthreads=1, rule=rule)
+    grads = list(grads[:4]) + [grads[4]]
+
+    def loss(a):
+        o, sf = oracle.forward(*a, nthreads=1, rule=rule)
+        return float((o * W).sum() + (sf * Wf).sum())
+
+    # rounding floor of a central difference: a few ulps of the loss over 2h
+    floor = 64 * np.finfo(float).eps * max(1.0, abs(loss(args))) / 1e-5
+    rng = _rng(seed)
+    for which, (x, g) in enumerate(zip(args, grads)):
+        idx = list(np.ndindex(x.shape))
+        if sample is not None and len(idx) > sample:
+            idx = [idx[i] for i in rng.choice(len(idx), sample, replace=False)]
+        fd = []
+        for ix in idx:
+            h = 1e-5 * max(1.0, abs(x[ix]))
+            a_p = [a.copy() for a in args]
+            a_m = [a.copy() for a in args]
+            a_p[which][ix] += h
+            a_m[which][ix] -= h
+            fd.append((loss(a_p) - loss(a_m)) / (2 * h))
+        fd = np.array(fd)
+        got = np.array([g[ix] for ix in idx])
+        scale = max(np.abs(fd).max(), 1e-12)
+        assert np.abs(fd - got).max() <= 2e-6 * scale + floor, (which, np.abs(fd - got).max(), scale)
+
+
+@pytest.mark.parametrize("rule", ["exact", "euler"])
+@pytest.mark.parametrize("regime", ["moderate", "stiff", "small"])
+def test_P12_backward_matches_finite_differences(rule, regime):
+    if rule == "euler" and regime == "stiff":
+        pytest.skip("the Euler step diverges for beta*lambda > 2; nothing to differentiate")
+    _fd_check(_fd_inputs(171, 2, 5, 2, 3, 2, regime), rule)
+
+
+def test_P12_backward_across_recompute_segments():
+    # 150 tokens: three 64-token recompute segments of the oracle's reverse sweep
+    _fd_check(_fd_inputs(172, 1, 150, 1, 2, 2, "moderate"), "exact", sample=12, seed=5)
+
+
+def test_P12_backward_without_final_state_gradient_and_state():
+    q, k, v, beta, s0, W, _ = _fd_inputs(173, 1, 4, 1, 3, 3, "moderate")
+    g0 = oracle.backward(q, k, v, beta, None, W, None, nthreads=1)
+    g1 = oracle.backward(q, k, v, beta, np.zeros_like(s0), W, np.zeros_like(s0), nthreads=1)
+    for a, b in zip(g0, g1):
+        assert np.array_equal(a, b)
+    # o_t is linear in q_t: dq_t = S_t do_t exactly
+    o, _ = oracle.forward(q, k, v, beta, None)
+    gq = g0[0]
+    assert np.allclose((gq * q).sum(), (o * W).sum(), rtol=1e-12)
+
+
+@pytest.mark.parametrize("x", [0.0, 1e-300, 1e-12, 1e-6, 1e-3, 0.02, 0.049, 0.051, 0.3, 1.0, 7.0, 40.0, 700.0])
+@pytest.mark.parametrize("lam", [1e-3, 1.0, 37.0])
+def test_P12_alpha_derivatives_against_60_digit_differentiation(x, lam):
+    """d alpha / d beta and d alpha / d lambda of (1 - exp(-beta lambda)) / lambda,
+    differentiated by mpmath at 60 digits, across both branches of the
+    oracle's evaluation (series below beta*lambda = 0.05)."""
+    beta = x / lam
+    b, l = mpmath.mpf(beta), mpmath.mpf(lam)
+    f_b = lambda bb: (1 - mpmath.exp(-bb * l)) / l if bb * l != 0 else bb
+    f_l = lambda ll: (1 - mpmath.exp(-b * ll)) / ll
+    want_b = mpmath.diff(f_b, b) if x > 0 else mpmath.mpf(1)
+    want_l = mpmath.diff(f_l, l) if x > 0 else -b * b / 2
+    got_b, got_l = oracle.alpha_grad(beta, lam)
+    assert abs(got_b - float(want_b)) <= 4e-15 * max(1.0, abs(float(want_b)))
+    assert abs(got_l - float(want_l)) <= 1e-13 * abs(float(want_l)) + 1e-300
+    assert oracle.alpha_grad(beta, lam, rule="euler") == (1.0, 0.0)
