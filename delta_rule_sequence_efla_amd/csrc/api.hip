@@ -311,3 +311,42 @@ efla_status efla_chunk_fwd_varlen(const void* q, const void* k, const void* v, c
   }
   return launch_rec(q, k, v, s0, o, s_final, 1, H, T, d_k, d_v, chunk, dtype, workspace, cu_seqlens, N, s);
 }
+
+size_t efla_chunk_bwd_workspace_size(int B, int H, int64_t L, int d_k, int d_v, int chunk, efla_dtype dtype) {
+  if (check_chunk_shape(B, H, L, d_k, d_v, chunk, dtype) != EFLA_OK) return 0;
+  if (L == 0) return 0;
+  return efla::bwd_layout(B, H, L, d_k, d_v, chunk, elem_bytes(dtype)).total;
+}
+
+efla_status efla_chunk_bwd(const void* q, const void* k, const void* v, const void* beta, const float* s0,
+                           const void* d_o, const float* ds_final, void* dq, void* dk, void* dv, void* dbeta,
+                           float* ds0, int B, int H, int64_t L, int d_k, int d_v, int chunk, efla_dtype dtype,
+                           efla_rule rule, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_rule(rule)) return EFLA_ERR_INVALID_ARG;
+  const efla_status st = check_chunk_shape(B, H, L, d_k, d_v, chunk, dtype);
+  if (st != EFLA_OK) return st;
+  if (L > 0) {
+    if (q == nullptr || k == nullptr || v == nullptr || beta == nullptr || d_o == nullptr || dq == nullptr ||
+        dk == nullptr || dv == nullptr || dbeta == nullptr)
+      return EFLA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return EFLA_ERR_INVALID_ARG;
+    const size_t need = efla_chunk_bwd_workspace_size(B, H, L, d_k, d_v, chunk, dtype);
+    if (workspace == nullptr || workspace_bytes < need) return EFLA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return EFLA_ERR_INVALID_ARG;
+  } else if (ds0 == nullptr) {
+    return EFLA_OK;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == EFLA_BF16) {
+    using U = uint16_t;
+    return from_hip(efla::launch_chunk_bwd<U>(
+        static_cast<const U*>(q), static_cast<const U*>(k), static_cast<const U*>(v), static_cast<const U*>(beta),
+        s0, static_cast<const U*>(d_o), ds_final, static_cast<U*>(dq), static_cast<U*>(dk), static_cast<U*>(dv),
+        static_cast<U*>(dbeta), ds0, B, H, L, d_k, d_v, chunk, int(rule), workspace, s));
+  }
+  return from_hip(efla::launch_chunk_bwd<float>(
+      static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
+      static_cast<const float*>(beta), s0, static_cast<const float*>(d_o), ds_final, static_cast<float*>(dq),
+      static_cast<float*>(dk), static_cast<float*>(dv), static_cast<float*>(dbeta), ds0, B, H, L, d_k, d_v, chunk,
+      int(rule), workspace, s));
+}

@@ -1,0 +1,105 @@
+// bwd.hip -- launches of the chunked backward pass (bwd_kernels.h), fp32 and
+// bf16 inputs.  Workspace layout, every region 256-byte aligned, per chunk
+// slot s of the dense batch ((b H + h) NC + n):
+//   T  [slots][C][C]     input dtype   UT transform (as in the forward pass)
+//   X  [slots][C][C]     fp32          (I + A)^{-1}
+//   P  [slots][C][C]     fp32          tril(Q K^T)
+//   a  [slots][C]        fp32          coefficients
+//   S  [slots][dk][dv]   fp32          state at the start of the chunk
+//   dS [slots][dk][dv]   fp32          loss gradient at the end of the chunk
+#include "bwd_kernels.h"
+#include "chunk_kernels.h"
+#include "launchers.h"
+
+namespace efla {
+
+namespace {
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+}  // namespace
+
+BwdLayout bwd_layout(int B, int H, int64_t L, int DK, int DV, int C, size_t esz) {
+  const int64_t NC = (L + C - 1) / C;
+  const size_t slots = size_t(B) * H * NC;
+  BwdLayout w{};
+  w.t = 0;
+  w.x = w.t + align256(slots * C * C * esz);
+  w.p = w.x + align256(slots * C * C * 4);
+  w.a = w.p + align256(slots * C * C * 4);
+  w.s = w.a + align256(slots * C * 4);
+  w.ds = w.s + align256(slots * size_t(DK) * DV * 4);
+  w.total = w.ds + align256(slots * size_t(DK) * DV * 4);
+  return w;
+}
+
+template <typename T, int DK, int C>
+hipError_t bwd_launch_impl(const T* q, const T* k, const T* v, const T* beta, const float* s0, const T* dout,
+                           const float* dsf, T* dq, T* dk, T* dv, T* dbeta, float* ds0, int B, int H, int64_t L,
+                           int DV, int rule, unsigned char* ws, hipStream_t s) {
+  const int NC = int((L + C - 1) / C);
+  const int BH = B * H;
+  const int64_t slots = int64_t(BH) * NC;
+  const BwdLayout lay = bwd_layout(B, H, L, DK, DV, C, sizeof(T));
+  T* tws = reinterpret_cast<T*>(ws + lay.t);
+  float* xws = reinterpret_cast<float*>(ws + lay.x);
+  float* pws = reinterpret_cast<float*>(ws + lay.p);
+  float* aws = reinterpret_cast<float*>(ws + lay.a);
+  float* sws = reinterpret_cast<float*>(ws + lay.s);
+  float* dsws = reinterpret_cast<float*>(ws + lay.ds);
+  if (slots > 0) {
+    // 1. T, X, P and a of every chunk
+    hipLaunchKernelGGL((ut_transform_kernel<T, DK, C, true>), dim3(unsigned(slots)), dim3(kThreads), 0, s, k,
+                       beta, tws, H, L, NC, rule, nullptr, 0, q, xws, aws, pws);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    // 2. the state at the start of every chunk (no output)
+    const int NVB = DV / 16;
+    hipLaunchKernelGGL((recurrence_kernel<T, DK, C, 16>), dim3(unsigned(BH * NVB)), dim3(kThreads), 0, s, q, k, v,
+                       tws, s0, static_cast<T*>(nullptr), static_cast<float*>(nullptr), H, L, NC, DV, NVB, 0,
+                       static_cast<const int32_t*>(nullptr), sws);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  }
+  // 3. reverse pass over chunks: dS at every chunk end, and dS_0
+  hipLaunchKernelGGL((bwd_state_kernel<T, DK, C>), dim3(unsigned(BH * (DV / 16))), dim3(kThreads), 0, s, q, k,
+                     dout, tws, pws, dsf, dsws, ds0, H, L, NC, DV, DV / 16);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  if (slots == 0) return hipSuccess;
+  // 4. every chunk's gradients
+  hipLaunchKernelGGL((bwd_chunk_kernel<T, DK, C>), dim3(unsigned(slots)), dim3(kThreads), 0, s, q, k, v, beta,
+                     dout, tws, xws, aws, pws, sws, dsws, dq, dk, dv, dbeta, H, L, NC, DV, rule);
+  return hipGetLastError();
+}
+
+template <typename T, int DK>
+hipError_t bwd_dispatch_c(const T* q, const T* k, const T* v, const T* beta, const float* s0, const T* dout,
+                          const float* dsf, T* dq, T* dk, T* dv, T* dbeta, float* ds0, int B, int H, int64_t L,
+                          int DV, int C, int rule, unsigned char* ws, hipStream_t s) {
+  switch (C) {
+    case 16: return bwd_launch_impl<T, DK, 16>(q, k, v, beta, s0, dout, dsf, dq, dk, dv, dbeta, ds0, B, H, L, DV, rule, ws, s);
+    case 32: return bwd_launch_impl<T, DK, 32>(q, k, v, beta, s0, dout, dsf, dq, dk, dv, dbeta, ds0, B, H, L, DV, rule, ws, s);
+    case 64: return bwd_launch_impl<T, DK, 64>(q, k, v, beta, s0, dout, dsf, dq, dk, dv, dbeta, ds0, B, H, L, DV, rule, ws, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t launch_chunk_bwd(const T* q, const T* k, const T* v, const T* beta, const float* s0, const T* dout,
+                            const float* dsf, T* dq, T* dk, T* dv, T* dbeta, float* ds0, int B, int H, int64_t L,
+                            int DK, int DV, int C, int rule, void* ws, hipStream_t s) {
+  auto* w = static_cast<unsigned char*>(ws);
+  switch (DK) {
+    case 16: return bwd_dispatch_c<T, 16>(q, k, v, beta, s0, dout, dsf, dq, dk, dv, dbeta, ds0, B, H, L, DV, C, rule, w, s);
+    case 32: return bwd_dispatch_c<T, 32>(q, k, v, beta, s0, dout, dsf, dq, dk, dv, dbeta, ds0, B, H, L, DV, C, rule, w, s);
+    case 64: return bwd_dispatch_c<T, 64>(q, k, v, beta, s0, dout, dsf, dq, dk, dv, dbeta, ds0, B, H, L, DV, C, rule, w, s);
+    case 128: return bwd_dispatch_c<T, 128>(q, k, v, beta, s0, dout, dsf, dq, dk, dv, dbeta, ds0, B, H, L, DV, C, rule, w, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template hipError_t launch_chunk_bwd<float>(const float*, const float*, const float*, const float*, const float*,
+                                            const float*, const float*, float*, float*, float*, float*, float*, int,
+                                            int, int64_t, int, int, int, int, void*, hipStream_t);
+template hipError_t launch_chunk_bwd<uint16_t>(const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*,
+                                               const float*, const uint16_t*, const float*, uint16_t*, uint16_t*,
+                                               uint16_t*, uint16_t*, float*, int, int, int64_t, int, int, int, int,
+                                               void*, hipStream_t);
+
+}  // namespace efla

@@ -90,18 +90,26 @@ __device__ __forceinline__ void lds_zero(T* p, int n, int tid) {
 //   X   = (I + diag(a) tril(G, -1))^{-1}          (blocked forward substitution, fp32)
 //   T   = X diag(a)                               -> workspace [B,H,NC,C,C]
 // The row scaling diag(a) is applied inside the solve instead of to G.
+// The instance for the backward pass (BWD) also writes, in fp32 per chunk
+// slot: X (C x C, zeros above the diagonal), a (C) and P = tril(Q K^T)
+// (C x C, the diagonal included), all zero for tokens past the end.
 // ---------------------------------------------------------------------------
-template <typename T, int DK, int C>
+template <typename T, int DK, int C, bool BWD = false>
 __global__ __launch_bounds__(kThreads) void ut_transform_kernel(const T* __restrict__ k,
                                                                 const T* __restrict__ beta,
                                                                 T* __restrict__ tws, int H,
                                                                 int64_t L, int NC, int rule,
-                                                                const int32_t* __restrict__ cu, int N) {
+                                                                const int32_t* __restrict__ cu, int N,
+                                                                const T* __restrict__ q = nullptr,
+                                                                float* __restrict__ xout = nullptr,
+                                                                float* __restrict__ aout = nullptr,
+                                                                float* __restrict__ pout = nullptr) {
   constexpr int DKP = round_up(DK, 32), CP = round_up(C, 32);
   constexpr int NRT = C / 16, NKU_D = DKP / 32;
   constexpr int KP = DKP + (sizeof(T) == 2 ? 8 : 4);
   constexpr int AP = C + 4;
   __shared__ __align__(16) T Ks[CP * KP];
+  __shared__ __align__(16) T Qs[BWD ? CP * KP : 8];
   __shared__ float lam_s[CP], alpha_s[CP];
   __shared__ __align__(16) float Gs[C * AP];  // strictly lower part of K K^T
   __shared__ __align__(16) float Xs[C * AP];  // X = (I + A)^{-1}, lower blocks
@@ -122,16 +130,39 @@ __global__ __launch_bounds__(kThreads) void ut_transform_kernel(const T* __restr
   const int valid = int(sp.len - t0 < C ? sp.len - t0 : C);
   const int64_t row0 = (sp.bos + t0) * H + h;  // token t0 of this sequence and head
 
-  if constexpr (DK < DKP || C < CP) lds_zero(Ks, CP * KP, tid);
+  if constexpr (DK < DKP || C < CP) {
+    lds_zero(Ks, CP * KP, tid);
+    if constexpr (BWD) lds_zero(Qs, CP * KP, tid);
+  }
   float bt = 0.0f;
   if (tid < valid) bt = to_f32(beta[row0 + int64_t(tid) * H]);
   {
-    RowStager<T, C, DK> sk;
+    RowStager<T, C, DK> sk, sq;
     sk.load(k + row0 * DK, int64_t(H) * DK, valid, tid);
+    if constexpr (BWD) sq.load(q + row0 * DK, int64_t(H) * DK, valid, tid);
     if constexpr (DK < DKP || C < CP) __syncthreads();
     sk.store(Ks, KP, tid);
+    if constexpr (BWD) sq.store(Qs, KP, tid);
   }
   __syncthreads();
+  if constexpr (BWD) {
+    // P = tril(Q K^T), diagonal included
+    float* pdst = pout + wg * int64_t(C) * C;
+    for (int i = w; i < NRT * NRT; i += 4) {
+      const int r = i / NRT, c = i % NRT;
+      f32x4 acc = zero4();
+      if (c <= r) {
+#pragma unroll
+        for (int ku = 0; ku < NKU_D; ++ku)
+          mma(acc, lds_frag(Qs, KP, 16 * r + li, ku, g), lds_frag(Ks, KP, 16 * c + li, ku, g));
+      }
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int ii = 16 * r + 4 * g + qq, jj = 16 * c + li;
+        pdst[ii * C + jj] = jj <= ii ? acc[qq] : 0.0f;
+      }
+    }
+  }
 
   // G tiles on and below the diagonal; the diagonal gives lambda.
   constexpr int NTILE = NRT * (NRT + 1) / 2;
@@ -197,6 +228,15 @@ __global__ __launch_bounds__(kThreads) void ut_transform_kernel(const T* __restr
     __syncthreads();
   }
 
+  if constexpr (BWD) {
+    float* xdst = xout + wg * int64_t(C) * C;
+    for (int i = tid; i < C * C; i += kThreads) {
+      const int t = i / C, s = i % C;
+      xdst[i] = s <= t ? Xs[t * AP + s] : 0.0f;
+    }
+    if (tid < C) aout[wg * int64_t(C) + tid] = alpha_s[tid];
+  }
+
   // T = X diag(a), lower triangle, zeros above.
   constexpr int VN = Vec16<T>::n;
   constexpr int VPR = C / VN;
@@ -236,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void recurrence_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ tws, const float* __restrict__ s0, T* __restrict__ o,
     float* __restrict__ sfin, int H, int64_t L, int NC, int DV, int NVB, int remap,
-    const int32_t* __restrict__ cu) {
+    const int32_t* __restrict__ cu, float* __restrict__ states = nullptr) {
   constexpr int DKP = round_up(DK, 32), CP = round_up(C, 32);
   constexpr int NRT = C / 16, NKU_D = DKP / 32, NKU_C = CP / 32;
   constexpr int NCT = BV / 16, NDP = 4 / NCT;
@@ -335,6 +375,20 @@ __global__ __launch_bounds__(kThreads) void recurrence_kernel(
     const int valid = int(sp.len - t0 < C ? sp.len - t0 : C);
     const int64_t row0 = (sp.bos + t0) * H + h;
     if (n + 1 < nc) load_chunk(n + 1);  // in flight during this chunk
+    if (states != nullptr) {  // the state at the start of this chunk (backward pass)
+      float* dst = states + (sp.slot0 + n) * DK * DV;
+#pragma unroll
+      for (int j = 0; j < MAXO; ++j) {
+        const int ku = pw + j * NDP;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const int dim = 32 * ku + 16 * hh + 4 * g + qq;
+            if (ku < NKU_D && dim < DK) dst[dim * DV + col] = Sacc[j][hh][qq];
+          }
+      }
+    }
 
     // partial K S and Q S over this wave's key dims
     f32x4 Y[NRT], Z[NRT];
@@ -465,7 +519,7 @@ __global__ __launch_bounds__(kThreads) void recurrence_kernel(
           const int r = lane / VPRow, c = (lane % VPRow) * VN;
           const int t = 16 * rt + r;
           const u32x4 val = *reinterpret_cast<const u32x4*>(Ow + r * OP + c);
-          if (t < valid)
+          if (t < valid && o != nullptr)
             *reinterpret_cast<u32x4*>(o + (row0 + int64_t(t) * H) * DV + v0 + 16 * cw + c) = val;
         }
       }

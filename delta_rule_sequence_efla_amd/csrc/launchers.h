@@ -50,4 +50,15 @@ bool ut_wave_bf16_supported(int DK, int C);
 hipError_t launch_ut_wave_bf16(const uint16_t* k, const uint16_t* beta, uint16_t* tws, int B, int H, int64_t L,
                                int DK, int C, int rule, const int32_t* cu, int N, hipStream_t s);
 
+// Backward pass of the chunked forward (bwd.hip, bwd_kernels.h): dense
+// batches, any supported d_k / d_v / chunk; ws holds bwd_layout(...).total bytes.
+struct BwdLayout {
+  size_t t, x, p, a, s, ds, total;  // byte offsets of the workspace regions, and the size
+};
+BwdLayout bwd_layout(int B, int H, int64_t L, int DK, int DV, int C, size_t esz);
+template <typename T>
+hipError_t launch_chunk_bwd(const T* q, const T* k, const T* v, const T* beta, const float* s0, const T* dout,
+                            const float* dsf, T* dq, T* dk, T* dv, T* dbeta, float* ds0, int B, int H, int64_t L,
+                            int DK, int DV, int C, int rule, void* ws, hipStream_t s);
+
 }  // namespace efla

@@ -70,6 +70,10 @@ def lib() -> ctypes.CDLL:
         L.efla_chunk_ut_transform_rule.argtypes = [_vp, _vp, _i, _i, _i64, _i, _i, _i, _i, _vp, _sz, _vp]
         L.efla_step_rule.restype = _i
         L.efla_step_rule.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]
+        L.efla_chunk_bwd_workspace_size.restype = _sz
+        L.efla_chunk_bwd_workspace_size.argtypes = [_i, _i, _i64, _i, _i, _i, _i]
+        L.efla_chunk_bwd.restype = _i
+        L.efla_chunk_bwd.argtypes = [_vp] * 12 + [_i, _i, _i64, _i, _i, _i, _i, _i, _vp, _sz, _vp]
         L.efla_chunk_fwd_varlen_workspace_size.restype = _sz
         L.efla_chunk_fwd_varlen_workspace_size.argtypes = [_i, _i, _i64, _i, _i, _i, _i]
         L.efla_chunk_fwd_varlen.restype = _i
@@ -223,6 +227,36 @@ def efla_chunk_recurrence(q, k, v, workspace, s0=None, chunk: int = 64, o=None, 
                                            dk, dv, chunk, _code(q.dtype), _p(workspace),
                                            workspace.numel(), _stream(dev)), "efla_chunk_recurrence")
     return o, s_final
+
+
+def efla_chunk_bwd_workspace_size(B, H, L, d_k, d_v, chunk, dtype) -> int:
+    return int(lib().efla_chunk_bwd_workspace_size(B, H, L, d_k, d_v, chunk, _code(dtype)))
+
+
+def efla_chunk_bwd(q, k, v, beta, d_o, s0=None, ds_final=None, chunk: int = 64, rule: str = "exact",
+                   want_ds0: bool = True, workspace=None):
+    """Gradients through efla_chunk_fwd for dLoss/do = d_o and dLoss/dS_L =
+    ds_final (None: zero).  Returns (dq, dk, dv, dbeta, ds0) in the input
+    dtype (ds0 fp32 [B,H,dk,dv], or None when want_ds0 is False)."""
+    dev = _dev(q, k, v, beta, d_o, workspace, dtype=None)
+    _dev(q, k, v, beta, d_o, dtype=q.dtype)
+    _dev(s0, ds_final, dtype=torch.float32)
+    B, L, H, dk, dv = _chunk_shapes(q, k, v, beta, s0)
+    if d_o.shape != v.shape:
+        raise ValueError("d_o must have the shape of v")
+    if ds_final is not None and ds_final.shape != (B, H, dk, dv):
+        raise ValueError("ds_final must be float32 [B,H,dk,dv]")
+    gq, gk, gv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    gb = torch.empty_like(beta)
+    gs0 = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if want_ds0 else None
+    if workspace is None:
+        n = efla_chunk_bwd_workspace_size(B, H, L, dk, dv, chunk, q.dtype)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib().efla_chunk_bwd(_p(q), _p(k), _p(v), _p(beta), _p(s0), _p(d_o), _p(ds_final), _p(gq), _p(gk),
+                                    _p(gv), _p(gb), _p(gs0), B, H, L, dk, dv, chunk, _code(q.dtype), _rule(rule),
+                                    _p(workspace), workspace.numel(), _stream(dev)), "efla_chunk_bwd")
+    return gq, gk, gv, gb, gs0
 
 
 def efla_chunk_fwd_varlen_workspace_size(N, H, T, d_k, d_v, chunk, dtype) -> int:

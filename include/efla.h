@@ -168,6 +168,29 @@ efla_status efla_chunk_recurrence(const void *q, const void *k, const void *v,
                                   size_t workspace_bytes, void *stream);
 
 /*
+ * efla_chunk_bwd -- gradients through efla_chunk_fwd (same q, k, v, beta, s0,
+ * sizes and rule).  The pages give the forward recurrence only (Method step
+ * 3); the backward pass is its reverse-mode derivative.  For a scalar loss with
+ *     d_o      [B, L, H, d_v] (dtype)     = dLoss / do
+ *     ds_final [B, H, d_k, d_v] float32   = dLoss / dS_L  (NULL: zero)
+ * it writes dq, dk [B, L, H, d_k], dv [B, L, H, d_v], dbeta [B, L, H] (dtype)
+ * and ds0 [B, H, d_k, d_v] float32 = dLoss / ds0 (NULL: not written).  dbeta
+ * and dk include the paths through alpha(beta, lambda) and lambda = ||k||^2.
+ * Arithmetic is float32 throughout (bf16 inputs and d_o are widened exactly;
+ * gradients are rounded to dtype on output).  The workspace (size below) holds
+ * per chunk the UT-transform quantities and the states the pass recomputes;
+ * it is scratch and may be reused once the call has completed on the stream.
+ * q, k, v and the workspace must be 16-byte aligned.
+ */
+size_t efla_chunk_bwd_workspace_size(int B, int H, int64_t L, int d_k, int d_v, int chunk,
+                                     efla_dtype dtype);
+efla_status efla_chunk_bwd(const void *q, const void *k, const void *v, const void *beta,
+                           const float *s0, const void *d_o, const float *ds_final, void *dq,
+                           void *dk, void *dv, void *dbeta, float *ds0, int B, int H, int64_t L,
+                           int d_k, int d_v, int chunk, efla_dtype dtype, efla_rule rule,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Variable-length batches.  N sequences of different lengths packed along one
  * token axis, as a training or serving batch without padding holds them:
  *     q, k [T, H, d_k]   v, o [T, H, d_v]   beta [T, H]   (dtype)

@@ -164,3 +164,23 @@ def test_varlen_workspace_size_and_validation():
     assert call(q=fake + 8) == 1                  # misaligned
     assert call() == 3                            # no workspace
     assert call(ws=fake, wsb=10) == 3             # too small
+
+
+def test_backward_workspace_size_and_validation():
+    f = efla.efla_chunk_bwd_workspace_size
+    assert f(1, 1, 0, 16, 16, 16, torch.float32) == 0
+    assert f(1, 1, 64, 24, 16, 16, torch.float32) == 0
+    # 1.3B shape: T (bf16), X, P (fp32), a, chunk states and their gradients (fp32)
+    slots = 4 * 16 * 64
+    want = slots * (64 * 64 * 2 + 2 * 64 * 64 * 4 + 64 * 4 + 2 * 128 * 128 * 4)
+    assert f(4, 16, 4096, 128, 128, 64, torch.bfloat16) == want
+    L = efla.lib()
+    nul, fake = None, 4096
+
+    def call(B=1, L_=64, dk=16, C=16, rule=0, p=fake, ws=nul, wsb=0, ds0=nul):
+        return L.efla_chunk_bwd(p, p, p, p, nul, p, nul, p, p, p, p, ds0, B, 1, L_, dk, 16, C, 0, rule, ws, wsb, nul)
+
+    assert call(rule=3) == 1 and call(B=0) == 1 and call(dk=24) == 2 and call(C=48) == 2
+    assert call(p=nul) == 1 and call(p=fake + 4) == 1
+    assert call() == 3 and call(ws=fake, wsb=16) == 3
+    assert call(L_=0, p=nul) == 0               # nothing to do, no ds0 wanted
