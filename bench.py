@@ -15,6 +15,8 @@ Prints ONE JSON line.  Besides the contract fields it carries:
                 timed the same way: the pages' throughput comparison of the two
   varlen        efla_chunk_fwd_varlen on the same 16384 tokens and 16 heads packed
                 as 16 sequences of mixed length (varlen_1p3b)
+  backward      efla_chunk_bwd on the benchmark workload (gradients of q, k, v,
+                beta and the initial state), and forward + backward together
   cpu_baseline  the fp64 oracle on the same workload, on this host's cores
 """
 from __future__ import annotations
@@ -47,6 +49,8 @@ def parse_args():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-euler", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--backward-steps", type=int, default=10)
     ap.add_argument("--event-every", type=int, default=8,
                     help="record per-kernel HIP events on one timed step in this many")
     ap.add_argument("--cold-iters", type=int, default=10,
@@ -250,6 +254,35 @@ def main():
                   "note": "back-to-back calls; the longest sequence bounds the sequential pass"}
         del pv, ov, sv, wsv, fv
 
+    backward = None
+    if not args.no_backward:
+        g = torch.Generator(device="cpu").manual_seed(7)
+        d_o = torch.randn(o.shape, generator=g).to(q.dtype).to(dev)
+        dsf = torch.randn(s_final.shape, generator=g).to(dev)
+        gq, gk, gv, gb = (torch.empty_like(x) for x in (q, k, v, beta))
+        gs0 = torch.empty_like(s_final)
+        nb = efla.efla_chunk_bwd_workspace_size(w.B, w.H, w.L, w.dk, w.dv, w.chunk, q.dtype)
+        wsb = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+        bwd = efla.prepare_chunk_bwd(q, k, v, beta, d_o, s0, dsf, gq, gk, gv, gb, gs0, wsb, chunk=w.chunk)
+        bwd()
+        torch.cuda.synchronize()
+        KB = max(1, args.backward_steps)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(KB):
+            bwd()
+        b.record()
+        torch.cuda.synchronize()
+        bus = a.elapsed_time(b) * 1e3 / KB
+        # bytes the backward must move: q, k, v, beta, d_o read; dq, dk, dv, dbeta written; states in/out
+        bwd_bytes = n_ht * ((2 * w.dk + 2 * w.dv + 1) * esz + (2 * w.dk + w.dv + 1) * esz) + 3 * state_bytes
+        backward = {"us": round(bus, 2), "tokens_per_s": round(tokens / (bus / 1e6), 1),
+                    "algorithmic_bytes": bwd_bytes,
+                    "hbm_frac": round(bwd_bytes / (bus / 1e6) / 1e9 / HBM_PEAK_GBS, 4),
+                    "workspace_bytes": nb,
+                    "fwd_plus_bwd_tokens_per_s": round(tokens / ((bus + ms_per_step * 1e3) / 1e6), 1)}
+        del wsb, gq, gk, gv, gb, gs0, d_o, dsf, bwd
+
     decode = None
     if not args.no_decode:
         wd = W.get("decode_1p3b")
@@ -321,6 +354,7 @@ def main():
         "decode": decode,
         "euler": euler,
         "varlen": varlen,
+        "backward": backward,
         "cpu_baseline": cpu,
         "kernel_source_sha256_16": kernel_source_hash(),
     }

@@ -329,7 +329,7 @@ efla_status efla_chunk_bwd(const void* q, const void* k, const void* v, const vo
     if (q == nullptr || k == nullptr || v == nullptr || beta == nullptr || d_o == nullptr || dq == nullptr ||
         dk == nullptr || dv == nullptr || dbeta == nullptr)
       return EFLA_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return EFLA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(d_o)) return EFLA_ERR_INVALID_ARG;
     const size_t need = efla_chunk_bwd_workspace_size(B, H, L, d_k, d_v, chunk, dtype);
     if (workspace == nullptr || workspace_bytes < need) return EFLA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return EFLA_ERR_INVALID_ARG;

@@ -5,7 +5,9 @@
 //   X  [slots][C][C]     fp32          (I + A)^{-1}
 //   P  [slots][C][C]     fp32          tril(Q K^T)
 //   a  [slots][C]        fp32          coefficients
-//   S  [slots][dk][dv]   fp32          state at the start of the chunk
+//   S  [slots][dk][dv]   input dtype   state at the start of the chunk (bf16
+//                                      inputs: the operand values the forward
+//                                      products use)
 //   dS [slots][dk][dv]   fp32          loss gradient at the end of the chunk
 #include "bwd_kernels.h"
 #include "chunk_kernels.h"
@@ -26,9 +28,28 @@ BwdLayout bwd_layout(int B, int H, int64_t L, int DK, int DV, int C, size_t esz)
   w.p = w.x + align256(slots * C * C * 4);
   w.a = w.p + align256(slots * C * C * 4);
   w.s = w.a + align256(slots * C * 4);
-  w.ds = w.s + align256(slots * size_t(DK) * DV * 4);
+  w.ds = w.s + align256(slots * size_t(DK) * DV * esz);
   w.total = w.ds + align256(slots * size_t(DK) * DV * 4);
   return w;
+}
+
+// The forward recurrence again, storing the state at the start of every chunk
+// and no output: the role kernel for the bf16 shapes it covers (its output
+// and P wavefronts then idle), else the generic kernel.
+template <typename T, int DK, int C>
+hipError_t chunk_states(const T* q, const T* k, const T* v, const T* tws, const float* s0, T* states, int B,
+                        int H, int64_t L, int DV, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    const int bv = DV >= 32 ? 32 : 16;
+    if (recurrence_roles_supported(DK, C, bv))
+      return launch_recurrence_roles_bf16(q, k, v, tws, s0, nullptr, nullptr, B, H, L, DK, DV, C, bv, nullptr, 0, s,
+                                          states);
+  }
+  const int NC = int((L + C - 1) / C), NVB = DV / 16;
+  hipLaunchKernelGGL((recurrence_kernel<T, DK, C, 16>), dim3(unsigned(B * H * NVB)), dim3(kThreads), 0, s, q, k, v,
+                     tws, s0, static_cast<T*>(nullptr), static_cast<float*>(nullptr), H, L, NC, DV, NVB, 0,
+                     static_cast<const int32_t*>(nullptr), states);
+  return hipGetLastError();
 }
 
 template <typename T, int DK, int C>
@@ -43,7 +64,7 @@ hipError_t bwd_launch_impl(const T* q, const T* k, const T* v, const T* beta, co
   float* xws = reinterpret_cast<float*>(ws + lay.x);
   float* pws = reinterpret_cast<float*>(ws + lay.p);
   float* aws = reinterpret_cast<float*>(ws + lay.a);
-  float* sws = reinterpret_cast<float*>(ws + lay.s);
+  T* sws = reinterpret_cast<T*>(ws + lay.s);
   float* dsws = reinterpret_cast<float*>(ws + lay.ds);
   if (slots > 0) {
     // 1. T, X, P and a of every chunk
@@ -51,11 +72,7 @@ hipError_t bwd_launch_impl(const T* q, const T* k, const T* v, const T* beta, co
                        beta, tws, H, L, NC, rule, nullptr, 0, q, xws, aws, pws);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     // 2. the state at the start of every chunk (no output)
-    const int NVB = DV / 16;
-    hipLaunchKernelGGL((recurrence_kernel<T, DK, C, 16>), dim3(unsigned(BH * NVB)), dim3(kThreads), 0, s, q, k, v,
-                       tws, s0, static_cast<T*>(nullptr), static_cast<float*>(nullptr), H, L, NC, DV, NVB, 0,
-                       static_cast<const int32_t*>(nullptr), sws);
-    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    if (hipError_t e = chunk_states<T, DK, C>(q, k, v, tws, s0, sws, B, H, L, DV, s); e != hipSuccess) return e;
   }
   // 3. reverse pass over chunks: dS at every chunk end, and dS_0
   hipLaunchKernelGGL((bwd_state_kernel<T, DK, C>), dim3(unsigned(BH * (DV / 16))), dim3(kThreads), 0, s, q, k,

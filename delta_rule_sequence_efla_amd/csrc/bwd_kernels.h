@@ -18,7 +18,8 @@
 //   1. the UT transform's backward instance: T (input dtype), and in fp32
 //      X, a and P per chunk slot;
 //   2. the forward recurrence again, storing the state at the start of every
-//      chunk (fp32);
+//      chunk (in the input dtype: for bf16 inputs the operand values the
+//      forward's products use);
 //   3. bwd_state_kernel: the sequential pass in reverse over chunks, per
 //      (b, h, 16 value columns), storing dS' of every chunk and dS_0;
 //   4. bwd_chunk_kernel: every chunk in parallel, the formulas above, streamed
@@ -82,16 +83,41 @@ __device__ __forceinline__ void efla_alpha_grad(float beta, float lam, int rule,
   da_dl = beta * beta * psi;
 }
 
-// Rows [0, valid) of a C x COLS tile at src (row stride `stride` elements)
-// into fp32 LDS dst (pitch), zeros for rows [valid, ROWS).
-template <typename T>
-__device__ __forceinline__ void load_rows_f32(float* dst, int pitch, const T* src, int64_t stride, int rows,
-                                              int cols, int valid, int tid) {
-  for (int i = tid; i < rows * cols; i += kThreads) {
-    const int r = i / cols, c = i % cols;
-    dst[r * pitch + c] = r < valid ? to_f32(src[r * stride + c]) : 0.0f;
+// A ROWS x COLS tile of T (rows `stride` elements apart) moved into fp32 LDS
+// in two steps, so that the loads of several tiles are all in flight before
+// any is waited on: load() issues 16-byte loads into registers (rows at or
+// past `valid` read as zero), store() widens them into dst (pitch in floats).
+// COLS * sizeof(T) must be a multiple of 16 and rows 16-byte aligned.
+template <typename T, int ROWS, int COLS>
+struct F32Stager {
+  static constexpr int VN = 16 / int(sizeof(T)), VPR = COLS / VN, TOT = ROWS * VPR, CNT = cdiv(TOT, kThreads);
+  u32x4 r[CNT];
+  __device__ __forceinline__ void load(const T* src, int64_t stride, int valid, int tid) {
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) {
+      const int idx = tid + i * kThreads;
+      const int t = idx / VPR, c = (idx % VPR) * VN;
+      r[i] = u32x4{0u, 0u, 0u, 0u};
+      if (idx < TOT && t < valid) r[i] = *reinterpret_cast<const u32x4*>(src + t * stride + c);
+    }
   }
-}
+  __device__ __forceinline__ void store(float* dst, int pitch, int tid) const {
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) {
+      const int idx = tid + i * kThreads;
+      if (idx < TOT) {
+        const int t = idx / VPR, c = (idx % VPR) * VN;
+        union {
+          u32x4 u;
+          T e[VN];
+        } x;
+        x.u = r[i];
+#pragma unroll
+        for (int e = 0; e < VN; ++e) dst[t * pitch + c + e] = to_f32(x.e[e]);
+      }
+    }
+  }
+};
 
 // ---------------------------------------------------------------------------
 // Stage 3: reverse sequential pass.  One workgroup per (b, h, 16 value
@@ -120,44 +146,47 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(
   const SeqSpan sp = seq_span<C>(nullptr, bh / H, h, H, L, NC);
   const int v0 = 16 * vb;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), li = lane & 15, g = lane >> 4;
+  const int64_t qk_stride = int64_t(H) * DK, v_stride = int64_t(H) * DV;
 
+  // zero what the stagers never write: padding rows / columns
+  for (int i = tid; i < CP * QP; i += kThreads) Qs[i] = Ks[i] = 0.0f;
+  for (int i = tid; i < CP * CPP; i += kThreads) Ts[i] = Ps[i] = 0.0f;
+  for (int i = tid; i < CP * VP; i += kThreads) dOs[i] = 0.0f;
   for (int i = tid; i < DKP * 16; i += kThreads) {
     const int d = i / 16, c = i % 16;
     dSs[d * VP + c] = (dsf != nullptr && d < DK) ? dsf[(int64_t(bh) * DK + d) * DV + v0 + c] : 0.0f;
   }
-  // zero what loads never write: padding rows and columns of the C x C tiles
-  if constexpr (C < CP) {
-    for (int i = tid; i < CP * CPP; i += kThreads) Ts[i] = Ps[i] = 0.0f;
-  }
-  __syncthreads();
 
-  for (int n = sp.nc - 1; n >= 0; --n) {
+  // chunk n's operands, staged through registers one chunk ahead
+  F32Stager<T, C, DK> sq, sk;
+  F32Stager<T, C, C> st;
+  F32Stager<float, C, C> spp;
+  F32Stager<T, C, 16> sdo;
+  auto load = [&](int n) {
     const int64_t t0 = int64_t(n) * C;
     const int valid = int(sp.len - t0 < C ? sp.len - t0 : C);
     const int64_t row0 = (sp.bos + t0) * H + h;
+    sq.load(q + row0 * DK, qk_stride, valid, tid);
+    sk.load(k + row0 * DK, qk_stride, valid, tid);
+    sdo.load(dout + row0 * DV + v0, v_stride, valid, tid);
+    st.load(tws + (sp.slot0 + n) * C * C, C, C, tid);
+    spp.load(pws + (sp.slot0 + n) * C * C, C, C, tid);
+  };
+  if (sp.nc > 0) load(sp.nc - 1);
+  __syncthreads();
+
+  for (int n = sp.nc - 1; n >= 0; --n) {
     float* dst = dstates + (sp.slot0 + n) * DK * DV;
     for (int i = tid; i < DK * 16; i += kThreads) {
       const int d = i / 16, c = i % 16;
       dst[d * DV + v0 + c] = dSs[d * VP + c];
     }
-    load_rows_f32(Qs, QP, q + row0 * DK, int64_t(H) * DK, CP, DK, valid, tid);
-    load_rows_f32(Ks, QP, k + row0 * DK, int64_t(H) * DK, CP, DK, valid, tid);
-    if constexpr (DK < DKP) {
-      for (int i = tid; i < CP * (DKP - DK); i += kThreads) {
-        const int r = i / (DKP - DK), c = DK + i % (DKP - DK);
-        Qs[r * QP + c] = Ks[r * QP + c] = 0.0f;
-      }
-    }
-    load_rows_f32(dOs, VP, dout + row0 * DV + v0, int64_t(H) * DV, CP, 16, valid, tid);
-    {
-      const T* ts = tws + (sp.slot0 + n) * C * C;
-      const float* ps = pws + (sp.slot0 + n) * C * C;
-      for (int i = tid; i < C * C; i += kThreads) {
-        const int r = i / C, c = i % C;
-        Ts[r * CPP + c] = to_f32(ts[i]);
-        Ps[r * CPP + c] = ps[i];
-      }
-    }
+    sq.store(Qs, QP, tid);
+    sk.store(Ks, QP, tid);
+    sdo.store(dOs, VP, tid);
+    st.store(Ts, CPP, tid);
+    spp.store(Ps, CPP, tid);
+    if (n > 0) load(n - 1);  // in flight during this chunk
     __syncthreads();
     // E = P^T dO + K dS
     for (int rt = w; rt < CP / 16; rt += 4) {
@@ -213,7 +242,7 @@ template <typename T, int DK, int C>
 __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ beta,
     const T* __restrict__ dout, const T* __restrict__ tws, const float* __restrict__ xws,
-    const float* __restrict__ aws, const float* __restrict__ pws, const float* __restrict__ states,
+    const float* __restrict__ aws, const float* __restrict__ pws, const T* __restrict__ states,
     const float* __restrict__ dstates, T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv,
     T* __restrict__ dbeta, int H, int64_t L, int NC, int DV, int rule) {
   using S = BwdChunkShape<T, DK, C>;
@@ -236,22 +265,24 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), li = lane & 15, g = lane >> 4;
   const int64_t qk_stride = int64_t(H) * DK, v_stride = int64_t(H) * DV;
 
-  // chunk operands
-  for (int i = tid; i < CP * DKP; i += kThreads) {
-    const int r = i / DKP, c = i % DKP;
-    const bool in = r < valid && c < DK;
-    Qs[r * QP + c] = in ? to_f32(q[(row0) * DK + r * qk_stride + c]) : 0.0f;
-    Ks[r * QP + c] = in ? to_f32(k[(row0) * DK + r * qk_stride + c]) : 0.0f;
-  }
+  // chunk operands (16-byte loads, all in flight before the first use)
   {
-    const T* ts = tws + slot * C * C;
-    const float* ps = pws + slot * C * C;
-    for (int i = tid; i < CP * CP; i += kThreads) {
-      const int r = i / CP, c = i % CP;
-      const bool in = r < C && c < C;
-      M0[r * CPP + c] = in ? to_f32(ts[r * C + c]) : 0.0f;
-      M1[r * CPP + c] = in ? ps[r * C + c] : 0.0f;
+    F32Stager<T, C, DK> sq, sk;
+    F32Stager<T, C, C> st;
+    F32Stager<float, C, C> spp;
+    sq.load(q + row0 * DK, qk_stride, valid, tid);
+    sk.load(k + row0 * DK, qk_stride, valid, tid);
+    st.load(tws + slot * C * C, C, C, tid);
+    spp.load(pws + slot * C * C, C, C, tid);
+    if constexpr (C < CP || DK < DKP) {
+      for (int i = tid; i < CP * QP; i += kThreads) Qs[i] = Ks[i] = 0.0f;
+      for (int i = tid; i < CP * CPP; i += kThreads) M0[i] = M1[i] = 0.0f;
+      __syncthreads();
     }
+    sq.store(Qs, QP, tid);
+    sk.store(Ks, QP, tid);
+    st.store(M0, CPP, tid);
+    spp.store(M1, CPP, tid);
   }
   if (tid < CP) as[tid] = tid < C ? aws[slot * C + tid] : 0.0f;
 
@@ -270,21 +301,30 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(
 #pragma unroll
   for (int i = 0; i < NP; ++i) dPa[i] = dTa[i] = zero4();
 
-  const float* st = states + slot * DK * DV;
+  const T* st = states + slot * DK * DV;
   const float* dst = dstates + slot * DK * DV;
+  // one 16-column value block's operands, staged through registers one block ahead
+  F32Stager<T, DK, 16> ss;
+  F32Stager<float, DK, 16> sds;
+  F32Stager<T, C, 16> sv, sdo;
+  auto load_block = [&](int v0) {
+    ss.load(st + v0, DV, DK, tid);
+    sds.load(dst + v0, DV, DK, tid);
+    sv.load(v + row0 * DV + v0, v_stride, valid, tid);
+    sdo.load(dout + row0 * DV + v0, v_stride, valid, tid);
+  };
+  load_block(0);
+  if constexpr (C < CP || DK < DKP) {  // padding rows of the block buffers stay zero
+    __syncthreads();
+    for (int i = tid; i < S::VBUF; i += kThreads) R[i] = 0.0f;
+  }
   for (int v0 = 0; v0 < DV; v0 += 16) {
     __syncthreads();  // previous block's buffers are free (and the operands above are in place)
-    for (int i = tid; i < DKP * 16; i += kThreads) {
-      const int d = i / 16, c = i % 16;
-      Sv[d * VP + c] = d < DK ? st[d * DV + v0 + c] : 0.0f;
-      dSv[d * VP + c] = d < DK ? dst[d * DV + v0 + c] : 0.0f;
-    }
-    for (int i = tid; i < CP * 16; i += kThreads) {
-      const int r = i / 16, c = i % 16;
-      const bool in = r < valid;
-      Vv[r * VP + c] = in ? to_f32(v[row0 * DV + r * v_stride + v0 + c]) : 0.0f;
-      dOv[r * VP + c] = in ? to_f32(dout[row0 * DV + r * v_stride + v0 + c]) : 0.0f;
-    }
+    ss.store(Sv, VP, tid);
+    sds.store(dSv, VP, tid);
+    sv.store(Vv, VP, tid);
+    sdo.store(dOv, VP, tid);
+    if (v0 + 16 < DV) load_block(v0 + 16);  // in flight during this block
     __syncthreads();
     // D = V - K S,  dU = P^T dO + K dS'
     for (int t = w; t < 2 * NCP; t += 4) {
@@ -358,11 +398,13 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(
     }
   }
   {
-    const float* xs = xws + slot * C * C;
-    for (int i = tid; i < CP * CP; i += kThreads) {
-      const int r = i / CP, c = i % CP;
-      X[r * CPP + c] = (r < C && c < C) ? xs[r * C + c] : 0.0f;
+    F32Stager<float, C, C> sx;
+    sx.load(xws + slot * C * C, C, C, tid);
+    if constexpr (C < CP) {
+      for (int i = tid; i < CP * CPP; i += kThreads) X[i] = 0.0f;
+      __syncthreads();
     }
+    sx.store(X, CPP, tid);  // X's rows and columns < C; the zeros above cover the padding
   }
   __syncthreads();
   // dQ += dP K;  dK += dP^T Q;  dX = dT diag(a);  da_j = sum_i dT_ij X_ij

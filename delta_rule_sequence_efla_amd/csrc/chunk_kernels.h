@@ -276,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void recurrence_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ tws, const float* __restrict__ s0, T* __restrict__ o,
     float* __restrict__ sfin, int H, int64_t L, int NC, int DV, int NVB, int remap,
-    const int32_t* __restrict__ cu, float* __restrict__ states = nullptr) {
+    const int32_t* __restrict__ cu, T* __restrict__ states = nullptr) {
   constexpr int DKP = round_up(DK, 32), CP = round_up(C, 32);
   constexpr int NRT = C / 16, NKU_D = DKP / 32, NKU_C = CP / 32;
   constexpr int NCT = BV / 16, NDP = 4 / NCT;
@@ -376,7 +376,7 @@ __global__ __launch_bounds__(kThreads) void recurrence_kernel(
     const int64_t row0 = (sp.bos + t0) * H + h;
     if (n + 1 < nc) load_chunk(n + 1);  // in flight during this chunk
     if (states != nullptr) {  // the state at the start of this chunk (backward pass)
-      float* dst = states + (sp.slot0 + n) * DK * DV;
+      T* dst = states + (sp.slot0 + n) * DK * DV;
 #pragma unroll
       for (int j = 0; j < MAXO; ++j) {
         const int ku = pw + j * NDP;
@@ -385,7 +385,7 @@ __global__ __launch_bounds__(kThreads) void recurrence_kernel(
 #pragma unroll
           for (int qq = 0; qq < 4; ++qq) {
             const int dim = 32 * ku + 16 * hh + 4 * g + qq;
-            if (ku < NKU_D && dim < DK) dst[dim * DV + col] = Sacc[j][hh][qq];
+            if (ku < NKU_D && dim < DK) dst[dim * DV + col] = from_f32<T>(Sacc[j][hh][qq]);
           }
       }
     }

@@ -38,11 +38,13 @@ hipError_t launch_recurrence_tile_bf16(const uint16_t* q, const uint16_t* k, con
 
 // bf16 recurrence with one role per wavefront: chain wavefronts, output, P
 // and DMA (recurrence_roles.h); same d_k and chunk, value blocks of 16 or 32.
+// With states given, the backward pass's instance runs instead: it writes the
+// state at the start of every chunk (bf16, per chunk slot) and no output.
 bool recurrence_roles_supported(int DK, int C, int BV);
 hipError_t launch_recurrence_roles_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                         const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
                                         int B, int H, int64_t L, int DK, int DV, int C, int BV,
-                                        const int32_t* cu, int N, hipStream_t s);
+                                        const int32_t* cu, int N, hipStream_t s, uint16_t* states = nullptr);
 
 // bf16 UT transform with one wavefront per chunk (ut_wave.h); d_k in
 // {32, 64, 128}, chunk in {32, 64}.

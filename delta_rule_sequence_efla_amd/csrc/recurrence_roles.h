@@ -47,12 +47,16 @@ struct RolesShape {
   static constexpr int kP = 0, kChain0 = 1, kOut = NT + 1, kDma = NT + 2;
 };
 
-template <int DK, int C, int BV>
+// ST: the instance for the backward pass, which writes the state at the start
+// of every chunk (the bf16 operand fragments the chains publish, i.e. the
+// values the forward products use) to `states` and no output: its output
+// wavefront copies the fragments and its P wavefront only keeps the barriers.
+template <int DK, int C, int BV, bool ST>
 __global__ __launch_bounds__(64 * (BV / 16 + 3)) void recurrence_roles_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ tws, const float* __restrict__ s0, uint16_t* __restrict__ o,
     float* __restrict__ sfin, int H, int64_t L, int NC, int DV, int NVB, int remap,
-    const int32_t* __restrict__ cu) {
+    const int32_t* __restrict__ cu, uint16_t* __restrict__ states) {
   using S = RolesShape<DK, C, BV>;
   constexpr int NT = S::NT, NRT = S::NRT, NDT = S::NDT, NKU_D = S::NKU_D, NKU_C = S::NKU_C;
   constexpr int NPF = S::NPF;
@@ -227,6 +231,27 @@ __global__ __launch_bounds__(64 * (BV / 16 + 3)) void recurrence_roles_kernel(
         for (int qq = 0; qq < 4; ++qq)
           sfin[(int64_t(bh) * DK + key_phys(16 * dt + 4 * g + qq)) * DV + col] = St[dt][qq];
     }
+  } else if (ST && role == S::kOut) {
+    // S_n fragments of tile ct, k-unit ku: element e of lane (li, g) is state
+    // row key_phys(32 ku + 16 (e / 4) + 4 g + e % 4), column v0 + 16 ct + li
+    for (int n = 0; n < nc; ++n) {
+      sync();  // A: S_n published
+      uint16_t* dst = states + (sp.slot0 + n) * DK * DV;
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+        for (int ku = 0; ku < NKU_D; ++ku) {
+          union {
+            u32x4 u;
+            uint16_t e16[8];
+          } f;
+          f.u = *reinterpret_cast<const u32x4*>(&bS_buf[ct][ku][lane]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            dst[key_phys(32 * ku + 16 * (e / 4) + 4 * g + e % 4) * DV + v0 + 16 * ct + li] = f.e16[e];
+        }
+      sync();  // B
+    }
   } else if (role == S::kOut) {
     // ------------------------------------------------------------- output
     auto step = [&](const uint16_t* __restrict__ cur, int n) {
@@ -281,6 +306,11 @@ __global__ __launch_bounds__(64 * (BV / 16 + 3)) void recurrence_roles_kernel(
       step(slot0, n);
       if (n + 1 < nc) step(slot1, n + 1);
       if (n + 2 < nc) step(slot2, n + 2);
+    }
+  } else if (ST && role == S::kP) {
+    for (int n = 0; n < nc; ++n) {
+      sync();
+      sync();
     }
   } else if (role == S::kP) {
     // ------------------------------------------------------------------ P
@@ -352,25 +382,31 @@ template <int DK, int C, int BV>
 hipError_t recurrence_roles_launch_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                      const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
                                      int B, int H, int64_t L, int DV, const int32_t* cu, int N,
-                                     hipStream_t stream) {
+                                     uint16_t* states, hipStream_t stream) {
   const int NC = cu == nullptr ? int((L + C - 1) / C) : int(L / C) + N;  // chunk slots per sequence / head
   const int BH = (cu == nullptr ? B : N) * H;
   const int NVB = DV / BV;
   const int nwg = BH * NVB;
   if (nwg == 0) return hipSuccess;
   const int remap = (BH % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((recurrence_roles_kernel<DK, C, BV>), dim3(unsigned(nwg)), dim3(RolesShape<DK, C, BV>::THREADS),
-                     0, stream, q, k, v, tws, s0, o, sfin, H, L, NC, DV, NVB, remap, cu);
+  if (states != nullptr)
+    hipLaunchKernelGGL((recurrence_roles_kernel<DK, C, BV, true>), dim3(unsigned(nwg)),
+                       dim3(RolesShape<DK, C, BV>::THREADS), 0, stream, q, k, v, tws, s0, o, sfin, H, L, NC, DV, NVB,
+                       remap, cu, states);
+  else
+    hipLaunchKernelGGL((recurrence_roles_kernel<DK, C, BV, false>), dim3(unsigned(nwg)),
+                       dim3(RolesShape<DK, C, BV>::THREADS), 0, stream, q, k, v, tws, s0, o, sfin, H, L, NC, DV, NVB,
+                       remap, cu, states);
   return hipGetLastError();
 }
 
 template <int DK, int C>
 hipError_t recurrence_roles_bv(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* tws,
                             const float* s0, uint16_t* o, float* sfin, int B, int H, int64_t L, int DV,
-                            int BV, const int32_t* cu, int N, hipStream_t s) {
+                            int BV, const int32_t* cu, int N, uint16_t* states, hipStream_t s) {
   switch (BV) {
-    case 16: return recurrence_roles_launch_impl<DK, C, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, s);
-    case 32: return recurrence_roles_launch_impl<DK, C, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, s);
+    case 16: return recurrence_roles_launch_impl<DK, C, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, states, s);
+    case 32: return recurrence_roles_launch_impl<DK, C, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, states, s);
   }
   return hipErrorInvalidValue;
 }
@@ -378,18 +414,18 @@ hipError_t recurrence_roles_bv(const uint16_t* q, const uint16_t* k, const uint1
 inline hipError_t launch_recurrence_roles(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                        const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
                                        int B, int H, int64_t L, int DK, int DV, int C, int BV,
-                                       const int32_t* cu, int N, hipStream_t s) {
+                                       const int32_t* cu, int N, uint16_t* states, hipStream_t s) {
   if (C == 32) {
     switch (DK) {
-      case 32: return recurrence_roles_bv<32, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, s);
-      case 64: return recurrence_roles_bv<64, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, s);
-      case 128: return recurrence_roles_bv<128, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, s);
+      case 32: return recurrence_roles_bv<32, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, states, s);
+      case 64: return recurrence_roles_bv<64, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, states, s);
+      case 128: return recurrence_roles_bv<128, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, states, s);
     }
   } else if (C == 64) {
     switch (DK) {
-      case 32: return recurrence_roles_bv<32, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, s);
-      case 64: return recurrence_roles_bv<64, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, s);
-      case 128: return recurrence_roles_bv<128, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, s);
+      case 32: return recurrence_roles_bv<32, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, states, s);
+      case 64: return recurrence_roles_bv<64, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, states, s);
+      case 128: return recurrence_roles_bv<128, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, states, s);
     }
   }
   return hipErrorInvalidValue;

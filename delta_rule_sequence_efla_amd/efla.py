@@ -375,6 +375,18 @@ def prepare_chunk_fwd(q, k, v, beta, s0, o, s_final, workspace, chunk: int = 64,
                         "efla_chunk_fwd", (q, k, v, beta, s0, o, s_final, workspace))
 
 
+def prepare_chunk_bwd(q, k, v, beta, d_o, s0, ds_final, dq, dk, dv, dbeta, ds0, workspace, chunk: int = 64,
+                      rule: str = "exact"):
+    dev = _dev(q, k, v, beta, d_o, dq, dk, dv, dbeta, dtype=q.dtype)
+    _dev(s0, ds_final, ds0, dtype=torch.float32)
+    B, L, H, d_k, d_v = _chunk_shapes(q, k, v, beta, s0)
+    return PreparedCall(lib().efla_chunk_bwd,
+                        (_p(q), _p(k), _p(v), _p(beta), _p(s0), _p(d_o), _p(ds_final), _p(dq), _p(dk), _p(dv),
+                         _p(dbeta), _p(ds0), B, H, L, d_k, d_v, chunk, _code(q.dtype), _rule(rule), _p(workspace),
+                         workspace.numel(), _stream(dev)),
+                        "efla_chunk_bwd", (q, k, v, beta, d_o, s0, ds_final, dq, dk, dv, dbeta, ds0, workspace))
+
+
 def prepare_step(q, k, v, beta, state, o, rule: str = "exact"):
     dev = _dev(q, k, v, beta, o, dtype=q.dtype)
     _dev(state, dtype=torch.float32)

@@ -180,7 +180,7 @@ efla_status efla_chunk_recurrence(const void *q, const void *k, const void *v,
  * gradients are rounded to dtype on output).  The workspace (size below) holds
  * per chunk the UT-transform quantities and the states the pass recomputes;
  * it is scratch and may be reused once the call has completed on the stream.
- * q, k, v and the workspace must be 16-byte aligned.
+ * q, k, v, d_o and the workspace must be 16-byte aligned.
  */
 size_t efla_chunk_bwd_workspace_size(int B, int H, int64_t L, int d_k, int d_v, int chunk,
                                      efla_dtype dtype);

@@ -104,3 +104,12 @@ def test_backward_1p3b_heads_short_sequence():
     w = W.get("shape_1p3b")
     inp = W.generate(w, device="cuda", B=1, L=512, H=4, seed=937)
     _check(inp, 64, "shape_1p3b heads, L=512", seed=8)
+
+
+@pytest.mark.slow
+def test_backward_full_1p3b_shape():
+    """The benchmark workload (B=4, H=16, L=4096, d=128, chunk 64, bf16) in the
+    launch configuration bench.py times."""
+    require_gpu()
+    w = W.get("shape_1p3b")
+    _check(W.generate(w, device="cuda"), 64, "shape_1p3b full", seed=9)
