@@ -17,6 +17,8 @@ Prints ONE JSON line.  Besides the contract fields it carries:
                 as 16 sequences of mixed length (varlen_1p3b)
   backward      efla_chunk_bwd on the benchmark workload (gradients of q, k, v,
                 beta and the initial state), and forward + backward together
+  segmented     the stiff long-context workload (B=1, H=16, L=65536): the plain
+                chunked pass against efla_chunk_fwd_segmented
   cpu_baseline  the fp64 oracle on the same workload, on this host's cores
 """
 from __future__ import annotations
@@ -50,6 +52,7 @@ def parse_args():
     ap.add_argument("--no-euler", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-segmented", action="store_true")
     ap.add_argument("--backward-steps", type=int, default=10)
     ap.add_argument("--event-every", type=int, default=8,
                     help="record per-kernel HIP events on one timed step in this many")
@@ -283,6 +286,39 @@ def main():
                     "fwd_plus_bwd_tokens_per_s": round(tokens / ((bus + ms_per_step * 1e3) / 1e6), 1)}
         del wsb, gq, gk, gv, gb, gs0, d_o, dsf, bwd
 
+    segmented = None
+    if not args.no_segmented:
+        wl = W.get("stiff_64k")
+        li = W.generate(wl, device=dev)
+        ol = torch.empty_like(li["v"])
+        sl = torch.empty((wl.B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device=dev)
+        segs = efla.default_segments(wl.B, wl.H, wl.L, wl.dv, wl.chunk)
+        wsp = efla.alloc_workspace(wl.B, wl.H, wl.L, wl.dk, wl.dv, wl.chunk, li["q"].dtype, dev)
+        nsg = efla.efla_chunk_fwd_segmented_workspace_size(wl.B, wl.H, wl.L, wl.dk, wl.dv, wl.chunk, segs,
+                                                           li["q"].dtype)
+        wss = torch.empty(max(nsg, 1), dtype=torch.uint8, device=dev)
+        plain = efla.prepare_chunk_fwd(li["q"], li["k"], li["v"], li["beta"], li["s0"], ol, sl, wsp, chunk=wl.chunk)
+        seg = efla.prepare_chunk_fwd_segmented(li["q"], li["k"], li["v"], li["beta"], li["s0"], ol, sl, wss,
+                                               chunk=wl.chunk, segments=segs)
+
+        def time_us(f, n=5):
+            f()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(n):
+                f()
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1e3 / n
+
+        pus, sus = time_us(plain), time_us(seg)
+        segmented = {"workload": wl.name, "segments": segs, "plain_us": round(pus, 1), "segmented_us": round(sus, 1),
+                     "plain_tokens_per_s": round(wl.tokens / (pus / 1e6), 1),
+                     "segmented_tokens_per_s": round(wl.tokens / (sus / 1e6), 1),
+                     "speedup": round(pus / sus, 3)}
+        del li, ol, sl, wsp, wss, plain, seg
+
     decode = None
     if not args.no_decode:
         wd = W.get("decode_1p3b")
@@ -355,6 +391,7 @@ def main():
         "euler": euler,
         "varlen": varlen,
         "backward": backward,
+        "segmented": segmented,
         "cpu_baseline": cpu,
         "kernel_source_sha256_16": kernel_source_hash(),
     }

@@ -94,11 +94,19 @@ efla_status launch_ut(const void* k, const void* beta, int B, int H, int64_t L, 
 
 // Stage 2 launch (arguments already validated).  The one-wavefront-per-tile
 // kernel takes dense batches only; packed batches use the role kernel there.
+// trans: the chunk-transition run of the segment scan (V = 0, identity start,
+// d_k value columns, final states only; v and d_v are ignored).
 efla_status launch_rec(const void* q, const void* k, const void* v, const float* s0, void* o, float* s_final,
                        int B, int H, int64_t L, int d_k, int d_v, int chunk, efla_dtype dtype,
-                       const void* workspace, const int32_t* cu, int N, hipStream_t s) {
+                       const void* workspace, const int32_t* cu, int N, hipStream_t s, bool trans = false) {
+  if (trans) {
+    v = k;
+    d_v = d_k;
+    o = nullptr;
+    s0 = nullptr;
+  }
   RecChoice rc = choose_recurrence(dtype, d_k, d_v, chunk);
-  if (rc.kind == Rec::kTile && cu != nullptr)
+  if (rc.kind == Rec::kTile && (cu != nullptr || trans || o == nullptr))
     rc.kind = efla::recurrence_roles_supported(d_k, chunk, rc.bv) ? Rec::kRoles : Rec::kGeneric;
   if (dtype == EFLA_BF16) {
     const auto* qb = static_cast<const uint16_t*>(q);
@@ -109,7 +117,7 @@ efla_status launch_rec(const void* q, const void* k, const void* v, const float*
     switch (rc.kind) {
       case Rec::kRoles:
         return from_hip(efla::launch_recurrence_roles_bf16(qb, kb, vb, tb, s0, ob, s_final, B, H, L, d_k, d_v,
-                                                           chunk, rc.bv, cu, N, s));
+                                                           chunk, rc.bv, cu, N, s, nullptr, trans));
       case Rec::kTile:
         return from_hip(efla::launch_recurrence_tile_bf16(qb, kb, vb, tb, s0, ob, s_final, B, H, L, d_k, d_v,
                                                           chunk, rc.bv, s));
@@ -117,12 +125,12 @@ efla_status launch_rec(const void* q, const void* k, const void* v, const float*
         break;
     }
     return from_hip(efla::launch_recurrence<uint16_t>(qb, kb, vb, tb, s0, ob, s_final, B, H, L, d_k, d_v,
-                                                      chunk, rc.bv, cu, N, s));
+                                                      chunk, rc.bv, cu, N, s, int(trans)));
   }
   return from_hip(efla::launch_recurrence<float>(
       static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
       static_cast<const float*>(workspace), s0, static_cast<float*>(o), s_final, B, H, L, d_k, d_v, chunk,
-      rc.bv, cu, N, s));
+      rc.bv, cu, N, s, int(trans)));
 }
 
 }  // namespace
@@ -349,4 +357,76 @@ efla_status efla_chunk_bwd(const void* q, const void* k, const void* v, const vo
       static_cast<const float*>(beta), s0, static_cast<const float*>(d_o), ds_final, static_cast<float*>(dq),
       static_cast<float*>(dk), static_cast<float*>(dv), static_cast<float*>(dbeta), ds0, B, H, L, d_k, d_v, chunk,
       int(rule), workspace, s));
+}
+
+namespace {
+// Layout of the segment scan's workspace (byte offsets, 256-aligned regions).
+struct SegLayout {
+  int G;        // segments per sequence actually used
+  int64_t Ls;   // tokens per segment (a multiple of the chunk)
+  size_t t, cu, m, n, sin, total;
+};
+size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+SegLayout seg_layout(int B, int H, int64_t L, int d_k, int d_v, int chunk, int segments, efla_dtype dt) {
+  SegLayout w{};
+  const int64_t nc = (L + chunk - 1) / chunk;
+  const int64_t per = (nc + segments - 1) / segments;  // chunks per segment
+  w.Ls = per * chunk;
+  w.G = int((L + w.Ls - 1) / w.Ls);
+  const int64_t U = int64_t(B) * w.G;
+  const int64_t slots = int64_t(H) * ((int64_t(B) * L) / chunk + U);
+  w.t = 0;
+  w.cu = al256(size_t(slots) * chunk * chunk * elem_bytes(dt));
+  w.m = w.cu + al256(size_t(U + 1) * 4);
+  w.n = w.m + al256(size_t(U) * H * d_k * d_k * 4);
+  w.sin = w.n + al256(size_t(U) * H * d_k * d_v * 4);
+  w.total = w.sin + al256(size_t(U) * H * d_k * d_v * 4);
+  return w;
+}
+}  // namespace
+
+size_t efla_chunk_fwd_segmented_workspace_size(int B, int H, int64_t L, int d_k, int d_v, int chunk, int segments,
+                                               efla_dtype dtype) {
+  if (segments < 1 || check_chunk_shape(B, H, L, d_k, d_v, chunk, dtype) != EFLA_OK || L == 0) return 0;
+  if (int64_t(B) * L > INT32_MAX) return 0;
+  return seg_layout(B, H, L, d_k, d_v, chunk, segments, dtype).total;
+}
+
+efla_status efla_chunk_fwd_segmented(const void* q, const void* k, const void* v, const void* beta,
+                                     const float* s0, void* o, float* s_final, int B, int H, int64_t L, int d_k,
+                                     int d_v, int chunk, int segments, efla_dtype dtype, efla_rule rule,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_rule(rule) || segments < 1) return EFLA_ERR_INVALID_ARG;
+  const efla_status st = check_chunk_shape(B, H, L, d_k, d_v, chunk, dtype);
+  if (st != EFLA_OK) return st;
+  if (int64_t(B) * L > INT32_MAX) return EFLA_ERR_UNSUPPORTED;  // offsets of the packed view are int32
+  if (L == 0) return efla_chunk_fwd_rule(q, k, v, beta, s0, o, s_final, B, H, L, d_k, d_v, chunk, dtype, rule,
+                                         nullptr, 0, stream);
+  if (q == nullptr || k == nullptr || v == nullptr || beta == nullptr || o == nullptr) return EFLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return EFLA_ERR_INVALID_ARG;
+  const SegLayout lay = seg_layout(B, H, L, d_k, d_v, chunk, segments, dtype);
+  if (workspace == nullptr || workspace_bytes < lay.total) return EFLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return EFLA_ERR_INVALID_ARG;
+  const int64_t U = int64_t(B) * lay.G, T = int64_t(B) * L;
+  if (U * H * (d_k / 16 > d_v / 16 ? d_k / 16 : d_v / 16) > kMaxGrid) return EFLA_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto* ws = static_cast<unsigned char*>(workspace);
+  void* tws = ws + lay.t;
+  auto* cu = reinterpret_cast<int32_t*>(ws + lay.cu);
+  auto* M = reinterpret_cast<float*>(ws + lay.m);
+  auto* Nf = reinterpret_cast<float*>(ws + lay.n);
+  auto* Sin = reinterpret_cast<float*>(ws + lay.sin);
+  const int Ui = int(U);
+  efla_status e = from_hip(efla::launch_seg_offsets(cu, B, lay.G, L, lay.Ls, s));
+  // T of every chunk of every segment (the packed view of the batch)
+  if (e == EFLA_OK) e = launch_ut(k, beta, 1, H, T, d_k, chunk, dtype, rule, tws, cu, Ui, s);
+  // every segment from zero: N_g
+  if (e == EFLA_OK) e = launch_rec(q, k, v, nullptr, nullptr, Nf, 1, H, T, d_k, d_v, chunk, dtype, tws, cu, Ui, s);
+  // every segment's transition: M_g
+  if (e == EFLA_OK) e = launch_rec(q, k, v, nullptr, nullptr, M, 1, H, T, d_k, d_v, chunk, dtype, tws, cu, Ui, s, true);
+  // incoming states along each sequence, and the final state
+  if (e == EFLA_OK) e = from_hip(efla::launch_seg_combine(M, Nf, s0, Sin, s_final, B, H, lay.G, d_k, d_v, s));
+  // every segment again from its incoming state, with output
+  if (e == EFLA_OK) e = launch_rec(q, k, v, Sin, o, nullptr, 1, H, T, d_k, d_v, chunk, dtype, tws, cu, Ui, s);
+  return e;
 }

@@ -276,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void recurrence_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ tws, const float* __restrict__ s0, T* __restrict__ o,
     float* __restrict__ sfin, int H, int64_t L, int NC, int DV, int NVB, int remap,
-    const int32_t* __restrict__ cu, T* __restrict__ states = nullptr) {
+    const int32_t* __restrict__ cu, T* __restrict__ states = nullptr, int trans = 0) {
   constexpr int DKP = round_up(DK, 32), CP = round_up(C, 32);
   constexpr int NRT = C / 16, NKU_D = DKP / 32, NKU_C = CP / 32;
   constexpr int NCT = BV / 16, NDP = 4 / NCT;
@@ -339,8 +339,9 @@ __global__ __launch_bounds__(kThreads) void recurrence_kernel(
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
         const int dim = 32 * ku + 16 * hh + 4 * g + qq;
-        Sacc[j][hh][qq] =
-            (s0 != nullptr && ku < NKU_D && dim < DK) ? s0[(int64_t(bh) * DK + dim) * DV + col] : 0.0f;
+        // trans: the chunk-transition run, from the identity with V = 0
+        Sacc[j][hh][qq] = trans ? (dim == col ? 1.0f : 0.0f)
+                        : (s0 != nullptr && ku < NKU_D && dim < DK) ? s0[(int64_t(bh) * DK + dim) * DV + col] : 0.0f;
       }
   }
 
@@ -354,7 +355,7 @@ __global__ __launch_bounds__(kThreads) void recurrence_kernel(
     const int64_t row0 = (sp.bos + t0) * H + h;
     sq.load(q + row0 * DK, qk_stride, valid, tid);
     sk.load(k + row0 * DK, qk_stride, valid, tid);
-    sv.load(v + row0 * DV + v0, v_stride, valid, tid);
+    sv.load(v + row0 * DV + v0, v_stride, trans ? 0 : valid, tid);
     st.load(tws + (sp.slot0 + n) * C * C, C, C, tid);
   };
   auto store_chunk = [&]() {
@@ -559,7 +560,7 @@ hipError_t ut_transform_launch_impl(const T* k, const T* beta, T* tws, int B, in
 template <typename T, int DK, int C, int BV>
 hipError_t recurrence_launch_impl(const T* q, const T* k, const T* v, const T* tws, const float* s0,
                                   T* o, float* sfin, int B, int H, int64_t L, int DV,
-                                  const int32_t* cu, int N, hipStream_t stream) {
+                                  const int32_t* cu, int N, hipStream_t stream, int trans) {
   const int NC = cu == nullptr ? int((L + C - 1) / C) : int(L / C) + N;
   const int BH = (cu == nullptr ? B : N) * H;
   const int NVB = DV / BV;
@@ -567,7 +568,7 @@ hipError_t recurrence_launch_impl(const T* q, const T* k, const T* v, const T* t
   if (nwg == 0) return hipSuccess;
   const int remap = (BH % 8 == 0) ? 1 : 0;
   hipLaunchKernelGGL((recurrence_kernel<T, DK, C, BV>), dim3(unsigned(nwg)), dim3(kThreads), 0, stream,
-                     q, k, v, tws, s0, o, sfin, H, L, NC, DV, NVB, remap, cu);
+                     q, k, v, tws, s0, o, sfin, H, L, NC, DV, NVB, remap, cu, static_cast<T*>(nullptr), trans);
   return hipGetLastError();
 }
 
@@ -601,23 +602,23 @@ template <> struct BVSet<float> { static constexpr bool has32 = false, has64 = f
 template <typename T, int DK, int C>
 hipError_t rec_dispatch_bv(const T* q, const T* k, const T* v, const T* tws, const float* s0, T* o,
                            float* sfin, int B, int H, int64_t L, int DV, int BV, const int32_t* cu, int N,
-                           hipStream_t s) {
-  if (BV == 16) return recurrence_launch_impl<T, DK, C, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, s);
+                           hipStream_t s, int trans) {
+  if (BV == 16) return recurrence_launch_impl<T, DK, C, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, s, trans);
   if constexpr (BVSet<T>::has32)
-    if (BV == 32) return recurrence_launch_impl<T, DK, C, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, s);
+    if (BV == 32) return recurrence_launch_impl<T, DK, C, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, s, trans);
   if constexpr (BVSet<T>::has64)
-    if (BV == 64) return recurrence_launch_impl<T, DK, C, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, s);
+    if (BV == 64) return recurrence_launch_impl<T, DK, C, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, s, trans);
   return hipErrorInvalidValue;
 }
 
 template <typename T, int DK>
 hipError_t rec_dispatch_c(const T* q, const T* k, const T* v, const T* tws, const float* s0, T* o,
                           float* sfin, int B, int H, int64_t L, int DV, int C, int BV, const int32_t* cu,
-                          int N, hipStream_t s) {
+                          int N, hipStream_t s, int trans) {
   switch (C) {
-    case 16: return rec_dispatch_bv<T, DK, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, s);
-    case 32: return rec_dispatch_bv<T, DK, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, s);
-    case 64: return rec_dispatch_bv<T, DK, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, s);
+    case 16: return rec_dispatch_bv<T, DK, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, s, trans);
+    case 32: return rec_dispatch_bv<T, DK, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, s, trans);
+    case 64: return rec_dispatch_bv<T, DK, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, s, trans);
   }
   return hipErrorInvalidValue;
 }
@@ -625,12 +626,12 @@ hipError_t rec_dispatch_c(const T* q, const T* k, const T* v, const T* tws, cons
 template <typename T>
 hipError_t launch_recurrence(const T* q, const T* k, const T* v, const T* tws, const float* s0,
                              T* o, float* sfin, int B, int H, int64_t L, int DK, int DV, int C,
-                             int BV, const int32_t* cu, int N, hipStream_t s) {
+                             int BV, const int32_t* cu, int N, hipStream_t s, int trans) {
   switch (DK) {
-    case 16: return rec_dispatch_c<T, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, C, BV, cu, N, s);
-    case 32: return rec_dispatch_c<T, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, C, BV, cu, N, s);
-    case 64: return rec_dispatch_c<T, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, C, BV, cu, N, s);
-    case 128: return rec_dispatch_c<T, 128>(q, k, v, tws, s0, o, sfin, B, H, L, DV, C, BV, cu, N, s);
+    case 16: return rec_dispatch_c<T, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, C, BV, cu, N, s, trans);
+    case 32: return rec_dispatch_c<T, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, C, BV, cu, N, s, trans);
+    case 64: return rec_dispatch_c<T, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, C, BV, cu, N, s, trans);
+    case 128: return rec_dispatch_c<T, 128>(q, k, v, tws, s0, o, sfin, B, H, L, DV, C, BV, cu, N, s, trans);
   }
   return hipErrorInvalidValue;
 }

@@ -25,7 +25,7 @@ hipError_t launch_ut_transform(const T* k, const T* beta, T* tws, int B, int H, 
 template <typename T>
 hipError_t launch_recurrence(const T* q, const T* k, const T* v, const T* tws, const float* s0,
                              T* o, float* sfin, int B, int H, int64_t L, int DK, int DV, int C,
-                             int BV, const int32_t* cu, int N, hipStream_t stream);
+                             int BV, const int32_t* cu, int N, hipStream_t stream, int trans = 0);
 
 // bf16 recurrence with one wavefront per 16-column state tile and a DMA-fed
 // LDS ring (recurrence_tile.h); d_k in {32, 64, 128}, chunk in {32, 64},
@@ -40,11 +40,14 @@ hipError_t launch_recurrence_tile_bf16(const uint16_t* q, const uint16_t* k, con
 // and DMA (recurrence_roles.h); same d_k and chunk, value blocks of 16 or 32.
 // With states given, the backward pass's instance runs instead: it writes the
 // state at the start of every chunk (bf16, per chunk slot) and no output.
+// o == NULL: final states only.  trans: the chunk-transition instance (V = 0,
+// identity initial state, final states only; pass v = k and DV = DK).
 bool recurrence_roles_supported(int DK, int C, int BV);
 hipError_t launch_recurrence_roles_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                         const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
                                         int B, int H, int64_t L, int DK, int DV, int C, int BV,
-                                        const int32_t* cu, int N, hipStream_t s, uint16_t* states = nullptr);
+                                        const int32_t* cu, int N, hipStream_t s, uint16_t* states = nullptr,
+                                        bool trans = false);
 
 // bf16 UT transform with one wavefront per chunk (ut_wave.h); d_k in
 // {32, 64, 128}, chunk in {32, 64}.
@@ -62,5 +65,11 @@ template <typename T>
 hipError_t launch_chunk_bwd(const T* q, const T* k, const T* v, const T* beta, const float* s0, const T* dout,
                             const float* dsf, T* dq, T* dk, T* dv, T* dbeta, float* ds0, int B, int H, int64_t L,
                             int DK, int DV, int C, int rule, void* ws, hipStream_t s);
+
+// Segment scan (seg.hip): offsets of the packed view of B sequences of L
+// tokens cut into G segments of Ls tokens, and the combine along each sequence.
+hipError_t launch_seg_offsets(int32_t* cu, int B, int G, int64_t L, int64_t Ls, hipStream_t s);
+hipError_t launch_seg_combine(const float* M, const float* N, const float* s0, float* sin, float* sfin, int B, int H,
+                              int G, int DK, int DV, hipStream_t s);
 
 }  // namespace efla

@@ -47,17 +47,27 @@ struct RolesShape {
   static constexpr int kP = 0, kChain0 = 1, kOut = NT + 1, kDma = NT + 2;
 };
 
-// ST: the instance for the backward pass, which writes the state at the start
-// of every chunk (the bf16 operand fragments the chains publish, i.e. the
-// values the forward products use) to `states` and no output: its output
-// wavefront copies the fragments and its P wavefront only keeps the barriers.
-template <int DK, int C, int BV, bool ST>
+// Instances (MODE):
+//   kFwd     the forward pass: output and final state.
+//   kStates  for the backward pass: writes the state at the start of every
+//            chunk (the bf16 operand fragments the chains publish, i.e. the
+//            values the forward's products use) to `states`, and no output;
+//            the output wavefront copies the fragments.
+//   kFinal   the final state only (no output).
+//   kTrans   the chunk transition: V = 0 and the identity as the initial
+//            state, final state only, so that it ends as the product of the
+//            chunks' (I - K^T T K) over the value columns' rows of I.
+// Without output the P wavefront (and in kFinal / kTrans the output
+// wavefront) only keeps the barriers.
+enum RolesMode { kFwd = 0, kStates = 1, kFinal = 2, kTrans = 3 };
+template <int DK, int C, int BV, int MODE>
 __global__ __launch_bounds__(64 * (BV / 16 + 3)) void recurrence_roles_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ tws, const float* __restrict__ s0, uint16_t* __restrict__ o,
     float* __restrict__ sfin, int H, int64_t L, int NC, int DV, int NVB, int remap,
     const int32_t* __restrict__ cu, uint16_t* __restrict__ states) {
   using S = RolesShape<DK, C, BV>;
+  constexpr bool ST = MODE == kStates, NOOUT = MODE != kFwd, VZERO = MODE == kTrans;
   constexpr int NT = S::NT, NRT = S::NRT, NDT = S::NDT, NKU_D = S::NKU_D, NKU_C = S::NKU_C;
   constexpr int NPF = S::NPF;
   __shared__ __align__(1024) uint16_t slot0[S::SLOT];
@@ -140,7 +150,8 @@ __global__ __launch_bounds__(64 * (BV / 16 + 3)) void recurrence_roles_kernel(
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq)
-        St[dt][qq] = s0 != nullptr ? s0[(int64_t(bh) * DK + key_phys(16 * dt + 4 * g + qq)) * DV + col] : 0.0f;
+        St[dt][qq] = VZERO ? (key_phys(16 * dt + 4 * g + qq) == col ? 1.0f : 0.0f)
+                   : s0 != nullptr ? s0[(int64_t(bh) * DK + key_phys(16 * dt + 4 * g + qq)) * DV + col] : 0.0f;
 #pragma unroll
     for (int ku = 0; ku < NKU_D; ++ku) {
       bS[ku] = acc_frag<uint16_t>(St[2 * ku], St[2 * ku + 1]);
@@ -180,7 +191,7 @@ __global__ __launch_bounds__(64 * (BV / 16 + 3)) void recurrence_roles_kernel(
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) Y[rt][qq] = static_cast<float>(Vt[rt][qq]) - Y[rt][qq];
+        for (int qq = 0; qq < 4; ++qq) Y[rt][qq] = (VZERO ? 0.0f : static_cast<float>(Vt[rt][qq])) - Y[rt][qq];
       Frag<uint16_t> bD[NKU_C];
 #pragma unroll
       for (int ku = 0; ku < NKU_C; ++ku)
@@ -237,9 +248,9 @@ __global__ __launch_bounds__(64 * (BV / 16 + 3)) void recurrence_roles_kernel(
     for (int n = 0; n < nc; ++n) {
       sync();  // A: S_n published
       uint16_t* dst = states + (sp.slot0 + n) * DK * DV;
-#pragma unroll
+#pragma unroll 1
       for (int ct = 0; ct < NT; ++ct)
-#pragma unroll
+#pragma unroll 1
         for (int ku = 0; ku < NKU_D; ++ku) {
           union {
             u32x4 u;
@@ -252,7 +263,7 @@ __global__ __launch_bounds__(64 * (BV / 16 + 3)) void recurrence_roles_kernel(
         }
       sync();  // B
     }
-  } else if (role == S::kOut) {
+  } else if (!NOOUT && role == S::kOut) {
     // ------------------------------------------------------------- output
     auto step = [&](const uint16_t* __restrict__ cur, int n) {
       const uint16_t* Qs = cur + S::QOFF;
@@ -307,12 +318,12 @@ __global__ __launch_bounds__(64 * (BV / 16 + 3)) void recurrence_roles_kernel(
       if (n + 1 < nc) step(slot1, n + 1);
       if (n + 2 < nc) step(slot2, n + 2);
     }
-  } else if (ST && role == S::kP) {
+  } else if (NOOUT && (role == S::kP || role == S::kOut)) {
     for (int n = 0; n < nc; ++n) {
       sync();
       sync();
     }
-  } else if (role == S::kP) {
+  } else if (!NOOUT && role == S::kP) {
     // ------------------------------------------------------------------ P
     // P_n = tril(Q K^T) of chunk n, split over the key dimension: k-units
     // 0 .. KH-1 after barrier B of step n-1 (chunk n is complete there, and
@@ -382,31 +393,42 @@ template <int DK, int C, int BV>
 hipError_t recurrence_roles_launch_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                      const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
                                      int B, int H, int64_t L, int DV, const int32_t* cu, int N,
-                                     uint16_t* states, hipStream_t stream) {
+                                     uint16_t* states, bool trans, hipStream_t stream) {
   const int NC = cu == nullptr ? int((L + C - 1) / C) : int(L / C) + N;  // chunk slots per sequence / head
   const int BH = (cu == nullptr ? B : N) * H;
   const int NVB = DV / BV;
   const int nwg = BH * NVB;
   if (nwg == 0) return hipSuccess;
   const int remap = (BH % 8 == 0) ? 1 : 0;
-  if (states != nullptr)
-    hipLaunchKernelGGL((recurrence_roles_kernel<DK, C, BV, true>), dim3(unsigned(nwg)),
-                       dim3(RolesShape<DK, C, BV>::THREADS), 0, stream, q, k, v, tws, s0, o, sfin, H, L, NC, DV, NVB,
-                       remap, cu, states);
-  else
-    hipLaunchKernelGGL((recurrence_roles_kernel<DK, C, BV, false>), dim3(unsigned(nwg)),
-                       dim3(RolesShape<DK, C, BV>::THREADS), 0, stream, q, k, v, tws, s0, o, sfin, H, L, NC, DV, NVB,
-                       remap, cu, states);
+  const int mode = states != nullptr ? kStates : trans ? kTrans : o == nullptr ? kFinal : kFwd;
+  const dim3 grid{unsigned(nwg)}, block{unsigned(RolesShape<DK, C, BV>::THREADS)};
+  switch (mode) {
+    case kFwd:
+      hipLaunchKernelGGL((recurrence_roles_kernel<DK, C, BV, kFwd>), grid, block, 0, stream, q, k, v, tws, s0, o,
+                         sfin, H, L, NC, DV, NVB, remap, cu, states);
+      break;
+    case kStates:
+      hipLaunchKernelGGL((recurrence_roles_kernel<DK, C, BV, kStates>), grid, block, 0, stream, q, k, v, tws, s0, o,
+                         sfin, H, L, NC, DV, NVB, remap, cu, states);
+      break;
+    case kFinal:
+      hipLaunchKernelGGL((recurrence_roles_kernel<DK, C, BV, kFinal>), grid, block, 0, stream, q, k, v, tws, s0, o,
+                         sfin, H, L, NC, DV, NVB, remap, cu, states);
+      break;
+    default:
+      hipLaunchKernelGGL((recurrence_roles_kernel<DK, C, BV, kTrans>), grid, block, 0, stream, q, k, v, tws, s0, o,
+                         sfin, H, L, NC, DV, NVB, remap, cu, states);
+  }
   return hipGetLastError();
 }
 
 template <int DK, int C>
 hipError_t recurrence_roles_bv(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* tws,
                             const float* s0, uint16_t* o, float* sfin, int B, int H, int64_t L, int DV,
-                            int BV, const int32_t* cu, int N, uint16_t* states, hipStream_t s) {
+                            int BV, const int32_t* cu, int N, uint16_t* states, bool trans, hipStream_t s) {
   switch (BV) {
-    case 16: return recurrence_roles_launch_impl<DK, C, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, states, s);
-    case 32: return recurrence_roles_launch_impl<DK, C, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, states, s);
+    case 16: return recurrence_roles_launch_impl<DK, C, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, states, trans, s);
+    case 32: return recurrence_roles_launch_impl<DK, C, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, states, trans, s);
   }
   return hipErrorInvalidValue;
 }
@@ -414,18 +436,18 @@ hipError_t recurrence_roles_bv(const uint16_t* q, const uint16_t* k, const uint1
 inline hipError_t launch_recurrence_roles(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                        const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
                                        int B, int H, int64_t L, int DK, int DV, int C, int BV,
-                                       const int32_t* cu, int N, uint16_t* states, hipStream_t s) {
+                                       const int32_t* cu, int N, uint16_t* states, bool trans, hipStream_t s) {
   if (C == 32) {
     switch (DK) {
-      case 32: return recurrence_roles_bv<32, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, states, s);
-      case 64: return recurrence_roles_bv<64, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, states, s);
-      case 128: return recurrence_roles_bv<128, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, states, s);
+      case 32: return recurrence_roles_bv<32, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, states, trans, s);
+      case 64: return recurrence_roles_bv<64, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, states, trans, s);
+      case 128: return recurrence_roles_bv<128, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, states, trans, s);
     }
   } else if (C == 64) {
     switch (DK) {
-      case 32: return recurrence_roles_bv<32, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, states, s);
-      case 64: return recurrence_roles_bv<64, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, states, s);
-      case 128: return recurrence_roles_bv<128, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, states, s);
+      case 32: return recurrence_roles_bv<32, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, states, trans, s);
+      case 64: return recurrence_roles_bv<64, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, states, trans, s);
+      case 128: return recurrence_roles_bv<128, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, states, trans, s);
     }
   }
   return hipErrorInvalidValue;

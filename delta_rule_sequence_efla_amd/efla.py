@@ -70,6 +70,10 @@ def lib() -> ctypes.CDLL:
         L.efla_chunk_ut_transform_rule.argtypes = [_vp, _vp, _i, _i, _i64, _i, _i, _i, _i, _vp, _sz, _vp]
         L.efla_step_rule.restype = _i
         L.efla_step_rule.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]
+        L.efla_chunk_fwd_segmented_workspace_size.restype = _sz
+        L.efla_chunk_fwd_segmented_workspace_size.argtypes = [_i, _i, _i64, _i, _i, _i, _i, _i]
+        L.efla_chunk_fwd_segmented.restype = _i
+        L.efla_chunk_fwd_segmented.argtypes = [_vp] * 7 + [_i, _i, _i64, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]
         L.efla_chunk_bwd_workspace_size.restype = _sz
         L.efla_chunk_bwd_workspace_size.argtypes = [_i, _i, _i64, _i, _i, _i, _i]
         L.efla_chunk_bwd.restype = _i
@@ -227,6 +231,56 @@ def efla_chunk_recurrence(q, k, v, workspace, s0=None, chunk: int = 64, o=None, 
                                            dk, dv, chunk, _code(q.dtype), _p(workspace),
                                            workspace.numel(), _stream(dev)), "efla_chunk_recurrence")
     return o, s_final
+
+
+COMPUTE_UNITS = 256  # MI355X
+
+
+def default_segments(B, H, L, d_v, chunk) -> int:
+    """Segments per sequence for efla_chunk_fwd_segmented: enough recurrence
+    workgroups (B * H * d_v / 32 per segment) to reach the compute units."""
+    per_seg = max(1, B * H * max(1, d_v // 32))
+    nc = max(1, (L + chunk - 1) // chunk)
+    return max(1, min(nc, COMPUTE_UNITS // per_seg))
+
+
+def efla_chunk_fwd_segmented_workspace_size(B, H, L, d_k, d_v, chunk, segments, dtype) -> int:
+    return int(lib().efla_chunk_fwd_segmented_workspace_size(B, H, L, d_k, d_v, chunk, segments, _code(dtype)))
+
+
+def efla_chunk_fwd_segmented(q, k, v, beta, s0=None, chunk: int = 64, segments=None, o=None, s_final=None,
+                             workspace=None, want_final: bool = True, rule: str = "exact"):
+    """efla_chunk_fwd with each sequence cut into `segments` runs that proceed
+    in parallel (None: default_segments).  Same results up to rounding."""
+    dev = _dev(q, k, v, beta, o, workspace, dtype=None)
+    _dev(q, k, v, beta, o, dtype=q.dtype)
+    _dev(s0, s_final, dtype=torch.float32)
+    B, L, H, dk, dv = _chunk_shapes(q, k, v, beta, s0)
+    if segments is None:
+        segments = default_segments(B, H, L, dv, chunk)
+    if o is None:
+        o = torch.empty((B, L, H, dv), dtype=q.dtype, device=dev)
+    if s_final is None and want_final:
+        s_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if workspace is None:
+        n = efla_chunk_fwd_segmented_workspace_size(B, H, L, dk, dv, chunk, segments, q.dtype)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib().efla_chunk_fwd_segmented(_p(q), _p(k), _p(v), _p(beta), _p(s0), _p(o), _p(s_final), B, H, L,
+                                              dk, dv, chunk, segments, _code(q.dtype), _rule(rule), _p(workspace),
+                                              workspace.numel(), _stream(dev)), "efla_chunk_fwd_segmented")
+    return o, s_final
+
+
+def prepare_chunk_fwd_segmented(q, k, v, beta, s0, o, s_final, workspace, chunk: int = 64, segments: int = 1,
+                                rule: str = "exact"):
+    dev = _dev(q, k, v, beta, o, dtype=q.dtype)
+    _dev(s0, s_final, dtype=torch.float32)
+    B, L, H, dk, dv = _chunk_shapes(q, k, v, beta, s0)
+    return PreparedCall(lib().efla_chunk_fwd_segmented,
+                        (_p(q), _p(k), _p(v), _p(beta), _p(s0), _p(o), _p(s_final), B, H, L, dk, dv, chunk,
+                         segments, _code(q.dtype), _rule(rule), _p(workspace), workspace.numel(), _stream(dev)),
+                        "efla_chunk_fwd_segmented", (q, k, v, beta, s0, o, s_final, workspace))
 
 
 def efla_chunk_bwd_workspace_size(B, H, L, d_k, d_v, chunk, dtype) -> int:

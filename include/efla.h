@@ -222,6 +222,28 @@ efla_status efla_chunk_fwd_varlen(const void *q, const void *k, const void *v, c
                                   size_t workspace_bytes, void *stream);
 
 /*
+ * efla_chunk_fwd_segmented -- efla_chunk_fwd for batches of few, long
+ * sequences: each sequence is cut into `segments` runs of whole chunks that
+ * proceed in parallel.  The update is affine in the state (Method step 3), so
+ * a run maps its incoming state S to M S + N, with M the product of the
+ * chunks' (I - K^T T K) and N the state the run reaches from zero.  The call
+ * computes every run's N and M (two passes over the segments in parallel),
+ * chains the incoming states along each sequence, then reruns every segment
+ * from its incoming state with output: three passes of the work over
+ * `segments` times as many workgroups, a gain where B * H * d_v / 32 is well
+ * below the GPU's 256 compute units.  Results equal efla_chunk_fwd's up to
+ * rounding.  Arguments as for efla_chunk_fwd_rule, plus segments >= 1 (more
+ * than the sequence's chunks is clamped); B * L < 2^31.
+ */
+size_t efla_chunk_fwd_segmented_workspace_size(int B, int H, int64_t L, int d_k, int d_v, int chunk,
+                                               int segments, efla_dtype dtype);
+efla_status efla_chunk_fwd_segmented(const void *q, const void *k, const void *v, const void *beta,
+                                     const float *s0, void *o, float *s_final, int B, int H, int64_t L,
+                                     int d_k, int d_v, int chunk, int segments, efla_dtype dtype,
+                                     efla_rule rule, void *workspace, size_t workspace_bytes,
+                                     void *stream);
+
+/*
  * efla_step -- one decode step: a single token per (n, h) applied in place
  * (Method step 3):
  *     state[n, h] = (I - alpha k k^T) state[n, h] + alpha k v^T

@@ -184,3 +184,25 @@ def test_backward_workspace_size_and_validation():
     assert call(p=nul) == 1 and call(p=fake + 4) == 1
     assert call() == 3 and call(ws=fake, wsb=16) == 3
     assert call(L_=0, p=nul) == 0               # nothing to do, no ds0 wanted
+
+
+def test_segmented_workspace_size_and_validation():
+    f = efla.efla_chunk_fwd_segmented_workspace_size
+    assert f(1, 1, 0, 16, 16, 16, 4, torch.float32) == 0
+    assert f(1, 1, 64, 16, 16, 16, 0, torch.float32) == 0
+    # stiff_64k with 4 segments: T slots, offsets, M, N and incoming states
+    U, slots = 4, 16 * (65536 // 64 + 4)
+    r = lambda x: (x + 255) // 256 * 256
+    want = r(slots * 64 * 64 * 2) + r((U + 1) * 4) + r(U * 16 * 128 * 128 * 4) + 2 * r(U * 16 * 128 * 128 * 4)
+    assert f(1, 16, 65536, 128, 128, 64, 4, torch.bfloat16) == want
+    assert efla.default_segments(1, 16, 65536, 128, 64) == 4
+    assert efla.default_segments(4, 16, 4096, 128, 64) == 1
+    assert efla.default_segments(1, 1, 64, 128, 64) == 1
+    L = efla.lib()
+    nul, fake = None, 4096
+
+    def call(seg=4, rule=0, p=fake, ws=nul, wsb=0, L_=256):
+        return L.efla_chunk_fwd_segmented(p, p, p, p, nul, p, nul, 1, 1, L_, 16, 16, 16, seg, 0, rule, ws, wsb, nul)
+
+    assert call(seg=0) == 1 and call(rule=5) == 1 and call(p=nul) == 1 and call(p=fake + 8) == 1
+    assert call() == 3 and call(ws=fake, wsb=64) == 3
