@@ -354,12 +354,18 @@ def main():
         cores = oracle.default_threads()
         threads = min(cores, w.B * w.H)
         qa, ka, va, ba, sa = (to_f64(x) for x in (q, k, v, beta, s0))
-        t = time.perf_counter()
-        oracle.forward(qa, ka, va, ba, sa, nthreads=threads)
-        ct = time.perf_counter() - t
-        cpu = {"value": round(tokens / ct, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        # whole passes over the workload until about 15 s of CPU time (1 to 8 passes)
+        passes, wall, cpu_s = 0, 0.0, 0.0
+        while passes < 8 and (passes == 0 or cpu_s < 15.0):
+            t, c = time.perf_counter(), time.process_time()
+            oracle.forward(qa, ka, va, ba, sa, nthreads=threads)
+            wall += time.perf_counter() - t
+            cpu_s += time.process_time() - c
+            passes += 1
+        cpu = {"value": round(tokens * passes / wall, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
                "sample": f"the whole {w.name} workload ({w.B * w.H} sequences x {w.L} tokens), "
-                         f"fp64 token-by-token recurrence, one pass, {ct:.2f} s wall"}
+                         f"fp64 token-by-token recurrence, {passes} passes, {wall:.2f} s wall, "
+                         f"{cpu_s:.1f} s of CPU time"}
 
     line = {
         "metric": METRIC,

@@ -18,6 +18,12 @@ constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
 
 efla_status from_hip(hipError_t e) { return e == hipSuccess ? EFLA_OK : EFLA_ERR_HIP; }
 
+size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Packed batches of at most this many sequences run longest first (the
+// ordering kernel compares every pair of sequences).
+constexpr int kMaxOrderedSeqs = 4096;
+
 // The kernels move q, k, v, T and states with 16-byte vector accesses.
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -98,7 +104,8 @@ efla_status launch_ut(const void* k, const void* beta, int B, int H, int64_t L, 
 // d_k value columns, final states only; v and d_v are ignored).
 efla_status launch_rec(const void* q, const void* k, const void* v, const float* s0, void* o, float* s_final,
                        int B, int H, int64_t L, int d_k, int d_v, int chunk, efla_dtype dtype,
-                       const void* workspace, const int32_t* cu, int N, hipStream_t s, bool trans = false) {
+                       const void* workspace, const int32_t* cu, int N, hipStream_t s, bool trans = false,
+                       const int32_t* order = nullptr) {
   if (trans) {
     v = k;
     d_v = d_k;
@@ -117,7 +124,7 @@ efla_status launch_rec(const void* q, const void* k, const void* v, const float*
     switch (rc.kind) {
       case Rec::kRoles:
         return from_hip(efla::launch_recurrence_roles_bf16(qb, kb, vb, tb, s0, ob, s_final, B, H, L, d_k, d_v,
-                                                           chunk, rc.bv, cu, N, s, nullptr, trans));
+                                                           chunk, rc.bv, cu, N, s, nullptr, trans, order));
       case Rec::kTile:
         return from_hip(efla::launch_recurrence_tile_bf16(qb, kb, vb, tb, s0, ob, s_final, B, H, L, d_k, d_v,
                                                           chunk, rc.bv, s));
@@ -125,12 +132,12 @@ efla_status launch_rec(const void* q, const void* k, const void* v, const float*
         break;
     }
     return from_hip(efla::launch_recurrence<uint16_t>(qb, kb, vb, tb, s0, ob, s_final, B, H, L, d_k, d_v,
-                                                      chunk, rc.bv, cu, N, s, int(trans)));
+                                                      chunk, rc.bv, cu, N, s, int(trans), order));
   }
   return from_hip(efla::launch_recurrence<float>(
       static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
       static_cast<const float*>(workspace), s0, static_cast<float*>(o), s_final, B, H, L, d_k, d_v, chunk,
-      rc.bv, cu, N, s, int(trans)));
+      rc.bv, cu, N, s, int(trans), order));
 }
 
 }  // namespace
@@ -288,7 +295,9 @@ size_t efla_chunk_fwd_varlen_workspace_size(int N, int H, int64_t T, int d_k, in
   if (!valid_dim(d_k) || !valid_dim(d_v) || !valid_chunk(chunk)) return 0;
   const int64_t slots = T / chunk + N;  // chunk slots per head
   if (int64_t(H) * slots > kMaxGrid) return 0;
-  return size_t(H) * size_t(slots) * size_t(chunk) * size_t(chunk) * elem_bytes(dtype);
+  // T slots, then the schedule (int32 per sequence)
+  return al256(size_t(H) * size_t(slots) * size_t(chunk) * size_t(chunk) * elem_bytes(dtype)) +
+         al256(size_t(N) * 4);
 }
 
 efla_status efla_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void* beta,
@@ -311,13 +320,22 @@ efla_status efla_chunk_fwd_varlen(const void* q, const void* k, const void* v, c
     if (!aligned16(workspace)) return EFLA_ERR_INVALID_ARG;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* order = nullptr;
   if (T > 0) {
+    if (N <= kMaxOrderedSeqs) {
+      order = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(workspace) +
+                                         al256(size_t(H) * size_t(slots) * size_t(chunk) * size_t(chunk) *
+                                               elem_bytes(dtype)));
+      const efla_status s0r = from_hip(efla::launch_varlen_order(cu_seqlens, N, T, chunk, order, s));
+      if (s0r != EFLA_OK) return s0r;
+    }
     const efla_status s1 = launch_ut(k, beta, 1, H, T, d_k, chunk, dtype, rule, workspace, cu_seqlens, N, s);
     if (s1 != EFLA_OK) return s1;
   } else if (s_final == nullptr) {
     return EFLA_OK;
   }
-  return launch_rec(q, k, v, s0, o, s_final, 1, H, T, d_k, d_v, chunk, dtype, workspace, cu_seqlens, N, s);
+  return launch_rec(q, k, v, s0, o, s_final, 1, H, T, d_k, d_v, chunk, dtype, workspace, cu_seqlens, N, s, false,
+                    order);
 }
 
 size_t efla_chunk_bwd_workspace_size(int B, int H, int64_t L, int d_k, int d_v, int chunk, efla_dtype dtype) {
@@ -366,7 +384,6 @@ struct SegLayout {
   int64_t Ls;   // tokens per segment (a multiple of the chunk)
   size_t t, cu, m, n, sin, total;
 };
-size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 SegLayout seg_layout(int B, int H, int64_t L, int d_k, int d_v, int chunk, int segments, efla_dtype dt) {
   SegLayout w{};
   const int64_t nc = (L + chunk - 1) / chunk;

@@ -10,7 +10,7 @@ template hipError_t launch_ut_transform<uint16_t>(const uint16_t*, const uint16_
 template hipError_t launch_recurrence<uint16_t>(const uint16_t*, const uint16_t*, const uint16_t*,
                                                 const uint16_t*, const float*, uint16_t*, float*, int,
                                                 int, int64_t, int, int, int, int, const int32_t*, int,
-                                                hipStream_t, int);
+                                                hipStream_t, int, const int32_t*);
 
 bool recurrence_tile_supported(int DK, int C, int BV) { return tile_supported(DK, C, BV); }
 hipError_t launch_recurrence_tile_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -276,7 +276,8 @@ __global__ __launch_bounds__(kThreads) void recurrence_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ tws, const float* __restrict__ s0, T* __restrict__ o,
     float* __restrict__ sfin, int H, int64_t L, int NC, int DV, int NVB, int remap,
-    const int32_t* __restrict__ cu, T* __restrict__ states = nullptr, int trans = 0) {
+    const int32_t* __restrict__ cu, T* __restrict__ states = nullptr, int trans = 0,
+    const int32_t* __restrict__ order = nullptr, int nseq = 0) {
   constexpr int DKP = round_up(DK, 32), CP = round_up(C, 32);
   constexpr int NRT = C / 16, NKU_D = DKP / 32, NKU_C = CP / 32;
   constexpr int NCT = BV / 16, NDP = 4 / NCT;
@@ -311,6 +312,7 @@ __global__ __launch_bounds__(kThreads) void recurrence_kernel(
     bh = x / NVB;
     vb = x % NVB;
   }
+  if (order != nullptr) bh = seq_of_rank(order, bh / H, nseq) * H + bh % H;  // packed: longest first
   const int64_t h = bh % H;
   const SeqSpan sp = seq_span<C>(cu, bh / H, h, H, L, NC);  // sequence bh / H
   const int nc = sp.nc;
@@ -560,15 +562,17 @@ hipError_t ut_transform_launch_impl(const T* k, const T* beta, T* tws, int B, in
 template <typename T, int DK, int C, int BV>
 hipError_t recurrence_launch_impl(const T* q, const T* k, const T* v, const T* tws, const float* s0,
                                   T* o, float* sfin, int B, int H, int64_t L, int DV,
-                                  const int32_t* cu, int N, hipStream_t stream, int trans) {
+                                  const int32_t* cu, int N, hipStream_t stream, int trans, const int32_t* order) {
   const int NC = cu == nullptr ? int((L + C - 1) / C) : int(L / C) + N;
   const int BH = (cu == nullptr ? B : N) * H;
   const int NVB = DV / BV;
   const int nwg = BH * NVB;
   if (nwg == 0) return hipSuccess;
+  if (cu == nullptr) order = nullptr;  // dense batches keep their order
   const int remap = (BH % 8 == 0) ? 1 : 0;
   hipLaunchKernelGGL((recurrence_kernel<T, DK, C, BV>), dim3(unsigned(nwg)), dim3(kThreads), 0, stream,
-                     q, k, v, tws, s0, o, sfin, H, L, NC, DV, NVB, remap, cu, static_cast<T*>(nullptr), trans);
+                     q, k, v, tws, s0, o, sfin, H, L, NC, DV, NVB, remap, cu, static_cast<T*>(nullptr), trans,
+                     order, N);
   return hipGetLastError();
 }
 
@@ -602,23 +606,23 @@ template <> struct BVSet<float> { static constexpr bool has32 = false, has64 = f
 template <typename T, int DK, int C>
 hipError_t rec_dispatch_bv(const T* q, const T* k, const T* v, const T* tws, const float* s0, T* o,
                            float* sfin, int B, int H, int64_t L, int DV, int BV, const int32_t* cu, int N,
-                           hipStream_t s, int trans) {
-  if (BV == 16) return recurrence_launch_impl<T, DK, C, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, s, trans);
+                           hipStream_t s, int trans, const int32_t* order) {
+  if (BV == 16) return recurrence_launch_impl<T, DK, C, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, s, trans, order);
   if constexpr (BVSet<T>::has32)
-    if (BV == 32) return recurrence_launch_impl<T, DK, C, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, s, trans);
+    if (BV == 32) return recurrence_launch_impl<T, DK, C, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, s, trans, order);
   if constexpr (BVSet<T>::has64)
-    if (BV == 64) return recurrence_launch_impl<T, DK, C, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, s, trans);
+    if (BV == 64) return recurrence_launch_impl<T, DK, C, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, s, trans, order);
   return hipErrorInvalidValue;
 }
 
 template <typename T, int DK>
 hipError_t rec_dispatch_c(const T* q, const T* k, const T* v, const T* tws, const float* s0, T* o,
                           float* sfin, int B, int H, int64_t L, int DV, int C, int BV, const int32_t* cu,
-                          int N, hipStream_t s, int trans) {
+                          int N, hipStream_t s, int trans, const int32_t* order) {
   switch (C) {
-    case 16: return rec_dispatch_bv<T, DK, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, s, trans);
-    case 32: return rec_dispatch_bv<T, DK, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, s, trans);
-    case 64: return rec_dispatch_bv<T, DK, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, s, trans);
+    case 16: return rec_dispatch_bv<T, DK, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, s, trans, order);
+    case 32: return rec_dispatch_bv<T, DK, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, s, trans, order);
+    case 64: return rec_dispatch_bv<T, DK, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, s, trans, order);
   }
   return hipErrorInvalidValue;
 }
@@ -626,12 +630,12 @@ hipError_t rec_dispatch_c(const T* q, const T* k, const T* v, const T* tws, cons
 template <typename T>
 hipError_t launch_recurrence(const T* q, const T* k, const T* v, const T* tws, const float* s0,
                              T* o, float* sfin, int B, int H, int64_t L, int DK, int DV, int C,
-                             int BV, const int32_t* cu, int N, hipStream_t s, int trans) {
+                             int BV, const int32_t* cu, int N, hipStream_t s, int trans, const int32_t* order) {
   switch (DK) {
-    case 16: return rec_dispatch_c<T, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, C, BV, cu, N, s, trans);
-    case 32: return rec_dispatch_c<T, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, C, BV, cu, N, s, trans);
-    case 64: return rec_dispatch_c<T, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, C, BV, cu, N, s, trans);
-    case 128: return rec_dispatch_c<T, 128>(q, k, v, tws, s0, o, sfin, B, H, L, DV, C, BV, cu, N, s, trans);
+    case 16: return rec_dispatch_c<T, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, C, BV, cu, N, s, trans, order);
+    case 32: return rec_dispatch_c<T, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, C, BV, cu, N, s, trans, order);
+    case 64: return rec_dispatch_c<T, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, C, BV, cu, N, s, trans, order);
+    case 128: return rec_dispatch_c<T, 128>(q, k, v, tws, s0, o, sfin, B, H, L, DV, C, BV, cu, N, s, trans, order);
   }
   return hipErrorInvalidValue;
 }

@@ -205,6 +205,14 @@ __device__ __forceinline__ SeqSpan seq_span(const int32_t* __restrict__ cu, int 
 // Packed batches: slot j (0 .. NC-1) of head h belongs to chunk n of sequence
 // u, found by binary search over the slot offsets floor(cu[u] / C) + u (which
 // increase with u); false for a slot no chunk uses.
+// Sequence handled in rank r of a packed batch of N sequences (order: the
+// permutation of [0, N) written by varlen_order_kernel; an entry outside it
+// falls back to r).
+__device__ __forceinline__ int seq_of_rank(const int32_t* __restrict__ order, int r, int N) {
+  const int u = order[r];
+  return (u >= 0 && u < N) ? u : r;
+}
+
 template <int C>
 __device__ __forceinline__ bool slot_chunk(const int32_t* __restrict__ cu, int N, int64_t j, int64_t h, int H,
                                            int64_t L, int NC, SeqSpan& sp, int& n) {

@@ -22,10 +22,13 @@ template <typename T>
 hipError_t launch_ut_transform(const T* k, const T* beta, T* tws, int B, int H, int64_t L, int DK,
                                int C, int rule, const int32_t* cu, int N, hipStream_t stream);
 
+// order (packed batches only, nullable): the schedule of sequences, rank ->
+// sequence, from launch_varlen_order; workgroups of rank 0 start first.
 template <typename T>
 hipError_t launch_recurrence(const T* q, const T* k, const T* v, const T* tws, const float* s0,
                              T* o, float* sfin, int B, int H, int64_t L, int DK, int DV, int C,
-                             int BV, const int32_t* cu, int N, hipStream_t stream, int trans = 0);
+                             int BV, const int32_t* cu, int N, hipStream_t stream, int trans = 0,
+                             const int32_t* order = nullptr);
 
 // bf16 recurrence with one wavefront per 16-column state tile and a DMA-fed
 // LDS ring (recurrence_tile.h); d_k in {32, 64, 128}, chunk in {32, 64},
@@ -47,7 +50,7 @@ hipError_t launch_recurrence_roles_bf16(const uint16_t* q, const uint16_t* k, co
                                         const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
                                         int B, int H, int64_t L, int DK, int DV, int C, int BV,
                                         const int32_t* cu, int N, hipStream_t s, uint16_t* states = nullptr,
-                                        bool trans = false);
+                                        bool trans = false, const int32_t* order = nullptr);
 
 // bf16 UT transform with one wavefront per chunk (ut_wave.h); d_k in
 // {32, 64, 128}, chunk in {32, 64}.
@@ -65,6 +68,12 @@ template <typename T>
 hipError_t launch_chunk_bwd(const T* q, const T* k, const T* v, const T* beta, const float* s0, const T* dout,
                             const float* dsf, T* dq, T* dk, T* dv, T* dbeta, float* ds0, int B, int H, int64_t L,
                             int DK, int DV, int C, int rule, void* ws, hipStream_t s);
+
+// Schedule of a packed batch (varlen.hip): order[r] = the sequence of rank r,
+// sequences by chunk count, longest first (ties by index), so that the
+// recurrence's workgroups, dispatched in index order, start the longest
+// chains first.  Always a permutation of [0, N), whatever the offsets hold.
+hipError_t launch_varlen_order(const int32_t* cu, int N, int64_t T, int C, int32_t* order, hipStream_t s);
 
 // Segment scan (seg.hip): offsets of the packed view of B sequences of L
 // tokens cut into G segments of Ls tokens, and the combine along each sequence.

@@ -65,7 +65,7 @@ __global__ __launch_bounds__(64 * (BV / 16 + 3)) void recurrence_roles_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ tws, const float* __restrict__ s0, uint16_t* __restrict__ o,
     float* __restrict__ sfin, int H, int64_t L, int NC, int DV, int NVB, int remap,
-    const int32_t* __restrict__ cu, uint16_t* __restrict__ states) {
+    const int32_t* __restrict__ cu, uint16_t* __restrict__ states, const int32_t* __restrict__ order, int nseq) {
   using S = RolesShape<DK, C, BV>;
   constexpr bool ST = MODE == kStates, NOOUT = MODE != kFwd, VZERO = MODE == kTrans;
   constexpr int NT = S::NT, NRT = S::NRT, NDT = S::NDT, NKU_D = S::NKU_D, NKU_C = S::NKU_C;
@@ -87,6 +87,7 @@ __global__ __launch_bounds__(64 * (BV / 16 + 3)) void recurrence_roles_kernel(
     bh = x / NVB;
     vb = x % NVB;
   }
+  if (order != nullptr) bh = seq_of_rank(order, bh / H, nseq) * H + bh % H;  // packed: longest first
   const int64_t h = bh % H;
   const SeqSpan sp = seq_span<C>(cu, bh / H, h, H, L, NC);  // sequence bh / H
   const int nc = sp.nc;
@@ -393,31 +394,32 @@ template <int DK, int C, int BV>
 hipError_t recurrence_roles_launch_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                      const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
                                      int B, int H, int64_t L, int DV, const int32_t* cu, int N,
-                                     uint16_t* states, bool trans, hipStream_t stream) {
+                                     uint16_t* states, bool trans, const int32_t* order, hipStream_t stream) {
   const int NC = cu == nullptr ? int((L + C - 1) / C) : int(L / C) + N;  // chunk slots per sequence / head
   const int BH = (cu == nullptr ? B : N) * H;
   const int NVB = DV / BV;
   const int nwg = BH * NVB;
   if (nwg == 0) return hipSuccess;
+  if (cu == nullptr) order = nullptr;  // dense batches keep their order
   const int remap = (BH % 8 == 0) ? 1 : 0;
   const int mode = states != nullptr ? kStates : trans ? kTrans : o == nullptr ? kFinal : kFwd;
   const dim3 grid{unsigned(nwg)}, block{unsigned(RolesShape<DK, C, BV>::THREADS)};
   switch (mode) {
     case kFwd:
       hipLaunchKernelGGL((recurrence_roles_kernel<DK, C, BV, kFwd>), grid, block, 0, stream, q, k, v, tws, s0, o,
-                         sfin, H, L, NC, DV, NVB, remap, cu, states);
+                         sfin, H, L, NC, DV, NVB, remap, cu, states, order, N);
       break;
     case kStates:
       hipLaunchKernelGGL((recurrence_roles_kernel<DK, C, BV, kStates>), grid, block, 0, stream, q, k, v, tws, s0, o,
-                         sfin, H, L, NC, DV, NVB, remap, cu, states);
+                         sfin, H, L, NC, DV, NVB, remap, cu, states, order, N);
       break;
     case kFinal:
       hipLaunchKernelGGL((recurrence_roles_kernel<DK, C, BV, kFinal>), grid, block, 0, stream, q, k, v, tws, s0, o,
-                         sfin, H, L, NC, DV, NVB, remap, cu, states);
+                         sfin, H, L, NC, DV, NVB, remap, cu, states, order, N);
       break;
     default:
       hipLaunchKernelGGL((recurrence_roles_kernel<DK, C, BV, kTrans>), grid, block, 0, stream, q, k, v, tws, s0, o,
-                         sfin, H, L, NC, DV, NVB, remap, cu, states);
+                         sfin, H, L, NC, DV, NVB, remap, cu, states, order, N);
   }
   return hipGetLastError();
 }
@@ -425,10 +427,11 @@ hipError_t recurrence_roles_launch_impl(const uint16_t* q, const uint16_t* k, co
 template <int DK, int C>
 hipError_t recurrence_roles_bv(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* tws,
                             const float* s0, uint16_t* o, float* sfin, int B, int H, int64_t L, int DV,
-                            int BV, const int32_t* cu, int N, uint16_t* states, bool trans, hipStream_t s) {
+                            int BV, const int32_t* cu, int N, uint16_t* states, bool trans, const int32_t* order,
+                            hipStream_t s) {
   switch (BV) {
-    case 16: return recurrence_roles_launch_impl<DK, C, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, states, trans, s);
-    case 32: return recurrence_roles_launch_impl<DK, C, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, states, trans, s);
+    case 16: return recurrence_roles_launch_impl<DK, C, 16>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, states, trans, order, s);
+    case 32: return recurrence_roles_launch_impl<DK, C, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, states, trans, order, s);
   }
   return hipErrorInvalidValue;
 }
@@ -436,18 +439,19 @@ hipError_t recurrence_roles_bv(const uint16_t* q, const uint16_t* k, const uint1
 inline hipError_t launch_recurrence_roles(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                        const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
                                        int B, int H, int64_t L, int DK, int DV, int C, int BV,
-                                       const int32_t* cu, int N, uint16_t* states, bool trans, hipStream_t s) {
+                                       const int32_t* cu, int N, uint16_t* states, bool trans, const int32_t* order,
+                                       hipStream_t s) {
   if (C == 32) {
     switch (DK) {
-      case 32: return recurrence_roles_bv<32, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, states, trans, s);
-      case 64: return recurrence_roles_bv<64, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, states, trans, s);
-      case 128: return recurrence_roles_bv<128, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, states, trans, s);
+      case 32: return recurrence_roles_bv<32, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, states, trans, order, s);
+      case 64: return recurrence_roles_bv<64, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, states, trans, order, s);
+      case 128: return recurrence_roles_bv<128, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, states, trans, order, s);
     }
   } else if (C == 64) {
     switch (DK) {
-      case 32: return recurrence_roles_bv<32, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, states, trans, s);
-      case 64: return recurrence_roles_bv<64, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, states, trans, s);
-      case 128: return recurrence_roles_bv<128, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, states, trans, s);
+      case 32: return recurrence_roles_bv<32, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, states, trans, order, s);
+      case 64: return recurrence_roles_bv<64, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, states, trans, order, s);
+      case 128: return recurrence_roles_bv<128, 64>(q, k, v, tws, s0, o, sfin, B, H, L, DV, BV, cu, N, states, trans, order, s);
     }
   }
   return hipErrorInvalidValue;

@@ -143,9 +143,11 @@ def test_rule_is_validated_first():
 
 def test_varlen_workspace_size_and_validation():
     f = efla.efla_chunk_fwd_varlen_workspace_size
-    # H x (floor(T / C) + N) slots of C x C
-    assert f(3, 2, 100, 16, 16, 16, torch.float32) == 2 * (6 + 3) * 16 * 16 * 4
-    assert f(16, 16, 16384, 128, 128, 64, torch.bfloat16) == 16 * (256 + 16) * 64 * 64 * 2
+    # H x (floor(T / C) + N) slots of C x C (256-byte aligned), then the
+    # schedule: one int32 per sequence, aligned up to 256 bytes
+    assert f(3, 2, 100, 16, 16, 16, torch.float32) == 2 * (6 + 3) * 16 * 16 * 4 + 256
+    assert f(16, 16, 16384, 128, 128, 64, torch.bfloat16) == 16 * (256 + 16) * 64 * 64 * 2 + 256
+    assert f(65, 1, 64, 16, 16, 16, torch.float32) == (4 + 65) * 16 * 16 * 4 + 512
     assert f(0, 2, 100, 16, 16, 16, torch.float32) == 0
     assert f(3, 2, 100, 24, 16, 16, torch.float32) == 0
     assert f(3, 2, 2 ** 31, 16, 16, 16, torch.float32) == 0

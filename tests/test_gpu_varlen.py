@@ -93,3 +93,47 @@ def test_varlen_empty_batches():
                                         None, chunk=32)
     torch.cuda.synchronize()
     assert torch.count_nonzero(sf0) == 0
+
+
+def _schedule(ws, N, H, T, dk, dv, chunk, dtype):
+    """The rank -> sequence schedule the call left in its workspace: int32 per
+    sequence after the 256-byte-aligned T slots."""
+    esz = torch.empty((), dtype=dtype).element_size()
+    off = (H * (T // chunk + N) * chunk * chunk * esz + 255) // 256 * 256
+    return ws[off:off + 4 * N].view(torch.int32).cpu().numpy()
+
+
+@pytest.mark.parametrize("lengths", [MIX, "mix"], ids=["boundary_mix", "1p3b_mix"])
+def test_varlen_schedule_is_longest_first(lengths):
+    """Sequences are handed to the recurrence by chunk count, longest first,
+    ties by index: the schedule is a permutation with non-increasing counts."""
+    require_gpu()
+    w = W.get("varlen_1p3b")
+    if lengths == "mix":
+        lengths = W.length_mix(w.B, 2048, seed=815)
+    inp = W.generate_packed(w, lengths, device="cuda", H=2, seed=816, lead=3, tail=4)
+    q, cu = inp["q"], inp["cu_seqlens"]
+    N, T, H = cu.numel() - 1, q.shape[0], q.shape[1]
+    n = efla.efla_chunk_fwd_varlen_workspace_size(N, H, T, w.dk, w.dv, w.chunk, q.dtype)
+    ws = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")
+    _check(dict(inp), w.chunk, f"schedule check, {N} sequences", lead=3, tail=4)
+    efla.efla_chunk_fwd_varlen(q, inp["k"], inp["v"], inp["beta"], cu, inp["s0"], chunk=w.chunk, workspace=ws)
+    torch.cuda.synchronize()
+    order = _schedule(ws, N, H, T, w.dk, w.dv, w.chunk, q.dtype)
+    assert sorted(order.tolist()) == list(range(N))
+    cuh = cu.cpu().numpy().astype(np.int64)
+    nc = (cuh[1:] - cuh[:-1] + w.chunk - 1) // w.chunk
+    keys = [(-int(nc[u]), int(u)) for u in order]
+    assert keys == sorted(keys)
+
+
+def test_varlen_many_sequences_unordered_path():
+    """Beyond the ordered-schedule limit (4096 sequences) the recurrence takes
+    sequences in index order; results still match the oracle."""
+    require_gpu()
+    w = W.get("shape_340m", dk=16, dv=16, chunk=16)
+    rng = np.random.default_rng(817)
+    lengths = rng.integers(0, 5, size=4100).tolist()
+    lengths[17] = 40   # one sequence of several chunks
+    inp = W.generate_packed(w, lengths, device="cuda", H=1, seed=818)
+    _check(inp, 16, "4100 short sequences")
