@@ -206,8 +206,15 @@ efla_status efla_chunk_bwd(const void *q, const void *k, const void *v, const vo
  * are clamped into [0, T]).  T < 2^31.
  *
  * efla_chunk_fwd_varlen_workspace_size -- bytes of workspace for these sizes:
- * H * (floor(T / chunk) + N) chunk slots of chunk x chunk (dtype); 0 for
- * unsupported or invalid arguments (N < 1 included).
+ * H * (floor(T / chunk) + N) chunk slots of chunk x chunk (dtype), rounded up
+ * to 256 bytes, then N int32 (the schedule below), rounded up to 256 bytes;
+ * 0 for unsupported or invalid arguments (N < 1 included).
+ *
+ * Schedule: with N <= 4096, a first kernel ranks the sequences by chunk
+ * count, longest first (ties by index), and the recurrence hands them to its
+ * workgroups in that order, so the longest chains start first.  The order
+ * only changes which workgroup runs a sequence, never its arithmetic: results
+ * are the same bits either way.
  */
 size_t efla_chunk_fwd_varlen_workspace_size(int N, int H, int64_t T, int d_k, int d_v, int chunk,
                                             efla_dtype dtype);
