@@ -345,16 +345,54 @@ def test_empty_sequence_copies_state():
     assert torch.count_nonzero(sf) == 0
 
 
-def test_degenerate_tokens():
-    """beta = 0 and zero keys are identity steps; beta*lambda huge overwrites."""
-    w, inp = _gen("shape_340m", dtype="f32", B=1, H=2, L=70, dk=32, dv=32, seed=94)
+@pytest.mark.parametrize("dt,dk,dv,chunk,L", [("f32", 32, 32, 32, 70), ("bf16", 128, 128, 64, 200),
+                                              ("bf16", 64, 32, 32, 130)], ids=lambda x: str(x))
+def test_degenerate_tokens(dt, dk, dv, chunk, L):
+    """beta = 0 and zero keys are identity steps; beta*lambda huge overwrites;
+    a whole chunk of beta = 0 leaves the state untouched across it."""
+    w, inp = _gen("shape_340m", dtype=dt, B=1, H=2, L=L, dk=dk, dv=dv, seed=94)
     beta = inp["beta"].clone()
     k = inp["k"].clone()
     beta[:, 5:9] = 0.0
     k[:, 20:23] = 0.0
     beta[:, 40:44] = 1e6
+    if L >= 2 * chunk + 10:
+        beta[:, chunk:2 * chunk] = 0.0   # one whole chunk of identity steps
     inp = dict(inp, beta=beta, k=k)
-    _check_forward(inp, 32, "degenerate tokens")
+    _check_forward(inp, chunk, f"degenerate tokens {dt} dk{dk} dv{dv} C{chunk} L{L}")
+
+
+def test_all_identity_steps_read_out_the_initial_state():
+    """beta = 0 everywhere: S stays s0 and every output is s0^T q_t."""
+    w, inp = _gen("shape_340m", B=1, H=2, L=150, seed=95)
+    beta = torch.zeros_like(inp["beta"])
+    o, sf = efla.efla_chunk_fwd(inp["q"], inp["k"], inp["v"], beta, inp["s0"], chunk=64)
+    torch.cuda.synchronize()
+    assert torch.equal(sf, inp["s0"])
+    ref = torch.einsum("blhk,bhkv->blhv", inp["q"].double().cpu(), inp["s0"].double().cpu())
+    err = normwise(to_f64(o), ref.numpy())
+    _say(f"[parity] all beta = 0: o err {err:.3e}")
+    assert err <= TOL["bf16"]["o"]
+
+
+def test_decode_degenerate_tokens():
+    """Decode steps with beta = 0 and zero keys leave the state bitwise unchanged;
+    a stiff step (beta lambda ~ 1e6) matches the oracle."""
+    require_gpu()
+    w = W.get("decode_1p3b")
+    inp = W.generate_decode(w, device="cuda", N=4, steps=1)
+    q, k, v, beta = inp["q"][0], inp["k"][0].clone(), inp["v"][0], inp["beta"][0].clone()
+    beta[0] = 0.0          # sequence 0: beta = 0 on every head
+    k[1] = 0.0             # sequence 1: zero keys
+    beta[2] = 1e6          # sequence 2: stiff
+    state = inp["s0"].clone()
+    o = efla.efla_step(q, k, v, beta, state)
+    torch.cuda.synchronize()
+    assert torch.equal(state[0], inp["s0"][0]) and torch.equal(state[1], inp["s0"][1])
+    ro, rs = oracle.step(to_f64(q), to_f64(k), to_f64(v), to_f64(beta), to_f64(inp["s0"]))
+    eo, es = normwise(to_f64(o), ro), normwise(to_f64(state), rs)
+    _say(f"[parity] decode degenerate tokens: o err {eo:.3e}, S err {es:.3e}")
+    assert eo <= TOL["bf16"]["o"] and es <= 1e-4
 
 
 def test_invalid_arguments_are_rejected():
