@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libefla.so")
 SOURCES = ["api.hip", "step_kernels.hip", "chunk_bf16.hip", "chunk_bf16_roles.hip", "ut_bf16.hip",
-           "chunk_f32.hip", "bwd.hip", "seg.hip", "varlen.hip"]
+           "chunk_f32.hip", "bwd.hip", "seg.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 CFLAGS = [

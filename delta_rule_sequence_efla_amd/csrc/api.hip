@@ -78,7 +78,7 @@ RecChoice choose_recurrence(efla_dtype dt, int d_k, int d_v, int chunk) {
 // packed batch: N sequences at device offsets cu into L tokens.
 efla_status launch_ut(const void* k, const void* beta, int B, int H, int64_t L, int d_k, int chunk,
                       efla_dtype dtype, efla_rule rule, void* workspace, const int32_t* cu, int N,
-                      hipStream_t s) {
+                      hipStream_t s, int32_t* order = nullptr) {
   // bf16: one wavefront per chunk (ut_wave.h) where it applies, else one
   // workgroup per chunk; EFLA_UT_IMPL=workgroup pins the latter for comparisons.
   const char* impl = getenv("EFLA_UT_IMPL");
@@ -86,16 +86,16 @@ efla_status launch_ut(const void* k, const void* beta, int B, int H, int64_t L, 
   if (dtype == EFLA_BF16 && !want_wg && efla::ut_wave_bf16_supported(d_k, chunk))
     return from_hip(efla::launch_ut_wave_bf16(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(beta),
                                               static_cast<uint16_t*>(workspace), B, H, L, d_k, chunk,
-                                              int(rule), cu, N, s));
+                                              int(rule), cu, N, s, order));
   if (dtype == EFLA_BF16)
     return from_hip(efla::launch_ut_transform<uint16_t>(static_cast<const uint16_t*>(k),
                                                         static_cast<const uint16_t*>(beta),
                                                         static_cast<uint16_t*>(workspace), B, H, L, d_k,
-                                                        chunk, int(rule), cu, N, s));
+                                                        chunk, int(rule), cu, N, s, order));
   return from_hip(efla::launch_ut_transform<float>(static_cast<const float*>(k),
                                                    static_cast<const float*>(beta),
                                                    static_cast<float*>(workspace), B, H, L, d_k, chunk,
-                                                   int(rule), cu, N, s));
+                                                   int(rule), cu, N, s, order));
 }
 
 // Stage 2 launch (arguments already validated).  The one-wavefront-per-tile
@@ -322,14 +322,12 @@ efla_status efla_chunk_fwd_varlen(const void* q, const void* k, const void* v, c
   hipStream_t s = static_cast<hipStream_t>(stream);
   int32_t* order = nullptr;
   if (T > 0) {
-    if (N <= kMaxOrderedSeqs) {
+    if (N <= kMaxOrderedSeqs)  // the UT launch also ranks the sequences, longest first
       order = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(workspace) +
                                          al256(size_t(H) * size_t(slots) * size_t(chunk) * size_t(chunk) *
                                                elem_bytes(dtype)));
-      const efla_status s0r = from_hip(efla::launch_varlen_order(cu_seqlens, N, T, chunk, order, s));
-      if (s0r != EFLA_OK) return s0r;
-    }
-    const efla_status s1 = launch_ut(k, beta, 1, H, T, d_k, chunk, dtype, rule, workspace, cu_seqlens, N, s);
+    const efla_status s1 = launch_ut(k, beta, 1, H, T, d_k, chunk, dtype, rule, workspace, cu_seqlens, N, s,
+                                     order);
     if (s1 != EFLA_OK) return s1;
   } else if (s_final == nullptr) {
     return EFLA_OK;

@@ -6,7 +6,7 @@
 
 namespace efla {
 template hipError_t launch_ut_transform<uint16_t>(const uint16_t*, const uint16_t*, uint16_t*, int, int,
-                                                  int64_t, int, int, int, const int32_t*, int, hipStream_t);
+                                                  int64_t, int, int, int, const int32_t*, int, hipStream_t, int32_t*);
 template hipError_t launch_recurrence<uint16_t>(const uint16_t*, const uint16_t*, const uint16_t*,
                                                 const uint16_t*, const float*, uint16_t*, float*, int,
                                                 int, int64_t, int, int, int, int, const int32_t*, int,

@@ -3,7 +3,7 @@
 
 namespace efla {
 template hipError_t launch_ut_transform<float>(const float*, const float*, float*, int, int, int64_t,
-                                               int, int, int, const int32_t*, int, hipStream_t);
+                                               int, int, int, const int32_t*, int, hipStream_t, int32_t*);
 template hipError_t launch_recurrence<float>(const float*, const float*, const float*, const float*,
                                              const float*, float*, float*, int, int, int64_t, int, int,
                                              int, int, const int32_t*, int, hipStream_t, int, const int32_t*);

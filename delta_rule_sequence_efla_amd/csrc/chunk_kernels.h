@@ -103,7 +103,9 @@ __global__ __launch_bounds__(kThreads) void ut_transform_kernel(const T* __restr
                                                                 const T* __restrict__ q = nullptr,
                                                                 float* __restrict__ xout = nullptr,
                                                                 float* __restrict__ aout = nullptr,
-                                                                float* __restrict__ pout = nullptr) {
+                                                                float* __restrict__ pout = nullptr,
+                                                                int64_t nwg_ut = 0,
+                                                                int32_t* __restrict__ order = nullptr) {
   constexpr int DKP = round_up(DK, 32), CP = round_up(C, 32);
   constexpr int NRT = C / 16, NKU_D = DKP / 32;
   constexpr int KP = DKP + (sizeof(T) == 2 ? 8 : 4);
@@ -113,7 +115,12 @@ __global__ __launch_bounds__(kThreads) void ut_transform_kernel(const T* __restr
   __shared__ float lam_s[CP], alpha_s[CP];
   __shared__ __align__(16) float Gs[C * AP];  // strictly lower part of K K^T
   __shared__ __align__(16) float Xs[C * AP];  // X = (I + A)^{-1}, lower blocks
+  static_assert(sizeof(Ks) >= kRankSeqs * sizeof(int), "ranking workgroups reuse Ks");
 
+  if (order != nullptr && int64_t(blockIdx.x) >= nwg_ut) {  // packed batch: rank the sequences
+    rank_sequences<C>(cu, N, L, int(blockIdx.x - nwg_ut), order, reinterpret_cast<int*>(Ks));
+    return;
+  }
   const int64_t wg = blockIdx.x;  // workspace slot of this workgroup's chunk
   // slot -> sequence and chunk (dense: wg = (b H + h) NC + chunk)
   SeqSpan sp;
@@ -550,12 +557,14 @@ __global__ __launch_bounds__(kThreads) void recurrence_kernel(
 
 template <typename T, int DK, int C>
 hipError_t ut_transform_launch_impl(const T* k, const T* beta, T* tws, int B, int H, int64_t L, int rule,
-                                    const int32_t* cu, int N, hipStream_t stream) {
+                                    const int32_t* cu, int N, int32_t* order, hipStream_t stream) {
   const int NC = cu == nullptr ? int((L + C - 1) / C) : int(L / C) + N;  // chunk slots per sequence / head
   const int64_t nwg = int64_t(cu == nullptr ? B : 1) * H * NC;
-  if (nwg == 0) return hipSuccess;
-  hipLaunchKernelGGL((ut_transform_kernel<T, DK, C>), dim3(unsigned(nwg)), dim3(kThreads), 0, stream,
-                     k, beta, tws, H, L, NC, rule, cu, N);
+  if (cu == nullptr) order = nullptr;
+  const int64_t nrank = order != nullptr ? (N + kRankSeqs - 1) / kRankSeqs : 0;
+  if (nwg + nrank == 0) return hipSuccess;
+  hipLaunchKernelGGL((ut_transform_kernel<T, DK, C>), dim3(unsigned(nwg + nrank)), dim3(kThreads), 0, stream,
+                     k, beta, tws, H, L, NC, rule, cu, N, nullptr, nullptr, nullptr, nullptr, nwg, order);
   return hipGetLastError();
 }
 
@@ -578,23 +587,23 @@ hipError_t recurrence_launch_impl(const T* q, const T* k, const T* v, const T* t
 
 template <typename T, int DK>
 hipError_t ut_dispatch_c(const T* k, const T* beta, T* tws, int B, int H, int64_t L, int C, int rule,
-                         const int32_t* cu, int N, hipStream_t s) {
+                         const int32_t* cu, int N, int32_t* order, hipStream_t s) {
   switch (C) {
-    case 16: return ut_transform_launch_impl<T, DK, 16>(k, beta, tws, B, H, L, rule, cu, N, s);
-    case 32: return ut_transform_launch_impl<T, DK, 32>(k, beta, tws, B, H, L, rule, cu, N, s);
-    case 64: return ut_transform_launch_impl<T, DK, 64>(k, beta, tws, B, H, L, rule, cu, N, s);
+    case 16: return ut_transform_launch_impl<T, DK, 16>(k, beta, tws, B, H, L, rule, cu, N, order, s);
+    case 32: return ut_transform_launch_impl<T, DK, 32>(k, beta, tws, B, H, L, rule, cu, N, order, s);
+    case 64: return ut_transform_launch_impl<T, DK, 64>(k, beta, tws, B, H, L, rule, cu, N, order, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename T>
 hipError_t launch_ut_transform(const T* k, const T* beta, T* tws, int B, int H, int64_t L, int DK,
-                               int C, int rule, const int32_t* cu, int N, hipStream_t s) {
+                               int C, int rule, const int32_t* cu, int N, hipStream_t s, int32_t* order) {
   switch (DK) {
-    case 16: return ut_dispatch_c<T, 16>(k, beta, tws, B, H, L, C, rule, cu, N, s);
-    case 32: return ut_dispatch_c<T, 32>(k, beta, tws, B, H, L, C, rule, cu, N, s);
-    case 64: return ut_dispatch_c<T, 64>(k, beta, tws, B, H, L, C, rule, cu, N, s);
-    case 128: return ut_dispatch_c<T, 128>(k, beta, tws, B, H, L, C, rule, cu, N, s);
+    case 16: return ut_dispatch_c<T, 16>(k, beta, tws, B, H, L, C, rule, cu, N, order, s);
+    case 32: return ut_dispatch_c<T, 32>(k, beta, tws, B, H, L, C, rule, cu, N, order, s);
+    case 64: return ut_dispatch_c<T, 64>(k, beta, tws, B, H, L, C, rule, cu, N, order, s);
+    case 128: return ut_dispatch_c<T, 128>(k, beta, tws, B, H, L, C, rule, cu, N, order, s);
   }
   return hipErrorInvalidValue;
 }

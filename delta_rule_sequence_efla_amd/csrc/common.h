@@ -205,9 +205,50 @@ __device__ __forceinline__ SeqSpan seq_span(const int32_t* __restrict__ cu, int 
 // Packed batches: slot j (0 .. NC-1) of head h belongs to chunk n of sequence
 // u, found by binary search over the slot offsets floor(cu[u] / C) + u (which
 // increase with u); false for a slot no chunk uses.
+// Schedule of a packed batch.  The recurrence runs one workgroup per
+// (sequence, head, value block), and a workgroup's time grows with its
+// sequence's chunk count; workgroups are dispatched in index order as compute
+// units free up, so handing out the sequences longest first is a
+// longest-processing-time-first list schedule.  The order is computed on the
+// device, by extra workgroups of the UT-transform launch:
+//     rank(u) = #{v : n(v) > n(u)} + #{v < u : n(v) = n(u)},  order[rank(u)] = u,
+// with n the chunk count from offsets clamped exactly as seq_span clamps them,
+// a bijection onto [0, N) whatever the offsets hold.
+constexpr int kRankSeqs = 256;  // sequences ranked per workgroup (one per thread of kThreads)
+
+template <int C>
+__device__ __forceinline__ int seq_chunks(const int32_t* __restrict__ cu, int u, int64_t T) {
+  const int64_t a = clamp_offset(cu[u], 0, T);
+  const int64_t e = clamp_offset(cu[u + 1], a, T);
+  return int((e - a + C - 1) / C);
+}
+
+// Ranks sequences blk * kRankSeqs .. +kRankSeqs - 1; every thread of the
+// (kThreads-wide) workgroup calls it; tile: kRankSeqs ints of LDS.
+template <int C>
+__device__ __forceinline__ void rank_sequences(const int32_t* __restrict__ cu, int N, int64_t T, int blk,
+                                               int32_t* __restrict__ order, int* tile) {
+  static_assert(kRankSeqs == kThreads, "one sequence per thread");
+  const int tid = threadIdx.x, u = blk * kRankSeqs + tid;
+  const int nu = u < N ? seq_chunks<C>(cu, u, T) : 0;
+  int rank = 0;
+  for (int base = 0; base < N; base += kRankSeqs) {
+    __syncthreads();
+    if (base + tid < N) tile[tid] = seq_chunks<C>(cu, base + tid, T);
+    __syncthreads();
+    const int n = N - base < kRankSeqs ? N - base : kRankSeqs;
+    if (u < N)
+      for (int i = 0; i < n; ++i) {
+        const int nv = tile[i];
+        rank += (nv > nu || (nv == nu && base + i < u)) ? 1 : 0;
+      }
+  }
+  if (u < N) order[rank] = u;
+}
+
 // Sequence handled in rank r of a packed batch of N sequences (order: the
-// permutation of [0, N) written by varlen_order_kernel; an entry outside it
-// falls back to r).
+// permutation of [0, N) written by rank_sequences; an entry outside it falls
+// back to r).
 __device__ __forceinline__ int seq_of_rank(const int32_t* __restrict__ order, int r, int N) {
   const int u = order[r];
   return (u >= 0 && u < N) ? u : r;

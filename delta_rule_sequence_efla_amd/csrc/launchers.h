@@ -18,12 +18,16 @@ template <typename T>
 hipError_t launch_step(const T* q, const T* k, const T* v, const T* beta, float* state, T* o,
                        int64_t units, int DK, int DV, int rule, hipStream_t s);
 
+// Packed batches: with order != nullptr the launch also writes the schedule
+// of the N sequences (rank -> sequence, longest first, see rank_sequences)
+// for the recurrence launch that follows.
 template <typename T>
 hipError_t launch_ut_transform(const T* k, const T* beta, T* tws, int B, int H, int64_t L, int DK,
-                               int C, int rule, const int32_t* cu, int N, hipStream_t stream);
+                               int C, int rule, const int32_t* cu, int N, hipStream_t stream,
+                               int32_t* order = nullptr);
 
 // order (packed batches only, nullable): the schedule of sequences, rank ->
-// sequence, from launch_varlen_order; workgroups of rank 0 start first.
+// sequence, written by the UT-transform launch; workgroups of rank 0 start first.
 template <typename T>
 hipError_t launch_recurrence(const T* q, const T* k, const T* v, const T* tws, const float* s0,
                              T* o, float* sfin, int B, int H, int64_t L, int DK, int DV, int C,
@@ -56,7 +60,8 @@ hipError_t launch_recurrence_roles_bf16(const uint16_t* q, const uint16_t* k, co
 // {32, 64, 128}, chunk in {32, 64}.
 bool ut_wave_bf16_supported(int DK, int C);
 hipError_t launch_ut_wave_bf16(const uint16_t* k, const uint16_t* beta, uint16_t* tws, int B, int H, int64_t L,
-                               int DK, int C, int rule, const int32_t* cu, int N, hipStream_t s);
+                               int DK, int C, int rule, const int32_t* cu, int N, hipStream_t s,
+                               int32_t* order = nullptr);
 
 // Backward pass of the chunked forward (bwd.hip, bwd_kernels.h): dense
 // batches, any supported d_k / d_v / chunk; ws holds bwd_layout(...).total bytes.
@@ -68,12 +73,6 @@ template <typename T>
 hipError_t launch_chunk_bwd(const T* q, const T* k, const T* v, const T* beta, const float* s0, const T* dout,
                             const float* dsf, T* dq, T* dk, T* dv, T* dbeta, float* ds0, int B, int H, int64_t L,
                             int DK, int DV, int C, int rule, void* ws, hipStream_t s);
-
-// Schedule of a packed batch (varlen.hip): order[r] = the sequence of rank r,
-// sequences by chunk count, longest first (ties by index), so that the
-// recurrence's workgroups, dispatched in index order, start the longest
-// chains first.  Always a permutation of [0, N), whatever the offsets hold.
-hipError_t launch_varlen_order(const int32_t* cu, int N, int64_t T, int C, int32_t* order, hipStream_t s);
 
 // Segment scan (seg.hip): offsets of the packed view of B sequences of L
 // tokens cut into G segments of Ls tokens, and the combine along each sequence.

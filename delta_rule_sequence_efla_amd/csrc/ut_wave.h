@@ -60,12 +60,16 @@ __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict
                                                       const uint16_t* __restrict__ beta,
                                                       uint16_t* __restrict__ tws, int H, int64_t L, int NC,
                                                       int64_t nchunks, int rule, const int32_t* __restrict__ cu,
-                                                      int N) {
+                                                      int N, int64_t nwg_ut, int32_t* __restrict__ order) {
   using S = UtWaveShape<DK, C>;
   constexpr int NRT = S::NRT, NKU = S::NKU, GP = S::GP, BLK = S::BLK, TP = S::TP;
   __shared__ __align__(16) unsigned char scratch_all[S::WAVES][S::SCRATCH];
   __shared__ float a_all[S::WAVES][64];
 
+  if (order != nullptr && int64_t(blockIdx.x) >= nwg_ut) {  // packed batch: the workgroups after the chunks rank the sequences
+    rank_sequences<C>(cu, N, L, int(blockIdx.x - nwg_ut), order, reinterpret_cast<int*>(scratch_all));
+    return;
+  }
   const int lane = threadIdx.x & 63, w = wave_id(), li = lane & 15, g = lane >> 4;
   const int64_t id = int64_t(blockIdx.x) * S::WAVES + w;  // workspace slot handled by this wavefront
   if (id >= nchunks) return;                              // no workgroup barriers below
@@ -219,29 +223,33 @@ inline bool ut_wave_supported(int DK, int C) { return (DK == 32 || DK == 64 || D
 // N sequences with offsets cu in a batch of L tokens (B is ignored).
 template <int DK, int C>
 hipError_t ut_wave_launch_impl(const uint16_t* k, const uint16_t* beta, uint16_t* tws, int B, int H, int64_t L,
-                               int rule, const int32_t* cu, int N, hipStream_t stream) {
+                               int rule, const int32_t* cu, int N, int32_t* order, hipStream_t stream) {
+  static_assert(64 * UtWaveShape<DK, C>::WAVES == kThreads && UtWaveShape<DK, C>::WAVES * UtWaveShape<DK, C>::SCRATCH >=
+                    int(kRankSeqs * sizeof(int)), "ranking workgroups reuse the kernel's shape and LDS");
   const int NC = cu == nullptr ? int((L + C - 1) / C) : int(L / C) + N;
   const int64_t nchunks = int64_t(cu == nullptr ? B : 1) * H * NC;
-  if (nchunks == 0) return hipSuccess;
+  if (cu == nullptr) order = nullptr;
   const int64_t nwg = (nchunks + UtWaveShape<DK, C>::WAVES - 1) / UtWaveShape<DK, C>::WAVES;
-  hipLaunchKernelGGL((ut_wave_kernel<DK, C>), dim3(unsigned(nwg)), dim3(64 * UtWaveShape<DK, C>::WAVES), 0, stream,
-                     k, beta, tws, H, L, NC, nchunks, rule, cu, N);
+  const int64_t nrank = order != nullptr ? (N + kRankSeqs - 1) / kRankSeqs : 0;
+  if (nwg + nrank == 0) return hipSuccess;
+  hipLaunchKernelGGL((ut_wave_kernel<DK, C>), dim3(unsigned(nwg + nrank)), dim3(64 * UtWaveShape<DK, C>::WAVES), 0,
+                     stream, k, beta, tws, H, L, NC, nchunks, rule, cu, N, nwg, order);
   return hipGetLastError();
 }
 
 inline hipError_t launch_ut_wave(const uint16_t* k, const uint16_t* beta, uint16_t* tws, int B, int H, int64_t L,
-                                 int DK, int C, int rule, const int32_t* cu, int N, hipStream_t s) {
+                                 int DK, int C, int rule, const int32_t* cu, int N, int32_t* order, hipStream_t s) {
   if (C == 32) {
     switch (DK) {
-      case 32: return ut_wave_launch_impl<32, 32>(k, beta, tws, B, H, L, rule, cu, N, s);
-      case 64: return ut_wave_launch_impl<64, 32>(k, beta, tws, B, H, L, rule, cu, N, s);
-      case 128: return ut_wave_launch_impl<128, 32>(k, beta, tws, B, H, L, rule, cu, N, s);
+      case 32: return ut_wave_launch_impl<32, 32>(k, beta, tws, B, H, L, rule, cu, N, order, s);
+      case 64: return ut_wave_launch_impl<64, 32>(k, beta, tws, B, H, L, rule, cu, N, order, s);
+      case 128: return ut_wave_launch_impl<128, 32>(k, beta, tws, B, H, L, rule, cu, N, order, s);
     }
   } else if (C == 64) {
     switch (DK) {
-      case 32: return ut_wave_launch_impl<32, 64>(k, beta, tws, B, H, L, rule, cu, N, s);
-      case 64: return ut_wave_launch_impl<64, 64>(k, beta, tws, B, H, L, rule, cu, N, s);
-      case 128: return ut_wave_launch_impl<128, 64>(k, beta, tws, B, H, L, rule, cu, N, s);
+      case 32: return ut_wave_launch_impl<32, 64>(k, beta, tws, B, H, L, rule, cu, N, order, s);
+      case 64: return ut_wave_launch_impl<64, 64>(k, beta, tws, B, H, L, rule, cu, N, order, s);
+      case 128: return ut_wave_launch_impl<128, 64>(k, beta, tws, B, H, L, rule, cu, N, order, s);
     }
   }
   return hipErrorInvalidValue;

@@ -210,9 +210,10 @@ efla_status efla_chunk_bwd(const void *q, const void *k, const void *v, const vo
  * to 256 bytes, then N int32 (the schedule below), rounded up to 256 bytes;
  * 0 for unsupported or invalid arguments (N < 1 included).
  *
- * Schedule: with N <= 4096, a first kernel ranks the sequences by chunk
- * count, longest first (ties by index), and the recurrence hands them to its
- * workgroups in that order, so the longest chains start first.  The order
+ * Schedule: with N <= 4096, the UT-transform launch also ranks the
+ * sequences by chunk count, longest first (ties by index), and the recurrence
+ * hands them to its workgroups in that order, so the longest chains start
+ * first.  The order
  * only changes which workgroup runs a sequence, never its arithmetic: results
  * are the same bits either way.
  */
