@@ -9,6 +9,10 @@
 //                                      inputs: the operand values the forward
 //                                      products use)
 //   dS [slots][dk][dv]   fp32          loss gradient at the end of the chunk
+#include <stdlib.h>
+#include <string.h>
+
+#include "bwd_bf16.h"
 #include "bwd_kernels.h"
 #include "chunk_kernels.h"
 #include "launchers.h"
@@ -79,7 +83,16 @@ hipError_t bwd_launch_impl(const T* q, const T* k, const T* v, const T* beta, co
                      dout, tws, pws, dsf, dsws, ds0, H, L, NC, DV, DV / 16);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   if (slots == 0) return hipSuccess;
-  // 4. every chunk's gradients
+  // 4. every chunk's gradients: bf16 inputs on bf16 matrix cores where the
+  // shape allows (EFLA_BWD_IMPL=fp32 keeps the fp32 kernel), else fp32
+  if constexpr (sizeof(T) == 2 && DK % 32 == 0 && C % 32 == 0) {
+    const char* impl = getenv("EFLA_BWD_IMPL");
+    if (!(impl && strcmp(impl, "fp32") == 0) && bwd_bf16_supported(DK, DV, C)) {
+      hipLaunchKernelGGL((bwd_chunk_bf16_kernel<DK, C>), dim3(unsigned(slots)), dim3(kThreads), 0, s, q, k, v, beta,
+                         dout, tws, xws, aws, pws, sws, dsws, dq, dk, dv, dbeta, H, L, NC, DV, rule);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((bwd_chunk_kernel<T, DK, C>), dim3(unsigned(slots)), dim3(kThreads), 0, s, q, k, v, beta,
                      dout, tws, xws, aws, pws, sws, dsws, dq, dk, dv, dbeta, H, L, NC, DV, rule);
   return hipGetLastError();

@@ -1,0 +1,288 @@
+// bwd_bf16.h -- the per-chunk gradients of the backward pass for bf16 inputs,
+// with the value-block products on bf16 matrix cores.
+//
+// Same formulas and work split as bwd_chunk_kernel (bwd_kernels.h): one
+// workgroup per (b, h, chunk), value columns streamed in blocks, dQ, dK, dP and
+// dT accumulated in fp32 registers, then the fp32 tail (bwd_chunk_tail).  What
+// differs is the value-block loop, which carries about three quarters of the
+// products: its operands sit in LDS as bf16 and every product is one
+// v_mfma_f32_16x16x32_bf16 per 32-deep slice.  The operands that are not bf16
+// already (P, dS', and the intermediates D = V - K S, dU, U, dD) are rounded to
+// bf16 once, like the states the forward products use.
+//
+// Every product is written acc += A B with A read as rows of an [M][K] array
+// and B as rows of an [N][K] array (B's transpose), so each operand fragment is
+// one 16-byte LDS read (lane (li, g) takes k = 32 ku + 8 g .. +7).  Arrays that
+// serve as B with the other orientation too are kept in both layouts:
+//     D = V - K S          A = K [C][DK]      B^T = S^T [BV][DK]
+//     dU = P^T dO + K dS'  A = P^T, K         B^T = dO^T [BV][C], dS'^T [BV][DK]
+//     U = T D              A = T              B^T = D^T [BV][C]
+//     dD = T^T dU          A = T^T            B^T = dU^T [BV][C]
+//     dQ += dO S^T         A = dO [C][BV]     B^T = S [DK][BV]
+//     dK += U dS'^T - dD S^T, dP += dO U^T, dT += dU D^T  (likewise, K = BV)
+#pragma once
+
+#include "bwd_kernels.h"
+
+namespace efla {
+
+constexpr int kBwdBV = 32;  // value columns per block
+
+template <int DK, int C>
+struct BwdBf16Shape {
+  static constexpr int BV = kBwdBV;
+  static constexpr int KBP = DK + 8;   // pitch (elements) of [*][DK] arrays
+  static constexpr int TBP = C + 8;    // pitch of [*][C] arrays
+  static constexpr int VBP = BV + 8;   // pitch of [*][BV] arrays
+  // byte offsets of the loop-phase arrays (all bf16, 16-byte aligned)
+  static constexpr int KB = 0;
+  static constexpr int TB = KB + C * KBP * 2;
+  static constexpr int TBT = TB + C * TBP * 2;
+  static constexpr int PBT = TBT + C * TBP * 2;
+  static constexpr int SV = PBT + C * TBP * 2;
+  static constexpr int DSV = SV + DK * VBP * 2;
+  static constexpr int SVT = DSV + DK * VBP * 2;
+  static constexpr int DSVT = SVT + BV * KBP * 2;
+  static constexpr int DOV = DSVT + BV * KBP * 2;
+  static constexpr int VV = DOV + C * VBP * 2;
+  static constexpr int DV_ = VV + C * VBP * 2;
+  static constexpr int DUV = DV_ + C * VBP * 2;
+  static constexpr int UV = DUV + C * VBP * 2;
+  static constexpr int DDV = UV + C * VBP * 2;
+  static constexpr int DOVT = DDV + C * VBP * 2;
+  static constexpr int DVT = DOVT + BV * TBP * 2;
+  static constexpr int DUVT = DVT + BV * TBP * 2;
+  static constexpr int LOOP_BYTES = DUVT + BV * TBP * 2;
+  // the tail's fp32 arrays (as in bwd_chunk_kernel)
+  using F = BwdChunkShape<uint16_t, DK, C>;
+  static constexpr int QS = 0;
+  static constexpr int KS = QS + F::CP * F::QP * 4;
+  static constexpr int M0 = KS + F::CP * F::QP * 4;
+  static constexpr int M1 = M0 + F::CP * F::CPP * 4;
+  static constexpr int R = M1 + F::CP * F::CPP * 4;
+  static constexpr int TAIL_BYTES = R + F::RBUF * 4;
+  static constexpr int BYTES = LOOP_BYTES > TAIL_BYTES ? LOOP_BYTES : TAIL_BYTES;
+};
+
+inline bool bwd_bf16_supported(int DK, int DV, int C) {
+  return (DK == 32 || DK == 64 || DK == 128) && (C == 32 || C == 64) && DV % kBwdBV == 0;
+}
+
+// One 16-byte operand fragment: row `row` of an [*][K] bf16 array, k-slice ku.
+__device__ __forceinline__ Frag<uint16_t> row8(const uint16_t* X, int pitch, int row, int ku, int g) {
+  Frag<uint16_t> f;
+  f.v = *reinterpret_cast<const bf16x8*>(X + row * pitch + 32 * ku + 8 * g);
+  return f;
+}
+
+// acc (16x16 tile, rows r0.., columns c0..) += A B over k < K (K % 32 == 0):
+// A rows from A [M][K], B columns from Bt [N][K].
+template <int K>
+__device__ __forceinline__ void tile_bf(f32x4& acc, const uint16_t* A, int lda, const uint16_t* Bt, int ldb, int r0,
+                                        int c0, int li, int g) {
+#pragma unroll
+  for (int ku = 0; ku < K / 32; ++ku) mma(acc, row8(A, lda, r0 + li, ku, g), row8(Bt, ldb, c0 + li, ku, g));
+}
+
+// An accumulator tile (rows r0 + 4 g + q, column c0 + li) stored as bf16 into
+// X [rows][pitch] (four 2-byte writes) and, if XT, into XT [cols][pitchT]
+// (one 8-byte write: the four rows are consecutive there).
+__device__ __forceinline__ void put_tile(uint16_t* X, int pitch, uint16_t* XT, int pitchT, const f32x4& a, int r0,
+                                         int c0, int li, int g) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) X[(r0 + 4 * g + q) * pitch + c0 + li] = from_f32<uint16_t>(a[q]);
+  if (XT != nullptr) st4(XT + (c0 + li) * pitchT + r0 + 4 * g, a);
+}
+
+// A ROWS x COLS tile of a bf16 or fp32 array in global memory (rows `stride`
+// elements apart, rows at or past `valid` read as zero), staged through
+// registers into bf16 LDS: load() issues 16-byte loads, store() writes the
+// tile as rows (dst [ROWS][pitch]) and, if dstT, as its transpose
+// (dstT [COLS][pitchT]).
+template <typename S, int ROWS, int COLS>
+struct Bf16Stager {
+  static constexpr int VN = 16 / int(sizeof(S)), VPR = COLS / VN, TOT = ROWS * VPR, CNT = cdiv(TOT, kThreads);
+  static_assert(COLS % VN == 0, "whole 16-byte vectors per row");
+  u32x4 r[CNT];
+  __device__ __forceinline__ void load(const S* src, int64_t stride, int valid, int tid) {
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) {
+      const int idx = tid + i * kThreads;
+      const int t = idx / VPR, c = (idx % VPR) * VN;
+      r[i] = u32x4{0u, 0u, 0u, 0u};
+      if (idx < TOT && t < valid) r[i] = *reinterpret_cast<const u32x4*>(src + t * stride + c);
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* dst, int pitch, uint16_t* dstT, int pitchT, int tid) const {
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) {
+      const int idx = tid + i * kThreads;
+      if (idx >= TOT) continue;
+      const int t = idx / VPR, c = (idx % VPR) * VN;
+      union {
+        u32x4 u;
+        S e[VN];
+      } x;
+      x.u = r[i];
+      uint16_t h[VN];
+#pragma unroll
+      for (int e = 0; e < VN; ++e) {
+        if constexpr (sizeof(S) == 2) h[e] = x.e[e];
+        else h[e] = from_f32<uint16_t>(x.e[e]);
+      }
+      if (dst != nullptr) {
+        if constexpr (VN == 8) {
+          *reinterpret_cast<u32x4*>(dst + t * pitch + c) = *reinterpret_cast<const u32x4*>(h);
+        } else {
+          *reinterpret_cast<uint2*>(dst + t * pitch + c) = *reinterpret_cast<const uint2*>(h);
+        }
+      }
+      if (dstT != nullptr) {
+#pragma unroll
+        for (int e = 0; e < VN; ++e) dstT[(c + e) * pitchT + t] = h[e];
+      }
+    }
+  }
+};
+
+template <int DK, int C>
+__global__ __launch_bounds__(kThreads) void bwd_chunk_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ beta, const uint16_t* __restrict__ dout, const uint16_t* __restrict__ tws,
+    const float* __restrict__ xws, const float* __restrict__ aws, const float* __restrict__ pws,
+    const uint16_t* __restrict__ states, const float* __restrict__ dstates, uint16_t* __restrict__ dq,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, uint16_t* __restrict__ dbeta, int H, int64_t L, int NC,
+    int DV, int rule) {
+  using S = BwdBf16Shape<DK, C>;
+  using F = BwdChunkShape<uint16_t, DK, C>;
+  constexpr int KBP = S::KBP, TBP = S::TBP, VBP = S::VBP, BV = S::BV;
+  constexpr int NQ = F::NQ, NP = F::NP, NCQ = DK / 16, NCP = C / 16, NRT = C / 16;
+  static_assert(F::CP == C && F::DKP == DK, "bf16 kernel: DK and C are multiples of 32");
+  __shared__ __align__(16) unsigned char lds[S::BYTES];
+  __shared__ float as[C], das[C], dls[C];
+  auto arr = [&](int off) { return reinterpret_cast<uint16_t*>(lds + off); };
+  uint16_t *Kb = arr(S::KB), *Tb = arr(S::TB), *TbT = arr(S::TBT), *PbT = arr(S::PBT);
+  uint16_t *Sv = arr(S::SV), *dSv = arr(S::DSV), *SvT = arr(S::SVT), *dSvT = arr(S::DSVT);
+  uint16_t *dOv = arr(S::DOV), *Vv = arr(S::VV), *Dv = arr(S::DV_), *dUv = arr(S::DUV), *Uv = arr(S::UV);
+  uint16_t *dDv = arr(S::DDV), *dOvT = arr(S::DOVT), *DvT = arr(S::DVT), *dUvT = arr(S::DUVT);
+
+  const int64_t slot = blockIdx.x;
+  const int n = int(slot % NC);
+  const int64_t bh = slot / NC, h = bh % H;
+  const SeqSpan sp = seq_span<C>(nullptr, int(bh / H), h, H, L, NC);
+  const int64_t t0 = int64_t(n) * C;
+  const int valid = int(sp.len - t0 < C ? sp.len - t0 : C);
+  const int64_t row0 = (sp.bos + t0) * H + h;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), li = lane & 15, g = lane >> 4;
+  const int64_t qk_stride = int64_t(H) * DK, v_stride = int64_t(H) * DV;
+
+  // chunk operands: K, T, T^T, P^T as bf16 for the loop; Q and K stay in
+  // registers for the fp32 tail
+  F32Stager<uint16_t, C, DK> sq, sk;
+  sq.load(q + row0 * DK, qk_stride, valid, tid);
+  sk.load(k + row0 * DK, qk_stride, valid, tid);
+  {
+    Bf16Stager<uint16_t, C, C> st;
+    Bf16Stager<float, C, C> spp;
+    st.load(tws + slot * C * C, C, C, tid);
+    spp.load(pws + slot * C * C, C, C, tid);
+    Bf16Stager<uint16_t, C, DK> skb;
+    skb.load(k + row0 * DK, qk_stride, valid, tid);
+    skb.store(Kb, KBP, nullptr, 0, tid);
+    st.store(Tb, TBP, TbT, TBP, tid);
+    spp.store(nullptr, 0, PbT, TBP, tid);
+  }
+  if (tid < C) as[tid] = aws[slot * C + tid];
+
+  f32x4 dQa[NQ], dKa[NQ], dPa[NP], dTa[NP];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) dQa[i] = dKa[i] = zero4();
+#pragma unroll
+  for (int i = 0; i < NP; ++i) dPa[i] = dTa[i] = zero4();
+
+  const uint16_t* st = states + slot * DK * DV;
+  const float* dst = dstates + slot * DK * DV;
+  // one value block's operands, staged through registers one block ahead
+  Bf16Stager<uint16_t, DK, BV> ss;
+  Bf16Stager<float, DK, BV> sds;
+  Bf16Stager<uint16_t, C, BV> sv, sdo;
+  auto load_block = [&](int v0) {
+    ss.load(st + v0, DV, DK, tid);
+    sds.load(dst + v0, DV, DK, tid);
+    sv.load(v + row0 * DV + v0, v_stride, valid, tid);
+    sdo.load(dout + row0 * DV + v0, v_stride, valid, tid);
+  };
+  load_block(0);
+  for (int v0 = 0; v0 < DV; v0 += BV) {
+    __syncthreads();  // the previous block's buffers are free (and the chunk operands are in place)
+    ss.store(Sv, VBP, SvT, KBP, tid);
+    sds.store(dSv, VBP, dSvT, KBP, tid);
+    sv.store(Vv, VBP, nullptr, 0, tid);
+    sdo.store(dOv, VBP, dOvT, TBP, tid);
+    if (v0 + BV < DV) load_block(v0 + BV);  // in flight during this block
+    __syncthreads();
+    // D = V - K S,  dU = P^T dO + K dS'   (tiles of [C][BV])
+    for (int t = w; t < 2 * NRT * (BV / 16); t += 4) {
+      const int tt = t % (NRT * (BV / 16)), r0 = 16 * (tt / (BV / 16)), c0 = 16 * (tt % (BV / 16));
+      f32x4 acc = zero4();
+      if (t < NRT * (BV / 16)) {
+        tile_bf<DK>(acc, Kb, KBP, SvT, KBP, r0, c0, li, g);
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) acc[qq] = to_f32(Vv[(r0 + 4 * g + qq) * VBP + c0 + li]) - acc[qq];
+        put_tile(Dv, VBP, DvT, TBP, acc, r0, c0, li, g);
+      } else {
+        tile_bf<C>(acc, PbT, TBP, dOvT, TBP, r0, c0, li, g);
+        tile_bf<DK>(acc, Kb, KBP, dSvT, KBP, r0, c0, li, g);
+        put_tile(dUv, VBP, dUvT, TBP, acc, r0, c0, li, g);
+      }
+    }
+    __syncthreads();
+    // U = T D,  dD = T^T dU (= dV)
+    for (int t = w; t < 2 * NRT * (BV / 16); t += 4) {
+      const int tt = t % (NRT * (BV / 16)), r0 = 16 * (tt / (BV / 16)), c0 = 16 * (tt % (BV / 16));
+      f32x4 acc = zero4();
+      if (t < NRT * (BV / 16)) {
+        tile_bf<C>(acc, Tb, TBP, DvT, TBP, r0, c0, li, g);
+        put_tile(Uv, VBP, nullptr, 0, acc, r0, c0, li, g);
+      } else {
+        tile_bf<C>(acc, TbT, TBP, dUvT, TBP, r0, c0, li, g);
+        put_tile(dDv, VBP, nullptr, 0, acc, r0, c0, li, g);
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const int r = r0 + 4 * g + qq;
+          if (r < valid) dv[row0 * DV + r * v_stride + v0 + c0 + li] = from_f32<uint16_t>(acc[qq]);
+        }
+      }
+    }
+    __syncthreads();
+    // dQ += dO S^T;  dK += U dS'^T - dD S^T;  dP += dO U^T;  dT += dU D^T   (K = BV)
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int t = w + 4 * i, r0 = 16 * (t / NCQ), c0 = 16 * (t % NCQ);
+      tile_bf<BV>(dQa[i], dOv, VBP, Sv, VBP, r0, c0, li, g);
+      tile_bf<BV>(dKa[i], Uv, VBP, dSv, VBP, r0, c0, li, g);
+      f32x4 m = zero4();
+      tile_bf<BV>(m, dDv, VBP, Sv, VBP, r0, c0, li, g);
+      dKa[i] -= m;
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int t = w + 4 * i, r0 = 16 * (t / NCP), c0 = 16 * (t % NCP);
+      tile_bf<BV>(dPa[i], dOv, VBP, Uv, VBP, r0, c0, li, g);
+      tile_bf<BV>(dTa[i], dUv, VBP, Dv, VBP, r0, c0, li, g);
+    }
+  }
+  __syncthreads();  // done with the loop's arrays: the tail's fp32 arrays take their place
+
+  float* Qs = reinterpret_cast<float*>(lds + S::QS);
+  float* Ks = reinterpret_cast<float*>(lds + S::KS);
+  float* M0 = reinterpret_cast<float*>(lds + S::M0);
+  float* M1 = reinterpret_cast<float*>(lds + S::M1);
+  float* R = reinterpret_cast<float*>(lds + S::R);
+  sq.store(Qs, F::QP, tid);
+  sk.store(Ks, F::QP, tid);
+  bwd_chunk_tail<uint16_t, DK, C>(Qs, Ks, M0, M1, R, as, das, dls, dQa, dKa, dPa, dTa, xws, beta, dq, dk, dbeta,
+                                  slot, row0, valid, H, rule);
+}
+
+}  // namespace efla

@@ -238,6 +238,135 @@ struct BwdChunkShape {
   static constexpr int RBUF = VBUF > 3 * CP * CPP ? VBUF : 3 * CP * CPP;
 };
 
+// The part of a chunk's gradients after the value blocks (fp32 throughout),
+// shared by both chunk kernels: dP and dT from their accumulators, then
+//   dQ += dP K;  dK += dP^T Q;  dX = dT diag(a);  da_j = sum_i dT_ij X_ij;
+//   W = X^T dX;  dA = -W X^T (strictly lower);  da_i += sum_{j<i} dA_ij G_ij;
+//   dG = diag(a) dA;  dbeta, dlambda;  dK += (dG + dG^T) K + 2 diag(dlambda) K
+// and the stores of dq, dk and dbeta.  Qs, Ks: fp32 [CP][QP]; M0, M1: fp32
+// [CP][CPP]; R: fp32, at least 3 CP CPP; as: the chunk's coefficients.
+// Called by all threads after a barrier that frees M0, M1 and R.
+template <typename T, int DK, int C>
+__device__ __forceinline__ void bwd_chunk_tail(
+    const float* __restrict__ Qs, const float* __restrict__ Ks, float* __restrict__ M0, float* __restrict__ M1,
+    float* __restrict__ R, const float* __restrict__ as, float* __restrict__ das, float* __restrict__ dls,
+    f32x4 (&dQa)[BwdChunkShape<T, DK, C>::NQ], f32x4 (&dKa)[BwdChunkShape<T, DK, C>::NQ],
+    const f32x4 (&dPa)[BwdChunkShape<T, DK, C>::NP], const f32x4 (&dTa)[BwdChunkShape<T, DK, C>::NP],
+    const float* __restrict__ xws, const T* __restrict__ beta, T* __restrict__ dq, T* __restrict__ dk,
+    T* __restrict__ dbeta, int64_t slot, int64_t row0, int valid, int H, int rule) {
+  using S = BwdChunkShape<T, DK, C>;
+  constexpr int DKP = S::DKP, CP = S::CP, QP = S::QP, CPP = S::CPP, NQ = S::NQ, NP = S::NP;
+  constexpr int NCQ = DKP / 16, NCP = CP / 16;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), li = lane & 15, g = lane >> 4;
+  const int64_t qk_stride = int64_t(H) * DK;
+  // dP (lower, diagonal included) -> M1; dT (lower) -> M0; X -> R0
+  float* X = R;
+  float* R1 = R + CP * CPP;
+  float* R2 = R1 + CP * CPP;
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int t = w + 4 * i, r0 = 16 * (t / NCP), c0 = 16 * (t % NCP);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int r = r0 + 4 * g + qq, c = c0 + li;
+      M1[r * CPP + c] = c <= r ? dPa[i][qq] : 0.0f;
+      M0[r * CPP + c] = c <= r ? dTa[i][qq] : 0.0f;
+    }
+  }
+  {
+    F32Stager<float, C, C> sx;
+    sx.load(xws + slot * C * C, C, C, tid);
+    if constexpr (C < CP) {
+      for (int i = tid; i < CP * CPP; i += kThreads) X[i] = 0.0f;
+      __syncthreads();
+    }
+    sx.store(X, CPP, tid);  // X's rows and columns < C; the zeros above cover the padding
+  }
+  __syncthreads();
+  // dQ += dP K;  dK += dP^T Q;  dX = dT diag(a);  da_j = sum_i dT_ij X_ij
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int t = w + 4 * i, r0 = 16 * (t / NCQ), c0 = 16 * (t % NCQ);
+    tile_mma16<false, false>(dQa[i], M1, CPP, Ks, QP, r0, c0, CP, li, g);
+    tile_mma16<true, false>(dKa[i], M1, CPP, Qs, QP, r0, c0, CP, li, g);
+  }
+  for (int i = tid; i < CP * CP; i += kThreads) {
+    const int r = i / CP, c = i % CP;
+    R1[r * CPP + c] = M0[r * CPP + c] * as[c];
+  }
+  if (tid < CP) {
+    float s = 0.0f;
+    for (int r = 0; r < CP; ++r) s = fmaf(M0[r * CPP + tid], X[r * CPP + tid], s);
+    das[tid] = s;
+  }
+  __syncthreads();
+  // W = X^T dX -> M1
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int t = w + 4 * i, r0 = 16 * (t / NCP), c0 = 16 * (t % NCP);
+    f32x4 acc = zero4();
+    tile_mma16<true, false>(acc, X, CPP, R1, CPP, r0, c0, CP, li, g);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) M1[(r0 + 4 * g + qq) * CPP + c0 + li] = acc[qq];
+  }
+  __syncthreads();
+  // dA = -W X^T (strictly lower) -> R2;  G = K K^T -> R1
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int t = w + 4 * i, r0 = 16 * (t / NCP), c0 = 16 * (t % NCP);
+    f32x4 acc = zero4(), gg = zero4();
+    tile_mma16<false, true>(acc, M1, CPP, X, CPP, r0, c0, CP, li, g);
+    tile_mma16<false, true>(gg, Ks, QP, Ks, QP, r0, c0, DKP, li, g);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int r = r0 + 4 * g + qq, c = c0 + li;
+      R2[r * CPP + c] = c < r ? -acc[qq] : 0.0f;
+      R1[r * CPP + c] = gg[qq];
+    }
+  }
+  __syncthreads();
+  // da_i += sum_{j<i} dA_ij G_ij;  dG = diag(a) dA -> R0 (X is done)
+  if (tid < CP) {
+    float s = 0.0f;
+    for (int c = 0; c < tid; ++c) s = fmaf(R2[tid * CPP + c], R1[tid * CPP + c], s);
+    das[tid] += s;
+  }
+  for (int i = tid; i < CP * CP; i += kThreads) {
+    const int r = i / CP, c = i % CP;
+    X[r * CPP + c] = as[r] * R2[r * CPP + c];
+  }
+  __syncthreads();
+  // dbeta, dlambda
+  if (tid < CP) {
+    float db = 0.0f, dl = 0.0f;
+    if (tid < valid) {
+      const float bt = to_f32(beta[row0 + int64_t(tid) * H]);
+      float da_db, da_dl;
+      efla_alpha_grad(bt, R1[tid * CPP + tid], rule, da_db, da_dl);
+      db = das[tid] * da_db;
+      dl = das[tid] * da_dl;
+      dbeta[row0 + int64_t(tid) * H] = from_f32<T>(db);
+    }
+    dls[tid] = dl;
+  }
+  __syncthreads();
+  // dK += (dG + dG^T) K + 2 diag(dlambda) K;  write dq, dk
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int t = w + 4 * i, r0 = 16 * (t / NCQ), c0 = 16 * (t % NCQ);
+    tile_mma16<false, false>(dKa[i], X, CPP, Ks, QP, r0, c0, CP, li, g);
+    tile_mma16<true, false>(dKa[i], X, CPP, Ks, QP, r0, c0, CP, li, g);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int r = r0 + 4 * g + qq, c = c0 + li;
+      if (r < valid && c < DK) {
+        dq[row0 * DK + r * qk_stride + c] = from_f32<T>(dQa[i][qq]);
+        dk[row0 * DK + r * qk_stride + c] = from_f32<T>(dKa[i][qq] + 2.0f * dls[r] * Ks[r * QP + c]);
+      }
+    }
+  }
+}
+
 template <typename T, int DK, int C>
 __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ beta,
@@ -383,112 +512,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(
   }
   __syncthreads();  // done with T, P and the value-block buffers
 
-  // dP (lower, diagonal included) -> M1; dT (lower) -> M0; X -> R0
-  float* X = R;
-  float* R1 = R + CP * CPP;
-  float* R2 = R1 + CP * CPP;
-#pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    const int t = w + 4 * i, r0 = 16 * (t / NCP), c0 = 16 * (t % NCP);
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      const int r = r0 + 4 * g + qq, c = c0 + li;
-      M1[r * CPP + c] = c <= r ? dPa[i][qq] : 0.0f;
-      M0[r * CPP + c] = c <= r ? dTa[i][qq] : 0.0f;
-    }
-  }
-  {
-    F32Stager<float, C, C> sx;
-    sx.load(xws + slot * C * C, C, C, tid);
-    if constexpr (C < CP) {
-      for (int i = tid; i < CP * CPP; i += kThreads) X[i] = 0.0f;
-      __syncthreads();
-    }
-    sx.store(X, CPP, tid);  // X's rows and columns < C; the zeros above cover the padding
-  }
-  __syncthreads();
-  // dQ += dP K;  dK += dP^T Q;  dX = dT diag(a);  da_j = sum_i dT_ij X_ij
-#pragma unroll
-  for (int i = 0; i < NQ; ++i) {
-    const int t = w + 4 * i, r0 = 16 * (t / NCQ), c0 = 16 * (t % NCQ);
-    tile_mma16<false, false>(dQa[i], M1, CPP, Ks, QP, r0, c0, CP, li, g);
-    tile_mma16<true, false>(dKa[i], M1, CPP, Qs, QP, r0, c0, CP, li, g);
-  }
-  for (int i = tid; i < CP * CP; i += kThreads) {
-    const int r = i / CP, c = i % CP;
-    R1[r * CPP + c] = M0[r * CPP + c] * as[c];
-  }
-  if (tid < CP) {
-    float s = 0.0f;
-    for (int r = 0; r < CP; ++r) s = fmaf(M0[r * CPP + tid], X[r * CPP + tid], s);
-    das[tid] = s;
-  }
-  __syncthreads();
-  // W = X^T dX -> M1
-#pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    const int t = w + 4 * i, r0 = 16 * (t / NCP), c0 = 16 * (t % NCP);
-    f32x4 acc = zero4();
-    tile_mma16<true, false>(acc, X, CPP, R1, CPP, r0, c0, CP, li, g);
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) M1[(r0 + 4 * g + qq) * CPP + c0 + li] = acc[qq];
-  }
-  __syncthreads();
-  // dA = -W X^T (strictly lower) -> R2;  G = K K^T -> R1
-#pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    const int t = w + 4 * i, r0 = 16 * (t / NCP), c0 = 16 * (t % NCP);
-    f32x4 acc = zero4(), gg = zero4();
-    tile_mma16<false, true>(acc, M1, CPP, X, CPP, r0, c0, CP, li, g);
-    tile_mma16<false, true>(gg, Ks, QP, Ks, QP, r0, c0, DKP, li, g);
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      const int r = r0 + 4 * g + qq, c = c0 + li;
-      R2[r * CPP + c] = c < r ? -acc[qq] : 0.0f;
-      R1[r * CPP + c] = gg[qq];
-    }
-  }
-  __syncthreads();
-  // da_i += sum_{j<i} dA_ij G_ij;  dG = diag(a) dA -> R0 (X is done)
-  if (tid < CP) {
-    float s = 0.0f;
-    for (int c = 0; c < tid; ++c) s = fmaf(R2[tid * CPP + c], R1[tid * CPP + c], s);
-    das[tid] += s;
-  }
-  for (int i = tid; i < CP * CP; i += kThreads) {
-    const int r = i / CP, c = i % CP;
-    X[r * CPP + c] = as[r] * R2[r * CPP + c];
-  }
-  __syncthreads();
-  // dbeta, dlambda
-  if (tid < CP) {
-    float db = 0.0f, dl = 0.0f;
-    if (tid < valid) {
-      const float bt = to_f32(beta[row0 + int64_t(tid) * H]);
-      float da_db, da_dl;
-      efla_alpha_grad(bt, R1[tid * CPP + tid], rule, da_db, da_dl);
-      db = das[tid] * da_db;
-      dl = das[tid] * da_dl;
-      dbeta[row0 + int64_t(tid) * H] = from_f32<T>(db);
-    }
-    dls[tid] = dl;
-  }
-  __syncthreads();
-  // dK += (dG + dG^T) K + 2 diag(dlambda) K;  write dq, dk
-#pragma unroll
-  for (int i = 0; i < NQ; ++i) {
-    const int t = w + 4 * i, r0 = 16 * (t / NCQ), c0 = 16 * (t % NCQ);
-    tile_mma16<false, false>(dKa[i], X, CPP, Ks, QP, r0, c0, CP, li, g);
-    tile_mma16<true, false>(dKa[i], X, CPP, Ks, QP, r0, c0, CP, li, g);
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      const int r = r0 + 4 * g + qq, c = c0 + li;
-      if (r < valid && c < DK) {
-        dq[row0 * DK + r * qk_stride + c] = from_f32<T>(dQa[i][qq]);
-        dk[row0 * DK + r * qk_stride + c] = from_f32<T>(dKa[i][qq] + 2.0f * dls[r] * Ks[r * QP + c]);
-      }
-    }
-  }
+  bwd_chunk_tail<T, DK, C>(Qs, Ks, M0, M1, R, as, das, dls, dQa, dKa, dPa, dTa, xws, beta, dq, dk, dbeta, slot,
+                           row0, valid, H, rule);
 }
 
 }  // namespace efla

@@ -1,7 +1,9 @@
 """The chunked backward pass (efla_chunk_bwd) against the fp64 oracle's
 reverse-mode gradients on the same inputs.  Error per gradient tensor is
 normwise (max|x - y| / max|y|), with the forward pass's bounds: 1e-4 for fp32
-inputs, 2e-2 for bf16 inputs (bf16 operands and gradients, fp32 arithmetic)."""
+inputs, 2e-2 for bf16 inputs (bf16 operands and gradients, fp32 accumulation).
+bf16 inputs take the bf16 matrix-core chunk kernel where d_k and the chunk are
+multiples of 32 and d_v of 32, else the fp32 one (EFLA_BWD_IMPL=fp32 forces it)."""
 import numpy as np
 import pytest
 import torch
@@ -54,6 +56,7 @@ SHAPES = [
     ("bf16", 64, 64, 64, 300),
     ("bf16", 128, 128, 64, 257),
     ("bf16", 64, 128, 32, 129),
+    ("bf16", 128, 16, 32, 47),    # d_v not a multiple of 32: the fp32 chunk kernel
 ]
 
 
@@ -113,3 +116,18 @@ def test_backward_full_1p3b_shape():
     require_gpu()
     w = W.get("shape_1p3b")
     _check(W.generate(w, device="cuda"), 64, "shape_1p3b full", seed=9)
+
+
+@pytest.mark.parametrize("impl", ["fp32", "bf16"])
+def test_backward_bf16_inputs_both_chunk_kernels(impl, monkeypatch):
+    """bf16 inputs through the fp32 chunk kernel and the bf16 one, at the 1.3B
+    head configuration with a ragged last chunk and the Euler rule too."""
+    require_gpu()
+    if impl == "fp32":
+        monkeypatch.setenv("EFLA_BWD_IMPL", "fp32")
+    else:
+        monkeypatch.delenv("EFLA_BWD_IMPL", raising=False)
+    w = W.get("shape_1p3b")
+    inp = W.generate(w, device="cuda", B=1, H=3, L=200, seed=930)
+    _check(inp, 64, f"bf16 inputs, {impl} chunk kernel", seed=31)
+    _check(inp, 64, f"bf16 inputs, {impl} chunk kernel, Euler rule", seed=32, rule="euler")
