@@ -3,12 +3,13 @@
 //
 // Same formulas and work split as bwd_chunk_kernel (bwd_kernels.h): one
 // workgroup per (b, h, chunk), value columns streamed in blocks, dQ, dK, dP and
-// dT accumulated in fp32 registers, then the fp32 tail (bwd_chunk_tail).  What
-// differs is the value-block loop, which carries about three quarters of the
-// products: its operands sit in LDS as bf16 and every product is one
-// v_mfma_f32_16x16x32_bf16 per 32-deep slice.  The operands that are not bf16
-// already (P, dS', and the intermediates D = V - K S, dU, U, dD) are rounded to
-// bf16 once, like the states the forward products use.
+// dT accumulated in fp32 registers, then the UT-transform part.  What differs
+// is where the products run: every product with a value block, Q or K is one
+// v_mfma_f32_16x16x32_bf16 per 32-deep slice on bf16 operands in LDS.  The
+// operands that are not bf16 already (P, dS', the intermediates D = V - K S,
+// dU, U, dD, and dP, dG + dG^T) are rounded to bf16 once, like the states the
+// forward products use; X, W = X^T dX, dA and the coefficient gradients stay
+// fp32 (fp32 matrix cores and VALU).
 //
 // Every product is written acc += A B with A read as rows of an [M][K] array
 // and B as rows of an [N][K] array (B's transpose), so each operand fragment is
@@ -53,14 +54,20 @@ struct BwdBf16Shape {
   static constexpr int DVT = DOVT + BV * TBP * 2;
   static constexpr int DUVT = DVT + BV * TBP * 2;
   static constexpr int LOOP_BYTES = DUVT + BV * TBP * 2;
-  // the tail's fp32 arrays (as in bwd_chunk_kernel)
-  using F = BwdChunkShape<uint16_t, DK, C>;
-  static constexpr int QS = 0;
-  static constexpr int KS = QS + F::CP * F::QP * 4;
-  static constexpr int M0 = KS + F::CP * F::QP * 4;
-  static constexpr int M1 = M0 + F::CP * F::CPP * 4;
-  static constexpr int R = M1 + F::CP * F::CPP * 4;
-  static constexpr int TAIL_BYTES = R + F::RBUF * 4;
+  // the tail's arrays (K stays where the loop had it): fp32 [C][CPP] for dT
+  // (then dX, then G), X, W and dA; bf16 K^T, Q^T [DK][TBP] and dP, dP^T,
+  // dG + dG^T [C][TBP]
+  static constexpr int CPP = C + 4;
+  static constexpr int TA0 = TB;
+  static constexpr int TX = TA0 + C * CPP * 4;
+  static constexpr int TW = TX + C * CPP * 4;
+  static constexpr int TDA = TW + C * CPP * 4;
+  static constexpr int TKBT = TDA + C * CPP * 4;
+  static constexpr int TQBT = TKBT + DK * TBP * 2;
+  static constexpr int TDPB = TQBT + DK * TBP * 2;
+  static constexpr int TDPBT = TDPB + C * TBP * 2;
+  static constexpr int TEB = TDPBT + C * TBP * 2;
+  static constexpr int TAIL_BYTES = TEB + C * TBP * 2;
   static constexpr int BYTES = LOOP_BYTES > TAIL_BYTES ? LOOP_BYTES : TAIL_BYTES;
 };
 
@@ -176,9 +183,9 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_bf16_kernel(
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), li = lane & 15, g = lane >> 4;
   const int64_t qk_stride = int64_t(H) * DK, v_stride = int64_t(H) * DV;
 
-  // chunk operands: K, T, T^T, P^T as bf16 for the loop; Q and K stay in
-  // registers for the fp32 tail
-  F32Stager<uint16_t, C, DK> sq, sk;
+  // chunk operands: K, T, T^T, P^T as bf16 for the loop; Q and K also stay in
+  // registers, for their transposes in the tail
+  Bf16Stager<uint16_t, C, DK> sq, sk;
   sq.load(q + row0 * DK, qk_stride, valid, tid);
   sk.load(k + row0 * DK, qk_stride, valid, tid);
   {
@@ -186,9 +193,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_bf16_kernel(
     Bf16Stager<float, C, C> spp;
     st.load(tws + slot * C * C, C, C, tid);
     spp.load(pws + slot * C * C, C, C, tid);
-    Bf16Stager<uint16_t, C, DK> skb;
-    skb.load(k + row0 * DK, qk_stride, valid, tid);
-    skb.store(Kb, KBP, nullptr, 0, tid);
+    sk.store(Kb, KBP, nullptr, 0, tid);
     st.store(Tb, TBP, TbT, TBP, tid);
     spp.store(nullptr, 0, PbT, TBP, tid);
   }
@@ -272,17 +277,123 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_bf16_kernel(
       tile_bf<BV>(dTa[i], dUv, VBP, Dv, VBP, r0, c0, li, g);
     }
   }
-  __syncthreads();  // done with the loop's arrays: the tail's fp32 arrays take their place
+  __syncthreads();  // done with the loop's arrays (K stays): the tail's arrays take their place
 
-  float* Qs = reinterpret_cast<float*>(lds + S::QS);
-  float* Ks = reinterpret_cast<float*>(lds + S::KS);
-  float* M0 = reinterpret_cast<float*>(lds + S::M0);
-  float* M1 = reinterpret_cast<float*>(lds + S::M1);
-  float* R = reinterpret_cast<float*>(lds + S::R);
-  sq.store(Qs, F::QP, tid);
-  sk.store(Ks, F::QP, tid);
-  bwd_chunk_tail<uint16_t, DK, C>(Qs, Ks, M0, M1, R, as, das, dls, dQa, dKa, dPa, dTa, xws, beta, dq, dk, dbeta,
-                                  slot, row0, valid, H, rule);
+  // The UT-transform part of the gradient:
+  //   dQ += dP K;  dK += dP^T Q;  dX = dT diag(a);  da_j = sum_i dT_ij X_ij;
+  //   W = X^T dX;  dA = -W X^T (strictly lower);  da_i += sum_{j<i} dA_ij G_ij;
+  //   dG = diag(a) dA;  dbeta, dlambda;  dK += (dG + dG^T) K + 2 diag(dlambda) K.
+  // The products with K and Q run on bf16 matrix cores (dP and dG + dG^T
+  // rounded once); X, W, dA, G and the coefficient gradients stay fp32.
+  constexpr int CPP = S::CPP;
+  auto f32 = [&](int off) { return reinterpret_cast<float*>(lds + off); };
+  float *A0 = f32(S::TA0), *X = f32(S::TX), *Wm = f32(S::TW), *dA = f32(S::TDA);
+  uint16_t *KbT = arr(S::TKBT), *QbT = arr(S::TQBT), *dPb = arr(S::TDPB), *dPbT = arr(S::TDPBT), *Eb = arr(S::TEB);
+  const int64_t qk_row = row0 * DK;
+  // dP (lower, diagonal included) as bf16 rows and transposed; dT (lower) -> A0; X; K^T, Q^T
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int t = w + 4 * i, r0 = 16 * (t / NCP), c0 = 16 * (t % NCP);
+    f32x4 p;
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int r = r0 + 4 * g + qq, c = c0 + li;
+      p[qq] = c <= r ? dPa[i][qq] : 0.0f;
+      A0[r * CPP + c] = c <= r ? dTa[i][qq] : 0.0f;
+    }
+    put_tile(dPb, TBP, dPbT, TBP, p, r0, c0, li, g);
+  }
+  {
+    F32Stager<float, C, C> sx;
+    sx.load(xws + slot * C * C, C, C, tid);
+    sx.store(X, CPP, tid);
+  }
+  sk.store(nullptr, 0, KbT, TBP, tid);
+  sq.store(nullptr, 0, QbT, TBP, tid);
+  __syncthreads();
+  // dQ += dP K;  dK += dP^T Q;  da_j = sum_i dT_ij X_ij
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int t = w + 4 * i, r0 = 16 * (t / NCQ), c0 = 16 * (t % NCQ);
+    tile_bf<C>(dQa[i], dPb, TBP, KbT, TBP, r0, c0, li, g);
+    tile_bf<C>(dKa[i], dPbT, TBP, QbT, TBP, r0, c0, li, g);
+  }
+  if (tid < C) {
+    float s = 0.0f;
+    for (int r = 0; r < C; ++r) s = fmaf(A0[r * CPP + tid], X[r * CPP + tid], s);
+    das[tid] = s;
+  }
+  __syncthreads();
+  // dX = dT diag(a), in place
+  for (int i = tid; i < C * C; i += kThreads) {
+    const int r = i / C, c = i % C;
+    A0[r * CPP + c] *= as[c];
+  }
+  __syncthreads();
+  // W = X^T dX
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int t = w + 4 * i, r0 = 16 * (t / NCP), c0 = 16 * (t % NCP);
+    f32x4 acc = zero4();
+    tile_mma16<true, false>(acc, X, CPP, A0, CPP, r0, c0, C, li, g);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) Wm[(r0 + 4 * g + qq) * CPP + c0 + li] = acc[qq];
+  }
+  __syncthreads();
+  // dA = -W X^T (strictly lower);  G = K K^T -> A0
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int t = w + 4 * i, r0 = 16 * (t / NCP), c0 = 16 * (t % NCP);
+    f32x4 acc = zero4(), gg = zero4();
+    tile_mma16<false, true>(acc, Wm, CPP, X, CPP, r0, c0, C, li, g);
+    tile_bf<DK>(gg, Kb, KBP, Kb, KBP, r0, c0, li, g);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int r = r0 + 4 * g + qq, c = c0 + li;
+      dA[r * CPP + c] = c < r ? -acc[qq] : 0.0f;
+      A0[r * CPP + c] = gg[qq];
+    }
+  }
+  __syncthreads();
+  // da_i += sum_{j<i} dA_ij G_ij;  dG + dG^T with dG = diag(a) dA, as bf16
+  if (tid < C) {
+    float s = 0.0f;
+    for (int c = 0; c < tid; ++c) s = fmaf(dA[tid * CPP + c], A0[tid * CPP + c], s);
+    das[tid] += s;
+  }
+  for (int i = tid; i < C * C; i += kThreads) {
+    const int r = i / C, c = i % C;
+    Eb[r * TBP + c] = from_f32<uint16_t>(as[r] * dA[r * CPP + c] + as[c] * dA[c * CPP + r]);
+  }
+  __syncthreads();
+  // dbeta, dlambda (lambda = G's diagonal)
+  if (tid < C) {
+    float dl = 0.0f;
+    if (tid < valid) {
+      const float bt = to_f32(beta[row0 + int64_t(tid) * H]);
+      float da_db, da_dl;
+      efla_alpha_grad(bt, A0[tid * CPP + tid], rule, da_db, da_dl);
+      dl = das[tid] * da_dl;
+      dbeta[row0 + int64_t(tid) * H] = from_f32<uint16_t>(das[tid] * da_db);
+    }
+    dls[tid] = dl;
+  }
+  __syncthreads();
+  // dK += (dG + dG^T) K + 2 diag(dlambda) K;  write dq, dk
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int t = w + 4 * i, r0 = 16 * (t / NCQ), c0 = 16 * (t % NCQ);
+    tile_bf<C>(dKa[i], Eb, TBP, KbT, TBP, r0, c0, li, g);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int r = r0 + 4 * g + qq, c = c0 + li;
+      if (r < valid) {
+        dq[qk_row + r * qk_stride + c] = from_f32<uint16_t>(dQa[i][qq]);
+        dk[qk_row + r * qk_stride + c] =
+            from_f32<uint16_t>(dKa[i][qq] + 2.0f * dls[r] * to_f32(Kb[r * KBP + c]));
+      }
+    }
+  }
 }
 
 }  // namespace efla
