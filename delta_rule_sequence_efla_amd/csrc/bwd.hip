@@ -78,9 +78,20 @@ hipError_t bwd_launch_impl(const T* q, const T* k, const T* v, const T* beta, co
     // 2. the state at the start of every chunk (no output)
     if (hipError_t e = chunk_states<T, DK, C>(q, k, v, tws, s0, sws, B, H, L, DV, s); e != hipSuccess) return e;
   }
-  // 3. reverse pass over chunks: dS at every chunk end, and dS_0
-  hipLaunchKernelGGL((bwd_state_kernel<T, DK, C>), dim3(unsigned(BH * (DV / 16))), dim3(kThreads), 0, s, q, k,
-                     dout, tws, pws, dsf, dsws, ds0, H, L, NC, DV, DV / 16);
+  // 3. reverse pass over chunks: dS at every chunk end, and dS_0 (bf16 inputs
+  // on bf16 matrix cores where the shape allows, like step 4)
+  bool state_done = false;
+  if constexpr (sizeof(T) == 2 && DK % 32 == 0 && C % 32 == 0) {
+    const char* impl = getenv("EFLA_BWD_IMPL");
+    if (!(impl && strcmp(impl, "fp32") == 0) && bwd_bf16_supported(DK, DV, C)) {
+      hipLaunchKernelGGL((bwd_state_bf16_kernel<DK, C>), dim3(unsigned(BH * (DV / kBwdBV))), dim3(kThreads), 0, s,
+                         q, k, dout, tws, pws, dsf, dsws, ds0, H, L, NC, DV, DV / kBwdBV);
+      state_done = true;
+    }
+  }
+  if (!state_done)
+    hipLaunchKernelGGL((bwd_state_kernel<T, DK, C>), dim3(unsigned(BH * (DV / 16))), dim3(kThreads), 0, s, q, k,
+                       dout, tws, pws, dsf, dsws, ds0, H, L, NC, DV, DV / 16);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   if (slots == 0) return hipSuccess;
   // 4. every chunk's gradients: bf16 inputs on bf16 matrix cores where the

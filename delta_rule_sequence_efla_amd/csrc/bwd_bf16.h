@@ -396,4 +396,136 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_bf16_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// The reverse sequential pass for bf16 inputs: one workgroup per (b, h, 32
+// value columns), for chunk n = last .. 0:
+//     dstates[n] = dS;   E = P^T dO + K dS;   F = T^T E;   dS += Q^T dO - K^T F
+// as in bwd_state_kernel, with dS (d_k x 32) in fp32 registers (each wavefront
+// owns d_k / 32 of its 16x16 tiles) and every product on bf16 matrix cores:
+// dS, E and F enter the products as bf16 copies (dS^T, E^T, F^T in LDS), Q, K,
+// T and P as bf16 in the layouts the products read (K rows; K^T, Q^T, T^T,
+// P^T, dO^T).  The next chunk's operands are loaded while this one computes.
+// ---------------------------------------------------------------------------
+template <int DK, int C>
+struct BwdStateBf16Shape {
+  static constexpr int BV = kBwdBV;
+  static constexpr int KBP = DK + 8, TBP = C + 8;
+  static constexpr int KB = 0;                          // K      [C][KBP]
+  static constexpr int KBT = KB + C * KBP * 2;          // K^T    [DK][TBP]
+  static constexpr int QBT = KBT + DK * TBP * 2;        // Q^T    [DK][TBP]
+  static constexpr int TBT = QBT + DK * TBP * 2;        // T^T    [C][TBP]
+  static constexpr int PBT = TBT + C * TBP * 2;         // P^T    [C][TBP]
+  static constexpr int DOT = PBT + C * TBP * 2;         // dO^T   [BV][TBP]
+  static constexpr int DST = DOT + BV * TBP * 2;        // dS^T   [BV][KBP]
+  static constexpr int ET = DST + BV * KBP * 2;         // E^T    [BV][TBP]
+  static constexpr int FT = ET + BV * TBP * 2;          // F^T    [BV][TBP]
+  static constexpr int BYTES = FT + BV * TBP * 2;
+  static constexpr int NS = (DK / 16) * (BV / 16) / 4;  // dS tiles per wavefront
+  static constexpr int NE = (C / 16) * (BV / 16) / 4;   // E / F tiles per wavefront
+};
+
+template <int DK, int C>
+__global__ __launch_bounds__(kThreads) void bwd_state_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ dout,
+    const uint16_t* __restrict__ tws, const float* __restrict__ pws, const float* __restrict__ dsf,
+    float* __restrict__ dstates, float* __restrict__ ds0, int H, int64_t L, int NC, int DV, int NVB) {
+  using S = BwdStateBf16Shape<DK, C>;
+  constexpr int KBP = S::KBP, TBP = S::TBP, BV = S::BV, NS = S::NS, NE = S::NE;
+  static_assert(NS >= 1 && NE >= 1, "d_k and the chunk are multiples of 32");
+  __shared__ __align__(16) unsigned char lds[S::BYTES];
+  auto arr = [&](int off) { return reinterpret_cast<uint16_t*>(lds + off); };
+  uint16_t *Kb = arr(S::KB), *KbT = arr(S::KBT), *QbT = arr(S::QBT), *TbT = arr(S::TBT), *PbT = arr(S::PBT);
+  uint16_t *dOT = arr(S::DOT), *dST = arr(S::DST), *ET = arr(S::ET), *FT = arr(S::FT);
+
+  const int x = blockIdx.x, bh = x / NVB, vb = x % NVB;
+  const int64_t h = bh % H;
+  const SeqSpan sp = seq_span<C>(nullptr, bh / H, h, H, L, NC);
+  const int v0 = BV * vb;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), li = lane & 15, g = lane >> 4;
+  const int64_t qk_stride = int64_t(H) * DK, v_stride = int64_t(H) * DV;
+
+  // dS tiles of this wavefront: tile t = w + 4 i covers dims 16 (t / 2) .., columns 16 (t % 2) ..
+  f32x4 dS[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int t = w + 4 * i, d0 = 16 * (t / 2), c0 = 16 * (t % 2);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq)
+      dS[i][qq] = dsf != nullptr ? dsf[(int64_t(bh) * DK + d0 + 4 * g + qq) * DV + v0 + c0 + li] : 0.0f;
+  }
+
+  // chunk n's operands, staged through registers one chunk ahead
+  Bf16Stager<uint16_t, C, DK> sq, sk;
+  Bf16Stager<uint16_t, C, C> st;
+  Bf16Stager<float, C, C> spp;
+  Bf16Stager<uint16_t, C, BV> sdo;
+  auto load = [&](int n) {
+    const int64_t t0 = int64_t(n) * C;
+    const int valid = int(sp.len - t0 < C ? sp.len - t0 : C);
+    const int64_t row0 = (sp.bos + t0) * H + h;
+    sq.load(q + row0 * DK, qk_stride, valid, tid);
+    sk.load(k + row0 * DK, qk_stride, valid, tid);
+    sdo.load(dout + row0 * DV + v0, v_stride, valid, tid);
+    st.load(tws + (sp.slot0 + n) * C * C, C, C, tid);
+    spp.load(pws + (sp.slot0 + n) * C * C, C, C, tid);
+  };
+  if (sp.nc > 0) load(sp.nc - 1);
+
+  for (int n = sp.nc - 1; n >= 0; --n) {
+    __syncthreads();  // the previous chunk's products are done with every array
+    // dstates[n] = dS (fp32, global) and dS^T (bf16, LDS)
+    float* dst = dstates + (sp.slot0 + n) * DK * DV;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int t = w + 4 * i, d0 = 16 * (t / 2), c0 = 16 * (t % 2);
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) dst[(d0 + 4 * g + qq) * DV + v0 + c0 + li] = dS[i][qq];
+      st4(dST + (c0 + li) * KBP + d0 + 4 * g, dS[i]);
+    }
+    sk.store(Kb, KBP, KbT, TBP, tid);
+    sq.store(nullptr, 0, QbT, TBP, tid);
+    st.store(nullptr, 0, TbT, TBP, tid);
+    spp.store(nullptr, 0, PbT, TBP, tid);
+    sdo.store(nullptr, 0, dOT, TBP, tid);
+    if (n > 0) load(n - 1);  // in flight during this chunk
+    __syncthreads();
+    // E = P^T dO + K dS   ([C][BV] tiles; stored as E^T)
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+      const int t = w + 4 * i, r0 = 16 * (t / 2), c0 = 16 * (t % 2);
+      f32x4 acc = zero4();
+      tile_bf<C>(acc, PbT, TBP, dOT, TBP, r0, c0, li, g);
+      tile_bf<DK>(acc, Kb, KBP, dST, KBP, r0, c0, li, g);
+      st4(ET + (c0 + li) * TBP + r0 + 4 * g, acc);
+    }
+    __syncthreads();
+    // F = T^T E   (stored as F^T)
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+      const int t = w + 4 * i, r0 = 16 * (t / 2), c0 = 16 * (t % 2);
+      f32x4 acc = zero4();
+      tile_bf<C>(acc, TbT, TBP, ET, TBP, r0, c0, li, g);
+      st4(FT + (c0 + li) * TBP + r0 + 4 * g, acc);
+    }
+    __syncthreads();
+    // dS += Q^T dO - K^T F
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int t = w + 4 * i, d0 = 16 * (t / 2), c0 = 16 * (t % 2);
+      f32x4 m = zero4();
+      tile_bf<C>(dS[i], QbT, TBP, dOT, TBP, d0, c0, li, g);
+      tile_bf<C>(m, KbT, TBP, FT, TBP, d0, c0, li, g);
+      dS[i] -= m;
+    }
+  }
+  if (ds0 != nullptr) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int t = w + 4 * i, d0 = 16 * (t / 2), c0 = 16 * (t % 2);
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) ds0[(int64_t(bh) * DK + d0 + 4 * g + qq) * DV + v0 + c0 + li] = dS[i][qq];
+    }
+  }
+}
+
 }  // namespace efla
