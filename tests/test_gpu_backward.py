@@ -87,18 +87,27 @@ def test_backward_unnormalised_and_stiff():
     _check(W.generate(wb, device="cuda", B=1, L=300, H=2, seed=934), 64, "stiff bf16", seed=6)
 
 
-def test_backward_optional_state_gradients_and_empty_sequence():
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_backward_optional_state_gradients_and_empty_sequence(dt):
     require_gpu()
-    w = W.get("shape_340m", dtype="f32", dk=32, dv=32, chunk=32)
+    w = W.get("shape_340m", dtype=dt, dk=32, dv=32, chunk=32)
     inp = W.generate(w, device="cuda", B=1, L=70, H=2, seed=935)
-    _check(inp, 32, "no final-state gradient", seed=7, with_dsf=False)
+    _check(inp, 32, f"{dt}: no final-state gradient", seed=7, with_dsf=False)
     inp0 = W.generate(w, device="cuda", B=1, L=0, H=2, seed=936)
     dsf = torch.randn(1, 2, 32, 32, device="cuda")
-    d_o = torch.empty(1, 0, 2, 32, device="cuda")
+    d_o = torch.empty(1, 0, 2, 32, device="cuda", dtype=inp0["q"].dtype)
     dq, dk, dv, db, ds0 = efla.efla_chunk_bwd(inp0["q"], inp0["k"], inp0["v"], inp0["beta"], d_o, inp0["s0"], dsf,
                                               chunk=32)
     torch.cuda.synchronize()
     assert dq.numel() == 0 and torch.equal(ds0, dsf)
+    # without ds0 the other gradients are the same bits
+    g = torch.Generator().manual_seed(8)
+    d_o = torch.randn(inp["v"].shape, generator=g).to(inp["v"].dtype).cuda()
+    args = (inp["q"], inp["k"], inp["v"], inp["beta"], d_o, inp["s0"], None)
+    full = efla.efla_chunk_bwd(*args, chunk=32)
+    part = efla.efla_chunk_bwd(*args, chunk=32, want_ds0=False)
+    torch.cuda.synchronize()
+    assert part[4] is None and all(torch.equal(a, b) for a, b in zip(full[:4], part[:4]))
 
 
 def test_backward_1p3b_heads_short_sequence():
