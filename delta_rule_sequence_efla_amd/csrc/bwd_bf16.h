@@ -105,7 +105,10 @@ __device__ __forceinline__ void put_tile(uint16_t* X, int pitch, uint16_t* XT, i
 // elements apart, rows at or past `valid` read as zero), staged through
 // registers into bf16 LDS: load() issues 16-byte loads, store() writes the
 // tile as rows (dst [ROWS][pitch]) and, if dstT, as its transpose
-// (dstT [COLS][pitchT]).
+// (dstT [COLS][pitchT]).  Consecutive threads take consecutive rows of one
+// 16-byte column slice, so the transposed 2-byte stores of a wavefront land on
+// consecutive halfwords (conflict-free); the row stores, 16 rows apart by the
+// padded pitch, spread over the banks too.
 template <typename S, int ROWS, int COLS>
 struct Bf16Stager {
   static constexpr int VN = 16 / int(sizeof(S)), VPR = COLS / VN, TOT = ROWS * VPR, CNT = cdiv(TOT, kThreads);
@@ -115,7 +118,7 @@ struct Bf16Stager {
 #pragma unroll
     for (int i = 0; i < CNT; ++i) {
       const int idx = tid + i * kThreads;
-      const int t = idx / VPR, c = (idx % VPR) * VN;
+      const int t = idx % ROWS, c = (idx / ROWS) * VN;
       r[i] = u32x4{0u, 0u, 0u, 0u};
       if (idx < TOT && t < valid) r[i] = *reinterpret_cast<const u32x4*>(src + t * stride + c);
     }
@@ -125,7 +128,7 @@ struct Bf16Stager {
     for (int i = 0; i < CNT; ++i) {
       const int idx = tid + i * kThreads;
       if (idx >= TOT) continue;
-      const int t = idx / VPR, c = (idx % VPR) * VN;
+      const int t = idx % ROWS, c = (idx / ROWS) * VN;
       union {
         u32x4 u;
         S e[VN];
