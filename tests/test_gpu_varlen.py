@@ -137,3 +137,13 @@ def test_varlen_many_sequences_unordered_path():
     lengths[17] = 40   # one sequence of several chunks
     inp = W.generate_packed(w, lengths, device="cuda", H=1, seed=818)
     _check(inp, 16, "4100 short sequences")
+
+
+@pytest.mark.slow
+def test_varlen_1p3b_full_size():
+    """The packed workload the benchmark times, at full size: 16 sequences of a
+    seeded log-uniform length mix, 16384 tokens, 16 heads of d = 128."""
+    require_gpu()
+    w = W.get("varlen_1p3b")
+    inp = W.generate_packed(w, W.length_mix(w.B, w.L, seed=w.seed), device="cuda")
+    _check(inp, w.chunk, "varlen_1p3b full size")
