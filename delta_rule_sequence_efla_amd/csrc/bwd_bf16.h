@@ -67,7 +67,8 @@ struct BwdBf16Shape {
   static constexpr int TDPB = TQBT + DK * TBP * 2;
   static constexpr int TDPBT = TDPB + C * TBP * 2;
   static constexpr int TEB = TDPBT + C * TBP * 2;
-  static constexpr int TAIL_BYTES = TEB + C * TBP * 2;
+  static constexpr int TRED = TEB + C * TBP * 2;  // fp32 partial sums, one per thread
+  static constexpr int TAIL_BYTES = TRED + kThreads * 4;
   static constexpr int BYTES = LOOP_BYTES > TAIL_BYTES ? LOOP_BYTES : TAIL_BYTES;
 };
 
@@ -292,6 +293,11 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_bf16_kernel(
   auto f32 = [&](int off) { return reinterpret_cast<float*>(lds + off); };
   float *A0 = f32(S::TA0), *X = f32(S::TX), *Wm = f32(S::TW), *dA = f32(S::TDA);
   uint16_t *KbT = arr(S::TKBT), *QbT = arr(S::TQBT), *dPb = arr(S::TDPB), *dPbT = arr(S::TDPBT), *Eb = arr(S::TEB);
+  float* red = f32(S::TRED);
+  // the sums over one index of a C x C product run on every thread: part
+  // `prt` of column / row `cr` covers indices prt * RPP .. +RPP
+  constexpr int NPART = kThreads / C, RPP = C / NPART;
+  const int cr = tid % C, prt = tid / C;
   const int64_t qk_row = row0 * DK;
   // dP (lower, diagonal included) as bf16 rows and transposed; dT (lower) -> A0; X; K^T, Q^T
 #pragma unroll
@@ -321,12 +327,19 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_bf16_kernel(
     tile_bf<C>(dQa[i], dPb, TBP, KbT, TBP, r0, c0, li, g);
     tile_bf<C>(dKa[i], dPbT, TBP, QbT, TBP, r0, c0, li, g);
   }
-  if (tid < C) {
+  {
     float s = 0.0f;
-    for (int r = 0; r < C; ++r) s = fmaf(A0[r * CPP + tid], X[r * CPP + tid], s);
-    das[tid] = s;
+#pragma unroll
+    for (int r = prt * RPP; r < (prt + 1) * RPP; ++r) s = fmaf(A0[r * CPP + cr], X[r * CPP + cr], s);
+    red[prt * C + cr] = s;
   }
   __syncthreads();
+  if (tid < C) {
+    float s = 0.0f;
+#pragma unroll
+    for (int p = 0; p < NPART; ++p) s += red[p * C + tid];
+    das[tid] = s;
+  }
   // dX = dT diag(a), in place
   for (int i = tid; i < C * C; i += kThreads) {
     const int r = i / C, c = i % C;
@@ -359,10 +372,11 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_bf16_kernel(
   }
   __syncthreads();
   // da_i += sum_{j<i} dA_ij G_ij;  dG + dG^T with dG = diag(a) dA, as bf16
-  if (tid < C) {
-    float s = 0.0f;
-    for (int c = 0; c < tid; ++c) s = fmaf(dA[tid * CPP + c], A0[tid * CPP + c], s);
-    das[tid] += s;
+  {
+    float s = 0.0f;  // dA is zero on and above the diagonal
+#pragma unroll
+    for (int c = prt * RPP; c < (prt + 1) * RPP; ++c) s = fmaf(dA[cr * CPP + c], A0[cr * CPP + c], s);
+    red[prt * C + cr] = s;
   }
   for (int i = tid; i < C * C; i += kThreads) {
     const int r = i / C, c = i % C;
@@ -371,6 +385,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_bf16_kernel(
   __syncthreads();
   // dbeta, dlambda (lambda = G's diagonal)
   if (tid < C) {
+#pragma unroll
+    for (int p = 0; p < NPART; ++p) das[tid] += red[p * C + tid];
     float dl = 0.0f;
     if (tid < valid) {
       const float bt = to_f32(beta[row0 + int64_t(tid) * H]);
