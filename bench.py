@@ -38,6 +38,7 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 CSRC = os.path.join(ROOT, "delta_rule_sequence_efla_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "recurrence_shape_1p3b_traffic.txt")
+TRACE_FILE = os.path.join(ROOT, "profiles", "efla_fwd_shape_1p3b_kernel_trace.txt")
 
 
 def parse_args():
@@ -95,6 +96,26 @@ def read_traffic(per_launch_units: dict):
         return int(float(kv["hbm_bytes_per_launch"]))
     except (KeyError, ValueError):
         return None
+
+
+def read_trace_avg_us(kernel: str):
+    """Average duration of `kernel` in the committed rocprofv3 kernel-trace
+    summary of this benchmark, or None when missing or taken on different
+    kernel sources.  Reported beside the live event timing, which also counts
+    the launch latency each bracketing event pair adds."""
+    if not os.path.exists(TRACE_FILE):
+        return None
+    lines = open(TRACE_FILE).read().splitlines()
+    if not any(kernel_source_hash() in ln for ln in lines if ln.startswith("#")):
+        return None
+    for ln in lines:
+        parts = ln.split()
+        if parts and not ln.startswith("#") and parts[0].startswith("efla::" + kernel + "<"):
+            try:
+                return float(parts[-4])   # columns: name.. calls avg min max pct
+            except ValueError:
+                return None
+    return None
 
 
 def pct(xs, p):
@@ -390,7 +411,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": rec_kernel, "avg_us": round(rec_avg * 1e3, 2), "event_samples": len(sampled),
-                     "algorithmic_bytes": rec_bytes},
+                     "algorithmic_bytes": rec_bytes, "trace_avg_us": read_trace_avg_us(rec_kernel)},
         "stages": {"ut_transform_us": round(ut_avg * 1e3, 2), "ut_transform_bytes": ut_bytes,
                    "recurrence_us": round(rec_avg * 1e3, 2),
                    "path_us_events": round(path_avg * 1e3, 2), "path_algorithmic_bytes": path_bytes,
