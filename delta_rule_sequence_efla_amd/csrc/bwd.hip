@@ -16,6 +16,7 @@
 #include "bwd_kernels.h"
 #include "chunk_kernels.h"
 #include "launchers.h"
+#include "ut_wave.h"
 
 namespace efla {
 
@@ -71,9 +72,24 @@ hipError_t bwd_launch_impl(const T* q, const T* k, const T* v, const T* beta, co
   T* sws = reinterpret_cast<T*>(ws + lay.s);
   float* dsws = reinterpret_cast<float*>(ws + lay.ds);
   if (slots > 0) {
-    // 1. T, X, P and a of every chunk
-    hipLaunchKernelGGL((ut_transform_kernel<T, DK, C, true>), dim3(unsigned(slots)), dim3(kThreads), 0, s, k,
-                       beta, tws, H, L, NC, rule, nullptr, 0, q, xws, aws, pws);
+    // 1. T, X, P and a of every chunk: one wavefront per chunk for the bf16
+    // shapes that kernel covers (EFLA_UT_IMPL=workgroup keeps the other),
+    // else one workgroup per chunk
+    bool ut_done = false;
+    if constexpr (sizeof(T) == 2 && (DK == 32 || DK == 64 || DK == 128) && (C == 32 || C == 64)) {
+      const char* impl = getenv("EFLA_UT_IMPL");
+      if (!(impl && strcmp(impl, "workgroup") == 0)) {
+        constexpr int NW = UtWaveShape<DK, C>::WAVES;
+        const int64_t nwg = (slots + NW - 1) / NW;
+        hipLaunchKernelGGL((ut_wave_kernel<DK, C, true>), dim3(unsigned(nwg)), dim3(64 * NW), 0, s, k, beta, tws,
+                           H, L, NC, slots, rule, static_cast<const int32_t*>(nullptr), 0, nwg,
+                           static_cast<int32_t*>(nullptr), q, xws, aws, pws);
+        ut_done = true;
+      }
+    }
+    if (!ut_done)
+      hipLaunchKernelGGL((ut_transform_kernel<T, DK, C, true>), dim3(unsigned(slots)), dim3(kThreads), 0, s, k,
+                         beta, tws, H, L, NC, rule, nullptr, 0, q, xws, aws, pws);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     // 2. the state at the start of every chunk (no output)
     if (hipError_t e = chunk_states<T, DK, C>(q, k, v, tws, s0, sws, B, H, L, DV, s); e != hipSuccess) return e;

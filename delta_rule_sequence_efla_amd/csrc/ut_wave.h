@@ -55,12 +55,19 @@ __device__ __forceinline__ void mma16_f32(f32x4& acc, const f32x4& At, const f32
 // hardware executes a wavefront's LDS operations in order).
 __device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory"); }
 
-template <int DK, int C>
+// The instance for the backward pass (BWD) also writes, in fp32 per chunk
+// slot: X (C x C, zeros above the diagonal), a (C) and P = tril(Q K^T) (C x C,
+// the diagonal included), with q the queries in the layout of k.
+template <int DK, int C, bool BWD = false>
 __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict__ k,
                                                       const uint16_t* __restrict__ beta,
                                                       uint16_t* __restrict__ tws, int H, int64_t L, int NC,
                                                       int64_t nchunks, int rule, const int32_t* __restrict__ cu,
-                                                      int N, int64_t nwg_ut, int32_t* __restrict__ order) {
+                                                      int N, int64_t nwg_ut, int32_t* __restrict__ order,
+                                                      const uint16_t* __restrict__ q = nullptr,
+                                                      float* __restrict__ xout = nullptr,
+                                                      float* __restrict__ aout = nullptr,
+                                                      float* __restrict__ pout = nullptr) {
   using S = UtWaveShape<DK, C>;
   constexpr int NRT = S::NRT, NKU = S::NKU, GP = S::GP, BLK = S::BLK, TP = S::TP;
   __shared__ __align__(16) unsigned char scratch_all[S::WAVES][S::SCRATCH];
@@ -104,6 +111,38 @@ __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict
     }
   }
   const float bt = (lane < valid) ? to_f32(beta[row0 + int64_t(lane) * H]) : 0.0f;
+
+  if constexpr (BWD) {
+    // P = tril(Q K^T), diagonal included, from Q row fragments in the same
+    // per-lane order of the key dims as Kf
+    Frag<uint16_t> Qf[NRT][NKU];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      const int t = 16 * rt + li;
+      const uint16_t* src = q + (row0 + int64_t(t) * H) * DK + 8 * g;
+#pragma unroll
+      for (int ku = 0; ku < NKU; ++ku) {
+        if (t < valid) Qf[rt][ku].v = *reinterpret_cast<const bf16x8*>(src + 32 * ku);
+        else Qf[rt][ku].v = bf16x8{};
+      }
+    }
+    float* pdst = pout + id * int64_t(C) * C;
+#pragma unroll
+    for (int r = 0; r < NRT; ++r)
+#pragma unroll
+      for (int c = 0; c < NRT; ++c) {
+        f32x4 acc = zero4();
+        if (c <= r) {
+#pragma unroll
+          for (int ku = 0; ku < NKU; ++ku) mma(acc, Qf[r][ku], Kf[c][ku]);
+        }
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const int ii = 16 * r + 4 * g + qq, jj = 16 * c + li;
+          pdst[ii * C + jj] = jj <= ii ? acc[qq] : 0.0f;
+        }
+      }
+  }
 
   // ---- G: diagonal tiles and the tiles above the diagonal ----------------
   // Gd[b][qq] = G[16b + 4g + qq][16b + li];  Gu[i][m][qq] = G[16m + 4g + qq][16i + li], m < i
@@ -194,6 +233,20 @@ __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) X[i][j][qq] = -Y[qq];
     }
+
+  if constexpr (BWD) {  // X (the diagonal blocks as solved, zeros above) and a
+    float* xdst = xout + id * int64_t(C) * C;
+#pragma unroll
+    for (int i = 0; i < NRT; ++i)
+#pragma unroll
+      for (int j = 0; j < NRT; ++j)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const int r = 16 * i + 4 * g + qq, c = 16 * j + li;
+          xdst[r * C + c] = (j < i || (j == i && c <= r)) ? X[i][j][qq] : 0.0f;
+        }
+    if (lane < C) aout[id * int64_t(C) + lane] = as[lane];
+  }
 
   // ---- T = X diag(a): stage as bf16 rows, then 16-byte row stores --------
 #pragma unroll

@@ -129,13 +129,17 @@ def test_backward_full_1p3b_shape():
 
 @pytest.mark.parametrize("impl", ["fp32", "bf16"])
 def test_backward_bf16_inputs_both_chunk_kernels(impl, monkeypatch):
-    """bf16 inputs through the fp32 chunk kernel and the bf16 one, at the 1.3B
-    head configuration with a ragged last chunk and the Euler rule too."""
+    """bf16 inputs through the fp32 chunk and state kernels with the
+    one-workgroup-per-chunk UT transform, and through the bf16 kernels with the
+    one-wavefront-per-chunk one, at the 1.3B head configuration with a ragged
+    last chunk and the Euler rule too."""
     require_gpu()
     if impl == "fp32":
         monkeypatch.setenv("EFLA_BWD_IMPL", "fp32")
+        monkeypatch.setenv("EFLA_UT_IMPL", "workgroup")
     else:
         monkeypatch.delenv("EFLA_BWD_IMPL", raising=False)
+        monkeypatch.delenv("EFLA_UT_IMPL", raising=False)
     w = W.get("shape_1p3b")
     inp = W.generate(w, device="cuda", B=1, H=3, L=200, seed=930)
     _check(inp, 64, f"bf16 inputs, {impl} chunk kernel", seed=31)
