@@ -106,22 +106,26 @@ __device__ __forceinline__ void put_tile(uint16_t* X, int pitch, uint16_t* XT, i
 // elements apart, rows at or past `valid` read as zero), staged through
 // registers into bf16 LDS: load() issues 16-byte loads, store() writes the
 // tile as rows (dst [ROWS][pitch]) and, if dstT, as its transpose
-// (dstT [COLS][pitchT]).  Consecutive threads take consecutive rows of one
-// 16-byte column slice, so the transposed 2-byte stores of a wavefront land on
-// consecutive halfwords (conflict-free); the row stores, 16 rows apart by the
-// padded pitch, spread over the banks too.
+// (dstT [COLS][pitchT], pitchT even).  Each thread takes two consecutive rows
+// of one 16-byte column slice, and consecutive threads consecutive row pairs:
+// a transposed store then writes both rows' halfwords of one column as one
+// 4-byte word, and a wavefront's such stores land on consecutive words
+// (conflict-free).
 template <typename S, int ROWS, int COLS>
 struct Bf16Stager {
-  static constexpr int VN = 16 / int(sizeof(S)), VPR = COLS / VN, TOT = ROWS * VPR, CNT = cdiv(TOT, kThreads);
-  static_assert(COLS % VN == 0, "whole 16-byte vectors per row");
-  u32x4 r[CNT];
+  static constexpr int VN = 16 / int(sizeof(S)), RP = ROWS / 2, TOT = RP * (COLS / VN), CNT = cdiv(TOT, kThreads);
+  static_assert(COLS % VN == 0 && ROWS % 2 == 0, "whole 16-byte vectors per row, row pairs");
+  u32x4 r[CNT][2];
   __device__ __forceinline__ void load(const S* src, int64_t stride, int valid, int tid) {
 #pragma unroll
     for (int i = 0; i < CNT; ++i) {
       const int idx = tid + i * kThreads;
-      const int t = idx % ROWS, c = (idx / ROWS) * VN;
-      r[i] = u32x4{0u, 0u, 0u, 0u};
-      if (idx < TOT && t < valid) r[i] = *reinterpret_cast<const u32x4*>(src + t * stride + c);
+      const int t = 2 * (idx % RP), c = (idx / RP) * VN;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        r[i][h] = u32x4{0u, 0u, 0u, 0u};
+        if (idx < TOT && t + h < valid) r[i][h] = *reinterpret_cast<const u32x4*>(src + (t + h) * stride + c);
+      }
     }
   }
   __device__ __forceinline__ void store(uint16_t* dst, int pitch, uint16_t* dstT, int pitchT, int tid) const {
@@ -129,28 +133,32 @@ struct Bf16Stager {
     for (int i = 0; i < CNT; ++i) {
       const int idx = tid + i * kThreads;
       if (idx >= TOT) continue;
-      const int t = idx % ROWS, c = (idx / ROWS) * VN;
-      union {
-        u32x4 u;
-        S e[VN];
-      } x;
-      x.u = r[i];
-      uint16_t h[VN];
+      const int t = 2 * (idx % RP), c = (idx / RP) * VN;
+      uint16_t hv[2][VN];
 #pragma unroll
-      for (int e = 0; e < VN; ++e) {
-        if constexpr (sizeof(S) == 2) h[e] = x.e[e];
-        else h[e] = from_f32<uint16_t>(x.e[e]);
-      }
-      if (dst != nullptr) {
-        if constexpr (VN == 8) {
-          *reinterpret_cast<u32x4*>(dst + t * pitch + c) = *reinterpret_cast<const u32x4*>(h);
-        } else {
-          *reinterpret_cast<uint2*>(dst + t * pitch + c) = *reinterpret_cast<const uint2*>(h);
+      for (int h = 0; h < 2; ++h) {
+        union {
+          u32x4 u;
+          S e[VN];
+        } x;
+        x.u = r[i][h];
+#pragma unroll
+        for (int e = 0; e < VN; ++e) {
+          if constexpr (sizeof(S) == 2) hv[h][e] = x.e[e];
+          else hv[h][e] = from_f32<uint16_t>(x.e[e]);
+        }
+        if (dst != nullptr) {
+          if constexpr (VN == 8) {
+            *reinterpret_cast<u32x4*>(dst + (t + h) * pitch + c) = *reinterpret_cast<const u32x4*>(hv[h]);
+          } else {
+            *reinterpret_cast<uint2*>(dst + (t + h) * pitch + c) = *reinterpret_cast<const uint2*>(hv[h]);
+          }
         }
       }
       if (dstT != nullptr) {
 #pragma unroll
-        for (int e = 0; e < VN; ++e) dstT[(c + e) * pitchT + t] = h[e];
+        for (int e = 0; e < VN; ++e)
+          *reinterpret_cast<uint32_t*>(dstT + (c + e) * pitchT + t) = uint32_t(hv[0][e]) | (uint32_t(hv[1][e]) << 16);
       }
     }
   }
