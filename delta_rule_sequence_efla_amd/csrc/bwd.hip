@@ -100,7 +100,8 @@ hipError_t bwd_launch_impl(const T* q, const T* k, const T* v, const T* beta, co
   if constexpr (sizeof(T) == 2 && DK % 32 == 0 && C % 32 == 0) {
     const char* impl = getenv("EFLA_BWD_IMPL");
     if (!(impl && strcmp(impl, "fp32") == 0) && bwd_bf16_supported(DK, DV, C)) {
-      hipLaunchKernelGGL((bwd_state_bf16_kernel<DK, C>), dim3(unsigned(BH * (DV / kBwdBV))), dim3(kThreads), 0, s,
+      hipLaunchKernelGGL((bwd_state_bf16_kernel<DK, C>), dim3(unsigned(BH * (DV / kBwdBV))),
+                         dim3(BwdStateBf16Shape<DK, C>::NTH), 0, s,
                          q, k, dout, tws, pws, dsf, dsws, ds0, H, L, NC, DV, DV / kBwdBV);
       state_done = true;
     }

@@ -111,15 +111,15 @@ __device__ __forceinline__ void put_tile(uint16_t* X, int pitch, uint16_t* XT, i
 // a transposed store then writes both rows' halfwords of one column as one
 // 4-byte word, and a wavefront's such stores land on consecutive words
 // (conflict-free).
-template <typename S, int ROWS, int COLS>
+template <typename S, int ROWS, int COLS, int NTH = kThreads>  // NTH: threads of the workgroup
 struct Bf16Stager {
-  static constexpr int VN = 16 / int(sizeof(S)), RP = ROWS / 2, TOT = RP * (COLS / VN), CNT = cdiv(TOT, kThreads);
+  static constexpr int VN = 16 / int(sizeof(S)), RP = ROWS / 2, TOT = RP * (COLS / VN), CNT = cdiv(TOT, NTH);
   static_assert(COLS % VN == 0 && ROWS % 2 == 0, "whole 16-byte vectors per row, row pairs");
   u32x4 r[CNT][2];
   __device__ __forceinline__ void load(const S* src, int64_t stride, int valid, int tid) {
 #pragma unroll
     for (int i = 0; i < CNT; ++i) {
-      const int idx = tid + i * kThreads;
+      const int idx = tid + i * NTH;
       const int t = 2 * (idx % RP), c = (idx / RP) * VN;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -131,7 +131,7 @@ struct Bf16Stager {
   __device__ __forceinline__ void store(uint16_t* dst, int pitch, uint16_t* dstT, int pitchT, int tid) const {
 #pragma unroll
     for (int i = 0; i < CNT; ++i) {
-      const int idx = tid + i * kThreads;
+      const int idx = tid + i * NTH;
       if (idx >= TOT) continue;
       const int t = 2 * (idx % RP), c = (idx / RP) * VN;
       uint16_t hv[2][VN];
@@ -447,17 +447,20 @@ struct BwdStateBf16Shape {
   static constexpr int ET = DST + BV * KBP * 2;         // E^T    [BV][TBP]
   static constexpr int FT = ET + BV * TBP * 2;          // F^T    [BV][TBP]
   static constexpr int BYTES = FT + BV * TBP * 2;
-  static constexpr int NS = (DK / 16) * (BV / 16) / 4;  // dS tiles per wavefront
-  static constexpr int NE = (C / 16) * (BV / 16) / 4;   // E / F tiles per wavefront
+  // eight wavefronts where the dS and E tiles split evenly over them, else four
+  static constexpr int NDS = (DK / 16) * (BV / 16), NEF = (C / 16) * (BV / 16);
+  static constexpr int NWV = (NDS % 8 == 0 && NEF % 8 == 0) ? 8 : 4, NTH = NWV * kWave;
+  static constexpr int NS = NDS / NWV;  // dS tiles per wavefront
+  static constexpr int NE = NEF / NWV;  // E / F tiles per wavefront
 };
 
 template <int DK, int C>
-__global__ __launch_bounds__(kThreads) void bwd_state_bf16_kernel(
+__global__ __launch_bounds__((BwdStateBf16Shape<DK, C>::NTH)) void bwd_state_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ dout,
     const uint16_t* __restrict__ tws, const float* __restrict__ pws, const float* __restrict__ dsf,
     float* __restrict__ dstates, float* __restrict__ ds0, int H, int64_t L, int NC, int DV, int NVB) {
   using S = BwdStateBf16Shape<DK, C>;
-  constexpr int KBP = S::KBP, TBP = S::TBP, BV = S::BV, NS = S::NS, NE = S::NE;
+  constexpr int KBP = S::KBP, TBP = S::TBP, BV = S::BV, NS = S::NS, NE = S::NE, NWV = S::NWV, NTH = S::NTH;
   static_assert(NS >= 1 && NE >= 1, "d_k and the chunk are multiples of 32");
   __shared__ __align__(16) unsigned char lds[S::BYTES];
   auto arr = [&](int off) { return reinterpret_cast<uint16_t*>(lds + off); };
@@ -475,17 +478,17 @@ __global__ __launch_bounds__(kThreads) void bwd_state_bf16_kernel(
   f32x4 dS[NS];
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
-    const int t = w + 4 * i, d0 = 16 * (t / 2), c0 = 16 * (t % 2);
+    const int t = w + NWV * i, d0 = 16 * (t / 2), c0 = 16 * (t % 2);
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq)
       dS[i][qq] = dsf != nullptr ? dsf[(int64_t(bh) * DK + d0 + 4 * g + qq) * DV + v0 + c0 + li] : 0.0f;
   }
 
   // chunk n's operands, staged through registers one chunk ahead
-  Bf16Stager<uint16_t, C, DK> sq, sk;
-  Bf16Stager<uint16_t, C, C> st;
-  Bf16Stager<float, C, C> spp;
-  Bf16Stager<uint16_t, C, BV> sdo;
+  Bf16Stager<uint16_t, C, DK, NTH> sq, sk;
+  Bf16Stager<uint16_t, C, C, NTH> st;
+  Bf16Stager<float, C, C, NTH> spp;
+  Bf16Stager<uint16_t, C, BV, NTH> sdo;
   auto load = [&](int n) {
     const int64_t t0 = int64_t(n) * C;
     const int valid = int(sp.len - t0 < C ? sp.len - t0 : C);
@@ -504,7 +507,7 @@ __global__ __launch_bounds__(kThreads) void bwd_state_bf16_kernel(
     float* dst = dstates + (sp.slot0 + n) * DK * DV;
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      const int t = w + 4 * i, d0 = 16 * (t / 2), c0 = 16 * (t % 2);
+      const int t = w + NWV * i, d0 = 16 * (t / 2), c0 = 16 * (t % 2);
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) dst[(d0 + 4 * g + qq) * DV + v0 + c0 + li] = dS[i][qq];
       st4(dST + (c0 + li) * KBP + d0 + 4 * g, dS[i]);
@@ -519,7 +522,7 @@ __global__ __launch_bounds__(kThreads) void bwd_state_bf16_kernel(
     // E = P^T dO + K dS   ([C][BV] tiles; stored as E^T)
 #pragma unroll
     for (int i = 0; i < NE; ++i) {
-      const int t = w + 4 * i, r0 = 16 * (t / 2), c0 = 16 * (t % 2);
+      const int t = w + NWV * i, r0 = 16 * (t / 2), c0 = 16 * (t % 2);
       f32x4 acc = zero4();
       tile_bf<C>(acc, PbT, TBP, dOT, TBP, r0, c0, li, g);
       tile_bf<DK>(acc, Kb, KBP, dST, KBP, r0, c0, li, g);
@@ -529,7 +532,7 @@ __global__ __launch_bounds__(kThreads) void bwd_state_bf16_kernel(
     // F = T^T E   (stored as F^T)
 #pragma unroll
     for (int i = 0; i < NE; ++i) {
-      const int t = w + 4 * i, r0 = 16 * (t / 2), c0 = 16 * (t % 2);
+      const int t = w + NWV * i, r0 = 16 * (t / 2), c0 = 16 * (t % 2);
       f32x4 acc = zero4();
       tile_bf<C>(acc, TbT, TBP, ET, TBP, r0, c0, li, g);
       st4(FT + (c0 + li) * TBP + r0 + 4 * g, acc);
@@ -538,7 +541,7 @@ __global__ __launch_bounds__(kThreads) void bwd_state_bf16_kernel(
     // dS += Q^T dO - K^T F
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      const int t = w + 4 * i, d0 = 16 * (t / 2), c0 = 16 * (t % 2);
+      const int t = w + NWV * i, d0 = 16 * (t / 2), c0 = 16 * (t % 2);
       f32x4 m = zero4();
       tile_bf<C>(dS[i], QbT, TBP, dOT, TBP, d0, c0, li, g);
       tile_bf<C>(m, KbT, TBP, FT, TBP, d0, c0, li, g);
@@ -548,7 +551,7 @@ __global__ __launch_bounds__(kThreads) void bwd_state_bf16_kernel(
   if (ds0 != nullptr) {
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      const int t = w + 4 * i, d0 = 16 * (t / 2), c0 = 16 * (t % 2);
+      const int t = w + NWV * i, d0 = 16 * (t / 2), c0 = 16 * (t % 2);
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) ds0[(int64_t(bh) * DK + d0 + 4 * g + qq) * DV + v0 + c0 + li] = dS[i][qq];
     }
