@@ -116,7 +116,8 @@ hipError_t bwd_launch_impl(const T* q, const T* k, const T* v, const T* beta, co
   if constexpr (sizeof(T) == 2 && DK % 32 == 0 && C % 32 == 0) {
     const char* impl = getenv("EFLA_BWD_IMPL");
     if (!(impl && strcmp(impl, "fp32") == 0) && bwd_bf16_supported(DK, DV, C)) {
-      hipLaunchKernelGGL((bwd_chunk_bf16_kernel<DK, C>), dim3(unsigned(slots)), dim3(kThreads), 0, s, q, k, v, beta,
+      hipLaunchKernelGGL((bwd_chunk_bf16_kernel<DK, C>), dim3(unsigned(slots)), dim3(BwdBf16Shape<DK, C>::NTH), 0, s,
+                         q, k, v, beta,
                          dout, tws, xws, aws, pws, sws, dsws, dq, dk, dv, dbeta, H, L, NC, DV, rule);
       return hipGetLastError();
     }

@@ -67,8 +67,14 @@ struct BwdBf16Shape {
   static constexpr int TDPB = TQBT + DK * TBP * 2;
   static constexpr int TDPBT = TDPB + C * TBP * 2;
   static constexpr int TEB = TDPBT + C * TBP * 2;
+  // eight wavefronts where every tile loop splits evenly over them, else four
+  static constexpr int NWV = ((C / 16) * (DK / 16) % 8 == 0 && (C / 16) * (C / 16) % 8 == 0 &&
+                              2 * (C / 16) * (BV / 16) % 8 == 0) ? 8 : 4;
+  static constexpr int NTH = NWV * kWave;
+  static constexpr int NQ = (C / 16) * (DK / 16) / NWV;  // dQ / dK tiles per wavefront
+  static constexpr int NP = (C / 16) * (C / 16) / NWV;   // dP / dT tiles per wavefront
   static constexpr int TRED = TEB + C * TBP * 2;  // fp32 partial sums, one per thread
-  static constexpr int TAIL_BYTES = TRED + kThreads * 4;
+  static constexpr int TAIL_BYTES = TRED + NTH * 4;
   static constexpr int BYTES = LOOP_BYTES > TAIL_BYTES ? LOOP_BYTES : TAIL_BYTES;
 };
 
@@ -165,7 +171,7 @@ struct Bf16Stager {
 };
 
 template <int DK, int C>
-__global__ __launch_bounds__(kThreads) void bwd_chunk_bf16_kernel(
+__global__ __launch_bounds__((BwdBf16Shape<DK, C>::NTH)) void bwd_chunk_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ beta, const uint16_t* __restrict__ dout, const uint16_t* __restrict__ tws,
     const float* __restrict__ xws, const float* __restrict__ aws, const float* __restrict__ pws,
@@ -175,7 +181,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_bf16_kernel(
   using S = BwdBf16Shape<DK, C>;
   using F = BwdChunkShape<uint16_t, DK, C>;
   constexpr int KBP = S::KBP, TBP = S::TBP, VBP = S::VBP, BV = S::BV;
-  constexpr int NQ = F::NQ, NP = F::NP, NCQ = DK / 16, NCP = C / 16, NRT = C / 16;
+  constexpr int NQ = S::NQ, NP = S::NP, NCQ = DK / 16, NCP = C / 16, NRT = C / 16;
+  constexpr int NWV = S::NWV, NTH = S::NTH;
   static_assert(F::CP == C && F::DKP == DK, "bf16 kernel: DK and C are multiples of 32");
   __shared__ __align__(16) unsigned char lds[S::BYTES];
   __shared__ float as[C], das[C], dls[C];
@@ -197,12 +204,12 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_bf16_kernel(
 
   // chunk operands: K, T, T^T, P^T as bf16 for the loop; Q and K also stay in
   // registers, for their transposes in the tail
-  Bf16Stager<uint16_t, C, DK> sq, sk;
+  Bf16Stager<uint16_t, C, DK, NTH> sq, sk;
   sq.load(q + row0 * DK, qk_stride, valid, tid);
   sk.load(k + row0 * DK, qk_stride, valid, tid);
   {
-    Bf16Stager<uint16_t, C, C> st;
-    Bf16Stager<float, C, C> spp;
+    Bf16Stager<uint16_t, C, C, NTH> st;
+    Bf16Stager<float, C, C, NTH> spp;
     st.load(tws + slot * C * C, C, C, tid);
     spp.load(pws + slot * C * C, C, C, tid);
     sk.store(Kb, KBP, nullptr, 0, tid);
@@ -220,9 +227,9 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_bf16_kernel(
   const uint16_t* st = states + slot * DK * DV;
   const float* dst = dstates + slot * DK * DV;
   // one value block's operands, staged through registers one block ahead
-  Bf16Stager<uint16_t, DK, BV> ss;
-  Bf16Stager<float, DK, BV> sds;
-  Bf16Stager<uint16_t, C, BV> sv, sdo;
+  Bf16Stager<uint16_t, DK, BV, NTH> ss;
+  Bf16Stager<float, DK, BV, NTH> sds;
+  Bf16Stager<uint16_t, C, BV, NTH> sv, sdo;
   auto load_block = [&](int v0) {
     ss.load(st + v0, DV, DK, tid);
     sds.load(dst + v0, DV, DK, tid);
@@ -239,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_bf16_kernel(
     if (v0 + BV < DV) load_block(v0 + BV);  // in flight during this block
     __syncthreads();
     // D = V - K S,  dU = P^T dO + K dS'   (tiles of [C][BV])
-    for (int t = w; t < 2 * NRT * (BV / 16); t += 4) {
+    for (int t = w; t < 2 * NRT * (BV / 16); t += NWV) {
       const int tt = t % (NRT * (BV / 16)), r0 = 16 * (tt / (BV / 16)), c0 = 16 * (tt % (BV / 16));
       f32x4 acc = zero4();
       if (t < NRT * (BV / 16)) {
@@ -255,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_bf16_kernel(
     }
     __syncthreads();
     // U = T D,  dD = T^T dU (= dV)
-    for (int t = w; t < 2 * NRT * (BV / 16); t += 4) {
+    for (int t = w; t < 2 * NRT * (BV / 16); t += NWV) {
       const int tt = t % (NRT * (BV / 16)), r0 = 16 * (tt / (BV / 16)), c0 = 16 * (tt % (BV / 16));
       f32x4 acc = zero4();
       if (t < NRT * (BV / 16)) {
@@ -275,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_bf16_kernel(
     // dQ += dO S^T;  dK += U dS'^T - dD S^T;  dP += dO U^T;  dT += dU D^T   (K = BV)
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
-      const int t = w + 4 * i, r0 = 16 * (t / NCQ), c0 = 16 * (t % NCQ);
+      const int t = w + NWV * i, r0 = 16 * (t / NCQ), c0 = 16 * (t % NCQ);
       tile_bf<BV>(dQa[i], dOv, VBP, Sv, VBP, r0, c0, li, g);
       tile_bf<BV>(dKa[i], Uv, VBP, dSv, VBP, r0, c0, li, g);
       f32x4 m = zero4();
@@ -284,7 +291,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_bf16_kernel(
     }
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      const int t = w + 4 * i, r0 = 16 * (t / NCP), c0 = 16 * (t % NCP);
+      const int t = w + NWV * i, r0 = 16 * (t / NCP), c0 = 16 * (t % NCP);
       tile_bf<BV>(dPa[i], dOv, VBP, Uv, VBP, r0, c0, li, g);
       tile_bf<BV>(dTa[i], dUv, VBP, Dv, VBP, r0, c0, li, g);
     }
@@ -304,13 +311,13 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_bf16_kernel(
   float* red = f32(S::TRED);
   // the sums over one index of a C x C product run on every thread: part
   // `prt` of column / row `cr` covers indices prt * RPP .. +RPP
-  constexpr int NPART = kThreads / C, RPP = C / NPART;
+  constexpr int NPART = NTH / C, RPP = C / NPART;
   const int cr = tid % C, prt = tid / C;
   const int64_t qk_row = row0 * DK;
   // dP (lower, diagonal included) as bf16 rows and transposed; dT (lower) -> A0; X; K^T, Q^T
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
-    const int t = w + 4 * i, r0 = 16 * (t / NCP), c0 = 16 * (t % NCP);
+    const int t = w + NWV * i, r0 = 16 * (t / NCP), c0 = 16 * (t % NCP);
     f32x4 p;
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
@@ -321,7 +328,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_bf16_kernel(
     put_tile(dPb, TBP, dPbT, TBP, p, r0, c0, li, g);
   }
   {
-    F32Stager<float, C, C> sx;
+    F32Stager<float, C, C, NTH> sx;
     sx.load(xws + slot * C * C, C, C, tid);
     sx.store(X, CPP, tid);
   }
@@ -331,7 +338,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_bf16_kernel(
   // dQ += dP K;  dK += dP^T Q;  da_j = sum_i dT_ij X_ij
 #pragma unroll
   for (int i = 0; i < NQ; ++i) {
-    const int t = w + 4 * i, r0 = 16 * (t / NCQ), c0 = 16 * (t % NCQ);
+    const int t = w + NWV * i, r0 = 16 * (t / NCQ), c0 = 16 * (t % NCQ);
     tile_bf<C>(dQa[i], dPb, TBP, KbT, TBP, r0, c0, li, g);
     tile_bf<C>(dKa[i], dPbT, TBP, QbT, TBP, r0, c0, li, g);
   }
@@ -349,7 +356,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_bf16_kernel(
     das[tid] = s;
   }
   // dX = dT diag(a), in place
-  for (int i = tid; i < C * C; i += kThreads) {
+  for (int i = tid; i < C * C; i += NTH) {
     const int r = i / C, c = i % C;
     A0[r * CPP + c] *= as[c];
   }
@@ -357,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_bf16_kernel(
   // W = X^T dX
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
-    const int t = w + 4 * i, r0 = 16 * (t / NCP), c0 = 16 * (t % NCP);
+    const int t = w + NWV * i, r0 = 16 * (t / NCP), c0 = 16 * (t % NCP);
     f32x4 acc = zero4();
     tile_mma16<true, false>(acc, X, CPP, A0, CPP, r0, c0, C, li, g);
 #pragma unroll
@@ -367,7 +374,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_bf16_kernel(
   // dA = -W X^T (strictly lower);  G = K K^T -> A0
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
-    const int t = w + 4 * i, r0 = 16 * (t / NCP), c0 = 16 * (t % NCP);
+    const int t = w + NWV * i, r0 = 16 * (t / NCP), c0 = 16 * (t % NCP);
     f32x4 acc = zero4(), gg = zero4();
     tile_mma16<false, true>(acc, Wm, CPP, X, CPP, r0, c0, C, li, g);
     tile_bf<DK>(gg, Kb, KBP, Kb, KBP, r0, c0, li, g);
@@ -386,7 +393,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_bf16_kernel(
     for (int c = prt * RPP; c < (prt + 1) * RPP; ++c) s = fmaf(dA[cr * CPP + c], A0[cr * CPP + c], s);
     red[prt * C + cr] = s;
   }
-  for (int i = tid; i < C * C; i += kThreads) {
+  for (int i = tid; i < C * C; i += NTH) {
     const int r = i / C, c = i % C;
     Eb[r * TBP + c] = from_f32<uint16_t>(as[r] * dA[r * CPP + c] + as[c] * dA[c * CPP + r]);
   }
@@ -409,7 +416,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_bf16_kernel(
   // dK += (dG + dG^T) K + 2 diag(dlambda) K;  write dq, dk
 #pragma unroll
   for (int i = 0; i < NQ; ++i) {
-    const int t = w + 4 * i, r0 = 16 * (t / NCQ), c0 = 16 * (t % NCQ);
+    const int t = w + NWV * i, r0 = 16 * (t / NCQ), c0 = 16 * (t % NCQ);
     tile_bf<C>(dKa[i], Eb, TBP, KbT, TBP, r0, c0, li, g);
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {

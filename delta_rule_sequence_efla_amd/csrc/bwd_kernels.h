@@ -88,14 +88,14 @@ __device__ __forceinline__ void efla_alpha_grad(float beta, float lam, int rule,
 // any is waited on: load() issues 16-byte loads into registers (rows at or
 // past `valid` read as zero), store() widens them into dst (pitch in floats).
 // COLS * sizeof(T) must be a multiple of 16 and rows 16-byte aligned.
-template <typename T, int ROWS, int COLS>
+template <typename T, int ROWS, int COLS, int NTH = kThreads>  // NTH: threads of the workgroup
 struct F32Stager {
-  static constexpr int VN = 16 / int(sizeof(T)), VPR = COLS / VN, TOT = ROWS * VPR, CNT = cdiv(TOT, kThreads);
+  static constexpr int VN = 16 / int(sizeof(T)), VPR = COLS / VN, TOT = ROWS * VPR, CNT = cdiv(TOT, NTH);
   u32x4 r[CNT];
   __device__ __forceinline__ void load(const T* src, int64_t stride, int valid, int tid) {
 #pragma unroll
     for (int i = 0; i < CNT; ++i) {
-      const int idx = tid + i * kThreads;
+      const int idx = tid + i * NTH;
       const int t = idx / VPR, c = (idx % VPR) * VN;
       r[i] = u32x4{0u, 0u, 0u, 0u};
       if (idx < TOT && t < valid) r[i] = *reinterpret_cast<const u32x4*>(src + t * stride + c);
@@ -104,7 +104,7 @@ struct F32Stager {
   __device__ __forceinline__ void store(float* dst, int pitch, int tid) const {
 #pragma unroll
     for (int i = 0; i < CNT; ++i) {
-      const int idx = tid + i * kThreads;
+      const int idx = tid + i * NTH;
       if (idx < TOT) {
         const int t = idx / VPR, c = (idx % VPR) * VN;
         union {
