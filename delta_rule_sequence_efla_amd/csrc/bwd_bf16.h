@@ -434,8 +434,9 @@ __global__ __launch_bounds__((BwdBf16Shape<DK, C>::NTH)) void bwd_chunk_bf16_ker
 // The reverse sequential pass for bf16 inputs: one workgroup per (b, h, 32
 // value columns), for chunk n = last .. 0:
 //     dstates[n] = dS;   E = P^T dO + K dS;   F = T^T E;   dS += Q^T dO - K^T F
-// as in bwd_state_kernel, with dS (d_k x 32) in fp32 registers (each wavefront
-// owns d_k / 32 of its 16x16 tiles) and every product on bf16 matrix cores:
+// as in bwd_state_kernel, with dS (d_k x 32) in fp32 registers (its 16x16
+// tiles spread over the workgroup's four or eight wavefronts) and every
+// product on bf16 matrix cores:
 // dS, E and F enter the products as bf16 copies (dS^T, E^T, F^T in LDS), Q, K,
 // T and P as bf16 in the layouts the products read (K rows; K^T, Q^T, T^T,
 // P^T, dO^T).  The next chunk's operands are loaded while this one computes.
