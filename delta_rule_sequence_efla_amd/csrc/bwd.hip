@@ -102,7 +102,7 @@ hipError_t bwd_launch_impl(const T* q, const T* k, const T* v, const T* beta, co
     if (!(impl && strcmp(impl, "fp32") == 0) && bwd_bf16_supported(DK, DV, C)) {
       hipLaunchKernelGGL((bwd_state_bf16_kernel<DK, C>), dim3(unsigned(BH * (DV / kBwdBV))),
                          dim3(BwdStateBf16Shape<DK, C>::NTH), 0, s,
-                         q, k, dout, tws, pws, dsf, dsws, ds0, H, L, NC, DV, DV / kBwdBV);
+                         q, k, dout, tws, pws, dsf, dsws, ds0, H, L, NC, DV, DV / kBwdBV, BH % 8 == 0 ? 1 : 0);
       state_done = true;
     }
   }

@@ -466,7 +466,7 @@ template <int DK, int C>
 __global__ __launch_bounds__((BwdStateBf16Shape<DK, C>::NTH)) void bwd_state_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ dout,
     const uint16_t* __restrict__ tws, const float* __restrict__ pws, const float* __restrict__ dsf,
-    float* __restrict__ dstates, float* __restrict__ ds0, int H, int64_t L, int NC, int DV, int NVB) {
+    float* __restrict__ dstates, float* __restrict__ ds0, int H, int64_t L, int NC, int DV, int NVB, int remap) {
   using S = BwdStateBf16Shape<DK, C>;
   constexpr int KBP = S::KBP, TBP = S::TBP, BV = S::BV, NS = S::NS, NE = S::NE, NWV = S::NWV, NTH = S::NTH;
   static_assert(NS >= 1 && NE >= 1, "d_k and the chunk are multiples of 32");
@@ -475,7 +475,19 @@ __global__ __launch_bounds__((BwdStateBf16Shape<DK, C>::NTH)) void bwd_state_bf1
   uint16_t *Kb = arr(S::KB), *KbT = arr(S::KBT), *QbT = arr(S::QBT), *TbT = arr(S::TBT), *PbT = arr(S::PBT);
   uint16_t *dOT = arr(S::DOT), *dST = arr(S::DST), *ET = arr(S::ET), *FT = arr(S::FT);
 
-  const int x = blockIdx.x, bh = x / NVB, vb = x % NVB;
+  // Workgroup -> (b, h, value block).  With remap, the value blocks of one
+  // (b, h), which read the same Q, K, T and P, get the same blockIdx % 8, i.e.
+  // the same XCD and L2.
+  const int x = blockIdx.x;
+  int bh, vb;
+  if (remap) {
+    const int slot = x >> 3;
+    vb = slot % NVB;
+    bh = (slot / NVB) * 8 + (x & 7);
+  } else {
+    bh = x / NVB;
+    vb = x % NVB;
+  }
   const int64_t h = bh % H;
   const SeqSpan sp = seq_span<C>(nullptr, bh / H, h, H, L, NC);
   const int v0 = BV * vb;
