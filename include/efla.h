@@ -176,10 +176,15 @@ efla_status efla_chunk_recurrence(const void *q, const void *k, const void *v,
  * it writes dq, dk [B, L, H, d_k], dv [B, L, H, d_v], dbeta [B, L, H] (dtype)
  * and ds0 [B, H, d_k, d_v] float32 = dLoss / ds0 (NULL: not written).  dbeta
  * and dk include the paths through alpha(beta, lambda) and lambda = ||k||^2.
- * Arithmetic is float32 throughout (bf16 inputs and d_o are widened exactly;
- * gradients are rounded to dtype on output).  The workspace (size below) holds
- * per chunk the UT-transform quantities and the states the pass recomputes;
- * it is scratch and may be reused once the call has completed on the stream.
+ * float32 inputs: float32 arithmetic throughout.  bf16 inputs (d_k, chunk
+ * and d_v multiples of 32): products on bf16 matrix cores with float32
+ * accumulation, each intermediate operand (P, the states, dS, the per-chunk
+ * products) rounded to bf16 once, the UT-transform part and the coefficient
+ * gradients in float32 (other bf16 shapes: float32 arithmetic on the widened
+ * values); gradients are rounded to dtype on output.  The
+ * workspace (size below) holds per chunk the UT-transform quantities, the
+ * states the pass recomputes and their gradients; it is scratch and may be
+ * reused once the call has completed on the stream.
  * q, k, v, d_o and the workspace must be 16-byte aligned.
  */
 size_t efla_chunk_bwd_workspace_size(int B, int H, int64_t L, int d_k, int d_v, int chunk,

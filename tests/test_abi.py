@@ -176,6 +176,9 @@ def test_backward_workspace_size_and_validation():
     slots = 4 * 16 * 64
     want = slots * (64 * 64 * 2 + 2 * 64 * 64 * 4 + 64 * 4 + 128 * 128 * 2 + 128 * 128 * 4)
     assert f(4, 16, 4096, 128, 128, 64, torch.bfloat16) == want
+    # float32: T and the states in float32
+    want32 = slots * (64 * 64 * 4 + 2 * 64 * 64 * 4 + 64 * 4 + 128 * 128 * 4 + 128 * 128 * 4)
+    assert f(4, 16, 4096, 128, 128, 64, torch.float32) == want32
     L = efla.lib()
     nul, fake = None, 4096
 
