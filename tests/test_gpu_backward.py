@@ -68,6 +68,18 @@ def test_backward_matches_oracle(dt, dk, dv, chunk, L):
     _check(inp, chunk, f"{dt} dk{dk} dv{dv} C{chunk} L{L}", seed=L)
 
 
+@pytest.mark.parametrize("dk,dv,chunk,L,B,H", [(128, 64, 32, 97, 2, 4), (32, 128, 64, 200, 1, 8),
+                                                (64, 32, 64, 65, 4, 4)], ids=lambda x: str(x))
+def test_backward_bf16_grouped_state_pass(dk, dv, chunk, L, B, H):
+    """bf16 matrix-core kernels with B*H a multiple of 8, where the state pass
+    numbers its workgroups so that the value blocks of one (b, h) share an XCD,
+    at d_k / chunk pairs the other cases leave out, with ragged last chunks."""
+    require_gpu()
+    w = W.get("shape_340m", dtype="bf16", dk=dk, dv=dv, chunk=chunk)
+    inp = W.generate(w, device="cuda", B=B, L=L, H=H, seed=940 + dk + dv + chunk + L)
+    _check(inp, chunk, f"bf16 dk{dk} dv{dv} C{chunk} L{L} B{B} H{H}", seed=L + 1)
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_backward_euler_rule(dt):
     require_gpu()
