@@ -67,9 +67,12 @@ struct BwdBf16Shape {
   static constexpr int TDPB = TQBT + DK * TBP * 2;
   static constexpr int TDPBT = TDPB + C * TBP * 2;
   static constexpr int TEB = TDPBT + C * TBP * 2;
-  // eight wavefronts where every tile loop splits evenly over them, else four
-  static constexpr int NWV = ((C / 16) * (DK / 16) % 8 == 0 && (C / 16) * (C / 16) % 8 == 0 &&
-                              2 * (C / 16) * (BV / 16) % 8 == 0) ? 8 : 4;
+  // sixteen, eight or four wavefronts: the most over which every tile loop
+  // splits evenly
+  static constexpr bool splits(int n) {
+    return (C / 16) * (DK / 16) % n == 0 && (C / 16) * (C / 16) % n == 0 && 2 * (C / 16) * (BV / 16) % n == 0;
+  }
+  static constexpr int NWV = splits(16) ? 16 : splits(8) ? 8 : 4;
   static constexpr int NTH = NWV * kWave;
   static constexpr int NQ = (C / 16) * (DK / 16) / NWV;  // dQ / dK tiles per wavefront
   static constexpr int NP = (C / 16) * (C / 16) / NWV;   // dP / dT tiles per wavefront
@@ -108,7 +111,7 @@ __device__ __forceinline__ void put_tile(uint16_t* X, int pitch, uint16_t* XT, i
   if (XT != nullptr) st4(XT + (c0 + li) * pitchT + r0 + 4 * g, a);
 }
 
-// A ROWS x COLS tile of a bf16 or fp32 array in global memory (rows `stride`
+// A ROWS x COLS tile of a bf16 or fp32 array in global memory or LDS (rows `stride`
 // elements apart, rows at or past `valid` read as zero), staged through
 // registers into bf16 LDS: load() issues 16-byte loads, store() writes the
 // tile as rows (dst [ROWS][pitch]) and, if dstT, as its transpose
@@ -170,6 +173,102 @@ struct Bf16Stager {
   }
 };
 
+// One value block's four operands staged through one set of registers: S
+// (bf16 [DK][BV]), dS' (fp32 [DK][BV]), V and dO (bf16 [C][BV]), their
+// 16-byte units numbered in that order and dealt to the workgroup's threads,
+// so a thread holds cdiv(units, NTH) row pairs instead of one per operand
+// (with 32 value columns every operand boundary falls on a whole wavefront).
+// Each unit is two consecutive rows of one 16-byte column slice, written as
+// in Bf16Stager: rows, and transposed as 4-byte words of the two rows.
+template <int DK, int C, int BV, int NTH>
+struct BlockStager {
+  static constexpr int U0 = (DK / 2) * (BV / 8), U1 = (DK / 2) * (BV / 4), U2 = (C / 2) * (BV / 8);
+  static constexpr int TOT = U0 + U1 + 2 * U2, CNT = cdiv(TOT, NTH);
+  u32x4 r[CNT][2];
+  // operand of unit idx, and its index within that operand
+  __device__ __forceinline__ static int which(int idx, int& j) {
+    if (idx < U0) { j = idx; return 0; }
+    if (idx < U0 + U1) { j = idx - U0; return 1; }
+    if (idx < U0 + U1 + U2) { j = idx - U0 - U1; return 2; }
+    j = idx - U0 - U1 - U2;
+    return 3;
+  }
+  __device__ __forceinline__ void load(const uint16_t* st, const float* dst, const uint16_t* vv, const uint16_t* dov,
+                                       int DV, int64_t v_stride, int valid, int tid) {
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) {
+      const int idx = tid + i * NTH;
+      r[i][0] = r[i][1] = u32x4{0u, 0u, 0u, 0u};
+      if (idx >= TOT) continue;
+      int j;
+      const int op = which(idx, j);
+      if (op == 0) {  // S rows: DK rows, stride DV
+        const int t = 2 * (j % (DK / 2)), c = (j / (DK / 2)) * 8;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) r[i][h] = *reinterpret_cast<const u32x4*>(st + (t + h) * int64_t(DV) + c);
+      } else if (op == 1) {  // dS' rows (fp32): DK rows, stride DV
+        const int t = 2 * (j % (DK / 2)), c = (j / (DK / 2)) * 4;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) r[i][h] = *reinterpret_cast<const u32x4*>(dst + (t + h) * int64_t(DV) + c);
+      } else {  // V or dO: C token rows, rows at or past `valid` read as zero
+        const uint16_t* src = op == 2 ? vv : dov;
+        const int t = 2 * (j % (C / 2)), c = (j / (C / 2)) * 8;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          if (t + h < valid) r[i][h] = *reinterpret_cast<const u32x4*>(src + (t + h) * v_stride + c);
+      }
+    }
+  }
+  // Sv [DK][VBP] + SvT [BV][KBP]; dSv + dSvT likewise; Vv [C][VBP]; dOv [C][VBP] + dOvT [BV][TBP]
+  __device__ __forceinline__ void store(uint16_t* Sv, uint16_t* SvT, uint16_t* dSv, uint16_t* dSvT, uint16_t* Vv,
+                                        uint16_t* dOv, uint16_t* dOvT, int VBP, int KBP, int TBP, int tid) const {
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) {
+      const int idx = tid + i * NTH;
+      if (idx >= TOT) continue;
+      int j;
+      const int op = which(idx, j);
+      if (op == 1) {  // fp32 -> bf16, four columns
+        const int t = 2 * (j % (DK / 2)), c = (j / (DK / 2)) * 4;
+        uint16_t hv[2][4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          union {
+            u32x4 u;
+            float e[4];
+          } x;
+          x.u = r[i][h];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) hv[h][e] = from_f32<uint16_t>(x.e[e]);
+          *reinterpret_cast<uint2*>(dSv + (t + h) * VBP + c) = *reinterpret_cast<const uint2*>(hv[h]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          *reinterpret_cast<uint32_t*>(dSvT + (c + e) * KBP + t) = uint32_t(hv[0][e]) | (uint32_t(hv[1][e]) << 16);
+      } else {  // bf16, eight columns
+        const int rows = op == 0 ? DK : C;
+        const int t = 2 * (j % (rows / 2)), c = (j / (rows / 2)) * 8;
+        uint16_t* X = op == 0 ? Sv : op == 2 ? Vv : dOv;
+        uint16_t* XT = op == 0 ? SvT : op == 2 ? nullptr : dOvT;
+        const int pitchT = op == 0 ? KBP : TBP;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) *reinterpret_cast<u32x4*>(X + (t + h) * VBP + c) = r[i][h];
+        if (XT != nullptr) {
+          union {
+            u32x4 u;
+            uint16_t e[8];
+          } x0, x1;
+          x0.u = r[i][0];
+          x1.u = r[i][1];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            *reinterpret_cast<uint32_t*>(XT + (c + e) * pitchT + t) = uint32_t(x0.e[e]) | (uint32_t(x1.e[e]) << 16);
+        }
+      }
+    }
+  }
+};
+
 template <int DK, int C>
 __global__ __launch_bounds__((BwdBf16Shape<DK, C>::NTH)) void bwd_chunk_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -202,12 +301,11 @@ __global__ __launch_bounds__((BwdBf16Shape<DK, C>::NTH)) void bwd_chunk_bf16_ker
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), li = lane & 15, g = lane >> 4;
   const int64_t qk_stride = int64_t(H) * DK, v_stride = int64_t(H) * DV;
 
-  // chunk operands: K, T, T^T, P^T as bf16 for the loop; Q and K also stay in
-  // registers, for their transposes in the tail
-  Bf16Stager<uint16_t, C, DK, NTH> sq, sk;
-  sq.load(q + row0 * DK, qk_stride, valid, tid);
-  sk.load(k + row0 * DK, qk_stride, valid, tid);
+  // chunk operands: K, T, T^T, P^T as bf16 for the loop (the tail loads Q
+  // and transposes K from these rows)
   {
+    Bf16Stager<uint16_t, C, DK, NTH> sk;
+    sk.load(k + row0 * DK, qk_stride, valid, tid);
     Bf16Stager<uint16_t, C, C, NTH> st;
     Bf16Stager<float, C, C, NTH> spp;
     st.load(tws + slot * C * C, C, C, tid);
@@ -227,22 +325,14 @@ __global__ __launch_bounds__((BwdBf16Shape<DK, C>::NTH)) void bwd_chunk_bf16_ker
   const uint16_t* st = states + slot * DK * DV;
   const float* dst = dstates + slot * DK * DV;
   // one value block's operands, staged through registers one block ahead
-  Bf16Stager<uint16_t, DK, BV, NTH> ss;
-  Bf16Stager<float, DK, BV, NTH> sds;
-  Bf16Stager<uint16_t, C, BV, NTH> sv, sdo;
+  BlockStager<DK, C, BV, NTH> sb;
   auto load_block = [&](int v0) {
-    ss.load(st + v0, DV, DK, tid);
-    sds.load(dst + v0, DV, DK, tid);
-    sv.load(v + row0 * DV + v0, v_stride, valid, tid);
-    sdo.load(dout + row0 * DV + v0, v_stride, valid, tid);
+    sb.load(st + v0, dst + v0, v + row0 * DV + v0, dout + row0 * DV + v0, DV, v_stride, valid, tid);
   };
   load_block(0);
   for (int v0 = 0; v0 < DV; v0 += BV) {
     __syncthreads();  // the previous block's buffers are free (and the chunk operands are in place)
-    ss.store(Sv, VBP, SvT, KBP, tid);
-    sds.store(dSv, VBP, dSvT, KBP, tid);
-    sv.store(Vv, VBP, nullptr, 0, tid);
-    sdo.store(dOv, VBP, dOvT, TBP, tid);
+    sb.store(Sv, SvT, dSv, dSvT, Vv, dOv, dOvT, VBP, KBP, TBP, tid);
     if (v0 + BV < DV) load_block(v0 + BV);  // in flight during this block
     __syncthreads();
     // D = V - K S,  dU = P^T dO + K dS'   (tiles of [C][BV])
@@ -328,12 +418,17 @@ __global__ __launch_bounds__((BwdBf16Shape<DK, C>::NTH)) void bwd_chunk_bf16_ker
     put_tile(dPb, TBP, dPbT, TBP, p, r0, c0, li, g);
   }
   {
+    // X and Q from global memory (their latencies overlap); K^T from K's rows,
+    // which stay in LDS
     F32Stager<float, C, C, NTH> sx;
+    Bf16Stager<uint16_t, C, DK, NTH> sq, sk;
     sx.load(xws + slot * C * C, C, C, tid);
+    sq.load(q + row0 * DK, qk_stride, valid, tid);
+    sk.load(Kb, KBP, C, tid);
+    sk.store(nullptr, 0, KbT, TBP, tid);
     sx.store(X, CPP, tid);
+    sq.store(nullptr, 0, QbT, TBP, tid);
   }
-  sk.store(nullptr, 0, KbT, TBP, tid);
-  sq.store(nullptr, 0, QbT, TBP, tid);
   __syncthreads();
   // dQ += dP K;  dK += dP^T Q;  da_j = sum_i dT_ij X_ij
 #pragma unroll
