@@ -530,7 +530,7 @@ __global__ __launch_bounds__((BwdBf16Shape<DK, C>::NTH)) void bwd_chunk_bf16_ker
 // value columns), for chunk n = last .. 0:
 //     dstates[n] = dS;   E = P^T dO + K dS;   F = T^T E;   dS += Q^T dO - K^T F
 // as in bwd_state_kernel, with dS (d_k x 32) in fp32 registers (its 16x16
-// tiles spread over the workgroup's four or eight wavefronts) and every
+// tiles spread over the workgroup's wavefronts) and every
 // product on bf16 matrix cores:
 // dS, E and F enter the products as bf16 copies (dS^T, E^T, F^T in LDS), Q, K,
 // T and P as bf16 in the layouts the products read (K rows; K^T, Q^T, T^T,
@@ -550,11 +550,105 @@ struct BwdStateBf16Shape {
   static constexpr int ET = DST + BV * KBP * 2;         // E^T    [BV][TBP]
   static constexpr int FT = ET + BV * TBP * 2;          // F^T    [BV][TBP]
   static constexpr int BYTES = FT + BV * TBP * 2;
-  // eight wavefronts where the dS and E tiles split evenly over them, else four
+  // sixteen wavefronts where the dS tiles split over them (the E and F tiles
+  // then take the first NEF), else eight where dS and E split evenly, else four
   static constexpr int NDS = (DK / 16) * (BV / 16), NEF = (C / 16) * (BV / 16);
-  static constexpr int NWV = (NDS % 8 == 0 && NEF % 8 == 0) ? 8 : 4, NTH = NWV * kWave;
+  static constexpr int NWV = NDS % 16 == 0 ? 16 : (NDS % 8 == 0 && NEF % 8 == 0) ? 8 : 4, NTH = NWV * kWave;
   static constexpr int NS = NDS / NWV;  // dS tiles per wavefront
-  static constexpr int NE = NEF / NWV;  // E / F tiles per wavefront
+};
+
+// The chunk operands of the reverse pass staged through one set of
+// registers: K (rows and transposed), Q, T, P (fp32) and the dO block
+// (transposed), all C token rows, their 16-byte units numbered in that order
+// and dealt to the workgroup's threads (two consecutive rows of one column
+// slice per unit, written as in Bf16Stager).
+template <int DK, int C, int BV, int NTH>
+struct StateStager {
+  static constexpr int RP = C / 2;
+  static constexpr int UK = RP * (DK / 8), UT = RP * (C / 8), UP = RP * (C / 4), UO = RP * (BV / 8);
+  static constexpr int E1 = UK, E2 = 2 * UK, E3 = E2 + UT, E4 = E3 + UP, TOT = E4 + UO, CNT = cdiv(TOT, NTH);
+  u32x4 r[CNT][2];
+  __device__ __forceinline__ static int which(int idx, int& j) {
+    if (idx < E1) { j = idx; return 0; }
+    if (idx < E2) { j = idx - E1; return 1; }
+    if (idx < E3) { j = idx - E2; return 2; }
+    if (idx < E4) { j = idx - E3; return 3; }
+    j = idx - E4;
+    return 4;
+  }
+  __device__ __forceinline__ void load(const uint16_t* kk, const uint16_t* qq, int64_t qk_stride, const uint16_t* tt,
+                                       const float* pp, const uint16_t* dov, int64_t v_stride, int valid, int tid) {
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) {
+      const int idx = tid + i * NTH;
+      r[i][0] = r[i][1] = u32x4{0u, 0u, 0u, 0u};
+      if (idx >= TOT) continue;
+      int j;
+      const int op = which(idx, j);
+      const int t = 2 * (j % RP), c = (j / RP) * (op == 3 ? 4 : 8);
+      const unsigned char* src;
+      int64_t stride;  // bytes
+      int lim = valid;
+      if (op <= 1) {
+        src = reinterpret_cast<const unsigned char*>((op == 0 ? kk : qq) + c);
+        stride = qk_stride * 2;
+      } else if (op == 2) {
+        src = reinterpret_cast<const unsigned char*>(tt + c);
+        stride = C * 2;
+        lim = C;
+      } else if (op == 3) {
+        src = reinterpret_cast<const unsigned char*>(pp + c);
+        stride = C * 4;
+        lim = C;
+      } else {
+        src = reinterpret_cast<const unsigned char*>(dov + c);
+        stride = v_stride * 2;
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        if (t + h < lim) r[i][h] = *reinterpret_cast<const u32x4*>(src + (t + h) * stride);
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* Kb, int KBP, uint16_t* KbT, uint16_t* QbT, uint16_t* TbT,
+                                        uint16_t* PbT, uint16_t* dOT, int TBP, int tid) const {
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) {
+      const int idx = tid + i * NTH;
+      if (idx >= TOT) continue;
+      int j;
+      const int op = which(idx, j);
+      const int t = 2 * (j % RP);
+      if (op == 3) {  // P: fp32 -> bf16, four columns, transposed only
+        const int c = (j / RP) * 4;
+        union {
+          u32x4 u;
+          float e[4];
+        } x0, x1;
+        x0.u = r[i][0];
+        x1.u = r[i][1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          *reinterpret_cast<uint32_t*>(PbT + (c + e) * TBP + t) =
+              uint32_t(from_f32<uint16_t>(x0.e[e])) | (uint32_t(from_f32<uint16_t>(x1.e[e])) << 16);
+      } else {
+        const int c = (j / RP) * 8;
+        if (op == 0) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) *reinterpret_cast<u32x4*>(Kb + (t + h) * KBP + c) = r[i][h];
+        }
+        uint16_t* XT = op == 0 ? KbT : op == 1 ? QbT : op == 2 ? TbT : dOT;
+        union {
+          u32x4 u;
+          uint16_t e[8];
+        } x0, x1;
+        x0.u = r[i][0];
+        x1.u = r[i][1];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          *reinterpret_cast<uint32_t*>(XT + (c + e) * TBP + t) = uint32_t(x0.e[e]) | (uint32_t(x1.e[e]) << 16);
+      }
+    }
+  }
 };
 
 template <int DK, int C>
@@ -563,8 +657,8 @@ __global__ __launch_bounds__((BwdStateBf16Shape<DK, C>::NTH)) void bwd_state_bf1
     const uint16_t* __restrict__ tws, const float* __restrict__ pws, const float* __restrict__ dsf,
     float* __restrict__ dstates, float* __restrict__ ds0, int H, int64_t L, int NC, int DV, int NVB, int remap) {
   using S = BwdStateBf16Shape<DK, C>;
-  constexpr int KBP = S::KBP, TBP = S::TBP, BV = S::BV, NS = S::NS, NE = S::NE, NWV = S::NWV, NTH = S::NTH;
-  static_assert(NS >= 1 && NE >= 1, "d_k and the chunk are multiples of 32");
+  constexpr int KBP = S::KBP, TBP = S::TBP, BV = S::BV, NS = S::NS, NEF = S::NEF, NWV = S::NWV, NTH = S::NTH;
+  static_assert(NS >= 1 && NEF >= 1, "d_k and the chunk are multiples of 32");
   __shared__ __align__(16) unsigned char lds[S::BYTES];
   auto arr = [&](int off) { return reinterpret_cast<uint16_t*>(lds + off); };
   uint16_t *Kb = arr(S::KB), *KbT = arr(S::KBT), *QbT = arr(S::QBT), *TbT = arr(S::TBT), *PbT = arr(S::PBT);
@@ -589,7 +683,7 @@ __global__ __launch_bounds__((BwdStateBf16Shape<DK, C>::NTH)) void bwd_state_bf1
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), li = lane & 15, g = lane >> 4;
   const int64_t qk_stride = int64_t(H) * DK, v_stride = int64_t(H) * DV;
 
-  // dS tiles of this wavefront: tile t = w + 4 i covers dims 16 (t / 2) .., columns 16 (t % 2) ..
+  // dS tiles of this wavefront: tile t = w + NWV i covers dims 16 (t / 2) .., columns 16 (t % 2) ..
   f32x4 dS[NS];
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
@@ -600,19 +694,13 @@ __global__ __launch_bounds__((BwdStateBf16Shape<DK, C>::NTH)) void bwd_state_bf1
   }
 
   // chunk n's operands, staged through registers one chunk ahead
-  Bf16Stager<uint16_t, C, DK, NTH> sq, sk;
-  Bf16Stager<uint16_t, C, C, NTH> st;
-  Bf16Stager<float, C, C, NTH> spp;
-  Bf16Stager<uint16_t, C, BV, NTH> sdo;
+  StateStager<DK, C, BV, NTH> so;
   auto load = [&](int n) {
     const int64_t t0 = int64_t(n) * C;
     const int valid = int(sp.len - t0 < C ? sp.len - t0 : C);
     const int64_t row0 = (sp.bos + t0) * H + h;
-    sq.load(q + row0 * DK, qk_stride, valid, tid);
-    sk.load(k + row0 * DK, qk_stride, valid, tid);
-    sdo.load(dout + row0 * DV + v0, v_stride, valid, tid);
-    st.load(tws + (sp.slot0 + n) * C * C, C, C, tid);
-    spp.load(pws + (sp.slot0 + n) * C * C, C, C, tid);
+    so.load(k + row0 * DK, q + row0 * DK, qk_stride, tws + (sp.slot0 + n) * C * C, pws + (sp.slot0 + n) * C * C,
+            dout + row0 * DV + v0, v_stride, valid, tid);
   };
   if (sp.nc > 0) load(sp.nc - 1);
 
@@ -627,17 +715,13 @@ __global__ __launch_bounds__((BwdStateBf16Shape<DK, C>::NTH)) void bwd_state_bf1
       for (int qq = 0; qq < 4; ++qq) dst[(d0 + 4 * g + qq) * DV + v0 + c0 + li] = dS[i][qq];
       st4(dST + (c0 + li) * KBP + d0 + 4 * g, dS[i]);
     }
-    sk.store(Kb, KBP, KbT, TBP, tid);
-    sq.store(nullptr, 0, QbT, TBP, tid);
-    st.store(nullptr, 0, TbT, TBP, tid);
-    spp.store(nullptr, 0, PbT, TBP, tid);
-    sdo.store(nullptr, 0, dOT, TBP, tid);
+    so.store(Kb, KBP, KbT, QbT, TbT, PbT, dOT, TBP, tid);
     if (n > 0) load(n - 1);  // in flight during this chunk
     __syncthreads();
     // E = P^T dO + K dS   ([C][BV] tiles; stored as E^T)
 #pragma unroll
-    for (int i = 0; i < NE; ++i) {
-      const int t = w + NWV * i, r0 = 16 * (t / 2), c0 = 16 * (t % 2);
+    for (int t = w; t < NEF; t += NWV) {
+      const int r0 = 16 * (t / 2), c0 = 16 * (t % 2);
       f32x4 acc = zero4();
       tile_bf<C>(acc, PbT, TBP, dOT, TBP, r0, c0, li, g);
       tile_bf<DK>(acc, Kb, KBP, dST, KBP, r0, c0, li, g);
@@ -646,8 +730,8 @@ __global__ __launch_bounds__((BwdStateBf16Shape<DK, C>::NTH)) void bwd_state_bf1
     __syncthreads();
     // F = T^T E   (stored as F^T)
 #pragma unroll
-    for (int i = 0; i < NE; ++i) {
-      const int t = w + NWV * i, r0 = 16 * (t / 2), c0 = 16 * (t % 2);
+    for (int t = w; t < NEF; t += NWV) {
+      const int r0 = 16 * (t / 2), c0 = 16 * (t % 2);
       f32x4 acc = zero4();
       tile_bf<C>(acc, TbT, TBP, ET, TBP, r0, c0, li, g);
       st4(FT + (c0 + li) * TBP + r0 + 4 * g, acc);
