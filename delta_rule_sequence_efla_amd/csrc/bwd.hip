@@ -3,7 +3,9 @@
 // slot s of the dense batch ((b H + h) NC + n):
 //   T  [slots][C][C]     input dtype   UT transform (as in the forward pass)
 //   X  [slots][C][C]     fp32          (I + A)^{-1}
-//   P  [slots][C][C]     fp32          tril(Q K^T)
+//   P  [slots][C][C]     fp32          tril(Q K^T) (bf16, packed from the
+//                                      region's start, where the bf16
+//                                      matrix-core kernels read it)
 //   a  [slots][C]        fp32          coefficients
 //   S  [slots][dk][dv]   input dtype   state at the start of the chunk (bf16
 //                                      inputs: the operand values the forward
@@ -71,19 +73,33 @@ hipError_t bwd_launch_impl(const T* q, const T* k, const T* v, const T* beta, co
   float* aws = reinterpret_cast<float*>(ws + lay.a);
   T* sws = reinterpret_cast<T*>(ws + lay.s);
   float* dsws = reinterpret_cast<float*>(ws + lay.ds);
+  // bf16 matrix-core kernels for steps 3 and 4 where the shape allows
+  // (EFLA_BWD_IMPL=fp32 keeps the fp32 ones); they read P as bf16, which the
+  // one-wavefront UT kernel then writes (it covers every such shape)
+  bool bf16k = false;
+  if constexpr (sizeof(T) == 2 && (DK == 32 || DK == 64 || DK == 128) && (C == 32 || C == 64)) {
+    const char* impl = getenv("EFLA_BWD_IMPL");
+    bf16k = !(impl && strcmp(impl, "fp32") == 0) && bwd_bf16_supported(DK, DV, C);
+  }
+  const uint16_t* pws16 = reinterpret_cast<const uint16_t*>(pws);
   if (slots > 0) {
     // 1. T, X, P and a of every chunk: one wavefront per chunk for the bf16
-    // shapes that kernel covers (EFLA_UT_IMPL=workgroup keeps the other),
-    // else one workgroup per chunk
+    // shapes that kernel covers (EFLA_UT_IMPL=workgroup keeps the other unless
+    // the bf16 kernels follow), else one workgroup per chunk
     bool ut_done = false;
     if constexpr (sizeof(T) == 2 && (DK == 32 || DK == 64 || DK == 128) && (C == 32 || C == 64)) {
       const char* impl = getenv("EFLA_UT_IMPL");
-      if (!(impl && strcmp(impl, "workgroup") == 0)) {
+      if (bf16k || !(impl && strcmp(impl, "workgroup") == 0)) {
         constexpr int NW = UtWaveShape<DK, C>::WAVES;
         const int64_t nwg = (slots + NW - 1) / NW;
-        hipLaunchKernelGGL((ut_wave_kernel<DK, C, true>), dim3(unsigned(nwg)), dim3(64 * NW), 0, s, k, beta, tws,
-                           H, L, NC, slots, rule, static_cast<const int32_t*>(nullptr), 0, nwg,
-                           static_cast<int32_t*>(nullptr), q, xws, aws, pws);
+        if (bf16k)
+          hipLaunchKernelGGL((ut_wave_kernel<DK, C, true, true>), dim3(unsigned(nwg)), dim3(64 * NW), 0, s, k, beta,
+                             tws, H, L, NC, slots, rule, static_cast<const int32_t*>(nullptr), 0, nwg,
+                             static_cast<int32_t*>(nullptr), q, xws, aws, pws);
+        else
+          hipLaunchKernelGGL((ut_wave_kernel<DK, C, true>), dim3(unsigned(nwg)), dim3(64 * NW), 0, s, k, beta, tws,
+                             H, L, NC, slots, rule, static_cast<const int32_t*>(nullptr), 0, nwg,
+                             static_cast<int32_t*>(nullptr), q, xws, aws, pws);
         ut_done = true;
       }
     }
@@ -98,11 +114,10 @@ hipError_t bwd_launch_impl(const T* q, const T* k, const T* v, const T* beta, co
   // on bf16 matrix cores where the shape allows, like step 4)
   bool state_done = false;
   if constexpr (sizeof(T) == 2 && DK % 32 == 0 && C % 32 == 0) {
-    const char* impl = getenv("EFLA_BWD_IMPL");
-    if (!(impl && strcmp(impl, "fp32") == 0) && bwd_bf16_supported(DK, DV, C)) {
+    if (bf16k) {
       hipLaunchKernelGGL((bwd_state_bf16_kernel<DK, C>), dim3(unsigned(BH * (DV / kBwdBV))),
                          dim3(BwdStateBf16Shape<DK, C>::NTH), 0, s,
-                         q, k, dout, tws, pws, dsf, dsws, ds0, H, L, NC, DV, DV / kBwdBV, BH % 8 == 0 ? 1 : 0);
+                         q, k, dout, tws, pws16, dsf, dsws, ds0, H, L, NC, DV, DV / kBwdBV, BH % 8 == 0 ? 1 : 0);
       state_done = true;
     }
   }
@@ -114,11 +129,10 @@ hipError_t bwd_launch_impl(const T* q, const T* k, const T* v, const T* beta, co
   // 4. every chunk's gradients: bf16 inputs on bf16 matrix cores where the
   // shape allows (EFLA_BWD_IMPL=fp32 keeps the fp32 kernel), else fp32
   if constexpr (sizeof(T) == 2 && DK % 32 == 0 && C % 32 == 0) {
-    const char* impl = getenv("EFLA_BWD_IMPL");
-    if (!(impl && strcmp(impl, "fp32") == 0) && bwd_bf16_supported(DK, DV, C)) {
+    if (bf16k) {
       hipLaunchKernelGGL((bwd_chunk_bf16_kernel<DK, C>), dim3(unsigned(slots)), dim3(BwdBf16Shape<DK, C>::NTH), 0, s,
                          q, k, v, beta,
-                         dout, tws, xws, aws, pws, sws, dsws, dq, dk, dv, dbeta, H, L, NC, DV, rule);
+                         dout, tws, xws, aws, pws16, sws, dsws, dq, dk, dv, dbeta, H, L, NC, DV, rule);
       return hipGetLastError();
     }
   }

@@ -273,7 +273,7 @@ template <int DK, int C>
 __global__ __launch_bounds__((BwdBf16Shape<DK, C>::NTH)) void bwd_chunk_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ beta, const uint16_t* __restrict__ dout, const uint16_t* __restrict__ tws,
-    const float* __restrict__ xws, const float* __restrict__ aws, const float* __restrict__ pws,
+    const float* __restrict__ xws, const float* __restrict__ aws, const uint16_t* __restrict__ pws,
     const uint16_t* __restrict__ states, const float* __restrict__ dstates, uint16_t* __restrict__ dq,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, uint16_t* __restrict__ dbeta, int H, int64_t L, int NC,
     int DV, int rule) {
@@ -307,7 +307,7 @@ __global__ __launch_bounds__((BwdBf16Shape<DK, C>::NTH)) void bwd_chunk_bf16_ker
     Bf16Stager<uint16_t, C, DK, NTH> sk;
     sk.load(k + row0 * DK, qk_stride, valid, tid);
     Bf16Stager<uint16_t, C, C, NTH> st;
-    Bf16Stager<float, C, C, NTH> spp;
+    Bf16Stager<uint16_t, C, C, NTH> spp;
     st.load(tws + slot * C * C, C, C, tid);
     spp.load(pws + slot * C * C, C, C, tid);
     sk.store(Kb, KBP, nullptr, 0, tid);
@@ -558,15 +558,15 @@ struct BwdStateBf16Shape {
 };
 
 // The chunk operands of the reverse pass staged through one set of
-// registers: K (rows and transposed), Q, T, P (fp32) and the dO block
-// (transposed), all C token rows, their 16-byte units numbered in that order
-// and dealt to the workgroup's threads (two consecutive rows of one column
-// slice per unit, written as in Bf16Stager).
+// registers: K (rows and transposed), Q, T, P and the dO block (transposed),
+// all bf16 with C token rows, their 16-byte units numbered in that order and
+// dealt to the workgroup's threads (two consecutive rows of one column slice
+// per unit, written as in Bf16Stager).
 template <int DK, int C, int BV, int NTH>
 struct StateStager {
   static constexpr int RP = C / 2;
-  static constexpr int UK = RP * (DK / 8), UT = RP * (C / 8), UP = RP * (C / 4), UO = RP * (BV / 8);
-  static constexpr int E1 = UK, E2 = 2 * UK, E3 = E2 + UT, E4 = E3 + UP, TOT = E4 + UO, CNT = cdiv(TOT, NTH);
+  static constexpr int UK = RP * (DK / 8), UT = RP * (C / 8), UO = RP * (BV / 8);
+  static constexpr int E1 = UK, E2 = 2 * UK, E3 = E2 + UT, E4 = E3 + UT, TOT = E4 + UO, CNT = cdiv(TOT, NTH);
   u32x4 r[CNT][2];
   __device__ __forceinline__ static int which(int idx, int& j) {
     if (idx < E1) { j = idx; return 0; }
@@ -577,7 +577,8 @@ struct StateStager {
     return 4;
   }
   __device__ __forceinline__ void load(const uint16_t* kk, const uint16_t* qq, int64_t qk_stride, const uint16_t* tt,
-                                       const float* pp, const uint16_t* dov, int64_t v_stride, int valid, int tid) {
+                                       const uint16_t* pp, const uint16_t* dov, int64_t v_stride, int valid,
+                                       int tid) {
 #pragma unroll
     for (int i = 0; i < CNT; ++i) {
       const int idx = tid + i * NTH;
@@ -585,24 +586,20 @@ struct StateStager {
       if (idx >= TOT) continue;
       int j;
       const int op = which(idx, j);
-      const int t = 2 * (j % RP), c = (j / RP) * (op == 3 ? 4 : 8);
-      const unsigned char* src;
-      int64_t stride;  // bytes
+      const int t = 2 * (j % RP), c = (j / RP) * 8;
+      const uint16_t* src;
+      int64_t stride;  // elements
       int lim = valid;
       if (op <= 1) {
-        src = reinterpret_cast<const unsigned char*>((op == 0 ? kk : qq) + c);
-        stride = qk_stride * 2;
-      } else if (op == 2) {
-        src = reinterpret_cast<const unsigned char*>(tt + c);
-        stride = C * 2;
-        lim = C;
-      } else if (op == 3) {
-        src = reinterpret_cast<const unsigned char*>(pp + c);
-        stride = C * 4;
+        src = (op == 0 ? kk : qq) + c;
+        stride = qk_stride;
+      } else if (op <= 3) {  // T, P: whole C x C slots
+        src = (op == 2 ? tt : pp) + c;
+        stride = C;
         lim = C;
       } else {
-        src = reinterpret_cast<const unsigned char*>(dov + c);
-        stride = v_stride * 2;
+        src = dov + c;
+        stride = v_stride;
       }
 #pragma unroll
       for (int h = 0; h < 2; ++h)
@@ -617,36 +614,21 @@ struct StateStager {
       if (idx >= TOT) continue;
       int j;
       const int op = which(idx, j);
-      const int t = 2 * (j % RP);
-      if (op == 3) {  // P: fp32 -> bf16, four columns, transposed only
-        const int c = (j / RP) * 4;
-        union {
-          u32x4 u;
-          float e[4];
-        } x0, x1;
-        x0.u = r[i][0];
-        x1.u = r[i][1];
+      const int t = 2 * (j % RP), c = (j / RP) * 8;
+      if (op == 0) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          *reinterpret_cast<uint32_t*>(PbT + (c + e) * TBP + t) =
-              uint32_t(from_f32<uint16_t>(x0.e[e])) | (uint32_t(from_f32<uint16_t>(x1.e[e])) << 16);
-      } else {
-        const int c = (j / RP) * 8;
-        if (op == 0) {
-#pragma unroll
-          for (int h = 0; h < 2; ++h) *reinterpret_cast<u32x4*>(Kb + (t + h) * KBP + c) = r[i][h];
-        }
-        uint16_t* XT = op == 0 ? KbT : op == 1 ? QbT : op == 2 ? TbT : dOT;
-        union {
-          u32x4 u;
-          uint16_t e[8];
-        } x0, x1;
-        x0.u = r[i][0];
-        x1.u = r[i][1];
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          *reinterpret_cast<uint32_t*>(XT + (c + e) * TBP + t) = uint32_t(x0.e[e]) | (uint32_t(x1.e[e]) << 16);
+        for (int h = 0; h < 2; ++h) *reinterpret_cast<u32x4*>(Kb + (t + h) * KBP + c) = r[i][h];
       }
+      uint16_t* XT = op == 0 ? KbT : op == 1 ? QbT : op == 2 ? TbT : op == 3 ? PbT : dOT;
+      union {
+        u32x4 u;
+        uint16_t e[8];
+      } x0, x1;
+      x0.u = r[i][0];
+      x1.u = r[i][1];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<uint32_t*>(XT + (c + e) * TBP + t) = uint32_t(x0.e[e]) | (uint32_t(x1.e[e]) << 16);
     }
   }
 };
@@ -654,7 +636,7 @@ struct StateStager {
 template <int DK, int C>
 __global__ __launch_bounds__((BwdStateBf16Shape<DK, C>::NTH)) void bwd_state_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ dout,
-    const uint16_t* __restrict__ tws, const float* __restrict__ pws, const float* __restrict__ dsf,
+    const uint16_t* __restrict__ tws, const uint16_t* __restrict__ pws, const float* __restrict__ dsf,
     float* __restrict__ dstates, float* __restrict__ ds0, int H, int64_t L, int NC, int DV, int NVB, int remap) {
   using S = BwdStateBf16Shape<DK, C>;
   constexpr int KBP = S::KBP, TBP = S::TBP, BV = S::BV, NS = S::NS, NEF = S::NEF, NWV = S::NWV, NTH = S::NTH;

@@ -57,8 +57,10 @@ __device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory")
 
 // The instance for the backward pass (BWD) also writes, in fp32 per chunk
 // slot: X (C x C, zeros above the diagonal), a (C) and P = tril(Q K^T) (C x C,
-// the diagonal included), with q the queries in the layout of k.
-template <int DK, int C, bool BWD = false>
+// the diagonal included; if PB16 rounded to bf16 and packed as [slots][C][C]
+// bf16 from the start of the same buffer), with q the queries in the layout of
+// k.
+template <int DK, int C, bool BWD = false, bool PB16 = false>
 __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict__ k,
                                                       const uint16_t* __restrict__ beta,
                                                       uint16_t* __restrict__ tws, int H, int64_t L, int NC,
@@ -126,7 +128,8 @@ __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict
         else Qf[rt][ku].v = bf16x8{};
       }
     }
-    float* pdst = pout + id * int64_t(C) * C;
+    float* pdst = pout + id * int64_t(C) * C;                          // fp32 P
+    uint16_t* pdst16 = reinterpret_cast<uint16_t*>(pout) + id * int64_t(C) * C;  // bf16 P (PB16)
 #pragma unroll
     for (int r = 0; r < NRT; ++r)
 #pragma unroll
@@ -139,7 +142,9 @@ __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
           const int ii = 16 * r + 4 * g + qq, jj = 16 * c + li;
-          pdst[ii * C + jj] = jj <= ii ? acc[qq] : 0.0f;
+          const float pv = jj <= ii ? acc[qq] : 0.0f;
+          if constexpr (PB16) pdst16[ii * C + jj] = from_f32<uint16_t>(pv);
+          else pdst[ii * C + jj] = pv;
         }
       }
   }
