@@ -245,23 +245,28 @@ __global__ __launch_bounds__(64 * (BV / 16 + 3)) void recurrence_roles_kernel(
     }
   } else if (ST && role == S::kOut) {
     // S_n fragments of tile ct, k-unit ku: element e of lane (li, g) is state
-    // row key_phys(32 ku + 16 (e / 4) + 4 g + e % 4), column v0 + 16 ct + li
+    // row key_phys(32 ku + 16 (e / 4) + 4 g + e % 4) = 32 ku + 8 g + e, column
+    // v0 + 16 ct + li.  So columns 8 j .. 8 j + 7 of row r are element r % 8
+    // of eight neighbouring lanes' fragments: the wave gathers them with 2-byte
+    // LDS reads and writes each (row, 8 columns) unit with one 16-byte store
+    // (eight stores per lane per chunk instead of 64 2-byte ones).
+    const uint16_t* frag = reinterpret_cast<const uint16_t*>(&bS_buf[0][0][0]);
     for (int n = 0; n < nc; ++n) {
       sync();  // A: S_n published
-      uint16_t* dst = states + (sp.slot0 + n) * DK * DV;
+      uint16_t* dst = states + (sp.slot0 + n) * DK * DV + v0;
 #pragma unroll 1
-      for (int ct = 0; ct < NT; ++ct)
-#pragma unroll 1
-        for (int ku = 0; ku < NKU_D; ++ku) {
-          union {
-            u32x4 u;
-            uint16_t e16[8];
-          } f;
-          f.u = *reinterpret_cast<const u32x4*>(&bS_buf[ct][ku][lane]);
+      for (int u = lane; u < DK * (BV / 8); u += kWave) {
+        const int r = u / (BV / 8), cg = u % (BV / 8);
+        const int ct = cg / 2, l0 = 8 * (cg % 2), ku = r / 32, gr = (r % 32) / 8, e = r % 8;
+        const uint16_t* src = frag + ((ct * NKU_D + ku) * kWave + 16 * gr + l0) * 8 + e;
+        union {
+          u32x4 u;
+          uint16_t e16[8];
+        } f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            dst[key_phys(32 * ku + 16 * (e / 4) + 4 * g + e % 4) * DV + v0 + 16 * ct + li] = f.e16[e];
-        }
+        for (int c = 0; c < 8; ++c) f.e16[c] = src[8 * c];
+        *reinterpret_cast<u32x4*>(dst + r * DV + 8 * cg) = f.u;
+      }
       sync();  // B
     }
   } else if (!NOOUT && role == S::kOut) {
