@@ -143,10 +143,19 @@ __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict
         for (int qq = 0; qq < 4; ++qq) {
           const int ii = 16 * r + 4 * g + qq, jj = 16 * c + li;
           const float pv = jj <= ii ? acc[qq] : 0.0f;
-          if constexpr (PB16) pdst16[ii * C + jj] = from_f32<uint16_t>(pv);
+          if constexpr (PB16) Ts[ii * TP + jj] = from_f32<uint16_t>(pv);  // staged, stored as rows below
           else pdst[ii * C + jj] = pv;
         }
       }
+    if constexpr (PB16) {  // bf16 P: 16-byte row stores from the staging tile
+      wave_lds_order();
+#pragma unroll
+      for (int idx = lane; idx < C * (C / 8); idx += 64) {
+        const int r = idx / (C / 8), c0 = (idx % (C / 8)) * 8;
+        *reinterpret_cast<u32x4*>(pdst16 + r * C + c0) = *reinterpret_cast<const u32x4*>(Ts + r * TP + c0);
+      }
+      wave_lds_order();  // the G blocks reuse the scratch
+    }
   }
 
   // ---- G: diagonal tiles and the tiles above the diagonal ----------------
@@ -240,16 +249,31 @@ __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict
     }
 
   if constexpr (BWD) {  // X (the diagonal blocks as solved, zeros above) and a
+    // X in blocks of 32 rows staged through the scratch as fp32 [32][C + 4],
+    // then stored with 16-byte row writes
+    constexpr int XP = C + 4;
+    static_assert(32 * XP * 4 <= S::SCRATCH, "a 32-row block of X fits the scratch");
+    float* Xst = reinterpret_cast<float*>(scratch_all[w]);
     float* xdst = xout + id * int64_t(C) * C;
 #pragma unroll
-    for (int i = 0; i < NRT; ++i)
+    for (int hb = 0; hb < C / 32; ++hb) {
 #pragma unroll
-      for (int j = 0; j < NRT; ++j)
+      for (int i = 2 * hb; i < 2 * hb + 2; ++i)
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const int r = 16 * i + 4 * g + qq, c = 16 * j + li;
-          xdst[r * C + c] = (j < i || (j == i && c <= r)) ? X[i][j][qq] : 0.0f;
-        }
+        for (int j = 0; j < NRT; ++j)
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const int r = 16 * i + 4 * g + qq, c = 16 * j + li;
+            Xst[(r - 32 * hb) * XP + c] = (j < i || (j == i && c <= r)) ? X[i][j][qq] : 0.0f;
+          }
+      wave_lds_order();
+#pragma unroll
+      for (int idx = lane; idx < 32 * (C / 4); idx += 64) {
+        const int r = idx / (C / 4), c0 = (idx % (C / 4)) * 4;
+        *reinterpret_cast<u32x4*>(xdst + (32 * hb + r) * C + c0) = *reinterpret_cast<const u32x4*>(Xst + r * XP + c0);
+      }
+      wave_lds_order();  // the next block, then T's staging, reuse the scratch
+    }
     if (lane < C) aout[id * int64_t(C) + lane] = as[lane];
   }
 
