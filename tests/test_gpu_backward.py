@@ -139,20 +139,24 @@ def test_backward_full_1p3b_shape():
     _check(W.generate(w, device="cuda"), 64, "shape_1p3b full", seed=9)
 
 
-@pytest.mark.parametrize("impl", ["fp32", "bf16"])
-def test_backward_bf16_inputs_both_chunk_kernels(impl, monkeypatch):
-    """bf16 inputs through the fp32 chunk and state kernels with the
-    one-workgroup-per-chunk UT transform, and through the bf16 kernels with the
-    one-wavefront-per-chunk one, at the 1.3B head configuration with a ragged
-    last chunk and the Euler rule too."""
+@pytest.mark.parametrize("impl,ut", [("fp32", "workgroup"), ("fp32", "wave"), ("bf16", "wave"),
+                                     ("bf16", "workgroup")])
+def test_backward_bf16_inputs_both_chunk_kernels(impl, ut, monkeypatch):
+    """bf16 inputs through the fp32 chunk and state kernels (P in fp32) with
+    either UT transform, and through the bf16 kernels (P in bf16, so the
+    one-wavefront-per-chunk UT transform runs even where the workgroup one is
+    asked for), at the 1.3B head configuration with a ragged last chunk and the
+    Euler rule too."""
     require_gpu()
     if impl == "fp32":
         monkeypatch.setenv("EFLA_BWD_IMPL", "fp32")
-        monkeypatch.setenv("EFLA_UT_IMPL", "workgroup")
     else:
         monkeypatch.delenv("EFLA_BWD_IMPL", raising=False)
+    if ut == "workgroup":
+        monkeypatch.setenv("EFLA_UT_IMPL", "workgroup")
+    else:
         monkeypatch.delenv("EFLA_UT_IMPL", raising=False)
     w = W.get("shape_1p3b")
     inp = W.generate(w, device="cuda", B=1, H=3, L=200, seed=930)
-    _check(inp, 64, f"bf16 inputs, {impl} chunk kernel", seed=31)
-    _check(inp, 64, f"bf16 inputs, {impl} chunk kernel, Euler rule", seed=32, rule="euler")
+    _check(inp, 64, f"bf16 inputs, {impl} chunk kernel, {ut} UT", seed=31)
+    _check(inp, 64, f"bf16 inputs, {impl} chunk kernel, {ut} UT, Euler rule", seed=32, rule="euler")
