@@ -127,8 +127,9 @@ def pct(xs, p):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
-              "the EFLA hot path shards over (batch, head) with no exchange, see DESIGN.md.",
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); the EFLA hot path "
+              "shards over (batch, head) with no exchange between GPUs, so N GPUs each run this "
+              "single-GPU workload on their share.",
               file=sys.stderr)
         sys.exit(2)
 
