@@ -281,8 +281,8 @@ __global__ __launch_bounds__(kThreads) void ut_transform_kernel(const T* __restr
 template <typename T, int DK, int C, int BV>
 __global__ __launch_bounds__(kThreads) void recurrence_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const T* __restrict__ tws, const float* __restrict__ s0, T* __restrict__ o,
-    float* __restrict__ sfin, int H, int64_t L, int NC, int DV, int NVB, int remap,
+    const T* __restrict__ tws, const float* s0, T* __restrict__ o,
+    float* sfin, int H, int64_t L, int NC, int DV, int NVB, int remap,
     const int32_t* __restrict__ cu, T* __restrict__ states = nullptr, int trans = 0,
     const int32_t* __restrict__ order = nullptr, int nseq = 0) {
   constexpr int DKP = round_up(DK, 32), CP = round_up(C, 32);

@@ -63,8 +63,8 @@ enum RolesMode { kFwd = 0, kStates = 1, kFinal = 2, kTrans = 3 };
 template <int DK, int C, int BV, int MODE>
 __global__ __launch_bounds__(64 * (BV / 16 + 3)) void recurrence_roles_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ tws, const float* __restrict__ s0, uint16_t* __restrict__ o,
-    float* __restrict__ sfin, int H, int64_t L, int NC, int DV, int NVB, int remap,
+    const uint16_t* __restrict__ tws, const float* s0, uint16_t* __restrict__ o,
+    float* sfin, int H, int64_t L, int NC, int DV, int NVB, int remap,
     const int32_t* __restrict__ cu, uint16_t* __restrict__ states, const int32_t* __restrict__ order, int nseq) {
   using S = RolesShape<DK, C, BV>;
   constexpr bool ST = MODE == kStates, NOOUT = MODE != kFwd, VZERO = MODE == kTrans;

@@ -44,8 +44,8 @@ struct TileShape {
 template <int DK, int C, int BV>
 __global__ __launch_bounds__(4 * BV) void recurrence_tile_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ tws, const float* __restrict__ s0, uint16_t* __restrict__ o,
-    float* __restrict__ sfin, int H, int64_t L, int NC, int DV, int NVB, int remap) {
+    const uint16_t* __restrict__ tws, const float* s0, uint16_t* __restrict__ o,
+    float* sfin, int H, int64_t L, int NC, int DV, int NVB, int remap) {
   using S = TileShape<DK, C, BV>;
   constexpr int NRT = S::NRT, NDT = S::NDT, NKU_D = S::NKU_D, NKU_C = S::NKU_C, NW = S::NW;
   // Three separate arrays (not one indexed ring) so that alias analysis can

@@ -33,8 +33,8 @@ __global__ void seg_offsets_kernel(int32_t* cu, int B, int G, int64_t L, int64_t
 template <int DK>
 __global__ __launch_bounds__(kThreads) void seg_combine_kernel(const float* __restrict__ M,
                                                                const float* __restrict__ Nf,
-                                                               const float* __restrict__ s0,
-                                                               float* __restrict__ sin, float* __restrict__ sfin,
+                                                               const float* s0,
+                                                               float* __restrict__ sin, float* sfin,
                                                                int H, int G, int DV) {
   constexpr int DKP = round_up(DK, 32), MP = DKP + 4, VP = 16 + 4;
   __shared__ __align__(16) float Ms[DKP * MP];

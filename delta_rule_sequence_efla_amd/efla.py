@@ -147,6 +147,26 @@ def _code(dtype) -> int:
     return _DTYPES[dtype]
 
 
+def _want(t, shape, name: str, dtype=None) -> None:
+    """A caller-supplied output or state must have exactly the shape (and
+    dtype) the kernels index it with: the library only sees a pointer."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _ws(workspace, dev, name: str = "workspace") -> int:
+    """Byte size of a workspace tensor, which must be on the call's device."""
+    if workspace is None:
+        return 0
+    if _dev(workspace) != dev:
+        raise ValueError(f"{name} must live on {dev}")
+    return workspace.numel() * workspace.element_size()
+
+
 def efla_coeff(k: torch.Tensor, beta: torch.Tensor, want_lambda: bool = True, rule: str = "exact"):
     """lambda = ||k||^2 and alpha per key row; k [..., d_k], beta [...] -> fp32."""
     dev = _dev(k, beta, dtype=k.dtype)
@@ -166,6 +186,9 @@ def efla_chunk_fwd_workspace_size(B, H, L, d_k, d_v, chunk, dtype) -> int:
 
 
 def _chunk_shapes(q, k, v, beta, s0):
+    _dev(q, k, v, beta, s0)  # one device for inputs and the initial state
+    if k.dim() != 4 or v.dim() != 4:
+        raise ValueError("expected q, k [B,L,H,dk], v [B,L,H,dv], beta [B,L,H]")
     B, L, H, dk = k.shape
     dv = v.shape[-1]
     if q.shape != k.shape or v.shape[:3] != (B, L, H) or beta.shape != (B, L, H):
@@ -173,6 +196,12 @@ def _chunk_shapes(q, k, v, beta, s0):
     if s0 is not None and (s0.shape != (B, H, dk, dv) or s0.dtype != torch.float32):
         raise ValueError("s0 must be float32 [B,H,dk,dv]")
     return B, L, H, dk, dv
+
+
+def _fwd_outs(o, s_final, B, L, H, dk, dv, dtype, ref=None) -> None:
+    _dev(ref, o, s_final)
+    _want(o, (B, L, H, dv), "o", dtype)
+    _want(s_final, (B, H, dk, dv), "s_final", torch.float32)
 
 
 def alloc_workspace(B, H, L, d_k, d_v, chunk, dtype, device) -> torch.Tensor:
@@ -187,28 +216,34 @@ def efla_chunk_fwd(q, k, v, beta, s0=None, chunk: int = 64, o=None, s_final=None
     _dev(q, k, v, beta, o, dtype=q.dtype)
     _dev(s0, s_final, dtype=torch.float32)
     B, L, H, dk, dv = _chunk_shapes(q, k, v, beta, s0)
+    _fwd_outs(o, s_final, B, L, H, dk, dv, q.dtype, q)
     if o is None:
         o = torch.empty((B, L, H, dv), dtype=q.dtype, device=dev)
     if s_final is None and want_final:
         s_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     if workspace is None:
         workspace = alloc_workspace(B, H, L, dk, dv, chunk, q.dtype, dev)
+    nws = _ws(workspace, dev)
     with torch.cuda.device(dev):
         _check(lib().efla_chunk_fwd_rule(_p(q), _p(k), _p(v), _p(beta), _p(s0), _p(o), _p(s_final),
                                          B, H, L, dk, dv, chunk, _code(q.dtype), _rule(rule), _p(workspace),
-                                         workspace.numel(), _stream(dev)), "efla_chunk_fwd")
+                                         nws, _stream(dev)), "efla_chunk_fwd")
     return o, s_final
 
 
 def efla_chunk_ut_transform(k, beta, chunk: int = 64, workspace=None, rule: str = "exact"):
     """Stage 1 only: per-chunk T into the workspace (returned as [B,H,NC,C,C] view)."""
     dev = _dev(k, beta, dtype=k.dtype)
+    if k.dim() != 4:
+        raise ValueError("k must be [B,L,H,dk]")
     B, L, H, dk = k.shape
+    _want(beta, (B, L, H), "beta")
     if workspace is None:
         workspace = alloc_workspace(B, H, L, dk, 16, chunk, k.dtype, dev)
+    nws = _ws(workspace, dev)
     with torch.cuda.device(dev):
         _check(lib().efla_chunk_ut_transform_rule(_p(k), _p(beta), B, H, L, dk, chunk, _code(k.dtype),
-                                                  _rule(rule), _p(workspace), workspace.numel(), _stream(dev)),
+                                                  _rule(rule), _p(workspace), nws, _stream(dev)),
                "efla_chunk_ut_transform")
     nc = (L + chunk - 1) // chunk
     n = B * H * nc * chunk * chunk
@@ -219,17 +254,25 @@ def efla_chunk_recurrence(q, k, v, workspace, s0=None, chunk: int = 64, o=None, 
                           want_final: bool = True):
     """Stage 2 only, reading T from a workspace filled by efla_chunk_ut_transform."""
     dev = _dev(q, k, v, o, dtype=q.dtype)
+    _dev(q, s0, s_final)
     _dev(s0, s_final, dtype=torch.float32)
+    if k.dim() != 4 or v.dim() != 4:
+        raise ValueError("expected q, k [B,L,H,dk], v [B,L,H,dv]")
     B, L, H, dk = k.shape
     dv = v.shape[-1]
+    _want(q, (B, L, H, dk), "q")
+    _want(v, (B, L, H, dv), "v")
+    _want(s0, (B, H, dk, dv), "s0")
+    _fwd_outs(o, s_final, B, L, H, dk, dv, q.dtype, q)
     if o is None:
         o = torch.empty((B, L, H, dv), dtype=q.dtype, device=dev)
     if s_final is None and want_final:
         s_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    nws = _ws(workspace, dev)
     with torch.cuda.device(dev):
         _check(lib().efla_chunk_recurrence(_p(q), _p(k), _p(v), _p(s0), _p(o), _p(s_final), B, H, L,
                                            dk, dv, chunk, _code(q.dtype), _p(workspace),
-                                           workspace.numel(), _stream(dev)), "efla_chunk_recurrence")
+                                           nws, _stream(dev)), "efla_chunk_recurrence")
     return o, s_final
 
 
@@ -256,6 +299,7 @@ def efla_chunk_fwd_segmented(q, k, v, beta, s0=None, chunk: int = 64, segments=N
     _dev(q, k, v, beta, o, dtype=q.dtype)
     _dev(s0, s_final, dtype=torch.float32)
     B, L, H, dk, dv = _chunk_shapes(q, k, v, beta, s0)
+    _fwd_outs(o, s_final, B, L, H, dk, dv, q.dtype, q)
     if segments is None:
         segments = default_segments(B, H, L, dv, chunk)
     if o is None:
@@ -265,10 +309,11 @@ def efla_chunk_fwd_segmented(q, k, v, beta, s0=None, chunk: int = 64, segments=N
     if workspace is None:
         n = efla_chunk_fwd_segmented_workspace_size(B, H, L, dk, dv, chunk, segments, q.dtype)
         workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    nws = _ws(workspace, dev)
     with torch.cuda.device(dev):
         _check(lib().efla_chunk_fwd_segmented(_p(q), _p(k), _p(v), _p(beta), _p(s0), _p(o), _p(s_final), B, H, L,
                                               dk, dv, chunk, segments, _code(q.dtype), _rule(rule), _p(workspace),
-                                              workspace.numel(), _stream(dev)), "efla_chunk_fwd_segmented")
+                                              nws, _stream(dev)), "efla_chunk_fwd_segmented")
     return o, s_final
 
 
@@ -277,9 +322,11 @@ def prepare_chunk_fwd_segmented(q, k, v, beta, s0, o, s_final, workspace, chunk:
     dev = _dev(q, k, v, beta, o, dtype=q.dtype)
     _dev(s0, s_final, dtype=torch.float32)
     B, L, H, dk, dv = _chunk_shapes(q, k, v, beta, s0)
+    _fwd_outs(o, s_final, B, L, H, dk, dv, q.dtype, q)
+    nws = _ws(workspace, dev)
     return PreparedCall(lib().efla_chunk_fwd_segmented,
                         (_p(q), _p(k), _p(v), _p(beta), _p(s0), _p(o), _p(s_final), B, H, L, dk, dv, chunk,
-                         segments, _code(q.dtype), _rule(rule), _p(workspace), workspace.numel(), _stream(dev)),
+                         segments, _code(q.dtype), _rule(rule), _p(workspace), nws, _stream(dev)),
                         "efla_chunk_fwd_segmented", (q, k, v, beta, s0, o, s_final, workspace))
 
 
@@ -306,10 +353,11 @@ def efla_chunk_bwd(q, k, v, beta, d_o, s0=None, ds_final=None, chunk: int = 64, 
     if workspace is None:
         n = efla_chunk_bwd_workspace_size(B, H, L, dk, dv, chunk, q.dtype)
         workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    nws = _ws(workspace, dev)
     with torch.cuda.device(dev):
         _check(lib().efla_chunk_bwd(_p(q), _p(k), _p(v), _p(beta), _p(s0), _p(d_o), _p(ds_final), _p(gq), _p(gk),
                                     _p(gv), _p(gb), _p(gs0), B, H, L, dk, dv, chunk, _code(q.dtype), _rule(rule),
-                                    _p(workspace), workspace.numel(), _stream(dev)), "efla_chunk_bwd")
+                                    _p(workspace), nws, _stream(dev)), "efla_chunk_bwd")
     return gq, gk, gv, gb, gs0
 
 
@@ -318,6 +366,7 @@ def efla_chunk_fwd_varlen_workspace_size(N, H, T, d_k, d_v, chunk, dtype) -> int
 
 
 def _varlen_shapes(q, k, v, beta, cu_seqlens, s0):
+    _dev(q, k, v, beta, cu_seqlens, s0)
     if k.dim() == 4 and k.shape[0] == 1:   # [1, T, H, d] packed layout
         q, k, v, beta = q[0], k[0], v[0], beta[0]
     T, H, dk = k.shape
@@ -332,6 +381,12 @@ def _varlen_shapes(q, k, v, beta, cu_seqlens, s0):
     return N, T, H, dk, dv
 
 
+def _varlen_outs(o, s_final, v, N, H, dk, dv, dtype) -> None:
+    _dev(v, o, s_final)
+    _want(o, v.shape, "o", dtype)
+    _want(s_final, (N, H, dk, dv), "s_final", torch.float32)
+
+
 def efla_chunk_fwd_varlen(q, k, v, beta, cu_seqlens, s0=None, chunk: int = 64, o=None, s_final=None,
                           workspace=None, want_final: bool = True, rule: str = "exact"):
     """Chunked forward over a packed variable-length batch: q, k [T,H,dk],
@@ -341,6 +396,7 @@ def efla_chunk_fwd_varlen(q, k, v, beta, cu_seqlens, s0=None, chunk: int = 64, o
     _dev(q, k, v, beta, o, dtype=q.dtype)
     _dev(s0, s_final, dtype=torch.float32)
     N, T, H, dk, dv = _varlen_shapes(q, k, v, beta, cu_seqlens, s0)
+    _varlen_outs(o, s_final, v, N, H, dk, dv, q.dtype)
     if o is None:
         o = torch.empty(v.shape, dtype=q.dtype, device=dev)
     if s_final is None and want_final:
@@ -348,10 +404,11 @@ def efla_chunk_fwd_varlen(q, k, v, beta, cu_seqlens, s0=None, chunk: int = 64, o
     if workspace is None:
         n = efla_chunk_fwd_varlen_workspace_size(N, H, T, dk, dv, chunk, q.dtype)
         workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    nws = _ws(workspace, dev)
     with torch.cuda.device(dev):
         _check(lib().efla_chunk_fwd_varlen(_p(q), _p(k), _p(v), _p(beta), _p(cu_seqlens), N, _p(s0), _p(o),
                                            _p(s_final), H, T, dk, dv, chunk, _code(q.dtype), _rule(rule),
-                                           _p(workspace), workspace.numel(), _stream(dev)),
+                                           _p(workspace), nws, _stream(dev)),
                "efla_chunk_fwd_varlen")
     return o, s_final
 
@@ -361,9 +418,12 @@ def prepare_chunk_fwd_varlen(q, k, v, beta, cu_seqlens, s0, o, s_final, workspac
     dev = _dev(q, k, v, beta, o, dtype=q.dtype)
     _dev(s0, s_final, dtype=torch.float32)
     N, T, H, dk, dv = _varlen_shapes(q, k, v, beta, cu_seqlens, s0)
+    _dev(q, cu_seqlens)
+    _varlen_outs(o, s_final, v, N, H, dk, dv, q.dtype)
+    nws = _ws(workspace, dev)
     return PreparedCall(lib().efla_chunk_fwd_varlen,
                         (_p(q), _p(k), _p(v), _p(beta), _p(cu_seqlens), N, _p(s0), _p(o), _p(s_final), H, T,
-                         dk, dv, chunk, _code(q.dtype), _rule(rule), _p(workspace), workspace.numel(),
+                         dk, dv, chunk, _code(q.dtype), _rule(rule), _p(workspace), nws,
                          _stream(dev)),
                         "efla_chunk_fwd_varlen", (q, k, v, beta, cu_seqlens, s0, o, s_final, workspace))
 
@@ -377,6 +437,7 @@ def efla_step(q, k, v, beta, state, o=None, rule: str = "exact"):
     if q.shape != k.shape or v.shape[:2] != (N, H) or beta.shape != (N, H) \
             or state.shape != (N, H, dk, dv):
         raise ValueError("expected q, k [N,H,dk], v [N,H,dv], beta [N,H], state [N,H,dk,dv]")
+    _want(o, (N, H, dv), "o", q.dtype)
     if o is None:
         o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
     with torch.cuda.device(dev):
@@ -406,9 +467,10 @@ def prepare_chunk_stages(q, k, v, beta, s0, o, s_final, workspace, chunk: int = 
     dev = _dev(q, k, v, beta, o, dtype=q.dtype)
     _dev(s0, s_final, dtype=torch.float32)
     B, L, H, dk, dv = _chunk_shapes(q, k, v, beta, s0)
+    _fwd_outs(o, s_final, B, L, H, dk, dv, q.dtype, q)
     code = _code(q.dtype)
     stream = _stream(dev)
-    ws, nbytes = _p(workspace), workspace.numel()
+    ws, nbytes = _p(workspace), _ws(workspace, dev)
     ut = PreparedCall(lib().efla_chunk_ut_transform_rule,
                       (_p(k), _p(beta), B, H, L, dk, chunk, code, _rule(rule), ws, nbytes, stream),
                       "efla_chunk_ut_transform", (k, beta, workspace))
@@ -423,9 +485,11 @@ def prepare_chunk_fwd(q, k, v, beta, s0, o, s_final, workspace, chunk: int = 64,
     dev = _dev(q, k, v, beta, o, dtype=q.dtype)
     _dev(s0, s_final, dtype=torch.float32)
     B, L, H, dk, dv = _chunk_shapes(q, k, v, beta, s0)
+    _fwd_outs(o, s_final, B, L, H, dk, dv, q.dtype, q)
+    nws = _ws(workspace, dev)
     return PreparedCall(lib().efla_chunk_fwd_rule,
                         (_p(q), _p(k), _p(v), _p(beta), _p(s0), _p(o), _p(s_final), B, H, L, dk, dv,
-                         chunk, _code(q.dtype), _rule(rule), _p(workspace), workspace.numel(), _stream(dev)),
+                         chunk, _code(q.dtype), _rule(rule), _p(workspace), nws, _stream(dev)),
                         "efla_chunk_fwd", (q, k, v, beta, s0, o, s_final, workspace))
 
 
@@ -434,10 +498,15 @@ def prepare_chunk_bwd(q, k, v, beta, d_o, s0, ds_final, dq, dk, dv, dbeta, ds0, 
     dev = _dev(q, k, v, beta, d_o, dq, dk, dv, dbeta, dtype=q.dtype)
     _dev(s0, ds_final, ds0, dtype=torch.float32)
     B, L, H, d_k, d_v = _chunk_shapes(q, k, v, beta, s0)
+    for t, like, name in ((d_o, v, "d_o"), (dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv"), (dbeta, beta, "dbeta")):
+        _want(t, like.shape, name)
+    _want(ds_final, (B, H, d_k, d_v), "ds_final")
+    _want(ds0, (B, H, d_k, d_v), "ds0")
+    nws = _ws(workspace, dev)
     return PreparedCall(lib().efla_chunk_bwd,
                         (_p(q), _p(k), _p(v), _p(beta), _p(s0), _p(d_o), _p(ds_final), _p(dq), _p(dk), _p(dv),
                          _p(dbeta), _p(ds0), B, H, L, d_k, d_v, chunk, _code(q.dtype), _rule(rule), _p(workspace),
-                         workspace.numel(), _stream(dev)),
+                         nws, _stream(dev)),
                         "efla_chunk_bwd", (q, k, v, beta, d_o, s0, ds_final, dq, dk, dv, dbeta, ds0, workspace))
 
 
@@ -446,6 +515,10 @@ def prepare_step(q, k, v, beta, state, o, rule: str = "exact"):
     _dev(state, dtype=torch.float32)
     N, H, dk = k.shape
     dv = v.shape[-1]
+    if q.shape != k.shape or v.shape[:2] != (N, H) or beta.shape != (N, H):
+        raise ValueError("expected q, k [N,H,dk], v [N,H,dv], beta [N,H]")
+    _want(state, (N, H, dk, dv), "state")
+    _want(o, (N, H, dv), "o")
     return PreparedCall(lib().efla_step_rule,
                         (_p(q), _p(k), _p(v), _p(beta), _p(state), _p(o), N, H, dk, dv,
                          _code(q.dtype), _rule(rule), _stream(dev)),

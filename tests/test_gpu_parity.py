@@ -440,3 +440,37 @@ def test_full_size_workloads(name):
     w, inp = _gen(name)
     _say(f"[parity] {name}: B={w.B} H={w.H} L={w.L} dk={w.dk} dv={w.dv} chunk={w.chunk}")
     _check_forward(inp, w.chunk, name)
+
+
+@pytest.mark.parametrize("dt,impl", [("bf16", "roles"), ("bf16", "tile"), ("bf16", "generic"), ("f32", "generic")])
+def test_state_updated_in_place(dt, impl, monkeypatch):
+    """s_final may alias s0 (the header's in-place state update): every
+    workgroup reads its block of s0 before it writes the same block, so the
+    aliased call gives the bits of the separate one, on every kernel path and
+    on the packed and segmented entry points."""
+    if impl != "roles":
+        monkeypatch.setenv("EFLA_RECURRENCE_IMPL", impl)
+    w, inp = _gen("shape_340m", dtype=dt, B=2, H=3, L=200, seed=97)
+    q, k, v, beta, s0 = inp["q"], inp["k"], inp["v"], inp["beta"], inp["s0"]
+    o_ref, s_ref = efla.efla_chunk_fwd(q, k, v, beta, s0, chunk=64)
+    st = s0.clone()
+    o_in, _ = efla.efla_chunk_fwd(q, k, v, beta, st, chunk=64, s_final=st)
+    torch.cuda.synchronize()
+    assert torch.equal(o_in, o_ref) and torch.equal(st, s_ref)
+    ro, rs = oracle_forward(inp)
+    assert normwise(to_f64(st), rs) <= TOL[dt]["s"]
+    # segmented: the combine step reads s0 before writing s_final
+    st = s0.clone()
+    o_sg, _ = efla.efla_chunk_fwd_segmented(q, k, v, beta, st, chunk=64, segments=3, s_final=st)
+    torch.cuda.synchronize()
+    assert normwise(to_f64(st), rs) <= TOL[dt]["s"] and normwise(to_f64(o_sg), ro) <= TOL[dt]["o"]
+    # packed batch of the same sequences, state per sequence updated in place
+    B, L = q.shape[:2]
+    pk = {n: inp[n].reshape(B * L, *inp[n].shape[2:]).contiguous() for n in ("q", "k", "v", "beta")}
+    cu = torch.arange(0, B * L + 1, L, dtype=torch.int32, device=q.device)
+    o_vr, s_vr = efla.efla_chunk_fwd_varlen(pk["q"], pk["k"], pk["v"], pk["beta"], cu, s0, chunk=64)
+    st = s0.clone()
+    o_vl, _ = efla.efla_chunk_fwd_varlen(pk["q"], pk["k"], pk["v"], pk["beta"], cu, st, chunk=64, s_final=st)
+    torch.cuda.synchronize()
+    assert torch.equal(st, s_vr) and torch.equal(o_vl, o_vr)
+    assert normwise(to_f64(st), rs) <= TOL[dt]["s"]
