@@ -76,6 +76,7 @@ def parse_args():
 # The sources the forward kernels (UT transform and recurrence), the decode
 # step and their launches are built from.
 FWD_SOURCES = ("api.hip", "common.h", "launchers.h", "lds_ring.h", "recurrence_roles.h", "chunk_bf16_roles.hip",
+               "recurrence_split.h", "chunk_bf16_split.hip",
                "ut_wave.h", "ut_bf16.hip", "step_kernels.hip")
 
 

@@ -53,12 +53,13 @@ int choose_value_block(efla_dtype dt, int d_v) {
   return d_v >= 32 ? 32 : 16;
 }
 
-// Which recurrence kernel runs for given sizes.  bf16: one role per
-// wavefront (recurrence_roles.h) where it applies, else the generic kernel;
-// fp32 always takes the generic kernel.  EFLA_RECURRENCE_IMPL=tile|generic
-// selects the one-wavefront-per-tile kernel (recurrence_tile.h) or the generic
-// one for comparisons (falling through where the choice does not apply).
-enum class Rec { kGeneric, kTile, kRoles };
+// Which recurrence kernel runs for given sizes.  bf16: the nine-wavefront
+// split kernel (recurrence_split.h) where it applies, else one role per
+// wavefront (recurrence_roles.h), else the generic kernel; fp32 always takes
+// the generic kernel.  EFLA_RECURRENCE_IMPL=roles|tile|generic selects the
+// role kernel, the one-wavefront-per-tile kernel (recurrence_tile.h) or the
+// generic one for comparisons (falling through where the choice does not apply).
+enum class Rec { kGeneric, kTile, kRoles, kSplit };
 struct RecChoice {
   Rec kind;
   int bv;
@@ -69,6 +70,8 @@ RecChoice choose_recurrence(efla_dtype dt, int d_k, int d_v, int chunk) {
   const char* impl = getenv("EFLA_RECURRENCE_IMPL");
   const bool generic = impl && strcmp(impl, "generic") == 0, tile = impl && strcmp(impl, "tile") == 0;
   if (generic) return {Rec::kGeneric, bv};
+  const bool roles = impl && strcmp(impl, "roles") == 0;
+  if (!tile && !roles && efla::recurrence_split_supported(d_k, chunk, bv)) return {Rec::kSplit, bv};
   if (!tile && efla::recurrence_roles_supported(d_k, chunk, bv)) return {Rec::kRoles, bv};
   if (efla::recurrence_tile_supported(d_k, chunk, bv)) return {Rec::kTile, bv};
   return {Rec::kGeneric, bv};
@@ -113,7 +116,10 @@ efla_status launch_rec(const void* q, const void* k, const void* v, const float*
     s0 = nullptr;
   }
   RecChoice rc = choose_recurrence(dtype, d_k, d_v, chunk);
-  if (rc.kind == Rec::kTile && (cu != nullptr || trans || o == nullptr))
+  // the split kernel has the forward instance only; the tile kernel takes
+  // dense forward passes only
+  if ((rc.kind == Rec::kTile && cu != nullptr) || ((rc.kind == Rec::kTile || rc.kind == Rec::kSplit) &&
+                                                   (trans || o == nullptr)))
     rc.kind = efla::recurrence_roles_supported(d_k, chunk, rc.bv) ? Rec::kRoles : Rec::kGeneric;
   if (dtype == EFLA_BF16) {
     const auto* qb = static_cast<const uint16_t*>(q);
@@ -122,6 +128,9 @@ efla_status launch_rec(const void* q, const void* k, const void* v, const float*
     const auto* tb = static_cast<const uint16_t*>(workspace);
     auto* ob = static_cast<uint16_t*>(o);
     switch (rc.kind) {
+      case Rec::kSplit:
+        return from_hip(efla::launch_recurrence_split_bf16(qb, kb, vb, tb, s0, ob, s_final, B, H, L, d_k, d_v,
+                                                           chunk, rc.bv, cu, N, order, s));
       case Rec::kRoles:
         return from_hip(efla::launch_recurrence_roles_bf16(qb, kb, vb, tb, s0, ob, s_final, B, H, L, d_k, d_v,
                                                            chunk, rc.bv, cu, N, s, nullptr, trans, order));
@@ -226,6 +235,7 @@ efla_status efla_chunk_recurrence(const void* q, const void* k, const void* v, c
 const char* efla_chunk_recurrence_kernel(int d_k, int d_v, int chunk, efla_dtype dtype) {
   if (!valid_dtype(dtype) || !valid_dim(d_k) || !valid_dim(d_v) || !valid_chunk(chunk)) return "unsupported";
   switch (choose_recurrence(dtype, d_k, d_v, chunk).kind) {
+    case Rec::kSplit: return "recurrence_split_kernel";
     case Rec::kRoles: return "recurrence_roles_kernel";
     case Rec::kTile: return "recurrence_tile_kernel";
     case Rec::kGeneric: break;

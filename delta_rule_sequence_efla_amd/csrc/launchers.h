@@ -56,6 +56,15 @@ hipError_t launch_recurrence_roles_bf16(const uint16_t* q, const uint16_t* k, co
                                         const int32_t* cu, int N, hipStream_t s, uint16_t* states = nullptr,
                                         bool trans = false, const int32_t* order = nullptr);
 
+// bf16 recurrence with each chunk's work spread over nine wavefronts
+// (recurrence_split.h): d_k in {64, 128}, chunk 64, value blocks of 32;
+// forward instance only (output and final state), dense or packed batches.
+bool recurrence_split_supported(int DK, int C, int BV);
+hipError_t launch_recurrence_split_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                        const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
+                                        int B, int H, int64_t L, int DK, int DV, int C, int BV,
+                                        const int32_t* cu, int N, const int32_t* order, hipStream_t s);
+
 // bf16 UT transform with one wavefront per chunk (ut_wave.h); d_k in
 // {32, 64, 128}, chunk in {32, 64}.
 bool ut_wave_bf16_supported(int DK, int C);

@@ -44,7 +44,9 @@ def test_recurrence_kernel_names():
     """The kernel-name query follows the dispatch rule and launches nothing."""
     import torch
     name = efla.efla_chunk_recurrence_kernel
-    assert name(128, 128, 64, torch.bfloat16) == "recurrence_roles_kernel"
+    assert name(128, 128, 64, torch.bfloat16) == "recurrence_split_kernel"
+    assert name(64, 64, 64, torch.bfloat16) == "recurrence_split_kernel"
+    assert name(128, 128, 32, torch.bfloat16) == "recurrence_roles_kernel"  # chunk 32
     assert name(128, 16, 64, torch.bfloat16) == "recurrence_roles_kernel"   # one 16-column tile
     assert name(16, 64, 16, torch.bfloat16) == "recurrence_kernel"       # d_k 16, chunk 16
     assert name(128, 128, 64, torch.float32) == "recurrence_kernel"

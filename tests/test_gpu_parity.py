@@ -115,9 +115,9 @@ def test_tiny_fp32_workload():
     _check_forward(inp, w.chunk, "tiny_fp32")
 
 
-@pytest.mark.parametrize("impl", ["roles", "tile", "generic"])
+@pytest.mark.parametrize("impl", ["split", "roles", "tile", "generic"])
 @pytest.mark.parametrize("bv", ["16", "32", "64"])
-@pytest.mark.parametrize("dk,chunk", [(128, 64), (64, 32), (32, 64)])
+@pytest.mark.parametrize("dk,chunk", [(128, 64), (64, 64), (64, 32), (32, 64)])
 def test_value_block_widths_agree(bv, impl, dk, chunk, monkeypatch):
     """Every value-block width and every bf16 recurrence kernel give oracle
     parity; these are launch-shape choices, not different computations (a
@@ -246,7 +246,7 @@ def test_chunk_fwd_euler_small_shapes(dt, dk, dv, chunk, L):
 
 
 @pytest.mark.parametrize("ut", ["wave", "workgroup"])
-@pytest.mark.parametrize("impl", ["roles", "tile", "generic"])
+@pytest.mark.parametrize("impl", ["split", "roles", "tile", "generic"])
 def test_euler_every_bf16_kernel(ut, impl, monkeypatch):
     monkeypatch.setenv("EFLA_UT_IMPL", ut)
     monkeypatch.setenv("EFLA_RECURRENCE_IMPL", impl)
@@ -442,14 +442,14 @@ def test_full_size_workloads(name):
     _check_forward(inp, w.chunk, name)
 
 
-@pytest.mark.parametrize("dt,impl", [("bf16", "roles"), ("bf16", "tile"), ("bf16", "generic"), ("f32", "generic")])
+@pytest.mark.parametrize("dt,impl", [("bf16", "split"), ("bf16", "roles"), ("bf16", "tile"), ("bf16", "generic"),
+                                     ("f32", "generic")])
 def test_state_updated_in_place(dt, impl, monkeypatch):
     """s_final may alias s0 (the header's in-place state update): every
     workgroup reads its block of s0 before it writes the same block, so the
     aliased call gives the bits of the separate one, on every kernel path and
     on the packed and segmented entry points."""
-    if impl != "roles":
-        monkeypatch.setenv("EFLA_RECURRENCE_IMPL", impl)
+    monkeypatch.setenv("EFLA_RECURRENCE_IMPL", impl)
     w, inp = _gen("shape_340m", dtype=dt, B=2, H=3, L=200, seed=97)
     q, k, v, beta, s0 = inp["q"], inp["k"], inp["v"], inp["beta"], inp["s0"]
     o_ref, s_ref = efla.efla_chunk_fwd(q, k, v, beta, s0, chunk=64)

@@ -39,6 +39,8 @@ CASES = [
     # dtype, dk, dv, chunk, implementation
     ("f32", 64, 32, 32, None),
     ("f32", 16, 16, 16, None),
+    ("bf16", 128, 128, 64, "split"),
+    ("bf16", 64, 64, 64, "split"),
     ("bf16", 128, 128, 64, "roles"),
     ("bf16", 128, 128, 64, "generic"),
     ("bf16", 64, 128, 32, "roles"),
