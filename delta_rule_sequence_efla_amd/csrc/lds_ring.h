@@ -224,6 +224,27 @@ struct ChunkDma {
     else if (j < 2 * PQ + PT) tt.template issue<false>(j - 2 * PQ, slot + 2 * TOFF, src.t, C);
     else tv.template issue<RAGGED>(j - 2 * PQ - PT, slot + 2 * VOFF, src.v, src.valid);
   }
+  // Transfers of tile set `set` (0: Q and T, 1: K and V) when two waves
+  // share the chunk's transfers, each issuing whole tiles.
+  static constexpr int SET0 = PQ + PT, SET1 = PQ + PV;
+  __device__ __forceinline__ static constexpr int set_instr(int set, int i) {
+    return set == 0 ? (i < PQ ? i : PQ + i) : (i < PQ ? PQ + i : PQ + PT + i);
+  }
+  // Piece `part` of `parts` (an even split of set `set`'s transfers) into the
+  // ring slot at LDS byte address `slot`; src pointers are wave-uniform.
+  template <int SET>
+  __device__ __forceinline__ void issue_set(int part, int parts, uint32_t slot, const Src& src) const {
+    constexpr int N = SET == 0 ? SET0 : SET1;
+    if (src.valid == C) {
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+        if (i >= part * N / parts && i < (part + 1) * N / parts) issue<false>(set_instr(SET, i), slot, src);
+    } else {
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+        if (i >= part * N / parts && i < (part + 1) * N / parts) issue<true>(set_instr(SET, i), slot, src);
+    }
+  }
   // Piece `part` of `parts` (an even split of the COUNT instructions) into
   // the ring slot at LDS byte address `slot`; src pointers are wave-uniform.
   __device__ __forceinline__ void issue_part(int part, int parts, uint32_t slot, const Src& src) const {

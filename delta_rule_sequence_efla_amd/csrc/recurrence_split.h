@@ -40,7 +40,7 @@
 
 namespace efla {
 
-template <int DK, int C, int BV>
+template <int DK, int C, int BV, int NDMA = 1>
 struct SplitShape {
   static_assert(C == 64 && BV == 32 && (DK == 64 || DK == 128), "shapes of the split recurrence");
   static constexpr int NT = BV / 16;  // state tiles of the workgroup
@@ -53,20 +53,21 @@ struct SplitShape {
   using Dma = ChunkDma<DK, C, BV, 1, true>;
   static constexpr int DMA_COUNT = Dma::COUNT;
   // roles; consecutive waves go to consecutive SIMDs, so each SIMD holds one
-  // Y or S wave and the lighter roles fill in
+  // Y or S wave and the lighter roles fill in.  With NDMA = 2 two DMA waves
+  // share each chunk's transfers, one streaming Q and T, the other K and V.
   static constexpr int kP0 = 0, kY0 = 1, kS0 = 3, kO0 = 5, kP1 = 7, kDma = 8;
-  static constexpr int NWAVES = 9, THREADS = NWAVES * kWave;
+  static constexpr int NWAVES = 8 + NDMA, THREADS = NWAVES * kWave;
 };
 
 inline bool split_supported(int DK, int C, int BV) { return C == 64 && BV == 32 && (DK == 64 || DK == 128); }
 
-template <int DK, int C, int BV>
-__global__ __launch_bounds__(576) void recurrence_split_kernel(
+template <int DK, int C, int BV, int NDMA>
+__global__ __launch_bounds__(64 * (8 + NDMA)) void recurrence_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ tws, const float* s0, uint16_t* __restrict__ o, float* sfin, int H, int64_t L,
     int NC, int DV, int NVB, int remap, const int32_t* __restrict__ cu, const int32_t* __restrict__ order,
     int nseq) {
-  using S = SplitShape<DK, C, BV>;
+  using S = SplitShape<DK, C, BV, NDMA>;
   constexpr int NT = S::NT, NRT = S::NRT, NKU_D = S::NKU_D, NKU_C = S::NKU_C, KH = S::KH, NPF = S::NPF;
   __shared__ __align__(1024) uint16_t ring[3 * S::SLOT];  // three chunk slots of 44 KiB
   uint16_t* const slot0 = ring;
@@ -101,9 +102,11 @@ __global__ __launch_bounds__(576) void recurrence_split_kernel(
   };
   // Output of chunk n from the staging tile: each output wave stores half of
   // the rows, one 16-byte piece per lane, so every row's 64 bytes leave in
-  // one instruction.  (Eight 32-byte pieces of each 256-byte row of o, from
-  // eight wavefronts, slowed the whole pass and most of all the heads whose
-  // rows sit at 256 mod 1024 bytes.)
+  // one instruction, as nontemporal stores.  (Eight 32-byte pieces of each
+  // 256-byte row of o, from eight wavefronts, slowed the whole pass and most
+  // of all the heads whose rows sit at 256 mod 1024 bytes; with ordinary
+  // stores of whole 64-byte pieces those heads still trailed the others by
+  // ~15 %, with nontemporal ones they do not.)
   auto store_staged = [&](int n, int half) {
     const int valid = chunk_valid(n);
     const int64_t row0 = row_of(n);
@@ -111,7 +114,7 @@ __global__ __launch_bounds__(576) void recurrence_split_kernel(
     for (int i = 0; i < C / 32; ++i) {
       const int r = 32 * half + 16 * i + (lane >> 2), piece = lane & 3;
       const u32x4 val = *reinterpret_cast<const u32x4*>(&O_st[r][8 * piece]);
-      if (r < valid) *reinterpret_cast<u32x4*>(o + (row0 + int64_t(r) * H) * DV + v0 + 8 * piece) = val;
+      if (r < valid) __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(o + (row0 + int64_t(r) * H) * DV + v0 + 8 * piece));
     }
   };
   // Steps of three chunks keep the ring slots compile-time addresses.
@@ -123,7 +126,7 @@ __global__ __launch_bounds__(576) void recurrence_split_kernel(
     }
   };
 
-  if (role == S::kDma) {
+  auto dma_role = [&](auto setc) {
     // ---------------------------------------------------------------- DMA
     // Every reader of chunk n is done with its slot by barrier B of step n
     // (the next chunk's fragments are read after that barrier, K^T and the
@@ -131,10 +134,14 @@ __global__ __launch_bounds__(576) void recurrence_split_kernel(
     // away: half after barrier B of step n, half after barrier A of step n+1,
     // and it is first needed after barrier B of step n+2 -- one and a half to
     // two chunk periods to land.  At most 63 transfers can be outstanding per
-    // wave, so the waits are expressed against one chunk's 44 (chunk n+1 is
-    // complete once only chunk n+2's transfers remain).  The DMA wave writes
-    // LDS only through global_load_lds, whose completion it tracks with
-    // vmcnt; it passes the barriers without an lgkmcnt drain.
+    // wave, so the waits are expressed against one chunk's (chunk n+1 is
+    // complete once only chunk n+2's transfers remain).  SET < 0: this wave
+    // issues every transfer; else transfer set SET of two.  The DMA waves
+    // write LDS only through global_load_lds, whose completion they track
+    // with vmcnt; they pass the barriers without an lgkmcnt drain.
+    constexpr int SET = decltype(setc)::value;
+    constexpr int D = SET < 0 ? S::DMA_COUNT : SET == 0 ? S::Dma::SET0 : S::Dma::SET1;
+    static_assert(D < 64, "one chunk's transfers fit the vmcnt counter");
     typename S::Dma dma;
     dma.init(int64_t(H) * DK, int64_t(H) * DV, lane, 0);
     auto issue = [&](int m, int part, int parts) {
@@ -143,10 +150,10 @@ __global__ __launch_bounds__(576) void recurrence_split_kernel(
       const typename S::Dma::Src src{(U)uniform_ptr(q + r0 * DK), (U)uniform_ptr(k + r0 * DK),
                                      (U)uniform_ptr(tws + (sp.slot0 + m) * C * C),
                                      (U)uniform_ptr(v + r0 * DV + v0), chunk_valid(m)};
-      dma.issue_part(part, parts, lds_addr_of(ring + (m % 3) * S::SLOT), src);
+      const uint32_t addr = lds_addr_of(ring + (m % 3) * S::SLOT);
+      if constexpr (SET < 0) dma.issue_part(part, parts, addr, src);
+      else dma.template issue_set<SET>(part, parts, addr, src);
     };
-    constexpr int D = S::DMA_COUNT;
-    static_assert(D < 64, "one chunk's transfers fit the vmcnt counter");
     if (nc > 0) issue(0, 0, 1);
     if (nc > 1) {
       issue(1, 0, 1);
@@ -164,6 +171,12 @@ __global__ __launch_bounds__(576) void recurrence_split_kernel(
       if (n + 3 < nc) issue(n + 3, 0, 2);
     }
     wait_vmcnt<0>();
+  };
+
+  if (role >= S::kDma) {
+    if constexpr (NDMA == 1) dma_role(std::integral_constant<int, -1>{});
+    else if (role == S::kDma) dma_role(std::integral_constant<int, 0>{});
+    else dma_role(std::integral_constant<int, 1>{});
   } else if (role == S::kY0 || role == S::kY0 + 1) {
     // ----------------------------------------------------------------- Y
     const int ct = role - S::kY0;
@@ -383,7 +396,7 @@ __global__ __launch_bounds__(576) void recurrence_split_kernel(
   if (nc > 0 && (role == S::kO0 || role == S::kO0 + 1)) store_staged(nc - 1, role - S::kO0);
 }
 
-template <int DK, int C, int BV>
+template <int DK, int C, int BV, int NDMA>
 hipError_t recurrence_split_launch_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                         const uint16_t* tws, const float* s0, uint16_t* o, float* sfin, int B,
                                         int H, int64_t L, int DV, const int32_t* cu, int N, const int32_t* order,
@@ -395,19 +408,26 @@ hipError_t recurrence_split_launch_impl(const uint16_t* q, const uint16_t* k, co
   if (nwg == 0) return hipSuccess;
   if (cu == nullptr) order = nullptr;  // dense batches keep their order
   const int remap = (BH % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((recurrence_split_kernel<DK, C, BV>), dim3(unsigned(nwg)),
-                     dim3(unsigned(SplitShape<DK, C, BV>::THREADS)), 0, stream, q, k, v, tws, s0, o, sfin, H, L, NC,
+  hipLaunchKernelGGL((recurrence_split_kernel<DK, C, BV, NDMA>), dim3(unsigned(nwg)),
+                     dim3(unsigned(SplitShape<DK, C, BV, NDMA>::THREADS)), 0, stream, q, k, v, tws, s0, o, sfin, H, L, NC,
                      DV, NVB, remap, cu, order, N);
   return hipGetLastError();
 }
 
+// ndma: DMA wavefronts per workgroup (1 or 2).
 inline hipError_t launch_recurrence_split(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                           const uint16_t* tws, const float* s0, uint16_t* o, float* sfin, int B,
                                           int H, int64_t L, int DK, int DV, int C, int BV, const int32_t* cu, int N,
-                                          const int32_t* order, hipStream_t s) {
+                                          const int32_t* order, int ndma, hipStream_t s) {
   if (C == 64 && BV == 32) {
-    if (DK == 64) return recurrence_split_launch_impl<64, 64, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, order, s);
-    if (DK == 128) return recurrence_split_launch_impl<128, 64, 32>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, order, s);
+    if (DK == 64) {
+      if (ndma == 2) return recurrence_split_launch_impl<64, 64, 32, 2>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, order, s);
+      return recurrence_split_launch_impl<64, 64, 32, 1>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, order, s);
+    }
+    if (DK == 128) {
+      if (ndma == 2) return recurrence_split_launch_impl<128, 64, 32, 2>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, order, s);
+      return recurrence_split_launch_impl<128, 64, 32, 1>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, order, s);
+    }
   }
   return hipErrorInvalidValue;
 }

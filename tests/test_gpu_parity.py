@@ -474,3 +474,15 @@ def test_state_updated_in_place(dt, impl, monkeypatch):
     torch.cuda.synchronize()
     assert torch.equal(st, s_vr) and torch.equal(o_vl, o_vr)
     assert normwise(to_f64(st), rs) <= TOL[dt]["s"]
+
+
+@pytest.mark.parametrize("dk", [64, 128])
+def test_split_kernel_dma_waves_agree(dk, monkeypatch):
+    """The split recurrence with one or two DMA wavefronts: the same
+    arithmetic, so the same bits, and oracle parity (ragged tail included)."""
+    w, inp = _gen("shape_1p3b", B=2, H=8, L=64 * 7 + 29, dk=dk, dv=dk, seed=98)
+    outs = {}
+    for nd in ("1", "2"):
+        monkeypatch.setenv("EFLA_SPLIT_DMA", nd)
+        outs[nd] = _check_forward(inp, 64, f"split kernel, {nd} DMA wave(s), dk {dk}")
+    assert torch.equal(outs["1"][0], outs["2"][0]) and torch.equal(outs["1"][1], outs["2"][1])
