@@ -4,6 +4,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "efla.h"
 #include "launchers.h"
 
@@ -149,6 +151,31 @@ efla_status launch_rec(const void* q, const void* k, const void* v, const float*
       rc.bv, cu, N, s, int(trans), order));
 }
 
+// Fixed scratch of efla_chunk_fwd_noalloc: the per-chunk T matrices of one
+// call.  Each GPU the library runs on holds its own copy from the time the
+// code object is loaded there until the process ends.  In host code the name
+// is only a stand-in; the device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[EFLA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+efla_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return EFLA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return EFLA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return EFLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -160,6 +187,8 @@ const char* efla_status_string(efla_status s) {
     case EFLA_ERR_UNSUPPORTED: return "EFLA_ERR_UNSUPPORTED: d_k/d_v must be 16/32/64/128, chunk 16/32/64";
     case EFLA_ERR_WORKSPACE: return "EFLA_ERR_WORKSPACE: workspace missing or too small";
     case EFLA_ERR_HIP: return "EFLA_ERR_HIP: a HIP launch or runtime call failed";
+    case EFLA_ERR_SCRATCH:
+      return "EFLA_ERR_SCRATCH: the problem needs more than the library's fixed scratch (EFLA_NOALLOC_SCRATCH_BYTES)";
   }
   return "EFLA_ERR_UNKNOWN";
 }
@@ -269,6 +298,29 @@ efla_status efla_chunk_fwd_rule(const void* q, const void* k, const void* v, con
   }
   return efla_chunk_recurrence(q, k, v, s0, o, s_final, B, H, L, d_k, d_v, chunk, dtype, workspace,
                                workspace_bytes, stream);
+}
+
+efla_status efla_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* beta,
+                                   const float* s0, void* o, float* s_final, int B, int H, int64_t L, int d_k,
+                                   int d_v, int chunk, efla_dtype dtype, efla_rule rule, void* stream) {
+  if (!valid_rule(rule)) return EFLA_ERR_INVALID_ARG;
+  const efla_status st = check_chunk_shape(B, H, L, d_k, d_v, chunk, dtype);
+  if (st != EFLA_OK) return st;
+  const size_t need = efla_chunk_fwd_workspace_size(B, H, L, d_k, d_v, chunk, dtype);
+  if (need > EFLA_NOALLOC_SCRATCH_BYTES) return EFLA_ERR_SCRATCH;  // before any HIP call
+  if (L > 0) {
+    if (q == nullptr || k == nullptr || v == nullptr || beta == nullptr || o == nullptr)
+      return EFLA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return EFLA_ERR_INVALID_ARG;
+  } else if (s_final == nullptr) {
+    return EFLA_OK;
+  }
+  void* ws = nullptr;
+  const efla_status sp = scratch_on_current_device(&ws);
+  if (sp != EFLA_OK) return sp;
+  // the same two launches as efla_chunk_fwd_rule, with the scratch as workspace
+  return efla_chunk_fwd_rule(q, k, v, beta, s0, o, s_final, B, H, L, d_k, d_v, chunk, dtype, rule, ws,
+                             EFLA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 efla_status efla_step(const void* q, const void* k, const void* v, const void* beta, float* state, void* o,

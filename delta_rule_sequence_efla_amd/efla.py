@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(_HERE, "libefla.so")
 EFLA_F32, EFLA_BF16 = 0, 1
 _DTYPES = {torch.float32: EFLA_F32, torch.bfloat16: EFLA_BF16}
 _STATUS = {0: "EFLA_OK", 1: "EFLA_ERR_INVALID_ARG", 2: "EFLA_ERR_UNSUPPORTED",
-           3: "EFLA_ERR_WORKSPACE", 4: "EFLA_ERR_HIP"}
+           3: "EFLA_ERR_WORKSPACE", 4: "EFLA_ERR_HIP", 5: "EFLA_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 64 << 20   # EFLA_NOALLOC_SCRATCH_BYTES of include/efla.h
 
 _lib = None
 _vp, _i, _i64, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
@@ -80,6 +81,9 @@ def lib() -> ctypes.CDLL:
         L.efla_chunk_bwd.argtypes = [_vp] * 12 + [_i, _i, _i64, _i, _i, _i, _i, _i, _vp, _sz, _vp]
         L.efla_chunk_fwd_varlen_workspace_size.restype = _sz
         L.efla_chunk_fwd_varlen_workspace_size.argtypes = [_i, _i, _i64, _i, _i, _i, _i]
+        L.efla_chunk_fwd_noalloc.restype = _i
+        L.efla_chunk_fwd_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i64, _i, _i, _i,
+                                             _i, _i, _vp]
         L.efla_chunk_fwd_varlen.restype = _i
         L.efla_chunk_fwd_varlen.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i64, _i, _i,
                                             _i, _i, _i, _vp, _sz, _vp]
@@ -228,6 +232,26 @@ def efla_chunk_fwd(q, k, v, beta, s0=None, chunk: int = 64, o=None, s_final=None
         _check(lib().efla_chunk_fwd_rule(_p(q), _p(k), _p(v), _p(beta), _p(s0), _p(o), _p(s_final),
                                          B, H, L, dk, dv, chunk, _code(q.dtype), _rule(rule), _p(workspace),
                                          nws, _stream(dev)), "efla_chunk_fwd")
+    return o, s_final
+
+
+def efla_chunk_fwd_noalloc(q, k, v, beta, s0=None, chunk: int = 64, o=None, s_final=None,
+                           want_final: bool = True, rule: str = "exact"):
+    """efla_chunk_fwd with the library's fixed per-GPU scratch instead of a
+    workspace (no device allocation inside the call; o and s_final are
+    allocated here unless given).  Calls that overlap on one GPU race."""
+    dev = _dev(q, k, v, beta, o, dtype=q.dtype)
+    _dev(s0, s_final, dtype=torch.float32)
+    B, L, H, dk, dv = _chunk_shapes(q, k, v, beta, s0)
+    _fwd_outs(o, s_final, B, L, H, dk, dv, q.dtype, q)
+    if o is None:
+        o = torch.empty((B, L, H, dv), dtype=q.dtype, device=dev)
+    if s_final is None and want_final:
+        s_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib().efla_chunk_fwd_noalloc(_p(q), _p(k), _p(v), _p(beta), _p(s0), _p(o), _p(s_final),
+                                            B, H, L, dk, dv, chunk, _code(q.dtype), _rule(rule), _stream(dev)),
+               "efla_chunk_fwd_noalloc")
     return o, s_final
 
 

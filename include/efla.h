@@ -15,7 +15,9 @@
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
  *     allocates nothing and keeps no mutable global state; calls on different
- *     streams with disjoint outputs may run concurrently.
+ *     streams with disjoint outputs may run concurrently.  The one exception
+ *     is efla_chunk_fwd_noalloc, whose fixed scratch array (one per GPU) is
+ *     shared by all its calls on that GPU.
  *   - Layouts are dense row-major:
  *         q, k   [B, L, H, d_k]       v, o   [B, L, H, d_v]       beta [B, L, H]
  *         state  [B, H, d_k, d_v]  (float32; S[i][j], i = key dim, j = value dim)
@@ -50,7 +52,9 @@ typedef enum efla_status {
     EFLA_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad enum       */
     EFLA_ERR_UNSUPPORTED = 2, /* d_k / d_v / chunk outside the supported set  */
     EFLA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required   */
-    EFLA_ERR_HIP = 4          /* a HIP launch or runtime call failed          */
+    EFLA_ERR_HIP = 4,         /* a HIP launch or runtime call failed          */
+    EFLA_ERR_SCRATCH = 5      /* efla_chunk_fwd_noalloc: problem exceeds the  */
+                              /* library's fixed scratch                      */
 } efla_status;
 
 typedef enum efla_dtype {
@@ -137,6 +141,31 @@ efla_status efla_chunk_fwd_rule(const void *q, const void *k, const void *v, con
                                 int B, int H, int64_t L, int d_k, int d_v, int chunk,
                                 efla_dtype dtype, efla_rule rule, void *workspace,
                                 size_t workspace_bytes, void *stream);
+
+/*
+ * efla_chunk_fwd_noalloc -- efla_chunk_fwd_rule with no workspace argument,
+ * for callers that cannot allocate device memory around the call: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It calls no hipMalloc, hipFree or other allocating routine.  The per-chunk T
+ * matrices go to a fixed device array of EFLA_NOALLOC_SCRATCH_BYTES (64 MiB)
+ * inside the library, one copy per GPU, which each GPU holds from the time
+ * the library's code is loaded on it until the process ends; the first call
+ * on a device looks up that copy's address (with the device current) and
+ * keeps it.  Sizes whose efla_chunk_fwd_workspace_size(...) exceeds the array
+ * return EFLA_ERR_SCRATCH before anything is launched (B*H*ceil(L/chunk)
+ * chunks of chunk x chunk elements: 8192 chunks of 64 x 64 in bf16, e.g. the
+ * B=4, H=16, L=4096 layer twice over).  Every call on one GPU uses the same
+ * array and leaves its contents behind: calls that overlap in time on one GPU
+ * (on different streams, or from different threads) race and give undefined
+ * results -- serialize them.  Nothing in the array needs to start at zero:
+ * each call writes every scratch byte it reads.  Other arguments, errors and
+ * results as for efla_chunk_fwd_rule.
+ */
+#define EFLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+efla_status efla_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const void *beta,
+                                   const float *s0, void *o, float *s_final,
+                                   int B, int H, int64_t L, int d_k, int d_v, int chunk,
+                                   efla_dtype dtype, efla_rule rule, void *stream);
 
 /*
  * The two stages of efla_chunk_fwd, exposed so that each can be checked and

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     for code, prefix in [(0, "EFLA_OK"), (1, "EFLA_ERR_INVALID_ARG"), (2, "EFLA_ERR_UNSUPPORTED"),
-                         (3, "EFLA_ERR_WORKSPACE"), (4, "EFLA_ERR_HIP")]:
+                         (3, "EFLA_ERR_WORKSPACE"), (4, "EFLA_ERR_HIP"), (5, "EFLA_ERR_SCRATCH")]:
         assert efla.efla_status_string(code).startswith(prefix)
     assert efla.efla_status_string(99) == "EFLA_ERR_UNKNOWN"
 
@@ -213,3 +213,21 @@ def test_segmented_workspace_size_and_validation():
 
     assert call(seg=0) == 1 and call(rule=5) == 1 and call(p=nul) == 1 and call(p=fake + 8) == 1
     assert call() == 3 and call(ws=fake, wsb=64) == 3
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch():
+    """efla_chunk_fwd_noalloc checks the size against its fixed scratch before
+    any HIP call (so this runs without a GPU)."""
+    L = efla.lib()
+    nul, fake = None, ctypes.c_void_p(4096)
+    # 4 x 16 x 4096 tokens in chunks of 64, bf16: 32 MiB of T -> fits; 3x the batch -> 96 MiB does not
+    need = efla.efla_chunk_fwd_workspace_size(12, 16, 4096, 128, 128, 64, torch.bfloat16)
+    assert need > efla.NOALLOC_SCRATCH_BYTES
+    assert L.efla_chunk_fwd_noalloc(fake, fake, fake, fake, nul, fake, nul, 12, 16, 4096, 128, 128, 64, 1, 0,
+                                    nul) == 5
+    assert efla.efla_chunk_fwd_workspace_size(4, 16, 4096, 128, 128, 64, torch.bfloat16) <= efla.NOALLOC_SCRATCH_BYTES
+    # ordinary validation first: unsupported sizes, bad rule
+    assert L.efla_chunk_fwd_noalloc(nul, nul, nul, nul, nul, nul, nul, 1, 1, 64, 24, 16, 16, 0, 0, nul) == 2
+    assert L.efla_chunk_fwd_noalloc(nul, nul, nul, nul, nul, nul, nul, 1, 1, 64, 16, 16, 16, 0, 7, nul) == 1
+    # nothing to do is success without a launch
+    assert L.efla_chunk_fwd_noalloc(nul, nul, nul, nul, nul, nul, nul, 1, 1, 0, 16, 16, 16, 0, 0, nul) == 0
