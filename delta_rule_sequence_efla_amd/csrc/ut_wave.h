@@ -17,8 +17,12 @@
 //     (for lambda and the diagonal solves) and the tiles above the diagonal,
 //     which by symmetry are the transposes of the tiles below it.
 //   * The diagonal 16x16 blocks of X are solved by forward substitution, one
-//     lane per column, all blocks at once (through a small LDS copy of the
-//     diagonal G blocks, read as broadcasts).
+//     lane per column, all blocks at once, through a small LDS copy of the
+//     diagonal G blocks: each lane stores a row piece of its G tile as one
+//     16-byte write (G is symmetric, so the tile's column piece is a row
+//     piece), and the solve reads each row of G as 16-byte broadcasts.  A
+//     wavefront's LDS instructions cost tens of cycles each whatever their
+//     width, so the solve's reads were the transform's largest cost.
 //   * The blocks below the diagonal follow block by block,
 //         X_ij = -X_ii diag(a_i) sum_{j <= m < i} G_im X_mj,
 //     on fp32 16x16x4 matrix-core products.  In the kk-th of the four
@@ -26,7 +30,10 @@
 //     then the B operand is element kk of an accumulator tile as it stands,
 //     and the A operand is element kk of the accumulator tile of its
 //     transpose, so every product reads its operands from registers.
-//   * T is staged through LDS as bf16 and stored with 16-byte row writes.
+//   * Every block below the diagonal is also formed transposed (the same two
+//     operand tiles, swapped), so each lane holds four consecutive columns
+//     of a row of T: T is staged through LDS as bf16 with one 8-byte write
+//     per tile and stored with 16-byte row writes.
 #pragma once
 
 #include "common.h"
@@ -36,11 +43,16 @@ namespace efla {
 template <int DK, int C>
 struct UtWaveShape {
   static constexpr int NRT = C / 16, NKU = DK / 32;
-  static constexpr int GP = 17;                       // padded pitch of the 16x16 fp32 blocks
-  static constexpr int BLK = 16 * GP;                 // floats per block
-  static constexpr int TP = C + 8;                    // padded pitch of the bf16 T staging tile
-  static constexpr int SCRATCH = (2 * 4 * BLK * 4 > C * TP * 2) ? 2 * 4 * BLK * 4 : C * TP * 2;  // bytes
-  static constexpr int WAVES = 4;                     // chunks per workgroup
+  // diagonal G blocks, row-major 16 x 16 fp32; blocks 272 floats apart, so
+  // the four blocks' rows fall on different banks (broadcast reads)
+  static constexpr int GBLK = 272;
+  // diagonal X blocks, column-major, columns of 16 (+4) floats
+  static constexpr int XP = 20, XBLK = 16 * XP + 16;
+  static constexpr int GX = (4 * GBLK + 4 * XBLK) * 4;  // bytes of the two
+  static constexpr int TP = C + 8;                      // padded pitch of the bf16 T staging tile
+  static constexpr int XST = 32 * (C + 4) * 4;          // a 32-row fp32 block of X (backward instance)
+  static constexpr int SCRATCH = GX > C * TP * 2 ? (GX > XST ? GX : XST) : (C * TP * 2 > XST ? C * TP * 2 : XST);
+  static constexpr int WAVES = 4;                       // chunks per workgroup
 };
 
 // acc += A B over a 16-deep sum with fp32 16x16x4 products: At holds the
@@ -71,7 +83,7 @@ __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict
                                                       float* __restrict__ aout = nullptr,
                                                       float* __restrict__ pout = nullptr) {
   using S = UtWaveShape<DK, C>;
-  constexpr int NRT = S::NRT, NKU = S::NKU, GP = S::GP, BLK = S::BLK, TP = S::TP;
+  constexpr int NRT = S::NRT, NKU = S::NKU, GBLK = S::GBLK, XP = S::XP, XBLK = S::XBLK, TP = S::TP;
   __shared__ __align__(16) unsigned char scratch_all[S::WAVES][S::SCRATCH];
   __shared__ float a_all[S::WAVES][64];
 
@@ -95,8 +107,8 @@ __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict
   const int64_t t0 = int64_t(chunk) * C;
   const int valid = int(sp.len - t0 < C ? sp.len - t0 : C);
   const int64_t row0 = (sp.bos + t0) * H + h;
-  float* Gs = reinterpret_cast<float*>(scratch_all[w]);   // [4][16][GP] diagonal G blocks
-  float* Xs = Gs + 4 * BLK;                               // [4][16][GP] diagonal X blocks
+  float* Gs = reinterpret_cast<float*>(scratch_all[w]);   // [4][GBLK] diagonal G blocks, row-major
+  float* Xs = Gs + 4 * GBLK;                              // [4][XBLK] diagonal X blocks, column-major
   uint16_t* Ts = reinterpret_cast<uint16_t*>(scratch_all[w]);  // [C][TP] bf16 (after Gs/Xs are read)
   float* as = a_all[w];
 
@@ -178,61 +190,73 @@ __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict
     }
 
   // ---- lambda (the diagonal of G) and a ----------------------------------
+  // Gd[bb][qq] = G[16bb + 4g + qq][16bb + li] = G[16bb + li][16bb + 4g + qq]:
+  // row li, columns 4g .. 4g+3 of block bb, one 16-byte write
 #pragma unroll
-  for (int bb = 0; bb < NRT; ++bb) {
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      Gs[bb * BLK + (4 * g + qq) * GP + li] = Gd[bb][qq];
-    }
-  }
+  for (int bb = 0; bb < NRT; ++bb) *reinterpret_cast<f32x4*>(Gs + bb * GBLK + li * 16 + 4 * g) = Gd[bb];
   wave_lds_order();
   if (lane < C) {
-    const float lam = Gs[(lane >> 4) * BLK + (lane & 15) * GP + (lane & 15)];
+    const float lam = Gs[(lane >> 4) * GBLK + (lane & 15) * 17];
     as[lane] = (lane < valid) ? efla_alpha_rule(bt, lam, rule) : 0.0f;
   }
   wave_lds_order();
 
   // ---- diagonal blocks of X: forward substitution, lane = (block, column) --
   //   x_r = delta_rc - a_r * sum_{m < r} G_rm x_m
+  // Row r of G is read as ceil(r / 4) 16-byte broadcasts (the lanes of one
+  // block share each address); the sum runs as two partial sums.
   {
     const int bb = lane >> 4, c = lane & 15;
     if (bb < NRT) {
-      const float* Gb = Gs + bb * BLK;
-      const float* ab = as + 16 * bb;
+      const float* Gb = Gs + bb * GBLK;
+      f32x4 ab[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ab[j] = *reinterpret_cast<const f32x4*>(as + 16 * bb + 4 * j);
       float x[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float s = 0.0f;
+        float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
-        for (int m = 0; m < r; ++m) s = fmaf(Gb[r * GP + m], x[m], s);
-        x[r] = (r == c ? 1.0f : 0.0f) - ab[r] * s;
+        for (int j = 0; 4 * j < r; ++j) {
+          const f32x4 gr = *reinterpret_cast<const f32x4*>(Gb + r * 16 + 4 * j);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int m = 4 * j + e;
+            if (m < r) {
+              if (e & 1) s1 = fmaf(gr[e], x[m], s1);
+              else s0 = fmaf(gr[e], x[m], s0);
+            }
+          }
+        }
+        x[r] = (r == c ? 1.0f : 0.0f) - ab[r / 4][r % 4] * (s0 + s1);
       }
+      // column c of X_bb, four 16-byte writes
 #pragma unroll
-      for (int r = 0; r < 16; ++r) Xs[bb * BLK + r * GP + c] = x[r];
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<f32x4*>(Xs + bb * XBLK + c * XP + 4 * j) = f32x4{x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]};
     }
   }
   wave_lds_order();
   // X[i][j][qq] = X[16i + 4g + qq][16j + li] (accumulator tiles), XT[i] the tile of X_ii^T
   f32x4 X[NRT][NRT], XT[NRT];
 #pragma unroll
-  for (int bb = 0; bb < NRT; ++bb)
+  for (int bb = 0; bb < NRT; ++bb) {
+    X[bb][bb] = *reinterpret_cast<const f32x4*>(Xs + bb * XBLK + li * XP + 4 * g);
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      X[bb][bb][qq] = Xs[bb * BLK + (4 * g + qq) * GP + li];
-      XT[bb][qq] = Xs[bb * BLK + li * GP + 4 * g + qq];
-    }
-  // row coefficients a[16 i + 4 g + qq] and column coefficients a[16 j + li]
-  f32x4 arow[NRT];
-  float acol[NRT];
-#pragma unroll
-  for (int i = 0; i < NRT; ++i) {
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) arow[i][qq] = as[16 * i + 4 * g + qq];
-    acol[i] = as[16 * i + li];
+    for (int qq = 0; qq < 4; ++qq) XT[bb][qq] = Xs[bb * XBLK + (4 * g + qq) * XP + li];
   }
+  // coefficients a[16 i + 4 g + qq]
+  f32x4 arow[NRT];
+#pragma unroll
+  for (int i = 0; i < NRT; ++i) arow[i] = *reinterpret_cast<const f32x4*>(as + 16 * i + 4 * g);
   wave_lds_order();
 
   // ---- blocks below the diagonal ----------------------------------------
+  // XTo[i][j] is the tile of X_ij^T: with the operands of the last product
+  // swapped it comes out of the same tiles, (X_ii D_i R)^T = R^T D_i X_ii^T.
+  f32x4 XTo[NRT][NRT];
+#pragma unroll
+  for (int i = 0; i < NRT; ++i) XTo[i][i] = XT[i];
 #pragma unroll
   for (int i = 1; i < NRT; ++i)
 #pragma unroll
@@ -242,10 +266,14 @@ __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict
       for (int m = j; m < i; ++m) mma16_f32(R, Gu[i][m], X[m][j]);  // Gu[i][m] is the tile of G_im^T
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) R[qq] *= arow[i][qq];
-      f32x4 Y = zero4();
+      f32x4 Y = zero4(), YT = zero4();
       mma16_f32(Y, XT[i], R);
+      mma16_f32(YT, R, XT[i]);
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) X[i][j][qq] = -Y[qq];
+      for (int qq = 0; qq < 4; ++qq) {
+        X[i][j][qq] = -Y[qq];
+        XTo[i][j][qq] = -YT[qq];
+      }
     }
 
   if constexpr (BWD) {  // X (the diagonal blocks as solved, zeros above) and a
@@ -278,17 +306,19 @@ __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict
   }
 
   // ---- T = X diag(a): stage as bf16 rows, then 16-byte row stores --------
+  // lane (li, g) holds T[16 i + li][16 j + 4 g .. 4 g + 3] = X_ij^T[4 g + qq][li] a[16 j + 4 g + qq]
 #pragma unroll
   for (int i = 0; i < NRT; ++i)
 #pragma unroll
-    for (int j = 0; j < NRT; ++j)
+    for (int j = 0; j < NRT; ++j) {
+      bf16x4 tv;
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
-        const int r = 16 * i + 4 * g + qq, c = 16 * j + li;
-        float val = 0.0f;
-        if (j < i || (j == i && c <= r)) val = X[i][j][qq] * acol[j];
-        Ts[r * TP + c] = from_f32<uint16_t>(val);
+        const bool on = j < i || (j == i && 4 * g + qq <= li);
+        tv[qq] = static_cast<__bf16>(on ? XTo[i][j < i ? j : i][qq] * arow[j][qq] : 0.0f);
       }
+      *reinterpret_cast<bf16x4*>(Ts + (16 * i + li) * TP + 16 * j + 4 * g) = tv;
+    }
   wave_lds_order();
   uint16_t* out = tws + id * int64_t(C) * C;
   constexpr int VPR = C / 8;  // 16-byte vectors per row
