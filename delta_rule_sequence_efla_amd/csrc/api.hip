@@ -444,6 +444,13 @@ struct SegLayout {
   int64_t Ls;   // tokens per segment (a multiple of the chunk)
   size_t t, cu, m, n, sin, total;
 };
+// The state-only pass (N and M together) of the segment scan; EFLA_SEG_STATES=0
+// selects the two separate passes of the general recurrence instead.
+bool seg_states_fused(efla_dtype dtype, int d_k, int d_v, int chunk) {
+  const char* env = getenv("EFLA_SEG_STATES");
+  if (env != nullptr && env[0] == '0') return false;
+  return dtype == EFLA_BF16 && efla::recurrence_states_supported(d_k, d_v, chunk);
+}
 SegLayout seg_layout(int B, int H, int64_t L, int d_k, int d_v, int chunk, int segments, efla_dtype dt) {
   SegLayout w{};
   const int64_t nc = (L + chunk - 1) / chunk;
@@ -497,10 +504,17 @@ efla_status efla_chunk_fwd_segmented(const void* q, const void* k, const void* v
   efla_status e = from_hip(efla::launch_seg_offsets(cu, B, lay.G, L, lay.Ls, s));
   // T of every chunk of every segment (the packed view of the batch)
   if (e == EFLA_OK) e = launch_ut(k, beta, 1, H, T, d_k, chunk, dtype, rule, tws, cu, Ui, s);
-  // every segment from zero: N_g
-  if (e == EFLA_OK) e = launch_rec(q, k, v, nullptr, nullptr, Nf, 1, H, T, d_k, d_v, chunk, dtype, tws, cu, Ui, s);
-  // every segment's transition: M_g
-  if (e == EFLA_OK) e = launch_rec(q, k, v, nullptr, nullptr, M, 1, H, T, d_k, d_v, chunk, dtype, tws, cu, Ui, s, true);
+  // every segment from zero (N_g) and every segment's transition (M_g): in
+  // one state-only pass where the kernel exists, else one pass each
+  if (e == EFLA_OK && seg_states_fused(dtype, d_k, d_v, chunk)) {
+    e = from_hip(efla::launch_recurrence_states_bf16(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                                                     static_cast<const uint16_t*>(tws), Nf, M, 1, H, T, d_k, d_v,
+                                                     chunk, cu, Ui, s));
+  } else {
+    if (e == EFLA_OK) e = launch_rec(q, k, v, nullptr, nullptr, Nf, 1, H, T, d_k, d_v, chunk, dtype, tws, cu, Ui, s);
+    if (e == EFLA_OK)
+      e = launch_rec(q, k, v, nullptr, nullptr, M, 1, H, T, d_k, d_v, chunk, dtype, tws, cu, Ui, s, true);
+  }
   // incoming states along each sequence, and the final state
   if (e == EFLA_OK) e = from_hip(efla::launch_seg_combine(M, Nf, s0, Sin, s_final, B, H, lay.G, d_k, d_v, s));
   // every segment again from its incoming state, with output

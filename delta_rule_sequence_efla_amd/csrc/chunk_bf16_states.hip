@@ -1,0 +1,15 @@
+// chunk_bf16_states.hip -- bf16 instantiations of the state-only pass of the
+// segment scan (recurrence_states.h), in a translation unit of its own.
+#include "launchers.h"
+#include "recurrence_states.h"
+
+namespace efla {
+bool recurrence_states_supported(int DK, int DV, int C) { return states_supported(DK, C, 32) && DV % 32 == 0; }
+hipError_t launch_recurrence_states_bf16(const uint16_t* k, const uint16_t* v, const uint16_t* tws, float* nout,
+                                         float* mout, int B, int H, int64_t L, int DK, int DV, int C,
+                                         const int32_t* cu, int N, hipStream_t s) {
+  if (!recurrence_states_supported(DK, DV, C)) return hipErrorInvalidValue;
+  if (DK == 64) return recurrence_states_launch_impl<64, 64, 32>(k, v, tws, nout, mout, B, H, L, DV, cu, N, s);
+  return recurrence_states_launch_impl<128, 64, 32>(k, v, tws, nout, mout, B, H, L, DV, cu, N, s);
+}
+}  // namespace efla

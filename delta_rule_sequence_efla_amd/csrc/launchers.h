@@ -65,6 +65,15 @@ hipError_t launch_recurrence_split_bf16(const uint16_t* q, const uint16_t* k, co
                                         int B, int H, int64_t L, int DK, int DV, int C, int BV,
                                         const int32_t* cu, int N, const int32_t* order, hipStream_t s);
 
+// bf16 state-only pass of the segment scan (recurrence_states.h): every
+// sequence's N (state from zero, true values) into nout [N*H, DK, DV] and M
+// (state from the identity, V = 0) into mout [N*H, DK, DK], fp32, in one
+// pass; d_k in {64, 128}, d_v a multiple of 32, chunk 64.
+bool recurrence_states_supported(int DK, int DV, int C);
+hipError_t launch_recurrence_states_bf16(const uint16_t* k, const uint16_t* v, const uint16_t* tws, float* nout,
+                                         float* mout, int B, int H, int64_t L, int DK, int DV, int C,
+                                         const int32_t* cu, int N, hipStream_t s);
+
 // bf16 UT transform with one wavefront per chunk (ut_wave.h); d_k in
 // {32, 64, 128}, chunk in {32, 64}.
 bool ut_wave_bf16_supported(int DK, int C);

@@ -25,62 +25,69 @@ __global__ void seg_offsets_kernel(int32_t* cu, int B, int G, int64_t L, int64_t
   cu[i] = int32_t(off);
 }
 
-// One workgroup per (b, h, 16 value columns): S (d_k x 16, fp32, LDS) runs
-// along the segments of sequence b,
+// One workgroup per (b, h, 16 value columns); S (d_k x 16, fp32) runs along
+// the segments of sequence b,
 //     sin[u] = S;   S = M[u] S + N[u],   u = b G + g,
 // and ends in sfin[b, h] (NULL: not written).  M [U, H, d_k, d_k], N and sin
-// [U, H, d_k, d_v], fp32.
+// [U, H, d_k, d_v], fp32.  Wavefront w keeps key rows 16 w .. 16 w + 15 of S
+// in a matrix-core accumulator (lane (i, g): rows 16 w + 4 g + q, column
+// v0 + i) and forms those rows of M[u] S + N[u] with v_mfma_f32_16x16x4f32.
+// Product j of k-block kb takes, in lane group g, key index 16 kb + 4 g + j:
+// then a lane's A operands are four consecutive floats of one row of M (one
+// 16-byte load), and its B operands are element j of the accumulator that
+// the same lane of wavefront kb holds, read back through LDS.  M[u+1] and
+// N[u+1] are in flight while step u computes.
 template <int DK>
-__global__ __launch_bounds__(kThreads) void seg_combine_kernel(const float* __restrict__ M,
-                                                               const float* __restrict__ Nf,
-                                                               const float* s0,
-                                                               float* __restrict__ sin, float* sfin,
-                                                               int H, int G, int DV) {
-  constexpr int DKP = round_up(DK, 32), MP = DKP + 4, VP = 16 + 4;
-  __shared__ __align__(16) float Ms[DKP * MP];
-  __shared__ __align__(16) float Ss[DKP * VP];
+__global__ __launch_bounds__(DK * 4) void seg_combine_kernel(const float* __restrict__ M,
+                                                             const float* __restrict__ Nf, const float* s0,
+                                                             float* __restrict__ sin, float* sfin, int H, int G,
+                                                             int DV) {
+  constexpr int NKB = DK / 16;  // k-blocks, and wavefronts
+  __shared__ f32x4 Sb[2][NKB][kWave];
   const int nvb = DV / 16, x = blockIdx.x, bh = x / nvb, v0 = 16 * (x % nvb);
   const int b = bh / H, h = bh % H;
-  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), li = lane & 15, g = lane >> 4;
-  for (int i = tid; i < DKP * MP; i += kThreads) Ms[i] = 0.0f;
-  for (int i = tid; i < DKP * 16; i += kThreads) {
-    const int d = i / 16, c = i % 16;
-    Ss[d * VP + c] = (s0 != nullptr && d < DK) ? s0[(int64_t(bh) * DK + d) * DV + v0 + c] : 0.0f;
-  }
-  __syncthreads();
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, i = lane & 15, g = lane >> 4;
+  const int row = 16 * w + 4 * g;  // this lane's accumulator rows: row .. row + 3
+  f32x4 S;
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) S[qq] = s0 != nullptr ? s0[(int64_t(bh) * DK + row + qq) * DV + v0 + i] : 0.0f;
+  f32x4 Mr[NKB], Nr;
+  auto load = [&](int gi) {
+    const int64_t u = int64_t(b) * G + gi;
+    const float* Mu = M + (u * H + h) * DK * DK + (16 * w + i) * DK + 4 * g;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) Mr[kb] = *reinterpret_cast<const f32x4*>(Mu + 16 * kb);
+    const float* Nu = Nf + ((u * H + h) * DK + row) * DV + v0 + i;
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) Nr[qq] = Nu[qq * DV];
+  };
+  load(0);
   for (int gi = 0; gi < G; ++gi) {
     const int64_t u = int64_t(b) * G + gi;
-    const float* Mu = M + (u * H + h) * DK * DK;
-    const float* Nu = Nf + (u * H + h) * DK * DV;
-    float* su = sin + (u * H + h) * DK * DV;
-    for (int i = tid; i < DK * 16; i += kThreads) {
-      const int d = i / 16, c = i % 16;
-      su[d * DV + v0 + c] = Ss[d * VP + c];
-    }
-    for (int i = tid; i < DK * DK; i += kThreads) Ms[(i / DK) * MP + i % DK] = Mu[i];
-    __syncthreads();
-    f32x4 acc[DKP / 64 > 0 ? DKP / 64 : 1];
-    int nt = 0;
-    for (int dt = w; dt < DKP / 16; dt += 4, ++nt) {
-      acc[nt] = zero4();
-      tile_mma16<false, false>(acc[nt], Ms, MP, Ss, VP, 16 * dt, 0, DKP, li, g);
-    }
-    __syncthreads();  // every wave has read S
-    nt = 0;
-    for (int dt = w; dt < DKP / 16; dt += 4, ++nt) {
+    float* su = sin + ((u * H + h) * DK + row) * DV + v0 + i;
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int d = 16 * dt + 4 * g + qq;
-        Ss[d * VP + li] = d < DK ? acc[nt][qq] + Nu[d * DV + v0 + li] : 0.0f;
-      }
-    }
+    for (int qq = 0; qq < 4; ++qq) su[qq * DV] = S[qq];
+    // two buffers: a wavefront writes buffer (gi & 1) only after every
+    // wavefront has passed the barrier of step gi - 1, i.e. has finished
+    // reading that buffer in step gi - 2
+    Sb[gi & 1][w][lane] = S;
     __syncthreads();
+    f32x4 Mc[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) Mc[kb] = Mr[kb];
+    f32x4 acc = Nr;
+    if (gi + 1 < G) load(gi + 1);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const f32x4 sb = Sb[gi & 1][kb][lane];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Mc[kb][j], sb[j], acc, 0, 0, 0);
+    }
+    S = acc;
   }
   if (sfin != nullptr) {
-    for (int i = tid; i < DK * 16; i += kThreads) {
-      const int d = i / 16, c = i % 16;
-      sfin[(int64_t(bh) * DK + d) * DV + v0 + c] = Ss[d * VP + c];
-    }
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) sfin[(int64_t(bh) * DK + row + qq) * DV + v0 + i] = S[qq];
   }
 }
 
@@ -92,7 +99,7 @@ hipError_t launch_seg_offsets(int32_t* cu, int B, int G, int64_t L, int64_t Ls, 
 
 hipError_t launch_seg_combine(const float* M, const float* N, const float* s0, float* sin, float* sfin, int B, int H,
                               int G, int DK, int DV, hipStream_t s) {
-  const dim3 grid{unsigned(B * H * (DV / 16))}, block{unsigned(kThreads)};
+  const dim3 grid{unsigned(B * H * (DV / 16))}, block{unsigned(DK * 4)};
   switch (DK) {
     case 16: hipLaunchKernelGGL((seg_combine_kernel<16>), grid, block, 0, s, M, N, s0, sin, sfin, H, G, DV); break;
     case 32: hipLaunchKernelGGL((seg_combine_kernel<32>), grid, block, 0, s, M, N, s0, sin, sfin, H, G, DV); break;

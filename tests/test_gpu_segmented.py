@@ -31,7 +31,10 @@ CASES = [
     ("f32", 16, 16, 16, 200, 4),
     ("f32", 64, 32, 32, 300, 3),        # segments not dividing the chunk count, ragged tail
     ("f32", 128, 128, 64, 257, 5),      # more segments than chunks' worth: clamped
-    ("bf16", 128, 128, 64, 1000, 4),    # role kernels for all three passes
+    ("bf16", 128, 128, 64, 1000, 4),    # state-only pass for N and M, split kernel for the output
+    ("bf16", 64, 64, 64, 700, 3),       # state-only pass at d_k = 64
+    ("bf16", 128, 64, 64, 900, 5),      # d_v < d_k: the last column blocks write M only
+    ("bf16", 64, 128, 64, 450, 2),      # d_v > d_k: the last column blocks write N only
     ("bf16", 64, 128, 32, 513, 7),
     ("bf16", 16, 32, 16, 300, 3),       # generic kernels
     ("bf16", 32, 32, 64, 640, 10),      # one chunk per segment
@@ -57,6 +60,24 @@ def test_segmented_stiff_and_euler():
     assert normwise(to_f64(o), to_f64(o1)) <= 2e-2 and normwise(to_f64(sf), to_f64(s1)) <= 1e-2
     w = W.get("shape_340m", dk=64, dv=64, chunk=32)
     _check(W.generate(w, device="cuda", B=1, L=700, H=2, seed=962), 32, 6, "euler", rule="euler")
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (128, 64), (64, 128)])
+def test_state_only_pass_matches_two_passes(dk, dv, monkeypatch):
+    """N and M from the one state-only pass against the two passes of the
+    general recurrence (EFLA_SEG_STATES=0); both round S to bf16 for the
+    products, so they agree to well inside the forward tolerances."""
+    require_gpu()
+    w = W.get("shape_340m", dk=dk, dv=dv, chunk=64)
+    inp = W.generate(w, device="cuda", B=2, L=1300, H=3, seed=964 + dk + dv)
+    args = (inp["q"], inp["k"], inp["v"], inp["beta"], inp["s0"])
+    o1, s1 = efla.efla_chunk_fwd_segmented(*args, chunk=64, segments=5)
+    monkeypatch.setenv("EFLA_SEG_STATES", "0")
+    o2, s2 = efla.efla_chunk_fwd_segmented(*args, chunk=64, segments=5)
+    torch.cuda.synchronize()
+    eo, es = normwise(to_f64(o1), to_f64(o2)), normwise(to_f64(s1), to_f64(s2))
+    print(f"[seg] state-only vs two passes dk{dk} dv{dv}: o {eo:.3e}, S {es:.3e}", flush=True)
+    assert eo <= 5e-3 and es <= 5e-3
 
 
 def test_one_segment_is_the_plain_pass():
