@@ -16,12 +16,16 @@
 //     work, then forms S += K^T U' and publishes its rows of S as bf16
 //     operand fragments.  Splitting the key dimension (not the columns)
 //     halves each S wave's K^T reads.
-//   * output wave per tile: Z^T = S^T Q^T, then O^T = Z^T + U'^T P^T; the
-//     next chunk's Q fragments are read once its output is stored.
+//   * output wave per half of the chunk's rows, both tiles: Z^T = S^T Q^T,
+//     then O^T = Z^T + U'^T P^T for its 32 rows; the next chunk's Q
+//     fragments (of those rows only) are read once its output is staged.
+//     Split by rows, each reads half of Q (split by tiles, each read all).
 //   * two P waves: P = tril(Q K^T), row tiles 0-2 and row tile 3; half of the
 //     key dimension is summed in the phase before.
 //   * DMA wave: streams Q, K, T and V into a three-slot LDS ring two chunks
 //     ahead (as in recurrence_roles.h).
+// Wavefront w runs on SIMD w % 4; each SIMD holds one Y or S wave, and the
+// lighter roles fill in.
 // Two barriers per chunk:
 //   A (chunk n in LDS, S_n published)
 //     Y: products -> publish U'_n | S: read K^T_n | O: Z^T | P: finish P_n -> publish | DMA: half of chunk n+2
@@ -52,10 +56,15 @@ struct SplitShape {
   static constexpr int OP = BV + 8;  // pitch of the output staging rows (80 bytes: 8-byte writes conflict-free)
   using Dma = ChunkDma<DK, C, BV, 1, true>;
   static constexpr int DMA_COUNT = Dma::COUNT;
-  // roles; consecutive waves go to consecutive SIMDs, so each SIMD holds one
-  // Y or S wave and the lighter roles fill in.  With NDMA = 2 two DMA waves
-  // share each chunk's transfers, one streaming Q and T, the other K and V.
-  static constexpr int kP0 = 0, kY0 = 1, kS0 = 3, kO0 = 5, kP1 = 7, kDma = 8;
+  // roles by wavefront index (SIMD = index % 4):
+  //   SIMD 0: P rows 0-47 (0), S rows 64-127 (4), DMA (8)
+  //   SIMD 1: Y tile 0 (1), output rows 0-31 (5)
+  //   SIMD 2: Y tile 1 (2), output rows 32-63 (6)
+  //   SIMD 3: S rows 0-63 (3), P rows 48-63 (7)[, second DMA wave (9)]
+  // With NDMA = 2 two DMA waves share each chunk's transfers, one streaming
+  // Q and T, the other K and V.
+  static constexpr int kP0 = 0, kY0 = 1, kY1 = 2, kS0 = 3, kS1 = 4, kO0 = 5, kO1 = 6, kP1 = 7, kDma = 8, kDma2 = 9;
+  __host__ __device__ static constexpr bool is_output(int w) { return w == kO0 || w == kO1; }
   static constexpr int NWAVES = 8 + NDMA, THREADS = NWAVES * kWave;
 };
 
@@ -100,23 +109,25 @@ __global__ __launch_bounds__(64 * (8 + NDMA)) void recurrence_split_kernel(
     wait_lgkm0();
     barrier_nowait();
   };
-  // Output of chunk n from the staging tile: each output wave stores half of
-  // the rows, one 16-byte piece per lane, so every row's 64 bytes leave in
-  // one instruction, as nontemporal stores.  (Eight 32-byte pieces of each
-  // 256-byte row of o, from eight wavefronts, slowed the whole pass and most
-  // of all the heads whose rows sit at 256 mod 1024 bytes; with ordinary
-  // stores of whole 64-byte pieces those heads still trailed the others by
-  // ~15 %, with nontemporal ones they do not.)
+  // Output of chunk n from the staging tile: output wave `half` stores rows
+  // 32 half .. 32 half + 31, one 16-byte piece per lane, so every row's 64
+  // bytes leave in one instruction, as nontemporal stores.  (Eight
+  // 32-byte pieces of each 256-byte row of o, from eight wavefronts, slowed
+  // the whole pass and most of all the heads whose rows sit at 256 mod 1024
+  // bytes; with ordinary stores of whole 64-byte pieces those heads still
+  // trailed the others by ~15 %, with nontemporal ones they do not.)
   auto store_staged = [&](int n, int half) {
     const int valid = chunk_valid(n);
     const int64_t row0 = row_of(n);
 #pragma unroll
-    for (int i = 0; i < C / 32; ++i) {
+    for (int i = 0; i < 2; ++i) {
       const int r = 32 * half + 16 * i + (lane >> 2), piece = lane & 3;
       const u32x4 val = *reinterpret_cast<const u32x4*>(&O_st[r][8 * piece]);
-      if (r < valid) __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(o + (row0 + int64_t(r) * H) * DV + v0 + 8 * piece));
+      if (r < valid)
+        __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(o + (row0 + int64_t(r) * H) * DV + v0 + 8 * piece));
     }
   };
+  const int o_rh = role == S::kO1 ? 1 : 0;  // output waves: row half
   // Steps of three chunks keep the ring slots compile-time addresses.
   auto run = [&](auto&& step) {
     for (int n = 0; n < nc; n += 3) {
@@ -173,13 +184,13 @@ __global__ __launch_bounds__(64 * (8 + NDMA)) void recurrence_split_kernel(
     wait_vmcnt<0>();
   };
 
-  if (role >= S::kDma) {
+  if (role == S::kDma || role == S::kDma2) {
     if constexpr (NDMA == 1) dma_role(std::integral_constant<int, -1>{});
     else if (role == S::kDma) dma_role(std::integral_constant<int, 0>{});
     else dma_role(std::integral_constant<int, 1>{});
-  } else if (role == S::kY0 || role == S::kY0 + 1) {
+  } else if (role == S::kY0 || role == S::kY1) {
     // ----------------------------------------------------------------- Y
-    const int ct = role - S::kY0;
+    const int ct = role == S::kY1 ? 1 : 0;
     Frag<uint16_t> Kf[NRT][NKU_D];
     Frag<uint16_t> Tf[NRT][NKU_C];
     bf16x4 Vt[NRT];
@@ -239,10 +250,10 @@ __global__ __launch_bounds__(64 * (8 + NDMA)) void recurrence_split_kernel(
       sync();  // B
       if (n + 1 < nc) load(ring + (sn == 2 ? 0 : (sn + 1) * S::SLOT));
     }
-  } else if (role == S::kS0 || role == S::kS0 + 1) {
+  } else if (role == S::kS0 || role == S::kS1) {
     // ----------------------------------------------------------------- S
     // rows: logical key dims 64 hh .. 64 hh + 63 (k-units KH hh .. KH hh + KH - 1)
-    const int hh = role - S::kS0, dt0 = 2 * KH * hh, ku0 = KH * hh;
+    const int hh = role == S::kS1 ? 1 : 0, dt0 = 2 * KH * hh, ku0 = KH * hh;
     // St[d][c][qq] = S[key_phys(16 (dt0 + d) + 4 g + qq)][v0 + 16 c + li]
     f32x4 St[2 * KH][NT];
 #pragma unroll
@@ -291,48 +302,61 @@ __global__ __launch_bounds__(64 * (8 + NDMA)) void recurrence_split_kernel(
           for (int qq = 0; qq < 4; ++qq)
             sfin[(int64_t(bh) * DK + key_phys(16 * (dt0 + d) + 4 * g + qq)) * DV + v0 + 16 * c + li] = St[d][c][qq];
     }
-  } else if (role == S::kO0 || role == S::kO0 + 1) {
+  } else if (S::is_output(role)) {
     // ------------------------------------------------------------- output
-    const int ct = role - S::kO0;
-    Frag<uint16_t> Qf[NRT][NKU_D];
+    // row tiles 2 rh and 2 rh + 1, both state tiles
+    const int rt0 = 2 * o_rh;
+    Frag<uint16_t> Qf[2][NKU_D];
     auto load = [&](const uint16_t* __restrict__ cur) {
 #pragma unroll
       for (int ku = 0; ku < NKU_D; ++ku)
 #pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) Qf[rt][ku] = wide_frag<DK>(cur + S::QOFF, 16 * rt + li, ku, g);
+        for (int r = 0; r < 2; ++r) Qf[r][ku] = wide_frag<DK>(cur + S::QOFF, 16 * (rt0 + r) + li, ku, g);
     };
     run([&](const uint16_t* __restrict__ cur, const uint16_t* __restrict__ nxt, int n) {
       sync();  // A
       if (n == 0) load(cur);
-      else store_staged(n - 1, ct);  // both output waves staged chunk n-1 before barrier A
-      // Zt[rt][qq] = Z[16 rt + li][16 ct + 4 g + qq]  (Z^T = S^T Q^T)
-      f32x4 Zt[NRT];
+      else store_staged(n - 1, o_rh);  // both output waves staged chunk n-1 before barrier A
+      // Zt[c][r][qq] = Z[16 (rt0 + r) + li][16 c + 4 g + qq]  (Z^T = S^T Q^T)
+      f32x4 Zt[NT][2];
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) Zt[rt] = zero4();
+      for (int c = 0; c < NT; ++c)
 #pragma unroll
-      for (int ku = 0; ku < NKU_D; ++ku) {
-        Frag<uint16_t> bSo;
-        bSo.v = bS_buf[ct][ku][lane];
+        for (int r = 0; r < 2; ++r) Zt[c][r] = zero4();
 #pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) mma(Zt[rt], bSo, Qf[rt][ku]);
-      }
+      for (int ku = 0; ku < NKU_D; ++ku)
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+          Frag<uint16_t> bSo;
+          bSo.v = bS_buf[c][ku][lane];
+#pragma unroll
+          for (int r = 0; r < 2; ++r) mma(Zt[c][r], bSo, Qf[r][ku]);
+        }
       sync();  // B
-      // O^T = Z^T + U'^T P^T; lane (li, g) stages O[16 rt + li][16 ct + 4g .. 4g + 3]
-      Frag<uint16_t> pf[NPF], bUo[NKU_C];
+      // O^T = Z^T + U'^T P^T; lane (li, g) stages O[16 rt + li][16 c + 4g .. 4g + 3]
+      Frag<uint16_t> bUo[NT][NKU_C];
 #pragma unroll
-      for (int i = 0; i < NPF; ++i) pf[i].v = P_buf[i][lane];
+      for (int c = 0; c < NT; ++c)
 #pragma unroll
-      for (int ku = 0; ku < NKU_C; ++ku) bUo[ku].v = bU_buf[ct][ku][lane];
+        for (int ku = 0; ku < NKU_C; ++ku) bUo[c][ku].v = bU_buf[c][ku][lane];
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) {
-        f32x4 acc = Zt[rt];
+      for (int r = 0; r < 2; ++r) {
+        const int rt = rt0 + r;
+        Frag<uint16_t> pf[NKU_C];
 #pragma unroll
         for (int ku = 0; ku < NKU_C; ++ku)
-          if (32 * ku <= 16 * rt + 15) mma(acc, bUo[ku], pf[pf_index(rt, ku)]);
-        bf16x4 ov;
+          if (32 * ku <= 16 * rt + 15) pf[ku].v = P_buf[pf_index(rt, ku)][lane];
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) ov[qq] = static_cast<__bf16>(acc[qq]);
-        *reinterpret_cast<bf16x4*>(&O_st[16 * rt + li][16 * ct + 4 * g]) = ov;
+        for (int c = 0; c < NT; ++c) {
+          f32x4 acc = Zt[c][r];
+#pragma unroll
+          for (int ku = 0; ku < NKU_C; ++ku)
+            if (32 * ku <= 16 * rt + 15) mma(acc, bUo[c][ku], pf[ku]);
+          bf16x4 ov;
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) ov[qq] = static_cast<__bf16>(acc[qq]);
+          *reinterpret_cast<bf16x4*>(&O_st[16 * rt + li][16 * c + 4 * g]) = ov;
+        }
       }
       if (n + 1 < nc) load(nxt);
     });
@@ -391,9 +415,9 @@ __global__ __launch_bounds__(64 * (8 + NDMA)) void recurrence_split_kernel(
     if (role == S::kP0) prole(std::integral_constant<int, 0>{}, std::integral_constant<int, NRT - 1>{});
     else prole(std::integral_constant<int, NRT - 1>{}, std::integral_constant<int, NRT>{});
   }
-  // the last chunk's output: staged by both output waves before this barrier
+  // the last chunk's output: staged by every output wave before this barrier
   sync();
-  if (nc > 0 && (role == S::kO0 || role == S::kO0 + 1)) store_staged(nc - 1, role - S::kO0);
+  if (nc > 0 && S::is_output(role)) store_staged(nc - 1, o_rh);
 }
 
 template <int DK, int C, int BV, int NDMA>
