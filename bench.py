@@ -64,8 +64,9 @@ def parse_args():
     ap.add_argument("--workload", default="shape_1p3b")
     ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--backward-steps", type=int, default=10)
-    ap.add_argument("--profile", choices=("fwd", "decode"), default=None,
-                    help="only the flushed forward (or decode) steps, for rocprofv3 runs of the same kernels")
+    ap.add_argument("--profile", choices=("fwd", "decode", "segmented", "training"), default=None,
+                    help="only the flushed forward steps (or the decode, segment-scan or training leg), "
+                         "for rocprofv3 runs of the same kernels")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip every leg after the headline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -221,6 +222,62 @@ def decode_leg(torch, efla, W, fl, dev, dtype, args, esz):
         "note": "flushed: a cache flush before every step; warm: back to back on the resident 256 MiB state"}
 
 
+def training_leg(torch, efla, w, inp, o, s_final, ws, dev, K, args, rules=("exact", "euler")):
+    """Forward + backward per step, back to back, under each rule."""
+    q, k, v, beta, s0 = inp["q"], inp["k"], inp["v"], inp["beta"], inp["s0"]
+    tokens = w.B * w.L
+    g = torch.Generator(device="cpu").manual_seed(7)
+    d_o = torch.randn(o.shape, generator=g).to(q.dtype).to(dev)
+    dsf = torch.randn(s_final.shape, generator=g).to(dev)
+    gq, gk, gv, gb = (torch.empty_like(x) for x in (q, k, v, beta))
+    gs0 = torch.empty_like(s_final)
+    nb = efla.efla_chunk_bwd_workspace_size(w.B, w.H, w.L, w.dk, w.dv, w.chunk, q.dtype)
+    wsb = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    train = {}
+    for rule in rules:
+        fwd = efla.prepare_chunk_fwd(q, k, v, beta, s0, o, s_final, ws, chunk=w.chunk, rule=rule)
+        bwd = efla.prepare_chunk_bwd(q, k, v, beta, d_o, s0, dsf, gq, gk, gv, gb, gs0, wsb, chunk=w.chunk,
+                                     rule=rule)
+        fwd()
+        bwd()
+        KB = max(1, args.backward_steps)
+        fus = warm_us(torch, (fwd,), K)
+        bus = warm_us(torch, (bwd,), KB)
+        tus = warm_us(torch, (fwd, bwd), KB)
+        train[rule] = {"fwd_us": round(fus, 2), "bwd_us": round(bus, 2), "fwd_bwd_us": round(tus, 2),
+                       "fwd_bwd_tokens_per_s": round(tokens / (tus / 1e6), 1)}
+    if "exact" in train and "euler" in train:
+        train["exact_over_euler_time"] = round(train["exact"]["fwd_bwd_us"] / train["euler"]["fwd_bwd_us"], 4)
+    train["note"] = ("back-to-back steps; the pages report EFLA training throughput matching DeltaNet's "
+                     "(Experimental Results), with no hardware or numbers given")
+    return train, nb
+
+
+def segmented_leg(torch, efla, W, fl, dev):
+    """The stiff long-context workload: the plain chunked pass against the
+    segment scan, flushed steps."""
+    wl = W.get("stiff_64k")
+    li = W.generate(wl, device=dev)
+    ol = torch.empty_like(li["v"])
+    sl = torch.empty((wl.B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device=dev)
+    segs = efla.default_segments(wl.B, wl.H, wl.L, wl.dv, wl.chunk)
+    wsp = efla.alloc_workspace(wl.B, wl.H, wl.L, wl.dk, wl.dv, wl.chunk, li["q"].dtype, dev)
+    nsg = efla.efla_chunk_fwd_segmented_workspace_size(wl.B, wl.H, wl.L, wl.dk, wl.dv, wl.chunk, segs,
+                                                       li["q"].dtype)
+    wss = torch.empty(max(nsg, 1), dtype=torch.uint8, device=dev)
+    plain = efla.prepare_chunk_fwd(li["q"], li["k"], li["v"], li["beta"], li["s0"], ol, sl, wsp, chunk=wl.chunk)
+    seg = efla.prepare_chunk_fwd_segmented(li["q"], li["k"], li["v"], li["beta"], li["s0"], ol, sl, wss,
+                                           chunk=wl.chunk, segments=segs)
+    plain()
+    seg()
+    pms, _ = flushed_steps(torch, (plain,), 10, fl.clean)
+    sms, _ = flushed_steps(torch, (seg,), 10, fl.clean)
+    pus, sus = pct(pms, 50) * 1e3, pct(sms, 50) * 1e3
+    return {"workload": wl.name, "segments": segs, "plain": stats_us(pms), "segmented": stats_us(sms),
+            "plain_tokens_per_s": round(wl.tokens / (pus / 1e6), 1),
+            "segmented_tokens_per_s": round(wl.tokens / (sus / 1e6), 1), "speedup": round(pus / sus, 3)}
+
+
 def fwd_bytes(w, esz, with_s0=True):
     """Algorithmic bytes of one forward pass: q, k, v, beta read and o written
     once, plus the fp32 states in (if given) and out."""
@@ -269,8 +326,22 @@ def main():
     rec_bytes = n_ht * (2 * w.dk + 2 * w.dv) * esz + (state_bytes if s0 is not None else 0) + state_bytes
     path_flops = n_ht * (6 * w.dk * w.dv + 5 * w.chunk * max(w.dk, w.dv) + w.chunk ** 2 // 3)
 
+    if args.copy_calibration:  # a device copy of known size, for the HBM counters under rocprofv3
+        src = torch.ones(1 << 26, dtype=torch.float32, device=dev)   # 256 MiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.profile == "decode":
         print(json.dumps({"decode": decode_leg(torch, efla, W, fl, dev, q.dtype, args, esz)}), flush=True)
+        return
+    if args.profile == "segmented":
+        print(json.dumps({"segmented": segmented_leg(torch, efla, W, fl, dev)}), flush=True)
+        return
+    if args.profile == "training":
+        train, _ = training_leg(torch, efla, w, inp, o, s_final, ws, dev, max(1, args.steps), args)
+        print(json.dumps({"training": train}), flush=True)
         return
     for _ in range(args.warmup):
         ut()
@@ -333,14 +404,6 @@ def main():
     dms, _ = flushed_steps(torch, (ut, rec), K, fl.dirty)
     line["dirty_flush"] = dict(stats_us(dms), note="write-only flush: the step competes with its write-back")
 
-    if args.copy_calibration:
-        src = torch.ones(1 << 26, dtype=torch.float32, device=dev)   # 256 MiB
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
     if extras:
         # ---- the other model-shaped workloads ----------------------------
         shapes = {}
@@ -367,29 +430,7 @@ def main():
         line["decode"] = decode_leg(torch, efla, W, fl, dev, q.dtype, args, esz)
 
         # ---- training step: forward + backward, exact and Euler ---------------
-        g = torch.Generator(device="cpu").manual_seed(7)
-        d_o = torch.randn(o.shape, generator=g).to(q.dtype).to(dev)
-        dsf = torch.randn(s_final.shape, generator=g).to(dev)
-        gq, gk, gv, gb = (torch.empty_like(x) for x in (q, k, v, beta))
-        gs0 = torch.empty_like(s_final)
-        nb = efla.efla_chunk_bwd_workspace_size(w.B, w.H, w.L, w.dk, w.dv, w.chunk, q.dtype)
-        wsb = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
-        train = {}
-        for rule in ("exact", "euler"):
-            fwd = efla.prepare_chunk_fwd(q, k, v, beta, s0, o, s_final, ws, chunk=w.chunk, rule=rule)
-            bwd = efla.prepare_chunk_bwd(q, k, v, beta, d_o, s0, dsf, gq, gk, gv, gb, gs0, wsb, chunk=w.chunk,
-                                         rule=rule)
-            fwd()
-            bwd()
-            KB = max(1, args.backward_steps)
-            fus = warm_us(torch, (fwd,), K)
-            bus = warm_us(torch, (bwd,), KB)
-            tus = warm_us(torch, (fwd, bwd), KB)
-            train[rule] = {"fwd_us": round(fus, 2), "bwd_us": round(bus, 2), "fwd_bwd_us": round(tus, 2),
-                           "fwd_bwd_tokens_per_s": round(tokens / (tus / 1e6), 1)}
-        train["exact_over_euler_time"] = round(train["exact"]["fwd_bwd_us"] / train["euler"]["fwd_bwd_us"], 4)
-        train["note"] = ("back-to-back steps; the pages report EFLA training throughput matching DeltaNet's "
-                         "(Experimental Results), with no hardware or numbers given")
+        train, nb = training_leg(torch, efla, w, inp, o, s_final, ws, dev, K, args)
         line["training"] = train
         line["euler"] = {"rule": "euler (alpha = beta)", "fwd_us": train["euler"]["fwd_us"],
                          "exact_fwd_us": train["exact"]["fwd_us"],
@@ -401,7 +442,6 @@ def main():
                             "algorithmic_bytes": bwd_bytes,
                             "hbm_frac": round(bwd_bytes / (bus / 1e6) / 1e9 / HBM_PEAK_GBS, 4),
                             "workspace_bytes": nb}
-        del wsb, gq, gk, gv, gb, gs0, d_o, dsf
 
         # ---- packed variable-length batch -----------------------------------
         wv = W.get("varlen_1p3b")
@@ -425,30 +465,7 @@ def main():
                           "warm_us": round(warm_us(torch, (fv,), K), 2)}
         del pv, ov, sv, wsv, fv
 
-        # ---- segment scan on the stiff long-context workload -----------------
-        wl = W.get("stiff_64k")
-        li = W.generate(wl, device=dev)
-        ol = torch.empty_like(li["v"])
-        sl = torch.empty((wl.B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device=dev)
-        segs = efla.default_segments(wl.B, wl.H, wl.L, wl.dv, wl.chunk)
-        wsp = efla.alloc_workspace(wl.B, wl.H, wl.L, wl.dk, wl.dv, wl.chunk, li["q"].dtype, dev)
-        nsg = efla.efla_chunk_fwd_segmented_workspace_size(wl.B, wl.H, wl.L, wl.dk, wl.dv, wl.chunk, segs,
-                                                           li["q"].dtype)
-        wss = torch.empty(max(nsg, 1), dtype=torch.uint8, device=dev)
-        plain = efla.prepare_chunk_fwd(li["q"], li["k"], li["v"], li["beta"], li["s0"], ol, sl, wsp, chunk=wl.chunk)
-        seg = efla.prepare_chunk_fwd_segmented(li["q"], li["k"], li["v"], li["beta"], li["s0"], ol, sl, wss,
-                                               chunk=wl.chunk, segments=segs)
-        plain()
-        seg()
-        pms, _ = flushed_steps(torch, (plain,), 10, fl.clean)
-        sms, _ = flushed_steps(torch, (seg,), 10, fl.clean)
-        pus, sus = pct(pms, 50) * 1e3, pct(sms, 50) * 1e3
-        line["segmented"] = {"workload": wl.name, "segments": segs, "plain": stats_us(pms),
-                             "segmented": stats_us(sms),
-                             "plain_tokens_per_s": round(wl.tokens / (pus / 1e6), 1),
-                             "segmented_tokens_per_s": round(wl.tokens / (sus / 1e6), 1),
-                             "speedup": round(pus / sus, 3)}
-        del li, ol, sl, wsp, wss, plain, seg
+        line["segmented"] = segmented_leg(torch, efla, W, fl, dev)
 
     # ---- the oracle on the host cores -----------------------------------------
     if not args.no_cpu_baseline:
