@@ -9,8 +9,11 @@
 //   a  [slots][C]        fp32          coefficients
 //   S  [slots][dk][dv]   input dtype   state at the start of the chunk (bf16
 //                                      inputs: the operand values the forward
-//                                      products use)
+//                                      products use; [slots][dv][dk] where
+//                                      the state-only kernel writes them)
 //   dS [slots][dk][dv]   fp32          loss gradient at the end of the chunk
+//                                      (bf16, packed from the region's start,
+//                                      for the bf16 matrix-core kernels)
 #include <stdlib.h>
 #include <string.h>
 
@@ -41,12 +44,20 @@ BwdLayout bwd_layout(int B, int H, int64_t L, int DK, int DV, int C, size_t esz)
 }
 
 // The forward recurrence again, storing the state at the start of every chunk
-// and no output: the role kernel for the bf16 shapes it covers (its output
-// and P wavefronts then idle), else the generic kernel.
+// and no output.  With allow_t, where the state-only kernel covers the shape,
+// that kernel writes the states transposed ([slots][DV][DK]) and *transposed
+// is set; else the role kernel for the bf16 shapes it covers (its output and
+// P wavefronts then idle), else the generic kernel, both [slots][DK][DV].
 template <typename T, int DK, int C>
 hipError_t chunk_states(const T* q, const T* k, const T* v, const T* tws, const float* s0, T* states, int B,
-                        int H, int64_t L, int DV, hipStream_t s) {
+                        int H, int64_t L, int DV, hipStream_t s, bool allow_t = false, bool* transposed = nullptr) {
+  if (transposed != nullptr) *transposed = false;
   if constexpr (sizeof(T) == 2) {
+    const char* impl = getenv("EFLA_BWD_STATES");
+    if (allow_t && !(impl && strcmp(impl, "roles") == 0) && recurrence_states_supported(DK, DV, C)) {
+      *transposed = true;
+      return launch_chunk_states_t_bf16(k, v, tws, s0, states, B, H, L, DK, DV, C, s);
+    }
     const int bv = DV >= 32 ? 32 : 16;
     if (recurrence_roles_supported(DK, C, bv))
       return launch_recurrence_roles_bf16(q, k, v, tws, s0, nullptr, nullptr, B, H, L, DK, DV, C, bv, nullptr, 0, s,
@@ -82,6 +93,7 @@ hipError_t bwd_launch_impl(const T* q, const T* k, const T* v, const T* beta, co
     bf16k = !(impl && strcmp(impl, "fp32") == 0) && bwd_bf16_supported(DK, DV, C);
   }
   const uint16_t* pws16 = reinterpret_cast<const uint16_t*>(pws);
+  bool states_t = false;  // the chunk states are stored transposed
   if (slots > 0) {
     // 1. T, X, P and a of every chunk: one wavefront per chunk for the bf16
     // shapes that kernel covers (EFLA_UT_IMPL=workgroup keeps the other unless
@@ -108,7 +120,9 @@ hipError_t bwd_launch_impl(const T* q, const T* k, const T* v, const T* beta, co
                          beta, tws, H, L, NC, rule, nullptr, 0, q, xws, aws, pws);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     // 2. the state at the start of every chunk (no output)
-    if (hipError_t e = chunk_states<T, DK, C>(q, k, v, tws, s0, sws, B, H, L, DV, s); e != hipSuccess) return e;
+    if (hipError_t e = chunk_states<T, DK, C>(q, k, v, tws, s0, sws, B, H, L, DV, s, bf16k, &states_t);
+        e != hipSuccess)
+      return e;
   }
   // 3. reverse pass over chunks: dS at every chunk end, and dS_0 (bf16 inputs
   // on bf16 matrix cores where the shape allows, like step 4)
@@ -117,7 +131,8 @@ hipError_t bwd_launch_impl(const T* q, const T* k, const T* v, const T* beta, co
     if (bf16k) {
       hipLaunchKernelGGL((bwd_state_bf16_kernel<DK, C>), dim3(unsigned(BH * (DV / kBwdBV))),
                          dim3(BwdStateBf16Shape<DK, C>::NTH), 0, s,
-                         q, k, dout, tws, pws16, dsf, dsws, ds0, H, L, NC, DV, DV / kBwdBV, BH % 8 == 0 ? 1 : 0);
+                         q, k, dout, tws, pws16, dsf, reinterpret_cast<uint16_t*>(dsws), ds0, H, L, NC, DV,
+                         DV / kBwdBV, BH % 8 == 0 ? 1 : 0);
       state_done = true;
     }
   }
@@ -130,9 +145,15 @@ hipError_t bwd_launch_impl(const T* q, const T* k, const T* v, const T* beta, co
   // shape allows (EFLA_BWD_IMPL=fp32 keeps the fp32 kernel), else fp32
   if constexpr (sizeof(T) == 2 && DK % 32 == 0 && C % 32 == 0) {
     if (bf16k) {
-      hipLaunchKernelGGL((bwd_chunk_bf16_kernel<DK, C>), dim3(unsigned(slots)), dim3(BwdBf16Shape<DK, C>::NTH), 0, s,
-                         q, k, v, beta,
-                         dout, tws, xws, aws, pws16, sws, dsws, dq, dk, dv, dbeta, H, L, NC, DV, rule);
+      const auto* ds16 = reinterpret_cast<const uint16_t*>(dsws);
+      if (states_t)
+        hipLaunchKernelGGL((bwd_chunk_bf16_kernel<DK, C, true>), dim3(unsigned(slots)),
+                           dim3(BwdBf16Shape<DK, C>::NTH), 0, s, q, k, v, beta, dout, tws, xws, aws, pws16, sws, ds16,
+                           dq, dk, dv, dbeta, H, L, NC, DV, rule);
+      else
+        hipLaunchKernelGGL((bwd_chunk_bf16_kernel<DK, C, false>), dim3(unsigned(slots)),
+                           dim3(BwdBf16Shape<DK, C>::NTH), 0, s, q, k, v, beta, dout, tws, xws, aws, pws16, sws, ds16,
+                           dq, dk, dv, dbeta, H, L, NC, DV, rule);
       return hipGetLastError();
     }
   }

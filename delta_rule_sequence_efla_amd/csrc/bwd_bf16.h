@@ -6,7 +6,7 @@
 // dT accumulated in fp32 registers, then the UT-transform part.  What differs
 // is where the products run: every product with a value block, Q or K is one
 // v_mfma_f32_16x16x32_bf16 per 32-deep slice on bf16 operands in LDS.  The
-// operands that are not bf16 already (P, dS', the intermediates D = V - K S,
+// operands that are not bf16 already (P, the intermediates D = V - K S,
 // dU, U, dD, and dP, dG + dG^T) are rounded to bf16 once, like the states the
 // forward products use; X, W = X^T dX, dA and the coefficient gradients stay
 // fp32 (fp32 matrix cores and VALU).
@@ -173,16 +173,18 @@ struct Bf16Stager {
   }
 };
 
-// One value block's four operands staged through one set of registers: S
-// (bf16 [DK][BV]), dS' (fp32 [DK][BV]), V and dO (bf16 [C][BV]), their
-// 16-byte units numbered in that order and dealt to the workgroup's threads,
-// so a thread holds cdiv(units, NTH) row pairs instead of one per operand
-// (with 32 value columns every operand boundary falls on a whole wavefront).
+// One value block's four operands staged through one set of registers: S and
+// dS' (bf16 [DK][BV]), V and dO (bf16 [C][BV]), their 16-byte units numbered
+// in that order and dealt to the workgroup's threads, so a thread holds
+// cdiv(units, NTH) row pairs instead of one per operand (with 32 value
+// columns every operand boundary falls on a whole wavefront).
 // Each unit is two consecutive rows of one 16-byte column slice, written as
-// in Bf16Stager: rows, and transposed as 4-byte words of the two rows.
-template <int DK, int C, int BV, int NTH>
+// in Bf16Stager: rows, and transposed as 4-byte words of the two rows.  STT:
+// S comes transposed (rows of d_k per value column), so its rows land in
+// S^T and its transpose in S.
+template <int DK, int C, int BV, int NTH, bool STT>
 struct BlockStager {
-  static constexpr int U0 = (DK / 2) * (BV / 8), U1 = (DK / 2) * (BV / 4), U2 = (C / 2) * (BV / 8);
+  static constexpr int U0 = (DK / 2) * (BV / 8), U1 = U0, U2 = (C / 2) * (BV / 8);
   static constexpr int TOT = U0 + U1 + 2 * U2, CNT = cdiv(TOT, NTH);
   u32x4 r[CNT][2];
   // operand of unit idx, and its index within that operand
@@ -193,8 +195,8 @@ struct BlockStager {
     j = idx - U0 - U1 - U2;
     return 3;
   }
-  __device__ __forceinline__ void load(const uint16_t* st, const float* dst, const uint16_t* vv, const uint16_t* dov,
-                                       int DV, int64_t v_stride, int valid, int tid) {
+  __device__ __forceinline__ void load(const uint16_t* st, const uint16_t* dst, const uint16_t* vv,
+                                       const uint16_t* dov, int DV, int64_t v_stride, int valid, int tid) {
 #pragma unroll
     for (int i = 0; i < CNT; ++i) {
       const int idx = tid + i * NTH;
@@ -202,14 +204,15 @@ struct BlockStager {
       if (idx >= TOT) continue;
       int j;
       const int op = which(idx, j);
-      if (op == 0) {  // S rows: DK rows, stride DV
+      if (op == 0 && STT) {  // S^T rows: BV rows, stride DK
+        const int t = 2 * (j % (BV / 2)), c = (j / (BV / 2)) * 8;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) r[i][h] = *reinterpret_cast<const u32x4*>(st + (t + h) * DK + c);
+      } else if (op <= 1) {  // S or dS' rows: DK rows, stride DV
         const int t = 2 * (j % (DK / 2)), c = (j / (DK / 2)) * 8;
+        const uint16_t* src = op == 0 ? st : dst;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) r[i][h] = *reinterpret_cast<const u32x4*>(st + (t + h) * int64_t(DV) + c);
-      } else if (op == 1) {  // dS' rows (fp32): DK rows, stride DV
-        const int t = 2 * (j % (DK / 2)), c = (j / (DK / 2)) * 4;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) r[i][h] = *reinterpret_cast<const u32x4*>(dst + (t + h) * int64_t(DV) + c);
+        for (int h = 0; h < 2; ++h) r[i][h] = *reinterpret_cast<const u32x4*>(src + (t + h) * int64_t(DV) + c);
       } else {  // V or dO: C token rows, rows at or past `valid` read as zero
         const uint16_t* src = op == 2 ? vv : dov;
         const int t = 2 * (j % (C / 2)), c = (j / (C / 2)) * 8;
@@ -228,31 +231,16 @@ struct BlockStager {
       if (idx >= TOT) continue;
       int j;
       const int op = which(idx, j);
-      if (op == 1) {  // fp32 -> bf16, four columns
-        const int t = 2 * (j % (DK / 2)), c = (j / (DK / 2)) * 4;
-        uint16_t hv[2][4];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          union {
-            u32x4 u;
-            float e[4];
-          } x;
-          x.u = r[i][h];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) hv[h][e] = from_f32<uint16_t>(x.e[e]);
-          *reinterpret_cast<uint2*>(dSv + (t + h) * VBP + c) = *reinterpret_cast<const uint2*>(hv[h]);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          *reinterpret_cast<uint32_t*>(dSvT + (c + e) * KBP + t) = uint32_t(hv[0][e]) | (uint32_t(hv[1][e]) << 16);
-      } else {  // bf16, eight columns
-        const int rows = op == 0 ? DK : C;
+      {  // eight bf16 columns
+        const bool st_t = STT && op == 0;
+        const int rows = st_t ? BV : op <= 1 ? DK : C;
         const int t = 2 * (j % (rows / 2)), c = (j / (rows / 2)) * 8;
-        uint16_t* X = op == 0 ? Sv : op == 2 ? Vv : dOv;
-        uint16_t* XT = op == 0 ? SvT : op == 2 ? nullptr : dOvT;
-        const int pitchT = op == 0 ? KBP : TBP;
+        uint16_t* X = st_t ? SvT : op == 0 ? Sv : op == 1 ? dSv : op == 2 ? Vv : dOv;
+        uint16_t* XT = st_t ? Sv : op == 0 ? SvT : op == 1 ? dSvT : op == 2 ? nullptr : dOvT;
+        const int pitch = st_t ? KBP : VBP;
+        const int pitchT = st_t ? VBP : op <= 1 ? KBP : TBP;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) *reinterpret_cast<u32x4*>(X + (t + h) * VBP + c) = r[i][h];
+        for (int h = 0; h < 2; ++h) *reinterpret_cast<u32x4*>(X + (t + h) * pitch + c) = r[i][h];
         if (XT != nullptr) {
           union {
             u32x4 u;
@@ -269,12 +257,14 @@ struct BlockStager {
   }
 };
 
-template <int DK, int C>
+// STT: `states` holds each chunk's start state transposed, [slots][DV][DK]
+// (else [slots][DK][DV]).
+template <int DK, int C, bool STT>
 __global__ __launch_bounds__((BwdBf16Shape<DK, C>::NTH)) void bwd_chunk_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ beta, const uint16_t* __restrict__ dout, const uint16_t* __restrict__ tws,
     const float* __restrict__ xws, const float* __restrict__ aws, const uint16_t* __restrict__ pws,
-    const uint16_t* __restrict__ states, const float* __restrict__ dstates, uint16_t* __restrict__ dq,
+    const uint16_t* __restrict__ states, const uint16_t* __restrict__ dstates, uint16_t* __restrict__ dq,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, uint16_t* __restrict__ dbeta, int H, int64_t L, int NC,
     int DV, int rule) {
   using S = BwdBf16Shape<DK, C>;
@@ -323,11 +313,12 @@ __global__ __launch_bounds__((BwdBf16Shape<DK, C>::NTH)) void bwd_chunk_bf16_ker
   for (int i = 0; i < NP; ++i) dPa[i] = dTa[i] = zero4();
 
   const uint16_t* st = states + slot * DK * DV;
-  const float* dst = dstates + slot * DK * DV;
+  const uint16_t* dst = dstates + slot * DK * DV;
   // one value block's operands, staged through registers one block ahead
-  BlockStager<DK, C, BV, NTH> sb;
+  BlockStager<DK, C, BV, NTH, STT> sb;
   auto load_block = [&](int v0) {
-    sb.load(st + v0, dst + v0, v + row0 * DV + v0, dout + row0 * DV + v0, DV, v_stride, valid, tid);
+    sb.load(st + (STT ? v0 * DK : v0), dst + v0, v + row0 * DV + v0, dout + row0 * DV + v0, DV, v_stride, valid,
+            tid);
   };
   load_block(0);
   for (int v0 = 0; v0 < DV; v0 += BV) {
@@ -637,7 +628,7 @@ template <int DK, int C>
 __global__ __launch_bounds__((BwdStateBf16Shape<DK, C>::NTH)) void bwd_state_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ dout,
     const uint16_t* __restrict__ tws, const uint16_t* __restrict__ pws, const float* __restrict__ dsf,
-    float* __restrict__ dstates, float* __restrict__ ds0, int H, int64_t L, int NC, int DV, int NVB, int remap) {
+    uint16_t* __restrict__ dstates, float* __restrict__ ds0, int H, int64_t L, int NC, int DV, int NVB, int remap) {
   using S = BwdStateBf16Shape<DK, C>;
   constexpr int KBP = S::KBP, TBP = S::TBP, BV = S::BV, NS = S::NS, NEF = S::NEF, NWV = S::NWV, NTH = S::NTH;
   static_assert(NS >= 1 && NEF >= 1, "d_k and the chunk are multiples of 32");
@@ -688,13 +679,14 @@ __global__ __launch_bounds__((BwdStateBf16Shape<DK, C>::NTH)) void bwd_state_bf1
 
   for (int n = sp.nc - 1; n >= 0; --n) {
     __syncthreads();  // the previous chunk's products are done with every array
-    // dstates[n] = dS (fp32, global) and dS^T (bf16, LDS)
-    float* dst = dstates + (sp.slot0 + n) * DK * DV;
+    // dstates[n] = dS and dS^T (LDS), both bf16: the per-chunk products use
+    // dS only as a bf16 operand
+    uint16_t* dst = dstates + (sp.slot0 + n) * DK * DV;
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       const int t = w + NWV * i, d0 = 16 * (t / 2), c0 = 16 * (t % 2);
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) dst[(d0 + 4 * g + qq) * DV + v0 + c0 + li] = dS[i][qq];
+      for (int qq = 0; qq < 4; ++qq) dst[(d0 + 4 * g + qq) * DV + v0 + c0 + li] = from_f32<uint16_t>(dS[i][qq]);
       st4(dST + (c0 + li) * KBP + d0 + 4 * g, dS[i]);
     }
     so.store(Kb, KBP, KbT, QbT, TbT, PbT, dOT, TBP, tid);

@@ -9,7 +9,20 @@ hipError_t launch_recurrence_states_bf16(const uint16_t* k, const uint16_t* v, c
                                          float* mout, int B, int H, int64_t L, int DK, int DV, int C,
                                          const int32_t* cu, int N, hipStream_t s) {
   if (!recurrence_states_supported(DK, DV, C)) return hipErrorInvalidValue;
-  if (DK == 64) return recurrence_states_launch_impl<64, 64, 32>(k, v, tws, nout, mout, B, H, L, DV, cu, N, s);
-  return recurrence_states_launch_impl<128, 64, 32>(k, v, tws, nout, mout, B, H, L, DV, cu, N, s);
+  if (DK == 64)
+    return recurrence_states_launch_impl<64, 64, 32, false>(k, v, tws, nout, mout, B, H, L, DV, cu, N, nullptr,
+                                                            nullptr, s);
+  return recurrence_states_launch_impl<128, 64, 32, false>(k, v, tws, nout, mout, B, H, L, DV, cu, N, nullptr,
+                                                           nullptr, s);
+}
+hipError_t launch_chunk_states_t_bf16(const uint16_t* k, const uint16_t* v, const uint16_t* tws, const float* s0,
+                                      uint16_t* statesT, int B, int H, int64_t L, int DK, int DV, int C,
+                                      hipStream_t s) {
+  if (!recurrence_states_supported(DK, DV, C)) return hipErrorInvalidValue;
+  if (DK == 64)
+    return recurrence_states_launch_impl<64, 64, 32, true>(k, v, tws, nullptr, nullptr, B, H, L, DV, nullptr, 0, s0,
+                                                           statesT, s);
+  return recurrence_states_launch_impl<128, 64, 32, true>(k, v, tws, nullptr, nullptr, B, H, L, DV, nullptr, 0, s0,
+                                                          statesT, s);
 }
 }  // namespace efla

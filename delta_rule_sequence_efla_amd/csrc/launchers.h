@@ -73,6 +73,12 @@ bool recurrence_states_supported(int DK, int DV, int C);
 hipError_t launch_recurrence_states_bf16(const uint16_t* k, const uint16_t* v, const uint16_t* tws, float* nout,
                                          float* mout, int B, int H, int64_t L, int DK, int DV, int C,
                                          const int32_t* cu, int N, hipStream_t s);
+// The same pass as the backward's chunk-state run over a dense batch: the
+// recurrence from s0 (NULL: zeros), writing the bf16 state at the start of
+// every chunk transposed, statesT [B*H*NC][DV][DK]; same shapes.
+hipError_t launch_chunk_states_t_bf16(const uint16_t* k, const uint16_t* v, const uint16_t* tws, const float* s0,
+                                      uint16_t* statesT, int B, int H, int64_t L, int DK, int DV, int C,
+                                      hipStream_t s);
 
 // bf16 UT transform with one wavefront per chunk (ut_wave.h); d_k in
 // {32, 64, 128}, chunk in {32, 64}.

@@ -25,6 +25,13 @@
 //     Y: read K, T, V of chunk n+1 | S: S += K^T U' -> publish S_{n+1}
 //     | DMA: other half
 // Every exchange buffer is written in one phase and read in the other.
+//
+// The same kernel with BWD set runs one chain, the true recurrence from the
+// initial state, for the backward pass: it writes the state at the start of
+// every chunk, as the bf16 values the forward products use, transposed
+// ([d_v][d_k] per chunk slot): each S wave's published operand fragment is
+// eight consecutive key dims of one value column, one 16-byte store.  Five
+// wavefronts: Y tiles 0 and 1, S halves 0 and 1, DMA.
 #pragma once
 
 #include <type_traits>
@@ -33,7 +40,7 @@
 
 namespace efla {
 
-template <int DK, int C, int BV>
+template <int DK, int C, int BV, bool BWD = false>
 struct StatesShape {
   static_assert(C == 64 && BV == 32 && (DK == 64 || DK == 128), "shapes of the state-only pass");
   static constexpr int NT = BV / 16;  // state tiles per chain
@@ -46,8 +53,9 @@ struct StatesShape {
   using TV = DmaTile<C, BV, 1>;
   static constexpr int PK = TK::PER_WAVE, PT = TT::PER_WAVE, PV = TV::PER_WAVE;
   static constexpr int COUNT = PK + PT + PV;  // transfers per chunk
-  // waves: Y (chain 0 tiles 0-1, chain 1 tiles 0-1), S (same order), DMA
-  static constexpr int kY0 = 0, kS0 = 4, kDma = 8, NWAVES = 9, THREADS = NWAVES * kWave;
+  // waves: Y (chain 0 tiles 0-1[, chain 1 tiles 0-1]), S (same order), DMA
+  static constexpr int NCH = BWD ? 1 : 2;  // chains
+  static constexpr int kY0 = 0, kS0 = 2 * NCH, kDma = 4 * NCH, NWAVES = 4 * NCH + 1, THREADS = NWAVES * kWave;
 };
 
 inline bool states_supported(int DK, int C, int BV) { return C == 64 && BV == 32 && (DK == 64 || DK == 128); }
@@ -55,19 +63,23 @@ inline bool states_supported(int DK, int C, int BV) { return C == 64 && BV == 32
 // N [nseq * H, DK, DV] and M [nseq * H, DK, DK], fp32, rows indexed by key
 // dim.  NVB = max(DV, DK) / BV workgroups per (sequence, head); the first
 // NVB_N = DV / BV of them write N, the first NVB_M = DK / BV write M.
-template <int DK, int C, int BV>
-__global__ __launch_bounds__(64 * 9) void recurrence_states_kernel(
+// BWD: chain 0 starts from s0 (NULL: zeros) and NVB = NVB_N; statesT gets
+// the bf16 start state of every chunk slot, [slots][DV][DK]; nout and mout
+// are not used.
+template <int DK, int C, int BV, bool BWD>
+__global__ __launch_bounds__((64 * StatesShape<DK, C, BV, BWD>::NWAVES)) void recurrence_states_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const uint16_t* __restrict__ tws,
     float* __restrict__ nout, float* __restrict__ mout, int H, int64_t L, int NC, int DV, int NVB, int NVB_N,
-    int NVB_M, int remap, const int32_t* __restrict__ cu) {
-  using S = StatesShape<DK, C, BV>;
+    int NVB_M, int remap, const int32_t* __restrict__ cu, const float* __restrict__ s0,
+    uint16_t* __restrict__ statesT) {
+  using S = StatesShape<DK, C, BV, BWD>;
   constexpr int NT = S::NT, NRT = S::NRT, NKU_D = S::NKU_D, NKU_C = S::NKU_C, KH = S::KH;
   __shared__ __align__(1024) uint16_t ring[3 * S::SLOT];
   uint16_t* const slot0 = ring;
   uint16_t* const slot1 = ring + S::SLOT;
   uint16_t* const slot2 = ring + 2 * S::SLOT;
-  __shared__ __align__(16) bf16x8 bS_buf[2][NT][NKU_D][kWave];  // S_n of each chain as operand fragments
-  __shared__ __align__(16) bf16x8 bU_buf[2][NT][NKU_C][kWave];  // U'_n of each chain
+  __shared__ __align__(16) bf16x8 bS_buf[S::NCH][NT][NKU_D][kWave];  // S_n of each chain as operand fragments
+  __shared__ __align__(16) bf16x8 bU_buf[S::NCH][NT][NKU_C][kWave];  // U'_n of each chain
 
   const int x = blockIdx.x;
   int bh, vb;
@@ -216,8 +228,12 @@ __global__ __launch_bounds__(64 * 9) void recurrence_states_kernel(
         if (n + 1 < nc) load(ring + (sn == 2 ? 0 : (sn + 1) * S::SLOT));
       }
     };
-    if (role < S::kY0 + 2) yrole(std::integral_constant<int, 0>{});
-    else yrole(std::integral_constant<int, 1>{});
+    if constexpr (BWD) {
+      yrole(std::integral_constant<int, 0>{});
+    } else {
+      if (role < S::kY0 + 2) yrole(std::integral_constant<int, 0>{});
+      else yrole(std::integral_constant<int, 1>{});
+    }
   } else {
     // ----------------------------------------------------------------- S
     // rows: logical key dims 64 hh .. 64 hh + 63 of chain ch's state
@@ -230,17 +246,32 @@ __global__ __launch_bounds__(64 * 9) void recurrence_states_kernel(
 #pragma unroll
       for (int c = 0; c < NT; ++c)
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq)
-          St[d][c][qq] = (ch == 1 && key_phys(16 * (dt0 + d) + 4 * g + qq) == col0 + 16 * c + li) ? 1.0f : 0.0f;
-    auto publish = [&]() {
+        for (int qq = 0; qq < 4; ++qq) {
+          const int key = key_phys(16 * (dt0 + d) + 4 * g + qq);
+          if constexpr (BWD)
+            St[d][c][qq] = s0 != nullptr ? s0[(int64_t(bh) * DK + key) * DV + col0 + 16 * c + li] : 0.0f;
+          else
+            St[d][c][qq] = (ch == 1 && key == col0 + 16 * c + li) ? 1.0f : 0.0f;
+        }
+    // S_m as operand fragments; BWD: also the start state of chunk m, whose
+    // fragment (u, c) holds key dims 32 (ku0 + u) + 8 g .. + 7 of column
+    // col0 + 16 c + li
+    auto publish = [&](int m) {
 #pragma unroll
       for (int u = 0; u < KH; ++u)
 #pragma unroll
-        for (int c = 0; c < NT; ++c)
-          bS_buf[ch][c][ku0 + u][lane] = acc_frag<uint16_t>(St[2 * u][c], St[2 * u + 1][c]).v;
+        for (int c = 0; c < NT; ++c) {
+          const bf16x8 f = acc_frag<uint16_t>(St[2 * u][c], St[2 * u + 1][c]).v;
+          bS_buf[ch][c][ku0 + u][lane] = f;
+          if constexpr (BWD) {
+            if (m < nc)
+              *reinterpret_cast<bf16x8*>(statesT + ((sp.slot0 + m) * DV + col0 + 16 * c + li) * DK +
+                                         32 * (ku0 + u) + 8 * g) = f;
+          }
+        }
     };
-    publish();
-    run([&](const uint16_t* __restrict__ cur, int) {
+    publish(0);
+    run([&](const uint16_t* __restrict__ cur, int n) {
       sync();  // A
       Frag<uint16_t> KT[2 * KH][NKU_C];
 #pragma unroll
@@ -259,9 +290,9 @@ __global__ __launch_bounds__(64 * 9) void recurrence_states_kernel(
         for (int c = 0; c < NT; ++c)
 #pragma unroll
           for (int kt = 0; kt < NKU_C; ++kt) mma(St[d][c], KT[d][kt], bU[c][kt]);
-      publish();
+      publish(n + 1);
     });
-    const bool owner = ch == 0 ? vb < NVB_N : vb < NVB_M;
+    const bool owner = !BWD && (ch == 0 ? vb < NVB_N : vb < NVB_M);
     float* const out = ch == 0 ? nout : mout;
     const int pitch = ch == 0 ? DV : DK;
     if (owner) {
@@ -277,20 +308,20 @@ __global__ __launch_bounds__(64 * 9) void recurrence_states_kernel(
   }
 }
 
-template <int DK, int C, int BV>
+template <int DK, int C, int BV, bool BWD>
 hipError_t recurrence_states_launch_impl(const uint16_t* k, const uint16_t* v, const uint16_t* tws, float* nout,
                                          float* mout, int B, int H, int64_t L, int DV, const int32_t* cu, int N,
-                                         hipStream_t stream) {
+                                         const float* s0, uint16_t* statesT, hipStream_t stream) {
   const int NC = cu == nullptr ? int((L + C - 1) / C) : int(L / C) + N;
   const int BH = (cu == nullptr ? B : N) * H;
-  const int NVB_N = DV / BV, NVB_M = DK / BV;
+  const int NVB_N = DV / BV, NVB_M = BWD ? 0 : DK / BV;
   const int NVB = NVB_N > NVB_M ? NVB_N : NVB_M;
   const int nwg = BH * NVB;
   if (nwg == 0) return hipSuccess;
   const int remap = (BH % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((recurrence_states_kernel<DK, C, BV>), dim3(unsigned(nwg)),
-                     dim3(unsigned(StatesShape<DK, C, BV>::THREADS)), 0, stream, k, v, tws, nout, mout, H, L, NC,
-                     DV, NVB, NVB_N, NVB_M, remap, cu);
+  hipLaunchKernelGGL((recurrence_states_kernel<DK, C, BV, BWD>), dim3(unsigned(nwg)),
+                     dim3(unsigned(StatesShape<DK, C, BV, BWD>::THREADS)), 0, stream, k, v, tws, nout, mout, H, L,
+                     NC, DV, NVB, NVB_N, NVB_M, remap, cu, s0, statesT);
   return hipGetLastError();
 }
 

@@ -160,3 +160,26 @@ def test_backward_bf16_inputs_both_chunk_kernels(impl, ut, monkeypatch):
     inp = W.generate(w, device="cuda", B=1, H=3, L=200, seed=930)
     _check(inp, 64, f"bf16 inputs, {impl} chunk kernel, {ut} UT", seed=31)
     _check(inp, 64, f"bf16 inputs, {impl} chunk kernel, {ut} UT, Euler rule", seed=32, rule="euler")
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64)])
+def test_backward_chunk_state_kernels_agree(dk, dv, monkeypatch):
+    """The chunk-start states from the state-only kernel (stored transposed)
+    and from the role kernel (EFLA_BWD_STATES=roles, stored row-major) give the
+    same gradients up to the order of fp32 sums, with a ragged last chunk and
+    an initial state."""
+    require_gpu()
+    w = W.get("shape_340m", dk=dk, dv=dv, chunk=64)
+    inp = W.generate(w, device="cuda", B=2, H=3, L=300, seed=940 + dk + dv)
+    g = torch.Generator().manual_seed(41)
+    d_o = torch.randn(inp["v"].shape, generator=g).to(inp["v"].dtype).cuda()
+    dsf = torch.randn((2, 3, dk, dv), generator=g).cuda()
+    args = (inp["q"], inp["k"], inp["v"], inp["beta"], d_o, inp["s0"], dsf)
+    monkeypatch.delenv("EFLA_BWD_STATES", raising=False)
+    a = efla.efla_chunk_bwd(*args, chunk=64)
+    monkeypatch.setenv("EFLA_BWD_STATES", "roles")
+    b = efla.efla_chunk_bwd(*args, chunk=64)
+    torch.cuda.synchronize()
+    errs = {n: normwise(to_f64(x), to_f64(y)) for n, x, y in zip(NAMES, a, b)}
+    print(f"[bwd] state kernels dk{dk} dv{dv}: " + ", ".join(f"{n} {e:.2e}" for n, e in errs.items()), flush=True)
+    assert all(e <= 5e-3 for e in errs.values()), errs
