@@ -355,7 +355,8 @@ __global__ __launch_bounds__((BwdBf16Shape<DK, C>::NTH)) void bwd_chunk_bf16_ker
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
           const int r = r0 + 4 * g + qq;
-          if (r < valid) dv[row0 * DV + r * v_stride + v0 + c0 + li] = from_f32<uint16_t>(acc[qq]);
+          if (r < valid)
+            __builtin_nontemporal_store(from_f32<uint16_t>(acc[qq]), dv + row0 * DV + r * v_stride + v0 + c0 + li);
         }
       }
     }
@@ -508,9 +509,9 @@ __global__ __launch_bounds__((BwdBf16Shape<DK, C>::NTH)) void bwd_chunk_bf16_ker
     for (int qq = 0; qq < 4; ++qq) {
       const int r = r0 + 4 * g + qq, c = c0 + li;
       if (r < valid) {
-        dq[qk_row + r * qk_stride + c] = from_f32<uint16_t>(dQa[i][qq]);
-        dk[qk_row + r * qk_stride + c] =
-            from_f32<uint16_t>(dKa[i][qq] + 2.0f * dls[r] * to_f32(Kb[r * KBP + c]));
+        __builtin_nontemporal_store(from_f32<uint16_t>(dQa[i][qq]), dq + qk_row + r * qk_stride + c);
+        __builtin_nontemporal_store(from_f32<uint16_t>(dKa[i][qq] + 2.0f * dls[r] * to_f32(Kb[r * KBP + c])),
+                                    dk + qk_row + r * qk_stride + c);
       }
     }
   }
@@ -686,7 +687,8 @@ __global__ __launch_bounds__((BwdStateBf16Shape<DK, C>::NTH)) void bwd_state_bf1
     for (int i = 0; i < NS; ++i) {
       const int t = w + NWV * i, d0 = 16 * (t / 2), c0 = 16 * (t % 2);
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) dst[(d0 + 4 * g + qq) * DV + v0 + c0 + li] = from_f32<uint16_t>(dS[i][qq]);
+      for (int qq = 0; qq < 4; ++qq)
+        __builtin_nontemporal_store(from_f32<uint16_t>(dS[i][qq]), dst + (d0 + 4 * g + qq) * DV + v0 + c0 + li);
       st4(dST + (c0 + li) * KBP + d0 + 4 * g, dS[i]);
     }
     so.store(Kb, KBP, KbT, QbT, TbT, PbT, dOT, TBP, tid);

@@ -263,10 +263,11 @@ __global__ __launch_bounds__((64 * StatesShape<DK, C, BV, BWD>::NWAVES)) void re
         for (int c = 0; c < NT; ++c) {
           const bf16x8 f = acc_frag<uint16_t>(St[2 * u][c], St[2 * u + 1][c]).v;
           bS_buf[ch][c][ku0 + u][lane] = f;
-          if constexpr (BWD) {
+          if constexpr (BWD) {  // nontemporal: plain stores stalled this wave's LDS reads (1.4x longer pass)
             if (m < nc)
-              *reinterpret_cast<bf16x8*>(statesT + ((sp.slot0 + m) * DV + col0 + 16 * c + li) * DK +
-                                         32 * (ku0 + u) + 8 * g) = f;
+              __builtin_nontemporal_store(f, reinterpret_cast<bf16x8*>(statesT + ((sp.slot0 + m) * DV + col0 +
+                                                                                  16 * c + li) * DK +
+                                                                        32 * (ku0 + u) + 8 * g));
           }
         }
     };

@@ -164,7 +164,8 @@ __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict
 #pragma unroll
       for (int idx = lane; idx < C * (C / 8); idx += 64) {
         const int r = idx / (C / 8), c0 = (idx % (C / 8)) * 8;
-        *reinterpret_cast<u32x4*>(pdst16 + r * C + c0) = *reinterpret_cast<const u32x4*>(Ts + r * TP + c0);
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(Ts + r * TP + c0),
+                                    reinterpret_cast<u32x4*>(pdst16 + r * C + c0));
       }
       wave_lds_order();  // the G blocks reuse the scratch
     }
@@ -298,7 +299,8 @@ __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict
 #pragma unroll
       for (int idx = lane; idx < 32 * (C / 4); idx += 64) {
         const int r = idx / (C / 4), c0 = (idx % (C / 4)) * 4;
-        *reinterpret_cast<u32x4*>(xdst + (32 * hb + r) * C + c0) = *reinterpret_cast<const u32x4*>(Xst + r * XP + c0);
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(Xst + r * XP + c0),
+                                    reinterpret_cast<u32x4*>(xdst + (32 * hb + r) * C + c0));
       }
       wave_lds_order();  // the next block, then T's staging, reuse the scratch
     }
@@ -325,7 +327,12 @@ __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict
 #pragma unroll
   for (int idx = lane; idx < C * VPR; idx += 64) {
     const int r = idx / VPR, c0 = (idx % VPR) * 8;
-    *reinterpret_cast<u32x4*>(out + r * C + c0) = *reinterpret_cast<const u32x4*>(Ts + r * TP + c0);
+    const u32x4 val = *reinterpret_cast<const u32x4*>(Ts + r * TP + c0);
+    // nontemporal in the backward instance (the backward's passes ran faster
+    // so, as with its other workspace stores); the forward's recurrence reads
+    // T right after this kernel and ran ~8 us slower when T was written so
+    if constexpr (BWD) __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(out + r * C + c0));
+    else *reinterpret_cast<u32x4*>(out + r * C + c0) = val;
   }
 }
 
