@@ -13,9 +13,15 @@
 //                                      the state-only kernel writes them)
 //   dS [slots][dk][dv]   fp32          loss gradient at the end of the chunk
 //                                      (bf16, packed from the region's start,
-//                                      for the bf16 matrix-core kernels)
+//                                      for the bf16 matrix-core kernels;
+//                                      [slots][dv][dk] where the reverse pass
+//                                      of recurrence_reverse.h writes it)
+//   Qe [slots][C][dk]    bf16          Q - P T K (bf16 inputs only), read by
+//                                      that reverse pass
 #include <stdlib.h>
 #include <string.h>
+
+#include <type_traits>
 
 #include "bwd_bf16.h"
 #include "bwd_kernels.h"
@@ -39,7 +45,8 @@ BwdLayout bwd_layout(int B, int H, int64_t L, int DK, int DV, int C, size_t esz)
   w.a = w.p + align256(slots * C * C * 4);
   w.s = w.a + align256(slots * C * 4);
   w.ds = w.s + align256(slots * size_t(DK) * DV * esz);
-  w.total = w.ds + align256(slots * size_t(DK) * DV * 4);
+  w.qe = w.ds + align256(slots * size_t(DK) * DV * 4);
+  w.total = w.qe + (esz == 2 ? align256(slots * size_t(C) * DK * 2) : 0);
   return w;
 }
 
@@ -93,6 +100,15 @@ hipError_t bwd_launch_impl(const T* q, const T* k, const T* v, const T* beta, co
     bf16k = !(impl && strcmp(impl, "fp32") == 0) && bwd_bf16_supported(DK, DV, C);
   }
   const uint16_t* pws16 = reinterpret_cast<const uint16_t*>(pws);
+  uint16_t* qews = reinterpret_cast<uint16_t*>(ws + lay.qe);
+  // reverse pass in the form of the forward's state-only pass (its UT
+  // instance writes Qe; EFLA_BWD_REVERSE=stager keeps the sixteen-wavefront
+  // kernel)
+  bool rev = false;
+  if constexpr (sizeof(T) == 2) {
+    const char* impl = getenv("EFLA_BWD_REVERSE");
+    rev = bf16k && !(impl && strcmp(impl, "stager") == 0) && reverse_states_supported(DK, DV, C);
+  }
   bool states_t = false;  // the chunk states are stored transposed
   if (slots > 0) {
     // 1. T, X, P and a of every chunk: one wavefront per chunk for the bf16
@@ -107,7 +123,7 @@ hipError_t bwd_launch_impl(const T* q, const T* k, const T* v, const T* beta, co
         if (bf16k)
           hipLaunchKernelGGL((ut_wave_kernel<DK, C, true, true>), dim3(unsigned(nwg)), dim3(64 * NW), 0, s, k, beta,
                              tws, H, L, NC, slots, rule, static_cast<const int32_t*>(nullptr), 0, nwg,
-                             static_cast<int32_t*>(nullptr), q, xws, aws, pws);
+                             static_cast<int32_t*>(nullptr), q, xws, aws, pws, rev ? qews : nullptr);
         else
           hipLaunchKernelGGL((ut_wave_kernel<DK, C, true>), dim3(unsigned(nwg)), dim3(64 * NW), 0, s, k, beta, tws,
                              H, L, NC, slots, rule, static_cast<const int32_t*>(nullptr), 0, nwg,
@@ -128,7 +144,15 @@ hipError_t bwd_launch_impl(const T* q, const T* k, const T* v, const T* beta, co
   // on bf16 matrix cores where the shape allows, like step 4)
   bool state_done = false;
   if constexpr (sizeof(T) == 2 && DK % 32 == 0 && C % 32 == 0) {
-    if (bf16k) {
+    if (rev) {
+      if (hipError_t e = launch_reverse_states_bf16(reinterpret_cast<const uint16_t*>(k), qews,
+                                                    reinterpret_cast<const uint16_t*>(tws),
+                                                    reinterpret_cast<const uint16_t*>(dout), dsf, ds0,
+                                                    reinterpret_cast<uint16_t*>(dsws), B, H, L, DK, DV, C, s);
+          e != hipSuccess)
+        return e;
+      state_done = true;
+    } else if (bf16k) {
       hipLaunchKernelGGL((bwd_state_bf16_kernel<DK, C>), dim3(unsigned(BH * (DV / kBwdBV))),
                          dim3(BwdStateBf16Shape<DK, C>::NTH), 0, s,
                          q, k, dout, tws, pws16, dsf, reinterpret_cast<uint16_t*>(dsws), ds0, H, L, NC, DV,
@@ -146,14 +170,17 @@ hipError_t bwd_launch_impl(const T* q, const T* k, const T* v, const T* beta, co
   if constexpr (sizeof(T) == 2 && DK % 32 == 0 && C % 32 == 0) {
     if (bf16k) {
       const auto* ds16 = reinterpret_cast<const uint16_t*>(dsws);
-      if (states_t)
-        hipLaunchKernelGGL((bwd_chunk_bf16_kernel<DK, C, true>), dim3(unsigned(slots)),
-                           dim3(BwdBf16Shape<DK, C>::NTH), 0, s, q, k, v, beta, dout, tws, xws, aws, pws16, sws, ds16,
-                           dq, dk, dv, dbeta, H, L, NC, DV, rule);
-      else
-        hipLaunchKernelGGL((bwd_chunk_bf16_kernel<DK, C, false>), dim3(unsigned(slots)),
-                           dim3(BwdBf16Shape<DK, C>::NTH), 0, s, q, k, v, beta, dout, tws, xws, aws, pws16, sws, ds16,
-                           dq, dk, dv, dbeta, H, L, NC, DV, rule);
+      auto chunk = [&](auto stt, auto dstt) {
+        hipLaunchKernelGGL((bwd_chunk_bf16_kernel<DK, C, decltype(stt)::value, decltype(dstt)::value>),
+                           dim3(unsigned(slots)), dim3(BwdBf16Shape<DK, C>::NTH), 0, s, q, k, v, beta, dout, tws, xws,
+                           aws, pws16, sws, ds16, dq, dk, dv, dbeta, H, L, NC, DV, rule);
+      };
+      using Y = std::true_type;
+      using N = std::false_type;
+      if (states_t && rev) chunk(Y{}, Y{});
+      else if (states_t) chunk(Y{}, N{});
+      else if (rev) chunk(N{}, Y{});
+      else chunk(N{}, N{});
       return hipGetLastError();
     }
   }

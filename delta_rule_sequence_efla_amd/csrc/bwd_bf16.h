@@ -181,8 +181,8 @@ struct Bf16Stager {
 // Each unit is two consecutive rows of one 16-byte column slice, written as
 // in Bf16Stager: rows, and transposed as 4-byte words of the two rows.  STT:
 // S comes transposed (rows of d_k per value column), so its rows land in
-// S^T and its transpose in S.
-template <int DK, int C, int BV, int NTH, bool STT>
+// S^T and its transpose in S; DSTT likewise for dS'.
+template <int DK, int C, int BV, int NTH, bool STT, bool DSTT>
 struct BlockStager {
   static constexpr int U0 = (DK / 2) * (BV / 8), U1 = U0, U2 = (C / 2) * (BV / 8);
   static constexpr int TOT = U0 + U1 + 2 * U2, CNT = cdiv(TOT, NTH);
@@ -204,10 +204,11 @@ struct BlockStager {
       if (idx >= TOT) continue;
       int j;
       const int op = which(idx, j);
-      if (op == 0 && STT) {  // S^T rows: BV rows, stride DK
+      if ((op == 0 && STT) || (op == 1 && DSTT)) {  // S^T or dS'^T rows: BV rows, stride DK
         const int t = 2 * (j % (BV / 2)), c = (j / (BV / 2)) * 8;
+        const uint16_t* src = op == 0 ? st : dst;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) r[i][h] = *reinterpret_cast<const u32x4*>(st + (t + h) * DK + c);
+        for (int h = 0; h < 2; ++h) r[i][h] = *reinterpret_cast<const u32x4*>(src + (t + h) * DK + c);
       } else if (op <= 1) {  // S or dS' rows: DK rows, stride DV
         const int t = 2 * (j % (DK / 2)), c = (j / (DK / 2)) * 8;
         const uint16_t* src = op == 0 ? st : dst;
@@ -232,13 +233,13 @@ struct BlockStager {
       int j;
       const int op = which(idx, j);
       {  // eight bf16 columns
-        const bool st_t = STT && op == 0;
-        const int rows = st_t ? BV : op <= 1 ? DK : C;
+        const bool tr = (STT && op == 0) || (DSTT && op == 1);
+        const int rows = tr ? BV : op <= 1 ? DK : C;
         const int t = 2 * (j % (rows / 2)), c = (j / (rows / 2)) * 8;
-        uint16_t* X = st_t ? SvT : op == 0 ? Sv : op == 1 ? dSv : op == 2 ? Vv : dOv;
-        uint16_t* XT = st_t ? Sv : op == 0 ? SvT : op == 1 ? dSvT : op == 2 ? nullptr : dOvT;
-        const int pitch = st_t ? KBP : VBP;
-        const int pitchT = st_t ? VBP : op <= 1 ? KBP : TBP;
+        uint16_t* X = tr ? (op == 0 ? SvT : dSvT) : op == 0 ? Sv : op == 1 ? dSv : op == 2 ? Vv : dOv;
+        uint16_t* XT = tr ? (op == 0 ? Sv : dSv) : op == 0 ? SvT : op == 1 ? dSvT : op == 2 ? nullptr : dOvT;
+        const int pitch = tr ? KBP : VBP;
+        const int pitchT = tr ? VBP : op <= 1 ? KBP : TBP;
 #pragma unroll
         for (int h = 0; h < 2; ++h) *reinterpret_cast<u32x4*>(X + (t + h) * pitch + c) = r[i][h];
         if (XT != nullptr) {
@@ -258,8 +259,8 @@ struct BlockStager {
 };
 
 // STT: `states` holds each chunk's start state transposed, [slots][DV][DK]
-// (else [slots][DK][DV]).
-template <int DK, int C, bool STT>
+// (else [slots][DK][DV]); DSTT: `dstates` likewise.
+template <int DK, int C, bool STT, bool DSTT>
 __global__ __launch_bounds__((BwdBf16Shape<DK, C>::NTH)) void bwd_chunk_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ beta, const uint16_t* __restrict__ dout, const uint16_t* __restrict__ tws,
@@ -315,9 +316,9 @@ __global__ __launch_bounds__((BwdBf16Shape<DK, C>::NTH)) void bwd_chunk_bf16_ker
   const uint16_t* st = states + slot * DK * DV;
   const uint16_t* dst = dstates + slot * DK * DV;
   // one value block's operands, staged through registers one block ahead
-  BlockStager<DK, C, BV, NTH, STT> sb;
+  BlockStager<DK, C, BV, NTH, STT, DSTT> sb;
   auto load_block = [&](int v0) {
-    sb.load(st + (STT ? v0 * DK : v0), dst + v0, v + row0 * DV + v0, dout + row0 * DV + v0, DV, v_stride, valid,
+    sb.load(st + (STT ? v0 * DK : v0), dst + (DSTT ? v0 * DK : v0), v + row0 * DV + v0, dout + row0 * DV + v0, DV, v_stride, valid,
             tid);
   };
   load_block(0);

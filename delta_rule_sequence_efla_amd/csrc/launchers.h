@@ -79,6 +79,15 @@ hipError_t launch_recurrence_states_bf16(const uint16_t* k, const uint16_t* v, c
 hipError_t launch_chunk_states_t_bf16(const uint16_t* k, const uint16_t* v, const uint16_t* tws, const float* s0,
                                       uint16_t* statesT, int B, int H, int64_t L, int DK, int DV, int C,
                                       hipStream_t s);
+// bf16 reverse pass of the backward (recurrence_reverse.h): dS at the end of
+// every chunk, transposed, dstatesT [B*H*NC][DV][DK], and ds0 (fp32
+// [B*H][DK][DV]) from dsf (same layout, NULL: zero), given the effective
+// queries qe [B*H*NC][C][DK] of the backward UT instance; d_k 64 or 128,
+// chunk 64, d_v a multiple of 32.
+bool reverse_states_supported(int DK, int DV, int C);
+hipError_t launch_reverse_states_bf16(const uint16_t* k, const uint16_t* qe, const uint16_t* tws,
+                                      const uint16_t* dout, const float* dsf, float* ds0, uint16_t* dstatesT, int B,
+                                      int H, int64_t L, int DK, int DV, int C, hipStream_t s);
 
 // bf16 UT transform with one wavefront per chunk (ut_wave.h); d_k in
 // {32, 64, 128}, chunk in {32, 64}.
@@ -90,7 +99,7 @@ hipError_t launch_ut_wave_bf16(const uint16_t* k, const uint16_t* beta, uint16_t
 // Backward pass of the chunked forward (bwd.hip, bwd_kernels.h): dense
 // batches, any supported d_k / d_v / chunk; ws holds bwd_layout(...).total bytes.
 struct BwdLayout {
-  size_t t, x, p, a, s, ds, total;  // byte offsets of the workspace regions, and the size
+  size_t t, x, p, a, s, ds, qe, total;  // byte offsets of the workspace regions, and the size
 };
 BwdLayout bwd_layout(int B, int H, int64_t L, int DK, int DV, int C, size_t esz);
 template <typename T>

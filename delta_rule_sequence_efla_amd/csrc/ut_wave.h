@@ -71,7 +71,10 @@ __device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory")
 // slot: X (C x C, zeros above the diagonal), a (C) and P = tril(Q K^T) (C x C,
 // the diagonal included; if PB16 rounded to bf16 and packed as [slots][C][C]
 // bf16 from the start of the same buffer), with q the queries in the layout of
-// k.
+// k.  With PB16 and qtout it also writes the chunk's effective queries
+//     Qe = Q - P T K   (bf16 [slots][C][d_k], rows of tokens past the end zero),
+// the operand through which the output reads the chunk's start state
+// (O = Qe S + P T V), so that the reverse pass over the chunks needs no P.
 template <int DK, int C, bool BWD = false, bool PB16 = false>
 __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict__ k,
                                                       const uint16_t* __restrict__ beta,
@@ -81,9 +84,11 @@ __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict
                                                       const uint16_t* __restrict__ q = nullptr,
                                                       float* __restrict__ xout = nullptr,
                                                       float* __restrict__ aout = nullptr,
-                                                      float* __restrict__ pout = nullptr) {
+                                                      float* __restrict__ pout = nullptr,
+                                                      uint16_t* __restrict__ qtout = nullptr) {
   using S = UtWaveShape<DK, C>;
   constexpr int NRT = S::NRT, NKU = S::NKU, GBLK = S::GBLK, XP = S::XP, XBLK = S::XBLK, TP = S::TP;
+  constexpr int NKC = C / 32;  // k-units over the tokens of the chunk
   __shared__ __align__(16) unsigned char scratch_all[S::WAVES][S::SCRATCH];
   __shared__ float a_all[S::WAVES][64];
 
@@ -126,6 +131,9 @@ __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict
   }
   const float bt = (lane < valid) ? to_f32(beta[row0 + int64_t(lane) * H]) : 0.0f;
 
+  // P^T as B operand fragments (k = token l, column = row 16 rt + li of P),
+  // for Qe; ku <= rt / 2 (P is lower triangular)
+  Frag<uint16_t> PtB[NRT][NKC];
   if constexpr (BWD) {
     // P = tril(Q K^T), diagonal included, from Q row fragments in the same
     // per-lane order of the key dims as Kf
@@ -166,6 +174,17 @@ __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict
         const int r = idx / (C / 8), c0 = (idx % (C / 8)) * 8;
         __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(Ts + r * TP + c0),
                                     reinterpret_cast<u32x4*>(pdst16 + r * C + c0));
+      }
+      if (qtout != nullptr) {  // element e of lane group g: P[16 rt + li][32 ku + 16 (e / 4) + 4 g + e % 4]
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+          for (int ku = 0; ku < NKC; ++ku)
+            if (2 * ku <= rt) {
+              const bf16x4 lo = *reinterpret_cast<const bf16x4*>(Ts + (16 * rt + li) * TP + 32 * ku + 4 * g);
+              const bf16x4 hi = *reinterpret_cast<const bf16x4*>(Ts + (16 * rt + li) * TP + 32 * ku + 16 + 4 * g);
+              PtB[rt][ku].v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
       }
       wave_lds_order();  // the G blocks reuse the scratch
     }
@@ -333,6 +352,102 @@ __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict
     // T right after this kernel and ran ~8 us slower when T was written so
     if constexpr (BWD) __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(out + r * C + c0));
     else *reinterpret_cast<u32x4*>(out + r * C + c0) = val;
+  }
+
+  // ---- Qe = Q - P T K (backward instance) --------------------------------
+  // Every operand comes from registers (the products are laid out so that
+  // accumulator tiles are the next product's fragments, as above):
+  //   (P T)^T = T^T P^T: tiles (j, rt), j <= rt; T^T's fragment (j, ku) is
+  //     X[2 ku + e/4][j] scaled by a[16 j + li] (T = X diag(a)), P^T's is PtB;
+  //   K in accumulator layout, token rows x key columns, by products of the
+  //     K row fragments with a selection fragment (exact: one nonzero term);
+  //   (P T K)^T = K^T (P T)^T: for key block D, accumulator rows 4 g + qq are
+  //     key dims 32 (D / 2) + 8 g + 4 (D % 2) + qq, so the two blocks of a
+  //     32-dim unit are, element for element, a Q row fragment (8 consecutive
+  //     dims per lane): Qe leaves as 16-byte row pieces.
+  if constexpr (BWD && PB16) {
+    if (qtout != nullptr) {
+      // K and Q row fragments again, all issued at once here so that their
+      // latency overlaps the (P T)^T products (keeping Kf and Qf live through
+      // the solve would halve the wavefronts per SIMD; loaded one k-unit at a
+      // time they cost the kernel ~35 us)
+      Frag<uint16_t> Kr[NKU][NRT], Qr[NKU][NRT];
+#pragma unroll
+      for (int ku2 = 0; ku2 < NKU; ++ku2)
+#pragma unroll
+        for (int tb = 0; tb < NRT; ++tb) {
+          const int t = 16 * tb + li;
+          Kr[ku2][tb].v = bf16x8{};
+          Qr[ku2][tb].v = bf16x8{};
+          if (t < valid) {
+            Kr[ku2][tb].v = *reinterpret_cast<const bf16x8*>(k + (row0 + int64_t(t) * H) * DK + 32 * ku2 + 8 * g);
+            Qr[ku2][tb].v = *reinterpret_cast<const bf16x8*>(q + (row0 + int64_t(t) * H) * DK + 32 * ku2 + 8 * g);
+          }
+        }
+      float acol[NRT];
+#pragma unroll
+      for (int j = 0; j < NRT; ++j) acol[j] = as[16 * j + li];
+      f32x4 PTt[NRT][NRT];  // [j][rt]: (P T)^T[16 j + 4 g + qq][16 rt + li]
+#pragma unroll
+      for (int j = 0; j < NRT; ++j)
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+          PTt[j][rt] = zero4();
+          if (j > rt) continue;
+#pragma unroll
+          for (int ku = j / 2; ku <= rt / 2; ++ku) {
+            f32x4 lo = zero4(), hi = zero4();
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+              if (j <= 2 * ku) lo[qq] = X[2 * ku][j][qq] * acol[j];
+              if (j <= 2 * ku + 1) hi[qq] = X[2 * ku + 1][j][qq] * acol[j];
+            }
+            mma(PTt[j][rt], acc_frag<uint16_t>(lo, hi), PtB[rt][ku]);
+          }
+        }
+      Frag<uint16_t> PTB[NKC][NRT];  // (P T)^T as B operand: k = token, column = row 16 rt + li of P T
+#pragma unroll
+      for (int ku = 0; ku < NKC; ++ku)
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+          if (2 * ku <= rt) PTB[ku][rt] = acc_frag<uint16_t>(PTt[2 * ku][rt], PTt[2 * ku + 1][rt]);
+      uint16_t* qdst = qtout + id * int64_t(C) * DK;
+#pragma unroll
+      for (int ku2 = 0; ku2 < NKU; ++ku2) {
+        f32x4 Cq[2][NRT];  // [h][rt]: (P T K)[16 rt + li][32 ku2 + 8 g + 4 h + qq]
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          // selection: slot (g, e) of the k-unit is key dim 32 ku2 + 8 g + e in Kf;
+          // column li picks dim 32 ku2 + 8 (li / 4) + 4 hh + li % 4
+          Frag<uint16_t> sel;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            sel.v[e] = static_cast<__bf16>((g == (li >> 2) && e == 4 * hh + (li & 3)) ? 1.0f : 0.0f);
+          f32x4 ZK[NRT];  // K[16 tb + 4 g + qq][that dim of column li]
+#pragma unroll
+          for (int tb = 0; tb < NRT; ++tb) {
+            ZK[tb] = zero4();
+            mma(ZK[tb], Kr[ku2][tb], sel);
+          }
+#pragma unroll
+          for (int rt = 0; rt < NRT; ++rt) {
+            Cq[hh][rt] = zero4();
+#pragma unroll
+            for (int ku = 0; 2 * ku <= rt; ++ku)
+              mma(Cq[hh][rt], acc_frag<uint16_t>(ZK[2 * ku], ZK[2 * ku + 1]), PTB[ku][rt]);
+          }
+        }
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+          const int t = 16 * rt + li;
+          const bf16x8 qv = Qr[ku2][rt].v;
+          bf16x8 o;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = static_cast<__bf16>(static_cast<float>(qv[e]) - Cq[e / 4][rt][e % 4]);
+          __builtin_nontemporal_store(o, reinterpret_cast<bf16x8*>(qdst + t * DK + 32 * ku2 + 8 * g));
+        }
+      }
+    }
   }
 }
 

@@ -212,8 +212,10 @@ efla_status efla_chunk_recurrence(const void *q, const void *k, const void *v,
  * gradients in float32 (other bf16 shapes: float32 arithmetic on the widened
  * values); gradients are rounded to dtype on output.  The
  * workspace (size below) holds per chunk the UT-transform quantities, the
- * states the pass recomputes and their gradients; it is scratch and may be
- * reused once the call has completed on the stream.
+ * states the pass recomputes and their gradients (bf16: also the chunk's
+ * Q - P T K, with P = tril(Q K^T) and T the UT transform, through which the
+ * reverse pass over the chunks reads d_o); it is scratch and may be reused
+ * once the call has completed on the stream.
  * q, k, v, d_o and the workspace must be 16-byte aligned.
  */
 size_t efla_chunk_bwd_workspace_size(int B, int H, int64_t L, int d_k, int d_v, int chunk,

@@ -174,9 +174,10 @@ def test_backward_workspace_size_and_validation():
     f = efla.efla_chunk_bwd_workspace_size
     assert f(1, 1, 0, 16, 16, 16, torch.float32) == 0
     assert f(1, 1, 64, 24, 16, 16, torch.float32) == 0
-    # 1.3B shape: T (bf16), X, P (fp32), a, chunk states (bf16) and their gradients (fp32)
+    # 1.3B shape: T (bf16), X, P (fp32), a, chunk states (bf16), their gradients (fp32)
+    # and the effective queries Q - P T K (bf16)
     slots = 4 * 16 * 64
-    want = slots * (64 * 64 * 2 + 2 * 64 * 64 * 4 + 64 * 4 + 128 * 128 * 2 + 128 * 128 * 4)
+    want = slots * (64 * 64 * 2 + 2 * 64 * 64 * 4 + 64 * 4 + 128 * 128 * 2 + 128 * 128 * 4 + 64 * 128 * 2)
     assert f(4, 16, 4096, 128, 128, 64, torch.bfloat16) == want
     # float32: T and the states in float32
     want32 = slots * (64 * 64 * 4 + 2 * 64 * 64 * 4 + 64 * 4 + 128 * 128 * 4 + 128 * 128 * 4)

@@ -183,3 +183,21 @@ def test_backward_chunk_state_kernels_agree(dk, dv, monkeypatch):
     errs = {n: normwise(to_f64(x), to_f64(y)) for n, x, y in zip(NAMES, a, b)}
     print(f"[bwd] state kernels dk{dk} dv{dv}: " + ", ".join(f"{n} {e:.2e}" for n, e in errs.items()), flush=True)
     assert all(e <= 5e-3 for e in errs.values()), errs
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64)])
+@pytest.mark.parametrize("impl", ["state-only", "stager"])
+def test_backward_both_reverse_passes(dk, dv, impl, monkeypatch):
+    """Both reverse passes over the chunks against the oracle: the one in the
+    state-only form (through Q - P T K, dS stored transposed; the default) and
+    the sixteen-wavefront kernel (EFLA_BWD_REVERSE=stager, through P^T dO),
+    with a ragged last chunk, an initial state and a final-state gradient."""
+    require_gpu()
+    if impl == "stager":
+        monkeypatch.setenv("EFLA_BWD_REVERSE", "stager")
+    else:
+        monkeypatch.delenv("EFLA_BWD_REVERSE", raising=False)
+    w = W.get("shape_340m", dk=dk, dv=dv, chunk=64)
+    inp = W.generate(w, device="cuda", B=2, H=3, L=300, seed=970 + dk + dv)
+    _check(inp, 64, f"{impl} reverse pass dk{dk} dv{dv}", seed=43)
+    _check(inp, 64, f"{impl} reverse pass dk{dk} dv{dv}, Euler rule", seed=44, rule="euler")
