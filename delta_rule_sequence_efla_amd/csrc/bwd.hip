@@ -120,11 +120,15 @@ hipError_t bwd_launch_impl(const T* q, const T* k, const T* v, const T* beta, co
       if (bf16k || !(impl && strcmp(impl, "workgroup") == 0)) {
         constexpr int NW = UtWaveShape<DK, C>::WAVES;
         const int64_t nwg = (slots + NW - 1) / NW;
-        if (bf16k)
-          hipLaunchKernelGGL((ut_wave_kernel<DK, C, true, true>), dim3(unsigned(nwg)), dim3(64 * NW), 0, s, k, beta,
-                             tws, H, L, NC, slots, rule, static_cast<const int32_t*>(nullptr), 0, nwg,
-                             static_cast<int32_t*>(nullptr), q, xws, aws, pws, rev ? qews : nullptr);
-        else
+        if (bf16k) {
+          if (hipError_t e = launch_ut_wave_bwd_bf16(reinterpret_cast<const uint16_t*>(k),
+                                                     reinterpret_cast<const uint16_t*>(beta),
+                                                     reinterpret_cast<const uint16_t*>(q),
+                                                     reinterpret_cast<uint16_t*>(tws), xws, aws, pws,
+                                                     rev ? qews : nullptr, B, H, L, DK, C, rule, s);
+              e != hipSuccess)
+            return e;
+        } else
           hipLaunchKernelGGL((ut_wave_kernel<DK, C, true>), dim3(unsigned(nwg)), dim3(64 * NW), 0, s, k, beta, tws,
                              H, L, NC, slots, rule, static_cast<const int32_t*>(nullptr), 0, nwg,
                              static_cast<int32_t*>(nullptr), q, xws, aws, pws);

@@ -95,6 +95,12 @@ bool ut_wave_bf16_supported(int DK, int C);
 hipError_t launch_ut_wave_bf16(const uint16_t* k, const uint16_t* beta, uint16_t* tws, int B, int H, int64_t L,
                                int DK, int C, int rule, const int32_t* cu, int N, hipStream_t s,
                                int32_t* order = nullptr);
+// Its backward instance over a dense batch: T, X (fp32), a (fp32) and P
+// (bf16, packed at the start of pws) of every chunk slot, and with qe the
+// chunk's Q - P T K (bf16 [slots][C][DK]); same shapes.
+hipError_t launch_ut_wave_bwd_bf16(const uint16_t* k, const uint16_t* beta, const uint16_t* q, uint16_t* tws,
+                                   float* xws, float* aws, float* pws, uint16_t* qe, int B, int H, int64_t L, int DK,
+                                   int C, int rule, hipStream_t s);
 
 // Backward pass of the chunked forward (bwd.hip, bwd_kernels.h): dense
 // batches, any supported d_k / d_v / chunk; ws holds bwd_layout(...).total bytes.

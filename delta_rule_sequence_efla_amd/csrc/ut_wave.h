@@ -131,64 +131,6 @@ __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict
   }
   const float bt = (lane < valid) ? to_f32(beta[row0 + int64_t(lane) * H]) : 0.0f;
 
-  // P^T as B operand fragments (k = token l, column = row 16 rt + li of P),
-  // for Qe; ku <= rt / 2 (P is lower triangular)
-  Frag<uint16_t> PtB[NRT][NKC];
-  if constexpr (BWD) {
-    // P = tril(Q K^T), diagonal included, from Q row fragments in the same
-    // per-lane order of the key dims as Kf
-    Frag<uint16_t> Qf[NRT][NKU];
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      const int t = 16 * rt + li;
-      const uint16_t* src = q + (row0 + int64_t(t) * H) * DK + 8 * g;
-#pragma unroll
-      for (int ku = 0; ku < NKU; ++ku) {
-        if (t < valid) Qf[rt][ku].v = *reinterpret_cast<const bf16x8*>(src + 32 * ku);
-        else Qf[rt][ku].v = bf16x8{};
-      }
-    }
-    float* pdst = pout + id * int64_t(C) * C;                          // fp32 P
-    uint16_t* pdst16 = reinterpret_cast<uint16_t*>(pout) + id * int64_t(C) * C;  // bf16 P (PB16)
-#pragma unroll
-    for (int r = 0; r < NRT; ++r)
-#pragma unroll
-      for (int c = 0; c < NRT; ++c) {
-        f32x4 acc = zero4();
-        if (c <= r) {
-#pragma unroll
-          for (int ku = 0; ku < NKU; ++ku) mma(acc, Qf[r][ku], Kf[c][ku]);
-        }
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const int ii = 16 * r + 4 * g + qq, jj = 16 * c + li;
-          const float pv = jj <= ii ? acc[qq] : 0.0f;
-          if constexpr (PB16) Ts[ii * TP + jj] = from_f32<uint16_t>(pv);  // staged, stored as rows below
-          else pdst[ii * C + jj] = pv;
-        }
-      }
-    if constexpr (PB16) {  // bf16 P: 16-byte row stores from the staging tile
-      wave_lds_order();
-#pragma unroll
-      for (int idx = lane; idx < C * (C / 8); idx += 64) {
-        const int r = idx / (C / 8), c0 = (idx % (C / 8)) * 8;
-        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(Ts + r * TP + c0),
-                                    reinterpret_cast<u32x4*>(pdst16 + r * C + c0));
-      }
-      if (qtout != nullptr) {  // element e of lane group g: P[16 rt + li][32 ku + 16 (e / 4) + 4 g + e % 4]
-#pragma unroll
-        for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-          for (int ku = 0; ku < NKC; ++ku)
-            if (2 * ku <= rt) {
-              const bf16x4 lo = *reinterpret_cast<const bf16x4*>(Ts + (16 * rt + li) * TP + 32 * ku + 4 * g);
-              const bf16x4 hi = *reinterpret_cast<const bf16x4*>(Ts + (16 * rt + li) * TP + 32 * ku + 16 + 4 * g);
-              PtB[rt][ku].v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            }
-      }
-      wave_lds_order();  // the G blocks reuse the scratch
-    }
-  }
 
   // ---- G: diagonal tiles and the tiles above the diagonal ----------------
   // Gd[b][qq] = G[16b + 4g + qq][16b + li];  Gu[i][m][qq] = G[16m + 4g + qq][16i + li], m < i
@@ -354,36 +296,79 @@ __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict
     else *reinterpret_cast<u32x4*>(out + r * C + c0) = val;
   }
 
-  // ---- Qe = Q - P T K (backward instance) --------------------------------
-  // Every operand comes from registers (the products are laid out so that
-  // accumulator tiles are the next product's fragments, as above):
+  // ---- backward instance: P = tril(Q K^T) and Qe = Q - P T K -------------
+  // Q is read only here (the part above needs only K, whose fragments Kf are
+  // held through the solve: with accumulators in ordinary VGPRs that still
+  // leaves two wavefronts per SIMD).
+  //
+  // Qe: every operand comes from registers (the products are laid out so
+  // that accumulator tiles are the next product's fragments, as above):
   //   (P T)^T = T^T P^T: tiles (j, rt), j <= rt; T^T's fragment (j, ku) is
-  //     X[2 ku + e/4][j] scaled by a[16 j + li] (T = X diag(a)), P^T's is PtB;
+  //     X[2 ku + e/4][j] scaled by a[16 j + li] (T = X diag(a)), P^T's is
+  //     read back from P's staging tile;
   //   K in accumulator layout, token rows x key columns, by products of the
   //     K row fragments with a selection fragment (exact: one nonzero term);
   //   (P T K)^T = K^T (P T)^T: for key block D, accumulator rows 4 g + qq are
   //     key dims 32 (D / 2) + 8 g + 4 (D % 2) + qq, so the two blocks of a
   //     32-dim unit are, element for element, a Q row fragment (8 consecutive
   //     dims per lane): Qe leaves as 16-byte row pieces.
-  if constexpr (BWD && PB16) {
-    if (qtout != nullptr) {
-      // K and Q row fragments again, all issued at once here so that their
-      // latency overlaps the (P T)^T products (keeping Kf and Qf live through
-      // the solve would halve the wavefronts per SIMD; loaded one k-unit at a
-      // time they cost the kernel ~35 us)
-      Frag<uint16_t> Kr[NKU][NRT], Qr[NKU][NRT];
+  if constexpr (BWD) {
+    Frag<uint16_t> Kr[NRT][NKU], Qr[NRT][NKU];
 #pragma unroll
-      for (int ku2 = 0; ku2 < NKU; ++ku2)
+    for (int rt = 0; rt < NRT; ++rt) {
+      const int t = 16 * rt + li;
 #pragma unroll
-        for (int tb = 0; tb < NRT; ++tb) {
-          const int t = 16 * tb + li;
-          Kr[ku2][tb].v = bf16x8{};
-          Qr[ku2][tb].v = bf16x8{};
-          if (t < valid) {
-            Kr[ku2][tb].v = *reinterpret_cast<const bf16x8*>(k + (row0 + int64_t(t) * H) * DK + 32 * ku2 + 8 * g);
-            Qr[ku2][tb].v = *reinterpret_cast<const bf16x8*>(q + (row0 + int64_t(t) * H) * DK + 32 * ku2 + 8 * g);
-          }
+      for (int ku = 0; ku < NKU; ++ku) {
+        Kr[rt][ku].v = Kf[rt][ku].v;
+        Qr[rt][ku].v = bf16x8{};
+        if (t < valid) Qr[rt][ku].v = *reinterpret_cast<const bf16x8*>(q + (row0 + int64_t(t) * H) * DK + 32 * ku + 8 * g);
+      }
+    }
+    wave_lds_order();  // T's staging tile has been read: the scratch takes P
+    // P = tril(Q K^T), diagonal included, in the same per-lane order of the
+    // key dims for Q and K
+    float* pdst = pout + id * int64_t(C) * C;                                    // fp32 P
+    uint16_t* pdst16 = reinterpret_cast<uint16_t*>(pout) + id * int64_t(C) * C;  // bf16 P (PB16)
+#pragma unroll
+    for (int r = 0; r < NRT; ++r)
+#pragma unroll
+      for (int c = 0; c < NRT; ++c) {
+        f32x4 acc = zero4();
+        if (c <= r) {
+#pragma unroll
+          for (int ku = 0; ku < NKU; ++ku) mma(acc, Qr[r][ku], Kr[c][ku]);
         }
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const int ii = 16 * r + 4 * g + qq, jj = 16 * c + li;
+          const float pv = jj <= ii ? acc[qq] : 0.0f;
+          if constexpr (PB16) Ts[ii * TP + jj] = from_f32<uint16_t>(pv);  // staged, stored as rows below
+          else pdst[ii * C + jj] = pv;
+        }
+      }
+    if constexpr (PB16) {  // bf16 P: 16-byte row stores from the staging tile
+      wave_lds_order();
+#pragma unroll
+      for (int idx = lane; idx < C * (C / 8); idx += 64) {
+        const int r = idx / (C / 8), c0 = (idx % (C / 8)) * 8;
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(Ts + r * TP + c0),
+                                    reinterpret_cast<u32x4*>(pdst16 + r * C + c0));
+      }
+    }
+    if (PB16 && qtout != nullptr) {
+      // P^T as B operand fragments (k = token l, column = row 16 rt + li of P;
+      // element e of lane group g is P[16 rt + li][32 ku + 16 (e / 4) + 4 g + e % 4]),
+      // ku <= rt / 2 (P is lower triangular)
+      Frag<uint16_t> PtB[NRT][NKC];
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int ku = 0; ku < NKC; ++ku)
+          if (2 * ku <= rt) {
+            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(Ts + (16 * rt + li) * TP + 32 * ku + 4 * g);
+            const bf16x4 hi = *reinterpret_cast<const bf16x4*>(Ts + (16 * rt + li) * TP + 32 * ku + 16 + 4 * g);
+            PtB[rt][ku].v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          }
       float acol[NRT];
 #pragma unroll
       for (int j = 0; j < NRT; ++j) acol[j] = as[16 * j + li];
@@ -417,7 +402,7 @@ __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict
         f32x4 Cq[2][NRT];  // [h][rt]: (P T K)[16 rt + li][32 ku2 + 8 g + 4 h + qq]
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          // selection: slot (g, e) of the k-unit is key dim 32 ku2 + 8 g + e in Kf;
+          // selection: slot (g, e) of the k-unit is key dim 32 ku2 + 8 g + e in Kr;
           // column li picks dim 32 ku2 + 8 (li / 4) + 4 hh + li % 4
           Frag<uint16_t> sel;
 #pragma unroll
@@ -427,7 +412,7 @@ __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict
 #pragma unroll
           for (int tb = 0; tb < NRT; ++tb) {
             ZK[tb] = zero4();
-            mma(ZK[tb], Kr[ku2][tb], sel);
+            mma(ZK[tb], Kr[tb][ku2], sel);
           }
 #pragma unroll
           for (int rt = 0; rt < NRT; ++rt) {
@@ -440,7 +425,7 @@ __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
           const int t = 16 * rt + li;
-          const bf16x8 qv = Qr[ku2][rt].v;
+          const bf16x8 qv = Qr[rt][ku2].v;
           bf16x8 o;
 #pragma unroll
           for (int e = 0; e < 8; ++e) o[e] = static_cast<__bf16>(static_cast<float>(qv[e]) - Cq[e / 4][rt][e % 4]);
