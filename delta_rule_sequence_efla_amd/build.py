@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libefla.so")
 SOURCES = ["api.hip", "step_kernels.hip", "chunk_bf16.hip", "chunk_bf16_roles.hip", "chunk_bf16_split.hip",
-           "chunk_bf16_states.hip", "ut_bf16.hip", "chunk_f32.hip", "bwd.hip", "seg.hip"]
+           "chunk_bf16_states.hip", "ut_bf16.hip", "chunk_f32.hip", "bwd.hip", "bwd_bf16_chunk.hip", "seg.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 CFLAGS = [
@@ -34,7 +34,8 @@ CFLAGS = [
 SOURCE_FLAGS = {"chunk_bf16_roles.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
                 "chunk_bf16_split.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
                 "chunk_bf16_states.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-                "ut_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+                "ut_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "bwd_bf16_chunk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

@@ -174,6 +174,17 @@ hipError_t bwd_launch_impl(const T* q, const T* k, const T* v, const T* beta, co
   if constexpr (sizeof(T) == 2 && DK % 32 == 0 && C % 32 == 0) {
     if (bf16k) {
       const auto* ds16 = reinterpret_cast<const uint16_t*>(dsws);
+      // the two-workgroup kernel where both state arrays are transposed
+      // (EFLA_BWD_CHUNK=stager keeps the one-workgroup kernel)
+      const char* cimpl = getenv("EFLA_BWD_CHUNK");
+      if (states_t && rev && !(cimpl && strcmp(cimpl, "stager") == 0) && bwd_chunk_tr_bf16_supported(DK, DV, C))
+        return launch_bwd_chunk_tr_bf16(reinterpret_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(k),
+                                        reinterpret_cast<const uint16_t*>(v), reinterpret_cast<const uint16_t*>(beta),
+                                        reinterpret_cast<const uint16_t*>(dout), reinterpret_cast<const uint16_t*>(tws),
+                                        xws, aws, pws16, reinterpret_cast<const uint16_t*>(sws), ds16,
+                                        reinterpret_cast<uint16_t*>(dq), reinterpret_cast<uint16_t*>(dk),
+                                        reinterpret_cast<uint16_t*>(dv), reinterpret_cast<uint16_t*>(dbeta), B, H, L,
+                                        DK, DV, C, rule, s);
       auto chunk = [&](auto stt, auto dstt) {
         hipLaunchKernelGGL((bwd_chunk_bf16_kernel<DK, C, decltype(stt)::value, decltype(dstt)::value>),
                            dim3(unsigned(slots)), dim3(BwdBf16Shape<DK, C>::NTH), 0, s, q, k, v, beta, dout, tws, xws,

@@ -1,0 +1,399 @@
+// bwd_chunk_tr.h -- the per-chunk gradients of the backward pass for bf16
+// inputs in ~76 KiB of LDS, so that two workgroups share a compute unit and
+// one's loads and barriers overlap the other's products.
+//
+// Same formulas, value blocks and roundings as bwd_chunk_bf16_kernel
+// (bwd_bf16.h):
+//     D = V - K S      dU = P^T dO + K dS'      U = T D      dD = T^T dU (= dV)
+//     dQ += dO S^T     dK += U dS'^T - dD S^T   dP += dO U^T  dT += dU D^T
+// per block of 32 value columns, then the UT-transform part
+//     dQ += dP K;  dK += dP^T Q;  dX = dT diag(a);  da_j = sum_i dT_ij X_ij;
+//     W = X^T dX;  dA = -W X^T (strictly lower);  da_i += sum_{j<i} dA_ij G_ij;
+//     dG = diag(a) dA;  dbeta, dlambda;  dK += (dG + dG^T) K + 2 diag(dlambda) K.
+// What differs is the layout: every operand is held once, as a swizzled bf16
+// tile, and read in whichever orientation a product needs -- rows as 16- or
+// 8-byte fragments, columns by transposing reads (ds_read_b64_tr_b16) --
+// instead of in both layouts; the fp32 C x C arrays of the UT-transform part
+// take the space of the value-block arrays, and W and dA share one.  K, the
+// states S and dS' come in the key-dimension order of the recurrence kernels
+// (lds_ring.h), so the products over the key dimension pair them as stored,
+// and dQ, dK come out with logical key columns, mapped back when stored.  The
+// states and dS' are read transposed, [slots][d_v][d_k], as the state-only
+// passes write them.  Eight wavefronts; the VGPRs stay at most 128 so that
+// two workgroups fit a SIMD's register file.
+#pragma once
+
+#include "bwd_kernels.h"
+#include "lds_ring.h"
+
+namespace efla {
+
+template <int DK, int C>
+struct BwdTrShape {
+  static_assert(C == 64 && (DK == 64 || DK == 128), "shapes of the two-workgroup per-chunk kernel");
+  static constexpr int BV = 32, NWV = 8, NTH = NWV * kWave;
+  static constexpr int NRT = C / 16, NDT = DK / 16, NKU_D = DK / 32, NKU_C = C / 32;
+  static constexpr int NQ = NRT * NDT / NWV;  // dQ / dK tiles per wavefront
+  static constexpr int NP = NRT * NRT / NWV;  // dP / dT (and C x C) tiles per wavefront
+  static constexpr int CPF = C + 4;           // pitch (floats) of the fp32 C x C arrays
+  // byte offsets; the loop's arrays
+  static constexpr int KT = 0;                 // K [C][DK] (stays to the end)
+  static constexpr int TT = KT + C * DK * 2;   // T [C][C]
+  static constexpr int PT = TT + C * C * 2;    // P [C][C]
+  static constexpr int ST = PT + C * C * 2;    // S^T of the value block [BV][DK]
+  static constexpr int DST = ST + BV * DK * 2;  // dS'^T [BV][DK]
+  static constexpr int VT = DST + BV * DK * 2;  // V block [C][BV]
+  static constexpr int DOT = VT + C * BV * 2;   // dO block
+  static constexpr int DT = DOT + C * BV * 2;   // D
+  static constexpr int DUT = DT + C * BV * 2;   // dU
+  static constexpr int UT = DUT + C * BV * 2;   // U
+  static constexpr int DDT = UT + C * BV * 2;   // dD
+  static constexpr int LOOP_END = DDT + C * BV * 2;
+  // the UT-transform part's arrays
+  static constexpr int QT = TT;                 // Q [C][DK]
+  static constexpr int DPT = QT + C * DK * 2;   // dP [C][C] bf16
+  static constexpr int WF = TT;                 // W = X^T dX (after Q and dP), fp32 [C][CPF]
+  static constexpr int A0 = (DPT + C * C * 2 > WF + C * CPF * 4) ? DPT + C * C * 2 : WF + C * CPF * 4;  // dT, dX, dA
+  static constexpr int XF = A0 + C * CPF * 4;   // X, then dG + dG^T (bf16 [C][C])
+  static constexpr int RED = XF + C * CPF * 4;  // partial sums, one per thread
+  static constexpr int TAIL_END = RED + NTH * 4;
+  static constexpr int BYTES = LOOP_END > TAIL_END ? LOOP_END : TAIL_END;
+};
+
+inline bool bwd_chunk_tr_supported(int DK, int DV, int C) {
+  return C == 64 && (DK == 64 || DK == 128) && DV % 32 == 0;
+}
+
+// `states` and `dstates`: [slots][DV][DK] bf16 (the chunk's start state and the
+// loss gradient at its end, transposed).
+template <int DK, int C>
+__global__ __launch_bounds__((BwdTrShape<DK, C>::NTH)) __attribute__((amdgpu_waves_per_eu(4, 4))) void bwd_chunk_tr_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ beta, const uint16_t* __restrict__ dout, const uint16_t* __restrict__ tws,
+    const float* __restrict__ xws, const float* __restrict__ aws, const uint16_t* __restrict__ pws,
+    const uint16_t* __restrict__ states, const uint16_t* __restrict__ dstates, uint16_t* __restrict__ dq,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, uint16_t* __restrict__ dbeta, int H, int64_t L, int NC,
+    int DV, int rule) {
+  using S = BwdTrShape<DK, C>;
+  constexpr int BV = S::BV, NRT = S::NRT, NDT = S::NDT, NKU_D = S::NKU_D, NKU_C = S::NKU_C, NWV = S::NWV;
+  constexpr int NTH = S::NTH, NQ = S::NQ, NP = S::NP, CPF = S::CPF;
+  __shared__ __align__(1024) unsigned char lds[S::BYTES];
+  __shared__ float as[C], das[C], dls[C], lam[C];
+  auto b16 = [&](int off) { return reinterpret_cast<uint16_t*>(lds + off); };
+  auto f32p = [&](int off) { return reinterpret_cast<float*>(lds + off); };
+  uint16_t *Kt = b16(S::KT), *Tt = b16(S::TT), *Pt = b16(S::PT), *St = b16(S::ST), *dSt = b16(S::DST);
+  uint16_t *Vt = b16(S::VT), *dOt = b16(S::DOT), *Dt = b16(S::DT), *dUt = b16(S::DUT), *Ut = b16(S::UT);
+  uint16_t* dDt = b16(S::DDT);
+
+  const int64_t slot = blockIdx.x;
+  const int n = int(slot % NC);
+  const int64_t bh = slot / NC, h = bh % H;
+  const SeqSpan sp = seq_span<C>(nullptr, int(bh / H), h, H, L, NC);
+  const int64_t t0 = int64_t(n) * C;
+  const int valid = int(sp.len - t0 < C ? sp.len - t0 : C);
+  const int64_t row0 = (sp.bos + t0) * H + h;
+  const int tid = threadIdx.x, lane0 = tid & 63, w = wave_id(), li0 = lane0 & 15, g0 = lane0 >> 4;
+  const int64_t qk_stride = int64_t(H) * DK, v_stride = int64_t(H) * DV;
+  auto ld16 = [](const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); };
+  // keeps the scheduler from hoisting the next tile's fragment reads over this
+  // one's products (which would need more than the 128 VGPRs two workgroups
+  // per compute unit allow)
+  auto fence_sched = []() { __builtin_amdgcn_sched_barrier(0); };
+  auto st16 = [](uint16_t* p, const u32x4& x) { *reinterpret_cast<u32x4*>(p) = x; };
+  constexpr u32x4 Z{0u, 0u, 0u, 0u};
+
+  // ---- the chunk's K, T, P (16-byte units dealt over the threads) ----------
+  constexpr int UK = C * DK / 8, UC = C * C / 8;  // 16-byte units of a [C][DK] / [C][C] tile
+  static_assert(UK % NTH == 0 && UC == NTH, "whole units per thread");
+  {
+    u32x4 rk[UK / NTH], rt_, rp;
+#pragma unroll
+    for (int i = 0; i < UK / NTH; ++i) {
+      const int u = tid + NTH * i, r = u / (DK / 8), ch = u % (DK / 8);
+      rk[i] = r < valid ? ld16(k + (row0 + int64_t(r) * H) * DK + 8 * ch) : Z;
+    }
+    {
+      const int r = tid / (C / 8), ch = tid % (C / 8);
+      rt_ = ld16(tws + slot * C * C + r * C + 8 * ch);
+      rp = ld16(pws + slot * C * C + r * C + 8 * ch);
+    }
+#pragma unroll
+    for (int i = 0; i < UK / NTH; ++i) {
+      const int u = tid + NTH * i, r = u / (DK / 8), ch = u % (DK / 8);
+      st16(Kt + swzw_off<DK>(r, 8 * ch), rk[i]);
+    }
+    const int r = tid / (C / 8), ch = tid % (C / 8);
+    st16(Tt + swz_off<C>(r, 8 * ch), rt_);
+    st16(Pt + swz_off<C>(r, 8 * ch), rp);
+  }
+  if (tid < C) as[tid] = aws[slot * C + tid];
+
+  // ---- one value block's S^T, dS'^T, V and dO, one unit of each per thread --
+  constexpr int US = BV * DK / 8, UV = C * BV / 8;
+  static_assert(US <= NTH && 2 * UV == NTH, "one unit of each operand per thread");
+  u32x4 rs, rds, rvo;
+  // wave-uniform bases and 32-bit lane offsets, so the loads take a scalar base
+  auto load_block = [&](int v0, int tid) {
+    rs = rds = Z;
+    const uint16_t* sb = states + (slot * DV + v0) * DK;
+    const uint16_t* db = dstates + (slot * DV + v0) * DK;
+    if (tid < US) {
+      const uint32_t o = uint32_t((tid / (DK / 8)) * DK + 8 * (tid % (DK / 8)));
+      rs = ld16(sb + o);
+      rds = ld16(db + o);
+    }
+    const int u = tid % UV, r = u / (BV / 8), ch = u % (BV / 8);
+    const uint16_t* vb = v + row0 * DV + v0;
+    const uint16_t* ob = dout + row0 * DV + v0;
+    const uint32_t o = uint32_t(r * v_stride + 8 * ch);
+    rvo = r < valid ? ld16((tid < UV ? vb : ob) + o) : Z;
+  };
+  auto store_block = [&](int tid) {
+    if (tid < US) {
+      const int r = tid / (DK / 8), ch = tid % (DK / 8);
+      st16(St + swzw_off<DK>(r, 8 * ch), rs);
+      st16(dSt + swzw_off<DK>(r, 8 * ch), rds);
+    }
+    const int u = tid % UV, r = u / (BV / 8), ch = u % (BV / 8);
+    st16((tid < UV ? Vt : dOt) + swz_off<BV>(r, 8 * ch), rvo);
+  };
+  // an accumulator tile (rows 16 rt + 4 g + qq, column 16 c + li) into a [C][BV] tile
+  auto put = [&](uint16_t* X, const f32x4& a, int rt, int c, int li, int g) {
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) X[swz_off<BV>(16 * rt + 4 * g + qq, 16 * c + li)] = from_f32<uint16_t>(a[qq]);
+  };
+
+  f32x4 dQa[NQ], dKa[NQ], dPa[NP], dTa[NP];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) dQa[i] = dKa[i] = zero4();
+#pragma unroll
+  for (int i = 0; i < NP; ++i) dPa[i] = dTa[i] = zero4();
+
+  // the tail's Q and X
+  constexpr int UX = C * C / 4;  // 16-byte units of fp32 X
+  u32x4 rq[UK / NTH], rx[UX / NTH];
+  static_assert(UX % NTH == 0, "whole units per thread");
+
+  load_block(0, tid);
+  for (int v0 = 0; v0 < DV; v0 += BV) {
+    // the lane indices as values the compiler cannot see to be the same in
+    // every block, so that the fragment addresses built from them are formed
+    // here rather than held in registers across the loop
+    int li = li0, g = g0, lane = lane0, tidv = tid;
+    asm volatile("" : "+v"(li), "+v"(g), "+v"(lane), "+v"(tidv));
+    __syncthreads();  // the previous block's arrays are free (and the chunk's K, T, P are in place)
+    store_block(tidv);
+    if (v0 + BV < DV) load_block(v0 + BV, tidv);  // in flight during this block
+    __syncthreads();
+    // D = V - K S and dU = P^T dO + K dS': tile (rt, c) of each, wavefront w = 2 rt + c
+    {
+      const int rt = w >> 1, c = w & 1;
+      f32x4 d = zero4(), du = zero4();
+#pragma unroll
+      for (int ku = 0; ku < NKU_D; ++ku) {
+        const Frag<uint16_t> a = wide_frag<DK>(Kt, 16 * rt + li, ku, g);
+        mma(d, a, wide_frag<DK>(St, 16 * c + li, ku, g));
+        mma(du, a, wide_frag<DK>(dSt, 16 * c + li, ku, g));
+      }
+#pragma unroll
+      for (int ku = 0; ku < NKU_C; ++ku)
+        if (32 * ku + 31 >= 16 * rt) mma(du, sw_frag_tr<C>(Pt, 16 * rt, ku, lane), sw_frag_tr<BV>(dOt, 16 * c, ku, lane));
+      const bf16x4 vv = lds_read_tr(Vt + swz_off<BV>(16 * rt + 4 * g + (li >> 2), 16 * c + 4 * (li & 3)));
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) d[qq] = static_cast<float>(vv[qq]) - d[qq];
+      put(Dt, d, rt, c, li, g);
+      put(dUt, du, rt, c, li, g);
+    }
+    __syncthreads();
+    // U = T D and dD = T^T dU (= dV)
+    {
+      const int rt = w >> 1, c = w & 1;
+      f32x4 u = zero4(), dd = zero4();
+#pragma unroll
+      for (int ku = 0; ku < NKU_C; ++ku) {
+        if (32 * ku <= 16 * rt + 15) mma(u, sw_frag<C>(Tt, 16 * rt + li, ku, g), sw_frag_tr<BV>(Dt, 16 * c, ku, lane));
+        if (32 * ku + 31 >= 16 * rt)
+          mma(dd, sw_frag_tr<C>(Tt, 16 * rt, ku, lane), sw_frag_tr<BV>(dUt, 16 * c, ku, lane));
+      }
+      put(Ut, u, rt, c, li, g);
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int r = 16 * rt + 4 * g + qq;
+        if (r < valid)
+          __builtin_nontemporal_store(from_f32<uint16_t>(dd[qq]), dv + row0 * DV + r * v_stride + v0 + 16 * c + li);
+        dd[qq] = -dd[qq];
+      }
+      put(dDt, dd, rt, c, li, g);  // as -dD
+    }
+    __syncthreads();
+    // dQ += dO S^T;  dK += U dS'^T - dD S^T  (tiles (rt, dt), logical key columns);
+    // dP += dO U^T;  dT += dU D^T  (lower tiles)
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int t = w + NWV * i, rt = t / NDT, dt = t % NDT;
+      const Frag<uint16_t> bS = wide_frag_tr<DK>(St, dt, 0, lane);
+      mma(dQa[i], sw_frag<BV>(dOt, 16 * rt + li, 0, g), bS);
+      mma(dKa[i], sw_frag<BV>(Ut, 16 * rt + li, 0, g), wide_frag_tr<DK>(dSt, dt, 0, lane));
+      mma(dKa[i], sw_frag<BV>(dDt, 16 * rt + li, 0, g), bS);
+      fence_sched();
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int t = w + NWV * i, rt = t / NRT, jt = t % NRT;
+      if (jt <= rt) {
+        mma(dPa[i], sw_frag<BV>(dOt, 16 * rt + li, 0, g), sw_frag<BV>(Ut, 16 * jt + li, 0, g));
+        mma(dTa[i], sw_frag<BV>(dUt, 16 * rt + li, 0, g), sw_frag<BV>(Dt, 16 * jt + li, 0, g));
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < UK / NTH; ++i) {
+    const int u = tid + NTH * i, r = u / (DK / 8), ch = u % (DK / 8);
+    rq[i] = r < valid ? ld16(q + (row0 + int64_t(r) * H) * DK + 8 * ch) : Z;
+  }
+#pragma unroll
+  for (int i = 0; i < UX / NTH; ++i) {
+    const int u = tid + NTH * i, r = u / (C / 4), ch = u % (C / 4);
+    rx[i] = *reinterpret_cast<const u32x4*>(xws + slot * C * C + r * C + 4 * ch);
+  }
+  __syncthreads();  // done with the loop's arrays (K stays)
+
+  // ---- the UT-transform part -----------------------------------------------
+  const int li = li0, g = g0, lane = lane0;
+  uint16_t *Qt = b16(S::QT), *dPt = b16(S::DPT), *Eb = b16(S::XF);
+  float *W = f32p(S::WF), *A0 = f32p(S::A0), *X = f32p(S::XF), *red = f32p(S::RED);
+  constexpr int NPART = NTH / C, RPP = C / NPART;
+  const int cr = tid % C, prt = tid / C;
+  // dP (lower, diagonal included) as bf16, dT (lower) fp32; Q and X
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int t = w + NWV * i, rt = t / NRT, jt = t % NRT;
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int r = 16 * rt + 4 * g + qq, c = 16 * jt + li;
+      dPt[swz_off<C>(r, c)] = from_f32<uint16_t>(c <= r ? dPa[i][qq] : 0.0f);
+      A0[r * CPF + c] = c <= r ? dTa[i][qq] : 0.0f;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < UK / NTH; ++i) {
+    const int u = tid + NTH * i, r = u / (DK / 8), ch = u % (DK / 8);
+    st16(Qt + swzw_off<DK>(r, 8 * ch), rq[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < UX / NTH; ++i) {
+    const int u = tid + NTH * i, r = u / (C / 4), ch = u % (C / 4);
+    *reinterpret_cast<u32x4*>(X + r * CPF + 4 * ch) = rx[i];
+  }
+  __syncthreads();
+  // dQ += dP K;  dK += dP^T Q;  da_j = sum_i dT_ij X_ij (partial sums)
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int t = w + NWV * i, rt = t / NDT, dt = t % NDT;
+#pragma unroll
+    for (int ku = 0; ku < NKU_C; ++ku) {
+      if (32 * ku <= 16 * rt + 15)
+        mma(dQa[i], sw_frag<C>(dPt, 16 * rt + li, ku, g), wide_frag_tr<DK>(Kt, dt, ku, lane));
+      if (32 * ku + 31 >= 16 * rt)
+        mma(dKa[i], sw_frag_tr<C>(dPt, 16 * rt, ku, lane), wide_frag_tr<DK>(Qt, dt, ku, lane));
+    }
+    fence_sched();
+  }
+  {
+    float s = 0.0f;
+#pragma unroll
+    for (int r = prt * RPP; r < (prt + 1) * RPP; ++r) s = fmaf(A0[r * CPF + cr], X[r * CPF + cr], s);
+    red[prt * C + cr] = s;
+  }
+  __syncthreads();
+  if (tid < C) {
+    float s = 0.0f;
+#pragma unroll
+    for (int p = 0; p < NPART; ++p) s += red[p * C + tid];
+    das[tid] = s;
+  }
+  for (int i = tid; i < C * C; i += NTH) A0[(i / C) * CPF + i % C] *= as[i % C];  // dX = dT diag(a)
+  __syncthreads();
+  // W = X^T dX (into the space of Q and dP)
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int t = w + NWV * i, rt = t / NRT, jt = t % NRT;
+    f32x4 acc = zero4();
+    tile_mma16<true, false>(acc, X, CPF, A0, CPF, 16 * rt, 16 * jt, C, li, g);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) W[(16 * rt + 4 * g + qq) * CPF + 16 * jt + li] = acc[qq];
+  }
+  __syncthreads();
+  // dA = -W X^T (strictly lower) over dX;  G = K K^T on the lower tiles: lambda
+  // (its diagonal) and the row sums of dA G, tile column by tile column
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int t = w + NWV * i, rt = t / NRT, jt = t % NRT;
+    f32x4 acc = zero4(), gg = zero4();
+    tile_mma16<false, true>(acc, W, CPF, X, CPF, 16 * rt, 16 * jt, C, li, g);
+    if (jt <= rt) {
+#pragma unroll
+      for (int ku = 0; ku < NKU_D; ++ku)
+        mma(gg, wide_frag<DK>(Kt, 16 * rt + li, ku, g), wide_frag<DK>(Kt, 16 * jt + li, ku, g));
+    }
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int r = 16 * rt + 4 * g + qq, c = 16 * jt + li;
+      const float da = c < r ? -acc[qq] : 0.0f;
+      A0[r * CPF + c] = da;
+      if (c == r) lam[r] = gg[qq];
+      float s = da * gg[qq];
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);  // over the 16 columns of the tile
+      if (li == 0) red[jt * C + r] = s;
+    }
+  }
+  __syncthreads();
+  // da_i += sum_{j<i} dA_ij G_ij;  dG + dG^T with dG = diag(a) dA, as bf16 (over X)
+  if (tid < C) {
+    float s = 0.0f;
+#pragma unroll
+    for (int jt = 0; jt < NRT; ++jt) s += red[jt * C + tid];
+    das[tid] += s;
+  }
+  for (int i = tid; i < C * C; i += NTH) {
+    const int r = i / C, c = i % C;
+    Eb[swz_off<C>(r, c)] = from_f32<uint16_t>(as[r] * A0[r * CPF + c] + as[c] * A0[c * CPF + r]);
+  }
+  __syncthreads();
+  // dbeta, dlambda
+  if (tid < C) {
+    float dl = 0.0f;
+    if (tid < valid) {
+      const float bt = to_f32(beta[row0 + int64_t(tid) * H]);
+      float da_db, da_dl;
+      efla_alpha_grad(bt, lam[tid], rule, da_db, da_dl);
+      dl = das[tid] * da_dl;
+      dbeta[row0 + int64_t(tid) * H] = from_f32<uint16_t>(das[tid] * da_db);
+    }
+    dls[tid] = dl;
+  }
+  __syncthreads();
+  // dK += (dG + dG^T) K + 2 diag(dlambda) K;  dq, dk (physical key columns)
+  const int64_t qk_row = row0 * DK;
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int t = w + NWV * i, rt = t / NDT, dt = t % NDT;
+#pragma unroll
+    for (int ku = 0; ku < NKU_C; ++ku)
+      mma(dKa[i], sw_frag<C>(Eb, 16 * rt + li, ku, g), wide_frag_tr<DK>(Kt, dt, ku, lane));
+    fence_sched();
+    const int cp = key_phys(16 * dt + li);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int r = 16 * rt + 4 * g + qq;
+      if (r < valid) {
+        const float kv = to_f32(Kt[swzw_off<DK>(r, cp)]);
+        __builtin_nontemporal_store(from_f32<uint16_t>(dQa[i][qq]), dq + qk_row + r * qk_stride + cp);
+        __builtin_nontemporal_store(from_f32<uint16_t>(dKa[i][qq] + 2.0f * dls[r] * kv), dk + qk_row + r * qk_stride + cp);
+      }
+    }
+  }
+}
+
+}  // namespace efla

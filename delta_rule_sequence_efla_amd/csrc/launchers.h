@@ -95,6 +95,15 @@ bool ut_wave_bf16_supported(int DK, int C);
 hipError_t launch_ut_wave_bf16(const uint16_t* k, const uint16_t* beta, uint16_t* tws, int B, int H, int64_t L,
                                int DK, int C, int rule, const int32_t* cu, int N, hipStream_t s,
                                int32_t* order = nullptr);
+// The per-chunk backward kernel in two-workgroup form (bwd_chunk_tr.h): states
+// and dstates transposed ([B*H*NC][DV][DK]); d_k 64 or 128, chunk 64, d_v a
+// multiple of 32.  Arguments as the chunk kernels of bwd.hip.
+bool bwd_chunk_tr_bf16_supported(int DK, int DV, int C);
+hipError_t launch_bwd_chunk_tr_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* beta,
+                                    const uint16_t* dout, const uint16_t* tws, const float* xws, const float* aws,
+                                    const uint16_t* pws, const uint16_t* statesT, const uint16_t* dstatesT,
+                                    uint16_t* dq, uint16_t* dk, uint16_t* dv, uint16_t* dbeta, int B, int H, int64_t L,
+                                    int DK, int DV, int C, int rule, hipStream_t s);
 // Its backward instance over a dense batch: T, X (fp32), a (fp32) and P
 // (bf16, packed at the start of pws) of every chunk slot, and with qe the
 // chunk's Q - P T K (bf16 [slots][C][DK]); same shapes.
