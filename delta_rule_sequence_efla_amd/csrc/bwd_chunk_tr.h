@@ -28,6 +28,8 @@
 
 namespace efla {
 
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
 template <int DK, int C>
 struct BwdTrShape {
   static_assert(C == 64 && (DK == 64 || DK == 128), "shapes of the two-workgroup per-chunk kernel");
@@ -49,13 +51,22 @@ struct BwdTrShape {
   static constexpr int UT = DUT + C * BV * 2;   // U
   static constexpr int DDT = UT + C * BV * 2;   // dD
   static constexpr int LOOP_END = DDT + C * BV * 2;
-  // the UT-transform part's arrays
-  static constexpr int QT = TT;                 // Q [C][DK]
-  static constexpr int DPT = QT + C * DK * 2;   // dP [C][C] bf16
-  static constexpr int WF = TT;                 // W = X^T dX (after Q and dP), fp32 [C][CPF]
-  static constexpr int A0 = (DPT + C * C * 2 > WF + C * CPF * 4) ? DPT + C * C * 2 : WF + C * CPF * 4;  // dT, dX, dA
-  static constexpr int XF = A0 + C * CPF * 4;   // X, then dG + dG^T (bf16 [C][C])
-  static constexpr int RED = XF + C * CPF * 4;  // partial sums, one per thread
+  // the UT-transform part's arrays, in three regions after K:
+  //   R1: Q [C][DK] and dP [C][C] (bf16), then dX (bf16 high and low parts),
+  //       then dA (fp32 [C][CPF]), then dK staged for the stores ([C][DK + 8])
+  //   A0: dT (fp32 [C][CPF]), then W (bf16 high and low parts), then dQ staged
+  //   XF: X (bf16 high and low parts), then dG + dG^T (bf16)
+  static constexpr int CPG = DK + 8;            // pitch of the staged dQ, dK rows
+  static constexpr int QT = TT;
+  static constexpr int DPT = QT + C * DK * 2;
+  static constexpr int DXH = TT, DXL = DXH + C * C * 2, DAF = TT, DKS = TT;
+  static constexpr int R1_BYTES = cmax(cmax(C * DK * 2 + C * C * 2, C * CPF * 4), cmax(4 * C * C, C * CPG * 2));
+  static constexpr int A0 = TT + R1_BYTES;
+  static constexpr int WH = A0, WL = A0 + C * C * 2, DQS = A0;
+  static constexpr int A0_BYTES = cmax(C * CPF * 4, C * CPG * 2);
+  static constexpr int XF = A0 + A0_BYTES;
+  static constexpr int XH = XF, XL = XF + C * C * 2, EB = XF;
+  static constexpr int RED = XF + 4 * C * C;    // partial sums, one per thread
   static constexpr int TAIL_END = RED + NTH * 4;
   static constexpr int BYTES = LOOP_END > TAIL_END ? LOOP_END : TAIL_END;
 };
@@ -95,10 +106,6 @@ __global__ __launch_bounds__((BwdTrShape<DK, C>::NTH)) __attribute__((amdgpu_wav
   const int tid = threadIdx.x, lane0 = tid & 63, w = wave_id(), li0 = lane0 & 15, g0 = lane0 >> 4;
   const int64_t qk_stride = int64_t(H) * DK, v_stride = int64_t(H) * DV;
   auto ld16 = [](const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); };
-  // keeps the scheduler from hoisting the next tile's fragment reads over this
-  // one's products (which would need more than the 128 VGPRs two workgroups
-  // per compute unit allow)
-  auto fence_sched = []() { __builtin_amdgcn_sched_barrier(0); };
   auto st16 = [](uint16_t* p, const u32x4& x) { *reinterpret_cast<u32x4*>(p) = x; };
   constexpr u32x4 Z{0u, 0u, 0u, 0u};
 
@@ -235,7 +242,7 @@ __global__ __launch_bounds__((BwdTrShape<DK, C>::NTH)) __attribute__((amdgpu_wav
       mma(dQa[i], sw_frag<BV>(dOt, 16 * rt + li, 0, g), bS);
       mma(dKa[i], sw_frag<BV>(Ut, 16 * rt + li, 0, g), wide_frag_tr<DK>(dSt, dt, 0, lane));
       mma(dKa[i], sw_frag<BV>(dDt, 16 * rt + li, 0, g), bS);
-      fence_sched();
+
     }
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
@@ -259,12 +266,30 @@ __global__ __launch_bounds__((BwdTrShape<DK, C>::NTH)) __attribute__((amdgpu_wav
   __syncthreads();  // done with the loop's arrays (K stays)
 
   // ---- the UT-transform part -----------------------------------------------
+  // Its C x C x C products W = X^T dX and dA = -W X^T run on bf16 matrix cores
+  // in three passes over a split of each fp32 operand into bf16 high and low
+  // parts (hi hi + hi lo + lo hi: ~16 significant bits, beside the single bf16
+  // rounding of the other operands), with every fragment one LDS read.
   const int li = li0, g = g0, lane = lane0;
-  uint16_t *Qt = b16(S::QT), *dPt = b16(S::DPT), *Eb = b16(S::XF);
-  float *W = f32p(S::WF), *A0 = f32p(S::A0), *X = f32p(S::XF), *red = f32p(S::RED);
+  uint16_t *Qt = b16(S::QT), *dPt = b16(S::DPT), *dXh = b16(S::DXH), *dXl = b16(S::DXL);
+  uint16_t *Wh = b16(S::WH), *Wl = b16(S::WL), *Xh = b16(S::XH), *Xl = b16(S::XL), *Eb = b16(S::EB);
+  uint16_t *dQs = b16(S::DQS), *dKs = b16(S::DKS);
+  float *A0 = f32p(S::A0), *dAf = f32p(S::DAF), *red = f32p(S::RED);
+  constexpr int CPG = S::CPG;
   constexpr int NPART = NTH / C, RPP = C / NPART;
   const int cr = tid % C, prt = tid / C;
-  // dP (lower, diagonal included) as bf16, dT (lower) fp32; Q and X
+  auto split = [](float x, uint16_t& hi, uint16_t& lo) {
+    hi = from_f32<uint16_t>(x);
+    lo = from_f32<uint16_t>(x - to_f32(hi));
+  };
+  // three-pass product acc += A B over one 32-deep slice
+  auto mma3 = [](f32x4& acc, const Frag<uint16_t>& ah, const Frag<uint16_t>& al, const Frag<uint16_t>& bh,
+                 const Frag<uint16_t>& bl) {
+    mma(acc, ah, bh);
+    mma(acc, ah, bl);
+    mma(acc, al, bh);
+  };
+  // dP (lower, diagonal included) as bf16, dT (lower) fp32; Q; X as high and low parts
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     const int t = w + NWV * i, rt = t / NRT, jt = t % NRT;
@@ -283,7 +308,16 @@ __global__ __launch_bounds__((BwdTrShape<DK, C>::NTH)) __attribute__((amdgpu_wav
 #pragma unroll
   for (int i = 0; i < UX / NTH; ++i) {
     const int u = tid + NTH * i, r = u / (C / 4), ch = u % (C / 4);
-    *reinterpret_cast<u32x4*>(X + r * CPF + 4 * ch) = rx[i];
+    union {
+      u32x4 u;
+      float f[4];
+    } x;
+    x.u = rx[i];
+    uint16_t hi[4], lo[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) split(x.f[e], hi[e], lo[e]);
+    *reinterpret_cast<uint2*>(Xh + swz_off<C>(r, 4 * ch)) = *reinterpret_cast<const uint2*>(hi);
+    *reinterpret_cast<uint2*>(Xl + swz_off<C>(r, 4 * ch)) = *reinterpret_cast<const uint2*>(lo);
   }
   __syncthreads();
   // dQ += dP K;  dK += dP^T Q;  da_j = sum_i dT_ij X_ij (partial sums)
@@ -297,41 +331,62 @@ __global__ __launch_bounds__((BwdTrShape<DK, C>::NTH)) __attribute__((amdgpu_wav
       if (32 * ku + 31 >= 16 * rt)
         mma(dKa[i], sw_frag_tr<C>(dPt, 16 * rt, ku, lane), wide_frag_tr<DK>(Qt, dt, ku, lane));
     }
-    fence_sched();
   }
   {
     float s = 0.0f;
 #pragma unroll
-    for (int r = prt * RPP; r < (prt + 1) * RPP; ++r) s = fmaf(A0[r * CPF + cr], X[r * CPF + cr], s);
+    for (int r = prt * RPP; r < (prt + 1) * RPP; ++r)
+      s = fmaf(A0[r * CPF + cr], to_f32(Xh[swz_off<C>(r, cr)]) + to_f32(Xl[swz_off<C>(r, cr)]), s);
     red[prt * C + cr] = s;
   }
   __syncthreads();
+  // dX = dT diag(a), as high and low parts (over Q)
   if (tid < C) {
     float s = 0.0f;
 #pragma unroll
     for (int p = 0; p < NPART; ++p) s += red[p * C + tid];
     das[tid] = s;
   }
-  for (int i = tid; i < C * C; i += NTH) A0[(i / C) * CPF + i % C] *= as[i % C];  // dX = dT diag(a)
+  for (int i = tid; i < C * C; i += NTH) {
+    const int r = i / C, c = i % C;
+    uint16_t hi, lo;
+    split(A0[r * CPF + c] * as[c], hi, lo);
+    dXh[swz_off<C>(r, c)] = hi;
+    dXl[swz_off<C>(r, c)] = lo;
+  }
   __syncthreads();
-  // W = X^T dX (into the space of Q and dP)
+  // W = X^T dX, as high and low parts (over dT)
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     const int t = w + NWV * i, rt = t / NRT, jt = t % NRT;
     f32x4 acc = zero4();
-    tile_mma16<true, false>(acc, X, CPF, A0, CPF, 16 * rt, 16 * jt, C, li, g);
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) W[(16 * rt + 4 * g + qq) * CPF + 16 * jt + li] = acc[qq];
+    for (int ku = 0; ku < NKU_C; ++ku)
+      if (32 * ku + 31 >= 16 * rt && 32 * ku + 31 >= 16 * jt)  // X and dT are lower triangular
+        mma3(acc, sw_frag_tr<C>(Xh, 16 * rt, ku, lane), sw_frag_tr<C>(Xl, 16 * rt, ku, lane),
+             sw_frag_tr<C>(dXh, 16 * jt, ku, lane), sw_frag_tr<C>(dXl, 16 * jt, ku, lane));
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int r = 16 * rt + 4 * g + qq, c = 16 * jt + li;
+      uint16_t hi, lo;
+      split(acc[qq], hi, lo);
+      Wh[swz_off<C>(r, c)] = hi;
+      Wl[swz_off<C>(r, c)] = lo;
+    }
   }
   __syncthreads();
-  // dA = -W X^T (strictly lower) over dX;  G = K K^T on the lower tiles: lambda
-  // (its diagonal) and the row sums of dA G, tile column by tile column
+  // dA = -W X^T (strictly lower, fp32, over dX);  G = K K^T on the lower tiles:
+  // lambda (its diagonal) and the row sums of dA G, tile column by tile column
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     const int t = w + NWV * i, rt = t / NRT, jt = t % NRT;
     f32x4 acc = zero4(), gg = zero4();
-    tile_mma16<false, true>(acc, W, CPF, X, CPF, 16 * rt, 16 * jt, C, li, g);
     if (jt <= rt) {
+#pragma unroll
+      for (int ku = 0; ku < NKU_C; ++ku)
+        if (32 * ku <= 16 * jt + 15)  // X^T's rows of this tile are zero past column 16 jt + 15
+          mma3(acc, sw_frag<C>(Wh, 16 * rt + li, ku, g), sw_frag<C>(Wl, 16 * rt + li, ku, g),
+               sw_frag<C>(Xh, 16 * jt + li, ku, g), sw_frag<C>(Xl, 16 * jt + li, ku, g));
 #pragma unroll
       for (int ku = 0; ku < NKU_D; ++ku)
         mma(gg, wide_frag<DK>(Kt, 16 * rt + li, ku, g), wide_frag<DK>(Kt, 16 * jt + li, ku, g));
@@ -340,7 +395,7 @@ __global__ __launch_bounds__((BwdTrShape<DK, C>::NTH)) __attribute__((amdgpu_wav
     for (int qq = 0; qq < 4; ++qq) {
       const int r = 16 * rt + 4 * g + qq, c = 16 * jt + li;
       const float da = c < r ? -acc[qq] : 0.0f;
-      A0[r * CPF + c] = da;
+      dAf[r * CPF + c] = da;
       if (c == r) lam[r] = gg[qq];
       float s = da * gg[qq];
 #pragma unroll
@@ -358,7 +413,7 @@ __global__ __launch_bounds__((BwdTrShape<DK, C>::NTH)) __attribute__((amdgpu_wav
   }
   for (int i = tid; i < C * C; i += NTH) {
     const int r = i / C, c = i % C;
-    Eb[swz_off<C>(r, c)] = from_f32<uint16_t>(as[r] * A0[r * CPF + c] + as[c] * A0[c * CPF + r]);
+    Eb[swz_off<C>(r, c)] = from_f32<uint16_t>(as[r] * dAf[r * CPF + c] + as[c] * dAf[c * CPF + r]);
   }
   __syncthreads();
   // dbeta, dlambda
@@ -374,24 +429,34 @@ __global__ __launch_bounds__((BwdTrShape<DK, C>::NTH)) __attribute__((amdgpu_wav
     dls[tid] = dl;
   }
   __syncthreads();
-  // dK += (dG + dG^T) K + 2 diag(dlambda) K;  dq, dk (physical key columns)
-  const int64_t qk_row = row0 * DK;
+  // dK += (dG + dG^T) K + 2 diag(dlambda) K;  dQ and dK staged as bf16 rows
+  // (physical key columns) over W and dA
 #pragma unroll
   for (int i = 0; i < NQ; ++i) {
     const int t = w + NWV * i, rt = t / NDT, dt = t % NDT;
 #pragma unroll
     for (int ku = 0; ku < NKU_C; ++ku)
       mma(dKa[i], sw_frag<C>(Eb, 16 * rt + li, ku, g), wide_frag_tr<DK>(Kt, dt, ku, lane));
-    fence_sched();
     const int cp = key_phys(16 * dt + li);
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       const int r = 16 * rt + 4 * g + qq;
-      if (r < valid) {
-        const float kv = to_f32(Kt[swzw_off<DK>(r, cp)]);
-        __builtin_nontemporal_store(from_f32<uint16_t>(dQa[i][qq]), dq + qk_row + r * qk_stride + cp);
-        __builtin_nontemporal_store(from_f32<uint16_t>(dKa[i][qq] + 2.0f * dls[r] * kv), dk + qk_row + r * qk_stride + cp);
-      }
+      const float kv = to_f32(Kt[swzw_off<DK>(r, cp)]);
+      dQs[r * CPG + cp] = from_f32<uint16_t>(dQa[i][qq]);
+      dKs[r * CPG + cp] = from_f32<uint16_t>(dKa[i][qq] + 2.0f * dls[r] * kv);
+    }
+  }
+  __syncthreads();
+  // dq, dk: 16-byte row pieces
+  const int64_t qk_row = row0 * DK;
+#pragma unroll
+  for (int i = 0; i < UK / NTH; ++i) {
+    const int u = tid + NTH * i, r = u / (DK / 8), ch = u % (DK / 8);
+    if (r < valid) {
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(dQs + r * CPG + 8 * ch),
+                                  reinterpret_cast<u32x4*>(dq + qk_row + r * qk_stride + 8 * ch));
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(dKs + r * CPG + 8 * ch),
+                                  reinterpret_cast<u32x4*>(dk + qk_row + r * qk_stride + 8 * ch));
     }
   }
 }
