@@ -67,6 +67,8 @@ struct BwdTrShape {
   static constexpr int XF = A0 + A0_BYTES;
   static constexpr int XH = XF, XL = XF + C * C * 2, EB = XF;
   static constexpr int RED = XF + 4 * C * C;    // partial sums, one per thread
+  using TS = DmaTile<BV, DK, NWV, true>;  // a value block's S^T or dS'^T rows (16-byte-fragment swizzle)
+  using TV = DmaTile<C, BV, NWV>;         // its V or dO rows
   static constexpr int TAIL_END = RED + NTH * 4;
   static constexpr int BYTES = LOOP_END > TAIL_END ? LOOP_END : TAIL_END;
 };
@@ -135,34 +137,38 @@ __global__ __launch_bounds__((BwdTrShape<DK, C>::NTH)) __attribute__((amdgpu_wav
   }
   if (tid < C) as[tid] = aws[slot * C + tid];
 
-  // ---- one value block's S^T, dS'^T, V and dO, one unit of each per thread --
-  constexpr int US = BV * DK / 8, UV = C * BV / 8;
-  static_assert(US <= NTH && 2 * UV == NTH, "one unit of each operand per thread");
-  u32x4 rs, rds, rvo;
-  // wave-uniform bases and 32-bit lane offsets, so the loads take a scalar base
-  auto load_block = [&](int v0, int tid) {
-    rs = rds = Z;
-    const uint16_t* sb = states + (slot * DV + v0) * DK;
-    const uint16_t* db = dstates + (slot * DV + v0) * DK;
-    if (tid < US) {
-      const uint32_t o = uint32_t((tid / (DK / 8)) * DK + 8 * (tid % (DK / 8)));
-      rs = ld16(sb + o);
-      rds = ld16(db + o);
+  // ---- one value block's S^T, dS'^T, V and dO: direct global -> LDS
+  // transfers spread over the wavefronts, so nothing is held in registers
+  // across a block (register staging cost ~16 VGPRs over the 128 two
+  // workgroups per compute unit allow).  Rows of V and dO past the end of the
+  // sequence are cleared after the transfers (they re-read row 0).
+  typename S::TS dma_s;
+  typename S::TV dma_v;
+  dma_s.init(DK, lane0, w);
+  dma_v.init(v_stride, lane0, w);
+  auto dma_block = [&](int v0) {
+    const auto* sb = static_cast<const uint16_t*>(uniform_ptr(states + (slot * DV + v0) * DK));
+    const auto* db = static_cast<const uint16_t*>(uniform_ptr(dstates + (slot * DV + v0) * DK));
+    const auto* vb = static_cast<const uint16_t*>(uniform_ptr(v + row0 * DV + v0));
+    const auto* ob = static_cast<const uint16_t*>(uniform_ptr(dout + row0 * DV + v0));
+#pragma unroll
+    for (int i = 0; i < S::TS::PER_WAVE; ++i) {
+      dma_s.template issue<false>(i, lds_addr_of(St), sb, BV);
+      dma_s.template issue<false>(i, lds_addr_of(dSt), db, BV);
     }
-    const int u = tid % UV, r = u / (BV / 8), ch = u % (BV / 8);
-    const uint16_t* vb = v + row0 * DV + v0;
-    const uint16_t* ob = dout + row0 * DV + v0;
-    const uint32_t o = uint32_t(r * v_stride + 8 * ch);
-    rvo = r < valid ? ld16((tid < UV ? vb : ob) + o) : Z;
-  };
-  auto store_block = [&](int tid) {
-    if (tid < US) {
-      const int r = tid / (DK / 8), ch = tid % (DK / 8);
-      st16(St + swzw_off<DK>(r, 8 * ch), rs);
-      st16(dSt + swzw_off<DK>(r, 8 * ch), rds);
+    if (valid == C) {
+#pragma unroll
+      for (int i = 0; i < S::TV::PER_WAVE; ++i) {
+        dma_v.template issue<false>(i, lds_addr_of(Vt), vb, C);
+        dma_v.template issue<false>(i, lds_addr_of(dOt), ob, C);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < S::TV::PER_WAVE; ++i) {
+        dma_v.template issue<true>(i, lds_addr_of(Vt), vb, valid);
+        dma_v.template issue<true>(i, lds_addr_of(dOt), ob, valid);
+      }
     }
-    const int u = tid % UV, r = u / (BV / 8), ch = u % (BV / 8);
-    st16((tid < UV ? Vt : dOt) + swz_off<BV>(r, 8 * ch), rvo);
   };
   // an accumulator tile (rows 16 rt + 4 g + qq, column 16 c + li) into a [C][BV] tile
   auto put = [&](uint16_t* X, const f32x4& a, int rt, int c, int li, int g) {
@@ -181,17 +187,22 @@ __global__ __launch_bounds__((BwdTrShape<DK, C>::NTH)) __attribute__((amdgpu_wav
   u32x4 rq[UK / NTH], rx[UX / NTH];
   static_assert(UX % NTH == 0, "whole units per thread");
 
-  load_block(0, tid);
+  dma_block(0);
   for (int v0 = 0; v0 < DV; v0 += BV) {
     // the lane indices as values the compiler cannot see to be the same in
     // every block, so that the fragment addresses built from them are formed
     // here rather than held in registers across the loop
     int li = li0, g = g0, lane = lane0, tidv = tid;
     asm volatile("" : "+v"(li), "+v"(g), "+v"(lane), "+v"(tidv));
-    __syncthreads();  // the previous block's arrays are free (and the chunk's K, T, P are in place)
-    store_block(tidv);
-    if (v0 + BV < DV) load_block(v0 + BV, tidv);  // in flight during this block
-    __syncthreads();
+    wait_vmcnt<0>();  // this wavefront's transfers of the block
+    if (valid < C) {
+      __syncthreads();  // every wavefront's transfers landed
+      for (int i = tidv; i < 2 * (C - valid) * (BV / 8); i += NTH) {
+        const int r = valid + (i >> 1) / (BV / 8), ch = (i >> 1) % (BV / 8);
+        st16(((i & 1) ? dOt : Vt) + swz_off<BV>(r, 8 * ch), Z);
+      }
+    }
+    __syncthreads();  // the block's operands in place (and the chunk's K, T, P)
     // D = V - K S and dU = P^T dO + K dS': tile (rt, c) of each, wavefront w = 2 rt + c
     {
       const int rt = w >> 1, c = w & 1;
@@ -251,6 +262,10 @@ __global__ __launch_bounds__((BwdTrShape<DK, C>::NTH)) __attribute__((amdgpu_wav
         mma(dPa[i], sw_frag<BV>(dOt, 16 * rt + li, 0, g), sw_frag<BV>(Ut, 16 * jt + li, 0, g));
         mma(dTa[i], sw_frag<BV>(dUt, 16 * rt + li, 0, g), sw_frag<BV>(Dt, 16 * jt + li, 0, g));
       }
+    }
+    if (v0 + BV < DV) {
+      __syncthreads();  // every read of this block's operands done
+      dma_block(v0 + BV);
     }
   }
 #pragma unroll
