@@ -69,6 +69,8 @@ struct BwdTrShape {
   static constexpr int RED = XF + 4 * C * C;    // partial sums, one per thread
   using TS = DmaTile<BV, DK, NWV, true>;  // a value block's S^T or dS'^T rows (16-byte-fragment swizzle)
   using TV = DmaTile<C, BV, NWV>;         // its V or dO rows
+  using TK = DmaTile<C, DK, NWV, true>;   // K, Q
+  using TC = DmaTile<C, C, NWV>;          // T, P
   static constexpr int TAIL_END = RED + NTH * 4;
   static constexpr int BYTES = LOOP_END > TAIL_END ? LOOP_END : TAIL_END;
 };
@@ -111,29 +113,29 @@ __global__ __launch_bounds__((BwdTrShape<DK, C>::NTH)) __attribute__((amdgpu_wav
   auto st16 = [](uint16_t* p, const u32x4& x) { *reinterpret_cast<u32x4*>(p) = x; };
   constexpr u32x4 Z{0u, 0u, 0u, 0u};
 
-  // ---- the chunk's K, T, P (16-byte units dealt over the threads) ----------
-  constexpr int UK = C * DK / 8, UC = C * C / 8;  // 16-byte units of a [C][DK] / [C][C] tile
-  static_assert(UK % NTH == 0 && UC == NTH, "whole units per thread");
+  // ---- the chunk's K, T, P: direct global -> LDS transfers, issued with the
+  // first value block's (rows of K past the end of the sequence re-read row 0
+  // and are cleared with the block's)
+  constexpr int UK = C * DK / 8;  // 16-byte units of a [C][DK] tile
+  static_assert(UK % NTH == 0, "whole units per thread");
+  typename S::TK dma_k;
+  typename S::TC dma_c;
+  dma_k.init(qk_stride, lane0, w);
+  dma_c.init(C, lane0, w);
   {
-    u32x4 rk[UK / NTH], rt_, rp;
+    const auto* ks = static_cast<const uint16_t*>(uniform_ptr(k + row0 * DK));
+    const auto* ts = static_cast<const uint16_t*>(uniform_ptr(tws + slot * C * C));
+    const auto* ps = static_cast<const uint16_t*>(uniform_ptr(pws + slot * C * C));
 #pragma unroll
-    for (int i = 0; i < UK / NTH; ++i) {
-      const int u = tid + NTH * i, r = u / (DK / 8), ch = u % (DK / 8);
-      rk[i] = r < valid ? ld16(k + (row0 + int64_t(r) * H) * DK + 8 * ch) : Z;
-    }
-    {
-      const int r = tid / (C / 8), ch = tid % (C / 8);
-      rt_ = ld16(tws + slot * C * C + r * C + 8 * ch);
-      rp = ld16(pws + slot * C * C + r * C + 8 * ch);
+    for (int i = 0; i < S::TK::PER_WAVE; ++i) {
+      if (valid == C) dma_k.template issue<false>(i, lds_addr_of(Kt), ks, C);
+      else dma_k.template issue<true>(i, lds_addr_of(Kt), ks, valid);
     }
 #pragma unroll
-    for (int i = 0; i < UK / NTH; ++i) {
-      const int u = tid + NTH * i, r = u / (DK / 8), ch = u % (DK / 8);
-      st16(Kt + swzw_off<DK>(r, 8 * ch), rk[i]);
+    for (int i = 0; i < S::TC::PER_WAVE; ++i) {
+      dma_c.template issue<false>(i, lds_addr_of(Tt), ts, C);
+      dma_c.template issue<false>(i, lds_addr_of(Pt), ps, C);
     }
-    const int r = tid / (C / 8), ch = tid % (C / 8);
-    st16(Tt + swz_off<C>(r, 8 * ch), rt_);
-    st16(Pt + swz_off<C>(r, 8 * ch), rp);
   }
   if (tid < C) as[tid] = aws[slot * C + tid];
 
@@ -182,9 +184,9 @@ __global__ __launch_bounds__((BwdTrShape<DK, C>::NTH)) __attribute__((amdgpu_wav
 #pragma unroll
   for (int i = 0; i < NP; ++i) dPa[i] = dTa[i] = zero4();
 
-  // the tail's Q and X
+  // the tail's X
   constexpr int UX = C * C / 4;  // 16-byte units of fp32 X
-  u32x4 rq[UK / NTH], rx[UX / NTH];
+  u32x4 rx[UX / NTH];
   static_assert(UX % NTH == 0, "whole units per thread");
 
   dma_block(0);
@@ -201,6 +203,9 @@ __global__ __launch_bounds__((BwdTrShape<DK, C>::NTH)) __attribute__((amdgpu_wav
         const int r = valid + (i >> 1) / (BV / 8), ch = (i >> 1) % (BV / 8);
         st16(((i & 1) ? dOt : Vt) + swz_off<BV>(r, 8 * ch), Z);
       }
+      if (v0 == 0)
+        for (int i = tidv; i < (C - valid) * (DK / 8); i += NTH)
+          st16(Kt + swzw_off<DK>(valid + i / (DK / 8), 8 * (i % (DK / 8))), Z);
     }
     __syncthreads();  // the block's operands in place (and the chunk's K, T, P)
     // D = V - K S and dU = P^T dO + K dS': tile (rt, c) of each, wavefront w = 2 rt + c
@@ -244,6 +249,14 @@ __global__ __launch_bounds__((BwdTrShape<DK, C>::NTH)) __attribute__((amdgpu_wav
       put(dDt, dd, rt, c, li, g);  // as -dD
     }
     __syncthreads();
+    if (v0 + BV >= DV) {  // the tail's Q, during the last block (over T and P, done with)
+      const auto* qs = static_cast<const uint16_t*>(uniform_ptr(q + row0 * DK));
+#pragma unroll
+      for (int i = 0; i < S::TK::PER_WAVE; ++i) {
+        if (valid == C) dma_k.template issue<false>(i, lds_addr_of(b16(S::QT)), qs, C);
+        else dma_k.template issue<true>(i, lds_addr_of(b16(S::QT)), qs, valid);
+      }
+    }
     // dQ += dO S^T;  dK += U dS'^T - dD S^T  (tiles (rt, dt), logical key columns);
     // dP += dO U^T;  dT += dU D^T  (lower tiles)
 #pragma unroll
@@ -269,16 +282,12 @@ __global__ __launch_bounds__((BwdTrShape<DK, C>::NTH)) __attribute__((amdgpu_wav
     }
   }
 #pragma unroll
-  for (int i = 0; i < UK / NTH; ++i) {
-    const int u = tid + NTH * i, r = u / (DK / 8), ch = u % (DK / 8);
-    rq[i] = r < valid ? ld16(q + (row0 + int64_t(r) * H) * DK + 8 * ch) : Z;
-  }
-#pragma unroll
   for (int i = 0; i < UX / NTH; ++i) {
     const int u = tid + NTH * i, r = u / (C / 4), ch = u % (C / 4);
     rx[i] = *reinterpret_cast<const u32x4*>(xws + slot * C * C + r * C + 4 * ch);
   }
-  __syncthreads();  // done with the loop's arrays (K stays)
+  wait_vmcnt<0>();   // Q's transfers and X
+  __syncthreads();  // done with the loop's arrays (K stays); Q in place
 
   // ---- the UT-transform part -----------------------------------------------
   // Its C x C x C products W = X^T dX and dA = -W X^T run on bf16 matrix cores
@@ -315,11 +324,8 @@ __global__ __launch_bounds__((BwdTrShape<DK, C>::NTH)) __attribute__((amdgpu_wav
       A0[r * CPF + c] = c <= r ? dTa[i][qq] : 0.0f;
     }
   }
-#pragma unroll
-  for (int i = 0; i < UK / NTH; ++i) {
-    const int u = tid + NTH * i, r = u / (DK / 8), ch = u % (DK / 8);
-    st16(Qt + swzw_off<DK>(r, 8 * ch), rq[i]);
-  }
+  for (int i = tid; i < (C - valid) * (DK / 8); i += NTH)  // Q's rows past the end re-read row 0
+    st16(Qt + swzw_off<DK>(valid + i / (DK / 8), 8 * (i % (DK / 8))), Z);
 #pragma unroll
   for (int i = 0; i < UX / NTH; ++i) {
     const int u = tid + NTH * i, r = u / (C / 4), ch = u % (C / 4);
@@ -413,8 +419,11 @@ __global__ __launch_bounds__((BwdTrShape<DK, C>::NTH)) __attribute__((amdgpu_wav
       dAf[r * CPF + c] = da;
       if (c == r) lam[r] = gg[qq];
       float s = da * gg[qq];
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);  // over the 16 columns of the tile
+      // over the 16 columns of the tile: rotations within each 16-lane row
+      s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0x121, 0xF, 0xF, false));
+      s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0x122, 0xF, 0xF, false));
+      s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0x124, 0xF, 0xF, false));
+      s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0x128, 0xF, 0xF, false));
       if (li == 0) red[jt * C + r] = s;
     }
   }
