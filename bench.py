@@ -433,9 +433,17 @@ def main():
         # ---- training step: forward + backward, exact and Euler ---------------
         train, nb = training_leg(torch, efla, w, inp, o, s_final, ws, dev, K, args)
         line["training"] = train
-        line["euler"] = {"rule": "euler (alpha = beta)", "fwd_us": train["euler"]["fwd_us"],
-                         "exact_fwd_us": train["exact"]["fwd_us"],
-                         "exact_over_euler_time": round(train["exact"]["fwd_us"] / train["euler"]["fwd_us"], 4)}
+        # the forward under each rule, flushed steps alternating between the rules
+        fx = efla.prepare_chunk_fwd(q, k, v, beta, s0, o, s_final, ws, chunk=w.chunk, rule="exact")
+        fe = efla.prepare_chunk_fwd(q, k, v, beta, s0, o, s_final, ws, chunk=w.chunk, rule="euler")
+        xs, es = [], []
+        for _ in range(max(1, K // 10)):
+            xs += flushed_steps(torch, (fx,), 10, fl.clean)[0]
+            es += flushed_steps(torch, (fe,), 10, fl.clean)[0]
+        xm, em = pct(xs, 50) * 1e3, pct(es, 50) * 1e3
+        line["euler"] = {"rule": "euler (alpha = beta)", "flushed_fwd_us": round(em, 2),
+                         "exact_flushed_fwd_us": round(xm, 2), "exact_over_euler_time": round(xm / em, 4),
+                         "samples": len(es)}
         # backward: bytes it must move: q, k, v, beta, d_o read; dq, dk, dv, dbeta written; states
         bus = train["exact"]["bwd_us"]
         bwd_bytes = n_ht * ((2 * w.dk + 2 * w.dv + 1) * esz + (2 * w.dk + w.dv + 1) * esz) + 3 * state_bytes
