@@ -148,29 +148,26 @@ __global__ __launch_bounds__((BwdTrShape<DK, C>::NTH)) __attribute__((amdgpu_wav
   typename S::TV dma_v;
   dma_s.init(DK, lane0, w);
   dma_v.init(v_stride, lane0, w);
-  auto dma_block = [&](int v0) {
+  // one [C][BV] tile (V or dO) of the block at v0
+  auto dma_rows = [&](uint16_t* dst, const uint16_t* src, int v0) {
+    const auto* sp_ = static_cast<const uint16_t*>(uniform_ptr(src + row0 * DV + v0));
+#pragma unroll
+    for (int i = 0; i < S::TV::PER_WAVE; ++i) {
+      if (valid == C) dma_v.template issue<false>(i, lds_addr_of(dst), sp_, C);
+      else dma_v.template issue<true>(i, lds_addr_of(dst), sp_, valid);
+    }
+  };
+  // the block's S^T, dS'^T and dO (with V: the first block)
+  auto dma_block = [&](int v0, bool with_v) {
     const auto* sb = static_cast<const uint16_t*>(uniform_ptr(states + (slot * DV + v0) * DK));
     const auto* db = static_cast<const uint16_t*>(uniform_ptr(dstates + (slot * DV + v0) * DK));
-    const auto* vb = static_cast<const uint16_t*>(uniform_ptr(v + row0 * DV + v0));
-    const auto* ob = static_cast<const uint16_t*>(uniform_ptr(dout + row0 * DV + v0));
 #pragma unroll
     for (int i = 0; i < S::TS::PER_WAVE; ++i) {
       dma_s.template issue<false>(i, lds_addr_of(St), sb, BV);
       dma_s.template issue<false>(i, lds_addr_of(dSt), db, BV);
     }
-    if (valid == C) {
-#pragma unroll
-      for (int i = 0; i < S::TV::PER_WAVE; ++i) {
-        dma_v.template issue<false>(i, lds_addr_of(Vt), vb, C);
-        dma_v.template issue<false>(i, lds_addr_of(dOt), ob, C);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < S::TV::PER_WAVE; ++i) {
-        dma_v.template issue<true>(i, lds_addr_of(Vt), vb, valid);
-        dma_v.template issue<true>(i, lds_addr_of(dOt), ob, valid);
-      }
-    }
+    dma_rows(dOt, dout, v0);
+    if (with_v) dma_rows(Vt, v, v0);
   };
   // an accumulator tile (rows 16 rt + 4 g + qq, column 16 c + li) into a [C][BV] tile
   auto put = [&](uint16_t* X, const f32x4& a, int rt, int c, int li, int g) {
@@ -189,7 +186,7 @@ __global__ __launch_bounds__((BwdTrShape<DK, C>::NTH)) __attribute__((amdgpu_wav
   u32x4 rx[UX / NTH];
   static_assert(UX % NTH == 0, "whole units per thread");
 
-  dma_block(0);
+  dma_block(0, true);
   for (int v0 = 0; v0 < DV; v0 += BV) {
     // the lane indices as values the compiler cannot see to be the same in
     // every block, so that the fragment addresses built from them are formed
@@ -228,6 +225,7 @@ __global__ __launch_bounds__((BwdTrShape<DK, C>::NTH)) __attribute__((amdgpu_wav
       put(dUt, du, rt, c, li, g);
     }
     __syncthreads();
+    if (v0 + BV < DV) dma_rows(Vt, v, v0 + BV);  // V is read only in the phase above
     // U = T D and dD = T^T dU (= dV)
     {
       const int rt = w >> 1, c = w & 1;
@@ -278,7 +276,7 @@ __global__ __launch_bounds__((BwdTrShape<DK, C>::NTH)) __attribute__((amdgpu_wav
     }
     if (v0 + BV < DV) {
       __syncthreads();  // every read of this block's operands done
-      dma_block(v0 + BV);
+      dma_block(v0 + BV, false);
     }
   }
 #pragma unroll
@@ -428,29 +426,25 @@ __global__ __launch_bounds__((BwdTrShape<DK, C>::NTH)) __attribute__((amdgpu_wav
     }
   }
   __syncthreads();
-  // da_i += sum_{j<i} dA_ij G_ij;  dG + dG^T with dG = diag(a) dA, as bf16 (over X)
+  // da_i += sum_{j<i} dA_ij G_ij, then dbeta and dlambda;  dG + dG^T with
+  // dG = diag(a) dA, as bf16 (over X)
   if (tid < C) {
-    float s = 0.0f;
+    float s = das[tid];
 #pragma unroll
     for (int jt = 0; jt < NRT; ++jt) s += red[jt * C + tid];
-    das[tid] += s;
-  }
-  for (int i = tid; i < C * C; i += NTH) {
-    const int r = i / C, c = i % C;
-    Eb[swz_off<C>(r, c)] = from_f32<uint16_t>(as[r] * dAf[r * CPF + c] + as[c] * dAf[c * CPF + r]);
-  }
-  __syncthreads();
-  // dbeta, dlambda
-  if (tid < C) {
     float dl = 0.0f;
     if (tid < valid) {
       const float bt = to_f32(beta[row0 + int64_t(tid) * H]);
       float da_db, da_dl;
       efla_alpha_grad(bt, lam[tid], rule, da_db, da_dl);
-      dl = das[tid] * da_dl;
-      dbeta[row0 + int64_t(tid) * H] = from_f32<uint16_t>(das[tid] * da_db);
+      dl = s * da_dl;
+      dbeta[row0 + int64_t(tid) * H] = from_f32<uint16_t>(s * da_db);
     }
     dls[tid] = dl;
+  }
+  for (int i = tid; i < C * C; i += NTH) {
+    const int r = i / C, c = i % C;
+    Eb[swz_off<C>(r, c)] = from_f32<uint16_t>(as[r] * dAf[r * CPF + c] + as[c] * dAf[c * CPF + r]);
   }
   __syncthreads();
   // dK += (dG + dG^T) K + 2 diag(dlambda) K;  dQ and dK staged as bf16 rows
