@@ -26,7 +26,9 @@ Besides the contract fields the JSON line carries:
   shapes        the flushed step on the other model-shaped workloads
   decode        efla_step at [256, 16, 128, 128] (fp32 state), flushed per step
   training      forward + backward per step under the exact rule and under
-                the Euler (delta-rule) rule, the pages' throughput comparison
+                the Euler (delta-rule) rule, the pages' throughput comparison;
+                also the training pair (forward storing the chunk states, the
+                backward reading them)
   euler         the forward alone under the Euler rule
   varlen        efla_chunk_fwd_varlen on the same heads packed as 16 sequences
   backward      efla_chunk_bwd on the benchmark workload
@@ -247,10 +249,25 @@ def training_leg(torch, efla, w, inp, o, s_final, ws, dev, K, args, rules=("exac
         tus = warm_us(torch, (fwd, bwd), KB)
         train[rule] = {"fwd_us": round(fus, 2), "bwd_us": round(bus, 2), "fwd_bwd_us": round(tus, 2),
                        "fwd_bwd_tokens_per_s": round(tokens / (tus / 1e6), 1)}
+        # the training pair: the forward stores the chunk start states, the
+        # backward reads them (its state pass skipped)
+        tf, tb = efla.prepare_chunk_train(q, k, v, beta, d_o, s0, o, s_final, dsf, gq, gk, gv, gb, gs0, wsb,
+                                          chunk=w.chunk, rule=rule)
+        tf()
+        tb()
+        pfus = warm_us(torch, (tf,), K)
+        pbus = warm_us(torch, (tb,), KB)
+        ptus = warm_us(torch, (tf, tb), KB)
+        train[rule]["pair"] = {"fwd_us": round(pfus, 2), "bwd_us": round(pbus, 2), "fwd_bwd_us": round(ptus, 2),
+                               "fwd_bwd_tokens_per_s": round(tokens / (ptus / 1e6), 1),
+                               "states_stored": efla.efla_chunk_train_saves_states(w.dk, w.dv, w.chunk, q.dtype)}
     if "exact" in train and "euler" in train:
         train["exact_over_euler_time"] = round(train["exact"]["fwd_bwd_us"] / train["euler"]["fwd_bwd_us"], 4)
-    train["note"] = ("back-to-back steps; the pages report EFLA training throughput matching DeltaNet's "
-                     "(Experimental Results), with no hardware or numbers given")
+        train["pair_exact_over_euler_time"] = round(train["exact"]["pair"]["fwd_bwd_us"] /
+                                                    train["euler"]["pair"]["fwd_bwd_us"], 4)
+    train["note"] = ("back-to-back steps; efla_chunk_fwd + efla_chunk_bwd, and under 'pair' "
+                     "efla_chunk_fwd_train + efla_chunk_bwd_train; the pages report EFLA training throughput "
+                     "matching DeltaNet's (Experimental Results), with no hardware or numbers given")
     return train, nb
 
 
@@ -450,7 +467,7 @@ def main():
         line["backward"] = {"us": bus, "tokens_per_s": round(tokens / (bus / 1e6), 1),
                             "algorithmic_bytes": bwd_bytes,
                             "hbm_frac": round(bwd_bytes / (bus / 1e6) / 1e9 / HBM_PEAK_GBS, 4),
-                            "workspace_bytes": nb}
+                            "workspace_bytes": nb, "train_pair_bwd_us": train["exact"]["pair"]["bwd_us"]}
 
         # ---- packed variable-length batch -----------------------------------
         wv = W.get("varlen_1p3b")

@@ -404,10 +404,11 @@ size_t efla_chunk_bwd_workspace_size(int B, int H, int64_t L, int d_k, int d_v, 
   return efla::bwd_layout(B, H, L, d_k, d_v, chunk, elem_bytes(dtype)).total;
 }
 
-efla_status efla_chunk_bwd(const void* q, const void* k, const void* v, const void* beta, const float* s0,
-                           const void* d_o, const float* ds_final, void* dq, void* dk, void* dv, void* dbeta,
-                           float* ds0, int B, int H, int64_t L, int d_k, int d_v, int chunk, efla_dtype dtype,
-                           efla_rule rule, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+efla_status chunk_bwd(const void* q, const void* k, const void* v, const void* beta, const float* s0,
+                      const void* d_o, const float* ds_final, void* dq, void* dk, void* dv, void* dbeta, float* ds0,
+                      int B, int H, int64_t L, int d_k, int d_v, int chunk, efla_dtype dtype, efla_rule rule,
+                      void* workspace, size_t workspace_bytes, void* stream, bool saved) {
   if (!valid_rule(rule)) return EFLA_ERR_INVALID_ARG;
   const efla_status st = check_chunk_shape(B, H, L, d_k, d_v, chunk, dtype);
   if (st != EFLA_OK) return st;
@@ -428,13 +429,67 @@ efla_status efla_chunk_bwd(const void* q, const void* k, const void* v, const vo
     return from_hip(efla::launch_chunk_bwd<U>(
         static_cast<const U*>(q), static_cast<const U*>(k), static_cast<const U*>(v), static_cast<const U*>(beta),
         s0, static_cast<const U*>(d_o), ds_final, static_cast<U*>(dq), static_cast<U*>(dk), static_cast<U*>(dv),
-        static_cast<U*>(dbeta), ds0, B, H, L, d_k, d_v, chunk, int(rule), workspace, s));
+        static_cast<U*>(dbeta), ds0, B, H, L, d_k, d_v, chunk, int(rule), workspace, s, saved));
   }
   return from_hip(efla::launch_chunk_bwd<float>(
       static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
       static_cast<const float*>(beta), s0, static_cast<const float*>(d_o), ds_final, static_cast<float*>(dq),
       static_cast<float*>(dk), static_cast<float*>(dv), static_cast<float*>(dbeta), ds0, B, H, L, d_k, d_v, chunk,
       int(rule), workspace, s));
+}
+}  // namespace
+
+efla_status efla_chunk_bwd(const void* q, const void* k, const void* v, const void* beta, const float* s0,
+                           const void* d_o, const float* ds_final, void* dq, void* dk, void* dv, void* dbeta,
+                           float* ds0, int B, int H, int64_t L, int d_k, int d_v, int chunk, efla_dtype dtype,
+                           efla_rule rule, void* workspace, size_t workspace_bytes, void* stream) {
+  return chunk_bwd(q, k, v, beta, s0, d_o, ds_final, dq, dk, dv, dbeta, ds0, B, H, L, d_k, d_v, chunk, dtype, rule,
+                   workspace, workspace_bytes, stream, false);
+}
+
+int efla_chunk_train_saves_states(int d_k, int d_v, int chunk, efla_dtype dtype) {
+  if (dtype != EFLA_BF16 || !valid_dim(d_k) || !valid_dim(d_v) || !valid_chunk(chunk)) return 0;
+  return efla::train_saves_states(d_k, d_v, chunk) ? 1 : 0;
+}
+
+efla_status efla_chunk_fwd_train(const void* q, const void* k, const void* v, const void* beta, const float* s0,
+                                 void* o, float* s_final, int B, int H, int64_t L, int d_k, int d_v, int chunk,
+                                 efla_dtype dtype, efla_rule rule, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  if (!valid_rule(rule)) return EFLA_ERR_INVALID_ARG;
+  const efla_status st = check_chunk_shape(B, H, L, d_k, d_v, chunk, dtype);
+  if (st != EFLA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (L > 0) {
+    if (q == nullptr || k == nullptr || v == nullptr || beta == nullptr || o == nullptr)
+      return EFLA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return EFLA_ERR_INVALID_ARG;
+    const size_t need = efla_chunk_bwd_workspace_size(B, H, L, d_k, d_v, chunk, dtype);
+    if (workspace == nullptr || workspace_bytes < need) return EFLA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return EFLA_ERR_INVALID_ARG;
+    // T at the workspace's start, where efla_chunk_fwd keeps it too
+    const efla_status s1 = launch_ut(k, beta, B, H, L, d_k, chunk, dtype, rule, workspace, nullptr, 0, s);
+    if (s1 != EFLA_OK) return s1;
+    if (efla_chunk_train_saves_states(d_k, d_v, chunk, dtype)) {
+      auto* states = reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(workspace) +
+                                                 efla::bwd_layout(B, H, L, d_k, d_v, chunk, 2).s);
+      return from_hip(efla::launch_recurrence_split_bf16(
+          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+          static_cast<const uint16_t*>(workspace), s0, static_cast<uint16_t*>(o), s_final, B, H, L, d_k, d_v, chunk,
+          32, nullptr, 0, nullptr, s, states));
+    }
+  } else if (s_final == nullptr) {
+    return EFLA_OK;
+  }
+  return launch_rec(q, k, v, s0, o, s_final, B, H, L, d_k, d_v, chunk, dtype, workspace, nullptr, 0, s);
+}
+
+efla_status efla_chunk_bwd_train(const void* q, const void* k, const void* v, const void* beta, const float* s0,
+                                 const void* d_o, const float* ds_final, void* dq, void* dk, void* dv, void* dbeta,
+                                 float* ds0, int B, int H, int64_t L, int d_k, int d_v, int chunk, efla_dtype dtype,
+                                 efla_rule rule, void* workspace, size_t workspace_bytes, void* stream) {
+  return chunk_bwd(q, k, v, beta, s0, d_o, ds_final, dq, dk, dv, dbeta, ds0, B, H, L, d_k, d_v, chunk, dtype, rule,
+                   workspace, workspace_bytes, stream, efla_chunk_train_saves_states(d_k, d_v, chunk, dtype) != 0);
 }
 
 namespace {

@@ -80,7 +80,7 @@ hipError_t chunk_states(const T* q, const T* k, const T* v, const T* tws, const 
 template <typename T, int DK, int C>
 hipError_t bwd_launch_impl(const T* q, const T* k, const T* v, const T* beta, const float* s0, const T* dout,
                            const float* dsf, T* dq, T* dk, T* dv, T* dbeta, float* ds0, int B, int H, int64_t L,
-                           int DV, int rule, unsigned char* ws, hipStream_t s) {
+                           int DV, int rule, unsigned char* ws, hipStream_t s, bool saved) {
   const int NC = int((L + C - 1) / C);
   const int BH = B * H;
   const int64_t slots = int64_t(BH) * NC;
@@ -139,9 +139,13 @@ hipError_t bwd_launch_impl(const T* q, const T* k, const T* v, const T* beta, co
       hipLaunchKernelGGL((ut_transform_kernel<T, DK, C, true>), dim3(unsigned(slots)), dim3(kThreads), 0, s, k,
                          beta, tws, H, L, NC, rule, nullptr, 0, q, xws, aws, pws);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    // 2. the state at the start of every chunk (no output)
-    if (hipError_t e = chunk_states<T, DK, C>(q, k, v, tws, s0, sws, B, H, L, DV, s, bf16k, &states_t);
-        e != hipSuccess)
+    // 2. the state at the start of every chunk (no output), unless the forward
+    // pass left them in the workspace, transposed (read only by the bf16
+    // matrix-core kernels)
+    if (saved && bf16k)
+      states_t = true;
+    else if (hipError_t e = chunk_states<T, DK, C>(q, k, v, tws, s0, sws, B, H, L, DV, s, bf16k, &states_t);
+             e != hipSuccess)
       return e;
   }
   // 3. reverse pass over chunks: dS at every chunk end, and dS_0 (bf16 inputs
@@ -207,11 +211,11 @@ hipError_t bwd_launch_impl(const T* q, const T* k, const T* v, const T* beta, co
 template <typename T, int DK>
 hipError_t bwd_dispatch_c(const T* q, const T* k, const T* v, const T* beta, const float* s0, const T* dout,
                           const float* dsf, T* dq, T* dk, T* dv, T* dbeta, float* ds0, int B, int H, int64_t L,
-                          int DV, int C, int rule, unsigned char* ws, hipStream_t s) {
+                          int DV, int C, int rule, unsigned char* ws, hipStream_t s, bool saved) {
   switch (C) {
-    case 16: return bwd_launch_impl<T, DK, 16>(q, k, v, beta, s0, dout, dsf, dq, dk, dv, dbeta, ds0, B, H, L, DV, rule, ws, s);
-    case 32: return bwd_launch_impl<T, DK, 32>(q, k, v, beta, s0, dout, dsf, dq, dk, dv, dbeta, ds0, B, H, L, DV, rule, ws, s);
-    case 64: return bwd_launch_impl<T, DK, 64>(q, k, v, beta, s0, dout, dsf, dq, dk, dv, dbeta, ds0, B, H, L, DV, rule, ws, s);
+    case 16: return bwd_launch_impl<T, DK, 16>(q, k, v, beta, s0, dout, dsf, dq, dk, dv, dbeta, ds0, B, H, L, DV, rule, ws, s, saved);
+    case 32: return bwd_launch_impl<T, DK, 32>(q, k, v, beta, s0, dout, dsf, dq, dk, dv, dbeta, ds0, B, H, L, DV, rule, ws, s, saved);
+    case 64: return bwd_launch_impl<T, DK, 64>(q, k, v, beta, s0, dout, dsf, dq, dk, dv, dbeta, ds0, B, H, L, DV, rule, ws, s, saved);
   }
   return hipErrorInvalidValue;
 }
@@ -219,23 +223,27 @@ hipError_t bwd_dispatch_c(const T* q, const T* k, const T* v, const T* beta, con
 template <typename T>
 hipError_t launch_chunk_bwd(const T* q, const T* k, const T* v, const T* beta, const float* s0, const T* dout,
                             const float* dsf, T* dq, T* dk, T* dv, T* dbeta, float* ds0, int B, int H, int64_t L,
-                            int DK, int DV, int C, int rule, void* ws, hipStream_t s) {
+                            int DK, int DV, int C, int rule, void* ws, hipStream_t s, bool saved) {
   auto* w = static_cast<unsigned char*>(ws);
   switch (DK) {
-    case 16: return bwd_dispatch_c<T, 16>(q, k, v, beta, s0, dout, dsf, dq, dk, dv, dbeta, ds0, B, H, L, DV, C, rule, w, s);
-    case 32: return bwd_dispatch_c<T, 32>(q, k, v, beta, s0, dout, dsf, dq, dk, dv, dbeta, ds0, B, H, L, DV, C, rule, w, s);
-    case 64: return bwd_dispatch_c<T, 64>(q, k, v, beta, s0, dout, dsf, dq, dk, dv, dbeta, ds0, B, H, L, DV, C, rule, w, s);
-    case 128: return bwd_dispatch_c<T, 128>(q, k, v, beta, s0, dout, dsf, dq, dk, dv, dbeta, ds0, B, H, L, DV, C, rule, w, s);
+    case 16: return bwd_dispatch_c<T, 16>(q, k, v, beta, s0, dout, dsf, dq, dk, dv, dbeta, ds0, B, H, L, DV, C, rule, w, s, saved);
+    case 32: return bwd_dispatch_c<T, 32>(q, k, v, beta, s0, dout, dsf, dq, dk, dv, dbeta, ds0, B, H, L, DV, C, rule, w, s, saved);
+    case 64: return bwd_dispatch_c<T, 64>(q, k, v, beta, s0, dout, dsf, dq, dk, dv, dbeta, ds0, B, H, L, DV, C, rule, w, s, saved);
+    case 128: return bwd_dispatch_c<T, 128>(q, k, v, beta, s0, dout, dsf, dq, dk, dv, dbeta, ds0, B, H, L, DV, C, rule, w, s, saved);
   }
   return hipErrorInvalidValue;
 }
 
 template hipError_t launch_chunk_bwd<float>(const float*, const float*, const float*, const float*, const float*,
                                             const float*, const float*, float*, float*, float*, float*, float*, int,
-                                            int, int64_t, int, int, int, int, void*, hipStream_t);
+                                            int, int64_t, int, int, int, int, void*, hipStream_t, bool);
 template hipError_t launch_chunk_bwd<uint16_t>(const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*,
                                                const float*, const uint16_t*, const float*, uint16_t*, uint16_t*,
                                                uint16_t*, uint16_t*, float*, int, int, int64_t, int, int, int, int,
-                                               void*, hipStream_t);
+                                               void*, hipStream_t, bool);
+
+bool train_saves_states(int DK, int DV, int C) {
+  return recurrence_split_supported(DK, C, 32) && DV % 32 == 0 && bwd_bf16_supported(DK, DV, C);
+}
 
 }  // namespace efla

@@ -58,12 +58,15 @@ hipError_t launch_recurrence_roles_bf16(const uint16_t* q, const uint16_t* k, co
 
 // bf16 recurrence with each chunk's work spread over nine wavefronts
 // (recurrence_split.h): d_k in {64, 128}, chunk 64, value blocks of 32;
-// forward instance only (output and final state), dense or packed batches.
+// forward instance only (output and final state), dense or packed batches;
+// statesT (dense batches, BV 32): also every chunk's start state as the bf16
+// operand values, [slots][DV][DK] as the backward's state-only pass writes them.
 bool recurrence_split_supported(int DK, int C, int BV);
 hipError_t launch_recurrence_split_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                         const uint16_t* tws, const float* s0, uint16_t* o, float* sfin,
                                         int B, int H, int64_t L, int DK, int DV, int C, int BV,
-                                        const int32_t* cu, int N, const int32_t* order, hipStream_t s);
+                                        const int32_t* cu, int N, const int32_t* order, hipStream_t s,
+                                        uint16_t* statesT = nullptr);
 
 // bf16 state-only pass of the segment scan (recurrence_states.h): every
 // sequence's N (state from zero, true values) into nout [N*H, DK, DV] and M
@@ -113,6 +116,8 @@ hipError_t launch_ut_wave_bwd_bf16(const uint16_t* k, const uint16_t* beta, cons
 
 // Backward pass of the chunked forward (bwd.hip, bwd_kernels.h): dense
 // batches, any supported d_k / d_v / chunk; ws holds bwd_layout(...).total bytes.
+// saved: the forward pass stored the chunk start states in ws (region s,
+// transposed); used where the bf16 matrix-core kernels run, else recomputed.
 struct BwdLayout {
   size_t t, x, p, a, s, ds, qe, total;  // byte offsets of the workspace regions, and the size
 };
@@ -120,7 +125,10 @@ BwdLayout bwd_layout(int B, int H, int64_t L, int DK, int DV, int C, size_t esz)
 template <typename T>
 hipError_t launch_chunk_bwd(const T* q, const T* k, const T* v, const T* beta, const float* s0, const T* dout,
                             const float* dsf, T* dq, T* dk, T* dv, T* dbeta, float* ds0, int B, int H, int64_t L,
-                            int DK, int DV, int C, int rule, void* ws, hipStream_t s);
+                            int DK, int DV, int C, int rule, void* ws, hipStream_t s, bool saved = false);
+// bf16 shapes whose training forward stores the chunk start states (the split
+// recurrence with value blocks of 32, and the bf16 backward kernels)
+bool train_saves_states(int DK, int DV, int C);
 
 // Segment scan (seg.hip): offsets of the packed view of B sequences of L
 // tokens cut into G segments of Ls tokens, and the combine along each sequence.

@@ -70,12 +70,16 @@ struct SplitShape {
 
 inline bool split_supported(int DK, int C, int BV) { return C == 64 && BV == 32 && (DK == 64 || DK == 128); }
 
-template <int DK, int C, int BV, int NDMA>
+// SAVE: the S wavefronts also store the state at the start of every chunk, as
+// the bf16 operand values the products use, transposed ([slots][DV][DK], the
+// layout of the backward's state-only pass), so that a training step's
+// backward pass need not recompute them.
+template <int DK, int C, int BV, int NDMA, bool SAVE = false>
 __global__ __launch_bounds__(64 * (8 + NDMA)) void recurrence_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ tws, const float* s0, uint16_t* __restrict__ o, float* sfin, int H, int64_t L,
     int NC, int DV, int NVB, int remap, const int32_t* __restrict__ cu, const int32_t* __restrict__ order,
-    int nseq) {
+    int nseq, uint16_t* __restrict__ statesT = nullptr) {
   using S = SplitShape<DK, C, BV, NDMA>;
   constexpr int NT = S::NT, NRT = S::NRT, NKU_D = S::NKU_D, NKU_C = S::NKU_C, KH = S::KH, NPF = S::NPF;
   __shared__ __align__(1024) uint16_t ring[3 * S::SLOT];  // three chunk slots of 44 KiB
@@ -265,14 +269,25 @@ __global__ __launch_bounds__(64 * (8 + NDMA)) void recurrence_split_kernel(
           St[d][c][qq] = s0 != nullptr
                              ? s0[(int64_t(bh) * DK + key_phys(16 * (dt0 + d) + 4 * g + qq)) * DV + v0 + 16 * c + li]
                              : 0.0f;
-    auto publish = [&]() {
+    // S_m as operand fragments; SAVE: also chunk m's start state, fragment
+    // (u, c) = key dims 32 (ku0 + u) + 8 g .. + 7 of column v0 + 16 c + li
+    auto publish = [&](int m) {
 #pragma unroll
       for (int u = 0; u < KH; ++u)
 #pragma unroll
-        for (int c = 0; c < NT; ++c) bS_buf[c][ku0 + u][lane] = acc_frag<uint16_t>(St[2 * u][c], St[2 * u + 1][c]).v;
+        for (int c = 0; c < NT; ++c) {
+          const bf16x8 f = acc_frag<uint16_t>(St[2 * u][c], St[2 * u + 1][c]).v;
+          bS_buf[c][ku0 + u][lane] = f;
+          if constexpr (SAVE) {
+            if (m < nc)
+              __builtin_nontemporal_store(
+                  f, reinterpret_cast<bf16x8*>(statesT + ((sp.slot0 + m) * DV + v0 + 16 * c + li) * DK +
+                                               32 * (ku0 + u) + 8 * g));
+          }
+        }
     };
-    publish();
-    run([&](const uint16_t* __restrict__ cur, const uint16_t*, int) {
+    publish(0);
+    run([&](const uint16_t* __restrict__ cur, const uint16_t*, int n) {
       sync();  // A
       Frag<uint16_t> KT[2 * KH][NKU_C];
 #pragma unroll
@@ -291,7 +306,7 @@ __global__ __launch_bounds__(64 * (8 + NDMA)) void recurrence_split_kernel(
         for (int c = 0; c < NT; ++c)
 #pragma unroll
           for (int kt = 0; kt < NKU_C; ++kt) mma(St[d][c], KT[d][kt], bU[c][kt]);
-      publish();
+      publish(n + 1);
     });
     if (sfin != nullptr) {
 #pragma unroll
@@ -424,7 +439,7 @@ template <int DK, int C, int BV, int NDMA>
 hipError_t recurrence_split_launch_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                         const uint16_t* tws, const float* s0, uint16_t* o, float* sfin, int B,
                                         int H, int64_t L, int DV, const int32_t* cu, int N, const int32_t* order,
-                                        hipStream_t stream) {
+                                        hipStream_t stream, uint16_t* statesT = nullptr) {
   const int NC = cu == nullptr ? int((L + C - 1) / C) : int(L / C) + N;  // chunk slots per sequence / head
   const int BH = (cu == nullptr ? B : N) * H;
   const int NVB = DV / BV;
@@ -432,25 +447,35 @@ hipError_t recurrence_split_launch_impl(const uint16_t* q, const uint16_t* k, co
   if (nwg == 0) return hipSuccess;
   if (cu == nullptr) order = nullptr;  // dense batches keep their order
   const int remap = (BH % 8 == 0) ? 1 : 0;
+  if constexpr (NDMA == 1) {
+    if (statesT != nullptr) {
+      hipLaunchKernelGGL((recurrence_split_kernel<DK, C, BV, NDMA, true>), dim3(unsigned(nwg)),
+                         dim3(unsigned(SplitShape<DK, C, BV, NDMA>::THREADS)), 0, stream, q, k, v, tws, s0, o, sfin, H, L,
+                         NC, DV, NVB, remap, cu, order, N, statesT);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((recurrence_split_kernel<DK, C, BV, NDMA>), dim3(unsigned(nwg)),
                      dim3(unsigned(SplitShape<DK, C, BV, NDMA>::THREADS)), 0, stream, q, k, v, tws, s0, o, sfin, H, L, NC,
                      DV, NVB, remap, cu, order, N);
   return hipGetLastError();
 }
 
-// ndma: DMA wavefronts per workgroup (1 or 2).
+// ndma: DMA wavefronts per workgroup (1 or 2); statesT (non-null: one DMA
+// wavefront) receives the chunk start states.
 inline hipError_t launch_recurrence_split(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                           const uint16_t* tws, const float* s0, uint16_t* o, float* sfin, int B,
                                           int H, int64_t L, int DK, int DV, int C, int BV, const int32_t* cu, int N,
-                                          const int32_t* order, int ndma, hipStream_t s) {
+                                          const int32_t* order, int ndma, hipStream_t s, uint16_t* statesT = nullptr) {
+  if (statesT != nullptr) ndma = 1;
   if (C == 64 && BV == 32) {
     if (DK == 64) {
       if (ndma == 2) return recurrence_split_launch_impl<64, 64, 32, 2>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, order, s);
-      return recurrence_split_launch_impl<64, 64, 32, 1>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, order, s);
+      return recurrence_split_launch_impl<64, 64, 32, 1>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, order, s, statesT);
     }
     if (DK == 128) {
       if (ndma == 2) return recurrence_split_launch_impl<128, 64, 32, 2>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, order, s);
-      return recurrence_split_launch_impl<128, 64, 32, 1>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, order, s);
+      return recurrence_split_launch_impl<128, 64, 32, 1>(q, k, v, tws, s0, o, sfin, B, H, L, DV, cu, N, order, s, statesT);
     }
   }
   return hipErrorInvalidValue;

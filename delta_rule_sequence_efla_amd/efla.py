@@ -79,6 +79,12 @@ def lib() -> ctypes.CDLL:
         L.efla_chunk_bwd_workspace_size.argtypes = [_i, _i, _i64, _i, _i, _i, _i]
         L.efla_chunk_bwd.restype = _i
         L.efla_chunk_bwd.argtypes = [_vp] * 12 + [_i, _i, _i64, _i, _i, _i, _i, _i, _vp, _sz, _vp]
+        L.efla_chunk_train_saves_states.restype = _i
+        L.efla_chunk_train_saves_states.argtypes = [_i, _i, _i, _i]
+        L.efla_chunk_fwd_train.restype = _i
+        L.efla_chunk_fwd_train.argtypes = [_vp] * 7 + [_i, _i, _i64, _i, _i, _i, _i, _i, _vp, _sz, _vp]
+        L.efla_chunk_bwd_train.restype = _i
+        L.efla_chunk_bwd_train.argtypes = [_vp] * 12 + [_i, _i, _i64, _i, _i, _i, _i, _i, _vp, _sz, _vp]
         L.efla_chunk_fwd_varlen_workspace_size.restype = _sz
         L.efla_chunk_fwd_varlen_workspace_size.argtypes = [_i, _i, _i64, _i, _i, _i, _i]
         L.efla_chunk_fwd_noalloc.restype = _i
@@ -385,6 +391,58 @@ def efla_chunk_bwd(q, k, v, beta, d_o, s0=None, ds_final=None, chunk: int = 64, 
     return gq, gk, gv, gb, gs0
 
 
+def efla_chunk_train_saves_states(d_k: int, d_v: int, chunk: int, dtype) -> bool:
+    return bool(lib().efla_chunk_train_saves_states(d_k, d_v, chunk, _code(dtype)))
+
+
+def efla_chunk_fwd_train(q, k, v, beta, s0=None, chunk: int = 64, o=None, s_final=None, workspace=None,
+                         want_final: bool = True, rule: str = "exact"):
+    """efla_chunk_fwd that also leaves in ``workspace`` (bytes of
+    efla_chunk_bwd_workspace_size; allocated here when None) what
+    efla_chunk_bwd_train reads.  Returns (o, S_L or None, workspace)."""
+    dev = _dev(q, k, v, beta, o, workspace, dtype=None)
+    _dev(q, k, v, beta, o, dtype=q.dtype)
+    _dev(s0, s_final, dtype=torch.float32)
+    B, L, H, dk, dv = _chunk_shapes(q, k, v, beta, s0)
+    _fwd_outs(o, s_final, B, L, H, dk, dv, q.dtype, q)
+    if o is None:
+        o = torch.empty((B, L, H, dv), dtype=q.dtype, device=dev)
+    if s_final is None and want_final:
+        s_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if workspace is None:
+        n = efla_chunk_bwd_workspace_size(B, H, L, dk, dv, chunk, q.dtype)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    nws = _ws(workspace, dev)
+    with torch.cuda.device(dev):
+        _check(lib().efla_chunk_fwd_train(_p(q), _p(k), _p(v), _p(beta), _p(s0), _p(o), _p(s_final),
+                                          B, H, L, dk, dv, chunk, _code(q.dtype), _rule(rule), _p(workspace),
+                                          nws, _stream(dev)), "efla_chunk_fwd_train")
+    return o, s_final, workspace
+
+
+def efla_chunk_bwd_train(q, k, v, beta, d_o, workspace, s0=None, ds_final=None, chunk: int = 64,
+                         rule: str = "exact", want_ds0: bool = True):
+    """efla_chunk_bwd after efla_chunk_fwd_train (same inputs, sizes, rule
+    and the workspace it filled).  Returns (dq, dk, dv, dbeta, ds0)."""
+    dev = _dev(q, k, v, beta, d_o, workspace, dtype=None)
+    _dev(q, k, v, beta, d_o, dtype=q.dtype)
+    _dev(s0, ds_final, dtype=torch.float32)
+    B, L, H, dk, dv = _chunk_shapes(q, k, v, beta, s0)
+    if d_o.shape != v.shape:
+        raise ValueError("d_o must have the shape of v")
+    if ds_final is not None and ds_final.shape != (B, H, dk, dv):
+        raise ValueError("ds_final must be float32 [B,H,dk,dv]")
+    gq, gk, gv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    gb = torch.empty_like(beta)
+    gs0 = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if want_ds0 else None
+    nws = _ws(workspace, dev)
+    with torch.cuda.device(dev):
+        _check(lib().efla_chunk_bwd_train(_p(q), _p(k), _p(v), _p(beta), _p(s0), _p(d_o), _p(ds_final), _p(gq),
+                                          _p(gk), _p(gv), _p(gb), _p(gs0), B, H, L, dk, dv, chunk, _code(q.dtype),
+                                          _rule(rule), _p(workspace), nws, _stream(dev)), "efla_chunk_bwd_train")
+    return gq, gk, gv, gb, gs0
+
+
 def efla_chunk_fwd_varlen_workspace_size(N, H, T, d_k, d_v, chunk, dtype) -> int:
     return int(lib().efla_chunk_fwd_varlen_workspace_size(N, H, T, d_k, d_v, chunk, _code(dtype)))
 
@@ -532,6 +590,29 @@ def prepare_chunk_bwd(q, k, v, beta, d_o, s0, ds_final, dq, dk, dv, dbeta, ds0, 
                          _p(dbeta), _p(ds0), B, H, L, d_k, d_v, chunk, _code(q.dtype), _rule(rule), _p(workspace),
                          nws, _stream(dev)),
                         "efla_chunk_bwd", (q, k, v, beta, d_o, s0, ds_final, dq, dk, dv, dbeta, ds0, workspace))
+
+
+def prepare_chunk_train(q, k, v, beta, d_o, s0, o, s_final, ds_final, dq, dk, dv, dbeta, ds0, workspace,
+                        chunk: int = 64, rule: str = "exact"):
+    """(forward, backward) prepared calls of the training pair sharing ``workspace``."""
+    dev = _dev(q, k, v, beta, d_o, o, dq, dk, dv, dbeta, dtype=q.dtype)
+    _dev(s0, s_final, ds_final, ds0, dtype=torch.float32)
+    B, L, H, d_k, d_v = _chunk_shapes(q, k, v, beta, s0)
+    _fwd_outs(o, s_final, B, L, H, d_k, d_v, q.dtype, q)
+    for t, like, name in ((d_o, v, "d_o"), (dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv"), (dbeta, beta, "dbeta")):
+        _want(t, like.shape, name)
+    _want(ds_final, (B, H, d_k, d_v), "ds_final")
+    _want(ds0, (B, H, d_k, d_v), "ds0")
+    code, ws, nws, stream = _code(q.dtype), _p(workspace), _ws(workspace, dev), _stream(dev)
+    fwd = PreparedCall(lib().efla_chunk_fwd_train,
+                       (_p(q), _p(k), _p(v), _p(beta), _p(s0), _p(o), _p(s_final), B, H, L, d_k, d_v, chunk, code,
+                        _rule(rule), ws, nws, stream),
+                       "efla_chunk_fwd_train", (q, k, v, beta, s0, o, s_final, workspace))
+    bwd = PreparedCall(lib().efla_chunk_bwd_train,
+                       (_p(q), _p(k), _p(v), _p(beta), _p(s0), _p(d_o), _p(ds_final), _p(dq), _p(dk), _p(dv),
+                        _p(dbeta), _p(ds0), B, H, L, d_k, d_v, chunk, code, _rule(rule), ws, nws, stream),
+                       "efla_chunk_bwd_train", (q, k, v, beta, d_o, s0, ds_final, dq, dk, dv, dbeta, ds0, workspace))
+    return fwd, bwd
 
 
 def prepare_step(q, k, v, beta, state, o, rule: str = "exact"):

@@ -227,6 +227,34 @@ efla_status efla_chunk_bwd(const void *q, const void *k, const void *v, const vo
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Training pair: a forward pass that keeps in the workspace what the backward
+ * pass would otherwise recompute, and that backward pass.  Same operation,
+ * arguments, layouts and results as efla_chunk_fwd_rule and efla_chunk_bwd
+ * (Method step 3 and its reverse-mode derivative); the workspace is the one
+ * of efla_chunk_bwd_workspace_size(...) (caller-owned, 16-byte aligned), and
+ * must pass unchanged from efla_chunk_fwd_train to efla_chunk_bwd_train with
+ * the same q, k, v, beta, s0, sizes, dtype and rule, on the same stream (or
+ * ordered after it).  Where efla_chunk_train_saves_states(...) is 1 (bf16,
+ * d_k 64 or 128, d_v a multiple of 32, chunk 64), the forward pass stores
+ * every chunk's start state there (as the bf16 values its products use) and
+ * the backward pass reads them instead of running the forward recurrence a
+ * second time; elsewhere the pair behaves as efla_chunk_fwd_rule followed by
+ * efla_chunk_bwd.  o and s_final are bitwise those of efla_chunk_fwd_rule.
+ * Errors as for those two calls; a workspace written by anything else in
+ * between gives wrong gradients, not an error.
+ */
+int efla_chunk_train_saves_states(int d_k, int d_v, int chunk, efla_dtype dtype);
+efla_status efla_chunk_fwd_train(const void *q, const void *k, const void *v, const void *beta,
+                                 const float *s0, void *o, float *s_final, int B, int H, int64_t L,
+                                 int d_k, int d_v, int chunk, efla_dtype dtype, efla_rule rule,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+efla_status efla_chunk_bwd_train(const void *q, const void *k, const void *v, const void *beta,
+                                 const float *s0, const void *d_o, const float *ds_final, void *dq,
+                                 void *dk, void *dv, void *dbeta, float *ds0, int B, int H, int64_t L,
+                                 int d_k, int d_v, int chunk, efla_dtype dtype, efla_rule rule,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Variable-length batches.  N sequences of different lengths packed along one
  * token axis, as a training or serving batch without padding holds them:
  *     q, k [T, H, d_k]   v, o [T, H, d_v]   beta [T, H]   (dtype)

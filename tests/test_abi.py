@@ -194,6 +194,41 @@ def test_backward_workspace_size_and_validation():
     assert call(L_=0, p=nul) == 0               # nothing to do, no ds0 wanted
 
 
+def test_training_pair_query_and_validation():
+    """The training pair stores chunk states only for the shapes whose split
+    recurrence and bf16 backward kernels both apply; both calls validate like
+    efla_chunk_fwd / efla_chunk_bwd, against the backward workspace size."""
+    saves = efla.efla_chunk_train_saves_states
+    assert saves(128, 128, 64, torch.bfloat16) and saves(64, 64, 64, torch.bfloat16)
+    assert saves(128, 64, 64, torch.bfloat16) and saves(64, 128, 64, torch.bfloat16)
+    assert not saves(128, 128, 64, torch.float32)       # fp32: no split recurrence
+    assert not saves(128, 128, 32, torch.bfloat16)      # chunk 32
+    assert not saves(32, 128, 64, torch.bfloat16)       # d_k 32
+    assert not saves(128, 16, 64, torch.bfloat16)       # d_v below one value block
+    assert not saves(48, 128, 64, torch.bfloat16)       # unsupported size
+    L = efla.lib()
+    nul, fake = None, 4096
+    need = efla.efla_chunk_bwd_workspace_size(1, 1, 64, 16, 16, 16, torch.float32)
+    assert need > efla.efla_chunk_fwd_workspace_size(1, 1, 64, 16, 16, 16, torch.float32)
+
+    def fwd(B=1, L_=64, dk=16, C=16, rule=0, p=fake, ws=nul, wsb=0, sf=nul):
+        return L.efla_chunk_fwd_train(p, p, p, p, nul, p, sf, B, 1, L_, dk, 16, C, 0, rule, ws, wsb, nul)
+
+    assert fwd(rule=3) == 1 and fwd(B=0) == 1 and fwd(dk=24) == 2 and fwd(C=48) == 2
+    assert fwd(p=nul) == 1 and fwd(p=fake + 4) == 1
+    assert fwd() == 3 and fwd(ws=fake, wsb=need - 1) == 3  # the forward's own size is too small
+    assert fwd(L_=0, p=nul) == 0                          # nothing to do, no final state wanted
+
+    def bwd(B=1, L_=64, dk=16, C=16, rule=0, p=fake, ws=nul, wsb=0, ds0=nul):
+        return L.efla_chunk_bwd_train(p, p, p, p, nul, p, nul, p, p, p, p, ds0, B, 1, L_, dk, 16, C, 0, rule, ws,
+                                      wsb, nul)
+
+    assert bwd(rule=3) == 1 and bwd(B=0) == 1 and bwd(dk=24) == 2 and bwd(C=48) == 2
+    assert bwd(p=nul) == 1 and bwd(p=fake + 4) == 1
+    assert bwd() == 3 and bwd(ws=fake, wsb=need - 1) == 3
+    assert bwd(L_=0, p=nul) == 0
+
+
 def test_segmented_workspace_size_and_validation():
     f = efla.efla_chunk_fwd_segmented_workspace_size
     assert f(1, 1, 0, 16, 16, 16, 4, torch.float32) == 0
