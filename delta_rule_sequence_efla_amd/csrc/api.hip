@@ -467,17 +467,28 @@ efla_status efla_chunk_fwd_train(const void* q, const void* k, const void* v, co
     const size_t need = efla_chunk_bwd_workspace_size(B, H, L, d_k, d_v, chunk, dtype);
     if (workspace == nullptr || workspace_bytes < need) return EFLA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return EFLA_ERR_INVALID_ARG;
+    if (efla_chunk_train_saves_states(d_k, d_v, chunk, dtype)) {
+      // the backward's UT instance (T, and X, a, bf16 P and Qe for the
+      // backward), then the recurrence storing the chunk start states, all
+      // in the backward workspace's regions
+      unsigned char* ws = static_cast<unsigned char*>(workspace);
+      const efla::BwdLayout lay = efla::bwd_layout(B, H, L, d_k, d_v, chunk, 2);
+      const auto* kb = static_cast<const uint16_t*>(k);
+      auto* tws = reinterpret_cast<uint16_t*>(ws + lay.t);
+      if (hipError_t e = efla::launch_ut_wave_bwd_bf16(
+              kb, static_cast<const uint16_t*>(beta), static_cast<const uint16_t*>(q), tws,
+              reinterpret_cast<float*>(ws + lay.x), reinterpret_cast<float*>(ws + lay.a),
+              reinterpret_cast<float*>(ws + lay.p), reinterpret_cast<uint16_t*>(ws + lay.qe), B, H, L, d_k, chunk,
+              int(rule), s, true);
+          e != hipSuccess)
+        return from_hip(e);
+      return from_hip(efla::launch_recurrence_split_bf16(
+          static_cast<const uint16_t*>(q), kb, static_cast<const uint16_t*>(v), tws, s0, static_cast<uint16_t*>(o),
+          s_final, B, H, L, d_k, d_v, chunk, 32, nullptr, 0, nullptr, s, reinterpret_cast<uint16_t*>(ws + lay.s)));
+    }
     // T at the workspace's start, where efla_chunk_fwd keeps it too
     const efla_status s1 = launch_ut(k, beta, B, H, L, d_k, chunk, dtype, rule, workspace, nullptr, 0, s);
     if (s1 != EFLA_OK) return s1;
-    if (efla_chunk_train_saves_states(d_k, d_v, chunk, dtype)) {
-      auto* states = reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(workspace) +
-                                                 efla::bwd_layout(B, H, L, d_k, d_v, chunk, 2).s);
-      return from_hip(efla::launch_recurrence_split_bf16(
-          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-          static_cast<const uint16_t*>(workspace), s0, static_cast<uint16_t*>(o), s_final, B, H, L, d_k, d_v, chunk,
-          32, nullptr, 0, nullptr, s, states));
-    }
   } else if (s_final == nullptr) {
     return EFLA_OK;
   }

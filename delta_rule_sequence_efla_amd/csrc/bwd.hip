@@ -110,7 +110,12 @@ hipError_t bwd_launch_impl(const T* q, const T* k, const T* v, const T* beta, co
     rev = bf16k && !(impl && strcmp(impl, "stager") == 0) && reverse_states_supported(DK, DV, C);
   }
   bool states_t = false;  // the chunk states are stored transposed
-  if (slots > 0) {
+  // saved: the training forward left steps 1 and 2's results in the workspace
+  // (T, X, a, bf16 P, Qe and the transposed chunk states), read only by the
+  // bf16 matrix-core kernels; else both steps run here
+  const bool from_fwd = saved && bf16k;
+  if (from_fwd) states_t = true;
+  if (slots > 0 && !from_fwd) {
     // 1. T, X, P and a of every chunk: one wavefront per chunk for the bf16
     // shapes that kernel covers (EFLA_UT_IMPL=workgroup keeps the other unless
     // the bf16 kernels follow), else one workgroup per chunk
@@ -139,13 +144,9 @@ hipError_t bwd_launch_impl(const T* q, const T* k, const T* v, const T* beta, co
       hipLaunchKernelGGL((ut_transform_kernel<T, DK, C, true>), dim3(unsigned(slots)), dim3(kThreads), 0, s, k,
                          beta, tws, H, L, NC, rule, nullptr, 0, q, xws, aws, pws);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    // 2. the state at the start of every chunk (no output), unless the forward
-    // pass left them in the workspace, transposed (read only by the bf16
-    // matrix-core kernels)
-    if (saved && bf16k)
-      states_t = true;
-    else if (hipError_t e = chunk_states<T, DK, C>(q, k, v, tws, s0, sws, B, H, L, DV, s, bf16k, &states_t);
-             e != hipSuccess)
+    // 2. the state at the start of every chunk (no output)
+    if (hipError_t e = chunk_states<T, DK, C>(q, k, v, tws, s0, sws, B, H, L, DV, s, bf16k, &states_t);
+        e != hipSuccess)
       return e;
   }
   // 3. reverse pass over chunks: dS at every chunk end, and dS_0 (bf16 inputs

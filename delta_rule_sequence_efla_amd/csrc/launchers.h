@@ -109,10 +109,11 @@ hipError_t launch_bwd_chunk_tr_bf16(const uint16_t* q, const uint16_t* k, const 
                                     int DK, int DV, int C, int rule, hipStream_t s);
 // Its backward instance over a dense batch: T, X (fp32), a (fp32) and P
 // (bf16, packed at the start of pws) of every chunk slot, and with qe the
-// chunk's Q - P T K (bf16 [slots][C][DK]); same shapes.
+// chunk's Q - P T K (bf16 [slots][C][DK]); same shapes.  t_plain: T with
+// ordinary stores, for a forward recurrence that reads it next.
 hipError_t launch_ut_wave_bwd_bf16(const uint16_t* k, const uint16_t* beta, const uint16_t* q, uint16_t* tws,
                                    float* xws, float* aws, float* pws, uint16_t* qe, int B, int H, int64_t L, int DK,
-                                   int C, int rule, hipStream_t s);
+                                   int C, int rule, hipStream_t s, bool t_plain = false);
 
 // Backward pass of the chunked forward (bwd.hip, bwd_kernels.h): dense
 // batches, any supported d_k / d_v / chunk; ws holds bwd_layout(...).total bytes.

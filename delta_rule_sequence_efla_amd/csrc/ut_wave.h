@@ -75,6 +75,7 @@ __device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory")
 //     Qe = Q - P T K   (bf16 [slots][C][d_k], rows of tokens past the end zero),
 // the operand through which the output reads the chunk's start state
 // (O = Qe S + P T V), so that the reverse pass over the chunks needs no P.
+// t_plain: T with ordinary stores (a recurrence reads it next).
 template <int DK, int C, bool BWD = false, bool PB16 = false>
 __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict__ k,
                                                       const uint16_t* __restrict__ beta,
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict
                                                       float* __restrict__ xout = nullptr,
                                                       float* __restrict__ aout = nullptr,
                                                       float* __restrict__ pout = nullptr,
-                                                      uint16_t* __restrict__ qtout = nullptr) {
+                                                      uint16_t* __restrict__ qtout = nullptr, int t_plain = 0) {
   using S = UtWaveShape<DK, C>;
   constexpr int NRT = S::NRT, NKU = S::NKU, GBLK = S::GBLK, XP = S::XP, XBLK = S::XBLK, TP = S::TP;
   constexpr int NKC = C / 32;  // k-units over the tokens of the chunk
@@ -292,7 +293,8 @@ __global__ __launch_bounds__(256) void ut_wave_kernel(const uint16_t* __restrict
     // nontemporal in the backward instance (the backward's passes ran faster
     // so, as with its other workspace stores); the forward's recurrence reads
     // T right after this kernel and ran ~8 us slower when T was written so
-    if constexpr (BWD) __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(out + r * C + c0));
+    // (t_plain: the backward instance run ahead of that recurrence)
+    if (BWD && !t_plain) __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(out + r * C + c0));
     else *reinterpret_cast<u32x4*>(out + r * C + c0) = val;
   }
 

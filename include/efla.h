@@ -236,10 +236,12 @@ efla_status efla_chunk_bwd(const void *q, const void *k, const void *v, const vo
  * the same q, k, v, beta, s0, sizes, dtype and rule, on the same stream (or
  * ordered after it).  Where efla_chunk_train_saves_states(...) is 1 (bf16,
  * d_k 64 or 128, d_v a multiple of 32, chunk 64), the forward pass stores
- * every chunk's start state there (as the bf16 values its products use) and
- * the backward pass reads them instead of running the forward recurrence a
- * second time; elsewhere the pair behaves as efla_chunk_fwd_rule followed by
- * efla_chunk_bwd.  o and s_final are bitwise those of efla_chunk_fwd_rule.
+ * there every chunk's UT-transform quantities (T, X, a, P and Q - P T K, as
+ * the backward pass forms them) and its start state (as the bf16 values the
+ * forward products use), and the backward pass reads them instead of running
+ * the UT transform and the forward recurrence a second time; elsewhere the
+ * pair behaves as efla_chunk_fwd_rule followed by efla_chunk_bwd.  o and
+ * s_final are bitwise those of efla_chunk_fwd_rule.
  * Errors as for those two calls; a workspace written by anything else in
  * between gives wrong gradients, not an error.
  */

@@ -1,6 +1,7 @@
 """The training pair (efla_chunk_fwd_train, efla_chunk_bwd_train): the forward
-pass stores every chunk's start state in the backward workspace and the
-backward pass reads them instead of running the recurrence again.
+pass stores every chunk's UT-transform quantities and start state in the
+backward workspace and the backward pass reads them instead of running the UT
+transform and the recurrence again.
 
 Checked here: the forward's outputs are bitwise those of efla_chunk_fwd; each
 stored state equals the oracle's state after that chunk's prefix of tokens
