@@ -269,24 +269,30 @@ __global__ __launch_bounds__(64 * (8 + NDMA)) void recurrence_split_kernel(
           St[d][c][qq] = s0 != nullptr
                              ? s0[(int64_t(bh) * DK + key_phys(16 * (dt0 + d) + 4 * g + qq)) * DV + v0 + 16 * c + li]
                              : 0.0f;
-    // S_m as operand fragments; SAVE: also chunk m's start state, fragment
-    // (u, c) = key dims 32 (ku0 + u) + 8 g .. + 7 of column v0 + 16 c + li
-    auto publish = [&](int m) {
+    // S_m as operand fragments: fragment (u, c) = key dims 32 (ku0 + u) +
+    // 8 g .. + 7 of column v0 + 16 c + li
+    auto publish = [&]() {
 #pragma unroll
       for (int u = 0; u < KH; ++u)
 #pragma unroll
-        for (int c = 0; c < NT; ++c) {
-          const bf16x8 f = acc_frag<uint16_t>(St[2 * u][c], St[2 * u + 1][c]).v;
-          bS_buf[c][ku0 + u][lane] = f;
-          if constexpr (SAVE) {
-            if (m < nc)
-              __builtin_nontemporal_store(
-                  f, reinterpret_cast<bf16x8*>(statesT + ((sp.slot0 + m) * DV + v0 + 16 * c + li) * DK +
-                                               32 * (ku0 + u) + 8 * g));
-          }
-        }
+        for (int c = 0; c < NT; ++c) bS_buf[c][ku0 + u][lane] = acc_frag<uint16_t>(St[2 * u][c], St[2 * u + 1][c]).v;
     };
-    publish(0);
+    // SAVE: chunk n's start state, from the fragments both S wavefronts
+    // published: this wavefront stores rows v0 + 16 hh .. + 15 of S^T, each
+    // instruction 8 rows x 128 contiguous bytes (each 16-lane read group
+    // takes 8 rows x 2 pieces: two lanes per bank)
+    auto save = [&](int n) {
+      constexpr int PR = DK / 8;  // 16-byte pieces per row
+#pragma unroll
+      for (int j = 0; j < PR / 4; ++j) {
+        const int rr = 8 * (j / (PR / 8)) + (lane & 7);
+        const int p = 8 * (j % (PR / 8)) + 2 * (lane >> 4) + ((lane >> 3) & 1);
+        const bf16x8 f = bS_buf[hh][p >> 2][16 * (p & 3) + rr];
+        __builtin_nontemporal_store(
+            f, reinterpret_cast<bf16x8*>(statesT + ((sp.slot0 + n) * DV + v0 + 16 * hh + rr) * DK + 8 * p));
+      }
+    };
+    publish();
     run([&](const uint16_t* __restrict__ cur, const uint16_t*, int n) {
       sync();  // A
       Frag<uint16_t> KT[2 * KH][NKU_C];
@@ -294,6 +300,7 @@ __global__ __launch_bounds__(64 * (8 + NDMA)) void recurrence_split_kernel(
       for (int d = 0; d < 2 * KH; ++d)
 #pragma unroll
         for (int kt = 0; kt < NKU_C; ++kt) KT[d][kt] = wide_frag_tr<DK>(cur + S::KOFF, dt0 + d, kt, lane);
+      if constexpr (SAVE) save(n);
       sync();  // B
       Frag<uint16_t> bU[NT][NKU_C];
 #pragma unroll
@@ -306,7 +313,7 @@ __global__ __launch_bounds__(64 * (8 + NDMA)) void recurrence_split_kernel(
         for (int c = 0; c < NT; ++c)
 #pragma unroll
           for (int kt = 0; kt < NKU_C; ++kt) mma(St[d][c], KT[d][kt], bU[c][kt]);
-      publish(n + 1);
+      publish();
     });
     if (sfin != nullptr) {
 #pragma unroll
