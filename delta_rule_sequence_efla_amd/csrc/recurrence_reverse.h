@@ -235,21 +235,34 @@ __global__ __launch_bounds__((64 * ReverseShape<DK, C, BV>::NWAVES)) void revers
           const int key = key_phys(16 * (2 * sw + d) + 4 * g + qq);
           St[d][c][qq] = dsf != nullptr ? dsf[(int64_t(bh) * DK + key) * DV + col0 + 16 * c + li] : 0.0f;
         }
-    // dS' of chunk m as operand fragments and as dstates[m]: fragment c holds
-    // key dims 32 sw + 8 g .. + 7 of column col0 + 16 c + li
-    auto publish = [&](int m) {
+    // dS' as operand fragments: fragment c holds key dims 32 sw + 8 g .. + 7
+    // of column col0 + 16 c + li
+    auto publish = [&]() {
 #pragma unroll
-      for (int c = 0; c < NT; ++c) {
-        const bf16x8 f = acc_frag<uint16_t>(St[0][c], St[1][c]).v;
-        bS_buf[c][sw][lane] = f;
-        if (m >= 0)
-          __builtin_nontemporal_store(
-              f, reinterpret_cast<bf16x8*>(dstatesT + ((sp.slot0 + m) * DV + col0 + 16 * c + li) * DK + 32 * sw + 8 * g));
+      for (int c = 0; c < NT; ++c) bS_buf[c][sw][lane] = acc_frag<uint16_t>(St[0][c], St[1][c]).v;
+    };
+    // dstates[m] (m: the chunk of this step, whose end-gradient the buffer
+    // holds), from the fragments every S wavefront published: this wavefront
+    // stores its share of the rows of dS'^T (8 with d_k 128, 16 with d_k 64),
+    // each instruction 8 rows x 128 contiguous bytes (two lanes per bank in
+    // each 16-lane read group), nontemporal; every row is written whole
+    // (from the registers, 64-byte pieces from several wavefronts wrote 1.16x
+    // the bytes)
+    auto save = [&](int m) {
+      constexpr int PR = DK / 8, RW = BV / NKU_D;  // 16-byte pieces per row, rows per S wavefront
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = RW * sw + 8 * (PR == 16 ? 0 : j) + (lane & 7);
+        const int p = 8 * (PR == 16 ? j : 0) + 2 * (lane >> 4) + ((lane >> 3) & 1);
+        const bf16x8 f = bS_buf[r >> 4][p >> 2][16 * (p & 3) + (r & 15)];
+        __builtin_nontemporal_store(
+            f, reinterpret_cast<bf16x8*>(dstatesT + ((sp.slot0 + m) * DV + col0 + r) * DK + 8 * p));
       }
     };
-    publish(nc - 1);
+    publish();
     run([&](const uint16_t* __restrict__ cur, int n) {
       sync();  // A
+      save(chunk_of(n));
       Frag<uint16_t> KT[2][NKU_C], QT[2][NKU_C], dOf[NT][NKU_C];
 #pragma unroll
       for (int d = 0; d < 2; ++d)
@@ -280,7 +293,7 @@ __global__ __launch_bounds__((64 * ReverseShape<DK, C, BV>::NWAVES)) void revers
         for (int c = 0; c < NT; ++c)
 #pragma unroll
           for (int kt = 0; kt < NKU_C; ++kt) mma(St[d][c], KT[d][kt], bF[c][kt]);
-      publish(chunk_of(n) - 1);
+      publish();
     });
     if (ds0 != nullptr) {
 #pragma unroll

@@ -253,25 +253,34 @@ __global__ __launch_bounds__((64 * StatesShape<DK, C, BV, BWD>::NWAVES)) void re
           else
             St[d][c][qq] = (ch == 1 && key == col0 + 16 * c + li) ? 1.0f : 0.0f;
         }
-    // S_m as operand fragments; BWD: also the start state of chunk m, whose
-    // fragment (u, c) holds key dims 32 (ku0 + u) + 8 g .. + 7 of column
-    // col0 + 16 c + li
-    auto publish = [&](int m) {
+    // S_m as operand fragments: fragment (u, c) holds key dims 32 (ku0 + u)
+    // + 8 g .. + 7 of column col0 + 16 c + li
+    auto publish = [&]() {
 #pragma unroll
       for (int u = 0; u < KH; ++u)
 #pragma unroll
-        for (int c = 0; c < NT; ++c) {
-          const bf16x8 f = acc_frag<uint16_t>(St[2 * u][c], St[2 * u + 1][c]).v;
-          bS_buf[ch][c][ku0 + u][lane] = f;
-          if constexpr (BWD) {  // nontemporal: plain stores stalled this wave's LDS reads (1.4x longer pass)
-            if (m < nc)
-              __builtin_nontemporal_store(f, reinterpret_cast<bf16x8*>(statesT + ((sp.slot0 + m) * DV + col0 +
-                                                                                  16 * c + li) * DK +
-                                                                        32 * (ku0 + u) + 8 * g));
-          }
-        }
+        for (int c = 0; c < NT; ++c)
+          bS_buf[ch][c][ku0 + u][lane] = acc_frag<uint16_t>(St[2 * u][c], St[2 * u + 1][c]).v;
     };
-    publish(0);
+    // BWD: the start state of chunk n, from the fragments both S wavefronts
+    // published: this wavefront stores rows col0 + 16 hh .. + 15 of S^T, each
+    // instruction 8 rows x 128 contiguous bytes (each 16-lane read group
+    // takes 8 rows x 2 pieces: two lanes per bank), nontemporal (plain stores
+    // stalled this wave's LDS reads: 1.4x longer pass).  Stored so, every
+    // row is written whole (from the registers, 64-byte pieces from two
+    // wavefronts wrote 1.3x the bytes).
+    auto save = [&](int n) {
+      constexpr int PR = DK / 8;  // 16-byte pieces per row
+#pragma unroll
+      for (int j = 0; j < PR / 4; ++j) {
+        const int rr = 8 * (j / (PR / 8)) + (lane & 7);
+        const int p = 8 * (j % (PR / 8)) + 2 * (lane >> 4) + ((lane >> 3) & 1);
+        const bf16x8 f = bS_buf[ch][hh][p >> 2][16 * (p & 3) + rr];
+        __builtin_nontemporal_store(
+            f, reinterpret_cast<bf16x8*>(statesT + ((sp.slot0 + n) * DV + col0 + 16 * hh + rr) * DK + 8 * p));
+      }
+    };
+    publish();
     run([&](const uint16_t* __restrict__ cur, int n) {
       sync();  // A
       Frag<uint16_t> KT[2 * KH][NKU_C];
@@ -279,6 +288,7 @@ __global__ __launch_bounds__((64 * StatesShape<DK, C, BV, BWD>::NWAVES)) void re
       for (int d = 0; d < 2 * KH; ++d)
 #pragma unroll
         for (int kt = 0; kt < NKU_C; ++kt) KT[d][kt] = wide_frag_tr<DK>(cur + S::KOFF, dt0 + d, kt, lane);
+      if constexpr (BWD) save(n);
       sync();  // B
       Frag<uint16_t> bU[NT][NKU_C];
 #pragma unroll
@@ -291,7 +301,7 @@ __global__ __launch_bounds__((64 * StatesShape<DK, C, BV, BWD>::NWAVES)) void re
         for (int c = 0; c < NT; ++c)
 #pragma unroll
           for (int kt = 0; kt < NKU_C; ++kt) mma(St[d][c], KT[d][kt], bU[c][kt]);
-      publish(n + 1);
+      publish();
     });
     const bool owner = !BWD && (ch == 0 ? vb < NVB_N : vb < NVB_M);
     float* const out = ch == 0 ? nout : mout;
