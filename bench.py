@@ -442,6 +442,23 @@ def main():
                                 tokens_per_s=round(ws_.tokens / (m / 1e3), 1), algorithmic_bytes=b,
                                 hbm_frac=round(b / (m / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                                 warm_us=round(warm_us(torch, (f,), K), 2))
+            # too few (b, h, value block) workgroups for the compute units: the
+            # segment scan on the same inputs beside it
+            G = efla.default_segments(ws_.B, ws_.H, ws_.L, ws_.dv, ws_.chunk)
+            if G > 1:
+                wsg = torch.empty(max(1, efla.efla_chunk_fwd_segmented_workspace_size(
+                    ws_.B, ws_.H, ws_.L, ws_.dk, ws_.dv, ws_.chunk, G, li["q"].dtype)), dtype=torch.uint8, device=dev)
+                fg = efla.prepare_chunk_fwd_segmented(li["q"], li["k"], li["v"], li["beta"], li["s0"], ol, sl, wsg,
+                                                      chunk=ws_.chunk, segments=G)
+                for _ in range(3):
+                    fg()
+                gms, _ = flushed_steps(torch, (fg,), K, fl.clean)
+                gm = pct(gms, 50)
+                shapes[name]["segmented"] = dict(stats_us(gms), segments=G,
+                                                 tokens_per_s=round(ws_.tokens / (gm / 1e3), 1),
+                                                 hbm_frac=round(b / (gm / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                                                 note="efla_chunk_fwd_segmented, the same inputs")
+                del wsg, fg
             del li, ol, sl, wsp, f
         line["shapes"] = shapes
 
