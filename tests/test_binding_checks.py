@@ -133,3 +133,25 @@ def test_prepared_calls_check_shapes(host):
         efla.prepare_chunk_stages(q, k, v, beta, None, o[..., :16], None, ws, chunk=16)
     with pytest.raises(ValueError):
         efla.prepare_chunk_bwd(q, k, v, beta, o, None, None, q, k, v[..., :16], beta, None, ws, chunk=16)
+
+
+def test_training_pair_checks_shapes_and_workspace_device(host):
+    q, k, v, beta = _inputs()
+    ws = torch.zeros(1 << 10, dtype=torch.uint8)
+    o = torch.zeros(2, 8, 3, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        efla.efla_chunk_fwd_train(q, k, v, beta, chunk=16, o=o[..., :16], workspace=ws)
+    with pytest.raises(ValueError):
+        efla.efla_chunk_fwd_train(q, k, v, beta, chunk=16, s_final=torch.zeros(2, 3, 16, 16), workspace=ws)
+    with pytest.raises(ValueError):
+        efla.efla_chunk_fwd_train(q, k, v, beta, chunk=16, workspace=ws.to("meta"))
+    with pytest.raises(ValueError):
+        efla.efla_chunk_bwd_train(q, k, v, beta, o[:, :4], ws, chunk=16)          # d_o not shaped like v
+    with pytest.raises(ValueError):
+        efla.efla_chunk_bwd_train(q, k, v, beta, o, ws, None, torch.zeros(2, 3, 16, 16), chunk=16)
+    with pytest.raises(ValueError):
+        efla.efla_chunk_bwd_train(q, k, v, beta, o, ws.to("meta"), chunk=16)
+    with pytest.raises(ValueError):
+        efla.prepare_chunk_train(q, k, v, beta, o, None, o, None, None, q, k, v[..., :16], beta, None, ws, chunk=16)
+    with pytest.raises(ValueError):
+        efla.prepare_chunk_train(q, k, v, beta, o, None, o[..., :16], None, None, q, k, v, beta, None, ws, chunk=16)
