@@ -20,6 +20,8 @@ Besides the contract fields the JSON line carries:
                 out, once) over its flushed event time
   path          the whole step (both kernels) against the same peak, and the
                 bytes each stage moves beyond the algorithmic ones
+  stream_copy   a flushed 1 GiB device copy: the measured bandwidth ceiling,
+                with the recurrence's and the path's fractions of it
   warm          the same step back to back with no flush (caches warm)
   dirty_flush   the step after a write-only flush (dirty lines left in the
                 caches, whose write-back then competes with the step)
@@ -413,6 +415,23 @@ def main():
         print(json.dumps(line), flush=True)
         return
     extras = not args.no_extras
+
+    # ---- the measured copy bandwidth: the secondary ceiling -------------------
+    # a 1 GiB device-to-device copy (1 GiB read + 1 GiB written), flushed like
+    # the steps; the spec 8 TB/s stays the primary peak
+    csrc_ = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    cdst_ = torch.empty_like(csrc_)
+    cpy = lambda: cdst_.copy_(csrc_)  # noqa: E731
+    for _ in range(3):
+        cpy()
+    cms, _ = flushed_steps(torch, (cpy,), 10, fl.clean)
+    copy_bytes = 2 * 4 * csrc_.numel()
+    copy_gbs = copy_bytes / (pct(cms, 50) / 1e3) / 1e9
+    del csrc_, cdst_, cpy
+    line["stream_copy"] = dict(stats_us(cms), bytes=copy_bytes, GBps=round(copy_gbs, 1),
+                               note="1 GiB device copy, read + write bytes, a flush before each")
+    line["roofline"]["frac_of_copy"] = round(achieved / copy_gbs, 4)
+    line["path"]["hbm_frac_of_copy"] = round(path_bytes / (med_ms / 1e3) / 1e9 / copy_gbs, 4)
 
     # ---- warm and dirty-flush references ----------------------------------
     wus = warm_us(torch, (ut, rec), K)
