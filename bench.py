@@ -20,8 +20,9 @@ Besides the contract fields the JSON line carries:
                 out, once) over its flushed event time
   path          the whole step (both kernels) against the same peak, and the
                 bytes each stage moves beyond the algorithmic ones
-  stream_copy   a flushed 1 GiB device copy: the measured bandwidth ceiling,
-                with the recurrence's and the path's fractions of it
+  stream        flushed 1 GiB read + write passes (device copy, in-place
+                scale): the measured bandwidth ceiling, with the recurrence's
+                and the path's fractions of it
   warm          the same step back to back with no flush (caches warm)
   dirty_flush   the step after a write-only flush (dirty lines left in the
                 caches, whose write-back then competes with the step)
@@ -416,22 +417,24 @@ def main():
         return
     extras = not args.no_extras
 
-    # ---- the measured copy bandwidth: the secondary ceiling -------------------
-    # a 1 GiB device-to-device copy (1 GiB read + 1 GiB written), flushed like
-    # the steps; the spec 8 TB/s stays the primary peak
-    csrc_ = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-    cdst_ = torch.empty_like(csrc_)
-    cpy = lambda: cdst_.copy_(csrc_)  # noqa: E731
-    for _ in range(3):
-        cpy()
-    cms, _ = flushed_steps(torch, (cpy,), 10, fl.clean)
-    copy_bytes = 2 * 4 * csrc_.numel()
-    copy_gbs = copy_bytes / (pct(cms, 50) / 1e3) / 1e9
-    del csrc_, cdst_, cpy
-    line["stream_copy"] = dict(stats_us(cms), bytes=copy_bytes, GBps=round(copy_gbs, 1),
-                               note="1 GiB device copy, read + write bytes, a flush before each")
-    line["roofline"]["frac_of_copy"] = round(achieved / copy_gbs, 4)
-    line["path"]["hbm_frac_of_copy"] = round(path_bytes / (med_ms / 1e3) / 1e9 / copy_gbs, 4)
+    # ---- the measured bandwidth: the secondary ceiling ----------------------
+    # 1 GiB read and written once (the runtime's device copy; an in-place scale
+    # by torch's elementwise kernel), flushed like the steps; the faster sets
+    # the measured ceiling, the spec 8 TB/s stays the primary peak
+    sa = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    sb = torch.empty_like(sa)
+    stream = {}
+    for sname, sfn in (("copy", lambda: sb.copy_(sa)), ("scale_in_place", lambda: sa.mul_(1.0))):
+        for _ in range(3):
+            sfn()
+        sms, _ = flushed_steps(torch, (sfn,), 10, fl.clean)
+        stream[sname] = dict(stats_us(sms), GBps=round(2 * 4 * sa.numel() / (pct(sms, 50) / 1e3) / 1e9, 1))
+    del sa, sb
+    ceiling = max(s["GBps"] for s in stream.values())
+    line["stream"] = dict(stream, bytes=2 * 4 * (1 << 28), ceiling_GBps=ceiling,
+                          note="1 GiB read + 1 GiB written, a flush before each of ten; median")
+    line["roofline"]["frac_of_measured"] = round(achieved / ceiling, 4)
+    line["path"]["hbm_frac_of_measured"] = round(path_bytes / (med_ms / 1e3) / 1e9 / ceiling, 4)
 
     # ---- warm and dirty-flush references ----------------------------------
     wus = warm_us(torch, (ut, rec), K)
