@@ -238,15 +238,22 @@ __global__ __launch_bounds__((BwdTrShape<DK, C>::NTH)) __attribute__((amdgpu_wav
       }
       put(Ut, u, rt, c, li, g);
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int r = 16 * rt + 4 * g + qq;
-        if (r < valid)
-          __builtin_nontemporal_store(from_f32<uint16_t>(dd[qq]), dv + row0 * DV + r * v_stride + v0 + 16 * c + li);
-        dd[qq] = -dd[qq];
-      }
+      for (int qq = 0; qq < 4; ++qq) dd[qq] = -dd[qq];
       put(dDt, dd, rt, c, li, g);  // as -dD
     }
     __syncthreads();
+    // dv = dD of the block from its staged tile, as whole 64-byte row pieces
+    // (four lanes a row; bf16 negation is exact): stored from the product
+    // tiles, as 32-byte pieces of two wavefronts, each 64-byte line was
+    // written in parts
+    if (tidv < 4 * C) {
+      const int r = tidv >> 2, p = tidv & 3;
+      if (r < valid) {
+        u32x4 x = *reinterpret_cast<const u32x4*>(dDt + r * BV + 8 * (p ^ swz_row<BV / 8>(r)));
+        x ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+        __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(dv + row0 * DV + r * v_stride + v0 + 8 * p));
+      }
+    }
     if (v0 + BV >= DV) {  // the tail's Q, during the last block (over T and P, done with)
       const auto* qs = static_cast<const uint16_t*>(uniform_ptr(q + row0 * DK));
 #pragma unroll
