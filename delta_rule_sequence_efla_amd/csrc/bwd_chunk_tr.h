@@ -23,6 +23,8 @@
 // two workgroups fit a SIMD's register file.
 #pragma once
 
+#include <type_traits>
+
 #include "bwd_kernels.h"
 #include "lds_ring.h"
 
@@ -187,7 +189,12 @@ __global__ __launch_bounds__((BwdTrShape<DK, C>::NTH)) __attribute__((amdgpu_wav
   static_assert(UX % NTH == 0, "whole units per thread");
 
   dma_block(0, true);
-  for (int v0 = 0; v0 < DV; v0 += BV) {
+  // one value block; the last one (LAST) also requests the tail's X after
+  // its first phase, so that the load overlaps the block's other two phases
+  // (requested after the block, the tail waited for it; before the first
+  // phase, the held registers spilled more)
+  auto block = [&](const int v0, auto lastc) {
+    constexpr bool LAST = decltype(lastc)::value;
     // the lane indices as values the compiler cannot see to be the same in
     // every block, so that the fragment addresses built from them are formed
     // here rather than held in registers across the loop
@@ -226,6 +233,13 @@ __global__ __launch_bounds__((BwdTrShape<DK, C>::NTH)) __attribute__((amdgpu_wav
     }
     __syncthreads();
     if (v0 + BV < DV) dma_rows(Vt, v, v0 + BV);  // V is read only in the phase above
+    if constexpr (LAST) {
+#pragma unroll
+      for (int i = 0; i < UX / NTH; ++i) {
+        const int u = tidv + NTH * i, r = u / (C / 4), ch = u % (C / 4);
+        rx[i] = *reinterpret_cast<const u32x4*>(xws + slot * C * C + r * C + 4 * ch);
+      }
+    }
     // U = T D and dD = T^T dU (= dV)
     {
       const int rt = w >> 1, c = w & 1;
@@ -285,12 +299,9 @@ __global__ __launch_bounds__((BwdTrShape<DK, C>::NTH)) __attribute__((amdgpu_wav
       __syncthreads();  // every read of this block's operands done
       dma_block(v0 + BV, false);
     }
-  }
-#pragma unroll
-  for (int i = 0; i < UX / NTH; ++i) {
-    const int u = tid + NTH * i, r = u / (C / 4), ch = u % (C / 4);
-    rx[i] = *reinterpret_cast<const u32x4*>(xws + slot * C * C + r * C + 4 * ch);
-  }
+  };
+  for (int v0 = 0; v0 + BV < DV; v0 += BV) block(v0, std::false_type{});
+  block(DV - BV, std::true_type{});
   wait_vmcnt<0>();   // Q's transfers and X
   __syncthreads();  // done with the loop's arrays (K stays); Q in place
 
