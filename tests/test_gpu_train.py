@@ -204,3 +204,28 @@ def test_train_pair_full_1p3b_shape():
         print(f"[train] full shape (b{b}, h{h}) vs oracle: " + ", ".join(f"{n} {e:.2e}" for n, e in errs.items()),
               flush=True)
         assert all(e <= GRAD_TOL for e in errs.values()), errs
+
+
+@pytest.mark.parametrize("env", [("EFLA_BWD_CHUNK", "stager"), ("EFLA_BWD_REVERSE", "stager"),
+                                 ("EFLA_BWD_IMPL", "fp32"), ("EFLA_BWD_STATES", "roles")],
+                         ids=lambda e: f"{e[0]}={e[1]}")
+def test_train_backward_under_every_kernel_choice(env, monkeypatch):
+    """The paired backward with each backward kernel the environment can
+    select (after a forward under the defaults): the stored states are read by
+    the one-workgroup per-chunk kernel and by the sixteen-wavefront reverse
+    pass too; with the fp32 kernels (and the state kernel choice, which the
+    stored states make moot) everything is recomputed."""
+    require_gpu()
+    inp = _inputs(128, 128, 200, 2, 2, 1800)
+    d_o, dsf = _cotangents(inp, 19)
+    q, k, v, beta, s0 = inp["q"], inp["k"], inp["v"], inp["beta"], inp["s0"]
+    for name in ("EFLA_BWD_CHUNK", "EFLA_BWD_REVERSE", "EFLA_BWD_IMPL", "EFLA_BWD_STATES"):
+        monkeypatch.delenv(name, raising=False)
+    _, _, ws = efla.efla_chunk_fwd_train(q, k, v, beta, s0, chunk=64)
+    monkeypatch.setenv(*env)
+    got = efla.efla_chunk_bwd_train(q, k, v, beta, d_o, ws, s0, dsf, chunk=64)
+    torch.cuda.synchronize()
+    want = oracle.backward(to_f64(q), to_f64(k), to_f64(v), to_f64(beta), to_f64(s0), to_f64(d_o), to_f64(dsf))
+    errs = {n: normwise(to_f64(a), b) for n, a, b in zip(NAMES, got, want)}
+    print(f"[train] {env[0]}={env[1]}: " + ", ".join(f"{n} {e:.2e}" for n, e in errs.items()), flush=True)
+    assert all(e <= GRAD_TOL for e in errs.values()), errs
