@@ -28,7 +28,8 @@ STATE_TOL = 1e-2     # bf16 operand values of a state (2^-9 relative rounding) a
 AGREE_TOL = 5e-3     # stored vs recomputed states: the same quantities, summed in another order
 
 # d_k, d_v, L (ragged last chunk where L % 64 != 0), B, H
-SHAPES = [(128, 128, 300, 2, 3), (64, 64, 257, 2, 2), (128, 64, 130, 1, 4), (64, 128, 64, 2, 2)]
+SHAPES = [(128, 128, 300, 2, 3), (64, 64, 257, 2, 2), (128, 64, 130, 1, 4), (64, 128, 64, 2, 2),
+          (128, 32, 190, 3, 1), (64, 32, 70, 1, 1)]   # one value block; a single sequence and head
 
 
 def _al(x):
